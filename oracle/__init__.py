@@ -1,0 +1,231 @@
+"""CPU oracle for the verification pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never loads it, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, serial fp64 sums, pthreads over
+output columns); this module only marshals numpy arrays through ctypes.  See
+the header of ``oracle.c`` for the definitions and the passages they follow.
+
+Parity unpinned (no page fixes them; they are internally consistent readings):
+the SiLU activation and the bf16 rounding of the MoE intermediate, and the
+bf16 rounding of the first product in the tiny chained verify pass.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+FMT_NVFP4 = 1
+FMT_Q4_0 = 2
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+             "-pthread"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        lib.orc_e2m1.restype = ctypes.c_double
+        lib.orc_e2m1.argtypes = [ctypes.c_uint32]
+        lib.orc_e4m3.restype = ctypes.c_double
+        lib.orc_e4m3.argtypes = [ctypes.c_uint32]
+        lib.orc_f16.restype = ctypes.c_double
+        lib.orc_f16.argtypes = [ctypes.c_uint32]
+        lib.orc_bf16.restype = ctypes.c_double
+        lib.orc_bf16.argtypes = [ctypes.c_uint32]
+        lib.orc_bf16_rne.restype = ctypes.c_uint16
+        lib.orc_bf16_rne.argtypes = [ctypes.c_double]
+        lib.orc_weight.restype = ctypes.c_double
+        lib.orc_weight.argtypes = [ctypes.c_int, ctypes.c_int, P, P, f32, i64, i64]
+        lib.orc_gemm.restype = ctypes.c_int
+        lib.orc_gemm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, i64,
+                                 P, P, f32, P, i64, P, P, ctypes.c_int]
+        lib.orc_moe.restype = ctypes.c_int
+        lib.orc_moe.argtypes = [ctypes.c_int] * 6 + [P] * 9 + [P, P, P, ctypes.c_int]
+        lib.orc_argmax.restype = i32
+        lib.orc_argmax.argtypes = [P, ctypes.c_int]
+        lib.orc_accept_greedy.restype = ctypes.c_int
+        lib.orc_accept_greedy.argtypes = [P, ctypes.c_int, ctypes.c_int, i64, P, i64, P, P, P]
+        lib.orc_accept_rejection.restype = ctypes.c_int
+        lib.orc_accept_rejection.argtypes = [P, ctypes.c_int, ctypes.c_int, i64, P, i64, P, P,
+                                             f32, f32, i64, P, P, P, P]
+        _lib = lib
+        return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _threads(n=None):
+    if n:
+        return int(n)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# ---------------------------------------------------------------------------
+# element decoders (scalar; for pins)
+# ---------------------------------------------------------------------------
+
+def e2m1(code: int) -> float:
+    return _load().orc_e2m1(int(code))
+
+
+def e4m3(byte: int) -> float:
+    return _load().orc_e4m3(int(byte))
+
+
+def f16(bits: int) -> float:
+    return _load().orc_f16(int(bits))
+
+
+def bf16(bits: int) -> float:
+    return _load().orc_bf16(int(bits))
+
+
+def bf16_rne(v: float) -> int:
+    return int(_load().orc_bf16_rne(float(v)))
+
+
+def weight(w: dict, n: int, k: int) -> float:
+    codes = np.ascontiguousarray(w["codes"])
+    scales = np.ascontiguousarray(w["scales"])
+    return _load().orc_weight(w["format"], w["K"], _ptr(codes), _ptr(scales),
+                              float(w.get("g", 1.0)), int(n), int(k))
+
+
+# ---------------------------------------------------------------------------
+# verify GEMM
+# ---------------------------------------------------------------------------
+
+def gemm(w: dict, x: np.ndarray, cols=None, with_bound: bool = True, nthreads=None):
+    """y[m][c] = sum_k x[m][k] * w(cols[c], k) in fp64.  x: uint16 bf16 bits
+    [M][K].  Returns (y, b) as float64 [M][len(cols)] (b = sum |x*w|, or None)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, K = x.shape
+    assert K == w["K"]
+    codes = np.ascontiguousarray(w["codes"], dtype=np.uint8)
+    scales = np.ascontiguousarray(w["scales"])
+    if cols is None:
+        ncols = w["N"]
+        colsarr = None
+    else:
+        colsarr = np.ascontiguousarray(cols, dtype=np.int64)
+        ncols = len(colsarr)
+    y = np.zeros((M, ncols), np.float64)
+    b = np.zeros((M, ncols), np.float64) if with_bound else None
+    rc = lib.orc_gemm(w["format"], M, w["N"], K, _ptr(x), K, _ptr(codes), _ptr(scales),
+                      float(w.get("g", 1.0)), _ptr(colsarr), ncols, _ptr(y), _ptr(b),
+                      _threads(nthreads))
+    if rc != 0:
+        raise ValueError("orc_gemm rejected its arguments")
+    return y, b
+
+
+# ---------------------------------------------------------------------------
+# MoE
+# ---------------------------------------------------------------------------
+
+def moe(cfg: dict, nthreads=None):
+    """Returns (out[T][H], outb[T][H], h[T*topk][F] bf16 bits)."""
+    lib = _load()
+    T, H, F, E, topk = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["topk"]
+    gu, dn = cfg["gate_up"], cfg["down"]
+    assert gu["format"] == dn["format"]
+    x = np.ascontiguousarray(cfg["x"], dtype=np.uint16)
+    ids = np.ascontiguousarray(cfg["ids"], dtype=np.int32)
+    gw = np.ascontiguousarray(cfg["gw"], dtype=np.float32)
+    arrs = [np.ascontiguousarray(a) for a in (gu["codes"], gu["scales"], dn["codes"], dn["scales"])]
+    gug = None if gu.get("g") is None else np.ascontiguousarray(gu["g"], dtype=np.float32)
+    dng = None if dn.get("g") is None else np.ascontiguousarray(dn["g"], dtype=np.float32)
+    out = np.zeros((T, H), np.float64)
+    outb = np.zeros((T, H), np.float64)
+    h = np.zeros((T * topk, F), np.uint16)
+    rc = lib.orc_moe(gu["format"], T, H, F, E, topk, _ptr(x), _ptr(ids), _ptr(gw),
+                     _ptr(arrs[0]), _ptr(arrs[1]), _ptr(gug), _ptr(arrs[2]), _ptr(arrs[3]),
+                     _ptr(dng), _ptr(out), _ptr(outb), _ptr(h), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("orc_moe rejected its arguments")
+    return out, outb, h
+
+
+# ---------------------------------------------------------------------------
+# acceptance
+# ---------------------------------------------------------------------------
+
+def argmax(row: np.ndarray) -> int:
+    row = np.ascontiguousarray(row, dtype=np.float32)
+    return int(_load().orc_argmax(_ptr(row), row.shape[0]))
+
+
+def accept_greedy(logits: np.ndarray, drafts: np.ndarray, base_len: int = 0):
+    lib = _load()
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    M, V = logits.shape
+    d = np.ascontiguousarray(drafts if drafts is not None and len(drafts) else np.zeros(1),
+                             dtype=np.int32)
+    tokens = np.zeros(M, np.int32)
+    counts = np.zeros(2, np.int32)
+    rb = np.zeros(1, np.int64)
+    rc = lib.orc_accept_greedy(_ptr(logits), M, V, V, _ptr(d), int(base_len), _ptr(tokens),
+                               _ptr(counts), _ptr(rb))
+    if rc != 0:
+        raise ValueError("orc_accept_greedy rejected its arguments")
+    return tokens, counts, int(rb[0])
+
+
+def accept_rejection(logits: np.ndarray, q: np.ndarray, drafts: np.ndarray, u: np.ndarray,
+                     temperature: float, top_p: float, base_len: int = 0,
+                     with_margins: bool = False):
+    lib = _load()
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    M, V = logits.shape
+    if M > 1:
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        assert q.shape == (M - 1, V)
+        d = np.ascontiguousarray(drafts, dtype=np.int32)
+    else:
+        q = np.zeros((1, V), np.float32)
+        d = np.zeros(1, np.int32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    assert u.shape[0] >= M
+    tokens = np.zeros(M, np.int32)
+    counts = np.zeros(2, np.int32)
+    rb = np.zeros(1, np.int64)
+    margins = np.zeros(M + 1, np.float64)
+    rc = lib.orc_accept_rejection(_ptr(logits), M, V, V, _ptr(q), V, _ptr(d), _ptr(u),
+                                  float(temperature), float(top_p), int(base_len), _ptr(tokens),
+                                  _ptr(counts), _ptr(rb), _ptr(margins))
+    if rc != 0:
+        raise ValueError("orc_accept_rejection rejected its arguments")
+    if with_margins:
+        return tokens, counts, int(rb[0]), margins
+    return tokens, counts, int(rb[0])
