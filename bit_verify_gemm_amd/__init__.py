@@ -1,0 +1,189 @@
+"""Python binding of libmtpverify (the MTP verification pass on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/mtp_verify.h``.  PyTorch
+supplies device memory and the current stream.  If the library has not been
+built this module raises on first use; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "FMT_NVFP4", "FMT_Q4_0", "MAX_M", "MtpError", "lib", "abi_version",
+    "gemm_workspace_bytes", "moe_workspace_bytes", "accept_workspace_bytes",
+    "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
+]
+
+FMT_NVFP4 = 1
+FMT_Q4_0 = 2
+MAX_M = 16
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtpverify.so")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MtpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmtpverify.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                ctypes.c_size_t)
+        L.mtp_abi_version.restype = i32
+        L.mtp_abi_version.argtypes = []
+        L.mtp_last_error.restype = ctypes.c_char_p
+        L.mtp_last_error.argtypes = []
+        L.mtp_gemm_workspace_bytes.restype = sz
+        L.mtp_gemm_workspace_bytes.argtypes = [i32, i32, i32]
+        L.mtp_verify_gemm.restype = i32
+        L.mtp_verify_gemm.argtypes = [i32, i32, i32, i32, P, i64, P, P, f32, P, i64, P, i64, P, sz, P]
+        L.mtp_moe_workspace_bytes.restype = sz
+        L.mtp_moe_workspace_bytes.argtypes = [i32] * 5
+        L.mtp_verify_moe.restype = i32
+        L.mtp_verify_moe.argtypes = [i32] * 6 + [P] * 3 + [P, P, P, P, P, P] + [P, P, P, sz, P]
+        L.mtp_accept_workspace_bytes.restype = sz
+        L.mtp_accept_workspace_bytes.argtypes = [i32, i32]
+        L.mtp_accept_greedy.restype = i32
+        L.mtp_accept_greedy.argtypes = [P, i32, i32, i64, P, i64, P, P, P, P, sz, P]
+        L.mtp_accept_rejection.restype = i32
+        L.mtp_accept_rejection.argtypes = [P, i32, i32, i64, P, i64, P, P, f32, f32, i64, P, P, P,
+                                           P, sz, P]
+        _lib = L
+        return L
+
+
+def abi_version() -> int:
+    return int(lib().mtp_abi_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise MtpError(status, lib().mtp_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _ld(t):
+    return int(t.stride(0)) if t is not None and t.dim() >= 2 else 0
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mtp_gemm_workspace_bytes(M, N, K))
+
+
+def moe_workspace_bytes(T: int, H: int, F: int, E: int, topk: int) -> int:
+    return int(lib().mtp_moe_workspace_bytes(T, H, F, E, topk))
+
+
+def accept_workspace_bytes(M: int, V: int) -> int:
+    return int(lib().mtp_accept_workspace_bytes(M, V))
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return ws
+    if ws is None or _nbytes(ws) < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws
+
+
+def verify_gemm(fmt: int, x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, N: int,
+                K: int, global_scale: float = 1.0, y: torch.Tensor | None = None,
+                y_bf16: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                want_fp32: bool = True, stream=None):
+    """y[M][N] = x[M][K] . W.  x: bf16 (or its uint16/int16 bits) [M][>=K] on
+    the GPU.  Returns (y, y_bf16); allocates the outputs it is not given."""
+    M = x.shape[0]
+    dev = x.device
+    if y is None and want_fp32:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    wsb = gemm_workspace_bytes(M, N, K)
+    ws = _workspace(wsb, dev, ws)
+    _check(lib().mtp_verify_gemm(fmt, M, N, K, _ptr(x), _ld(x), _ptr(codes), _ptr(scales),
+                                 float(global_scale), _ptr(y), _ld(y), _ptr(y_bf16), _ld(y_bf16),
+                                 _ptr(ws), _nbytes(ws), _stream(stream)))
+    return y, y_bf16
+
+
+def verify_moe(fmt: int, x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+               gu_codes: torch.Tensor, gu_scales: torch.Tensor, dn_codes: torch.Tensor,
+               dn_scales: torch.Tensor, E: int, F: int, gu_global=None, dn_global=None,
+               out: torch.Tensor | None = None, h_out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None, stream=None):
+    """Routed MoE verify pass; returns out [T][H] fp32 (and h_out if given)."""
+    T, H = x.shape
+    topk = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    ws = _workspace(moe_workspace_bytes(T, H, F, E, topk), x.device, ws)
+    _check(lib().mtp_verify_moe(fmt, T, H, F, E, topk, _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+                                _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_global), _ptr(dn_codes),
+                                _ptr(dn_scales), _ptr(dn_global), _ptr(out), _ptr(h_out),
+                                _ptr(ws), _nbytes(ws), _stream(stream)))
+    return out, h_out
+
+
+def _accept_outputs(M, dev, outs):
+    if outs is not None:
+        return outs
+    return (torch.empty(M, dtype=torch.int32, device=dev),
+            torch.empty(2, dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int64, device=dev))
+
+
+def accept_greedy(logits: torch.Tensor, draft_ids: torch.Tensor | None, base_len: int = 0,
+                  outs=None, ws: torch.Tensor | None = None, stream=None):
+    """Returns (tokens[M] int32, counts[2] int32, rollback[1] int64) on the GPU."""
+    M, V = logits.shape
+    tok, cnt, rb = _accept_outputs(M, logits.device, outs)
+    ws = _workspace(accept_workspace_bytes(M, V), logits.device, ws)
+    _check(lib().mtp_accept_greedy(_ptr(logits), M, V, _ld(logits), _ptr(draft_ids),
+                                   int(base_len), _ptr(tok), _ptr(cnt), _ptr(rb), _ptr(ws),
+                                   _nbytes(ws), _stream(stream)))
+    return tok, cnt, rb
+
+
+def accept_rejection(logits: torch.Tensor, draft_probs: torch.Tensor | None,
+                     draft_ids: torch.Tensor | None, uniforms: torch.Tensor, temperature: float,
+                     top_p: float, base_len: int = 0, outs=None, ws: torch.Tensor | None = None,
+                     stream=None):
+    """Returns (tokens[M] int32, counts[2] int32, rollback[1] int64) on the GPU."""
+    M, V = logits.shape
+    tok, cnt, rb = _accept_outputs(M, logits.device, outs)
+    ws = _workspace(accept_workspace_bytes(M, V), logits.device, ws)
+    _check(lib().mtp_accept_rejection(_ptr(logits), M, V, _ld(logits), _ptr(draft_probs),
+                                      _ld(draft_probs), _ptr(draft_ids), _ptr(uniforms),
+                                      float(temperature), float(top_p), int(base_len), _ptr(tok),
+                                      _ptr(cnt), _ptr(rb), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)))
+    return tok, cnt, rb

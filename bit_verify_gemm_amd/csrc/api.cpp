@@ -1,0 +1,184 @@
+// C ABI of the verify-pass library: argument checks on the host, workspace
+// sizing, and dispatch to the HIP launchers.  Every check runs before any HIP
+// call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mtp_verify.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) {
+    g_error.clear();
+    return MTP_OK;
+  }
+  return fail(MTP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_format(int f) { return f == MTP_FMT_NVFP4 || f == MTP_FMT_Q4_0; }
+
+// Checks shared by the dense GEMM and the MoE weight sets.
+int check_weights(const char *who, int format, int K, const void *codes, const void *scales) {
+  if (!valid_format(format)) return fail(MTP_ERR_FORMAT, "%s: unknown weight format %d", who, format);
+  if (K < 32 || K % 32) return fail(MTP_ERR_SHAPE, "%s: K=%d must be a positive multiple of 32", who, K);
+  if (!codes || !scales) return fail(MTP_ERR_NULL, "%s: codes and scales are required", who);
+  if (!aligned(codes, 16) || !aligned(scales, 16))
+    return fail(MTP_ERR_ALIGN, "%s: codes and scales must be 16-byte aligned", who);
+  return MTP_OK;
+}
+
+constexpr int kMaxAcceptRows = 64;
+constexpr int kMaxVocab = 1 << 26;
+
+int check_accept_common(const char *who, const float *logits, int M, int V, int64_t ldl,
+                        const int32_t *drafts, int32_t *tokens, int32_t *counts,
+                        int64_t *rollback, void *ws, size_t ws_bytes) {
+  if (M < 1 || M > kMaxAcceptRows) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, %d]", who, M, kMaxAcceptRows);
+  if (V < 1 || V > kMaxVocab) return fail(MTP_ERR_SHAPE, "%s: V=%d out of [1, %d]", who, V, kMaxVocab);
+  if (ldl < V) return fail(MTP_ERR_SHAPE, "%s: ldl=%lld < V=%d", who, (long long)ldl, V);
+  if (!logits || !tokens || !counts || !rollback)
+    return fail(MTP_ERR_NULL, "%s: logits and outputs are required", who);
+  if (M > 1 && !drafts) return fail(MTP_ERR_NULL, "%s: draft_ids required for M > 1", who);
+  if (!aligned(logits, 4)) return fail(MTP_ERR_ALIGN, "%s: logits must be 4-byte aligned", who);
+  const size_t need = mtp::accept_ws_bytes(M, V);
+  if (!ws || ws_bytes < need)
+    return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 256)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+  return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtp_abi_version(void) { return MTP_ABI_VERSION; }
+
+const char *mtp_last_error(void) { return g_error.c_str(); }
+
+size_t mtp_gemm_workspace_bytes(int M, int N, int K) {
+  if (M < 1 || M > MTP_MAX_M || N < 1 || K < 32 || K % 32) return 0;
+  return mtp::gemm_plan(M, N, K).ws_bytes;
+}
+
+int mtp_verify_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t ldx,
+                    const uint8_t *codes, const void *scales, float global_scale, float *y,
+                    int64_t ldy, uint16_t *y_bf16, int64_t ldyb, void *ws, size_t ws_bytes,
+                    void *stream) {
+  const char *who = "mtp_verify_gemm";
+  if (int rc = check_weights(who, format, K, codes, scales)) return rc;
+  if (M < 1 || M > MTP_MAX_M) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, %d]", who, M, MTP_MAX_M);
+  if (N < 1) return fail(MTP_ERR_SHAPE, "%s: N=%d must be positive", who, N);
+  if (!x) return fail(MTP_ERR_NULL, "%s: x is required", who);
+  if (!y && !y_bf16) return fail(MTP_ERR_NULL, "%s: y or y_bf16 is required", who);
+  if (ldx < K) return fail(MTP_ERR_SHAPE, "%s: ldx=%lld < K=%d", who, (long long)ldx, K);
+  if (ldx % 8 || !aligned(x, 16)) return fail(MTP_ERR_ALIGN, "%s: x must be 16-byte aligned with ldx %% 8 == 0", who);
+  if (y && ldy < N) return fail(MTP_ERR_SHAPE, "%s: ldy=%lld < N=%d", who, (long long)ldy, N);
+  if (y_bf16 && ldyb < N) return fail(MTP_ERR_SHAPE, "%s: ldyb=%lld < N=%d", who, (long long)ldyb, N);
+  if (y && !aligned(y, 4)) return fail(MTP_ERR_ALIGN, "%s: y must be 4-byte aligned", who);
+  if (y_bf16 && !aligned(y_bf16, 2)) return fail(MTP_ERR_ALIGN, "%s: y_bf16 must be 2-byte aligned", who);
+  const mtp::GemmPlan plan = mtp::gemm_plan(M, N, K);
+  if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
+    return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who,
+                plan.ws_bytes, ws ? ws_bytes : (size_t)0);
+  if (plan.ws_bytes && !aligned(ws, 16)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  return hip_status(mtp::launch_gemm(format, M, N, K, x, ldx, codes, scales, global_scale, y, ldy,
+                                     y_bf16, ldyb, ws, plan, static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk) {
+  if (T < 1 || topk < 1 || (int64_t)T * topk > 1024 || E < 1 || H < 32 || H % 32 || F < 32 || F % 32)
+    return 0;
+  return mtp::moe_ws_bytes(T, H, F, E, topk);
+}
+
+int mtp_verify_moe(int format, int T, int H, int F, int E, int topk, const uint16_t *x,
+                   const int32_t *topk_ids, const float *topk_w, const uint8_t *gu_codes,
+                   const void *gu_scales, const float *gu_global, const uint8_t *dn_codes,
+                   const void *dn_scales, const float *dn_global, float *out, uint16_t *h_out,
+                   void *ws, size_t ws_bytes, void *stream) {
+  const char *who = "mtp_verify_moe";
+  if (!valid_format(format)) return fail(MTP_ERR_FORMAT, "%s: unknown weight format %d", who, format);
+  if (T < 1 || topk < 1 || (int64_t)T * topk > 1024)
+    return fail(MTP_ERR_SHAPE, "%s: need T >= 1, topk >= 1, T*topk <= 1024 (T=%d, topk=%d)", who, T, topk);
+  if (E < 1 || E > (1 << 20)) return fail(MTP_ERR_SHAPE, "%s: E=%d out of [1, 2^20]", who, E);
+  if (int rc = check_weights(who, format, H, gu_codes, gu_scales)) return rc;
+  if (int rc = check_weights(who, format, F, dn_codes, dn_scales)) return rc;
+  if (!x || !topk_ids || !topk_w || !out) return fail(MTP_ERR_NULL, "%s: x, ids, weights and out are required", who);
+  if (!aligned(x, 16)) return fail(MTP_ERR_ALIGN, "%s: x must be 16-byte aligned", who);
+  const size_t need = mtp::moe_ws_bytes(T, H, F, E, topk);
+  if (!ws || ws_bytes < need)
+    return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 256)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+  return hip_status(mtp::launch_moe(format, T, H, F, E, topk, x, topk_ids, topk_w, gu_codes,
+                                    gu_scales, gu_global, dn_codes, dn_scales, dn_global, out,
+                                    h_out, ws, static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+size_t mtp_accept_workspace_bytes(int M, int V) {
+  if (M < 1 || M > kMaxAcceptRows || V < 1 || V > kMaxVocab) return 0;
+  return mtp::accept_ws_bytes(M, V);
+}
+
+int mtp_accept_greedy(const float *logits, int M, int V, int64_t ldl, const int32_t *draft_ids,
+                      int64_t base_len, int32_t *out_tokens, int32_t *out_counts,
+                      int64_t *out_rollback, void *ws, size_t ws_bytes, void *stream) {
+  const char *who = "mtp_accept_greedy";
+  if (int rc = check_accept_common(who, logits, M, V, ldl, draft_ids, out_tokens, out_counts,
+                                   out_rollback, ws, ws_bytes))
+    return rc;
+  return hip_status(mtp::launch_accept_greedy(logits, M, V, ldl, draft_ids, base_len, out_tokens,
+                                              out_counts, out_rollback, ws,
+                                              static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
+                         const float *draft_probs, int64_t ldq, const int32_t *draft_ids,
+                         const float *uniforms, float temperature, float top_p, int64_t base_len,
+                         int32_t *out_tokens, int32_t *out_counts, int64_t *out_rollback,
+                         void *ws, size_t ws_bytes, void *stream) {
+  const char *who = "mtp_accept_rejection";
+  if (int rc = check_accept_common(who, logits, M, V, ldl, draft_ids, out_tokens, out_counts,
+                                   out_rollback, ws, ws_bytes))
+    return rc;
+  if (!(temperature >= 0.0f) || temperature != temperature)
+    return fail(MTP_ERR_VALUE, "%s: temperature must be >= 0 (got %g)", who, (double)temperature);
+  if (top_p != top_p) return fail(MTP_ERR_VALUE, "%s: top_p is NaN", who);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (temperature == 0.0f)
+    return hip_status(mtp::launch_accept_greedy(logits, M, V, ldl, draft_ids, base_len,
+                                                out_tokens, out_counts, out_rollback, ws, s),
+                      who);
+  if (!uniforms) return fail(MTP_ERR_NULL, "%s: uniforms are required", who);
+  if (M > 1 && !draft_probs) return fail(MTP_ERR_NULL, "%s: draft_probs required for M > 1", who);
+  if (M > 1 && ldq < V) return fail(MTP_ERR_SHAPE, "%s: ldq=%lld < V=%d", who, (long long)ldq, V);
+  return hip_status(mtp::launch_accept_rejection(logits, M, V, ldl, draft_probs, ldq, draft_ids,
+                                                 uniforms, temperature, top_p, base_len,
+                                                 out_tokens, out_counts, out_rollback, ws, s),
+                    who);
+}
+
+}  // extern "C"

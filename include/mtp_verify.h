@@ -1,0 +1,197 @@
+/*
+ * mtp_verify.h -- the verification pass of multi-token-prediction (MTP)
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages' own sections):
+ *
+ *  - The verify GEMM.  "Faster Gemma 4 on MLX with multi-token prediction"
+ *    (Ollama news item), sixth paragraph: verification costs most of an MTP
+ *    step; its batch of 2-8 tokens sits between matrix-vector and large
+ *    matrix-matrix shapes; the kernel reads and unpacks every block of nvfp4
+ *    weights once and reuses it for the whole batch, with computation
+ *    identical to the per-token product.  The Qiita roofline article (§2-3)
+ *    adds that the weight bytes stay the same while only the arithmetic
+ *    grows with the batch, and ("前提") fixes Q4-class weights at about half
+ *    a byte per parameter.
+ *  - The MoE variant.  Same article, §3-2: a verify mini-batch routes its
+ *    tokens to more distinct experts ("expert scattering"), so the unique
+ *    expert bytes grow with the batch; each unique expert is read once here.
+ *  - Acceptance.  Gemini Nano summary, analysis §3, and the Qiita article,
+ *    §2-4: greedy verification keeps the longest prefix agreeing with the
+ *    target and always commits one more token.  MTPLX blog post, "Why it is
+ *    interesting on a Mac specifically": Leviathan/Chen rejection sampling
+ *    with residual correction at temperature 0.6, top_p 0.95.  Ollama mtp.go
+ *    commit log, sampler rework and "greedy is a special case": temperature,
+ *    softmax, top-p, normalise, categorical; at temperature 0 acceptance is
+ *    argmax matching.  Ollama news item, fifth paragraph: a rollback point is
+ *    recorded so that a rejection rewinds to the last accepted token.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory, including the workspace; the library never allocates, frees or
+ *    keeps device memory, and keeps no pointer after it returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) of the calling thread's current
+ *    device.  The library never synchronises.  Buffers must stay alive
+ *    until the stream passes the work.
+ *  - Return value: MTP_OK (0) or a negative MTP_ERR_* code.  Arguments are
+ *    checked on the host before anything is enqueued; on error nothing is
+ *    enqueued and mtp_last_error() describes the problem.  Launch failures
+ *    return MTP_ERR_HIP.  Device faults surface at the caller's next
+ *    synchronisation.  Device-resident data (ids, uniforms) is never read on
+ *    the host; out-of-range ids are handled as documented per call.
+ *  - Calls are reentrant; the only global state is the thread-local error
+ *    string.  Calls that share a workspace must be ordered on one stream.
+ *
+ * Weight formats (the pages name "nvfp4" and "Q4"; the layouts are this
+ * library's): a K x N matrix used as y = x . W is stored per output row n.
+ *   codes : uint8 [N][K/2]; weight (n, k) is the low nibble of byte
+ *           n*K/2 + k/2 for even k and the high nibble for odd k.
+ *   MTP_FMT_NVFP4: nibble = E2M1 (bit3 sign, bits2..1 exponent bias 1, bit0
+ *           mantissa); scales = uint8 E4M3 "FN" [N][K/16] (bias 7, 0x7F/0xFF
+ *           NaN); w = global_scale * e4m3(scale[n][k/16]) * e2m1(nibble).
+ *   MTP_FMT_Q4_0: nibble u = offset-binary int4; scales = IEEE fp16
+ *           [N][K/32]; w = global_scale * f16(scale[n][k/32]) * (u - 8).
+ *   K must be a positive multiple of 32; codes and scales 16-byte aligned.
+ *   Matrices stacked along N (fused Q/K/V, gate||up) are just more rows.
+ * Activations: bf16 bit patterns (uint16), row-major with a row stride in
+ * elements; accumulation is fp32.
+ */
+#ifndef MTP_VERIFY_H
+#define MTP_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_ABI_VERSION 1
+
+enum {
+  MTP_OK = 0,
+  MTP_ERR_NULL = -1,      /* a required pointer is NULL                       */
+  MTP_ERR_SHAPE = -2,     /* a size, count or stride is out of range          */
+  MTP_ERR_ALIGN = -3,     /* a pointer or stride breaks an alignment rule     */
+  MTP_ERR_FORMAT = -4,    /* unknown weight format                            */
+  MTP_ERR_WORKSPACE = -5, /* workspace missing or smaller than required       */
+  MTP_ERR_HIP = -6,       /* a HIP launch failed                              */
+  MTP_ERR_VALUE = -7      /* a scalar argument is out of range (temperature)  */
+};
+
+enum { MTP_FMT_NVFP4 = 1, MTP_FMT_Q4_0 = 2 };
+
+/* Largest row count of one verify pass (drafts + 1). */
+#define MTP_MAX_M 16
+
+/*
+ * Verify GEMM: y[m][n] = global_scale * sum_k x[m][k] * w(n, k) for
+ * m < M, n < N, with every weight byte read once for all M rows.
+ *   format       MTP_FMT_NVFP4 or MTP_FMT_Q4_0
+ *   M            1..MTP_MAX_M rows (the committed token plus the drafts)
+ *   N, K         output columns (>= 1) and reduction length (multiple of 32)
+ *   x, ldx       bf16 [M][ldx], ldx >= K, ldx % 8 == 0, x 16-byte aligned
+ *   codes,scales the weight matrix as described above
+ *   global_scale (host) fp32 multiplier applied to every weight
+ *   y, ldy       fp32 output [M][ldy], ldy >= N; may be NULL if y_bf16 is set
+ *   y_bf16,ldyb  optional bf16 copy of y (round to nearest even) [M][ldyb];
+ *                may be NULL.  At least one of y and y_bf16 must be non-NULL.
+ *   ws, ws_bytes workspace of at least mtp_gemm_workspace_bytes(M, N, K)
+ *                bytes (may be NULL when that is 0)
+ * Accuracy: |y - exact| <= 1e-3 * sum_k |x * w| + 1e-5 (fp32 accumulation);
+ * results are deterministic and do not depend on M for a given row.
+ */
+int mtp_verify_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t ldx,
+                    const uint8_t *codes, const void *scales, float global_scale, float *y,
+                    int64_t ldy, uint16_t *y_bf16, int64_t ldyb, void *ws, size_t ws_bytes,
+                    void *stream);
+
+size_t mtp_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * Routed MoE verify pass for T token rows, each routed to `topk` of E
+ * experts.  Expert e is a gated FFN H -> F -> H:
+ *   a = W_gu[e] . x_t   (2F outputs: rows [0, F) gate, rows [F, 2F) up)
+ *   h = bf16_rne( silu(a_gate) * a_up ),  silu(v) = v / (1 + exp(-v))
+ *   y = W_d[e] . h      (H outputs)
+ *   out[t] = sum over slots s = 0..topk-1, in slot order, of topk_w[t][s] * y
+ * Each expert that at least one token selects is read once for all of its
+ * tokens (the grouping and deduplication run on the device).
+ *   format          both weight sets use it
+ *   T, H, F, E, topk  1 <= T, 1 <= topk, T*topk <= 1024, 1 <= E,
+ *                   H and F multiples of 32
+ *   x               bf16 [T][H] (row stride H), 16-byte aligned
+ *   topk_ids        int32 [T][topk]; an id outside [0, E) contributes nothing
+ *   topk_w          fp32 [T][topk]
+ *   gu_codes/gu_scales  expert e at byte offset e*2F*H/2 (codes) and
+ *                   e*2F*(H/bs)*sizeof(scale) (scales), bs = 16 or 32
+ *   gu_global       device fp32 [E] per-expert global scales, or NULL (1.0)
+ *   dn_codes/dn_scales/dn_global  the same for the down projections (K = F,
+ *                   N = H)
+ *   out             fp32 [T][H]
+ *   h_out           optional bf16 [T*topk][F] copy of h (pair p = t*topk+s;
+ *                   rows of out-of-range ids are zero); may be NULL
+ *   ws, ws_bytes    at least mtp_moe_workspace_bytes(T, H, F, E, topk)
+ */
+int mtp_verify_moe(int format, int T, int H, int F, int E, int topk, const uint16_t *x,
+                   const int32_t *topk_ids, const float *topk_w, const uint8_t *gu_codes,
+                   const void *gu_scales, const float *gu_global, const uint8_t *dn_codes,
+                   const void *dn_scales, const float *dn_global, float *out, uint16_t *h_out,
+                   void *ws, size_t ws_bytes, void *stream);
+
+size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk);
+
+/*
+ * Greedy acceptance over M verified rows.  Row i of `logits` is the target's
+ * next-token scores after row i's input (row 0: the last committed token,
+ * row i+1: draft i).  g_i = argmax of row i (NaN ranks below every number,
+ * the lowest index wins ties, an all-NaN row gives 0).  a = number of leading
+ * drafts with draft_ids[i] == g_i.  Outputs, written together:
+ *   out_tokens[0..a] = g_0..g_a (a accepted drafts, then the correction or
+ *                      bonus token), out_tokens[a+1..M-1] = -1
+ *   out_counts       = {a, a + 1}   (accepted, committed)
+ *   out_rollback     = base_len + a + 1 (cache length to restore to)
+ *   logits, ldl      fp32 [M][ldl], 1 <= M <= 64, 1 <= V <= ldl
+ *   draft_ids        int32 [M-1] (may be NULL when M == 1)
+ *   ws, ws_bytes     at least mtp_accept_workspace_bytes(M, V)
+ */
+int mtp_accept_greedy(const float *logits, int M, int V, int64_t ldl, const int32_t *draft_ids,
+                      int64_t base_len, int32_t *out_tokens, int32_t *out_counts,
+                      int64_t *out_rollback, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Rejection-sampling acceptance (Leviathan/Chen) with residual correction.
+ * Target of row i, in fp64: e_j = exp((z_j - max z) / temperature); order j
+ * by (z descending, j ascending); the nucleus is the shortest prefix whose
+ * mass reaches top_p * sum(e) (top_p >= 1 keeps all, top_p <= 0 keeps one);
+ * p'_j = e_j / (nucleus mass) inside the nucleus, 0 outside.
+ * For i = 0..M-2: accept draft x_i iff u_i * q_i(x_i) < p'_i(x_i) (an id
+ * outside [0, V) is rejected); stop at the first rejection a.  Then draw the
+ * last committed token with u_{M-1}: from max(0, p'_a - q_a) if a < M-1
+ * (from p'_a if that is all zero), else from p'_{M-1} (bonus).  A draw from
+ * weights w picks the smallest j with w_0 + .. + w_j > u * sum(w).
+ * temperature == 0 gives exactly mtp_accept_greedy; temperature < 0 or NaN
+ * is MTP_ERR_VALUE.  Logits must be finite.
+ *   draft_probs, ldq fp32 [M-1][ldq] (the draft's final distributions)
+ *   uniforms         fp32 [M] in [0, 1), supplied by the caller (reproducible)
+ *   other arguments and outputs as for mtp_accept_greedy
+ */
+int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
+                         const float *draft_probs, int64_t ldq, const int32_t *draft_ids,
+                         const float *uniforms, float temperature, float top_p, int64_t base_len,
+                         int32_t *out_tokens, int32_t *out_counts, int64_t *out_rollback,
+                         void *ws, size_t ws_bytes, void *stream);
+
+size_t mtp_accept_workspace_bytes(int M, int V);
+
+/* Thread-local message for the last non-zero status of this thread. */
+const char *mtp_last_error(void);
+
+int mtp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_VERIFY_H */

@@ -1,0 +1,118 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+that include/mtp_verify.h declares, and rejects bad arguments on the host
+before enqueueing anything (no GPU work is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_verify_gemm_amd as bv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtp_verify.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("mtp_verify_gemm", "mtp_verify_moe", "mtp_accept_greedy", "mtp_accept_rejection"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bv.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version():
+    assert bv.abi_version() == 1
+
+
+def test_workspace_queries():
+    assert bv.gemm_workspace_bytes(8, 262144, 5376) == 0          # no K split needed
+    assert bv.gemm_workspace_bytes(8, 5120, 17408) > 0            # long K is split
+    assert bv.gemm_workspace_bytes(0, 10, 32) == 0
+    assert bv.gemm_workspace_bytes(1, 10, 33) == 0
+    assert bv.moe_workspace_bytes(8, 2048, 768, 128, 8) > 8 * 8 * 2048 * 4
+    assert bv.accept_workspace_bytes(8, 262144) > 0
+    assert bv.accept_workspace_bytes(65, 10) == 0
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced (checks fail first)
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+def gemm(**kw):
+    a = dict(fmt=1, M=4, N=64, K=256, x=FAKE, ldx=256, codes=FAKE, scales=FAKE, g=1.0, y=FAKE,
+             ldy=64, yb=None, ldyb=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return bv.lib().mtp_verify_gemm(a["fmt"], a["M"], a["N"], a["K"], a["x"], a["ldx"],
+                                    a["codes"], a["scales"], a["g"], a["y"], a["ldy"], a["yb"],
+                                    a["ldyb"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=3), -4), (dict(M=0), -2), (dict(M=17), -2), (dict(K=100), -2), (dict(K=0), -2),
+    (dict(N=0), -2), (dict(x=None), -1), (dict(codes=None), -1), (dict(y=None), -1),
+    (dict(ldx=128), -2), (dict(ldx=260), -3), (dict(x=FAKE_ODD), -3), (dict(codes=FAKE_ODD), -3),
+    (dict(ldy=10), -2), (dict(N=5120, K=17408, ldx=17408, ldy=5120), -5),
+])
+def test_gemm_rejects_bad_arguments(kw, code):
+    assert gemm(**kw) == code
+    assert bv.lib().mtp_last_error()
+
+
+def test_accept_rejects_bad_arguments():
+    L = bv.lib()
+    ws = ctypes.c_void_p(0x100000)
+    need = bv.accept_workspace_bytes(4, 100)
+    # M out of range
+    assert L.mtp_accept_greedy(FAKE, 0, 100, 100, FAKE, 0, FAKE, FAKE, FAKE, ws, need, None) == -2
+    # ldl < V
+    assert L.mtp_accept_greedy(FAKE, 4, 100, 50, FAKE, 0, FAKE, FAKE, FAKE, ws, need, None) == -2
+    # missing drafts with M > 1
+    assert L.mtp_accept_greedy(FAKE, 4, 100, 100, None, 0, FAKE, FAKE, FAKE, ws, need, None) == -1
+    # workspace too small
+    assert L.mtp_accept_greedy(FAKE, 4, 100, 100, FAKE, 0, FAKE, FAKE, FAKE, ws, need - 1, None) == -5
+    # negative / NaN temperature
+    assert L.mtp_accept_rejection(FAKE, 4, 100, 100, FAKE, 100, FAKE, FAKE, -1.0, 0.9, 0, FAKE,
+                                  FAKE, FAKE, ws, need, None) == -7
+    assert L.mtp_accept_rejection(FAKE, 4, 100, 100, FAKE, 100, FAKE, FAKE, float("nan"), 0.9, 0,
+                                  FAKE, FAKE, FAKE, ws, need, None) == -7
+    # missing uniforms / draft probabilities at T > 0
+    assert L.mtp_accept_rejection(FAKE, 4, 100, 100, FAKE, 100, FAKE, None, 0.6, 0.9, 0, FAKE,
+                                  FAKE, FAKE, ws, need, None) == -1
+    assert L.mtp_accept_rejection(FAKE, 4, 100, 100, None, 100, FAKE, FAKE, 0.6, 0.9, 0, FAKE,
+                                  FAKE, FAKE, ws, need, None) == -1
+
+
+def test_moe_rejects_bad_arguments():
+    L = bv.lib()
+    ws = ctypes.c_void_p(0x100000)
+    need = bv.moe_workspace_bytes(8, 2048, 768, 128, 8)
+    args = [1, 8, 2048, 768, 128, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+            None, ws, need, None]
+
+    def call(**kw):
+        a = list(args)
+        idx = {"fmt": 0, "T": 1, "H": 2, "F": 3, "E": 4, "topk": 5, "x": 6, "gu": 9, "wsb": 18}
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return L.mtp_verify_moe(*a)
+
+    assert call(fmt=0) == -4
+    assert call(T=0) == -2
+    assert call(T=200, topk=8) == -2
+    assert call(H=100) == -2
+    assert call(F=40) == -2
+    assert call(x=None) == -1
+    assert call(gu=None) == -1
+    assert call(wsb=need - 1) == -5

@@ -1,0 +1,176 @@
+"""GPU parity of mtp_accept_greedy / mtp_accept_rejection against the oracle.
+
+Bar: committed tokens, counts and the rollback index match bit for bit.  Both
+sides take every decision in fp64 from the same fp32 inputs; the oracle's
+margins are printed when a case disagrees (a mismatch can only come from a
+decision within ~1e-15 of its boundary).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import DEV, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+bv = pytest.importorskip("bit_verify_gemm_amd")
+
+
+def gpu_greedy(z, d, base):
+    t, c, r = bv.accept_greedy(dev(z), dev(d) if d is not None and len(d) else None, base)
+    return host(t), host(c), int(host(r)[0])
+
+
+def gpu_rej(z, q, d, u, T, top_p, base):
+    M = z.shape[0]
+    qt = dev(q) if M > 1 else None
+    dt = dev(d) if M > 1 else None
+    t, c, r = bv.accept_rejection(dev(z), qt, dt, dev(u), T, top_p, base)
+    return host(t), host(c), int(host(r)[0])
+
+
+def check_same(g, o, what, margins=None):
+    ok = np.array_equal(g[0], o[0]) and np.array_equal(g[1], o[1]) and g[2] == o[2]
+    if not ok:
+        raise AssertionError(f"{what}: gpu={g[0].tolist()} {g[1].tolist()} {g[2]} "
+                             f"oracle={o[0].tolist()} {o[1].tolist()} {o[2]} margins={margins}")
+
+
+@pytest.mark.parametrize("M,V", [(1, 1), (1, 7), (2, 5), (4, 1024), (8, 4097), (8, 262144),
+                                 (16, 300), (64, 33)])
+def test_greedy_matches_oracle(M, V):
+    rng = np.random.default_rng(M * 7 + V)
+    for trial in range(6):
+        if trial % 2:
+            z = rng.integers(-3, 4, size=(M, V)).astype(np.float32)     # many ties
+        else:
+            z = rng.standard_normal((M, V)).astype(np.float32)
+        if trial == 3 and V > 2:
+            z[0, :] = np.nan
+            z[min(1, M - 1), ::2] = np.nan
+        g = np.array([oracle.argmax(z[i]) for i in range(M)], np.int32)
+        L = int(rng.integers(0, M))
+        d = rng.integers(0, V, M - 1).astype(np.int32)
+        d[:L] = g[:L]
+        o = oracle.accept_greedy(z, d, 100 + trial)
+        check_same(gpu_greedy(z, d, 100 + trial), o, f"greedy M={M} V={V} trial={trial}")
+
+
+CASES = [
+    # M, V, T, top_p, alpha
+    (1, 5, 0.6, 0.95, 1.0), (2, 5, 1.0, 1.0, 1.0), (4, 64, 0.6, 0.95, 0.1), (4, 64, 1.7, 0.5, 1.0),
+    (8, 1000, 0.6, 0.95, 0.1), (8, 1000, 0.6, 0.0, 0.3), (3, 4099, 0.9, 0.999, 0.5),
+    (8, 262144, 0.6, 0.95, 0.1), (8, 262144, 1.0, 1.0, 0.1), (16, 2048, 0.3, 0.7, 1.0),
+]
+
+
+@pytest.mark.parametrize("M,V,T,top_p,alpha", CASES)
+def test_rejection_matches_oracle(M, V, T, top_p, alpha):
+    rng = np.random.default_rng(M + V + int(100 * T) + int(1000 * top_p))
+    log("rejection", M, V, T, top_p, alpha)
+    for trial in range(4 if V > 100000 else 12):
+        z = rng.standard_normal((M, V)).astype(np.float32) * np.float32(1 + trial % 3)
+        q = W.rand_dirichlet_rows(rng, max(M - 1, 1), V, alpha)[:M - 1]
+        d = np.zeros(M - 1, np.int32)
+        for i in range(M - 1):
+            if trial % 3 == 0:
+                d[i] = oracle.argmax(z[i])                     # likely accepted
+            else:
+                qd = q[i].astype(np.float64)
+                d[i] = rng.choice(V, p=qd / qd.sum())         # drafted from q
+        u = W.rand_uniforms(rng, M)
+        o = oracle.accept_rejection(z, q, d, u, T, top_p, 7, with_margins=True)
+        check_same(gpu_rej(z, q, d, u, T, top_p, 7), o[:3], f"rej trial={trial}", o[3])
+
+
+def test_rejection_ties_at_the_nucleus_cut():
+    rng = np.random.default_rng(4)
+    for trial in range(20):
+        M, V = 4, int(rng.integers(20, 3000))
+        z = rng.integers(-2, 3, size=(M, V)).astype(np.float32)   # heavy ties
+        q = W.rand_dirichlet_rows(rng, M - 1, V, 1.0)
+        d = rng.integers(0, V, M - 1).astype(np.int32)
+        u = W.rand_uniforms(rng, M)
+        top_p = float(rng.uniform(0.05, 0.99))
+        o = oracle.accept_rejection(z, q, d, u, 0.8, top_p, 0, with_margins=True)
+        check_same(gpu_rej(z, q, d, u, 0.8, top_p, 0), o[:3], f"ties trial={trial}", o[3])
+
+
+def test_temperature_zero_is_greedy_on_gpu():
+    rng = np.random.default_rng(5)
+    for trial in range(10):
+        M, V = 6, 777
+        z = rng.integers(-5, 5, size=(M, V)).astype(np.float32)
+        q = W.rand_dirichlet_rows(rng, M - 1, V, 1.0)
+        d = rng.integers(0, V, M - 1).astype(np.int32)
+        g = np.array([oracle.argmax(z[i]) for i in range(M)], np.int32)
+        d[:trial % M] = g[:trial % M]
+        u = W.rand_uniforms(rng, M)
+        check_same(gpu_rej(z, q, d, u, 0.0, 0.9, 3), gpu_greedy(z, d, 3), f"T0 trial={trial}")
+        check_same(gpu_rej(z, q, d, u, 0.0, 0.9, 3), oracle.accept_greedy(z, d, 3), "T0 oracle")
+
+
+def test_out_of_range_and_zero_probability_drafts():
+    V = 50
+    z = np.zeros((3, V), np.float32)
+    z[:, 0] = 10.0
+    q = np.full((2, V), 1.0 / V, np.float32)
+    u = np.array([0.5, 0.5, 0.3], np.float32)
+    for d in ([-1, 0], [V, 0], [7, 0], [0, 10 ** 6]):
+        d = np.array(d, np.int32)
+        o = oracle.accept_rejection(z, q, d, u, 1.0, 0.5, 0)
+        check_same(gpu_rej(z, q, d, u, 1.0, 0.5, 0), o, f"drafts {d.tolist()}")
+
+
+def test_same_trials_as_the_oracle_law():
+    # The GPU reproduces the oracle trial by trial on the uniforms the oracle's
+    # chi-square tests use, so the sampling law checked there holds here too.
+    rng = np.random.default_rng(11)
+    V, M, n = 8, 3, 400
+    z = rng.standard_normal((M, V)).astype(np.float32)
+    q = rng.dirichlet(np.full(V, 0.3), size=M - 1).astype(np.float32)
+    for t in range(n):
+        qd = q.astype(np.float64)
+        d = np.array([rng.choice(V, p=qd[i] / qd[i].sum()) for i in range(M - 1)], np.int32)
+        u = rng.random(M).astype(np.float32)
+        o = oracle.accept_rejection(z, q, d, u, 0.6, 0.95, 0)
+        check_same(gpu_rej(z, q, d, u, 0.6, 0.95, 0), o, f"law trial {t}")
+
+
+def test_lm_head_acceptance_staged():
+    # C3 shape: logits from the oracle's own fp64 head (rounded to fp32) feed
+    # both acceptance implementations; drafts planted on the oracle's argmax.
+    c = W.config3_inputs()
+    cols = None
+    log("C3 oracle logits (full head, fp64)")
+    y_ref, _ = oracle.gemm(c["w"], c["x"], cols=cols, with_bound=False)
+    z = y_ref.astype(np.float32)
+    g = np.array([oracle.argmax(z[i]) for i in range(c["M"])], np.int32)
+    d = W.plant_drafts(g, c["L"], c["filler"], c["miss"], c["V"])
+    o = oracle.accept_greedy(z, d, 4096)
+    assert o[1][0] == min(c["L"], c["M"] - 1)
+    check_same(gpu_greedy(z, d, 4096), o, "C3 greedy")
+    o = oracle.accept_rejection(z, c["q"], d, c["u"], c["temperature"], c["top_p"], 4096,
+                                with_margins=True)
+    check_same(gpu_rej(z, c["q"], d, c["u"], c["temperature"], c["top_p"], 4096), o[:3],
+               "C3 rejection", o[3])
+    # the same shape with spread logits (a nucleus of many thousand tokens)
+    zs = W.spread_logits(3, c["M"], c["V"])
+    gs = np.array([oracle.argmax(zs[i]) for i in range(c["M"])], np.int32)
+    ds = W.plant_drafts(gs, c["L"], c["filler"], c["miss"], c["V"])
+    o = oracle.accept_rejection(zs, c["q"], ds, c["u"], 0.6, 0.95, 4096, with_margins=True)
+    check_same(gpu_rej(zs, c["q"], ds, c["u"], 0.6, 0.95, 4096), o[:3], "C3 spread", o[3])
+
+
+def test_repeatable():
+    rng = np.random.default_rng(8)
+    M, V = 8, 100000
+    z = rng.standard_normal((M, V)).astype(np.float32)
+    q = W.rand_dirichlet_rows(rng, M - 1, V, 0.1)
+    d = rng.integers(0, V, M - 1).astype(np.int32)
+    u = W.rand_uniforms(rng, M)
+    a = gpu_rej(z, q, d, u, 0.6, 0.95, 0)
+    for _ in range(3):
+        check_same(gpu_rej(z, q, d, u, 0.6, 0.95, 0), a, "repeat")

@@ -1,0 +1,56 @@
+"""The tiny verify pass end to end on the GPU: x[4][2048] -> nvfp4 2048x2048
+-> bf16 -> nvfp4 head 2048->1024 -> greedy acceptance of 3 drafts.
+
+Staged parity: each stage gets the same inputs on both sides (the oracle's own
+bf16 intermediate feeds the GPU head; the oracle's fp32 logits feed both
+acceptance implementations).  End to end, the GPU chain must agree with the
+oracle chain except on rows whose top-2 logit gap is below the GEMM error
+bound (reported, not failed).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import DEV, assert_gemm_close, dev, gemm_gpu, host, log
+
+pytestmark = pytest.mark.gpu
+
+bv = pytest.importorskip("bit_verify_gemm_amd")
+
+
+def test_tiny_chained_verify_pass():
+    c = W.config0()
+    M, V = c["M"], c["V"]
+    # stage 1
+    y1, y1b = gemm_gpu(bv, c["w1"], c["x"], want_bf16=True)
+    y1_ref, b1 = oracle.gemm(c["w1"], c["x"])
+    assert_gemm_close(y1, y1_ref, b1, "C0 stage 1")
+    h_ref = np.array([[oracle.bf16_rne(v) for v in row] for row in y1_ref], np.uint16)
+    # stage 2 on the oracle's bf16 intermediate
+    z2 = gemm_gpu(bv, c["head"], h_ref)
+    z_ref, b2 = oracle.gemm(c["head"], h_ref)
+    assert_gemm_close(z2, z_ref, b2, "C0 head")
+    # stage 3 on the oracle's logits
+    z = z_ref.astype(np.float32)
+    t, cnt, rb = bv.accept_greedy(dev(z), dev(c["drafts"]), 123)
+    o = oracle.accept_greedy(z, c["drafts"], 123)
+    assert host(t).tolist() == o[0].tolist() and host(cnt).tolist() == o[1].tolist()
+    assert int(host(rb)[0]) == o[2]
+    # end to end on the GPU (bf16 intermediate written by the first GEMM)
+    xg = dev(c["x"])
+    yb = torch.empty((M, 2048), dtype=torch.int16, device=DEV)
+    bv.verify_gemm(W.FMT_NVFP4, xg, dev(c["w1"]["codes"]), dev(c["w1"]["scales"]), 2048, 2048,
+                   1.0, y_bf16=yb, want_fp32=False)
+    logits, _ = bv.verify_gemm(W.FMT_NVFP4, yb, dev(c["head"]["codes"]),
+                               dev(c["head"]["scales"]), V, 2048)
+    t, cnt, rb = bv.accept_greedy(logits, dev(c["drafts"]), 123)
+    gpu = (host(t).tolist(), host(cnt).tolist(), int(host(rb)[0]))
+    srt = np.sort(z_ref, axis=1)
+    gap = srt[:, -1] - srt[:, -2]
+    bound = 1e-3 * b2.max(axis=1) + 1e-5
+    if (gap > 2 * bound).all():
+        assert gpu == (o[0].tolist(), o[1].tolist(), o[2])
+    else:
+        log("C0 end to end: near-tie rows", np.flatnonzero(gap <= 2 * bound).tolist())

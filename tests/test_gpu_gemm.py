@@ -1,0 +1,182 @@
+"""GPU parity of mtp_verify_gemm against the fp64 oracle.
+
+Bar: |y_gpu - y_oracle| <= 1e-3 * sum_k |x*w| + 1e-5 per output, and bitwise
+equality where the exact result is representable and every fp32 partial sum
+is exact (one-hot readout, integer activations with power-of-two scales).
+Shapes span several tiles, several LDS chunks and K splits, ragged N and K
+tails, M = 1..16, and the full workload sizes (sampled columns).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_gemm_close, gemm_gpu, log
+
+pytestmark = pytest.mark.gpu
+
+bv = pytest.importorskip("bit_verify_gemm_amd")
+FMTS = [W.FMT_NVFP4, W.FMT_Q4_0]
+FNAME = {W.FMT_NVFP4: "nvfp4", W.FMT_Q4_0: "q4_0"}
+
+
+def weight(fmt, N, K, seed, g=1.0):
+    rng = np.random.default_rng(seed)
+    w = W.rand_weight(fmt, rng, rng, N, K)
+    w["g"] = g
+    return w
+
+
+def pack_nibbles(nib):
+    nib = nib.astype(np.uint8)
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("N,K", [(16, 32), (37, 96), (100, 256), (130, 1056), (70, 2080)])
+def test_small_shapes(fmt, M, N, K):
+    log("gemm small", FNAME[fmt], M, N, K)
+    w = weight(fmt, N, K, seed=M * 1000 + N + K, g=0.75)
+    x = W.rand_bf16(np.random.default_rng(N * K + M), (M, K))
+    y = gemm_gpu(bv, w, x)
+    y_ref, b_ref = oracle.gemm(w, x)
+    assert_gemm_close(y, y_ref, b_ref, f"{FNAME[fmt]} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_hot_readout_is_exact(fmt):
+    # x = e_k reads back weight (n, k) exactly: pins nibble order, scale
+    # indexing, the hardware E2M1/E4M3 decode (all finite E4M3 scale codes),
+    # the Q4_0 offset removal and the lane-group transpose.
+    N, K = 48, 1024
+    rng = np.random.default_rng(17)
+    nib = rng.integers(0, 16, size=(N, K))
+    if fmt == W.FMT_NVFP4:
+        codes_all = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+        sc = rng.choice(codes_all, size=(N, K // 16))
+        sc.reshape(-1)[:len(codes_all)] = codes_all
+    else:
+        sc = W.to_f16_bits(np.abs(rng.normal(0, 0.02, size=(N, K // 32))))
+        sc.reshape(-1)[:8] = [0x0001, 0x03FF, 0x0400, 0x7BFF, 0x8001, 0xFBFF, 0x3C00, 0x0000]
+    w = {"format": fmt, "N": N, "K": K, "codes": pack_nibbles(nib), "scales": sc, "g": 1.0}
+    for k0 in range(0, K, 16):
+        x = W.to_bf16_bits(np.eye(K, dtype=np.float32)[k0:k0 + 16])
+        y = gemm_gpu(bv, w, x)
+        y_ref, _ = oracle.gemm(w, x)
+        assert np.array_equal(y, y_ref), f"k0={k0}: first diff at {np.argwhere(y != y_ref)[0]}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", [(8, 96, 4096), (5, 333, 3104), (16, 64, 17408)])
+def test_exact_regime_bitwise(fmt, M, N, K):
+    log("gemm exact regime", FNAME[fmt], M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    x = W.to_bf16_bits(rng.integers(-4, 5, size=(M, K)).astype(np.float32))
+    nib = rng.integers(0, 16, size=(N, K))
+    if fmt == W.FMT_NVFP4:
+        sc = W.to_e4m3_bits(np.exp2(rng.integers(-1, 3, size=(N, K // 16))).astype(np.float32))
+    else:
+        sc = W.to_f16_bits(np.exp2(rng.integers(-3, 2, size=(N, K // 32))))
+    w = {"format": fmt, "N": N, "K": K, "codes": pack_nibbles(nib), "scales": sc, "g": 1.0}
+    y = gemm_gpu(bv, w, x)
+    y_ref, _ = oracle.gemm(w, x)
+    assert np.array_equal(y, y_ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rows_do_not_depend_on_m(fmt):
+    # the M-row pass equals M single-row passes, bit for bit
+    N, K = 300, 2304
+    w = weight(fmt, N, K, seed=5)
+    x = W.rand_bf16(np.random.default_rng(6), (16, K))
+    y16 = gemm_gpu(bv, w, x)
+    for M in (1, 2, 5, 8):
+        yM = gemm_gpu(bv, w, x[:M])
+        assert np.array_equal(yM, y16[:M]), M
+    for m in (0, 7, 15):
+        assert np.array_equal(gemm_gpu(bv, w, x[m:m + 1])[0], y16[m])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_strides_scale_and_bf16_output(fmt):
+    N, K, M = 250, 1536, 6
+    w = weight(fmt, N, K, seed=8, g=0.37)
+    x = W.rand_bf16(np.random.default_rng(9), (M, K))
+    y, yb = gemm_gpu(bv, w, x, ldx_pad=24, ldy_pad=7, want_bf16=True)
+    y_ref, b_ref = oracle.gemm(w, x)
+    assert_gemm_close(y, y_ref, b_ref, "strided")
+    # the bf16 copy is the nearest-even rounding of the fp32 result
+    expect = W.to_bf16_bits(y.astype(np.float32))
+    assert np.array_equal(yb, expect)
+
+
+def test_deterministic_across_calls():
+    N, K, M = 5120, 17408, 8          # split-K path
+    w = weight(W.FMT_Q4_0, N, K, seed=3)
+    x = W.rand_bf16(np.random.default_rng(3), (M, K))
+    y1 = gemm_gpu(bv, w, x)
+    y2 = gemm_gpu(bv, w, x)
+    assert np.array_equal(y1, y2)
+    y_ref, b_ref = oracle.gemm(w, x, cols=np.arange(0, N, 7))
+    assert_gemm_close(y1[:, ::7], y_ref, b_ref, "q4 down")
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, sampled columns
+# ---------------------------------------------------------------------------
+
+def sample_cols(N, n=1536, seed=0):
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([np.arange(min(N, 64)), np.arange(max(0, N - 64), N),
+                                     rng.integers(0, N, n)]))
+    return cols
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_ffn_up_4096x14336_nvfp4(M):
+    cfg = W.config1(M=8)
+    log("C1 M", M)
+    x = cfg["x"][:M]
+    y = gemm_gpu(bv, cfg["w"], x)
+    cols = sample_cols(cfg["w"]["N"], seed=M)
+    y_ref, b_ref = oracle.gemm(cfg["w"], x, cols=cols)
+    assert_gemm_close(y[:, cols], y_ref, b_ref, f"C1 M={M}")
+
+
+def test_dense_layer_q4_0_projections():
+    cfg = W.config2(M=8)
+    for name, p in cfg["proj"].items():
+        log("C2", name)
+        for M in (2, 8):
+            y = gemm_gpu(bv, p["w"], p["x"][:M])
+            cols = sample_cols(p["w"]["N"], n=512, seed=M)
+            y_ref, b_ref = oracle.gemm(p["w"], p["x"][:M], cols=cols)
+            assert_gemm_close(y[:, cols], y_ref, b_ref, f"C2 {name} M={M}")
+
+
+def test_dense_layer_fused_qkv_and_gate_up():
+    cfg = W.config2(M=8, shapes=(("q", 5120, 6144), ("k", 5120, 1024), ("v", 5120, 1024),
+                                  ("gate", 5120, 17408), ("up", 5120, 17408)))
+    p = cfg["proj"]
+    x = p["q"]["x"]
+    for names in (("q", "k", "v"), ("gate", "up")):
+        ws = [p[n]["w"] for n in names]
+        fused = {"format": W.FMT_Q4_0, "K": 5120, "N": sum(w["N"] for w in ws), "g": 1.0,
+                 "codes": np.concatenate([w["codes"] for w in ws]),
+                 "scales": np.concatenate([w["scales"] for w in ws])}
+        log("C2 fused", names, fused["N"])
+        y = gemm_gpu(bv, fused, x)
+        cols = sample_cols(fused["N"], n=1024, seed=1)
+        y_ref, b_ref = oracle.gemm(fused, x, cols=cols)
+        assert_gemm_close(y[:, cols], y_ref, b_ref, f"fused {names}")
+
+
+def test_lm_head_5376x262144_nvfp4():
+    c = W.config3_inputs()
+    log("C3 gemm")
+    y = gemm_gpu(bv, c["w"], c["x"])
+    cols = sample_cols(c["V"], n=2048, seed=3)
+    y_ref, b_ref = oracle.gemm(c["w"], c["x"], cols=cols)
+    assert_gemm_close(y[:, cols], y_ref, b_ref, "C3")
