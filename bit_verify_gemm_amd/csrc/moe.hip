@@ -28,6 +28,7 @@ using core::kThreads;
 using core::kWaves;
 
 constexpr int kMaxPairs = 1024;
+constexpr int kInvalidKey = 0x7FFFFFFF - kMaxPairs;  // above e * kMaxPairs + p for e < 2^20
 
 struct MoeLayout {
   size_t nuniq, uexp, ustart, ucount, spair, stok, h, y, bytes;
@@ -82,7 +83,8 @@ __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
   if (p < P) {
     e = a.ids[p];
     if (e < 0 || e >= a.E) e = -1;
-    key[p] = (e < 0) ? 0x7FFFFFFF : e * kMaxPairs + p;
+    // distinct keys: invalid pairs sort after every valid one, in pair order
+    key[p] = (e < 0) ? kInvalidKey + p : e * kMaxPairs + p;
   }
   __syncthreads();
   int rank = 0;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
   if (p < P) {
     const int pp = sorted[p];
     const int ke = key[pp];
-    const bool valid = ke != 0x7FFFFFFF;
+    const bool valid = ke < kInvalidKey;
     const bool first = valid && (p == 0 || key[sorted[p - 1]] / kMaxPairs != ke / kMaxPairs);
     start[p] = first ? 1 : 0;
     a.spair[p] = pp;
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
   if (p == 0) {
     int u = 0, prev = -1;
     for (int i = 0; i < P; ++i) {
-      if (key[sorted[i]] == 0x7FFFFFFF) break;
+      if (key[sorted[i]] >= kInvalidKey) break;
       if (start[i]) {
         if (prev >= 0) a.ucount[u - 1] = i - prev;
         a.uexp[u] = key[sorted[i]] / kMaxPairs;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
     }
     if (prev >= 0) {
       int end = prev;
-      while (end < P && key[sorted[end]] != 0x7FFFFFFF) ++end;
+      while (end < P && key[sorted[end]] < kInvalidKey) ++end;
       a.ucount[u - 1] = end - prev;
     }
     *a.nuniq = u;
@@ -125,6 +127,14 @@ __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
   // rows of h for invalid pairs are zero
   if (a.h_out && p < P && e < 0)
     for (int f = 0; f < a.F; ++f) a.h_out[(int64_t)p * a.F + f] = 0;
+}
+
+// silu(v) = v / (1 + exp(-v)), written so that no intermediate overflows:
+// for v < 0 it is v * e / (1 + e) with e = exp(v) (gradual underflow).
+__device__ __forceinline__ float silu(float v) {
+  if (v >= 0.0f) return v / (1.0f + expf(-v));
+  const float e = expf(v);
+  return v * e / (1.0f + e);
 }
 
 template <int FMT>
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up(MoeArgs a) {
         const int m = 4 * g + i;
         if (m < mc) {
           const float gate = gsc * gv[i], up = gsc * uv[i];
-          const float act = gate / (1.0f + __expf(-gate));
+          const float act = silu(gate);
           const uint16_t hb = f32_to_bf16_rne(act * up);
           const int pair = a.spair[first + c0 + m];
           a.h[(int64_t)pair * F + f] = hb;

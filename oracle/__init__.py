@@ -68,7 +68,7 @@ def _load():
         lib.orc_gemm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, i64,
                                  P, P, f32, P, i64, P, P, ctypes.c_int]
         lib.orc_moe.restype = ctypes.c_int
-        lib.orc_moe.argtypes = [ctypes.c_int] * 6 + [P] * 9 + [P, P, P, ctypes.c_int]
+        lib.orc_moe.argtypes = [ctypes.c_int] * 6 + [P] * 9 + [P, P, P, P, P, ctypes.c_int]
         lib.orc_argmax.restype = i32
         lib.orc_argmax.argtypes = [P, ctypes.c_int]
         lib.orc_accept_greedy.restype = ctypes.c_int
@@ -154,8 +154,10 @@ def gemm(w: dict, x: np.ndarray, cols=None, with_bound: bool = True, nthreads=No
 # MoE
 # ---------------------------------------------------------------------------
 
-def moe(cfg: dict, nthreads=None):
-    """Returns (out[T][H], outb[T][H], h[T*topk][F] bf16 bits)."""
+def moe(cfg: dict, nthreads=None, with_preact: bool = False):
+    """Returns (out[T][H], outb[T][H], h[T*topk][F] bf16 bits), plus the
+    gate/up pre-activations a[T*topk][2F] and their error scale ab (sum of
+    |x*w|) when with_preact is set."""
     lib = _load()
     T, H, F, E, topk = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["topk"]
     gu, dn = cfg["gate_up"], cfg["down"]
@@ -169,11 +171,16 @@ def moe(cfg: dict, nthreads=None):
     out = np.zeros((T, H), np.float64)
     outb = np.zeros((T, H), np.float64)
     h = np.zeros((T * topk, F), np.uint16)
+    a = np.zeros((T * topk, 2 * F), np.float64) if with_preact else None
+    ab = np.zeros((T * topk, 2 * F), np.float64) if with_preact else None
     rc = lib.orc_moe(gu["format"], T, H, F, E, topk, _ptr(x), _ptr(ids), _ptr(gw),
                      _ptr(arrs[0]), _ptr(arrs[1]), _ptr(gug), _ptr(arrs[2]), _ptr(arrs[3]),
-                     _ptr(dng), _ptr(out), _ptr(outb), _ptr(h), _threads(nthreads))
+                     _ptr(dng), _ptr(out), _ptr(outb), _ptr(h), _ptr(a), _ptr(ab),
+                     _threads(nthreads))
     if rc != 0:
         raise ValueError("orc_moe rejected its arguments")
+    if with_preact:
+        return out, outb, h, a, ab
     return out, outb, h
 
 

@@ -236,6 +236,7 @@ typedef struct {
     const float *gu_g, *dn_g;
     double *y, *yb;              /* [T*topk][H] */
     uint16_t *h;                 /* [T*topk][F] */
+    double *a_out, *ab_out;      /* [T*topk][2F] pre-activations and their error scale, or NULL */
     int64_t begin, end;
 } moe_job;
 
@@ -251,6 +252,10 @@ static void *moe_worker(void *arg) {
         double *yrow = j->y + p * H, *ybrow = j->yb + p * H;
         if (e < 0 || e >= j->E) {
             for (int f = 0; f < F; ++f) hrow[f] = 0;
+            for (int n = 0; n < 2 * F; ++n) {
+                if (j->a_out) j->a_out[p * 2 * F + n] = 0.0;
+                if (j->ab_out) j->ab_out[p * 2 * F + n] = 0.0;
+            }
             for (int n = 0; n < H; ++n) yrow[n] = 0.0, ybrow[n] = 0.0;
             continue;
         }
@@ -267,10 +272,15 @@ static void *moe_worker(void *arg) {
         double ggu = j->gu_g ? (double)j->gu_g[e] : 1.0;
         double gdn = j->dn_g ? (double)j->dn_g[e] : 1.0;
         for (int n = 0; n < 2 * F; ++n) {
-            double acc = 0.0;
-            for (int k = 0; k < H; ++k)
-                acc += j->xd[t * H + k] * weight_nk(j->fmt, H, gc, gs, ggu, n, k);
+            double acc = 0.0, mag = 0.0;
+            for (int k = 0; k < H; ++k) {
+                double pr = j->xd[t * H + k] * weight_nk(j->fmt, H, gc, gs, ggu, n, k);
+                acc += pr;
+                mag += fabs(pr);
+            }
             a[n] = acc;
+            if (j->a_out) j->a_out[p * 2 * F + n] = acc;
+            if (j->ab_out) j->ab_out[p * 2 * F + n] = mag;
         }
         for (int f = 0; f < F; ++f) {
             double gate = a[f], up = a[F + f];
@@ -299,12 +309,14 @@ static void *moe_worker(void *arg) {
  * gate/up codes [E][2F][H/2], scales [E][2F][H/bs]; down codes [E][H][F/2],
  * scales [E][H][F/bs].  gu_g, dn_g: per-expert global scales or NULL (1.0).
  * Outputs: out [T][H] and outb [T][H] = sum_s |w| * sum_f |h * w_d| (error
- * scale), h [T*topk][F] bf16 bits.  Returns 0 or -1.
+ * scale), h [T*topk][F] bf16 bits, and optionally the gate/up
+ * pre-activations a_out [T*topk][2F] with their error scale ab_out
+ * (sum_k |x * w|).  Returns 0 or -1.
  */
 int orc_moe(int fmt, int T, int H, int F, int E, int topk, const uint16_t *x, const int32_t *ids,
             const float *gw, const uint8_t *gu_codes, const void *gu_scales, const float *gu_g,
             const uint8_t *dn_codes, const void *dn_scales, const float *dn_g, double *out,
-            double *outb, uint16_t *h, int nthreads) {
+            double *outb, uint16_t *h, double *a_out, double *ab_out, int nthreads) {
     if (T < 1 || topk < 1 || E < 1 || H < 32 || H % 32 || F < 32 || F % 32 ||
         (fmt != ORC_NVFP4 && fmt != ORC_Q4_0))
         return -1;
@@ -325,7 +337,7 @@ int orc_moe(int fmt, int T, int H, int F, int E, int topk, const uint16_t *x, co
         j->fmt = fmt; j->T = T; j->H = H; j->F = F; j->E = E; j->topk = topk; j->xd = xd;
         j->ids = ids; j->gw = gw; j->gu_codes = gu_codes; j->dn_codes = dn_codes;
         j->gu_scales = gu_scales; j->dn_scales = dn_scales; j->gu_g = gu_g; j->dn_g = dn_g;
-        j->y = y; j->yb = yb; j->h = h;
+        j->y = y; j->yb = yb; j->h = h; j->a_out = a_out; j->ab_out = ab_out;
         j->begin = P * t / nthreads;
         j->end = P * (t + 1) / nthreads;
     }

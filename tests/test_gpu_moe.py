@@ -1,8 +1,11 @@
 """GPU parity of mtp_verify_moe against the oracle.
 
 Bar: out within 1e-3 * B + 1e-5 per element, B = sum_s |w| * sum_f |h * w_d|
-(the oracle's error scale); the bf16 intermediate h within one bf16 step of
-the oracle's (its rounding decision sees fp32 vs fp64 pre-activations).
+(the oracle's error scale).  The bf16 intermediate h = bf16(silu(g) * u) is
+checked against the oracle's within the GEMM tolerance of its inputs carried
+through the activation: with dg = 1e-3 * B_g + 1e-5 (likewise du) and
+|silu'| <= 1.1, |dh| <= 1.1 dg (|u| + du) + (|silu(g)| + 1.1 dg) du, plus one
+bf16 rounding step and 2^-126 (values below the fp32 normal range).
 """
 import numpy as np
 import pytest
@@ -30,21 +33,35 @@ def run_moe(cfg):
     return host(out).astype(np.float64), host(h).view(np.uint16)
 
 
-def bf16_steps_apart(a, b):
-    """Distance in representable bf16 steps (same-sign finite values)."""
-    ai = a.astype(np.int32)
-    bi = b.astype(np.int32)
-    ai = np.where(ai & 0x8000, 0x8000 - ai, ai)
-    bi = np.where(bi & 0x8000, 0x8000 - bi, bi)
-    return np.abs(ai - bi)
+def bf16_value(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def silu(v):
+    e = np.exp(-np.abs(v))
+    return np.where(v >= 0, v / (1 + e), v * e / (1 + e))
+
+
+def h_allowed(a, ab, F, h_or):
+    g, u = a[:, :F], a[:, F:]
+    dg = 1e-3 * ab[:, :F] + 1e-5
+    du = 1e-3 * ab[:, F:] + 1e-5
+    prop = 1.1 * dg * (np.abs(u) + du) + (np.abs(silu(g)) + 1.1 * dg) * du
+    mag = np.abs(h_or) + prop
+    step = np.exp2(np.floor(np.log2(np.maximum(mag, 2.0 ** -133))) - 7)
+    return prop + step + 2.0 ** -126
 
 
 def check(cfg, what):
     out, h = run_moe(cfg)
-    o_out, o_b, o_h = oracle.moe(cfg)
-    steps = bf16_steps_apart(h, o_h)
-    assert steps.max() <= 1, f"{what}: h differs by {steps.max()} bf16 steps"
-    log(what, "h mismatches:", int((steps > 0).sum()), "of", steps.size)
+    o_out, o_b, o_h, a, ab = oracle.moe(cfg, with_preact=True)
+    hv, ov = bf16_value(h), bf16_value(o_h)
+    diff = np.abs(hv - ov)
+    allowed = h_allowed(a, ab, cfg["F"], ov)
+    bad = ~(diff <= allowed)
+    assert not bad.any(), (f"{what}: h outside bound at {np.argwhere(bad)[:4].tolist()}: "
+                           f"gpu {hv[bad][:4]} oracle {ov[bad][:4]}")
+    log(what, "h entries differing:", int((h != o_h).sum()), "of", h.size)
     assert_gemm_close(out, o_out, o_b, what)
 
 
