@@ -62,17 +62,17 @@ class GemmRunner:
         self.R = max(2, -(-ROTATE_BYTES // self.bytes_per_call))
         codes = torch.from_numpy(w["codes"]).to(dev)
         scales = torch.from_numpy(w["scales"]).to(dev)
-        self.codes = [codes] + [codes.clone() for _ in range(self.R - 1)]
-        self.scales = [scales] + [scales.clone() for _ in range(self.R - 1)]
+        packed = bv.pack_weights(bv.FMT_NVFP4, codes, scales, self.N, self.K)
+        del codes, scales
+        self.packed = [packed] + [packed.clone() for _ in range(self.R - 1)]
         self.x = torch.from_numpy(np.ascontiguousarray(x[:M]).view(np.int16)).to(dev)
         self.y = torch.empty((M, self.N), dtype=torch.float32, device=dev)
-        wsb = bv.gemm_workspace_bytes(M, self.N, self.K)
-        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        self.ws = bv.gemm_workspace(self.N, self.K, dev)
         self.graphs = {}
 
     def call(self, i):
-        self.bv.verify_gemm(self.bv.FMT_NVFP4, self.x, self.codes[i % self.R],
-                            self.scales[i % self.R], self.N, self.K, 1.0, y=self.y, ws=self.ws)
+        self.bv.verify_gemm(self.bv.FMT_NVFP4, self.x, self.packed[i % self.R], self.N, self.K,
+                            1.0, y=self.y, ws=self.ws)
 
     def graph(self, n):
         """A graph of n consecutive calls over the rotating copies."""

@@ -15,7 +15,9 @@ import torch
 
 __all__ = [
     "FMT_NVFP4", "FMT_Q4_0", "MAX_M", "MtpError", "lib", "abi_version",
-    "gemm_workspace_bytes", "moe_workspace_bytes", "accept_workspace_bytes",
+    "packed_weight_bytes", "pack_weights", "gemm_workspace_bytes", "gemm_workspace",
+    "gemm_plan_info",
+    "moe_workspace_bytes", "accept_workspace_bytes",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -51,14 +53,20 @@ def lib() -> ctypes.CDLL:
         L.mtp_abi_version.argtypes = []
         L.mtp_last_error.restype = ctypes.c_char_p
         L.mtp_last_error.argtypes = []
+        L.mtp_packed_weight_bytes.restype = sz
+        L.mtp_packed_weight_bytes.argtypes = [i32, i32]
+        L.mtp_pack_weights.restype = i32
+        L.mtp_pack_weights.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.mtp_gemm_plan_info.restype = i32
+        L.mtp_gemm_plan_info.argtypes = [i32, i32, i32, i32, P, i32]
         L.mtp_gemm_workspace_bytes.restype = sz
-        L.mtp_gemm_workspace_bytes.argtypes = [i32, i32, i32]
+        L.mtp_gemm_workspace_bytes.argtypes = [i32, i32]
         L.mtp_verify_gemm.restype = i32
-        L.mtp_verify_gemm.argtypes = [i32, i32, i32, i32, P, i64, P, P, f32, P, i64, P, i64, P, sz, P]
+        L.mtp_verify_gemm.argtypes = [i32, i32, i32, i32, P, i64, P, f32, P, i64, P, i64, P, sz, P]
         L.mtp_moe_workspace_bytes.restype = sz
         L.mtp_moe_workspace_bytes.argtypes = [i32] * 5
         L.mtp_verify_moe.restype = i32
-        L.mtp_verify_moe.argtypes = [i32] * 6 + [P] * 3 + [P, P, P, P, P, P] + [P, P, P, sz, P]
+        L.mtp_verify_moe.argtypes = [i32] * 6 + [P] * 3 + [P, P, P, P] + [P, P, P, sz, P]
         L.mtp_accept_workspace_bytes.restype = sz
         L.mtp_accept_workspace_bytes.argtypes = [i32, i32]
         L.mtp_accept_greedy.restype = i32
@@ -97,8 +105,43 @@ def _ld(t):
     return int(t.stride(0)) if t is not None and t.dim() >= 2 else 0
 
 
-def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
-    return int(lib().mtp_gemm_workspace_bytes(M, N, K))
+def packed_weight_bytes(N: int, K: int) -> int:
+    return int(lib().mtp_packed_weight_bytes(N, K))
+
+
+def pack_weights(fmt: int, codes: torch.Tensor, scales: torch.Tensor, N: int, K: int,
+                 count: int = 1, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Repack `count` stacked source matrices (codes [count*N][K/2] uint8,
+    scales [count*N][K/bs]) into the packed layout the GEMM reads."""
+    nb = packed_weight_bytes(N, K) * count
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    _check(lib().mtp_pack_weights(fmt, count, N, K, _ptr(codes), _ptr(scales), _ptr(out),
+                                  _stream(stream)))
+    return out
+
+
+def gemm_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().mtp_gemm_workspace_bytes(N, K))
+
+
+PLAN_FIELDS = ("T", "P", "S", "ppj", "J", "KG", "TW", "TG", "G", "grid", "threads", "lds",
+               "ws_bytes")
+
+
+def gemm_plan_info(fmt: int, M: int, N: int, K: int) -> dict:
+    """The launch shape mtp_verify_gemm uses (diagnostic; enqueues nothing)."""
+    info = (ctypes.c_int32 * len(PLAN_FIELDS))()
+    _check(lib().mtp_gemm_plan_info(fmt, M, N, K, ctypes.cast(info, ctypes.c_void_p),
+                                    len(PLAN_FIELDS)))
+    return dict(zip(PLAN_FIELDS, list(info)))
+
+
+def gemm_workspace(N: int, K: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace for mtp_verify_gemm on N x K (None if not needed).
+    Keep it for later calls: the library leaves it zero after every call."""
+    nb = gemm_workspace_bytes(N, K)
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb else None
 
 
 def moe_workspace_bytes(T: int, H: int, F: int, E: int, topk: int) -> int:
@@ -117,38 +160,39 @@ def _workspace(nbytes: int, device, ws):
     return ws
 
 
-def verify_gemm(fmt: int, x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, N: int,
-                K: int, global_scale: float = 1.0, y: torch.Tensor | None = None,
+def verify_gemm(fmt: int, x: torch.Tensor, packed: torch.Tensor, N: int, K: int,
+                global_scale: float = 1.0, y: torch.Tensor | None = None,
                 y_bf16: torch.Tensor | None = None, ws: torch.Tensor | None = None,
                 want_fp32: bool = True, stream=None):
     """y[M][N] = x[M][K] . W.  x: bf16 (or its uint16/int16 bits) [M][>=K] on
-    the GPU.  Returns (y, y_bf16); allocates the outputs it is not given."""
+    the GPU; packed: from pack_weights.  Returns (y, y_bf16); allocates the
+    outputs it is not given.  ws must come from gemm_workspace (zero-filled)."""
     M = x.shape[0]
     dev = x.device
     if y is None and want_fp32:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    wsb = gemm_workspace_bytes(M, N, K)
-    ws = _workspace(wsb, dev, ws)
-    _check(lib().mtp_verify_gemm(fmt, M, N, K, _ptr(x), _ld(x), _ptr(codes), _ptr(scales),
+    if ws is None and gemm_workspace_bytes(N, K):
+        ws = gemm_workspace(N, K, dev)
+    _check(lib().mtp_verify_gemm(fmt, M, N, K, _ptr(x), _ld(x), _ptr(packed),
                                  float(global_scale), _ptr(y), _ld(y), _ptr(y_bf16), _ld(y_bf16),
                                  _ptr(ws), _nbytes(ws), _stream(stream)))
     return y, y_bf16
 
 
 def verify_moe(fmt: int, x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
-               gu_codes: torch.Tensor, gu_scales: torch.Tensor, dn_codes: torch.Tensor,
-               dn_scales: torch.Tensor, E: int, F: int, gu_global=None, dn_global=None,
-               out: torch.Tensor | None = None, h_out: torch.Tensor | None = None,
-               ws: torch.Tensor | None = None, stream=None):
-    """Routed MoE verify pass; returns out [T][H] fp32 (and h_out if given)."""
+               gu_packed: torch.Tensor, dn_packed: torch.Tensor, E: int, F: int,
+               gu_global=None, dn_global=None, out: torch.Tensor | None = None,
+               h_out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """Routed MoE verify pass over packed experts (pack_weights with count=E);
+    returns out [T][H] fp32 (and h_out if given)."""
     T, H = x.shape
     topk = topk_ids.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=x.device)
     ws = _workspace(moe_workspace_bytes(T, H, F, E, topk), x.device, ws)
     _check(lib().mtp_verify_moe(fmt, T, H, F, E, topk, _ptr(x), _ptr(topk_ids), _ptr(topk_w),
-                                _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_global), _ptr(dn_codes),
-                                _ptr(dn_scales), _ptr(dn_global), _ptr(out), _ptr(h_out),
+                                _ptr(gu_packed), _ptr(gu_global), _ptr(dn_packed),
+                                _ptr(dn_global), _ptr(out), _ptr(h_out),
                                 _ptr(ws), _nbytes(ws), _stream(stream)))
     return out, h_out
 

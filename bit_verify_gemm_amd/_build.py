@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "gemm.hip", "accept.hip", "moe.hip"]
-HEADERS = ["device.h", "gemm_core.h", "internal.h"]
+HEADERS = ["device.h", "engine.h", "internal.h"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

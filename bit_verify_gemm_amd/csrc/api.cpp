@@ -37,13 +37,17 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool valid_format(int f) { return f == MTP_FMT_NVFP4 || f == MTP_FMT_Q4_0; }
 
 // Checks shared by the dense GEMM and the MoE weight sets.
-int check_weights(const char *who, int format, int K, const void *codes, const void *scales) {
+int check_packed(const char *who, int format, int K, const void *packed) {
   if (!valid_format(format)) return fail(MTP_ERR_FORMAT, "%s: unknown weight format %d", who, format);
   if (K < 32 || K % 32) return fail(MTP_ERR_SHAPE, "%s: K=%d must be a positive multiple of 32", who, K);
-  if (!codes || !scales) return fail(MTP_ERR_NULL, "%s: codes and scales are required", who);
-  if (!aligned(codes, 16) || !aligned(scales, 16))
-    return fail(MTP_ERR_ALIGN, "%s: codes and scales must be 16-byte aligned", who);
+  if (!packed) return fail(MTP_ERR_NULL, "%s: packed weights are required", who);
+  if (!aligned(packed, 16)) return fail(MTP_ERR_ALIGN, "%s: packed weights must be 16-byte aligned", who);
   return MTP_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
 }
 
 constexpr int kMaxAcceptRows = 64;
@@ -75,17 +79,42 @@ int mtp_abi_version(void) { return MTP_ABI_VERSION; }
 
 const char *mtp_last_error(void) { return g_error.c_str(); }
 
-size_t mtp_gemm_workspace_bytes(int M, int N, int K) {
-  if (M < 1 || M > MTP_MAX_M || N < 1 || K < 32 || K % 32) return 0;
-  return mtp::gemm_plan(M, N, K).ws_bytes;
+size_t mtp_packed_weight_bytes(int N, int K) {
+  if (N < 1 || K < 32 || K % 32) return 0;
+  return mtp::packed_weight_bytes(N, K);
+}
+
+int mtp_pack_weights(int format, int count, int N, int K, const uint8_t *codes,
+                     const void *scales, uint8_t *packed, void *stream) {
+  const char *who = "mtp_pack_weights";
+  if (!valid_format(format)) return fail(MTP_ERR_FORMAT, "%s: unknown weight format %d", who, format);
+  if (K < 32 || K % 32) return fail(MTP_ERR_SHAPE, "%s: K=%d must be a positive multiple of 32", who, K);
+  if (N < 1 || count < 1) return fail(MTP_ERR_SHAPE, "%s: N=%d and count=%d must be positive", who, N, count);
+  const int64_t blocks = (int64_t)count * ((N + 15) / 16) * ((K + 255) / 256);
+  if (blocks > INT32_MAX) return fail(MTP_ERR_SHAPE, "%s: %lld blocks exceed one launch", who, (long long)blocks);
+  if (!codes || !scales || !packed) return fail(MTP_ERR_NULL, "%s: codes, scales and packed are required", who);
+  if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(packed, 16))
+    return fail(MTP_ERR_ALIGN, "%s: codes, scales and packed must be 16-byte aligned", who);
+  const size_t cb = (size_t)count * N * (K / 2);
+  const size_t sb = (size_t)count * N * (format == MTP_FMT_NVFP4 ? K / 16 : (K / 32) * 2);
+  const size_t pb = (size_t)count * mtp::packed_weight_bytes(N, K);
+  if (overlaps(packed, pb, codes, cb) || overlaps(packed, pb, scales, sb))
+    return fail(MTP_ERR_SHAPE, "%s: packed output overlaps the source", who);
+  return hip_status(mtp::launch_pack(format, count, N, K, codes, scales, packed,
+                                     static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+size_t mtp_gemm_workspace_bytes(int N, int K) {
+  if (N < 1 || K < 32 || K % 32) return 0;
+  return mtp::gemm_ws_bytes(N, K);
 }
 
 int mtp_verify_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t ldx,
-                    const uint8_t *codes, const void *scales, float global_scale, float *y,
-                    int64_t ldy, uint16_t *y_bf16, int64_t ldyb, void *ws, size_t ws_bytes,
-                    void *stream) {
+                    const uint8_t *packed, float global_scale, float *y, int64_t ldy,
+                    uint16_t *y_bf16, int64_t ldyb, void *ws, size_t ws_bytes, void *stream) {
   const char *who = "mtp_verify_gemm";
-  if (int rc = check_weights(who, format, K, codes, scales)) return rc;
+  if (int rc = check_packed(who, format, K, packed)) return rc;
   if (M < 1 || M > MTP_MAX_M) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, %d]", who, M, MTP_MAX_M);
   if (N < 1) return fail(MTP_ERR_SHAPE, "%s: N=%d must be positive", who, N);
   if (!x) return fail(MTP_ERR_NULL, "%s: x is required", who);
@@ -96,14 +125,29 @@ int mtp_verify_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t 
   if (y_bf16 && ldyb < N) return fail(MTP_ERR_SHAPE, "%s: ldyb=%lld < N=%d", who, (long long)ldyb, N);
   if (y && !aligned(y, 4)) return fail(MTP_ERR_ALIGN, "%s: y must be 4-byte aligned", who);
   if (y_bf16 && !aligned(y_bf16, 2)) return fail(MTP_ERR_ALIGN, "%s: y_bf16 must be 2-byte aligned", who);
-  const mtp::GemmPlan plan = mtp::gemm_plan(M, N, K);
+  const mtp::GemmPlan plan = mtp::gemm_plan(format, M, N, K);
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who,
                 plan.ws_bytes, ws ? ws_bytes : (size_t)0);
-  if (plan.ws_bytes && !aligned(ws, 16)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
-  return hip_status(mtp::launch_gemm(format, M, N, K, x, ldx, codes, scales, global_scale, y, ldy,
-                                     y_bf16, ldyb, ws, plan, static_cast<hipStream_t>(stream)),
+  if (plan.ws_bytes && !aligned(ws, 256)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+  return hip_status(mtp::launch_gemm(format, M, N, K, x, ldx, packed, global_scale, y, ldy,
+                                     y_bf16, ldyb, plan.ws_bytes ? ws : nullptr, plan,
+                                     static_cast<hipStream_t>(stream)),
                     who);
+}
+
+int mtp_gemm_plan_info(int format, int M, int N, int K, int32_t *info, int n) {
+  const char *who = "mtp_gemm_plan_info";
+  if (!valid_format(format)) return fail(MTP_ERR_FORMAT, "%s: unknown weight format %d", who, format);
+  if (M < 1 || M > MTP_MAX_M || N < 1 || K < 32 || K % 32)
+    return fail(MTP_ERR_SHAPE, "%s: bad shape M=%d N=%d K=%d", who, M, N, K);
+  if (!info || n < 1) return fail(MTP_ERR_NULL, "%s: info is required", who);
+  const mtp::GemmPlan p = mtp::gemm_plan(format, M, N, K);
+  const int32_t v[13] = {p.T, p.P, p.S, p.ppj, p.J, p.KG, p.TW, p.TG, p.G, p.grid, p.threads,
+                         (int32_t)p.lds, (int32_t)p.ws_bytes};
+  for (int i = 0; i < n && i < 13; ++i) info[i] = v[i];
+  g_error.clear();
+  return MTP_OK;
 }
 
 size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk) {
@@ -113,27 +157,28 @@ size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk) {
 }
 
 int mtp_verify_moe(int format, int T, int H, int F, int E, int topk, const uint16_t *x,
-                   const int32_t *topk_ids, const float *topk_w, const uint8_t *gu_codes,
-                   const void *gu_scales, const float *gu_global, const uint8_t *dn_codes,
-                   const void *dn_scales, const float *dn_global, float *out, uint16_t *h_out,
-                   void *ws, size_t ws_bytes, void *stream) {
+                   const int32_t *topk_ids, const float *topk_w, const uint8_t *gu_packed,
+                   const float *gu_global, const uint8_t *dn_packed, const float *dn_global,
+                   float *out, uint16_t *h_out, void *ws, size_t ws_bytes, void *stream) {
   const char *who = "mtp_verify_moe";
   if (!valid_format(format)) return fail(MTP_ERR_FORMAT, "%s: unknown weight format %d", who, format);
   if (T < 1 || topk < 1 || (int64_t)T * topk > 1024)
     return fail(MTP_ERR_SHAPE, "%s: need T >= 1, topk >= 1, T*topk <= 1024 (T=%d, topk=%d)", who, T, topk);
   if (E < 1 || E > (1 << 20)) return fail(MTP_ERR_SHAPE, "%s: E=%d out of [1, 2^20]", who, E);
-  if (int rc = check_weights(who, format, H, gu_codes, gu_scales)) return rc;
-  if (int rc = check_weights(who, format, F, dn_codes, dn_scales)) return rc;
+  if (int rc = check_packed(who, format, H, gu_packed)) return rc;
+  if (int rc = check_packed(who, format, F, dn_packed)) return rc;
   if (!x || !topk_ids || !topk_w || !out) return fail(MTP_ERR_NULL, "%s: x, ids, weights and out are required", who);
   if (!aligned(x, 16)) return fail(MTP_ERR_ALIGN, "%s: x must be 16-byte aligned", who);
+  if (!mtp::moe_fits(format, T, H, F))
+    return fail(MTP_ERR_SHAPE, "%s: H=%d, F=%d too large for one expert pass", who, H, F);
   const size_t need = mtp::moe_ws_bytes(T, H, F, E, topk);
   if (!ws || ws_bytes < need)
     return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need,
                 ws ? ws_bytes : (size_t)0);
   if (!aligned(ws, 256)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
-  return hip_status(mtp::launch_moe(format, T, H, F, E, topk, x, topk_ids, topk_w, gu_codes,
-                                    gu_scales, gu_global, dn_codes, dn_scales, dn_global, out,
-                                    h_out, ws, static_cast<hipStream_t>(stream)),
+  return hip_status(mtp::launch_moe(format, T, H, F, E, topk, x, topk_ids, topk_w, gu_packed,
+                                    gu_global, dn_packed, dn_global, out, h_out, ws,
+                                    static_cast<hipStream_t>(stream)),
                     who);
 }
 

@@ -1,0 +1,405 @@
+// The streaming engine of the verify GEMM (gfx950, wave64), shared by the
+// dense and the MoE kernels.
+//
+// Weights are read in the packed layout produced by mtp_pack_weights (see
+// mtp_verify.h): one 2304-byte block per (16-row tile, 256-wide K pair)
+// holds the codes of two 128-wide K steps (64 lanes x 16 B each) followed by
+// all of their block scales.  Every load a wave issues is 1 KiB (codes) or
+// 256 B (scales) of contiguous memory, and one tile's K range is one
+// contiguous run of blocks.
+//
+// Work split.  The K range of a matrix is cut into S slices of ppj pairs; the
+// slices, and the order in which their partial sums are added (slice 0 first),
+// depend only on the matrix shape, never on the row count, so a row's result
+// does not depend on which other rows share the pass.  A workgroup has
+// TW x J waves: TW tiles, each with J consecutive slices (one per wave); KG
+// workgroups cover the S slices of a tile group.  A workgroup stages the
+// activation rows of its K range in LDS once (the x loads are issued before
+// the weight prefetch so they return first), then every wave streams its
+// (tile, slice) blocks with kPP blocks of loads in flight, decodes each
+// weight once and feeds the matrix cores for all rows at once.  A workgroup
+// may process several tile groups in turn; its load stream runs on across
+// tile-group boundaries.  The J slices of a tile meet in LDS; with KG > 1 the
+// slice partials go to the workspace and the last workgroup of the tile group
+// to arrive adds all S of them in slice order.
+#pragma once
+
+#include "../../include/mtp_verify.h"
+#include "device.h"
+
+namespace mtp {
+namespace eng {
+
+constexpr int kPairK = 256;
+constexpr int kPairBytes = 2304;
+constexpr int kHalfBytes = 1024;
+constexpr int kScaleOff = 2048;
+constexpr int kSlotBytes = 512;   // one pair of one activation row in LDS (256 bf16)
+constexpr int kPP = 2;            // blocks in flight per wave
+constexpr int kMaxWaves = 16;
+constexpr int kMaxThreads = kMaxWaves * kWave;
+constexpr int kXU = 8;            // activation vectors per thread in the first staging round
+constexpr int kMaxLds = 160 * 1024;
+
+__host__ __device__ inline int tiles_of(int N) { return (N + 15) / 16; }
+__host__ __device__ inline int pairs_of(int K) { return (K + kPairK - 1) / kPairK; }
+__host__ __device__ inline size_t packed_bytes(int N, int K) {
+  return (size_t)tiles_of(N) * pairs_of(K) * kPairBytes;
+}
+
+// LDS layout of a workgroup: M staged rows of np pairs plus a zero slot each,
+// the Q4_0 accumulator starts, and one wave-sized slot per wave for the slice
+// partials (the first TW slots then hold the summed tiles).
+__host__ __device__ inline int row_bytes(int np) { return (np + 1) * kSlotBytes + 16; }
+__host__ __device__ inline int cinit_floats(int format, int np) {
+  return format == MTP_FMT_Q4_0 ? (np + 1) * 8 * 16 : 0;
+}
+__host__ __device__ inline size_t lds_bytes(int format, int M, int np, int TW, int J) {
+  return (size_t)M * row_bytes(np) + (size_t)cinit_floats(format, np) * 4 +
+         (size_t)(TW * J) * kWave * 16;
+}
+
+// Lets `kernel` use more than 64 KiB of dynamic LDS (once per kernel).
+template <typename Kernel>
+inline void allow_large_lds(Kernel *kernel) {
+  static const bool done = [kernel] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 64);
+    (void)hipGetLastError();   // a refusal shows up as the launch's own error
+    return true;
+  }();
+  (void)done;
+}
+
+// Activation rows: row m is base + idx[m] * ld (idx == nullptr: m).
+struct XSource {
+  const uint16_t *base;
+  int64_t ld;
+  const int32_t *idx;
+  __device__ __forceinline__ const uint16_t *row(int m) const {
+    return base + (int64_t)(idx ? idx[m] : m) * ld;
+  }
+};
+
+// How one workgroup walks the matrix.
+struct Plan {
+  int TW, J;       // tiles per workgroup, slices per tile in the workgroup
+  int S, ppj;      // slices of the K range and pairs per slice
+  int KG, kg;      // workgroups per tile group and this one's K group
+  int tg_first, tg_step, tg_count;  // tile groups of this workgroup
+};
+
+// Cross-workgroup partial sums (KG > 1): part[(tile * S + slice) * 64 + lane]
+// and one arrival counter per tile group, zero between calls.
+struct Fixup {
+  f32x4 *part;
+  uint32_t *cnt;
+};
+
+// One wave's share of one block: 2 x 16 code bytes + the scales.
+template <int FMT> struct Blk;
+template <> struct Blk<MTP_FMT_NVFP4> {
+  u32x4 c0, c1;
+  uint32_t s;   // E4M3 bytes: step 0 (k0, k0+16), step 1 (k1, k1+16)
+};
+template <> struct Blk<MTP_FMT_Q4_0> {
+  u32x4 c0, c1;
+  u32x4 s;      // the 8 fp16 scales of the lane's row for this pair
+};
+
+__device__ __forceinline__ void load_blk(Blk<MTP_FMT_NVFP4> &b, const uint8_t *p, int lane) {
+  b.c0 = *reinterpret_cast<const u32x4 *>(p + 16 * lane);
+  b.c1 = *reinterpret_cast<const u32x4 *>(p + kHalfBytes + 16 * lane);
+  b.s = *reinterpret_cast<const uint32_t *>(p + kScaleOff + 4 * lane);
+}
+
+__device__ __forceinline__ void load_blk(Blk<MTP_FMT_Q4_0> &b, const uint8_t *p, int lane) {
+  b.c0 = *reinterpret_cast<const u32x4 *>(p + 16 * lane);
+  b.c1 = *reinterpret_cast<const u32x4 *>(p + kHalfBytes + 16 * lane);
+  b.s = *reinterpret_cast<const u32x4 *>(p + kScaleOff + 16 * (lane & 15));
+}
+
+__device__ __forceinline__ float half_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// nvfp4.  Lane (r, g) holds, for step h, the codes of k = 128h + 32g .. +31
+// of its row; code dword j meets the activation slots 128h + 32g + 8j .. +7,
+// which the same lane supplies for activation row r in MFMA j of the step.
+__device__ __forceinline__ f32x4 compute_blk(f32x4 acc, const Blk<MTP_FMT_NVFP4> &b,
+                                             const uint8_t *xl, const float *) {
+  const float s0 = e4m3_to_f32<0>(b.s), s1 = e4m3_to_f32<1>(b.s);
+  const float s2 = e4m3_to_f32<2>(b.s), s3 = e4m3_to_f32<3>(b.s);
+  const u32x4 *xa = reinterpret_cast<const u32x4 *>(xl);
+  const u32x4 *xb = reinterpret_cast<const u32x4 *>(xl + 256);
+  acc = mfma_16x16x32(xa[0], nvfp4_decode8(b.c0.x, s0), acc);
+  acc = mfma_16x16x32(xa[1], nvfp4_decode8(b.c0.y, s0), acc);
+  acc = mfma_16x16x32(xa[2], nvfp4_decode8(b.c0.z, s1), acc);
+  acc = mfma_16x16x32(xa[3], nvfp4_decode8(b.c0.w, s1), acc);
+  acc = mfma_16x16x32(xb[0], nvfp4_decode8(b.c1.x, s2), acc);
+  acc = mfma_16x16x32(xb[1], nvfp4_decode8(b.c1.y, s2), acc);
+  acc = mfma_16x16x32(xb[2], nvfp4_decode8(b.c1.z, s3), acc);
+  acc = mfma_16x16x32(xb[3], nvfp4_decode8(b.c1.w, s3), acc);
+  return acc;
+}
+
+// Q4_0.  One MFMA per 32-block: lane (r, g) supplies slots 8g .. 8g+7 of
+// block q of the pair (code dword q % 4 of step q / 4), activations staged in
+// the matching (0,4,1,5,2,6,3,7) order.  The accumulator starts at
+// -136 * sum(x) of the block, which turns the exact operands 128 + u into
+// u - 8; the fp16 block scale is applied in fp32 afterwards.
+__device__ __forceinline__ f32x4 q4_block(f32x4 acc, uint32_t codes, float d, const uint8_t *xl,
+                                          const float *ci) {
+  const u32x4 a = *reinterpret_cast<const u32x4 *>(xl);
+  const f32x4 c0 = *reinterpret_cast<const f32x4 *>(ci);
+  const f32x4 p = mfma_16x16x32(a, q4_decode8_offset128(codes), c0);
+  acc.x = __builtin_fmaf(d, p.x, acc.x);
+  acc.y = __builtin_fmaf(d, p.y, acc.y);
+  acc.z = __builtin_fmaf(d, p.z, acc.z);
+  acc.w = __builtin_fmaf(d, p.w, acc.w);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 compute_blk(f32x4 acc, const Blk<MTP_FMT_Q4_0> &b,
+                                             const uint8_t *xl, const float *ci) {
+  // scheduling fences between block pairs bound the LDS operands held at once
+  acc = q4_block(acc, b.c0.x, half_lo(b.s.x), xl + 0, ci + 0);
+  acc = q4_block(acc, b.c0.y, half_hi(b.s.x), xl + 64, ci + 16);
+  __builtin_amdgcn_sched_barrier(0);
+  acc = q4_block(acc, b.c0.z, half_lo(b.s.y), xl + 128, ci + 32);
+  acc = q4_block(acc, b.c0.w, half_hi(b.s.y), xl + 192, ci + 48);
+  __builtin_amdgcn_sched_barrier(0);
+  acc = q4_block(acc, b.c1.x, half_lo(b.s.z), xl + 256, ci + 64);
+  acc = q4_block(acc, b.c1.y, half_hi(b.s.z), xl + 320, ci + 80);
+  __builtin_amdgcn_sched_barrier(0);
+  acc = q4_block(acc, b.c1.z, half_lo(b.s.w), xl + 384, ci + 96);
+  acc = q4_block(acc, b.c1.w, half_hi(b.s.w), xl + 448, ci + 112);
+  return acc;
+}
+
+// Byte offset of lane group g's activation fragment inside a pair slot.
+template <int FMT>
+__device__ __forceinline__ int x_lane_offset(int g) {
+  return (FMT == MTP_FMT_NVFP4) ? 64 * g : 16 * g;
+}
+
+// Partial sums cross workgroups (and XCDs) through agent-scope accesses,
+// which bypass the per-XCD caches.
+__device__ __forceinline__ void agent_store(f32x4 *p, f32x4 v) {
+  float *f = reinterpret_cast<float *>(p);
+  __hip_atomic_store(f + 0, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(f + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(f + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(f + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 agent_load(const f32x4 *p) {
+  const float *f = reinterpret_cast<const float *>(p);
+  f32x4 v;
+  v.x = __hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.y = __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.z = __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.w = __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// Element (activation row m, column c) of slot tw of the summed tiles.
+__device__ __forceinline__ float fin_at(const f32x4 *fin, int tw, int m, int c) {
+  return reinterpret_cast<const float *>(fin)[(tw * kWave + (m >> 2) * 16 + c) * 4 + (m & 3)];
+}
+
+// Runs the engine over the tile groups of `pl`.
+//   w, T, P   packed matrix with T tiles of P pairs; K its reduction length
+//   M, xs     1..16 activation rows
+//   tile_of   tile_of(tg, tw) -> tile index of slot tw of tile group tg, or
+//             -1 for a slot past the matrix (computed on tile 0, never used)
+//   epi       epi(tg, fin) is called by every thread of the workgroup once a
+//             tile group's sums are final (only by the last-arriving
+//             workgroup when KG > 1); fin_at(fin, tw, m, c) is row m of
+//             column c (0..15) of slot tw.
+// Every thread of the workgroup calls run with the same arguments.
+template <int FMT, typename TileOf, typename Epi>
+__device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
+                                    const Plan &pl, const TileOf &tile_of, const Fixup &fx,
+                                    uint8_t *lds, Epi &&epi) {
+  const int nthreads = pl.TW * pl.J * kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int g = lane >> 4, r = lane & 15;
+  const int tw = wave % pl.TW, j = wave / pl.TW;
+  const int pa = pl.kg * pl.J * pl.ppj;               // first pair of the workgroup
+  const int np = min(pl.J * pl.ppj, P - pa);          // pairs staged
+  const int rowb = row_bytes(np);
+  float *cinit = reinterpret_cast<float *>(lds + (size_t)M * rowb);
+  f32x4 *red = reinterpret_cast<f32x4 *>(cinit + cinit_floats(FMT, np));
+  f32x4 *fin = red;   // slot tw is read only by wave (tw, 0) before it holds the sum
+  __shared__ uint32_t last_flag;
+
+  // this wave's slice: pairs [pa + js, pa + js + n), n may be 0
+  const int js = min(np, j * pl.ppj);
+  const int n = min(np, js + pl.ppj) - js;
+  const int nr = (pl.ppj + kPP - 1) / kPP * kPP;      // iterations per tile group
+  const int slice = pl.kg * pl.J + j;
+
+  // load stream: tile group su, pair si of the slice (clamped into the slice;
+  // after the last block it repeats that block, which the caches hold)
+  auto tile_base = [&](int u) -> const uint8_t * {
+    int t = tile_of(pl.tg_first + u * pl.tg_step, tw);
+    t = t < 0 ? 0 : t;
+    const int p0 = n > 0 ? pa + js : P - 1;
+    return w + ((int64_t)t * P + p0) * kPairBytes;
+  };
+  int su = 0, si = 0;
+  const uint8_t *sbase = tile_base(0);
+  auto next_block = [&]() -> const uint8_t * {
+    const int i = n > 0 ? min(si, n - 1) : 0;
+    const uint8_t *p = sbase + (int64_t)i * kPairBytes;
+    if (++si == nr) {
+      if (su + 1 < pl.tg_count) {
+        si = 0;
+        ++su;
+        sbase = tile_base(su);
+      } else {
+        si = nr - 1;
+      }
+    }
+    return p;
+  };
+
+  __syncthreads();  // LDS may still be read by a previous call's epilogue
+
+  // 1) activation loads, 2) weight prefetch, 3) activation stores to LDS.
+  // Vector i = u * nthreads + tid of the staged rows is (m, v) = divmod(i,
+  // vpr); (m, v) advance incrementally so that no division sits between the
+  // loads.  Every load reads a valid address (row 0 / the first staged
+  // vector when out of range) so no branch splits them.
+  const int vpr = np * 32;                  // 16-byte vectors per staged row
+  const int k0 = pa * kPairK;
+  const int rstep = nthreads / vpr, vstep = nthreads - rstep * vpr;
+  int xm = threadIdx.x / vpr, xvi = threadIdx.x - xm * vpr;
+  u32x4 xv[kXU];
+  int xoff[kXU];
+#pragma unroll
+  for (int u = 0; u < kXU; ++u) {
+    const int k = k0 + xvi * 8;
+    const bool ok = xm < M && k < K;
+    const u32x4 t = *reinterpret_cast<const u32x4 *>(xs.row(xm < M ? xm : 0) + (ok ? k : k0));
+    xv[u] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    xoff[u] = xm < M ? xm * rowb + xvi * 16 : -1;
+    xvi += vstep;
+    xm += rstep;
+    if (xvi >= vpr) {
+      xvi -= vpr;
+      ++xm;
+    }
+  }
+  Blk<FMT> buf[kPP];
+#pragma unroll
+  for (int i = 0; i < kPP; ++i) load_blk(buf[i], next_block(), lane);
+#pragma unroll
+  for (int u = 0; u < kXU; ++u) {
+    u32x4 val = xv[u];
+    if (FMT == MTP_FMT_Q4_0) val = interleave_halves(val);
+    if (xoff[u] >= 0) *reinterpret_cast<u32x4 *>(lds + xoff[u]) = val;
+  }
+  // rows that did not fit the first round (many rows on few waves)
+  for (; xm < M; ) {
+    const int k = k0 + xvi * 8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (k < K) val = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k);
+    if (FMT == MTP_FMT_Q4_0) val = interleave_halves(val);
+    *reinterpret_cast<u32x4 *>(lds + xm * rowb + xvi * 16) = val;
+    xvi += vstep;
+    xm += rstep;
+    if (xvi >= vpr) {
+      xvi -= vpr;
+      ++xm;
+    }
+  }
+  for (int i = threadIdx.x; i < M * 32; i += nthreads) {   // zero slot of every row
+    const int m = i >> 5, v = i & 31;
+    *reinterpret_cast<u32x4 *>(lds + (size_t)m * rowb + np * kSlotBytes + v * 16) =
+        u32x4{0u, 0u, 0u, 0u};
+  }
+  if (FMT == MTP_FMT_Q4_0) {
+    __syncthreads();
+    // accumulator starts -136 * sum of each 32-block per row; 0 for rows >= M
+    // and for the zero slot
+    for (int i = threadIdx.x; i < (np + 1) * 128; i += nthreads) {
+      const int b = i >> 4, m = i & 15;
+      float s = 0.0f;
+      if (m < M && b < np * 8) {
+        const u32x4 *xr = reinterpret_cast<const u32x4 *>(lds + (size_t)m * rowb + b * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = xr[q];
+          s += bf16_to_f32(v.x) + bf16_to_f32(v.x >> 16);
+          s += bf16_to_f32(v.y) + bf16_to_f32(v.y >> 16);
+          s += bf16_to_f32(v.z) + bf16_to_f32(v.z >> 16);
+          s += bf16_to_f32(v.w) + bf16_to_f32(v.w >> 16);
+        }
+      }
+      cinit[i] = -136.0f * s;
+    }
+  }
+  __syncthreads();
+
+  const uint8_t *xrow = lds + (size_t)(r % M) * rowb + x_lane_offset<FMT>(g);
+  const float *crow = cinit + 4 * g;
+  for (int u = 0; u < pl.tg_count; ++u) {
+    const int tg = pl.tg_first + u * pl.tg_step;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b0 = 0; b0 < nr; b0 += kPP) {
+#pragma unroll
+      for (int i = 0; i < kPP; ++i) {
+        const int st = b0 + i;
+        const int slot = (st < n) ? js + st : np;   // zero slot past the slice
+        acc = compute_blk(acc, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
+        load_blk(buf[i], next_block(), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    if (pl.KG == 1) {
+      // add the J slices of each tile in slice order
+      red[wave * kWave + lane] = acc;
+      __syncthreads();
+      if (j == 0) {
+        f32x4 t = red[tw * kWave + lane];
+        for (int q = 1; q < pl.J; ++q) t += red[(q * pl.TW + tw) * kWave + lane];
+        fin[tw * kWave + lane] = t;
+      }
+      __syncthreads();
+      epi(tg, fin);
+    } else {
+      const int tile = tile_of(tg, tw);
+      if (tile >= 0 && slice < pl.S)
+        agent_store(fx.part + ((int64_t)tile * pl.S + slice) * kWave + lane, acc);
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores are complete
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t old =
+            __hip_atomic_fetch_add(fx.cnt + tg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t last = old == (uint32_t)(pl.KG - 1);
+        if (last) __hip_atomic_store(fx.cnt + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = last;
+      }
+      __syncthreads();
+      if (last_flag) {
+        if (j == 0 && tile >= 0) {
+          const f32x4 *src = fx.part + (int64_t)tile * pl.S * kWave + lane;
+          f32x4 t = agent_load(src);
+          for (int q = 1; q < pl.S; ++q) t += agent_load(src + q * kWave);
+          fin[tw * kWave + lane] = t;
+        }
+        __syncthreads();
+        epi(tg, fin);
+      }
+    }
+  }
+}
+
+}  // namespace eng
+}  // namespace mtp

@@ -8,139 +8,237 @@
 // article, §2-3: the weight bytes stay those of one token while only the
 // arithmetic grows, so the pass stays bound by memory bandwidth.
 //
-// MI355X design:
-//  * A wave owns a tile of 16 output columns (weight rows).  Each lane streams
-//    16 contiguous code bytes (32 weights) of one row per 128-wide K step with
-//    one 128-bit load; the 4 lane groups of a wave cover the step.
-//  * Decoded weights feed v_mfma_f32_16x16x32_bf16 as the B operand; the M
-//    activation rows (zero-padded to 16) are the A operand, read from LDS.
-//    The matrix cores absorb the M-fold arithmetic that would otherwise bound
-//    a vector-ALU kernel at M = 8, so the cost stays that of the weight stream.
-//  * nvfp4: E2M1 x E4M3 products are exact in bf16, so weights are decoded
-//    once per step directly into MFMA operands.
-//  * Q4_0-style: d*(u-8) is not exact in bf16, so one MFMA covers exactly one
-//    32-weight block on the raw codes (128+u, exact) with the accumulator
-//    started at -136*sum(x) (removing the offset), and the fp16 block scale is
-//    applied afterwards in fp32.  A lane-group transpose (permlane swaps) turns
-//    the coalesced per-lane block loads into the per-MFMA block layout.
-//  * Activations are staged in LDS in 1024-wide chunks shared by the four
-//    waves of a workgroup; weight loads run several steps ahead of the math.
-//  * Long K is split across workgroups; the fp32 partials are summed in a
-//    fixed order by a second kernel, so results are deterministic.
-#include "gemm_core.h"
+// MI355X design (the engine is in engine.h):
+//  * Weights are repacked once (mtp_pack_weights) into 2304-byte blocks of
+//    16 rows x 256 K that match the matrix-core operand layout, so a wave
+//    streams 1 KiB code loads and one scale load per 128-wide K step.
+//  * Decoded weights are the B operand of v_mfma_f32_16x16x32_bf16 and the
+//    M activation rows (staged once in LDS) the A operand: the matrix cores
+//    absorb the M-fold arithmetic that would otherwise bound a vector-ALU
+//    kernel at M = 8, so the cost stays that of the weight stream.
+//  * nvfp4: E2M1 x E4M3 products are exact in bf16, so every weight is
+//    decoded once into an MFMA operand.  Q4_0-style: d*(u-8) is not exact in
+//    bf16, so one MFMA covers exactly one 32-block on the exact values 128+u
+//    with the accumulator started at -136*sum(x), and the fp16 scale is
+//    applied in fp32 afterwards.
+//  * The slice split of K is a function of the matrix shape only and partial
+//    sums are added in slice order, so results are deterministic and a row's
+//    result does not depend on M or on the other rows.
+#include <algorithm>
+
+#include "engine.h"
 #include "internal.h"
 
 namespace mtp {
 namespace {
 
-using core::kThreads;
-using core::kWaves;
-using core::kStepK;
+using eng::kPairBytes;
+using eng::kPairK;
+
+// ---- packing ---------------------------------------------------------------
+
+// One wave per (matrix, tile, pair) block; lane l = 16 g + r covers row
+// 16 t + r.  Rows past N and K past the matrix are written as zero codes and
+// zero scales, which contribute exactly nothing.
+template <int FMT>
+__global__ __launch_bounds__(64) void pack_kernel(const uint8_t *__restrict__ codes,
+                                                  const uint8_t *__restrict__ scales, int N,
+                                                  int K, int T, int P,
+                                                  uint8_t *__restrict__ out) {
+  const int64_t blk = blockIdx.x;
+  const int e = (int)(blk / ((int64_t)T * P));
+  const int rem = (int)(blk - (int64_t)e * T * P);
+  const int t = rem / P, p = rem - t * P;
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const int n = 16 * t + r;
+  const bool row_ok = n < N;
+  const uint8_t *crow = codes + ((int64_t)e * N + (row_ok ? n : 0)) * (K / 2);
+  uint8_t *o = out + blk * kPairBytes;
+  if (FMT == MTP_FMT_NVFP4) {
+    const uint8_t *srow = scales + ((int64_t)e * N + (row_ok ? n : 0)) * (K / 16);
+    const int k0 = kPairK * p + 32 * g, k1 = k0 + 128;
+    const bool ok0 = row_ok && k0 < K, ok1 = row_ok && k1 < K;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 c0 = ok0 ? *reinterpret_cast<const u32x4 *>(crow + k0 / 2) : z;
+    const u32x4 c1 = ok1 ? *reinterpret_cast<const u32x4 *>(crow + k1 / 2) : z;
+    const uint32_t s0 = ok0 ? *reinterpret_cast<const uint16_t *>(srow + k0 / 16) : 0u;
+    const uint32_t s1 = ok1 ? *reinterpret_cast<const uint16_t *>(srow + k1 / 16) : 0u;
+    *reinterpret_cast<u32x4 *>(o + 16 * lane) = c0;
+    *reinterpret_cast<u32x4 *>(o + eng::kHalfBytes + 16 * lane) = c1;
+    *reinterpret_cast<uint32_t *>(o + eng::kScaleOff + 4 * lane) = s0 | (s1 << 16);
+  } else {
+    const uint16_t *srow =
+        reinterpret_cast<const uint16_t *>(scales) + ((int64_t)e * N + (row_ok ? n : 0)) * (K / 32);
+    uint32_t d[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = kPairK * p + 128 * h + 32 * q + 8 * g;
+        d[4 * h + q] = (row_ok && k < K) ? *reinterpret_cast<const uint32_t *>(crow + k / 2) : 0u;
+      }
+    *reinterpret_cast<u32x4 *>(o + 16 * lane) = u32x4{d[0], d[1], d[2], d[3]};
+    *reinterpret_cast<u32x4 *>(o + eng::kHalfBytes + 16 * lane) = u32x4{d[4], d[5], d[6], d[7]};
+    const int b0 = 8 * p + 2 * g, nb = K / 32;
+    const uint32_t s0 = (row_ok && b0 < nb) ? srow[b0] : 0u;
+    const uint32_t s1 = (row_ok && b0 + 1 < nb) ? srow[b0 + 1] : 0u;
+    *reinterpret_cast<uint32_t *>(o + eng::kScaleOff + 16 * r + 4 * g) = s0 | (s1 << 16);
+  }
+}
+
+// ---- dense GEMM ------------------------------------------------------------
 
 struct GemmArgs {
-  const uint8_t *codes;
-  const void *scales;
+  const uint8_t *w;
   const uint16_t *x;
   int64_t ldx;
   float *y;
   int64_t ldy;
   uint16_t *yb;
   int64_t ldyb;
-  float *part;
   float gscale;
-  int M, N, K;
-  int split_k;
-  int splits;
+  int M, N, K, T, P;
+  int TW, J, S, ppj, KG, TG, G;
+  eng::Fixup fx;
 };
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int r = lane & 15, g = lane >> 4;
-  const int M = p.M, N = p.N, K = p.K;
-  const int n0 = (blockIdx.x * kWaves + wave) * 16;
-  const int nrow = min(n0 + r, N - 1);  // rows past N read row N-1, never stored
-  const uint8_t *crow[1] = {p.codes + (int64_t)nrow * (K / 2)};
-  const void *srow[1] = {core::scale_row<FMT>(p.scales, nrow, K)};
-  const int k_begin = blockIdx.y * p.split_k;
-  const int k_end = min(K, k_begin + p.split_k);
-  const core::XSource xs{p.x, p.ldx, nullptr};
-  f32x4 acc[1];
-  core::run_tiles<FMT, 1>(acc, crow, srow, xs, M, K, k_begin, k_end, lds);
+struct DenseTiles {
+  int TW, T;
+  __device__ __forceinline__ int operator()(int tg, int tw) const {
+    const int t = tg * TW + tw;
+    return t < T ? t : -1;
+  }
+};
 
-  const int n = n0 + r;
-  if (n < N) {
-    const float v[4] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * g + i;
-      if (m < M) {
-        if (p.splits == 1) {
-          const float o = p.gscale * v[i];
-          if (p.y) p.y[(int64_t)m * p.ldy + n] = o;
-          if (p.yb) p.yb[(int64_t)m * p.ldyb + n] = f32_to_bf16_rne(o);
-        } else {
-          p.part[((int64_t)blockIdx.y * M + m) * N + n] = v[i];
-        }
+// Thread o writes output (m, c) = divmod(o, 16 TW) of the tile group, so a
+// row's columns are stored by consecutive lanes.
+struct DenseEpi {
+  const GemmArgs *a;
+  __device__ __forceinline__ void operator()(int tg, const f32x4 *fin) const {
+    const int cols = a->TW * 16, nthreads = a->TW * a->J * kWave;
+    for (int o = threadIdx.x; o < a->M * cols; o += nthreads) {
+      const int m = o / cols, c = o - m * cols;
+      const int n = tg * cols + c;
+      if (n < a->N) {
+        const float v = a->gscale * eng::fin_at(fin, c >> 4, m, c & 15);
+        if (a->y) a->y[(int64_t)m * a->ldy + n] = v;
+        if (a->yb) a->yb[(int64_t)m * a->ldyb + n] = f32_to_bf16_rne(v);
       }
     }
   }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(eng::kMaxThreads) void gemm_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  eng::Plan pl;
+  pl.TW = a.TW; pl.J = a.J; pl.S = a.S; pl.ppj = a.ppj; pl.KG = a.KG;
+  pl.kg = blockIdx.x % a.KG;
+  pl.tg_first = blockIdx.x / a.KG;
+  pl.tg_step = a.G;
+  pl.tg_count = (a.TG - pl.tg_first + a.G - 1) / a.G;
+  const eng::XSource xs{a.x, a.ldx, nullptr};
+  eng::run<FMT>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx, lds, DenseEpi{&a});
 }
 
-// Sum the split-K partials in split order, scale, store.
-__global__ __launch_bounds__(256) void gemm_combine(const float *part, int splits, int M, int N,
-                                                    float gscale, float *y, int64_t ldy,
-                                                    uint16_t *yb, int64_t ldyb) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t MN = (int64_t)M * N;
-  if (i >= MN) return;
-  float s = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) s += part[sp * MN + i];
-  const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
-  const float o = gscale * s;
-  if (y) y[(int64_t)m * ldy + n] = o;
-  if (yb) yb[(int64_t)m * ldyb + n] = f32_to_bf16_rne(o);
+// Slices of the K range: a function of the shape only (see engine.h).  About
+// 2048 (tile, slice) streams keep every CU busy without making them short;
+// a slice holds at most kMaxPpj pairs so that one slice of MTP_MAX_M rows
+// always fits the LDS of one workgroup.
+constexpr int kMaxPpj = 16;
+
+void slices(int T, int P, int &S, int &ppj) {
+  int s = (int)((2048.0 + T / 2) / T);
+  s = s < 1 ? 1 : (s > P ? P : s);
+  s = std::max(s, (P + kMaxPpj - 1) / kMaxPpj);
+  ppj = (P + s - 1) / s;
+  S = (P + ppj - 1) / ppj;
 }
 
 }  // namespace
 
-GemmPlan gemm_plan(int M, int N, int K) {
-  GemmPlan plan;
-  const int groups = (N + kWaves * 16 - 1) / (kWaves * 16);
-  const int steps = (K + kStepK - 1) / kStepK;
-  const int target_wgs = 1024;  // about four workgroups per CU
-  int splits = (target_wgs + groups - 1) / groups;
-  splits = max(1, min(splits, steps / 4));
-  const int per = (steps + splits - 1) / splits;
-  splits = (steps + per - 1) / per;
-  plan.splits = splits;
-  plan.split_k = per * kStepK;
-  plan.ws_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
-  return plan;
+size_t packed_weight_bytes(int N, int K) { return eng::packed_bytes(N, K); }
+
+hipError_t launch_pack(int format, int count, int N, int K, const uint8_t *codes,
+                       const void *scales, uint8_t *packed, hipStream_t stream) {
+  const int T = eng::tiles_of(N), P = eng::pairs_of(K);
+  const int64_t blocks = (int64_t)count * T * P;
+  const uint8_t *s = static_cast<const uint8_t *>(scales);
+  if (format == MTP_FMT_NVFP4)
+    hipLaunchKernelGGL(pack_kernel<MTP_FMT_NVFP4>, dim3((unsigned)blocks), dim3(64), 0, stream,
+                       codes, s, N, K, T, P, packed);
+  else
+    hipLaunchKernelGGL(pack_kernel<MTP_FMT_Q4_0>, dim3((unsigned)blocks), dim3(64), 0, stream,
+                       codes, s, N, K, T, P, packed);
+  return hipGetLastError();
+}
+
+size_t gemm_ws_bytes(int N, int K) {
+  const int T = eng::tiles_of(N), P = eng::pairs_of(K);
+  int S, ppj;
+  slices(T, P, S, ppj);
+  if (S == 1) return 0;
+  return (((size_t)T * 4 + 255) & ~(size_t)255) + (size_t)T * S * kWave * 16;
+}
+
+GemmPlan gemm_plan(int format, int M, int N, int K) {
+  GemmPlan pl;
+  pl.T = eng::tiles_of(N);
+  pl.P = eng::pairs_of(K);
+  slices(pl.T, pl.P, pl.S, pl.ppj);
+  // slices per workgroup: all of them unless the staged rows get too large
+  const size_t budget = 144 * 1024;
+  pl.KG = 1;
+  for (;;) {
+    pl.J = (pl.S + pl.KG - 1) / pl.KG;
+    if (pl.J <= 16 && eng::lds_bytes(format, M, std::min(pl.J * pl.ppj, pl.P), 16 / pl.J, pl.J) <= budget)
+      break;
+    if (pl.J == 1) break;
+    ++pl.KG;
+  }
+  pl.KG = (pl.S + pl.J - 1) / pl.J;
+  // tiles per workgroup: as many as fit 16 waves while enough workgroups remain
+  pl.TW = 1;
+  while (pl.TW * 2 * pl.J <= eng::kMaxWaves &&
+         (int64_t)((pl.T + pl.TW * 2 - 1) / (pl.TW * 2)) * pl.KG >= 192)
+    pl.TW *= 2;
+  pl.TG = (pl.T + pl.TW - 1) / pl.TW;
+  pl.threads = pl.TW * pl.J * kWave;
+  pl.lds = eng::lds_bytes(format, M, std::min(pl.J * pl.ppj, pl.P), pl.TW, pl.J);
+  return finish_plan(pl);
+}
+
+GemmPlan finish_plan(GemmPlan pl) {
+  // resident workgroups: LDS and wave slots of 256 CUs
+  int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds, 1));
+  per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
+  const int64_t cap = (int64_t)256 * per_cu / pl.KG;
+  pl.G = (int)std::max<int64_t>(1, std::min<int64_t>(pl.TG, cap));
+  pl.grid = pl.G * pl.KG;
+  pl.ws_bytes = pl.KG > 1 ? (((size_t)pl.T * 4 + 255) & ~(size_t)255) +
+                                (size_t)pl.T * pl.S * kWave * 16
+                          : 0;
+  return pl;
 }
 
 hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t ldx,
-                       const uint8_t *codes, const void *scales, float gscale, float *y,
-                       int64_t ldy, uint16_t *yb, int64_t ldyb, void *ws, const GemmPlan &plan,
-                       hipStream_t stream) {
+                       const uint8_t *packed, float gscale, float *y, int64_t ldy, uint16_t *yb,
+                       int64_t ldyb, void *ws, const GemmPlan &pl, hipStream_t stream) {
   GemmArgs a;
-  a.codes = codes; a.scales = scales; a.x = x; a.ldx = ldx;
+  a.w = packed; a.x = x; a.ldx = ldx;
   a.y = y; a.ldy = ldy; a.yb = yb; a.ldyb = ldyb;
-  a.part = static_cast<float *>(ws);
-  a.gscale = gscale; a.M = M; a.N = N; a.K = K;
-  a.split_k = plan.split_k; a.splits = plan.splits;
-  const dim3 grid((N + kWaves * 16 - 1) / (kWaves * 16), plan.splits);
-  const size_t shm = core::lds_bytes(M, format);
-  if (format == MTP_FMT_NVFP4)
-    hipLaunchKernelGGL(gemm_kernel<MTP_FMT_NVFP4>, grid, dim3(kThreads), shm, stream, a);
-  else
-    hipLaunchKernelGGL(gemm_kernel<MTP_FMT_Q4_0>, grid, dim3(kThreads), shm, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.splits == 1) return e;
-  const int64_t MN = (int64_t)M * N;
-  hipLaunchKernelGGL(gemm_combine, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream,
-                     a.part, plan.splits, M, N, gscale, y, ldy, yb, ldyb);
+  a.gscale = gscale; a.M = M; a.N = N; a.K = K; a.T = pl.T; a.P = pl.P;
+  a.TW = pl.TW; a.J = pl.J; a.S = pl.S; a.ppj = pl.ppj; a.KG = pl.KG; a.TG = pl.TG; a.G = pl.G;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  a.fx.cnt = reinterpret_cast<uint32_t *>(w8);
+  a.fx.part = reinterpret_cast<f32x4 *>(w8 ? w8 + (((size_t)pl.T * 4 + 255) & ~(size_t)255) : nullptr);
+  if (format == MTP_FMT_NVFP4) {
+    eng::allow_large_lds(gemm_kernel<MTP_FMT_NVFP4>);
+    hipLaunchKernelGGL(gemm_kernel<MTP_FMT_NVFP4>, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
+  } else {
+    eng::allow_large_lds(gemm_kernel<MTP_FMT_Q4_0>);
+    hipLaunchKernelGGL(gemm_kernel<MTP_FMT_Q4_0>, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
+  }
   return hipGetLastError();
 }
 

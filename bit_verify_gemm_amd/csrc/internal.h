@@ -7,20 +7,33 @@
 
 namespace mtp {
 
-// ---- verify GEMM -----------------------------------------------------------
+// ---- packing and the verify GEMM -------------------------------------------
 
+size_t packed_weight_bytes(int N, int K);
+
+hipError_t launch_pack(int format, int count, int N, int K, const uint8_t *codes,
+                       const void *scales, uint8_t *packed, hipStream_t stream);
+
+// Launch shape of the dense GEMM (see engine.h for the terms).
 struct GemmPlan {
-  int splits;      // K-ranges processed by separate workgroups
-  int split_k;     // length of each K-range (multiple of 128, last one ragged)
-  size_t ws_bytes; // fp32 partials [splits][M][N] when splits > 1
+  int T, P;          // tiles of 16 rows, pairs of 256 K
+  int S, ppj;        // K slices and pairs per slice (shape only)
+  int J, KG, TW;     // slices per workgroup, workgroups per tile group, tiles per workgroup
+  int TG, G, grid;   // tile groups, workgroups per K group, total workgroups
+  int threads;
+  size_t lds;
+  size_t ws_bytes;   // arrival counters + slice partials when KG > 1
 };
 
-GemmPlan gemm_plan(int M, int N, int K);
+GemmPlan gemm_plan(int format, int M, int N, int K);
+GemmPlan finish_plan(GemmPlan pl);   // fills G, grid and ws_bytes from the rest
+
+// Workspace that covers every M for this shape (0 when K has one slice).
+size_t gemm_ws_bytes(int N, int K);
 
 hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t ldx,
-                       const uint8_t *codes, const void *scales, float gscale, float *y,
-                       int64_t ldy, uint16_t *yb, int64_t ldyb, void *ws, const GemmPlan &plan,
-                       hipStream_t stream);
+                       const uint8_t *packed, float gscale, float *y, int64_t ldy, uint16_t *yb,
+                       int64_t ldyb, void *ws, const GemmPlan &plan, hipStream_t stream);
 
 // ---- acceptance ------------------------------------------------------------
 
@@ -40,10 +53,12 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
 
 size_t moe_ws_bytes(int T, int H, int F, int E, int topk);
 
+// Whether the staged rows of one expert pass fit a workgroup's LDS.
+bool moe_fits(int format, int T, int H, int F);
+
 hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const uint16_t *x,
-                      const int32_t *ids, const float *gw, const uint8_t *gu_codes,
-                      const void *gu_scales, const float *gu_global, const uint8_t *dn_codes,
-                      const void *dn_scales, const float *dn_global, float *out,
-                      uint16_t *h_out, void *ws, hipStream_t stream);
+                      const int32_t *ids, const float *gw, const uint8_t *gu_packed,
+                      const float *gu_global, const uint8_t *dn_packed, const float *dn_global,
+                      float *out, uint16_t *h_out, void *ws, hipStream_t stream);
 
 }  // namespace mtp

@@ -11,21 +11,23 @@
 // Pipeline (all on the device, no host round trip):
 //  1. route:   one workgroup sorts the T*topk (expert, pair) keys, lists the
 //              unique experts and each expert's pairs in pair order.
-//  2. gate_up: grid = (F tiles) x (unique-expert slots); a wave computes a
-//              gate tile and the matching up tile for all rows of its expert
-//              and writes h = bf16(silu(gate) * up) per pair.
-//  3. down:    grid = (H tiles) x (slots); y[pair] = W_d[e] . h[pair].
+//  2. gate_up: grid = (tile groups) x (unique-expert slots); a workgroup
+//              streams gate tiles and the matching up tiles of its expert
+//              through the engine of the dense GEMM (engine.h) for all rows
+//              of that expert and writes h = bf16(silu(gate) * up) per pair.
+//  3. down:    the same for y[pair] = W_d[e] . h[pair].
 //  4. combine: out[t] = sum over slots in slot order of w[t][s] * y[t, s].
 // The grids are sized for the largest possible number of unique experts;
-// slots beyond the actual count exit at once.
-#include "gemm_core.h"
+// slots beyond the actual count exit at once.  The K split of each expert
+// matrix depends only on its shape, so a pair's result does not depend on
+// which other tokens chose the same expert.
+#include <algorithm>
+
+#include "engine.h"
 #include "internal.h"
 
 namespace mtp {
 namespace {
-
-using core::kThreads;
-using core::kWaves;
 
 constexpr int kMaxPairs = 1024;
 constexpr int kInvalidKey = 0x7FFFFFFF - kMaxPairs;  // above e * kMaxPairs + p for e < 2^20
@@ -59,15 +61,15 @@ struct MoeArgs {
   const uint16_t *x;
   const int32_t *ids;
   const float *gw;
-  const uint8_t *gu_codes;
-  const void *gu_scales;
+  const uint8_t *gu_packed;
   const float *gu_global;
-  const uint8_t *dn_codes;
-  const void *dn_scales;
+  const uint8_t *dn_packed;
   const float *dn_global;
   float *out;
   uint16_t *h_out;
   int T, H, F, E, topk, P;
+  int rc;                 // rows per engine pass
+  struct { int TW, J, S, ppj; } gu, dn;
   int32_t *nuniq, *uexp, *ustart, *ucount, *spair, *stok;
   uint16_t *h;
   float *y;
@@ -137,81 +139,99 @@ __device__ __forceinline__ float silu(float v) {
   return v * e / (1.0f + e);
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void moe_gate_up(MoeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int slot = blockIdx.y;
-  if (slot >= *a.nuniq) return;  // whole workgroup
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int r = lane & 15, g = lane >> 4;
-  const int H = a.H, F = a.F;
-  const int e = a.uexp[slot], first = a.ustart[slot], rows = a.ucount[slot];
-  const int f0 = (blockIdx.x * kWaves + wave) * 16;
-  const int frow = min(f0 + r, F - 1);
-  const uint8_t *cb = a.gu_codes + (int64_t)e * (2 * F) * (H / 2);
-  const int bs = (FMT == MTP_FMT_NVFP4) ? 16 : 32;
-  const int ssz = (FMT == MTP_FMT_NVFP4) ? 1 : 2;
-  const uint8_t *sb = static_cast<const uint8_t *>(a.gu_scales) + (int64_t)e * (2 * F) * (H / bs) * ssz;
-  const uint8_t *crow[2] = {cb + (int64_t)frow * (H / 2), cb + (int64_t)(F + frow) * (H / 2)};
-  const void *srow[2] = {core::scale_row<FMT>(sb, frow, H), core::scale_row<FMT>(sb, F + frow, H)};
-  const float gsc = a.gu_global ? a.gu_global[e] : 1.0f;
-  for (int c0 = 0; c0 < rows; c0 += 16) {
-    const int mc = min(16, rows - c0);
-    const core::XSource xs{a.x, H, a.stok + first + c0};
-    f32x4 acc[2];
-    core::run_tiles<FMT, 2>(acc, crow, srow, xs, mc, H, 0, H, lds);
-    const int f = f0 + r;
-    if (f < F) {
-      const float gv[4] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w};
-      const float uv[4] = {acc[1].x, acc[1].y, acc[1].z, acc[1].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m < mc) {
-          const float gate = gsc * gv[i], up = gsc * uv[i];
-          const float act = silu(gate);
-          const uint16_t hb = f32_to_bf16_rne(act * up);
-          const int pair = a.spair[first + c0 + m];
-          a.h[(int64_t)pair * F + f] = hb;
-          if (a.h_out) a.h_out[(int64_t)pair * F + f] = hb;
-        }
+struct GateUpTiles {
+  int TWh, Fg;   // gate tiles per workgroup, gate tiles of the expert
+  __device__ __forceinline__ int operator()(int tg, int tw) const {
+    const int t = tg * TWh + tw / 2;
+    if (t >= Fg) return -1;
+    return (tw & 1) ? Fg + t : t;   // slot 2q: gate tile, slot 2q + 1: the matching up tile
+  }
+};
+
+struct GateUpEpi {
+  const MoeArgs *a;
+  int TWh, nthreads, mc, c0, first;
+  float gsc;
+  __device__ __forceinline__ void operator()(int tg, const f32x4 *fin) const {
+    const int cols = TWh * 16;
+    for (int o = threadIdx.x; o < mc * cols; o += nthreads) {
+      const int m = o / cols, c = o - m * cols;
+      const int f = tg * cols + c;
+      if (f < a->F) {
+        const int q = c >> 4;
+        const float gate = gsc * eng::fin_at(fin, 2 * q, m, c & 15);
+        const float up = gsc * eng::fin_at(fin, 2 * q + 1, m, c & 15);
+        const uint16_t hb = f32_to_bf16_rne(silu(gate) * up);
+        const int pair = a->spair[first + c0 + m];
+        a->h[(int64_t)pair * a->F + f] = hb;
+        if (a->h_out) a->h_out[(int64_t)pair * a->F + f] = hb;
       }
     }
   }
-}
+};
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void moe_down(MoeArgs a) {
+__global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int slot = blockIdx.y;
   if (slot >= *a.nuniq) return;  // whole workgroup
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int r = lane & 15, g = lane >> 4;
-  const int H = a.H, F = a.F;
   const int e = a.uexp[slot], first = a.ustart[slot], rows = a.ucount[slot];
-  const int n0 = (blockIdx.x * kWaves + wave) * 16;
-  const int nrow = min(n0 + r, H - 1);
-  const uint8_t *cb = a.dn_codes + (int64_t)e * H * (F / 2);
-  const int bs = (FMT == MTP_FMT_NVFP4) ? 16 : 32;
-  const int ssz = (FMT == MTP_FMT_NVFP4) ? 1 : 2;
-  const uint8_t *sb = static_cast<const uint8_t *>(a.dn_scales) + (int64_t)e * H * (F / bs) * ssz;
-  const uint8_t *crow[1] = {cb + (int64_t)nrow * (F / 2)};
-  const void *srow[1] = {core::scale_row<FMT>(sb, nrow, F)};
-  const float gsc = a.dn_global ? a.dn_global[e] : 1.0f;
-  for (int c0 = 0; c0 < rows; c0 += 16) {
-    const int mc = min(16, rows - c0);
-    const core::XSource xs{a.h, F, a.spair + first + c0};
-    f32x4 acc[1];
-    core::run_tiles<FMT, 1>(acc, crow, srow, xs, mc, F, 0, F, lds);
-    const int n = n0 + r;
-    if (n < H) {
-      const float v[4] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m < mc) a.y[(int64_t)a.spair[first + c0 + m] * H + n] = gsc * v[i];
-      }
+  const int P = eng::pairs_of(a.H);
+  const uint8_t *w = a.gu_packed + (int64_t)e * eng::packed_bytes(2 * a.F, a.H);
+  eng::Plan pl;
+  pl.TW = a.gu.TW; pl.J = a.gu.J; pl.S = a.gu.S; pl.ppj = a.gu.ppj; pl.KG = 1; pl.kg = 0;
+  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x; pl.tg_count = 1;
+  const GateUpTiles tiles{pl.TW / 2, a.F / 16};
+  const float gsc = a.gu_global ? a.gu_global[e] : 1.0f;
+  for (int c0 = 0; c0 < rows; c0 += a.rc) {
+    const int mc = min(a.rc, rows - c0);
+    const eng::XSource xs{a.x, a.H, a.stok + first + c0};
+    eng::run<FMT>(w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds,
+                  GateUpEpi{&a, pl.TW / 2, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+  }
+}
+
+struct DownEpi {
+  const MoeArgs *a;
+  int TW, nthreads, mc, c0, first;
+  float gsc;
+  __device__ __forceinline__ void operator()(int tg, const f32x4 *fin) const {
+    const int cols = TW * 16;
+    for (int o = threadIdx.x; o < mc * cols; o += nthreads) {
+      const int m = o / cols, c = o - m * cols;
+      const int n = tg * cols + c;
+      if (n < a->H)
+        a->y[(int64_t)a->spair[first + c0 + m] * a->H + n] = gsc * eng::fin_at(fin, c >> 4, m, c & 15);
     }
+  }
+};
+
+struct DownTiles {
+  int TW, T;
+  __device__ __forceinline__ int operator()(int tg, int tw) const {
+    const int t = tg * TW + tw;
+    return t < T ? t : -1;
+  }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int slot = blockIdx.y;
+  if (slot >= *a.nuniq) return;  // whole workgroup
+  const int e = a.uexp[slot], first = a.ustart[slot], rows = a.ucount[slot];
+  const int P = eng::pairs_of(a.F);
+  const uint8_t *w = a.dn_packed + (int64_t)e * eng::packed_bytes(a.H, a.F);
+  eng::Plan pl;
+  pl.TW = a.dn.TW; pl.J = a.dn.J; pl.S = a.dn.S; pl.ppj = a.dn.ppj; pl.KG = 1; pl.kg = 0;
+  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x; pl.tg_count = 1;
+  const DownTiles tiles{pl.TW, eng::tiles_of(a.H)};
+  const float gsc = a.dn_global ? a.dn_global[e] : 1.0f;
+  for (int c0 = 0; c0 < rows; c0 += a.rc) {
+    const int mc = min(a.rc, rows - c0);
+    const eng::XSource xs{a.h, a.F, a.spair + first + c0};
+    eng::run<FMT>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds,
+                  DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, c0, first, gsc});
   }
 }
 
@@ -228,7 +248,47 @@ __global__ __launch_bounds__(256) void moe_combine(MoeArgs a) {
   a.out[i] = s;
 }
 
+// Engine shape of one expert matrix: a single workgroup covers all slices
+// (S of about 8 pairs each); rc rows are staged per pass.
+struct MoePlan {
+  int TW, J, S, ppj, tg, threads;
+  size_t lds;
+};
+
+MoePlan moe_plan(int format, int N, int K, int rc, int tw_max, bool paired) {
+  MoePlan m;
+  const int P = eng::pairs_of(K);
+  m.S = std::max(1, std::min((P + 4) / 8, paired ? eng::kMaxWaves / 2 : eng::kMaxWaves));
+  m.ppj = (P + m.S - 1) / m.S;
+  m.S = (P + m.ppj - 1) / m.ppj;
+  m.J = m.S;
+  m.TW = std::max(paired ? 2 : 1, std::min(tw_max, eng::kMaxWaves / m.J));
+  if (paired) m.TW &= ~1;
+  const int tiles = paired ? eng::tiles_of(N) / 2 : eng::tiles_of(N);
+  const int per = paired ? m.TW / 2 : m.TW;
+  m.tg = (tiles + per - 1) / per;
+  m.threads = m.TW * m.J * kWave;
+  m.lds = eng::lds_bytes(format, rc, std::min(m.J * m.ppj, P), m.TW, m.J);
+  return m;
+}
+
+// Rows staged per pass: up to 16 (and T, which bounds the rows of an expert
+// unless a token repeats an expert), fewer if the staged rows would not fit.
+int moe_rows(int format, int T, int H, int F) {
+  int rc = std::min(16, T);
+  while (rc > 1 && (moe_plan(format, 2 * F, H, rc, 4, true).lds > 144 * 1024 ||
+                    moe_plan(format, H, F, rc, 8, false).lds > 144 * 1024))
+    --rc;
+  return rc;
+}
+
 }  // namespace
+
+bool moe_fits(int format, int T, int H, int F) {
+  const int rc = moe_rows(format, T, H, F);
+  return moe_plan(format, 2 * F, H, rc, 4, true).lds <= 144 * 1024 &&
+         moe_plan(format, H, F, rc, 8, false).lds <= 144 * 1024;
+}
 
 size_t moe_ws_bytes(int T, int H, int F, int E, int topk) {
   (void)E;
@@ -236,16 +296,15 @@ size_t moe_ws_bytes(int T, int H, int F, int E, int topk) {
 }
 
 hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const uint16_t *x,
-                      const int32_t *ids, const float *gw, const uint8_t *gu_codes,
-                      const void *gu_scales, const float *gu_global, const uint8_t *dn_codes,
-                      const void *dn_scales, const float *dn_global, float *out,
-                      uint16_t *h_out, void *ws, hipStream_t stream) {
+                      const int32_t *ids, const float *gw, const uint8_t *gu_packed,
+                      const float *gu_global, const uint8_t *dn_packed, const float *dn_global,
+                      float *out, uint16_t *h_out, void *ws, hipStream_t stream) {
   const MoeLayout L = moe_layout(T, H, F, topk);
   uint8_t *w = static_cast<uint8_t *>(ws);
   MoeArgs a;
   a.x = x; a.ids = ids; a.gw = gw;
-  a.gu_codes = gu_codes; a.gu_scales = gu_scales; a.gu_global = gu_global;
-  a.dn_codes = dn_codes; a.dn_scales = dn_scales; a.dn_global = dn_global;
+  a.gu_packed = gu_packed; a.gu_global = gu_global;
+  a.dn_packed = dn_packed; a.dn_global = dn_global;
   a.out = out; a.h_out = h_out;
   a.T = T; a.H = H; a.F = F; a.E = E; a.topk = topk; a.P = T * topk;
   a.nuniq = reinterpret_cast<int32_t *>(w + L.nuniq);
@@ -256,19 +315,26 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
   a.stok = reinterpret_cast<int32_t *>(w + L.stok);
   a.h = reinterpret_cast<uint16_t *>(w + L.h);
   a.y = reinterpret_cast<float *>(w + L.y);
+  a.rc = moe_rows(format, T, H, F);
+  const MoePlan gu = moe_plan(format, 2 * F, H, a.rc, 4, true);
+  const MoePlan dn = moe_plan(format, H, F, a.rc, 8, false);
+  a.gu = {gu.TW, gu.J, gu.S, gu.ppj};
+  a.dn = {dn.TW, dn.J, dn.S, dn.ppj};
   const int slots = (a.P < E) ? a.P : E;
   hipLaunchKernelGGL(moe_route, dim3(1), dim3(kMaxPairs), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t shm = core::lds_bytes(16, format);
-  const dim3 gu_grid((F + kWaves * 16 - 1) / (kWaves * 16), slots);
-  const dim3 dn_grid((H + kWaves * 16 - 1) / (kWaves * 16), slots);
+  const dim3 gu_grid(gu.tg, slots), dn_grid(dn.tg, slots);
   if (format == MTP_FMT_NVFP4) {
-    hipLaunchKernelGGL(moe_gate_up<MTP_FMT_NVFP4>, gu_grid, dim3(kThreads), shm, stream, a);
-    hipLaunchKernelGGL(moe_down<MTP_FMT_NVFP4>, dn_grid, dim3(kThreads), shm, stream, a);
+    eng::allow_large_lds(moe_gate_up<MTP_FMT_NVFP4>);
+    eng::allow_large_lds(moe_down<MTP_FMT_NVFP4>);
+    hipLaunchKernelGGL(moe_gate_up<MTP_FMT_NVFP4>, gu_grid, dim3(gu.threads), gu.lds, stream, a);
+    hipLaunchKernelGGL(moe_down<MTP_FMT_NVFP4>, dn_grid, dim3(dn.threads), dn.lds, stream, a);
   } else {
-    hipLaunchKernelGGL(moe_gate_up<MTP_FMT_Q4_0>, gu_grid, dim3(kThreads), shm, stream, a);
-    hipLaunchKernelGGL(moe_down<MTP_FMT_Q4_0>, dn_grid, dim3(kThreads), shm, stream, a);
+    eng::allow_large_lds(moe_gate_up<MTP_FMT_Q4_0>);
+    eng::allow_large_lds(moe_down<MTP_FMT_Q4_0>);
+    hipLaunchKernelGGL(moe_gate_up<MTP_FMT_Q4_0>, gu_grid, dim3(gu.threads), gu.lds, stream, a);
+    hipLaunchKernelGGL(moe_down<MTP_FMT_Q4_0>, dn_grid, dim3(dn.threads), dn.lds, stream, a);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;

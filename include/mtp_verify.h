@@ -44,7 +44,8 @@
  *    string.  Calls that share a workspace must be ordered on one stream.
  *
  * Weight formats (the pages name "nvfp4" and "Q4"; the layouts are this
- * library's): a K x N matrix used as y = x . W is stored per output row n.
+ * library's).  A K x N matrix used as y = x . W is given per output row n in
+ * the row-major SOURCE layout:
  *   codes : uint8 [N][K/2]; weight (n, k) is the low nibble of byte
  *           n*K/2 + k/2 for even k and the high nibble for odd k.
  *   MTP_FMT_NVFP4: nibble = E2M1 (bit3 sign, bits2..1 exponent bias 1, bit0
@@ -52,8 +53,23 @@
  *           NaN); w = global_scale * e4m3(scale[n][k/16]) * e2m1(nibble).
  *   MTP_FMT_Q4_0: nibble u = offset-binary int4; scales = IEEE fp16
  *           [N][K/32]; w = global_scale * f16(scale[n][k/32]) * (u - 8).
- *   K must be a positive multiple of 32; codes and scales 16-byte aligned.
- *   Matrices stacked along N (fused Q/K/V, gate||up) are just more rows.
+ *   K must be a positive multiple of 32.
+ * The GEMM reads weights in a PACKED layout made once (at load time) by
+ * mtp_pack_weights: for tile t (rows 16t .. 16t+15) and pair p (k = 256p ..
+ * 256p+255) a 2304-byte block at byte (t * ceil(K/256) + p) * 2304.  With
+ * lane l = 16g + r (row 16t + r), k0 = 256p + 32g and k1 = k0 + 128:
+ *   nvfp4: bytes [16l, 16l+16)       source code bytes of k0 .. k0+31
+ *          bytes [1024+16l, +16)     source code bytes of k1 .. k1+31
+ *          bytes [2048+4l, +4)       scales of k0, k0+16, k1, k1+16
+ *   Q4_0:  bytes [16l + 4q, +4)      source code bytes of k = 256p + 32q + 8g
+ *                                    .. +7 (q = 0..3), bytes [1024 + 16l + 4q,
+ *                                    +4) the same with k + 128
+ *          bytes [2048+16r, +16)     the 8 fp16 scales of row 16t+r, blocks
+ *                                    8p .. 8p+7
+ * Rows past N and k past K are zero codes with zero scales.  This is the
+ * order in which the matrix cores consume operands, so each wave streams
+ * 1 KiB-contiguous loads and decodes every weight once.  Matrices stacked
+ * along N (fused Q/K/V, gate||up) are just more rows.
  * Activations: bf16 bit patterns (uint16), row-major with a row stride in
  * elements; accumulation is fp32.
  */
@@ -67,7 +83,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 1
+#define MTP_ABI_VERSION 2
 
 enum {
   MTP_OK = 0,
@@ -86,28 +102,61 @@ enum { MTP_FMT_NVFP4 = 1, MTP_FMT_Q4_0 = 2 };
 #define MTP_MAX_M 16
 
 /*
+ * Bytes of one packed K x N matrix: ceil(N/16) * ceil(K/256) * 2304.
+ * Returns 0 for N < 1 or K not a positive multiple of 32.
+ */
+size_t mtp_packed_weight_bytes(int N, int K);
+
+/*
+ * Repack `count` stacked source matrices (codes [count][N][K/2], scales
+ * [count][N][K/16] bytes for nvfp4 or [count][N][K/32] fp16 for Q4_0) into
+ * the packed layout, matrix i at packed + i * mtp_packed_weight_bytes(N, K).
+ * A pure data movement (no arithmetic on weights); run once at load time.
+ *   codes, scales  device, 16-byte aligned; packed  device, 16-byte aligned,
+ *   not overlapping the sources.  count >= 1, N >= 1, K as above.
+ */
+int mtp_pack_weights(int format, int count, int N, int K, const uint8_t *codes,
+                     const void *scales, uint8_t *packed, void *stream);
+
+/*
  * Verify GEMM: y[m][n] = global_scale * sum_k x[m][k] * w(n, k) for
  * m < M, n < N, with every weight byte read once for all M rows.
  *   format       MTP_FMT_NVFP4 or MTP_FMT_Q4_0
  *   M            1..MTP_MAX_M rows (the committed token plus the drafts)
  *   N, K         output columns (>= 1) and reduction length (multiple of 32)
  *   x, ldx       bf16 [M][ldx], ldx >= K, ldx % 8 == 0, x 16-byte aligned
- *   codes,scales the weight matrix as described above
+ *   packed       the weight matrix in the packed layout (mtp_pack_weights),
+ *                16-byte aligned
  *   global_scale (host) fp32 multiplier applied to every weight
  *   y, ldy       fp32 output [M][ldy], ldy >= N; may be NULL if y_bf16 is set
  *   y_bf16,ldyb  optional bf16 copy of y (round to nearest even) [M][ldyb];
  *                may be NULL.  At least one of y and y_bf16 must be non-NULL.
- *   ws, ws_bytes workspace of at least mtp_gemm_workspace_bytes(M, N, K)
- *                bytes (may be NULL when that is 0)
- * Accuracy: |y - exact| <= 1e-3 * sum_k |x * w| + 1e-5 (fp32 accumulation);
- * results are deterministic and do not depend on M for a given row.
+ *   ws, ws_bytes workspace of at least mtp_gemm_workspace_bytes(N, K) bytes
+ *                (NULL allowed when that is 0), 256-byte aligned.  It holds
+ *                arrival counters that must be ZERO before its first use
+ *                (fill it with zeros once); every call leaves them zero
+ *                again.  Between GEMM calls nothing else may write it, and
+ *                calls sharing it must be ordered on one stream.
+ * Accuracy: |y - exact| <= 1e-3 * sum_k |x * w| + 1e-5 (fp32 accumulation).
+ * Results are deterministic, and row m's result depends only on x[m] and W
+ * (not on M or the other rows): the K split is a function of (N, K) alone.
  */
 int mtp_verify_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t ldx,
-                    const uint8_t *codes, const void *scales, float global_scale, float *y,
-                    int64_t ldy, uint16_t *y_bf16, int64_t ldyb, void *ws, size_t ws_bytes,
-                    void *stream);
+                    const uint8_t *packed, float global_scale, float *y, int64_t ldy,
+                    uint16_t *y_bf16, int64_t ldyb, void *ws, size_t ws_bytes, void *stream);
 
-size_t mtp_gemm_workspace_bytes(int M, int N, int K);
+/* Workspace bytes for mtp_verify_gemm on an N x K matrix, any M (may be 0). */
+size_t mtp_gemm_workspace_bytes(int N, int K);
+
+/*
+ * Diagnostic: the launch shape mtp_verify_gemm uses for (format, M, N, K).
+ * Writes min(n, 13) int32 values to host array `info`: tiles T (16 rows),
+ * pairs P (256 K), K slices S, pairs per slice, slices per workgroup J,
+ * workgroups per tile group KG, tiles per workgroup TW, tile groups, resident
+ * workgroups per K group, grid size, threads per workgroup, dynamic LDS bytes,
+ * workspace bytes this M needs.  Enqueues nothing.
+ */
+int mtp_gemm_plan_info(int format, int M, int N, int K, int32_t *info, int n);
 
 /*
  * Routed MoE verify pass for T token rows, each routed to `topk` of E
@@ -124,21 +173,20 @@ size_t mtp_gemm_workspace_bytes(int M, int N, int K);
  *   x               bf16 [T][H] (row stride H), 16-byte aligned
  *   topk_ids        int32 [T][topk]; an id outside [0, E) contributes nothing
  *   topk_w          fp32 [T][topk]
- *   gu_codes/gu_scales  expert e at byte offset e*2F*H/2 (codes) and
- *                   e*2F*(H/bs)*sizeof(scale) (scales), bs = 16 or 32
+ *   gu_packed       the E gate||up matrices (N = 2F rows, K = H), packed
+ *                   and stacked: expert e at e * mtp_packed_weight_bytes(2F, H)
  *   gu_global       device fp32 [E] per-expert global scales, or NULL (1.0)
- *   dn_codes/dn_scales/dn_global  the same for the down projections (K = F,
- *                   N = H)
+ *   dn_packed/dn_global  the same for the down projections (N = H, K = F),
+ *                   expert e at e * mtp_packed_weight_bytes(H, F)
  *   out             fp32 [T][H]
  *   h_out           optional bf16 [T*topk][F] copy of h (pair p = t*topk+s;
  *                   rows of out-of-range ids are zero); may be NULL
  *   ws, ws_bytes    at least mtp_moe_workspace_bytes(T, H, F, E, topk)
  */
 int mtp_verify_moe(int format, int T, int H, int F, int E, int topk, const uint16_t *x,
-                   const int32_t *topk_ids, const float *topk_w, const uint8_t *gu_codes,
-                   const void *gu_scales, const float *gu_global, const uint8_t *dn_codes,
-                   const void *dn_scales, const float *dn_global, float *out, uint16_t *h_out,
-                   void *ws, size_t ws_bytes, void *stream);
+                   const int32_t *topk_ids, const float *topk_w, const uint8_t *gu_packed,
+                   const float *gu_global, const uint8_t *dn_packed, const float *dn_global,
+                   float *out, uint16_t *h_out, void *ws, size_t ws_bytes, void *stream);
 
 size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk);
 

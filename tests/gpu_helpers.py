@@ -26,7 +26,14 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def gemm_gpu(bv, w: dict, x: np.ndarray, ldx_pad: int = 0, ldy_pad: int = 0, want_bf16=False):
+def pack_gpu(bv, w: dict, count: int = 1) -> torch.Tensor:
+    """Device copy of the source-layout weights of `w`, packed by the library."""
+    return bv.pack_weights(w["format"], dev(w["codes"]), dev(w["scales"]), w["N"], w["K"],
+                           count=count)
+
+
+def gemm_gpu(bv, w: dict, x: np.ndarray, ldx_pad: int = 0, ldy_pad: int = 0, want_bf16=False,
+             packed=None):
     """Run mtp_verify_gemm on device copies of (w, x); returns host y (and
     y_bf16 bits)."""
     M, K = x.shape
@@ -39,8 +46,9 @@ def gemm_gpu(bv, w: dict, x: np.ndarray, ldx_pad: int = 0, ldy_pad: int = 0, wan
         xd = dev(x)
     y = torch.full((M, N + ldy_pad), float("nan"), dtype=torch.float32, device=DEV)
     yb = torch.zeros((M, N + ldy_pad), dtype=torch.int16, device=DEV) if want_bf16 else None
-    bv.verify_gemm(w["format"], xd if not ldx_pad else xd, dev(w["codes"]), dev(w["scales"]), N,
-                   K, float(w.get("g", 1.0)), y=y, y_bf16=yb)
+    if packed is None:
+        packed = pack_gpu(bv, w)
+    bv.verify_gemm(w["format"], xd, packed, N, K, float(w.get("g", 1.0)), y=y, y_bf16=yb)
     yh = host(y)[:, :N].astype(np.float64)
     if want_bf16:
         return yh, host(yb)[:, :N].view(np.uint16)

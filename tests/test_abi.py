@@ -32,14 +32,23 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bv.abi_version() == 1
+    assert bv.abi_version() == 2
+
+
+def test_packed_sizes():
+    # one 2304-byte block per (16 rows, 256 K): codes 16*256/2 + scales 256
+    assert bv.packed_weight_bytes(14336, 4096) == 14336 * 4096 // 2 + 14336 * 4096 // 16
+    assert bv.packed_weight_bytes(1, 32) == 2304
+    assert bv.packed_weight_bytes(17, 288) == 4 * 2304
+    assert bv.packed_weight_bytes(0, 32) == 0
+    assert bv.packed_weight_bytes(16, 48) == 0
 
 
 def test_workspace_queries():
-    assert bv.gemm_workspace_bytes(8, 262144, 5376) == 0          # no K split needed
-    assert bv.gemm_workspace_bytes(8, 5120, 17408) > 0            # long K is split
-    assert bv.gemm_workspace_bytes(0, 10, 32) == 0
-    assert bv.gemm_workspace_bytes(1, 10, 33) == 0
+    assert bv.gemm_workspace_bytes(262144, 5376) == 0             # one K slice: no split
+    assert bv.gemm_workspace_bytes(5120, 17408) > 0               # long K is split
+    assert bv.gemm_workspace_bytes(0, 32) == 0
+    assert bv.gemm_workspace_bytes(10, 33) == 0
     assert bv.moe_workspace_bytes(8, 2048, 768, 128, 8) > 8 * 8 * 2048 * 4
     assert bv.accept_workspace_bytes(8, 262144) > 0
     assert bv.accept_workspace_bytes(65, 10) == 0
@@ -51,22 +60,45 @@ FAKE_ODD = ctypes.c_void_p(0x10001)
 
 
 def gemm(**kw):
-    a = dict(fmt=1, M=4, N=64, K=256, x=FAKE, ldx=256, codes=FAKE, scales=FAKE, g=1.0, y=FAKE,
+    a = dict(fmt=1, M=4, N=64, K=256, x=FAKE, ldx=256, packed=FAKE, g=1.0, y=FAKE,
              ldy=64, yb=None, ldyb=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return bv.lib().mtp_verify_gemm(a["fmt"], a["M"], a["N"], a["K"], a["x"], a["ldx"],
-                                    a["codes"], a["scales"], a["g"], a["y"], a["ldy"], a["yb"],
+                                    a["packed"], a["g"], a["y"], a["ldy"], a["yb"],
                                     a["ldyb"], a["ws"], a["wsb"], a["stream"])
+
+
+BIG = dict(N=5120, K=17408, ldx=17408, ldy=5120)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(fmt=3), -4), (dict(M=0), -2), (dict(M=17), -2), (dict(K=100), -2), (dict(K=0), -2),
-    (dict(N=0), -2), (dict(x=None), -1), (dict(codes=None), -1), (dict(y=None), -1),
-    (dict(ldx=128), -2), (dict(ldx=260), -3), (dict(x=FAKE_ODD), -3), (dict(codes=FAKE_ODD), -3),
-    (dict(ldy=10), -2), (dict(N=5120, K=17408, ldx=17408, ldy=5120), -5),
+    (dict(N=0), -2), (dict(x=None), -1), (dict(packed=None), -1), (dict(y=None), -1),
+    (dict(ldx=128), -2), (dict(ldx=260), -3), (dict(x=FAKE_ODD), -3),
+    (dict(packed=FAKE_ODD), -3), (dict(ldy=10), -2), (BIG, -5),
+    (dict(BIG, ws=ctypes.c_void_p(0x100010), wsb=1 << 30), -3),
 ])
 def test_gemm_rejects_bad_arguments(kw, code):
     assert gemm(**kw) == code
+    assert bv.lib().mtp_last_error()
+
+
+def pack(**kw):
+    a = dict(fmt=1, count=1, N=64, K=256, codes=FAKE, scales=ctypes.c_void_p(0x20000),
+             packed=ctypes.c_void_p(0x40000), stream=None)
+    a.update(kw)
+    return bv.lib().mtp_pack_weights(a["fmt"], a["count"], a["N"], a["K"], a["codes"],
+                                     a["scales"], a["packed"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=0), -4), (dict(K=48), -2), (dict(N=0), -2), (dict(count=0), -2),
+    (dict(codes=None), -1), (dict(packed=None), -1), (dict(scales=FAKE_ODD), -3),
+    (dict(packed=ctypes.c_void_p(0x10100)), -2),            # overlaps the codes
+    (dict(count=1 << 20, N=1 << 20, K=4096), -2),           # more blocks than one launch
+])
+def test_pack_rejects_bad_arguments(kw, code):
+    assert pack(**kw) == code
     assert bv.lib().mtp_last_error()
 
 
@@ -98,12 +130,13 @@ def test_moe_rejects_bad_arguments():
     L = bv.lib()
     ws = ctypes.c_void_p(0x100000)
     need = bv.moe_workspace_bytes(8, 2048, 768, 128, 8)
-    args = [1, 8, 2048, 768, 128, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+    args = [1, 8, 2048, 768, 128, 8, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
             None, ws, need, None]
 
     def call(**kw):
         a = list(args)
-        idx = {"fmt": 0, "T": 1, "H": 2, "F": 3, "E": 4, "topk": 5, "x": 6, "gu": 9, "wsb": 18}
+        idx = {"fmt": 0, "T": 1, "H": 2, "F": 3, "E": 4, "topk": 5, "x": 6, "gu": 9, "dn": 11,
+               "wsb": 16}
         for k, v in kw.items():
             a[idx[k]] = v
         return L.mtp_verify_moe(*a)
@@ -115,4 +148,5 @@ def test_moe_rejects_bad_arguments():
     assert call(F=40) == -2
     assert call(x=None) == -1
     assert call(gu=None) == -1
+    assert call(dn=FAKE_ODD) == -3
     assert call(wsb=need - 1) == -5

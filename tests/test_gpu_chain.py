@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import DEV, assert_gemm_close, dev, gemm_gpu, host, log
+from gpu_helpers import DEV, assert_gemm_close, dev, gemm_gpu, host, log, pack_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,9 @@ def test_tiny_chained_verify_pass():
     # end to end on the GPU (bf16 intermediate written by the first GEMM)
     xg = dev(c["x"])
     yb = torch.empty((M, 2048), dtype=torch.int16, device=DEV)
-    bv.verify_gemm(W.FMT_NVFP4, xg, dev(c["w1"]["codes"]), dev(c["w1"]["scales"]), 2048, 2048,
-                   1.0, y_bf16=yb, want_fp32=False)
-    logits, _ = bv.verify_gemm(W.FMT_NVFP4, yb, dev(c["head"]["codes"]),
-                               dev(c["head"]["scales"]), V, 2048)
+    bv.verify_gemm(W.FMT_NVFP4, xg, pack_gpu(bv, c["w1"]), 2048, 2048, 1.0, y_bf16=yb,
+                   want_fp32=False)
+    logits, _ = bv.verify_gemm(W.FMT_NVFP4, yb, pack_gpu(bv, c["head"]), V, 2048)
     t, cnt, rb = bv.accept_greedy(logits, dev(c["drafts"]), 123)
     gpu = (host(t).tolist(), host(cnt).tolist(), int(host(rb)[0]))
     srt = np.sort(z_ref, axis=1)

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import assert_gemm_close, gemm_gpu, log
+from gpu_helpers import DEV, assert_gemm_close, dev, gemm_gpu, host, log, pack_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -85,10 +85,57 @@ def test_exact_regime_bitwise(fmt, M, N, K):
     assert np.array_equal(y, y_ref)
 
 
+def packed_reference(w):
+    """The packed layout, written out from its definition in mtp_verify.h."""
+    N, K, fmt = w["N"], w["K"], w["format"]
+    T, P = -(-N // 16), -(-K // 256)
+    codes = np.zeros((T * 16, P * 128), np.uint8)
+    codes[:N, :K // 2] = w["codes"]
+    if fmt == W.FMT_NVFP4:
+        sc = np.zeros((T * 16, P * 16), np.uint8)
+        sc[:N, :K // 16] = w["scales"]
+    else:
+        sc = np.zeros((T * 16, P * 8), np.uint16)
+        sc[:N, :K // 32] = w["scales"]
+    out = np.zeros((T, P, 2304), np.uint8)
+    for t in range(T):
+        for p in range(P):
+            blk = out[t, p]
+            for l in range(64):
+                r, g = l % 16, l // 16
+                row = 16 * t + r
+                k0 = 256 * p + 32 * g
+                if fmt == W.FMT_NVFP4:
+                    blk[16 * l:16 * l + 16] = codes[row, k0 // 2:k0 // 2 + 16]
+                    blk[1024 + 16 * l:1024 + 16 * l + 16] = codes[row, (k0 + 128) // 2:(k0 + 128) // 2 + 16]
+                    blk[2048 + 4 * l:2048 + 4 * l + 4] = [sc[row, k0 // 16], sc[row, k0 // 16 + 1],
+                                                          sc[row, (k0 + 128) // 16],
+                                                          sc[row, (k0 + 128) // 16 + 1]]
+                else:
+                    for h in range(2):
+                        for q in range(4):
+                            k = 256 * p + 128 * h + 32 * q + 8 * g
+                            o = 1024 * h + 16 * l + 4 * q
+                            blk[o:o + 4] = codes[row, k // 2:k // 2 + 4]
+                    if g == 0:
+                        blk[2048 + 16 * r:2048 + 16 * r + 16] = \
+                            sc[row, 8 * p:8 * p + 8].view(np.uint8)
+    return out.reshape(-1)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-def test_rows_do_not_depend_on_m(fmt):
-    # the M-row pass equals M single-row passes, bit for bit
-    N, K = 300, 2304
+@pytest.mark.parametrize("N,K", [(16, 256), (37, 96), (130, 1056)])
+def test_pack_matches_layout_definition(fmt, N, K):
+    w = weight(fmt, N, K, seed=11)
+    got = host(pack_gpu(bv, w))
+    assert np.array_equal(got, packed_reference(w))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(300, 2304), (2048, 4096)])
+def test_rows_do_not_depend_on_m(fmt, N, K):
+    # the M-row pass equals M single-row passes, bit for bit, also where the
+    # row count changes how the K slices are spread over workgroups
     w = weight(fmt, N, K, seed=5)
     x = W.rand_bf16(np.random.default_rng(6), (16, K))
     y16 = gemm_gpu(bv, w, x)
@@ -113,12 +160,20 @@ def test_strides_scale_and_bf16_output(fmt):
 
 
 def test_deterministic_across_calls():
-    N, K, M = 5120, 17408, 8          # split-K path
+    N, K, M = 5120, 17408, 8          # K split over workgroups
+    assert bv.gemm_plan_info(W.FMT_Q4_0, M, N, K)["KG"] > 1
     w = weight(W.FMT_Q4_0, N, K, seed=3)
     x = W.rand_bf16(np.random.default_rng(3), (M, K))
-    y1 = gemm_gpu(bv, w, x)
-    y2 = gemm_gpu(bv, w, x)
-    assert np.array_equal(y1, y2)
+    packed = pack_gpu(bv, w)
+    ws = bv.gemm_workspace(N, K, DEV)
+    xd = dev(x)
+    ys = []
+    for _ in range(3):                # one workspace: its counters must return to zero
+        y, _ = bv.verify_gemm(W.FMT_Q4_0, xd, packed, N, K, ws=ws)
+        ys.append(host(y).astype(np.float64))
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+    assert not host(ws)[:4 * 320].any()
+    y1 = ys[0]
     y_ref, b_ref = oracle.gemm(w, x, cols=np.arange(0, N, 7))
     assert_gemm_close(y1[:, ::7], y_ref, b_ref, "q4 down")
 

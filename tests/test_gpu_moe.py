@@ -27,9 +27,10 @@ def run_moe(cfg):
     h = torch.full((T * cfg["topk"], F), -1, dtype=torch.int16, device=DEV)
     gug = dev(gu["g"]) if gu.get("g") is not None else None
     dng = dev(dn["g"]) if dn.get("g") is not None else None
+    gup = bv.pack_weights(gu["format"], dev(gu["codes"]), dev(gu["scales"]), 2 * F, H, count=E)
+    dnp = bv.pack_weights(dn["format"], dev(dn["codes"]), dev(dn["scales"]), H, F, count=E)
     out, _ = bv.verify_moe(gu["format"], dev(cfg["x"]), dev(cfg["ids"]), dev(cfg["gw"]),
-                           dev(gu["codes"]), dev(gu["scales"]), dev(dn["codes"]),
-                           dev(dn["scales"]), E, F, gu_global=gug, dn_global=dng, h_out=h)
+                           gup, dnp, E, F, gu_global=gug, dn_global=dng, h_out=h)
     return host(out).astype(np.float64), host(h).view(np.uint16)
 
 
