@@ -11,6 +11,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
@@ -20,6 +22,12 @@ constexpr int kWave = 64;
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The same product on fp16 operands (same lane layout).
+__device__ __forceinline__ f32x4 mfma_16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
@@ -58,6 +66,40 @@ __device__ __forceinline__ u32x4 nvfp4_decode8(uint32_t codes, float scale) {
   r.y = pack_hi16(p1.x * scale, p1.y * scale);
   r.z = pack_hi16(p2.x * scale, p2.y * scale);
   r.w = pack_hi16(p3.x * scale, p3.y * scale);
+  return r;
+}
+
+// Eight E2M1 codes times an E4M3 scale held as fp16 in both halves of `s2`
+// -> eight fp16 values in element order.  The products carry at most six
+// significant bits and lie in [2^-10, 2688], so every result is exact in
+// fp16; the hardware decode and one packed multiply per two weights make
+// this half the vector work of the bf16 form.
+__device__ __forceinline__ u32x4 nvfp4_decode8_f16(uint32_t codes, f16x2 s2) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2);
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2);
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2);
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2);
+  return r;
+}
+
+// Eight bf16 values -> eight fp16 values (conversion toward zero).  Exact for
+// every bf16 value of magnitude in [2^-17, 65280], for zeros, infinities and
+// NaNs; smaller magnitudes lose at most 2^-24.  `ovf` is set when a finite
+// value lies beyond the fp16 range (|x| >= 65536).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v, uint32_t &ovf) {
+  u32x4 r;
+  uint32_t bad = 0;
+#define MTP_CVT_DWORD(c)                                                                    \
+  {                                                                                         \
+    const uint32_t lo = (v.c & 0x7FFFu) - 0x4780u, hi = ((v.c >> 16) & 0x7FFFu) - 0x4780u;  \
+    bad |= (uint32_t)(lo < 0x3800u) | (uint32_t)(hi < 0x3800u);                             \
+    r.c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v.c << 16), \
+                                                                 __uint_as_float(v.c & 0xFFFF0000u))); \
+  }
+  MTP_CVT_DWORD(x) MTP_CVT_DWORD(y) MTP_CVT_DWORD(z) MTP_CVT_DWORD(w)
+#undef MTP_CVT_DWORD
+  ovf |= bad;
   return r;
 }
 

@@ -64,7 +64,7 @@ template <typename Kernel>
 inline void allow_large_lds(Kernel *kernel) {
   static const bool done = [kernel] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 64);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 1024);
     (void)hipGetLastError();   // a refusal shows up as the launch's own error
     return true;
   }();
@@ -107,16 +107,23 @@ template <> struct Blk<MTP_FMT_Q4_0> {
   u32x4 s;      // the 8 fp16 scales of the lane's row for this pair
 };
 
+// Weights are read once per pass: streaming (non-temporal) loads keep them
+// from displacing the activations and partial sums in the caches.
+template <typename T>
+__device__ __forceinline__ T stream_load(const uint8_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T *>(p));
+}
+
 __device__ __forceinline__ void load_blk(Blk<MTP_FMT_NVFP4> &b, const uint8_t *p, int lane) {
-  b.c0 = *reinterpret_cast<const u32x4 *>(p + 16 * lane);
-  b.c1 = *reinterpret_cast<const u32x4 *>(p + kHalfBytes + 16 * lane);
-  b.s = *reinterpret_cast<const uint32_t *>(p + kScaleOff + 4 * lane);
+  b.c0 = stream_load<u32x4>(p + 16 * lane);
+  b.c1 = stream_load<u32x4>(p + kHalfBytes + 16 * lane);
+  b.s = stream_load<uint32_t>(p + kScaleOff + 4 * lane);
 }
 
 __device__ __forceinline__ void load_blk(Blk<MTP_FMT_Q4_0> &b, const uint8_t *p, int lane) {
-  b.c0 = *reinterpret_cast<const u32x4 *>(p + 16 * lane);
-  b.c1 = *reinterpret_cast<const u32x4 *>(p + kHalfBytes + 16 * lane);
-  b.s = *reinterpret_cast<const u32x4 *>(p + kScaleOff + 16 * (lane & 15));
+  b.c0 = stream_load<u32x4>(p + 16 * lane);
+  b.c1 = stream_load<u32x4>(p + kHalfBytes + 16 * lane);
+  b.s = stream_load<u32x4>(p + kScaleOff + 16 * (lane & 15));
 }
 
 __device__ __forceinline__ float half_lo(uint32_t v) {
@@ -145,6 +152,29 @@ __device__ __forceinline__ f32x4 compute_blk(f32x4 acc, const Blk<MTP_FMT_NVFP4>
   acc = mfma_16x16x32(xb[3], nvfp4_decode8(b.c1.w, s3), acc);
   return acc;
 }
+
+// The same on fp16 activations (staged as fp16), with an fp16 decode.
+__device__ __forceinline__ f32x4 compute_blk_f16(f32x4 acc, const Blk<MTP_FMT_NVFP4> &b,
+                                                 const uint8_t *xl) {
+  const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.s, 1.0f, false);
+  const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.s, 1.0f, true);
+  const f16x2 h0 = {s01.x, s01.x}, h1 = {s01.y, s01.y}, h2 = {s23.x, s23.x}, h3 = {s23.y, s23.y};
+  const u32x4 *xa = reinterpret_cast<const u32x4 *>(xl);
+  const u32x4 *xb = reinterpret_cast<const u32x4 *>(xl + 256);
+  acc = mfma_16x16x32_f16(xa[0], nvfp4_decode8_f16(b.c0.x, h0), acc);
+  acc = mfma_16x16x32_f16(xa[1], nvfp4_decode8_f16(b.c0.y, h0), acc);
+  acc = mfma_16x16x32_f16(xa[2], nvfp4_decode8_f16(b.c0.z, h1), acc);
+  acc = mfma_16x16x32_f16(xa[3], nvfp4_decode8_f16(b.c0.w, h1), acc);
+  acc = mfma_16x16x32_f16(xb[0], nvfp4_decode8_f16(b.c1.x, h2), acc);
+  acc = mfma_16x16x32_f16(xb[1], nvfp4_decode8_f16(b.c1.y, h2), acc);
+  acc = mfma_16x16x32_f16(xb[2], nvfp4_decode8_f16(b.c1.z, h3), acc);
+  acc = mfma_16x16x32_f16(xb[3], nvfp4_decode8_f16(b.c1.w, h3), acc);
+  return acc;
+}
+
+// (Q4_0 has no fp16 path; this declaration only satisfies the discarded branch.)
+template <typename B>
+__device__ f32x4 compute_blk_f16(f32x4 acc, const B &b, const uint8_t *xl);
 
 // Q4_0.  One MFMA per 32-block: lane (r, g) supplies slots 8g .. 8g+7 of
 // block q of the pair (code dword q % 4 of step q / 4), activations staged in
@@ -179,6 +209,8 @@ __device__ __forceinline__ f32x4 compute_blk(f32x4 acc, const Blk<MTP_FMT_Q4_0> 
   acc = q4_block(acc, b.c1.w, half_hi(b.s.w), xl + 448, ci + 112);
   return acc;
 }
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 // Byte offset of lane group g's activation fragment inside a pair slot.
 template <int FMT>
@@ -220,13 +252,18 @@ __device__ __forceinline__ float fin_at(const f32x4 *fin, int tw, int m, int c) 
 //             tile group's sums are final (only by the last-arriving
 //             workgroup when KG > 1); fin_at(fin, tw, m, c) is row m of
 //             column c (0..15) of slot tw.
-// Every thread of the workgroup calls run with the same arguments.
+// Every thread of the workgroup calls run with the same arguments;
+// sync_entry must be true when the workgroup ran the engine before (its LDS
+// may still be in use).
 template <int FMT, typename TileOf, typename Epi>
 __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
                                     const Plan &pl, const TileOf &tile_of, const Fixup &fx,
-                                    uint8_t *lds, Epi &&epi) {
+                                    uint8_t *lds, bool sync_entry, Epi &&epi) {
   const int nthreads = pl.TW * pl.J * kWave;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  // wave-uniform values are pinned to scalar registers so that branches on
+  // them stay scalar branches (no exec-masked both-ways execution)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4, r = lane & 15;
   const int tw = wave % pl.TW, j = wave / pl.TW;
   const int pa = pl.kg * pl.J * pl.ppj;               // first pair of the workgroup
@@ -236,6 +273,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   f32x4 *red = reinterpret_cast<f32x4 *>(cinit + cinit_floats(FMT, np));
   f32x4 *fin = red;   // slot tw is read only by wave (tw, 0) before it holds the sum
   __shared__ uint32_t last_flag;
+  __shared__ uint32_t wave_ovf[kMaxWaves];
 
   // this wave's slice: pairs [pa + js, pa + js + n), n may be 0
   const int js = min(np, j * pl.ppj);
@@ -268,9 +306,20 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     return p;
   };
 
-  __syncthreads();  // LDS may still be read by a previous call's epilogue
+  if (sync_entry) __syncthreads();  // LDS may still be read by a previous call's epilogue
 
-  // 1) activation loads, 2) weight prefetch, 3) activation stores to LDS.
+  // Activations are staged as fp16 for nvfp4 (exact for the bf16 values met
+  // in practice; see bf16x8_to_f16x8) and as bf16 in MFMA slot order for
+  // Q4_0.  If any staged nvfp4 activation exceeds the fp16 range the
+  // workgroup stages bf16 instead and takes the bf16 path.
+  uint32_t ovf = 0;
+  auto encode = [&](u32x4 v) -> u32x4 {
+    if constexpr (FMT == MTP_FMT_Q4_0) return interleave_halves(v);
+    else return bf16x8_to_f16x8(v, ovf);
+  };
+
+  // 1) activation loads, 2) activation stores to LDS, 3) weight prefetch:
+  // the few activation bytes must not queue behind the weight stream.
   // Vector i = u * nthreads + tid of the staged rows is (m, v) = divmod(i,
   // vpr); (m, v) advance incrementally so that no division sits between the
   // loads.  Every load reads a valid address (row 0 / the first staged
@@ -295,28 +344,32 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
       ++xm;
     }
   }
+#pragma unroll
+  for (int u = 0; u < kXU; ++u) {
+    const u32x4 val = encode(xv[u]);
+    if (xoff[u] >= 0) *reinterpret_cast<u32x4 *>(lds + xoff[u]) = val;
+  }
+  __builtin_amdgcn_sched_barrier(0);
   Blk<FMT> buf[kPP];
 #pragma unroll
   for (int i = 0; i < kPP; ++i) load_blk(buf[i], next_block(), lane);
-#pragma unroll
-  for (int u = 0; u < kXU; ++u) {
-    u32x4 val = xv[u];
-    if (FMT == MTP_FMT_Q4_0) val = interleave_halves(val);
-    if (xoff[u] >= 0) *reinterpret_cast<u32x4 *>(lds + xoff[u]) = val;
-  }
+  __builtin_amdgcn_sched_barrier(0);
   // rows that did not fit the first round (many rows on few waves)
   for (; xm < M; ) {
     const int k = k0 + xvi * 8;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (k < K) val = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k);
-    if (FMT == MTP_FMT_Q4_0) val = interleave_halves(val);
-    *reinterpret_cast<u32x4 *>(lds + xm * rowb + xvi * 16) = val;
+    *reinterpret_cast<u32x4 *>(lds + xm * rowb + xvi * 16) = encode(val);
     xvi += vstep;
     xm += rstep;
     if (xvi >= vpr) {
       xvi -= vpr;
       ++xm;
     }
+  }
+  {
+    const bool any = __builtin_amdgcn_ballot_w64(ovf != 0u) != 0ull;
+    if (lane == 0) wave_ovf[wave] = any ? 1u : 0u;
   }
   for (int i = threadIdx.x; i < M * 32; i += nthreads) {   // zero slot of every row
     const int m = i >> 5, v = i & 31;
@@ -346,22 +399,8 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   }
   __syncthreads();
 
-  const uint8_t *xrow = lds + (size_t)(r % M) * rowb + x_lane_offset<FMT>(g);
-  const float *crow = cinit + 4 * g;
-  for (int u = 0; u < pl.tg_count; ++u) {
-    const int tg = pl.tg_first + u * pl.tg_step;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int b0 = 0; b0 < nr; b0 += kPP) {
-#pragma unroll
-      for (int i = 0; i < kPP; ++i) {
-        const int st = b0 + i;
-        const int slot = (st < n) ? js + st : np;   // zero slot past the slice
-        acc = compute_blk(acc, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
-        load_blk(buf[i], next_block(), lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
+  // sum the slices of the tile group and hand it to the epilogue
+  auto finish_group = [&](int tg, f32x4 acc) {
     if (pl.KG == 1) {
       // add the J slices of each tile in slice order
       red[wave * kWave + lane] = acc;
@@ -387,7 +426,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
         last_flag = last;
       }
       __syncthreads();
-      if (last_flag) {
+      if (__builtin_amdgcn_readfirstlane(last_flag)) {
         if (j == 0 && tile >= 0) {
           const f32x4 *src = fx.part + (int64_t)tile * pl.S * kWave + lane;
           f32x4 t = agent_load(src);
@@ -398,6 +437,56 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
         epi(tg, fin);
       }
     }
+  };
+
+  uint32_t x_ovf = 0;
+  if (FMT == MTP_FMT_NVFP4)
+    for (int q = 0; q < pl.TW * pl.J; ++q) x_ovf |= wave_ovf[q];
+  bool use_f16 = FMT == MTP_FMT_NVFP4;
+  if (FMT == MTP_FMT_NVFP4 && __builtin_amdgcn_readfirstlane(x_ovf)) {
+    use_f16 = false;
+    for (int i = threadIdx.x; i < M * vpr; i += nthreads) {
+      const int m = i / vpr, v = i - m * vpr;
+      const int k = k0 + v * 8;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (k < K) val = *reinterpret_cast<const u32x4 *>(xs.row(m) + k);
+      *reinterpret_cast<u32x4 *>(lds + m * rowb + v * 16) = val;
+    }
+    __syncthreads();
+  }
+
+  const uint8_t *xrow = lds + (size_t)(r % M) * rowb + x_lane_offset<FMT>(g);
+  const float *crow = cinit + 4 * g;
+  auto tile_groups = [&](auto f16_tag) {
+    constexpr bool kF16 = decltype(f16_tag)::value;
+    for (int u = 0; u < pl.tg_count; ++u) {
+      const int tg = pl.tg_first + u * pl.tg_step;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int b0 = 0; b0 < nr; b0 += kPP) {
+#pragma unroll
+        for (int i = 0; i < kPP; ++i) {
+          const int st = b0 + i;
+          const int slot = (st < n) ? js + st : np;   // zero slot past the slice
+          if constexpr (kF16) acc = compute_blk_f16(acc, buf[i], xrow + slot * kSlotBytes);
+          else acc = compute_blk(acc, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
+          load_blk(buf[i], next_block(), lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      finish_group(tg, acc);
+    }
+  };
+  if constexpr (FMT == MTP_FMT_NVFP4) {
+    if (use_f16) {
+      tile_groups(BoolTag<true>{});
+    } else {
+      tile_groups(BoolTag<false>{});
+      // the stream's trailing loads are never consumed; retire them here so
+      // that no later code has to assume they are still outstanding
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  } else {
+    tile_groups(BoolTag<false>{});
   }
 }
 

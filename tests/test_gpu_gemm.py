@@ -159,6 +159,30 @@ def test_strides_scale_and_bf16_output(fmt):
     assert np.array_equal(yb, expect)
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_nvfp4_activations_outside_fp16_range(M):
+    # nvfp4 activations are staged as fp16 when every value fits; a value
+    # beyond the fp16 range sends the workgroup through the bf16 path, and
+    # magnitudes below the fp16 normal range stay within the tolerance
+    N, K = 200, 1536
+    w = weight(W.FMT_NVFP4, N, K, seed=12)
+    rng = np.random.default_rng(13)
+    xf = rng.normal(size=(M, K)).astype(np.float32)
+    xf[:, 5] = 3.0e5
+    xf[0, 700] = -2.5e34          # times |w| <= 2688 stays inside fp32
+    xf[:, 900:940] = 1.0e-30 * rng.normal(size=(M, 40))
+    xf[:, 1000:1040] = 3.0e-6 * rng.normal(size=(M, 40))
+    x = W.to_bf16_bits(xf)
+    y = gemm_gpu(bv, w, x)
+    y_ref, b_ref = oracle.gemm(w, x)
+    assert_gemm_close(y, y_ref, b_ref, "wide-range activations")
+    # only tiny values: fp16 path throughout
+    xs = W.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32) * 1e-5)
+    y = gemm_gpu(bv, w, xs)
+    y_ref, b_ref = oracle.gemm(w, xs)
+    assert_gemm_close(y, y_ref, b_ref, "tiny activations")
+
+
 def test_deterministic_across_calls():
     N, K, M = 5120, 17408, 8          # K split over workgroups
     assert bv.gemm_plan_info(W.FMT_Q4_0, M, N, K)["KG"] > 1
