@@ -1,28 +1,38 @@
 """Benchmark of the MTP verify pass on one MI355X.
 
-Headline: effective weight GB/s of the nvfp4 verify GEMM on the dense
-FFN-up shape (K=4096 -> N=14336), M = 8 draft rows, and the M = 1/2/4/8
-sweep with the M=8 / M=1 time ratio.  A step is one verify GEMM call over
-one batch of activations.
+Headline (one JSON line): effective weight GB/s of the nvfp4 verify GEMM on
+the dense FFN-up shape (K=4096 -> N=14336) with M = 8 rows, plus the
+M = 1/2/4/8 sweep and the M=8 / M=1 time ratio.  A step is one verify GEMM
+call over one batch of activations (this workload's whole pass).
+
+The same run also reports, as context next to the headline, the other
+steps of the verify pass at their own workloads:
+* the Q4_0 projections of one 27B-class decoder layer (M = 8),
+* the 5376 -> 262144 LM head (M = 8) and the greedy and rejection accept
+  steps on its logits,
+* the routed MoE pass (8 tokens, 128 experts, top-8, 2048 -> 768 -> 2048),
+  with its unique-expert bytes.
 
 Method:
-* R rotating copies of the weights (R * 33 MB >= 1 GiB, four times the
-  256 MiB Infinity Cache) so every step streams its weights from HBM;
-* the R calls are captured once in a HIP graph (torch.cuda.CUDAGraph) and
-  replayed, so host launch overhead does not leak into the timing;
-* K timed steps bracketed by torch.cuda.synchronize(); HIP events recorded
-  on the launch stream give the average duration per call;
-* effective GB/s = algorithmic weight bytes (4-bit codes + E4M3 scales,
+* weights are packed once (mtp_pack_weights, outside the timed region);
+* R rotating copies of the weights (R * bytes >= 1 GiB, four times the
+  256 MiB Infinity Cache) so every call streams its weights from HBM;
+* the calls are captured once in a HIP graph (torch.cuda.CUDAGraph) and
+  replayed; K timed steps are bracketed by torch.cuda.synchronize();
+* HIP events recorded on the launch stream around the timed replays give
+  the average duration per launch (including the gaps between launches);
+* effective GB/s = algorithmic weight bytes (4-bit codes + block scales,
   9/16 byte per weight) / time;
-* the CPU oracle (fp64, all host threads) runs the same workload once for
-  the baseline.
-Prints one JSON line.
+* the CPU oracle (fp64, 16 host threads at most) runs repeated passes of
+  the same workload for a bounded sample as the baseline.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,6 +46,9 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nvfp4_4096x14336_m8_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_verify_gemm_amd", "csrc", f)
+                  for f in ("engine.h", "device.h", "gemm.hip")]
 
 
 def parse():
@@ -46,91 +59,119 @@ def parse():
     ap.add_argument("--m", type=int, default=8, help="rows of the headline pass")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1/2/4 sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (Q4_0 layer, LM head + accept, MoE)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline GEMM only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for PMC scaling)")
     return ap.parse_args()
 
 
-class GemmRunner:
-    """R rotating weight copies of one nvfp4 matrix and a captured graph of
-    one verify call per copy."""
+def dev_bits(a: np.ndarray, dev) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev)
 
-    def __init__(self, bv, w, x, M, dev):
-        self.bv = bv
-        self.N, self.K, self.M = w["N"], w["K"], M
-        self.bytes_per_call = W.weight_bytes(self.N, self.K)
-        self.R = max(2, -(-ROTATE_BYTES // self.bytes_per_call))
-        codes = torch.from_numpy(w["codes"]).to(dev)
-        scales = torch.from_numpy(w["scales"]).to(dev)
-        packed = bv.pack_weights(bv.FMT_NVFP4, codes, scales, self.N, self.K)
-        del codes, scales
+
+def time_graph(calls, R, steps, warmup):
+    """Capture calls(0..R-1) in one graph; replay it so that about `steps`
+    calls are timed.  Returns (wall seconds, ms per call from HIP events,
+    calls timed)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(R):                 # warm the launch path outside capture
+            calls(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            calls(i)
+    reps = max(1, -(-steps // R))
+    for _ in range(max(1, -(-warmup // R))):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / (reps * R), reps * R
+
+
+class Gemm:
+    """R rotating packed copies of one matrix; one verify call per copy."""
+
+    def __init__(self, bv, fmt, codes, scales, N, K, x, dev, g=1.0):
+        self.bv, self.fmt, self.N, self.K, self.g = bv, fmt, N, K, g
+        self.bytes = W.weight_bytes(N, K)
+        self.R = max(2, -(-ROTATE_BYTES // self.bytes))
+        packed = bv.pack_weights(fmt, codes, scales, N, K)
         self.packed = [packed] + [packed.clone() for _ in range(self.R - 1)]
-        self.x = torch.from_numpy(np.ascontiguousarray(x[:M]).view(np.int16)).to(dev)
-        self.y = torch.empty((M, self.N), dtype=torch.float32, device=dev)
-        self.ws = bv.gemm_workspace(self.N, self.K, dev)
-        self.graphs = {}
+        self.x = x
+        self.y = torch.empty((x.shape[0], N), dtype=torch.float32, device=dev)
+        self.ws = bv.gemm_workspace(N, K, dev)
 
-    def call(self, i):
-        self.bv.verify_gemm(self.bv.FMT_NVFP4, self.x, self.packed[i % self.R], self.N, self.K,
-                            1.0, y=self.y, ws=self.ws)
-
-    def graph(self, n):
-        """A graph of n consecutive calls over the rotating copies."""
-        if n not in self.graphs:
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                for i in range(n):          # warm the launch path outside capture
-                    self.call(i)
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(n):
-                    self.call(i)
-            self.graphs[n] = g
-        return self.graphs[n]
-
-    def run(self, steps):
-        full, tail = divmod(steps, self.R)
-        for _ in range(full):
-            self.graph(self.R).replay()
-        if tail:
-            self.graph(tail).replay()
-
-    def time(self, steps, warmup):
-        for n in {self.R, steps % self.R} - {0}:
-            self.graph(n)
-        self.run(warmup)
-        stream = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        self.run(steps)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ev_ms = e0.elapsed_time(e1)
-        return wall, ev_ms / steps
+    def __call__(self, i):
+        self.bv.verify_gemm(self.fmt, self.x, self.packed[i % self.R], self.N, self.K, self.g,
+                            y=self.y, ws=self.ws)
 
 
-def cpu_baseline(cfg, M):
+def gemm_from_host(bv, w, x, M, dev):
+    return Gemm(bv, w["format"], dev_bits(w["codes"], dev), dev_bits(w["scales"], dev), w["N"],
+                w["K"], dev_bits(x[:M], dev), dev, float(w.get("g", 1.0)))
+
+
+def cpu_baseline(cfg, M, budget_s=1.5):
+    """The oracle as it stands, on repeated whole passes of the workload
+    until about budget_s of wall time (16 host threads at most)."""
     import oracle
     w = cfg["w"]
     x = cfg["x"][:M]
     threads = max(1, min(16, os.cpu_count() or 1))
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
+    oracle.gemm(w, x, nthreads=threads)                # load and warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
         oracle.gemm(w, x, nthreads=threads)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
-    return {"value": round(W.weight_bytes(w["N"], w["K"]) / t / 1e9, 4), "unit": "GB/s",
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= budget_s:
+            break
+    return {"value": round(W.weight_bytes(w["N"], w["K"]) * reps / t / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"whole workload (M={M}, K={w['K']}, N={w['N']}), fp64 serial sums with "
-                      f"|x*w| bound, {threads} threads, median of 3 runs of {t:.2f}s"}
+            "sample": f"{reps} whole passes of the workload (M={M}, K={w['K']}, N={w['N']}, "
+                      f"fp64 sums with the |x*w| bound) in {t:.2f} s wall on {threads} threads "
+                      f"(about {t * threads:.0f} CPU-seconds)"}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return float(m.group(1))
 
 
 def copy_calibration(dev):
@@ -145,6 +186,91 @@ def copy_calibration(dev):
     return n
 
 
+def extra_q4_layer(bv, dev, steps, warmup):
+    cfg = W.config2(M=8)
+    out = {}
+    total_bytes, total_us = 0, 0.0
+    for name, p in cfg["proj"].items():
+        gm = gemm_from_host(bv, p["w"], p["x"], 8, dev)
+        _, ms, _ = time_graph(gm, gm.R, steps, warmup)
+        out[name] = {"N": gm.N, "K": gm.K, "us": round(ms * 1e3, 3),
+                     "gbs": round(gm.bytes / (ms * 1e-3) / 1e9, 1)}
+        total_bytes += gm.bytes
+        total_us += ms * 1e3
+        del gm
+        torch.cuda.empty_cache()
+    out["layer"] = {"bytes": total_bytes, "us": round(total_us, 3),
+                    "gbs": round(total_bytes / (total_us * 1e-6) / 1e9, 1)}
+    return out
+
+
+def extra_lm_head_and_accept(bv, dev, steps, warmup):
+    import oracle
+    c = W.config3_inputs(M=8)
+    M, V = c["M"], c["V"]
+    gm = gemm_from_host(bv, c["w"], c["x"], M, dev)
+    _, ms, _ = time_graph(gm, gm.R, max(20, steps // 20), max(4, warmup // 20))
+    out = {"lm_head": {"N": V, "K": c["K"], "us": round(ms * 1e3, 3),
+                       "gbs": round(gm.bytes / (ms * 1e-3) / 1e9, 1)}}
+    gm(0)
+    torch.cuda.synchronize()
+    logits = gm.y
+    am = np.array([oracle.argmax(r) for r in logits.cpu().numpy()], np.int32)
+    drafts = W.plant_drafts(am, c["L"], c["filler"], c["miss"], V)
+    dd = torch.from_numpy(drafts).to(dev)
+    q = torch.from_numpy(c["q"]).to(dev)
+    u = torch.from_numpy(c["u"]).to(dev)
+    outs = (torch.empty(M, dtype=torch.int32, device=dev),
+            torch.empty(2, dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int64, device=dev))
+    ws = torch.empty(bv.accept_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
+
+    def greedy(i):
+        bv.accept_greedy(logits, dd, 100, outs=outs, ws=ws)
+
+    def rejection(i):
+        bv.accept_rejection(logits, q, dd, u, c["temperature"], c["top_p"], 100, outs=outs,
+                            ws=ws)
+
+    _, ms_g, _ = time_graph(greedy, 1, max(50, steps // 4), 10)
+    _, ms_r, _ = time_graph(rejection, 1, max(50, steps // 4), 10)
+    out["accept_greedy"] = {"M": M, "V": V, "us": round(ms_g * 1e3, 3), "planted_L": c["L"]}
+    out["accept_rejection"] = {"M": M, "V": V, "us": round(ms_r * 1e3, 3),
+                               "temperature": c["temperature"], "top_p": c["top_p"]}
+    del gm
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_moe(bv, dev, steps, warmup):
+    c = W.config4()
+    T, E, F, H, topk = c["T"], c["E"], c["F"], c["H"], c["topk"]
+    gu, dn = c["gate_up"], c["down"]
+    per_expert = W.weight_bytes(2 * F, H) + W.weight_bytes(H, F)
+    R = max(2, -(-ROTATE_BYTES // (per_expert * E)))
+    gup = bv.pack_weights(gu["format"], dev_bits(gu["codes"], dev), dev_bits(gu["scales"], dev),
+                          2 * F, H, count=E)
+    dnp = bv.pack_weights(dn["format"], dev_bits(dn["codes"], dev), dev_bits(dn["scales"], dev),
+                          H, F, count=E)
+    gups = [gup] + [gup.clone() for _ in range(R - 1)]
+    dnps = [dnp] + [dnp.clone() for _ in range(R - 1)]
+    x = dev_bits(c["x"], dev)
+    ids = torch.from_numpy(c["ids"]).to(dev)
+    gw = torch.from_numpy(c["gw"]).to(dev)
+    out_t = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(bv.moe_workspace_bytes(T, H, F, E, topk), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        bv.verify_moe(gu["format"], x, ids, gw, gups[i % R], dnps[i % R], E, F, out=out_t, ws=ws)
+
+    _, ms, _ = time_graph(call, R, max(40, steps // 10), 10)
+    uniq = len(np.unique(c["ids"]))
+    ub = uniq * per_expert
+    return {"T": T, "E": E, "topk": topk, "H": H, "F": F, "unique_experts": uniq,
+            "unique_bytes": ub, "us": round(ms * 1e3, 3), "gbs": round(ub / (ms * 1e-3) / 1e9, 1),
+            "m1_gemv_bytes": topk * per_expert, "no_dedup_bytes": T * topk * per_expert}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -157,55 +283,67 @@ def main():
     cfg = W.config1(M=8)
     M = args.m
 
-    runner = GemmRunner(bv, cfg["w"], cfg["x"], M, dev)
-    wall, per_call_ms = runner.time(args.steps, args.warmup)
-    bytes_call = runner.bytes_per_call
-    value = bytes_call * args.steps / wall / 1e9
+    head = gemm_from_host(bv, cfg["w"], cfg["x"], M, dev)
+    wall, per_call_ms, ncalls = time_graph(head, head.R, args.steps, args.warmup)
+    bytes_call = head.bytes
+    value = bytes_call * ncalls / wall / 1e9
     achieved = bytes_call / (per_call_ms * 1e-3) / 1e9
+    plan = bv.gemm_plan_info(bv.FMT_NVFP4, M, cfg["w"]["N"], cfg["w"]["K"])
 
     sweep = {}
-    if not args.no_sweep:
+    if not args.no_sweep and not args.only_headline:
         for m in (1, 2, 4, 8):
             if m == M:
                 sweep[str(m)] = {"us_per_call": round(per_call_ms * 1e3, 3),
                                  "gbs": round(achieved, 1)}
                 continue
-            r = GemmRunner(bv, cfg["w"], cfg["x"], m, dev)
-            _, ms = r.time(args.steps, args.warmup)
+            r = gemm_from_host(bv, cfg["w"], cfg["x"], m, dev)
+            _, ms, _ = time_graph(r, r.R, args.steps, args.warmup)
             sweep[str(m)] = {"us_per_call": round(ms * 1e3, 3),
                              "gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1)}
             del r
             torch.cuda.empty_cache()
 
+    extra = {}
+    if not args.no_extra and not args.only_headline:
+        extra["q4_0_layer_27b_m8"] = extra_q4_layer(bv, dev, args.steps, args.warmup)
+        extra["lm_head_5376x262144_m8"] = extra_lm_head_and_accept(bv, dev, args.steps,
+                                                                   args.warmup)
+        extra["moe_8tok_128x_top8"] = extra_moe(bv, dev, args.steps, args.warmup)
+
     if args.copy_calibration:
         copy_calibration(dev)
 
+    traffic = pmc_traffic()
     out = {
         "metric": "effective weight GB/s (% of HBM peak) for nvfp4 verify GEMM at M=1/2/4/8",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": ncalls,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "ms_per_step": round(wall / ncalls * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": f"nvfp4 verify GEMM, dense FFN-up K=4096 -> N=14336, M={M} "
-                               f"bf16 rows, fp32 accumulate",
+                               f"bf16 rows (staged as fp16, exact), fp32 accumulate",
                    "M": M, "K": 4096, "N": 14336, "weight_bytes_per_call": bytes_call,
-                   "rotating_weight_copies": runner.R, "graph_replay": True},
+                   "rotating_weight_copies": head.R, "graph_replay": True,
+                   "plan": {k: plan[k] for k in ("S", "J", "KG", "TW", "grid", "threads")}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     "traffic": traffic},
     }
     if sweep:
         out["m_sweep"] = sweep
         if "1" in sweep and "8" in sweep:
             out["m8_over_m1_time"] = round(sweep["8"]["us_per_call"] / sweep["1"]["us_per_call"], 4)
-    if not args.no_cpu:
+    if extra:
+        out["other_workloads"] = extra
+    if not args.no_cpu and not args.only_headline:
         out["cpu_baseline"] = cpu_baseline(cfg, M)
     print(json.dumps(out), flush=True)
 
