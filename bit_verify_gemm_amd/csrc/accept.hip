@@ -143,15 +143,26 @@ struct RowState {
   double mass;      // nucleus mass S' (sum of e over the nucleus)
 };
 
-struct Global {
-  int32_t a;        // accepted drafts
-  int32_t row;      // row of the final draw
-  int32_t residual; // 1: draw from max(0, p' - q), else from p'
+// Radix-select state after s passes: the selected key prefix (top 8s bits)
+// and the mass of the entries strictly above it.
+struct SelState {
+  u64 above_lo, above_hi;
+  uint32_t prefix;
   int32_t pad;
 };
 
+// Inputs of the acceptance test of one draft: p'(x) and q(x).
+struct AccIn {
+  double px, qx;
+};
+
 struct Layout {
-  size_t maxp, hist, total, rows, glob, blk, gpart, bytes;
+  size_t maxp, zmax, hist, total, sel, rows, acc, glob, blk, gpart, bytes;
+};
+
+struct Global {
+  uint32_t arrived;  // blocks of the draw that have stored their sums
+  int32_t pad[3];
 };
 
 Layout layout(int M, int V) {
@@ -164,9 +175,12 @@ Layout layout(int M, int V) {
     return at;
   };
   L.maxp = take(sizeof(float) * M * nb);
+  L.zmax = take(sizeof(float) * M);
   L.hist = take(sizeof(u64) * 3 * kBins * 4 * M);
   L.total = take(sizeof(u64) * 2 * M);
+  L.sel = take(sizeof(SelState) * 4 * M);
   L.rows = take(sizeof(RowState) * M);
+  L.acc = take(sizeof(AccIn) * M);
   L.glob = take(sizeof(Global));
   L.blk = take(sizeof(u64) * 4 * nb);
   L.gpart = take(sizeof(float) * 2 * M * nb);
@@ -188,16 +202,34 @@ struct RejArgs {
   int32_t *tokens;
   int32_t *counts;
   int64_t *rollback;
-  float *maxp;
-  u64 *hist;     // [pass][row][bin][lo, hi, count]
-  u64 *total;    // [row][lo, hi]
+  float *maxp;      // [row][block] partial maxima
+  float *zmax;      // [row]
+  u64 *hist;        // [pass][row][bin][lo, hi, count]
+  u64 *total;       // [row][lo, hi]
+  SelState *sel;    // [pass][row]: state after `pass` selections (pass >= 1)
   RowState *rows;
+  AccIn *acc;       // [row]: inputs of draft row's acceptance test
   Global *glob;
-  u64 *blk;      // [block][res lo, res hi, e lo, e hi]
+  u64 *blk;         // [block][res lo, res hi, e lo, e hi]
 };
 
 __device__ __forceinline__ u64 *hist_at(const RejArgs &p, int pass, int row) {
   return p.hist + ((size_t)(pass * p.M + row) * kBins) * 3;
+}
+
+__device__ __forceinline__ Fx fx_shfl(const Fx &a, int src) {
+  return Fx{(u64)__shfl((long long)a.lo, src), (u64)__shfl((long long)a.hi, src)};
+}
+
+__device__ __forceinline__ Fx fx_shfl_up(const Fx &a, int d) {
+  return Fx{(u64)__shfl_up((long long)a.lo, d), (u64)__shfl_up((long long)a.hi, d)};
+}
+
+__device__ __forceinline__ Fx fx_sub(Fx a, const Fx &b) {
+  const u64 lo = a.lo - b.lo;
+  a.hi = a.hi - b.hi - (a.lo < b.lo ? 1ull : 0ull);
+  a.lo = lo;
+  return a;
 }
 
 // ---- greedy -------------------------------------------------------------------
@@ -208,6 +240,14 @@ __device__ __forceinline__ bool better(float v, int j, float bv, int bj) {
   if (isnan(v)) return false;
   if (isnan(bv)) return true;
   return v > bv || (v == bv && j < bj);
+}
+
+__device__ __forceinline__ void wave_best(float &bv, int &bj) {
+  for (int m = kWave / 2; m > 0; m >>= 1) {
+    const float ov = __shfl_xor(bv, m);
+    const int oj = __shfl_xor(bj, m);
+    if (better(ov, oj, bv, bj)) { bv = ov; bj = oj; }
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void greedy_partial(const float *z, int64_t ldl, int V,
@@ -221,11 +261,7 @@ __global__ __launch_bounds__(kBlock) void greedy_partial(const float *z, int64_t
     const float v = zr[j];
     if (better(v, j, bv, bj)) { bv = v; bj = j; }
   }
-  for (int m = kWave / 2; m > 0; m >>= 1) {
-    const float ov = __shfl_xor(bv, m);
-    const int oj = __shfl_xor(bj, m);
-    if (better(ov, oj, bv, bj)) { bv = ov; bj = oj; }
-  }
+  wave_best(bv, bj);
   __shared__ float sv[kBlock / kWave];
   __shared__ int sj[kBlock / kWave];
   if ((threadIdx.x & (kWave - 1)) == 0) { sv[threadIdx.x / kWave] = bv; sj[threadIdx.x / kWave] = bj; }
@@ -238,23 +274,28 @@ __global__ __launch_bounds__(kBlock) void greedy_partial(const float *z, int64_t
   }
 }
 
-__global__ __launch_bounds__(64) void greedy_final(const float *pv, const int *pj, int M, int nb,
-                                                   const int32_t *drafts, int64_t base_len,
-                                                   int32_t *tokens, int32_t *counts,
-                                                   int64_t *rollback) {
+// Row argmax from the block partials (one wave per row), then the prefix
+// match, tokens, counts and rollback.
+__global__ __launch_bounds__(kBlock) void greedy_final(const float *pv, const int *pj, int M, int nb,
+                                                       const int32_t *drafts, int64_t base_len,
+                                                       int32_t *tokens, int32_t *counts,
+                                                       int64_t *rollback) {
   __shared__ int g[64];
-  const int row = threadIdx.x;
-  if (row < M) {
+  __shared__ int d[64];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int row = wave; row < M; row += kBlock / kWave) {
     float bv = __int_as_float(0x7FC00000);
     int bj = 0x7FFFFFFF;
-    for (int b = 0; b < nb; ++b)
+    for (int b = lane; b < nb; b += kWave)
       if (better(pv[row * nb + b], pj[row * nb + b], bv, bj)) { bv = pv[row * nb + b]; bj = pj[row * nb + b]; }
-    g[row] = (bj == 0x7FFFFFFF) ? 0 : bj;  // all-NaN row: index 0
+    wave_best(bv, bj);
+    if (lane == 0) g[row] = (bj == 0x7FFFFFFF) ? 0 : bj;  // all-NaN row: index 0
   }
+  if (threadIdx.x < M - 1) d[threadIdx.x] = drafts[threadIdx.x];
   __syncthreads();
   if (threadIdx.x == 0) {
     int a = 0;
-    while (a < M - 1 && drafts[a] == g[a]) ++a;
+    while (a < M - 1 && d[a] == g[a]) ++a;
     for (int i = 0; i < M; ++i) tokens[i] = (i <= a) ? g[i] : -1;
     counts[0] = a;
     counts[1] = a + 1;
@@ -268,12 +309,6 @@ __device__ __forceinline__ double e_of(float z, float zmax, double T) {
   return exp(((double)z - (double)zmax) / T);
 }
 
-__device__ __forceinline__ float row_max_from_partials(const RejArgs &p, int row) {
-  float m = -__builtin_inff();
-  for (int b = 0; b < p.nb; ++b) m = fmaxf(m, p.maxp[row * p.nb + b]);
-  return m;
-}
-
 // Nucleus threshold in fixed point: top_p * S (at least one unit, so that
 // top_p <= 0 keeps exactly the first entry).
 __device__ __forceinline__ Fx threshold(const RejArgs &p, int row) {
@@ -283,40 +318,53 @@ __device__ __forceinline__ Fx threshold(const RejArgs &p, int row) {
   return t;
 }
 
-// Walk the bins of one pass from the top: the chosen bin is the first whose
-// inclusion brings the mass to the threshold (or the lowest occupied bin if
-// rounding never gets there).  `above` is updated to the mass strictly above.
-__device__ int select_bin(const u64 *h, const Fx &thr, Fx &above) {
-  Fx cum = above;
-  int last = -1;
-  Fx last_above = cum;
-  for (int b = kBins - 1; b >= 0; --b) {
-    const u64 cnt = h[3 * b + 2];
-    if (!cnt) continue;
-    const Fx mass = Fx{h[3 * b], h[3 * b + 1]};
-    const Fx next = fx_sum(cum, mass);
-    if (fx_ge(next, thr)) {
-      above = cum;
-      return b;
+// One radix-select step, run by all lanes of one wave over a 256-bin
+// histogram in LDS (h[3b] mass lo, h[3b+1] mass hi, h[3b+2] count).  Walking
+// from the top bin down, the chosen bin is the first whose inclusion brings
+// the mass to `thr`; if rounding never gets there, the lowest occupied bin.
+// `above` enters as the mass above the histogram's range and leaves as the
+// mass strictly above the chosen bin.  Lane L covers bins 255-4L .. 252-4L.
+__device__ int select_bin_wave(const u64 *h, const Fx &thr, Fx &above) {
+  const int lane = threadIdx.x & (kWave - 1);
+  Fx m[4];
+  u64 c[4];
+  Fx lsum = fx_zero();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = kBins - 1 - 4 * lane - i;
+    m[i] = Fx{h[3 * b], h[3 * b + 1]};
+    c[i] = h[3 * b + 2];
+    fx_add(lsum, m[i]);
+  }
+  Fx incl = lsum;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const Fx o = fx_shfl_up(incl, off);
+    if (lane >= off) fx_add(incl, o);
+  }
+  Fx cum = fx_sum(above, fx_sub(incl, lsum));   // mass of all higher bins
+  int found = -1, last = -1;
+  Fx found_above = fx_zero(), last_above = fx_zero();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (c[i]) {
+      const Fx next = fx_sum(cum, m[i]);
+      if (found < 0 && fx_ge(next, thr)) { found = kBins - 1 - 4 * lane - i; found_above = cum; }
+      last = kBins - 1 - 4 * lane - i;
+      last_above = cum;
+      cum = next;
     }
-    last = b;
-    last_above = cum;
-    cum = next;
   }
-  above = last_above;
-  return last;
-}
-
-// Selected key prefix after `passes` passes (8 bits per pass, from the top).
-__device__ uint32_t prefix_after(const RejArgs &p, int row, int passes, Fx &above) {
-  const Fx thr = threshold(p, row);
-  above = fx_zero();
-  uint32_t prefix = 0;
-  for (int s = 0; s < passes; ++s) {
-    const int b = select_bin(hist_at(p, s, row), thr, above);
-    prefix = (prefix << 8) | (uint32_t)(b < 0 ? 0 : b);
+  const u64 hit = __ballot(found >= 0);
+  if (hit) {
+    const int src = __ffsll((long long)hit) - 1;
+    above = fx_shfl(found_above, src);
+    return __shfl(found, src);
   }
-  return prefix;
+  const u64 occ = __ballot(last >= 0);
+  if (!occ) return -1;
+  const int src = 63 - __clzll((long long)occ);
+  above = fx_shfl(last_above, src);
+  return __shfl(last, src);
 }
 
 // Row maxima (partial) and zeroing of this call's accumulators.
@@ -341,22 +389,58 @@ __global__ __launch_bounds__(kBlock) void rej_rowmax(RejArgs p) {
     hist_at(p, pass, row)[w] = 0ull;
   }
   if (b == 0 && threadIdx.x < 2) p.total[2 * row + threadIdx.x] = 0ull;
+  if (b == 0 && row == 0 && threadIdx.x == 0) p.glob->arrived = 0u;
 }
 
-// Radix pass `pass` (0..3): histogram of e-mass by key digit for the entries
-// matching the prefix selected so far; pass 0 also sums the row's total mass.
+// Radix pass `pass` (0..3).  Pass 0 reduces the row maximum and sums the
+// row's total mass; pass s >= 1 first takes selection step s on histogram
+// s-1 (every block computes the same result, block 0 records it for the
+// next pass).  Then the pass histograms, by key digit, the mass of the
+// entries that match the selected prefix and have non-zero mass.
 __global__ __launch_bounds__(kBlock) void rej_pass(RejArgs p, int pass, int with_hist) {
   __shared__ u64 sh[kBins * 3];
+  __shared__ u64 hprev[kBins * 3];
   __shared__ Fx red[kBlock / kWave];
+  __shared__ float s_zmax;
+  __shared__ uint32_t s_prefix;
   const int b = blockIdx.x, row = blockIdx.y;
-  const float zmax = row_max_from_partials(p, row);
-  uint32_t prefix = 0;
-  if (pass > 0) {
-    Fx above;
-    prefix = prefix_after(p, row, pass, above);
-  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   for (int i = threadIdx.x; i < kBins * 3; i += kBlock) sh[i] = 0ull;
+  if (pass == 0) {
+    if (wave == 0) {
+      float m = -__builtin_inff();
+      for (int k = lane; k < p.nb; k += kWave) m = fmaxf(m, p.maxp[row * p.nb + k]);
+      for (int s = kWave / 2; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
+      if (lane == 0) {
+        s_zmax = m;
+        s_prefix = 0;
+        if (b == 0) p.zmax[row] = m;
+      }
+    }
+  } else {
+    const u64 *hp = hist_at(p, pass - 1, row);
+    for (int i = threadIdx.x; i < kBins * 3; i += kBlock) hprev[i] = hp[i];
+    __syncthreads();
+    if (wave == 0) {
+      Fx above = fx_zero();
+      uint32_t prefix = 0;
+      if (pass > 1) {
+        const SelState st = p.sel[(pass - 1) * p.M + row];
+        above = Fx{st.above_lo, st.above_hi};
+        prefix = st.prefix;
+      }
+      const int bin = select_bin_wave(hprev, threshold(p, row), above);
+      prefix = (prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
+      if (lane == 0) {
+        s_prefix = prefix;
+        s_zmax = p.zmax[row];
+        if (b == 0) p.sel[pass * p.M + row] = SelState{above.lo, above.hi, prefix, 0};
+      }
+    }
+  }
   __syncthreads();
+  const float zmax = s_zmax;
+  const uint32_t prefix = s_prefix;
   const float *zr = p.z + (int64_t)row * p.ldl;
   const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
   const int shift = 24 - 8 * pass;
@@ -366,6 +450,7 @@ __global__ __launch_bounds__(kBlock) void rej_pass(RejArgs p, int pass, int with
     const uint32_t key = fkey(zj);
     if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
     const Fx e = to_fx(e_of(zj, zmax, p.T));
+    if (!fx_nonzero(e)) continue;     // below the fixed-point resolution: no mass
     if (pass == 0) fx_add(tot, e);
     if (with_hist) {
       const int d = (key >> shift) & 0xFF;
@@ -373,7 +458,7 @@ __global__ __launch_bounds__(kBlock) void rej_pass(RejArgs p, int pass, int with
       if (e.lo) {
         const u64 old = atomicAdd(bin, e.lo);
         atomicAdd(bin + 1, e.hi + ((old + e.lo < old) ? 1ull : 0ull));
-      } else if (e.hi) {
+      } else {
         atomicAdd(bin + 1, e.hi);
       }
       atomicAdd(bin + 2, 1ull);
@@ -432,60 +517,78 @@ __device__ __forceinline__ bool in_nucleus(const RowState &rs, float z, int j) {
   return k > rs.kappa || (k == rs.kappa && j <= rs.cutoff);
 }
 
-// Per-row nucleus description, then the sequential acceptance tests.
-__global__ __launch_bounds__(kBlock) void rej_decide(RejArgs p) {
-  for (int row = 0; row < p.M; ++row) {
-    RowState rs;
-    rs.zmax = row_max_from_partials(p, row);
-    const double S = fx_to_double(fx_load(p.total + 2 * row));
-    if (p.top_p >= 1.0) {
-      rs.all = 1; rs.kappa = 0; rs.cutoff = p.V; rs.mass = S;
-    } else {
-      Fx above;
-      const uint32_t kappa = prefix_after(p, row, 4, above);
-      const u64 *h3 = hist_at(p, 3, row) + 3 * (kappa & 0xFF);
-      const u64 n = h3[2];
-      const double ek = e_of(key_to_float(kappa), rs.zmax, p.T);
-      const double above_d = fx_to_double(above);
-      const Fx thr = threshold(p, row);
-      const double thr_d = fx_to_double(thr);
-      double tt = ceil((thr_d - above_d) / ek);
-      u64 t = (tt < 1.0) ? 1ull : (tt >= (double)n ? n : (u64)tt);
-      rs.all = 0;
-      rs.kappa = kappa;
-      if (t >= n) {
-        rs.cutoff = p.V;
-      } else {
-        rs.cutoff = find_tth_tie(p.z + (int64_t)row * p.ldl, p.V, kappa, (int)t);
-      }
-      rs.mass = above_d + (double)t * ek;
-    }
-    if (threadIdx.x == 0) p.rows[row] = rs;
+// One block per row: the last selection step fixes the nucleus (kappa and
+// the tie cut), then the inputs of the row's acceptance test are taken.
+__global__ __launch_bounds__(kBlock) void rej_select(RejArgs p) {
+  __shared__ u64 hprev[kBins * 3];
+  __shared__ RowState s_rs;
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const float zmax = p.zmax[row];
+  const double S = fx_to_double(fx_load(p.total + 2 * row));
+  if (p.top_p >= 1.0) {
+    if (threadIdx.x == 0) s_rs = RowState{zmax, 0u, p.V, 1, S};
     __syncthreads();
+  } else {
+    const u64 *hp = hist_at(p, 3, row);
+    for (int i = threadIdx.x; i < kBins * 3; i += kBlock) hprev[i] = hp[i];
+    __syncthreads();
+    __shared__ uint32_t s_kappa;
+    __shared__ u64 s_t, s_n;
+    __shared__ double s_above;
+    if (wave == 0) {
+      const SelState st = p.sel[3 * p.M + row];
+      Fx above = Fx{st.above_lo, st.above_hi};
+      const Fx thr = threshold(p, row);
+      const int bin = select_bin_wave(hprev, thr, above);
+      const uint32_t kappa = (st.prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
+      if (lane == 0) {
+        const u64 n = hprev[3 * (kappa & 0xFF) + 2];
+        const double ek = e_of(key_to_float(kappa), zmax, p.T);
+        const double above_d = fx_to_double(above);
+        const double tt = ceil((fx_to_double(thr) - above_d) / ek);
+        const u64 t = (tt < 1.0) ? 1ull : (tt >= (double)n ? n : (u64)tt);
+        s_kappa = kappa;
+        s_t = t;
+        s_n = n;
+        s_above = above_d;
+        s_rs = RowState{zmax, kappa, p.V, 0, above_d + (double)t * ek};
+      }
+    }
+    __syncthreads();
+    if (s_t < s_n) {   // ties at the cut: the first t of them in index order are inside
+      const int cut = find_tth_tie(p.z + (int64_t)row * p.ldl, p.V, s_kappa, (int)s_t);
+      if (threadIdx.x == 0) s_rs.cutoff = cut;
+      __syncthreads();
+    }
   }
+  const RowState rs = s_rs;
   if (threadIdx.x == 0) {
-    int a = 0;
-    int residual = 0;
-    while (a < p.M - 1) {
-      const int x = p.drafts[a];
-      const RowState rs = p.rows[a];
+    p.rows[row] = rs;
+    if (row < p.M - 1) {
+      const int x = p.drafts[row];
       double px = 0.0, qx = 0.0;
       if (x >= 0 && x < p.V) {
-        const float zx = p.z[(int64_t)a * p.ldl + x];
+        const float zx = p.z[(int64_t)row * p.ldl + x];
         if (in_nucleus(rs, zx, x)) px = e_of(zx, rs.zmax, p.T) / rs.mass;
-        qx = (double)p.q[(int64_t)a * p.ldq + x];
+        qx = (double)p.q[(int64_t)row * p.ldq + x];
       }
-      if ((double)p.u[a] * qx < px) {
-        ++a;
-      } else {
-        residual = 1;
-        break;
-      }
+      p.acc[row] = AccIn{px, qx};
     }
-    p.glob->a = a;
-    p.glob->row = a;
-    p.glob->residual = residual;
   }
+}
+
+// Accepted drafts: the first row i < M-1 with u_i * q_i(x_i) >= p'_i(x_i)
+// stops the run (evaluated by every wave; wave-uniform result).
+__device__ __forceinline__ int accepted_run(const RejArgs &p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  bool reject = false;
+  if (lane < p.M - 1) {
+    const AccIn in = p.acc[lane];
+    reject = !((double)p.u[lane] * in.qx < in.px);
+  }
+  const u64 rej = __ballot(reject);
+  return rej ? __ffsll((long long)rej) - 1 : p.M - 1;
 }
 
 // Weights of the final draw for entry j of row `row`.
@@ -503,116 +606,158 @@ __device__ __forceinline__ void draw_weights(const RejArgs &p, const RowState &r
   }
 }
 
-__global__ __launch_bounds__(kBlock) void rej_draw_sums(RejArgs p) {
-  __shared__ Fx red[kBlock / kWave];
-  const Global gl = *p.glob;
-  const RowState rs = p.rows[gl.row];
-  const int b = blockIdx.x;
-  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
-  Fx sr = fx_zero(), se = fx_zero();
-  for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
-    Fx wr, we;
-    draw_weights(p, rs, gl.row, gl.residual != 0, j, wr, we);
-    fx_add(sr, wr);
-    fx_add(se, we);
+// Exclusive 128-bit prefix sums over the threads of the block (thread order);
+// also returns the block total.  `wsum` holds kBlock/kWave Fx.
+__device__ Fx fx_block_exclusive(Fx v, Fx *wsum, Fx &total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  Fx incl = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const Fx o = fx_shfl_up(incl, off);
+    if (lane >= off) fx_add(incl, o);
   }
-  sr = fx_block_sum(sr, red);
-  se = fx_block_sum(se, red);
-  if (threadIdx.x == 0) {
-    u64 *o = p.blk + 4 * b;
-    o[0] = sr.lo; o[1] = sr.hi; o[2] = se.lo; o[3] = se.hi;
+  __syncthreads();
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  Fx before = fx_zero();
+  total = fx_zero();
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    if (w < wave) fx_add(before, wsum[w]);
+    fx_add(total, wsum[w]);
   }
+  return fx_sum(before, fx_sub(incl, v));
 }
 
-// Smallest j with prefix weight > u * total (index order); the last j with a
-// positive weight if rounding passes the end.  Writes the committed run.
-__global__ __launch_bounds__(kBlock) void rej_draw_final(RejArgs p) {
-  __shared__ Fx part[kBlock];
-  __shared__ int s_blk, s_use_res, s_pick;
+constexpr int kDrawPer = 8;   // entries per thread in the final draw
+
+// Draw weights: every block sums its chunk for the row of the final draw
+// (row a of the first rejection, or the last row for the bonus); the last
+// block to finish picks the smallest j with prefix weight > u * total
+// (index order), or the last j with a positive weight if rounding passes
+// the end, and writes the committed run.
+__global__ __launch_bounds__(kBlock) void rej_draw(RejArgs p) {
+  __shared__ Fx wsum[kBlock / kWave];
+  __shared__ Fx sb_res[kMaxBlocksPerRow], sb_e[kMaxBlocksPerRow];
+  __shared__ uint32_t s_last;
+  __shared__ int s_blk, s_mode, s_use_res, s_pick;
   __shared__ Fx s_before, s_target;
-  const Global gl = *p.glob;
-  const RowState rs = p.rows[gl.row];
+  const int a = accepted_run(p);
+  const int residual = a < p.M - 1;
+  const RowState rs = p.rows[a];
+  const int b = blockIdx.x;
+  {
+    const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
+    Fx sr = fx_zero(), se = fx_zero();
+    for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
+      Fx wr, we;
+      draw_weights(p, rs, a, residual != 0, j, wr, we);
+      fx_add(sr, wr);
+      fx_add(se, we);
+    }
+    sr = fx_block_sum(sr, wsum);
+    se = fx_block_sum(se, wsum);
+    if (threadIdx.x == 0) {
+      u64 *o = p.blk + 4 * b;
+      __hip_atomic_store(o + 0, sr.lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(o + 1, sr.hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(o + 2, se.lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(o + 3, se.hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);   // the block sums are stored before arriving
+      const uint32_t old =
+          __hip_atomic_fetch_add(&p.glob->arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (uint32_t)(p.nb - 1);
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(s_last)) return;   // whole block
+  }
+  // ---- the last block: the draw --------------------------------------------
+  for (int k = threadIdx.x; k < p.nb; k += kBlock) {
+    const u64 *o = p.blk + 4 * k;
+    sb_res[k] = Fx{__hip_atomic_load(o + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                   __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+    sb_e[k] = Fx{__hip_atomic_load(o + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                 __hip_atomic_load(o + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     Fx wres = fx_zero(), we = fx_zero();
-    for (int b = 0; b < p.nb; ++b) {
-      fx_add(wres, fx_load(p.blk + 4 * b));
-      fx_add(we, fx_load(p.blk + 4 * b + 2));
+    for (int k = 0; k < p.nb; ++k) {
+      fx_add(wres, sb_res[k]);
+      fx_add(we, sb_e[k]);
     }
-    const int use_res = gl.residual && fx_nonzero(wres);
+    const int use_res = residual && fx_nonzero(wres);
     const Fx W = use_res ? wres : we;
     const Fx target = to_fx((double)p.u[p.M - 1] * fx_to_double(W));
     Fx cum = fx_zero();
     int blk = -1, last_nz = -1;
     Fx last_before = fx_zero();
-    for (int b = 0; b < p.nb; ++b) {
-      const Fx s = fx_load(p.blk + 4 * b + (use_res ? 0 : 2));
+    for (int k = 0; k < p.nb; ++k) {
+      const Fx s = use_res ? sb_res[k] : sb_e[k];
       const Fx next = fx_sum(cum, s);
-      if (fx_gt(next, target)) { blk = b; break; }
-      if (fx_nonzero(s)) { last_nz = b; last_before = cum; }
+      if (fx_gt(next, target)) { blk = k; break; }
+      if (fx_nonzero(s)) { last_nz = k; last_before = cum; }
       cum = next;
     }
     s_use_res = use_res;
     s_target = target;
+    s_pick = p.V - 1;
     if (blk >= 0) {
+      s_mode = 0;            // the crossing lies in block blk
       s_blk = blk;
       s_before = cum;
-      s_pick = -1;
     } else {
-      s_blk = last_nz;       // rounding passed the end
+      s_mode = 1;            // rounding passed the end: last positive entry of that block
+      s_blk = last_nz;
       s_before = last_before;
-      s_pick = -2;
+    }
+    p.glob->arrived = 0u;     // ready for the next call
+  }
+  __syncthreads();
+  const bool exact = s_mode == 0;
+  const int blk = s_blk;
+  if (blk >= 0) {
+    const int j0 = blk * p.chunk, j1 = min(p.V, j0 + p.chunk);
+    const bool use_res = s_use_res != 0;
+    for (int base = j0; base < j1; base += kBlock * kDrawPer) {
+      // thread t holds entries base + kDrawPer*t .. +kDrawPer-1
+      Fx w[kDrawPer];
+      Fx mine = fx_zero();
+      const int jt = base + kDrawPer * threadIdx.x;
+#pragma unroll
+      for (int i = 0; i < kDrawPer; ++i) {
+        Fx wr = fx_zero(), we = fx_zero();
+        if (jt + i < j1) draw_weights(p, rs, a, residual != 0, jt + i, wr, we);
+        w[i] = use_res ? wr : we;
+        fx_add(mine, w[i]);
+      }
+      Fx total;
+      const Fx before = fx_sum(s_before, fx_block_exclusive(mine, wsum, total));
+      if (exact) {
+        // the thread whose range crosses the target picks inside it
+        if (!fx_gt(before, s_target) && fx_gt(fx_sum(before, mine), s_target)) {
+          Fx c = before;
+          for (int i = 0; i < kDrawPer; ++i) {
+            fx_add(c, w[i]);
+            if (fx_gt(c, s_target)) { s_pick = jt + i; break; }
+          }
+        }
+      } else {
+        int lastj = -1;
+        for (int i = 0; i < kDrawPer; ++i)
+          if (fx_nonzero(w[i])) lastj = jt + i;
+        if (lastj >= 0) atomicMax(&s_pick, lastj);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) s_before = fx_sum(s_before, total);
+      __syncthreads();
     }
   }
   __syncthreads();
-  const int blk = s_blk;
-  int pick = p.V - 1;
-  if (blk >= 0) {
-    const int j0 = blk * p.chunk, j1 = min(p.V, j0 + p.chunk);
-    const int per = (j1 - j0 + kBlock - 1) / kBlock;
-    const int a0 = j0 + threadIdx.x * per, a1 = min(j1, a0 + per);
-    Fx mine = fx_zero();
-    for (int j = a0; j < a1; ++j) {
-      Fx wr, we;
-      draw_weights(p, rs, gl.row, gl.residual != 0, j, wr, we);
-      fx_add(mine, s_use_res ? wr : we);
-    }
-    part[threadIdx.x] = mine;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      if (s_pick == -1) {
-        Fx cum = s_before;
-        for (int i = 0; i < kBlock && s_pick == -1; ++i) {
-          const Fx next = fx_sum(cum, part[i]);
-          if (fx_gt(next, s_target)) {
-            const int b0 = j0 + i * per, b1 = min(j1, b0 + per);
-            for (int j = b0; j < b1; ++j) {
-              Fx wr, we;
-              draw_weights(p, rs, gl.row, gl.residual != 0, j, wr, we);
-              fx_add(cum, s_use_res ? wr : we);
-              if (fx_gt(cum, s_target)) { s_pick = j; break; }
-            }
-            if (s_pick == -1) s_pick = b1 - 1;
-          } else {
-            cum = next;
-          }
-        }
-        if (s_pick == -1) s_pick = j1 - 1;
-      } else {
-        // last entry with a positive weight in the last occupied block
-        s_pick = j1 - 1;
-        for (int j = j1 - 1; j >= j0; --j) {
-          Fx wr, we;
-          draw_weights(p, rs, gl.row, gl.residual != 0, j, wr, we);
-          if (fx_nonzero(s_use_res ? wr : we)) { s_pick = j; break; }
-        }
-      }
-    }
-    __syncthreads();
-    pick = s_pick;
+  const int pick = s_pick;
+  if (threadIdx.x < p.M) {
+    const int i = threadIdx.x;
+    p.tokens[i] = (i < a) ? p.drafts[i] : (i == a ? pick : -1);
   }
   if (threadIdx.x == 0) {
-    const int a = gl.a;
-    for (int i = 0; i < p.M; ++i) p.tokens[i] = (i < a) ? p.drafts[i] : (i == a ? pick : -1);
     p.counts[0] = a;
     p.counts[1] = a + 1;
     *p.rollback = p.base_len + a + 1;
@@ -636,8 +781,8 @@ hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
                      chunk, pv, pj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(greedy_final, dim3(1), dim3(64), 0, stream, pv, pj, M, nb, drafts, base_len,
-                     tokens, counts, rollback);
+  hipLaunchKernelGGL(greedy_final, dim3(1), dim3(kBlock), 0, stream, pv, pj, M, nb, drafts,
+                     base_len, tokens, counts, rollback);
   return hipGetLastError();
 }
 
@@ -654,9 +799,12 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   p.M = M; p.V = V; p.nb = blocks_per_row(V); p.chunk = (V + p.nb - 1) / p.nb;
   p.base_len = base_len; p.tokens = tokens; p.counts = counts; p.rollback = rollback;
   p.maxp = reinterpret_cast<float *>(w + L.maxp);
+  p.zmax = reinterpret_cast<float *>(w + L.zmax);
   p.hist = reinterpret_cast<u64 *>(w + L.hist);
   p.total = reinterpret_cast<u64 *>(w + L.total);
+  p.sel = reinterpret_cast<SelState *>(w + L.sel);
   p.rows = reinterpret_cast<RowState *>(w + L.rows);
+  p.acc = reinterpret_cast<AccIn *>(w + L.acc);
   p.glob = reinterpret_cast<Global *>(w + L.glob);
   p.blk = reinterpret_cast<u64 *>(w + L.blk);
   const dim3 rows_grid(p.nb, M);
@@ -665,9 +813,8 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   const int passes = with_hist ? 4 : 1;
   for (int pass = 0; pass < passes; ++pass)
     hipLaunchKernelGGL(rej_pass, rows_grid, dim3(kBlock), 0, stream, p, pass, with_hist);
-  hipLaunchKernelGGL(rej_decide, dim3(1), dim3(kBlock), 0, stream, p);
-  hipLaunchKernelGGL(rej_draw_sums, dim3(p.nb), dim3(kBlock), 0, stream, p);
-  hipLaunchKernelGGL(rej_draw_final, dim3(1), dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL(rej_select, dim3(M), dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL(rej_draw, dim3(p.nb), dim3(kBlock), 0, stream, p);
   return hipGetLastError();
 }
 
