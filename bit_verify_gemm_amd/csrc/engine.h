@@ -36,8 +36,9 @@ constexpr int kHalfBytes = 1024;
 constexpr int kScaleOff = 2048;
 constexpr int kSlotBytes = 512;   // one pair of one activation row in LDS (256 bf16)
 constexpr int kPP = 2;            // blocks in flight per wave
-constexpr int kMaxWaves = 16;
-constexpr int kMaxThreads = kMaxWaves * kWave;
+constexpr int kMaxWaves = 16;         // waves of all workgroups on one CU (<= 128 VGPRs)
+constexpr int kWgWaves = 8;           // waves of one workgroup at most
+constexpr int kMaxThreads = kWgWaves * kWave;
 constexpr int kXU = 8;            // activation vectors per thread in the first staging round
 constexpr int kMaxLds = 160 * 1024;
 
@@ -273,7 +274,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   f32x4 *red = reinterpret_cast<f32x4 *>(cinit + cinit_floats(FMT, np));
   f32x4 *fin = red;   // slot tw is read only by wave (tw, 0) before it holds the sum
   __shared__ uint32_t last_flag;
-  __shared__ uint32_t wave_ovf[kMaxWaves];
+  __shared__ uint32_t wave_ovf[kWgWaves];
 
   // this wave's slice: pairs [pa + js, pa + js + n), n may be 0
   const int js = min(np, j * pl.ppj);

@@ -141,15 +141,22 @@ __global__ __launch_bounds__(eng::kMaxThreads) void gemm_kernel(GemmArgs a) {
   eng::run<FMT>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx, lds, false, DenseEpi{&a});
 }
 
-// Slices of the K range: a function of the shape only (see engine.h).  About
-// 2048 (tile, slice) streams keep every CU busy without making them short;
-// a slice holds at most kMaxPpj pairs so that one slice of MTP_MAX_M rows
-// always fits the LDS of one workgroup.
+// Slices of the K range: a function of the shape only (see engine.h).
+// Workgroups are 8 waves (TW tiles x J slices).  Small matrices (<= 128
+// tiles) spread their K over up to 8 slices of at least 2 pairs so that
+// enough waves stream;
+// matrices of 768..1024 tiles take 2 slices (4 tiles per workgroup fill the
+// CUs in one round); the rest take 4 (2 tiles per workgroup, several rounds
+// or a persistent loop).  A slice holds at most kMaxPpj pairs so that one
+// slice of MTP_MAX_M rows always fits the LDS of one workgroup.
 constexpr int kMaxPpj = 16;
 
 void slices(int T, int P, int &S, int &ppj) {
-  int s = (int)((2048.0 + T / 2) / T);
-  s = s < 1 ? 1 : (s > P ? P : s);
+  int s;
+  if (T <= 128) s = std::max(1, std::min(8, P / 2));   // slices of >= 2 pairs
+  else if (T >= 768 && T <= 1024) s = 2;
+  else s = 4;
+  s = std::min(s, P);
   s = std::max(s, (P + kMaxPpj - 1) / kMaxPpj);
   ppj = (P + s - 1) / s;
   S = (P + ppj - 1) / ppj;
@@ -186,22 +193,19 @@ GemmPlan gemm_plan(int format, int M, int N, int K) {
   pl.T = eng::tiles_of(N);
   pl.P = eng::pairs_of(K);
   slices(pl.T, pl.P, pl.S, pl.ppj);
-  // slices per workgroup: all of them unless the staged rows get too large
+  // slices per workgroup: all of them if the staged rows fit; otherwise one
+  // (the K groups then meet through the workspace)
   const size_t budget = 144 * 1024;
-  pl.KG = 1;
-  for (;;) {
-    pl.J = (pl.S + pl.KG - 1) / pl.KG;
-    if (pl.J <= 16 && eng::lds_bytes(format, M, std::min(pl.J * pl.ppj, pl.P), 16 / pl.J, pl.J) <= budget)
-      break;
-    if (pl.J == 1) break;
-    ++pl.KG;
-  }
+  pl.J = std::min(pl.S, eng::kWgWaves);
+  auto fits = [&](int J) {
+    return eng::lds_bytes(format, M, std::min(J * pl.ppj, pl.P), eng::kWgWaves / J, J) <= budget;
+  };
+  if (pl.J < pl.S || !fits(pl.J)) pl.J = 1;
+  while (pl.J > 1 && !fits(pl.J)) --pl.J;
   pl.KG = (pl.S + pl.J - 1) / pl.J;
-  // tiles per workgroup: as many as fit 16 waves while enough workgroups remain
+  // tiles per workgroup: fill the 8 waves
   pl.TW = 1;
-  while (pl.TW * 2 * pl.J <= eng::kMaxWaves &&
-         (int64_t)((pl.T + pl.TW * 2 - 1) / (pl.TW * 2)) * pl.KG >= 192)
-    pl.TW *= 2;
+  while (pl.TW * 2 * pl.J <= eng::kWgWaves) pl.TW *= 2;
   pl.TG = (pl.T + pl.TW - 1) / pl.TW;
   pl.threads = pl.TW * pl.J * kWave;
   pl.lds = eng::lds_bytes(format, M, std::min(pl.J * pl.ppj, pl.P), pl.TW, pl.J);
@@ -209,10 +213,10 @@ GemmPlan gemm_plan(int format, int M, int N, int K) {
 }
 
 GemmPlan finish_plan(GemmPlan pl) {
-  // resident workgroups: LDS and wave slots of 256 CUs
-  int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds, 1));
+  // resident workgroups on 256 CUs: LDS and wave slots
+  int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds + 1024, 1));
   per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
-  const int64_t cap = (int64_t)256 * per_cu / pl.KG;
+  const int64_t cap = std::max<int64_t>(1, (int64_t)256 * per_cu / pl.KG);
   pl.G = (int)std::max<int64_t>(1, std::min<int64_t>(pl.TG, cap));
   pl.grid = pl.G * pl.KG;
   pl.ws_bytes = pl.KG > 1 ? (((size_t)pl.T * 4 + 255) & ~(size_t)255) +

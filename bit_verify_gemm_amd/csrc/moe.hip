@@ -258,11 +258,11 @@ struct MoePlan {
 MoePlan moe_plan(int format, int N, int K, int rc, int tw_max, bool paired) {
   MoePlan m;
   const int P = eng::pairs_of(K);
-  m.S = std::max(1, std::min((P + 4) / 8, paired ? eng::kMaxWaves / 2 : eng::kMaxWaves));
+  m.S = std::max(1, std::min((P + 4) / 8, paired ? eng::kWgWaves / 2 : eng::kWgWaves));
   m.ppj = (P + m.S - 1) / m.S;
   m.S = (P + m.ppj - 1) / m.ppj;
   m.J = m.S;
-  m.TW = std::max(paired ? 2 : 1, std::min(tw_max, eng::kMaxWaves / m.J));
+  m.TW = std::max(paired ? 2 : 1, std::min(tw_max, eng::kWgWaves / m.J));
   if (paired) m.TW &= ~1;
   const int tiles = paired ? eng::tiles_of(N) / 2 : eng::tiles_of(N);
   const int per = paired ? m.TW / 2 : m.TW;

@@ -45,7 +45,7 @@ def test_packed_sizes():
 
 
 def test_workspace_queries():
-    assert bv.gemm_workspace_bytes(262144, 4096) == 0             # one K slice: no split
+    assert bv.gemm_workspace_bytes(262144, 256) == 0              # one K slice: no split
     assert bv.gemm_workspace_bytes(5120, 17408) > 0               # long K is split
     assert bv.gemm_workspace_bytes(0, 32) == 0
     assert bv.gemm_workspace_bytes(10, 33) == 0
