@@ -68,7 +68,7 @@ def gemm(**kw):
                                     a["ldyb"], a["ws"], a["wsb"], a["stream"])
 
 
-BIG = dict(N=5120, K=17408, ldx=17408, ldy=5120)
+BIG = dict(M=16, N=5120, K=17408, ldx=17408, ldy=5120)   # K split over workgroups
 
 
 @pytest.mark.parametrize("kw,code", [
