@@ -75,6 +75,38 @@ def dev_bits(a: np.ndarray, dev) -> torch.Tensor:
     return torch.from_numpy(a).to(dev)
 
 
+class Graphed:
+    """calls(0..R-1) captured once in a graph, replayed on demand."""
+
+    def __init__(self, calls, R):
+        self.R = R
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(R):             # warm the launch path outside capture
+                calls(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            for i in range(R):
+                calls(i)
+
+    def ms_per_call(self, calls_wanted):
+        """HIP-event time per call over about calls_wanted calls."""
+        reps = max(1, -(-calls_wanted // self.R))
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            self.g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * self.R)
+
+
 def time_graph(calls, R, steps, warmup):
     """Capture calls(0..R-1) in one graph; replay it so that about `steps`
     calls are timed.  Returns (wall seconds, ms per call from HIP events,
@@ -290,19 +322,25 @@ def main():
     achieved = bytes_call / (per_call_ms * 1e-3) / 1e9
     plan = bv.gemm_plan_info(bv.FMT_NVFP4, M, cfg["w"]["N"], cfg["w"]["K"])
 
+    # M sweep: the row counts take turns in 5 rounds and each reports its
+    # median, so that clock drift between separate measurements does not
+    # enter the ratios between them
     sweep = {}
     if not args.no_sweep and not args.only_headline:
-        for m in (1, 2, 4, 8):
-            if m == M:
-                sweep[str(m)] = {"us_per_call": round(per_call_ms * 1e3, 3),
-                                 "gbs": round(achieved, 1)}
-                continue
-            r = gemm_from_host(bv, cfg["w"], cfg["x"], m, dev)
-            _, ms, _ = time_graph(r, r.R, args.steps, args.warmup)
+        ms_of = {m: [] for m in (1, 2, 4, 8)}
+        runners = {m: gemm_from_host(bv, cfg["w"], cfg["x"], m, dev) for m in ms_of}
+        graphs = {m: Graphed(r, r.R) for m, r in runners.items()}
+        for g in graphs.values():
+            g.ms_per_call(args.warmup)
+        for _ in range(5):
+            for m, g in graphs.items():
+                ms_of[m].append(g.ms_per_call(max(1, args.steps // 4)))
+        for m, v in ms_of.items():
+            ms = float(np.median(v))
             sweep[str(m)] = {"us_per_call": round(ms * 1e3, 3),
                              "gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1)}
-            del r
-            torch.cuda.empty_cache()
+        del graphs, runners
+        torch.cuda.empty_cache()
 
     extra = {}
     if not args.no_extra and not args.only_headline:

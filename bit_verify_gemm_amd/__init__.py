@@ -126,7 +126,7 @@ def gemm_workspace_bytes(N: int, K: int) -> int:
 
 
 PLAN_FIELDS = ("T", "P", "S", "ppj", "J", "KG", "TW", "TG", "G", "grid", "threads", "lds",
-               "ws_bytes")
+               "ws_bytes", "PP")
 
 
 def gemm_plan_info(fmt: int, M: int, N: int, K: int) -> dict:

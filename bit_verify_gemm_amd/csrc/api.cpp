@@ -143,9 +143,10 @@ int mtp_gemm_plan_info(int format, int M, int N, int K, int32_t *info, int n) {
     return fail(MTP_ERR_SHAPE, "%s: bad shape M=%d N=%d K=%d", who, M, N, K);
   if (!info || n < 1) return fail(MTP_ERR_NULL, "%s: info is required", who);
   const mtp::GemmPlan p = mtp::gemm_plan(format, M, N, K);
-  const int32_t v[13] = {p.T, p.P, p.S, p.ppj, p.J, p.KG, p.TW, p.TG, p.G, p.grid, p.threads,
-                         (int32_t)p.lds, (int32_t)p.ws_bytes};
-  for (int i = 0; i < n && i < 13; ++i) info[i] = v[i];
+  const int32_t v[14] = {p.T,       p.P,       p.S,    p.ppj,         p.J,
+                         p.KG,      p.TW,      p.TG,   p.G,           p.grid,
+                         p.threads, (int32_t)p.lds,    (int32_t)p.ws_bytes, p.PP};
+  for (int i = 0; i < n && i < 14; ++i) info[i] = v[i];
   g_error.clear();
   return MTP_OK;
 }

@@ -16,7 +16,7 @@
 // workgroups cover the S slices of a tile group.  A workgroup stages the
 // activation rows of its K range in LDS once (the x loads are issued before
 // the weight prefetch so they return first), then every wave streams its
-// (tile, slice) blocks with kPP blocks of loads in flight, decodes each
+// (tile, slice) blocks with PP blocks of loads in flight, decodes each
 // weight once and feeds the matrix cores for all rows at once.  A workgroup
 // may process several tile groups in turn; its load stream runs on across
 // tile-group boundaries.  The J slices of a tile meet in LDS; with KG > 1 the
@@ -35,7 +35,8 @@ constexpr int kPairBytes = 2304;
 constexpr int kHalfBytes = 1024;
 constexpr int kScaleOff = 2048;
 constexpr int kSlotBytes = 512;   // one pair of one activation row in LDS (256 bf16)
-constexpr int kPP = 2;            // blocks in flight per wave
+constexpr int kPPShallow = 2;     // blocks in flight per wave: workgroups with many tile groups
+constexpr int kPPDeep = 4;        // ... one tile group per workgroup (one 8-wave workgroup per CU)
 constexpr int kMaxWaves = 16;         // waves of all workgroups on one CU (<= 128 VGPRs)
 constexpr int kWgWaves = 8;           // waves of one workgroup at most
 constexpr int kMaxThreads = kWgWaves * kWave;
@@ -108,23 +109,34 @@ template <> struct Blk<MTP_FMT_Q4_0> {
   u32x4 s;      // the 8 fp16 scales of the lane's row for this pair
 };
 
-// Weights are read once per pass: streaming (non-temporal) loads keep them
-// from displacing the activations and partial sums in the caches.
-template <typename T>
-__device__ __forceinline__ T stream_load(const uint8_t *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T *>(p));
+// Weights are read through a buffer window per block: a window of one
+// block's bytes, or an empty window whose loads return zeros without a memory
+// access (blocks past a slice or past the matrix).  The loads are streaming
+// (non-temporal): weights are read once per pass and must not displace the
+// activations and partial sums in the caches.
+using Window = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit untyped data, gfx9 family
+constexpr int kLoadNT = 2;               // cache policy: non-temporal
+
+__device__ __forceinline__ Window block_window(const uint8_t *p, bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p), 0, valid ? kPairBytes : 0,
+                                           kRsrcWord3);
 }
 
-__device__ __forceinline__ void load_blk(Blk<MTP_FMT_NVFP4> &b, const uint8_t *p, int lane) {
-  b.c0 = stream_load<u32x4>(p + 16 * lane);
-  b.c1 = stream_load<u32x4>(p + kHalfBytes + 16 * lane);
-  b.s = stream_load<uint32_t>(p + kScaleOff + 4 * lane);
+__device__ __forceinline__ u32x4 win_load16(Window w, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w, off, 0, kLoadNT));
 }
 
-__device__ __forceinline__ void load_blk(Blk<MTP_FMT_Q4_0> &b, const uint8_t *p, int lane) {
-  b.c0 = stream_load<u32x4>(p + 16 * lane);
-  b.c1 = stream_load<u32x4>(p + kHalfBytes + 16 * lane);
-  b.s = stream_load<u32x4>(p + kScaleOff + 16 * (lane & 15));
+__device__ __forceinline__ void load_blk(Blk<MTP_FMT_NVFP4> &b, Window w, int lane) {
+  b.c0 = win_load16(w, 16 * lane);
+  b.c1 = win_load16(w, kHalfBytes + 16 * lane);
+  b.s = __builtin_amdgcn_raw_buffer_load_b32(w, kScaleOff + 4 * lane, 0, kLoadNT);
+}
+
+__device__ __forceinline__ void load_blk(Blk<MTP_FMT_Q4_0> &b, Window w, int lane) {
+  b.c0 = win_load16(w, 16 * lane);
+  b.c1 = win_load16(w, kHalfBytes + 16 * lane);
+  b.s = win_load16(w, kScaleOff + 16 * (lane & 15));
 }
 
 __device__ __forceinline__ float half_lo(uint32_t v) {
@@ -256,7 +268,7 @@ __device__ __forceinline__ float fin_at(const f32x4 *fin, int tw, int m, int c) 
 // Every thread of the workgroup calls run with the same arguments;
 // sync_entry must be true when the workgroup ran the engine before (its LDS
 // may still be in use).
-template <int FMT, typename TileOf, typename Epi>
+template <int FMT, int PP, typename TileOf, typename Epi>
 __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
                                     const Plan &pl, const TileOf &tile_of, const Fixup &fx,
                                     uint8_t *lds, bool sync_entry, Epi &&epi) {
@@ -279,32 +291,32 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   // this wave's slice: pairs [pa + js, pa + js + n), n may be 0
   const int js = min(np, j * pl.ppj);
   const int n = min(np, js + pl.ppj) - js;
-  const int nr = (pl.ppj + kPP - 1) / kPP * kPP;      // iterations per tile group
+  const int nr = (pl.ppj + PP - 1) / PP * PP;        // iterations per tile group
   const int slice = pl.kg * pl.J + j;
 
-  // load stream: tile group su, pair si of the slice (clamped into the slice;
-  // after the last block it repeats that block, which the caches hold)
-  auto tile_base = [&](int u) -> const uint8_t * {
-    int t = tile_of(pl.tg_first + u * pl.tg_step, tw);
-    t = t < 0 ? 0 : t;
-    const int p0 = n > 0 ? pa + js : P - 1;
-    return w + ((int64_t)t * P + p0) * kPairBytes;
-  };
+  // load stream: block si of the slice of tile group su; positions past the
+  // slice, past the matrix or past the last tile group get empty windows
   int su = 0, si = 0;
-  const uint8_t *sbase = tile_base(0);
-  auto next_block = [&]() -> const uint8_t * {
-    const int i = n > 0 ? min(si, n - 1) : 0;
-    const uint8_t *p = sbase + (int64_t)i * kPairBytes;
+  int stile = 0;
+  auto tile_at = [&](int u) {
+    return __builtin_amdgcn_readfirstlane(tile_of(pl.tg_first + u * pl.tg_step, tw));
+  };
+  stile = tile_at(0);
+  auto next_block = [&]() -> Window {
+    const bool valid = si < n && stile >= 0;
+    const int64_t blk = valid ? ((int64_t)stile * P + pa + js + si) : 0;
+    const Window win = block_window(w + blk * kPairBytes, valid);
     if (++si == nr) {
       if (su + 1 < pl.tg_count) {
         si = 0;
         ++su;
-        sbase = tile_base(su);
+        stile = tile_at(su);
       } else {
-        si = nr - 1;
+        si = nr;   // stays past the slice
+        stile = -1;
       }
     }
-    return p;
+    return win;
   };
 
   if (sync_entry) __syncthreads();  // LDS may still be read by a previous call's epilogue
@@ -319,8 +331,11 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     else return bf16x8_to_f16x8(v, ovf);
   };
 
-  // 1) activation loads, 2) activation stores to LDS, 3) weight prefetch:
-  // the few activation bytes must not queue behind the weight stream.
+  // 1) activation loads, 2) the first kPPShallow weight blocks, 3) activation
+  // stores to LDS (waiting for the activation loads only), 4) the rest of the
+  // prefetch: the activation bytes do not queue behind the weight stream, and
+  // the weight stream starts before the staging ends.  (More loads before
+  // the stores only stall the stores behind a full memory queue.)
   // Vector i = u * nthreads + tid of the staged rows is (m, v) = divmod(i,
   // vpr); (m, v) advance incrementally so that no division sits between the
   // loads.  Every load reads a valid address (row 0 / the first staged
@@ -345,15 +360,20 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
       ++xm;
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kEarly = PP < kPPShallow ? PP : kPPShallow;
+  Blk<FMT> buf[PP];
+#pragma unroll
+  for (int i = 0; i < kEarly; ++i) load_blk(buf[i], next_block(), lane);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < kXU; ++u) {
     const u32x4 val = encode(xv[u]);
     if (xoff[u] >= 0) *reinterpret_cast<u32x4 *>(lds + xoff[u]) = val;
   }
   __builtin_amdgcn_sched_barrier(0);
-  Blk<FMT> buf[kPP];
 #pragma unroll
-  for (int i = 0; i < kPP; ++i) load_blk(buf[i], next_block(), lane);
+  for (int i = kEarly; i < PP; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
   // rows that did not fit the first round (many rows on few waves)
   for (; xm < M; ) {
@@ -463,9 +483,9 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     for (int u = 0; u < pl.tg_count; ++u) {
       const int tg = pl.tg_first + u * pl.tg_step;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int b0 = 0; b0 < nr; b0 += kPP) {
+      for (int b0 = 0; b0 < nr; b0 += PP) {
 #pragma unroll
-        for (int i = 0; i < kPP; ++i) {
+        for (int i = 0; i < PP; ++i) {
           const int st = b0 + i;
           const int slot = (st < n) ? js + st : np;   // zero slot past the slice
           if constexpr (kF16) acc = compute_blk_f16(acc, buf[i], xrow + slot * kSlotBytes);

@@ -128,7 +128,7 @@ struct DenseEpi {
   }
 };
 
-template <int FMT>
+template <int FMT, int PP>
 __global__ __launch_bounds__(eng::kMaxThreads) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   eng::Plan pl;
@@ -138,7 +138,8 @@ __global__ __launch_bounds__(eng::kMaxThreads) void gemm_kernel(GemmArgs a) {
   pl.tg_step = a.G;
   pl.tg_count = (a.TG - pl.tg_first + a.G - 1) / a.G;
   const eng::XSource xs{a.x, a.ldx, nullptr};
-  eng::run<FMT>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx, lds, false, DenseEpi{&a});
+  eng::run<FMT, PP>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx, lds, false,
+                    DenseEpi{&a});
 }
 
 // Slices of the K range: a function of the shape only (see engine.h).
@@ -213,11 +214,22 @@ GemmPlan gemm_plan(int format, int M, int N, int K) {
 }
 
 GemmPlan finish_plan(GemmPlan pl) {
-  // resident workgroups on 256 CUs: LDS and wave slots
-  int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds + 1024, 1));
-  per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
-  const int64_t cap = std::max<int64_t>(1, (int64_t)256 * per_cu / pl.KG);
-  pl.G = (int)std::max<int64_t>(1, std::min<int64_t>(pl.TG, cap));
+  // Tile groups that fit one workgroup per CU in one round take the deeper
+  // stream (kPPDeep blocks per wave in flight; its registers allow one
+  // 8-wave workgroup per CU).  Otherwise: workgroups resident on 256 CUs by
+  // LDS and wave slots, a short lead, and the load stream running on across
+  // the tile groups of a workgroup.
+  const int64_t one_round = std::max<int64_t>(1, 256 / pl.KG);
+  if (pl.TG <= one_round) {
+    pl.G = pl.TG;
+    pl.PP = eng::kPPDeep;
+  } else {
+    int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds + 1024, 1));
+    per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
+    const int64_t cap = std::max<int64_t>(1, (int64_t)256 * per_cu / pl.KG);
+    pl.G = (int)std::min<int64_t>(pl.TG, cap);
+    pl.PP = eng::kPPShallow;
+  }
   pl.grid = pl.G * pl.KG;
   pl.ws_bytes = pl.KG > 1 ? (((size_t)pl.T * 4 + 255) & ~(size_t)255) +
                                 (size_t)pl.T * pl.S * kWave * 16
@@ -236,13 +248,16 @@ hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   a.fx.cnt = reinterpret_cast<uint32_t *>(w8);
   a.fx.part = reinterpret_cast<f32x4 *>(w8 ? w8 + (((size_t)pl.T * 4 + 255) & ~(size_t)255) : nullptr);
-  if (format == MTP_FMT_NVFP4) {
-    eng::allow_large_lds(gemm_kernel<MTP_FMT_NVFP4>);
-    hipLaunchKernelGGL(gemm_kernel<MTP_FMT_NVFP4>, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
-  } else {
-    eng::allow_large_lds(gemm_kernel<MTP_FMT_Q4_0>);
-    hipLaunchKernelGGL(gemm_kernel<MTP_FMT_Q4_0>, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
-  }
+  auto go = [&](auto kernel) {
+    eng::allow_large_lds(kernel);
+    hipLaunchKernelGGL(kernel, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
+  };
+  constexpr int kN = MTP_FMT_NVFP4, kQ = MTP_FMT_Q4_0;
+  const bool deep = pl.PP == eng::kPPDeep;
+  if (format == kN)
+    deep ? go(gemm_kernel<kN, eng::kPPDeep>) : go(gemm_kernel<kN, eng::kPPShallow>);
+  else
+    deep ? go(gemm_kernel<kQ, eng::kPPDeep>) : go(gemm_kernel<kQ, eng::kPPShallow>);
   return hipGetLastError();
 }
 

@@ -23,10 +23,11 @@ struct GemmPlan {
   int threads;
   size_t lds;
   size_t ws_bytes;   // arrival counters + slice partials when KG > 1
+  int PP;            // weight blocks each wave keeps in flight
 };
 
 GemmPlan gemm_plan(int format, int M, int N, int K);
-GemmPlan finish_plan(GemmPlan pl);   // fills G, grid and ws_bytes from the rest
+GemmPlan finish_plan(GemmPlan pl);   // fills G, grid, PP and ws_bytes from the rest
 
 // Workspace that covers every M for this shape (0 when K has one slice).
 size_t gemm_ws_bytes(int N, int K);

@@ -186,8 +186,9 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
     const eng::XSource xs{a.x, a.H, a.stok + first + c0};
-    eng::run<FMT>(w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds, c0 > 0,
-                  GateUpEpi{&a, pl.TW / 2, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+    eng::run<FMT, eng::kPPShallow>(w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr},
+                                   lds, c0 > 0,
+                                   GateUpEpi{&a, pl.TW / 2, pl.TW * pl.J * kWave, mc, c0, first, gsc});
   }
 }
 
@@ -230,8 +231,9 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
     const eng::XSource xs{a.h, a.F, a.spair + first + c0};
-    eng::run<FMT>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds, c0 > 0,
-                  DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+    eng::run<FMT, eng::kPPShallow>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr},
+                                   lds, c0 > 0,
+                                   DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, c0, first, gsc});
   }
 }
 

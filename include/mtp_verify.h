@@ -150,11 +150,12 @@ size_t mtp_gemm_workspace_bytes(int N, int K);
 
 /*
  * Diagnostic: the launch shape mtp_verify_gemm uses for (format, M, N, K).
- * Writes min(n, 13) int32 values to host array `info`: tiles T (16 rows),
+ * Writes min(n, 14) int32 values to host array `info`: tiles T (16 rows),
  * pairs P (256 K), K slices S, pairs per slice, slices per workgroup J,
  * workgroups per tile group KG, tiles per workgroup TW, tile groups, resident
  * workgroups per K group, grid size, threads per workgroup, dynamic LDS bytes,
- * workspace bytes this M needs.  Enqueues nothing.
+ * workspace bytes this M needs, weight blocks each wave keeps in flight.
+ * Enqueues nothing.
  */
 int mtp_gemm_plan_info(int format, int M, int N, int K, int32_t *info, int n);
 

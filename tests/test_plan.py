@@ -40,6 +40,11 @@ def test_plan_invariants(fmt, N, K):
         assert p["lds"] == lds and lds + 16 <= MAX_LDS
         assert p["ws_bytes"] <= bv.gemm_workspace_bytes(N, K)
         assert (p["ws_bytes"] > 0) == (KG > 1)
+        # the deep stream's registers leave room for one 8-wave workgroup per
+        # CU: it is planned only when every workgroup is resident at once
+        deep = 4
+        assert p["PP"] in (2, deep)
+        assert (p["PP"] == deep) == (p["grid"] <= 256 and p["G"] == p["TG"])
         slices.add((S, ppj))
     assert len(slices) == 1, "the K split must not depend on M"
 
@@ -64,11 +69,11 @@ def replay(p, M, N, K):
                 for j in range(J):
                     js = min(np_, j * ppj)
                     n = min(np_, js + ppj) - js
-                    p0 = pa + js if n > 0 else P - 1
-                    last = p0 + max(n - 1, 0)
-                    tt = max(tile, 0)
-                    hi["block"] = max(hi["block"], tt * P + last)
-                    hi["pair_lo"] = min(hi["pair_lo"], p0)
+                    # stream positions past the slice or the matrix read
+                    # nothing (empty buffer windows)
+                    if tile >= 0 and n > 0:
+                        hi["block"] = max(hi["block"], tile * P + pa + js + n - 1)
+                        hi["pair_lo"] = min(hi["pair_lo"], pa + js)
                     hi["slot"] = max(hi["slot"], js + n if n else np_)
                     assert js + n <= np_
                     if tile >= 0 and n > 0:
