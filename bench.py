@@ -54,8 +54,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "bit_verify_gemm_amd", "csrc", f)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--m", type=int, default=8, help="rows of the headline pass")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1/2/4 sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

@@ -21,7 +21,11 @@
 // may process several tile groups in turn; its load stream runs on across
 // tile-group boundaries.  The J slices of a tile meet in LDS; with KG > 1 the
 // slice partials go to the workspace and the last workgroup of the tile group
-// to arrive adds all S of them in slice order.
+// to arrive adds all S of them in slice order.  With one slice per tile in
+// the workgroup (J == 1, KG == 1) a wave may instead finish its own tiles
+// (LOCAL), with no LDS round trip or barrier between tile groups, and may
+// then stream two tiles at once (NT == 2) so that one wave holds e.g. the
+// matching gate and up columns of a gated MLP.
 #pragma once
 
 #include "../../include/mtp_verify.h"
@@ -256,11 +260,20 @@ __device__ __forceinline__ float fin_at(const f32x4 *fin, int tw, int m, int c) 
   return reinterpret_cast<const float *>(fin)[(tw * kWave + (m >> 2) * 16 + c) * 4 + (m & 3)];
 }
 
+// Element i (0..3) of a wave's accumulator belongs to activation row
+// 4 * (lane / 16) + i and column lane % 16 of the tile.
+__device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4) + i; }
+
 // Runs the engine over the tile groups of `pl`.
 //   w, T, P   packed matrix with T tiles of P pairs; K its reduction length
 //   M, xs     1..16 activation rows
-//   tile_of   tile_of(tg, tw) -> tile index of slot tw of tile group tg, or
-//             -1 for a slot past the matrix (computed on tile 0, never used)
+//   tile_of   tile_of(tg, s) -> tile index of slot s of tile group tg, or
+//             -1 for a slot past the matrix (nothing is read for it)
+//   NT        tiles per wave: wave (tw, j) streams slots NT*tw .. NT*tw+NT-1
+//             of each tile group, block by block in turn, into NT sums
+//   LOCAL     each wave hands its own sums to epi.wave(tg, tw, acc) (acc:
+//             NT accumulators, see acc_row) with no LDS or barrier; needs
+//             J == 1 and KG == 1.  Otherwise (NT == 1):
 //   epi       epi(tg, fin) is called by every thread of the workgroup once a
 //             tile group's sums are final (only by the last-arriving
 //             workgroup when KG > 1); fin_at(fin, tw, m, c) is row m of
@@ -268,7 +281,7 @@ __device__ __forceinline__ float fin_at(const f32x4 *fin, int tw, int m, int c) 
 // Every thread of the workgroup calls run with the same arguments;
 // sync_entry must be true when the workgroup ran the engine before (its LDS
 // may still be in use).
-template <int FMT, int PP, typename TileOf, typename Epi>
+template <int FMT, int PP, int NT, bool LOCAL, typename TileOf, typename Epi>
 __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
                                     const Plan &pl, const TileOf &tile_of, const Fixup &fx,
                                     uint8_t *lds, bool sync_entry, Epi &&epi) {
@@ -291,29 +304,35 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   // this wave's slice: pairs [pa + js, pa + js + n), n may be 0
   const int js = min(np, j * pl.ppj);
   const int n = min(np, js + pl.ppj) - js;
-  const int nr = (pl.ppj + PP - 1) / PP * PP;        // iterations per tile group
+  static_assert(NT == 1 || (NT == 2 && LOCAL), "two tiles per wave need the wave-local finish");
+  static_assert(PP % NT == 0, "a prefetch slot always feeds the same tile");
+  const int nr = (pl.ppj * NT + PP - 1) / PP * PP;   // iterations per tile group
   const int slice = pl.kg * pl.J + j;
 
-  // load stream: block si of the slice of tile group su; positions past the
-  // slice, past the matrix or past the last tile group get empty windows
+  // load stream: position si of tile group su is block si / NT of the slice
+  // of the wave's tile si % NT; positions past the slice, past the matrix or
+  // past the last tile group get empty windows
   int su = 0, si = 0;
-  int stile = 0;
-  auto tile_at = [&](int u) {
-    return __builtin_amdgcn_readfirstlane(tile_of(pl.tg_first + u * pl.tg_step, tw));
+  int stile[NT];
+  auto tiles_at = [&](int u) {
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+      stile[q] = __builtin_amdgcn_readfirstlane(tile_of(pl.tg_first + u * pl.tg_step, NT * tw + q));
   };
-  stile = tile_at(0);
+  tiles_at(0);
   auto next_block = [&]() -> Window {
-    const bool valid = si < n && stile >= 0;
-    const int64_t blk = valid ? ((int64_t)stile * P + pa + js + si) : 0;
+    const int t = (NT == 1 || si % NT == 0) ? stile[0] : stile[NT - 1];
+    const int pi = si / NT;
+    const bool valid = pi < n && t >= 0;
+    const int64_t blk = valid ? ((int64_t)t * P + pa + js + pi) : 0;
     const Window win = block_window(w + blk * kPairBytes, valid);
     if (++si == nr) {
       if (su + 1 < pl.tg_count) {
         si = 0;
         ++su;
-        stile = tile_at(su);
+        tiles_at(su);
       } else {
         si = nr;   // stays past the slice
-        stile = -1;
       }
     }
     return win;
@@ -482,19 +501,23 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     constexpr bool kF16 = decltype(f16_tag)::value;
     for (int u = 0; u < pl.tg_count; ++u) {
       const int tg = pl.tg_first + u * pl.tg_step;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 acc[NT];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       for (int b0 = 0; b0 < nr; b0 += PP) {
 #pragma unroll
         for (int i = 0; i < PP; ++i) {
-          const int st = b0 + i;
-          const int slot = (st < n) ? js + st : np;   // zero slot past the slice
-          if constexpr (kF16) acc = compute_blk_f16(acc, buf[i], xrow + slot * kSlotBytes);
-          else acc = compute_blk(acc, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
+          const int pi = (b0 + i) / NT;
+          const int slot = (pi < n) ? js + pi : np;   // zero slot past the slice
+          f32x4 &a = acc[i % NT];
+          if constexpr (kF16) a = compute_blk_f16(a, buf[i], xrow + slot * kSlotBytes);
+          else a = compute_blk(a, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
           load_blk(buf[i], next_block(), lane);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      finish_group(tg, acc);
+      if constexpr (LOCAL) epi.wave(tg, tw, acc);
+      else finish_group(tg, acc[0]);
     }
   };
   if constexpr (FMT == MTP_FMT_NVFP4) {

@@ -69,16 +69,20 @@ struct MoeArgs {
   uint16_t *h_out;
   int T, H, F, E, topk, P;
   int rc;                 // rows per engine pass
-  struct { int TW, J, S, ppj; } gu, dn;
+  struct { int TW, J, S, ppj, tg; } gu, dn;
   int32_t *nuniq, *uexp, *ustart, *ucount, *spair, *stok;
   uint16_t *h;
   float *y;
 };
 
+// One workgroup of roundup(P, 64) threads: thread p ranks key p, then
+// position p of the sorted order knows whether it starts an expert; block
+// prefix counts of those starts number the unique experts.
 __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
   __shared__ int32_t key[kMaxPairs];
   __shared__ int32_t sorted[kMaxPairs];
-  __shared__ int32_t start[kMaxPairs];
+  __shared__ int32_t ustart[kMaxPairs];
+  __shared__ int32_t wave_starts[kMaxPairs / kWave], wave_valid[kMaxPairs / kWave];
   const int p = threadIdx.x;
   const int P = a.P;
   int e = -1;
@@ -89,43 +93,46 @@ __global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
     key[p] = (e < 0) ? kInvalidKey + p : e * kMaxPairs + p;
   }
   __syncthreads();
-  int rank = 0;
   if (p < P) {
+    int rank = 0;
     for (int q = 0; q < P; ++q) rank += key[q] < key[p];
     sorted[rank] = p;
   }
   __syncthreads();
-  // a sorted position starts a new expert when its expert differs from the
-  // previous one; invalid pairs sort last and start nothing
+  // sorted position p starts an expert when its expert differs from the one
+  // before; invalid pairs sort last and start nothing
+  bool first = false, valid = false;
+  int ke = 0;
   if (p < P) {
     const int pp = sorted[p];
-    const int ke = key[pp];
-    const bool valid = ke < kInvalidKey;
-    const bool first = valid && (p == 0 || key[sorted[p - 1]] / kMaxPairs != ke / kMaxPairs);
-    start[p] = first ? 1 : 0;
+    ke = key[pp];
+    valid = ke < kInvalidKey;
+    first = valid && (p == 0 || key[sorted[p - 1]] / kMaxPairs != ke / kMaxPairs);
     a.spair[p] = pp;
     a.stok[p] = pp / a.topk;
   }
-  __syncthreads();
-  if (p == 0) {
-    int u = 0, prev = -1;
-    for (int i = 0; i < P; ++i) {
-      if (key[sorted[i]] >= kInvalidKey) break;
-      if (start[i]) {
-        if (prev >= 0) a.ucount[u - 1] = i - prev;
-        a.uexp[u] = key[sorted[i]] / kMaxPairs;
-        a.ustart[u] = i;
-        prev = i;
-        ++u;
-      }
-    }
-    if (prev >= 0) {
-      int end = prev;
-      while (end < P && key[sorted[end]] < kInvalidKey) ++end;
-      a.ucount[u - 1] = end - prev;
-    }
-    *a.nuniq = u;
+  const uint64_t fb = __builtin_amdgcn_ballot_w64(first);
+  const uint64_t vb = __builtin_amdgcn_ballot_w64(valid);
+  const int w = p / kWave, l = p % kWave;
+  if (l == 0) {
+    wave_starts[w] = __builtin_popcountll(fb);
+    wave_valid[w] = __builtin_popcountll(vb);
   }
+  __syncthreads();
+  int u = __builtin_popcountll(fb & ((1ull << l) - 1ull)), nuniq = 0, nvalid = 0;
+  for (int q = 0; q < (int)(blockDim.x / kWave); ++q) {
+    if (q < w) u += wave_starts[q];
+    nuniq += wave_starts[q];
+    nvalid += wave_valid[q];   // the valid positions are a prefix of the order
+  }
+  if (first) {
+    ustart[u] = p;
+    a.uexp[u] = ke / kMaxPairs;
+    a.ustart[u] = p;
+  }
+  __syncthreads();
+  if (p < nuniq) a.ucount[p] = (p + 1 < nuniq ? ustart[p + 1] : nvalid) - ustart[p];
+  if (p == 0) *a.nuniq = nuniq;
   // rows of h for invalid pairs are zero
   if (a.h_out && p < P && e < 0)
     for (int f = 0; f < a.F; ++f) a.h_out[(int64_t)p * a.F + f] = 0;
@@ -140,11 +147,11 @@ __device__ __forceinline__ float silu(float v) {
 }
 
 struct GateUpTiles {
-  int TWh, Fg;   // gate tiles per workgroup, gate tiles of the expert
-  __device__ __forceinline__ int operator()(int tg, int tw) const {
-    const int t = tg * TWh + tw / 2;
+  int TWh, Fg;   // gate tiles per tile group, gate tiles of the expert
+  __device__ __forceinline__ int operator()(int tg, int s) const {
+    const int t = tg * TWh + s / 2;
     if (t >= Fg) return -1;
-    return (tw & 1) ? Fg + t : t;   // slot 2q: gate tile, slot 2q + 1: the matching up tile
+    return (s & 1) ? Fg + t : t;   // slot 2q: gate tile, slot 2q + 1: the matching up tile
   }
 };
 
@@ -168,9 +175,27 @@ struct GateUpEpi {
       }
     }
   }
+  // one wave holds gate tile tg * TWh + tw in acc[0] and its up tile in acc[1]
+  __device__ __forceinline__ void wave(int tg, int tw, const f32x4 *acc) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int f = (tg * TWh + tw) * 16 + (lane & 15);
+    if (f >= a->F) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = eng::acc_row(lane, i);
+      if (m < mc) {
+        const float gate = gsc * acc[0][i], up = gsc * acc[1][i];
+        const uint16_t hb = f32_to_bf16_rne(silu(gate) * up);
+        const int pair = a->spair[first + c0 + m];
+        a->h[(int64_t)pair * a->F + f] = hb;
+        if (a->h_out) a->h_out[(int64_t)pair * a->F + f] = hb;
+      }
+    }
+  }
 };
 
-template <int FMT>
+// PAIRED: one wave streams a gate tile and its up tile together (J == 1)
+template <int FMT, int PP, bool PAIRED>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int slot = blockIdx.y;
@@ -180,15 +205,17 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   const uint8_t *w = a.gu_packed + (int64_t)e * eng::packed_bytes(2 * a.F, a.H);
   eng::Plan pl;
   pl.TW = a.gu.TW; pl.J = a.gu.J; pl.S = a.gu.S; pl.ppj = a.gu.ppj; pl.KG = 1; pl.kg = 0;
-  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x; pl.tg_count = 1;
-  const GateUpTiles tiles{pl.TW / 2, a.F / 16};
+  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x;
+  pl.tg_count = (a.gu.tg - pl.tg_first + gridDim.x - 1) / gridDim.x;
+  const int TWh = PAIRED ? pl.TW : pl.TW / 2;
+  const GateUpTiles tiles{TWh, a.F / 16};
   const float gsc = a.gu_global ? a.gu_global[e] : 1.0f;
   for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
     const eng::XSource xs{a.x, a.H, a.stok + first + c0};
-    eng::run<FMT, eng::kPPShallow>(w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr},
-                                   lds, c0 > 0,
-                                   GateUpEpi{&a, pl.TW / 2, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+    eng::run<FMT, PP, PAIRED ? 2 : 1, PAIRED>(
+        w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds, c0 > 0,
+        GateUpEpi{&a, TWh, pl.TW * pl.J * kWave, mc, c0, first, gsc});
   }
 }
 
@@ -205,6 +232,16 @@ struct DownEpi {
         a->y[(int64_t)a->spair[first + c0 + m] * a->H + n] = gsc * eng::fin_at(fin, c >> 4, m, c & 15);
     }
   }
+  __device__ __forceinline__ void wave(int tg, int tw, const f32x4 *acc) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = (tg * TW + tw) * 16 + (lane & 15);
+    if (n >= a->H) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = eng::acc_row(lane, i);
+      if (m < mc) a->y[(int64_t)a->spair[first + c0 + m] * a->H + n] = gsc * acc[0][i];
+    }
+  }
 };
 
 struct DownTiles {
@@ -215,7 +252,8 @@ struct DownTiles {
   }
 };
 
-template <int FMT>
+// LOCAL: one slice per tile (J == 1), each wave finishes its own tile
+template <int FMT, int PP, bool LOCAL>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int slot = blockIdx.y;
@@ -225,15 +263,15 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   const uint8_t *w = a.dn_packed + (int64_t)e * eng::packed_bytes(a.H, a.F);
   eng::Plan pl;
   pl.TW = a.dn.TW; pl.J = a.dn.J; pl.S = a.dn.S; pl.ppj = a.dn.ppj; pl.KG = 1; pl.kg = 0;
-  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x; pl.tg_count = 1;
+  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x;
+  pl.tg_count = (a.dn.tg - pl.tg_first + gridDim.x - 1) / gridDim.x;
   const DownTiles tiles{pl.TW, eng::tiles_of(a.H)};
   const float gsc = a.dn_global ? a.dn_global[e] : 1.0f;
   for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
     const eng::XSource xs{a.h, a.F, a.spair + first + c0};
-    eng::run<FMT, eng::kPPShallow>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr},
-                                   lds, c0 > 0,
-                                   DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+    eng::run<FMT, PP, 1, LOCAL>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds,
+                                c0 > 0, DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, c0, first, gsc});
   }
 }
 
@@ -251,9 +289,14 @@ __global__ __launch_bounds__(256) void moe_combine(MoeArgs a) {
 }
 
 // Engine shape of one expert matrix: a single workgroup covers all slices
-// (S of about 8 pairs each); rc rows are staged per pass.
+// (S of about 8 pairs each); rc rows are staged per pass.  G workgroups per
+// expert slot share its tg tile groups, so that the grid holds about
+// kWaveTarget waves: a workgroup stages its rows once for several tile
+// groups when there are many slots.
+constexpr int kWaveTarget = 2048;   // 8 waves on each of the 256 CUs
+
 struct MoePlan {
-  int TW, J, S, ppj, tg, threads;
+  int TW, J, S, ppj, tg, G, threads;
   size_t lds;
 };
 
@@ -264,14 +307,29 @@ MoePlan moe_plan(int format, int N, int K, int rc, int tw_max, bool paired) {
   m.ppj = (P + m.S - 1) / m.S;
   m.S = (P + m.ppj - 1) / m.ppj;
   m.J = m.S;
-  m.TW = std::max(paired ? 2 : 1, std::min(tw_max, eng::kWgWaves / m.J));
-  if (paired) m.TW &= ~1;
   const int tiles = paired ? eng::tiles_of(N) / 2 : eng::tiles_of(N);
-  const int per = paired ? m.TW / 2 : m.TW;
+  int per;   // tiles (gate/up tile pairs) per tile group
+  if (m.J == 1) {
+    // one wave per tile (per gate/up pair, streamed together) finishes it alone
+    m.TW = std::min(tw_max, eng::kWgWaves);
+    per = m.TW;
+  } else {
+    // the slices of a tile meet in LDS; gate and up tiles sit in separate waves
+    m.TW = std::max(paired ? 2 : 1, std::min(tw_max, eng::kWgWaves / m.J));
+    if (paired) m.TW &= ~1;
+    per = paired ? m.TW / 2 : m.TW;
+  }
   m.tg = (tiles + per - 1) / per;
   m.threads = m.TW * m.J * kWave;
   m.lds = eng::lds_bytes(format, rc, std::min(m.J * m.ppj, P), m.TW, m.J);
+  m.G = m.tg;
   return m;
+}
+
+void moe_spread(MoePlan &m, int slots) {
+  const int per_slot = std::max(1, kWaveTarget / (slots * (m.threads / kWave)));
+  const int rounds = (m.tg + per_slot - 1) / per_slot;   // tile groups per workgroup
+  m.G = (m.tg + rounds - 1) / rounds;                     // balanced
 }
 
 // Rows staged per pass: up to 16 (and T, which bounds the rows of an expert
@@ -318,25 +376,38 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
   a.h = reinterpret_cast<uint16_t *>(w + L.h);
   a.y = reinterpret_cast<float *>(w + L.y);
   a.rc = moe_rows(format, T, H, F);
-  const MoePlan gu = moe_plan(format, 2 * F, H, a.rc, 4, true);
-  const MoePlan dn = moe_plan(format, H, F, a.rc, 8, false);
-  a.gu = {gu.TW, gu.J, gu.S, gu.ppj};
-  a.dn = {dn.TW, dn.J, dn.S, dn.ppj};
   const int slots = (a.P < E) ? a.P : E;
-  hipLaunchKernelGGL(moe_route, dim3(1), dim3(kMaxPairs), 0, stream, a);
+  MoePlan gu = moe_plan(format, 2 * F, H, a.rc, 4, true);
+  MoePlan dn = moe_plan(format, H, F, a.rc, 8, false);
+  moe_spread(gu, slots);
+  moe_spread(dn, slots);
+  a.gu = {gu.TW, gu.J, gu.S, gu.ppj, gu.tg};
+  a.dn = {dn.TW, dn.J, dn.S, dn.ppj, dn.tg};
+  const int route_threads = (a.P + kWave - 1) / kWave * kWave;
+  hipLaunchKernelGGL(moe_route, dim3(1), dim3(route_threads), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 gu_grid(gu.tg, slots), dn_grid(dn.tg, slots);
-  if (format == MTP_FMT_NVFP4) {
-    eng::allow_large_lds(moe_gate_up<MTP_FMT_NVFP4>);
-    eng::allow_large_lds(moe_down<MTP_FMT_NVFP4>);
-    hipLaunchKernelGGL(moe_gate_up<MTP_FMT_NVFP4>, gu_grid, dim3(gu.threads), gu.lds, stream, a);
-    hipLaunchKernelGGL(moe_down<MTP_FMT_NVFP4>, dn_grid, dim3(dn.threads), dn.lds, stream, a);
+  const dim3 gu_grid(gu.G, slots), dn_grid(dn.G, slots);
+  auto go = [&](auto gate_up, auto down) {
+    eng::allow_large_lds(gate_up);
+    eng::allow_large_lds(down);
+    hipLaunchKernelGGL(gate_up, gu_grid, dim3(gu.threads), gu.lds, stream, a);
+    hipLaunchKernelGGL(down, dn_grid, dim3(dn.threads), dn.lds, stream, a);
+  };
+  // four blocks per wave in flight: the grid holds about one 8-wave
+  // workgroup per CU
+  constexpr int kD = eng::kPPDeep, kN = MTP_FMT_NVFP4, kQ = MTP_FMT_Q4_0;
+  const bool pg = gu.J == 1, ld = dn.J == 1;
+  if (format == kN) {
+    if (pg) ld ? go(moe_gate_up<kN, kD, true>, moe_down<kN, kD, true>)
+               : go(moe_gate_up<kN, kD, true>, moe_down<kN, kD, false>);
+    else    ld ? go(moe_gate_up<kN, kD, false>, moe_down<kN, kD, true>)
+               : go(moe_gate_up<kN, kD, false>, moe_down<kN, kD, false>);
   } else {
-    eng::allow_large_lds(moe_gate_up<MTP_FMT_Q4_0>);
-    eng::allow_large_lds(moe_down<MTP_FMT_Q4_0>);
-    hipLaunchKernelGGL(moe_gate_up<MTP_FMT_Q4_0>, gu_grid, dim3(gu.threads), gu.lds, stream, a);
-    hipLaunchKernelGGL(moe_down<MTP_FMT_Q4_0>, dn_grid, dim3(dn.threads), dn.lds, stream, a);
+    if (pg) ld ? go(moe_gate_up<kQ, kD, true>, moe_down<kQ, kD, true>)
+               : go(moe_gate_up<kQ, kD, true>, moe_down<kQ, kD, false>);
+    else    ld ? go(moe_gate_up<kQ, kD, false>, moe_down<kQ, kD, true>)
+               : go(moe_gate_up<kQ, kD, false>, moe_down<kQ, kD, false>);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
