@@ -126,6 +126,14 @@ __device__ __forceinline__ u32x4 interleave_halves(u32x4 v) {
   return r;
 }
 
+// Value of lane (l ^ 1), resp. (l ^ 2), within each aligned quad of lanes.
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+
 // 4x4 transpose of dwords across the four 16-lane groups of a wave: on entry
 // lane (r, g) holds a[j] = element (g, j); on exit it holds element (j, g).
 __device__ __forceinline__ void transpose_lane_groups(uint32_t &a0, uint32_t &a1, uint32_t &a2,

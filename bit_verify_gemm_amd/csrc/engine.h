@@ -44,7 +44,7 @@ constexpr int kPPDeep = 4;        // ... one tile group per workgroup (one 8-wav
 constexpr int kMaxWaves = 16;         // waves of all workgroups on one CU (<= 128 VGPRs)
 constexpr int kWgWaves = 8;           // waves of one workgroup at most
 constexpr int kMaxThreads = kWgWaves * kWave;
-constexpr int kXU = 8;            // activation vectors per thread in the first staging round
+constexpr int kXU = 12;           // activation staging rounds in flight at once
 constexpr int kMaxLds = 160 * 1024;
 
 __host__ __device__ inline int tiles_of(int N) { return (N + 15) / 16; }
@@ -357,27 +357,56 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   // the stores only stall the stores behind a full memory queue.)
   // Vector i = u * nthreads + tid of the staged rows is (m, v) = divmod(i,
   // vpr); (m, v) advance incrementally so that no division sits between the
-  // loads.  Every load reads a valid address (row 0 / the first staged
-  // vector when out of range) so no branch splits them.
+  // loads.  Only the rounds that hold staged vectors load (xr, the same for
+  // every wave); up to kXU rounds are in flight at once, so one memory
+  // latency stages every shape but the largest.  Inside a round every load
+  // reads a valid address (row 0 / the first staged vector when out of range)
+  // so no branch splits them.
+  // Q4_0 also needs the accumulator starts -136 * (sum of each 32-block of a
+  // row): the four vectors of a block sit in the four lanes of an aligned
+  // lane quad (vpr and nthreads are multiples of 4), which add their sums
+  // across the quad; rows >= M are never stored, and the zero slot gets 0.
   const int vpr = np * 32;                  // 16-byte vectors per staged row
   const int k0 = pa * kPairK;
   const int rstep = nthreads / vpr, vstep = nthreads - rstep * vpr;
+  const int xr = __builtin_amdgcn_readfirstlane((M * vpr + nthreads - 1) / nthreads);
   int xm = threadIdx.x / vpr, xvi = threadIdx.x - xm * vpr;
+  auto advance = [&](int &m, int &v) {
+    v += vstep;
+    m += rstep;
+    if (v >= vpr) {
+      v -= vpr;
+      ++m;
+    }
+  };
+  // one staged vector: LDS store (rows < M) and, for Q4_0, its block sum
+  auto stage = [&](u32x4 v, int m, int vi) {
+    const u32x4 val = encode(v);
+    if (m < M) *reinterpret_cast<u32x4 *>(lds + m * rowb + vi * 16) = val;
+    if constexpr (FMT == MTP_FMT_Q4_0) {
+      float s = (bf16_to_f32(v.x) + bf16_to_f32(v.x >> 16)) +
+                (bf16_to_f32(v.y) + bf16_to_f32(v.y >> 16));
+      s += (bf16_to_f32(v.z) + bf16_to_f32(v.z >> 16)) +
+           (bf16_to_f32(v.w) + bf16_to_f32(v.w >> 16));
+      s += quad_xor1(s);
+      s += quad_xor2(s);
+      if ((lane & 3) == 0 && m < M) cinit[(vi >> 2) * 16 + m] = -136.0f * s;
+    }
+  };
+  // straight-line code for the first kXU rounds (no loop around the loads, so
+  // the waits before the stores count only the activation loads)
   u32x4 xv[kXU];
-  int xoff[kXU];
+  const int xm0 = xm, xvi0 = xvi;
 #pragma unroll
   for (int u = 0; u < kXU; ++u) {
     const int k = k0 + xvi * 8;
     const bool ok = xm < M && k < K;
-    const u32x4 t = *reinterpret_cast<const u32x4 *>(xs.row(xm < M ? xm : 0) + (ok ? k : k0));
-    xv[u] = ok ? t : u32x4{0u, 0u, 0u, 0u};
-    xoff[u] = xm < M ? xm * rowb + xvi * 16 : -1;
-    xvi += vstep;
-    xm += rstep;
-    if (xvi >= vpr) {
-      xvi -= vpr;
-      ++xm;
+    xv[u] = u32x4{0u, 0u, 0u, 0u};
+    if (u < xr) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(xs.row(xm < M ? xm : 0) + (ok ? k : k0));
+      if (ok) xv[u] = v;
     }
+    advance(xm, xvi);
   }
   __builtin_amdgcn_sched_barrier(0);
   constexpr int kEarly = PP < kPPShallow ? PP : kPPShallow;
@@ -385,27 +414,26 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
 #pragma unroll
   for (int i = 0; i < kEarly; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
+  {
+    int sm = xm0, sv = xvi0;   // the same walk again for the stores
 #pragma unroll
-  for (int u = 0; u < kXU; ++u) {
-    const u32x4 val = encode(xv[u]);
-    if (xoff[u] >= 0) *reinterpret_cast<u32x4 *>(lds + xoff[u]) = val;
+    for (int u = 0; u < kXU; ++u) {
+      if (u < xr) stage(xv[u], sm, sv);
+      advance(sm, sv);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = kEarly; i < PP; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
-  // rows that did not fit the first round (many rows on few waves)
-  for (; xm < M; ) {
+  // rounds beyond kXU (only very long staged rows)
+  for (int u = kXU; u < xr; ++u) {
     const int k = k0 + xvi * 8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (k < K) val = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k);
-    *reinterpret_cast<u32x4 *>(lds + xm * rowb + xvi * 16) = encode(val);
-    xvi += vstep;
-    xm += rstep;
-    if (xvi >= vpr) {
-      xvi -= vpr;
-      ++xm;
-    }
+    const bool ok = xm < M && k < K;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k);
+    stage(v, xm, xvi);
+    advance(xm, xvi);
   }
   {
     const bool any = __builtin_amdgcn_ballot_w64(ovf != 0u) != 0ull;
@@ -416,27 +444,8 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     *reinterpret_cast<u32x4 *>(lds + (size_t)m * rowb + np * kSlotBytes + v * 16) =
         u32x4{0u, 0u, 0u, 0u};
   }
-  if (FMT == MTP_FMT_Q4_0) {
-    __syncthreads();
-    // accumulator starts -136 * sum of each 32-block per row; 0 for rows >= M
-    // and for the zero slot
-    for (int i = threadIdx.x; i < (np + 1) * 128; i += nthreads) {
-      const int b = i >> 4, m = i & 15;
-      float s = 0.0f;
-      if (m < M && b < np * 8) {
-        const u32x4 *xr = reinterpret_cast<const u32x4 *>(lds + (size_t)m * rowb + b * 64);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v = xr[q];
-          s += bf16_to_f32(v.x) + bf16_to_f32(v.x >> 16);
-          s += bf16_to_f32(v.y) + bf16_to_f32(v.y >> 16);
-          s += bf16_to_f32(v.z) + bf16_to_f32(v.z >> 16);
-          s += bf16_to_f32(v.w) + bf16_to_f32(v.w >> 16);
-        }
-      }
-      cinit[i] = -136.0f * s;
-    }
-  }
+  if constexpr (FMT == MTP_FMT_Q4_0)
+    for (int i = threadIdx.x; i < 128; i += nthreads) cinit[np * 128 + i] = 0.0f;
   __syncthreads();
 
   // sum the slices of the tile group and hand it to the epilogue
