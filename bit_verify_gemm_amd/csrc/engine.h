@@ -31,6 +31,10 @@
 #include "../../include/mtp_verify.h"
 #include "device.h"
 
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
 namespace mtp {
 namespace eng {
 
@@ -65,16 +69,18 @@ __host__ __device__ inline size_t lds_bytes(int format, int M, int np, int TW, i
          (size_t)(TW * J) * kWave * 16;
 }
 
-// Lets `kernel` use more than 64 KiB of dynamic LDS (once per kernel).
+// Lets `kernel` use more than 64 KiB of dynamic LDS (once per kernel: the
+// kernels that were set up are remembered by address).
 template <typename Kernel>
 inline void allow_large_lds(Kernel *kernel) {
-  static const bool done = [kernel] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 1024);
-    (void)hipGetLastError();   // a refusal shows up as the launch's own error
-    return true;
-  }();
-  (void)done;
+  static std::mutex mu;
+  static std::vector<const void *> done;
+  const void *k = reinterpret_cast<const void *>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  if (std::find(done.begin(), done.end(), k) != done.end()) return;
+  (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 1024);
+  (void)hipGetLastError();   // a refusal shows up as the launch's own error
+  done.push_back(k);
 }
 
 // Activation rows: row m is base + idx[m] * ld (idx == nullptr: m).
@@ -306,7 +312,10 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   const int n = min(np, js + pl.ppj) - js;
   static_assert(NT == 1 || (NT == 2 && LOCAL), "two tiles per wave need the wave-local finish");
   static_assert(PP % NT == 0, "a prefetch slot always feeds the same tile");
-  const int nr = (pl.ppj * NT + PP - 1) / PP * PP;   // iterations per tile group
+  // iterations per tile group: whole rounds of PP (the ring slot of a stream
+  // position is its index mod PP); positions past the tile's blocks load
+  // empty windows and skip the arithmetic
+  const int nr = (pl.ppj * NT + PP - 1) / PP * PP;
   const int slice = pl.kg * pl.J + j;
 
   // load stream: position si of tile group su is block si / NT of the slice
@@ -490,7 +499,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
 
   uint32_t x_ovf = 0;
   if (FMT == MTP_FMT_NVFP4)
-    for (int q = 0; q < pl.TW * pl.J; ++q) x_ovf |= wave_ovf[q];
+    for (int q = 0; q < nthreads / kWave; ++q) x_ovf |= wave_ovf[q];
   bool use_f16 = FMT == MTP_FMT_NVFP4;
   if (FMT == MTP_FMT_NVFP4 && __builtin_amdgcn_readfirstlane(x_ovf)) {
     use_f16 = false;
@@ -516,11 +525,15 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
       for (int b0 = 0; b0 < nr; b0 += PP) {
 #pragma unroll
         for (int i = 0; i < PP; ++i) {
+          // the branch holds no memory loads, so the waits before each
+          // block still count the loads of the blocks behind it
           const int pi = (b0 + i) / NT;
-          const int slot = (pi < n) ? js + pi : np;   // zero slot past the slice
-          f32x4 &a = acc[i % NT];
-          if constexpr (kF16) a = compute_blk_f16(a, buf[i], xrow + slot * kSlotBytes);
-          else a = compute_blk(a, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
+          if (pi < n) {
+            const int slot = js + pi;
+            f32x4 &a = acc[i % NT];
+            if constexpr (kF16) a = compute_blk_f16(a, buf[i], xrow + slot * kSlotBytes);
+            else a = compute_blk(a, buf[i], xrow + slot * kSlotBytes, crow + slot * 128);
+          }
           load_blk(buf[i], next_block(), lane);
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -25,6 +25,7 @@
 //    sums are added in slice order, so results are deterministic and a row's
 //    result does not depend on M or on the other rows.
 #include <algorithm>
+#include <type_traits>
 
 #include "engine.h"
 #include "internal.h"
@@ -194,9 +195,9 @@ GemmPlan gemm_plan(int format, int M, int N, int K) {
   pl.T = eng::tiles_of(N);
   pl.P = eng::pairs_of(K);
   slices(pl.T, pl.P, pl.S, pl.ppj);
+  const size_t budget = 144 * 1024;
   // slices per workgroup: all of them if the staged rows fit; otherwise one
   // (the K groups then meet through the workspace)
-  const size_t budget = 144 * 1024;
   pl.J = std::min(pl.S, eng::kWgWaves);
   auto fits = [&](int J) {
     return eng::lds_bytes(format, M, std::min(J * pl.ppj, pl.P), eng::kWgWaves / J, J) <= budget;
@@ -214,21 +215,26 @@ GemmPlan gemm_plan(int format, int M, int N, int K) {
 }
 
 GemmPlan finish_plan(GemmPlan pl) {
-  // Tile groups that fit one workgroup per CU in one round take the deeper
-  // stream (kPPDeep blocks per wave in flight; its registers allow one
-  // 8-wave workgroup per CU).  Otherwise: workgroups resident on 256 CUs by
-  // LDS and wave slots, a short lead, and the load stream running on across
-  // the tile groups of a workgroup.
+  // Workgroups resident on 256 CUs by LDS and wave slots; when every tile
+  // group has its own workgroup, one round; otherwise a persistent loop whose
+  // load stream runs on across the tile groups of a workgroup.  A wave's
+  // positions per tile group are rounded up to whole rounds of PP blocks in
+  // flight (padding positions load empty windows and skip the arithmetic),
+  // so PP is kPPDeep - 1 or kPPDeep, whichever pads less (the deeper on a
+  // tie); two workgroups on one CU take kPPShallow, whose registers leave
+  // room for both.
+  int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds + 1024, 1));
+  per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
   const int64_t one_round = std::max<int64_t>(1, 256 / pl.KG);
+  auto pad = [&](int pp) { return (pl.ppj + pp - 1) / pp * pp - pl.ppj; };
+  const int deep = pad(eng::kPPDeep - 1) < pad(eng::kPPDeep) ? eng::kPPDeep - 1 : eng::kPPDeep;
   if (pl.TG <= one_round) {
     pl.G = pl.TG;
-    pl.PP = eng::kPPDeep;
+    pl.PP = deep;
   } else {
-    int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds + 1024, 1));
-    per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
     const int64_t cap = std::max<int64_t>(1, (int64_t)256 * per_cu / pl.KG);
     pl.G = (int)std::min<int64_t>(pl.TG, cap);
-    pl.PP = eng::kPPShallow;
+    pl.PP = per_cu == 1 ? deep : eng::kPPShallow;
   }
   pl.grid = pl.G * pl.KG;
   pl.ws_bytes = pl.KG > 1 ? (((size_t)pl.T * 4 + 255) & ~(size_t)255) +
@@ -252,12 +258,16 @@ hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64
     eng::allow_large_lds(kernel);
     hipLaunchKernelGGL(kernel, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
   };
-  constexpr int kN = MTP_FMT_NVFP4, kQ = MTP_FMT_Q4_0;
-  const bool deep = pl.PP == eng::kPPDeep;
-  if (format == kN)
-    deep ? go(gemm_kernel<kN, eng::kPPDeep>) : go(gemm_kernel<kN, eng::kPPShallow>);
-  else
-    deep ? go(gemm_kernel<kQ, eng::kPPDeep>) : go(gemm_kernel<kQ, eng::kPPShallow>);
+  // one kernel per (format, blocks in flight 2..4)
+  auto pick = [&](auto fmt_tag) {
+    constexpr int F = decltype(fmt_tag)::value;
+    if (pl.PP == 2) go(gemm_kernel<F, 2>);
+    else if (pl.PP == 3) go(gemm_kernel<F, 3>);
+    else go(gemm_kernel<F, 4>);
+  };
+  static_assert(eng::kPPShallow == 2 && eng::kPPDeep == 4, "kernels exist for 2..4 blocks in flight");
+  if (format == MTP_FMT_NVFP4) pick(std::integral_constant<int, MTP_FMT_NVFP4>{});
+  else pick(std::integral_constant<int, MTP_FMT_Q4_0>{});
   return hipGetLastError();
 }
 

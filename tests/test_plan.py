@@ -15,7 +15,8 @@ import workloads as W
 MAX_LDS = 160 * 1024
 PAIR_BYTES = 2304
 SHAPES = [(16, 32), (37, 96), (100, 256), (130, 1056), (70, 2080), (2048, 2048), (1024, 2048),
-          (14336, 4096), (262144, 5376), (8192, 5120), (2176 * 16, 5120)] + \
+          (14336, 4096), (262144, 5376), (8192, 5120), (2176 * 16, 5120), (65536, 5376),
+          (65536, 1536)] + \
     [(n, k) for _, k, n in W.LAYER_27B]
 
 
@@ -33,18 +34,22 @@ def test_plan_invariants(fmt, N, K):
         assert T == -(-N // 16) and P == -(-K // 256)
         assert 1 <= ppj <= 16 and S * ppj >= P and (S - 1) * ppj < P
         assert 1 <= J <= 16 and J * KG >= S and (KG - 1) * J < S
-        assert TW >= 1 and TW * J <= 16 and p["threads"] == TW * J * 64
+        waves = TW * J
+        assert TW >= 1 and waves <= 8 and p["threads"] == waves * 64
         assert p["TG"] == -(-T // TW) and p["grid"] == p["G"] * KG and 1 <= p["G"] <= p["TG"]
         np_ = min(J * ppj, P)
-        lds = M * row_bytes(np_) + (fmt == W.FMT_Q4_0) * (np_ + 1) * 128 * 4 + TW * J * 1024
+        lds = M * row_bytes(np_) + (fmt == W.FMT_Q4_0) * (np_ + 1) * 128 * 4 + waves * 1024
         assert p["lds"] == lds and lds + 16 <= MAX_LDS
         assert p["ws_bytes"] <= bv.gemm_workspace_bytes(N, K)
         assert (p["ws_bytes"] > 0) == (KG > 1)
-        # the deep stream's registers leave room for one 8-wave workgroup per
-        # CU: it is planned only when every workgroup is resident at once
-        deep = 4
-        assert p["PP"] in (2, deep)
-        assert (p["PP"] == deep) == (p["grid"] <= 256 and p["G"] == p["TG"])
+        # blocks in flight: 2 when two persistent workgroups share a CU (their
+        # registers must fit together); otherwise 3 or 4, whichever pads a
+        # wave's positions per tile group less, 4 on a tie
+        one_round = p["grid"] <= 256 and p["G"] == p["TG"]
+        pad = {pp: -(-ppj // pp) * pp - ppj for pp in (3, 4)}
+        deep = 3 if pad[3] < pad[4] else 4
+        per_cu = min(MAX_LDS // (p["lds"] + 1024), 16 // waves)
+        assert p["PP"] == (2 if not one_round and per_cu >= 2 else deep)
         slices.add((S, ppj))
     assert len(slices) == 1, "the K split must not depend on M"
 
