@@ -30,10 +30,30 @@ typedef unsigned long long u64;
 constexpr int kBlock = 256;
 constexpr int kMaxBlocksPerRow = 128;
 constexpr int kBins = 256;
+constexpr int kBatch = 8;   // row entries each thread loads at once (all in flight)
+
+// Entries base + t + i * kBlock (i < kBatch) of row zr for thread t, or
+// `fill` past j1: all loads are issued before any value is used.
+__device__ __forceinline__ void load_batch(const float *zr, int base, int j1, float fill,
+                                           float (&v)[kBatch]) {
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const int j = base + (int)threadIdx.x + i * kBlock;
+    v[i] = j < j1 ? zr[j] : fill;
+  }
+}
 
 int blocks_per_row(int V) {
   int nb = (V + 2047) / 2048;
   return nb < 1 ? 1 : (nb > kMaxBlocksPerRow ? kMaxBlocksPerRow : nb);
+}
+
+// The final draw spreads its one row over more blocks (one entry per thread
+// up to kMaxDrawBlocks blocks).
+constexpr int kMaxDrawBlocks = 2048;
+int draw_blocks(int V) {
+  int nb = (V + kBlock - 1) / kBlock;
+  return nb < 1 ? 1 : (nb > kMaxDrawBlocks ? kMaxDrawBlocks : nb);
 }
 
 // ---- 128-bit fixed point (value * 2^100) -----------------------------------
@@ -157,12 +177,7 @@ struct AccIn {
 };
 
 struct Layout {
-  size_t maxp, zmax, hist, total, sel, rows, acc, glob, blk, gpart, bytes;
-};
-
-struct Global {
-  uint32_t arrived;  // blocks of the draw that have stored their sums
-  int32_t pad[3];
+  size_t maxp, zmax, hist, total, sel, rows, acc, blk, gpart, bytes;
 };
 
 Layout layout(int M, int V) {
@@ -181,8 +196,7 @@ Layout layout(int M, int V) {
   L.sel = take(sizeof(SelState) * 4 * M);
   L.rows = take(sizeof(RowState) * M);
   L.acc = take(sizeof(AccIn) * M);
-  L.glob = take(sizeof(Global));
-  L.blk = take(sizeof(u64) * 4 * nb);
+  L.blk = take(sizeof(u64) * 4 * (size_t)draw_blocks(V));
   L.gpart = take(sizeof(float) * 2 * M * nb);
   L.bytes = o;
   return L;
@@ -198,6 +212,7 @@ struct RejArgs {
   double T;
   double top_p;
   int M, V, nb, chunk;
+  int nbd, chunkd;  // blocks of the final draw and entries per draw block
   int64_t base_len;
   int32_t *tokens;
   int32_t *counts;
@@ -209,7 +224,6 @@ struct RejArgs {
   SelState *sel;    // [pass][row]: state after `pass` selections (pass >= 1)
   RowState *rows;
   AccIn *acc;       // [row]: inputs of draft row's acceptance test
-  Global *glob;
   u64 *blk;         // [block][res lo, res hi, e lo, e hi]
 };
 
@@ -257,9 +271,14 @@ __global__ __launch_bounds__(kBlock) void greedy_partial(const float *z, int64_t
   const int j0 = b * chunk, j1 = min(V, j0 + chunk);
   float bv = __int_as_float(0x7FC00000);
   int bj = 0x7FFFFFFF;
-  for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
-    const float v = zr[j];
-    if (better(v, j, bv, bj)) { bv = v; bj = j; }
+  for (int base = j0; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(zr, base, j1, __int_as_float(0x7FC00000), v);   // NaN never wins
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = base + (int)threadIdx.x + i * kBlock;
+      if (better(v[i], j, bv, bj)) { bv = v[i]; bj = j; }
+    }
   }
   wave_best(bv, bj);
   __shared__ float sv[kBlock / kWave];
@@ -307,6 +326,14 @@ __global__ __launch_bounds__(kBlock) void greedy_final(const float *pv, const in
 
 __device__ __forceinline__ double e_of(float z, float zmax, double T) {
   return exp(((double)z - (double)zmax) / T);
+}
+
+// e_of(z) when its fixed-point value can be non-zero, else 0: below
+// (z - zmax) / T = -70.5, e < 2.4e-31 < 2^-100 and floor(e * 2^100) is 0, so
+// the exponential is skipped.  Every sum of the row is the same either way.
+__device__ __forceinline__ double e_or_zero(float z, float zmax, double T) {
+  const double x = ((double)z - (double)zmax) / T;
+  return x < -70.5 ? 0.0 : exp(x);
 }
 
 // Nucleus threshold in fixed point: top_p * S (at least one unit, so that
@@ -373,7 +400,12 @@ __global__ __launch_bounds__(kBlock) void rej_rowmax(RejArgs p) {
   const float *zr = p.z + (int64_t)row * p.ldl;
   const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
   float m = -__builtin_inff();
-  for (int j = j0 + threadIdx.x; j < j1; j += kBlock) m = fmaxf(m, zr[j]);
+  for (int base = j0; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(zr, base, j1, -__builtin_inff(), v);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) m = fmaxf(m, v[i]);
+  }
   for (int s = kWave / 2; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
   __shared__ float sm[kBlock / kWave];
   if ((threadIdx.x & (kWave - 1)) == 0) sm[threadIdx.x / kWave] = m;
@@ -389,7 +421,6 @@ __global__ __launch_bounds__(kBlock) void rej_rowmax(RejArgs p) {
     hist_at(p, pass, row)[w] = 0ull;
   }
   if (b == 0 && threadIdx.x < 2) p.total[2 * row + threadIdx.x] = 0ull;
-  if (b == 0 && row == 0 && threadIdx.x == 0) p.glob->arrived = 0u;
 }
 
 // Radix pass `pass` (0..3).  Pass 0 reduces the row maximum and sums the
@@ -445,23 +476,28 @@ __global__ __launch_bounds__(kBlock) void rej_pass(RejArgs p, int pass, int with
   const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
   const int shift = 24 - 8 * pass;
   Fx tot = fx_zero();
-  for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
-    const float zj = zr[j];
-    const uint32_t key = fkey(zj);
-    if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
-    const Fx e = to_fx(e_of(zj, zmax, p.T));
-    if (!fx_nonzero(e)) continue;     // below the fixed-point resolution: no mass
-    if (pass == 0) fx_add(tot, e);
-    if (with_hist) {
-      const int d = (key >> shift) & 0xFF;
-      u64 *bin = sh + 3 * d;
-      if (e.lo) {
-        const u64 old = atomicAdd(bin, e.lo);
-        atomicAdd(bin + 1, e.hi + ((old + e.lo < old) ? 1ull : 0ull));
-      } else {
-        atomicAdd(bin + 1, e.hi);
+  for (int base = j0; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(zr, base, j1, -__builtin_inff(), v);   // -inf: no mass
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float zj = v[i];
+      const uint32_t key = fkey(zj);
+      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+      const Fx e = to_fx(e_or_zero(zj, zmax, p.T));
+      if (!fx_nonzero(e)) continue;     // below the fixed-point resolution: no mass
+      if (pass == 0) fx_add(tot, e);
+      if (with_hist) {
+        const int d = (key >> shift) & 0xFF;
+        u64 *bin = sh + 3 * d;
+        if (e.lo) {
+          const u64 old = atomicAdd(bin, e.lo);
+          atomicAdd(bin + 1, e.hi + ((old + e.lo < old) ? 1ull : 0ull));
+        } else {
+          atomicAdd(bin + 1, e.hi);
+        }
+        atomicAdd(bin + 2, 1ull);
       }
-      atomicAdd(bin + 2, 1ull);
     }
   }
   if (pass == 0) {
@@ -595,8 +631,10 @@ __device__ __forceinline__ int accepted_run(const RejArgs &p) {
 __device__ __forceinline__ void draw_weights(const RejArgs &p, const RowState &rs, int row,
                                              bool residual, int j, Fx &wres, Fx &we) {
   const float zj = p.z[(int64_t)row * p.ldl + j];
+  // (rs.mass >= 1, the row maximum's own weight, so a weight that is 0 in
+  // fixed point also gives a residual of 0)
   double e = 0.0;
-  if (in_nucleus(rs, zj, j)) e = e_of(zj, rs.zmax, p.T);
+  if (in_nucleus(rs, zj, j)) e = e_or_zero(zj, rs.zmax, p.T);
   we = to_fx(e);
   if (residual) {
     const double d = e / rs.mass - (double)p.q[(int64_t)row * p.ldq + j];
@@ -627,124 +665,118 @@ __device__ Fx fx_block_exclusive(Fx v, Fx *wsum, Fx &total) {
   return fx_sum(before, fx_sub(incl, v));
 }
 
-constexpr int kDrawPer = 8;   // entries per thread in the final draw
-
-// Draw weights: every block sums its chunk for the row of the final draw
-// (row a of the first rejection, or the last row for the bonus); the last
-// block to finish picks the smallest j with prefix weight > u * total
-// (index order), or the last j with a positive weight if rounding passes
-// the end, and writes the committed run.
-__global__ __launch_bounds__(kBlock) void rej_draw(RejArgs p) {
+// The final draw, in two kernels: rej_draw_sums has every block sum its chunk
+// of the draw weights of the row of the final draw (row a of the first
+// rejection, or the last row for the bonus); rej_draw_pick (one block)
+// picks the smallest j with prefix weight > u * total (index order), or the
+// last j with a positive weight if rounding passes the end, and writes the
+// committed run.  It finds the chunk of the crossing from the chunk sums (a
+// block-wide prefix, then the first crossing by atomic minimum), then the
+// entry inside it.  (The kernel boundary, not an arrival counter, orders the
+// chunk sums before the pick: one counter shared by thousands of blocks
+// serialises their arrivals.)
+__global__ __launch_bounds__(kBlock) void rej_draw_sums(RejArgs p) {
   __shared__ Fx wsum[kBlock / kWave];
-  __shared__ Fx sb_res[kMaxBlocksPerRow], sb_e[kMaxBlocksPerRow];
-  __shared__ uint32_t s_last;
-  __shared__ int s_blk, s_mode, s_use_res, s_pick;
-  __shared__ Fx s_before, s_target;
   const int a = accepted_run(p);
   const int residual = a < p.M - 1;
   const RowState rs = p.rows[a];
   const int b = blockIdx.x;
-  {
-    const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
-    Fx sr = fx_zero(), se = fx_zero();
-    for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
-      Fx wr, we;
-      draw_weights(p, rs, a, residual != 0, j, wr, we);
-      fx_add(sr, wr);
-      fx_add(se, we);
-    }
-    sr = fx_block_sum(sr, wsum);
-    se = fx_block_sum(se, wsum);
-    if (threadIdx.x == 0) {
-      u64 *o = p.blk + 4 * b;
-      __hip_atomic_store(o + 0, sr.lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(o + 1, sr.hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(o + 2, se.lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(o + 3, se.hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);   // the block sums are stored before arriving
-      const uint32_t old =
-          __hip_atomic_fetch_add(&p.glob->arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = old == (uint32_t)(p.nb - 1);
-    }
-    __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_last)) return;   // whole block
+  const int j0 = b * p.chunkd, j1 = min(p.V, j0 + p.chunkd);
+  Fx sr = fx_zero(), se = fx_zero();
+  for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
+    Fx wr, we;
+    draw_weights(p, rs, a, residual != 0, j, wr, we);
+    fx_add(sr, wr);
+    fx_add(se, we);
   }
-  // ---- the last block: the draw --------------------------------------------
-  for (int k = threadIdx.x; k < p.nb; k += kBlock) {
-    const u64 *o = p.blk + 4 * k;
-    sb_res[k] = Fx{__hip_atomic_load(o + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                   __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
-    sb_e[k] = Fx{__hip_atomic_load(o + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                 __hip_atomic_load(o + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
-  }
-  __syncthreads();
+  sr = fx_block_sum(sr, wsum);
+  se = fx_block_sum(se, wsum);
   if (threadIdx.x == 0) {
-    Fx wres = fx_zero(), we = fx_zero();
-    for (int k = 0; k < p.nb; ++k) {
-      fx_add(wres, sb_res[k]);
-      fx_add(we, sb_e[k]);
+    u64 *o = p.blk + 4 * b;
+    o[0] = sr.lo;
+    o[1] = sr.hi;
+    o[2] = se.lo;
+    o[3] = se.hi;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
+  __shared__ Fx wsum[kBlock / kWave];
+  __shared__ int s_blk, s_lastnz, s_pick;
+  __shared__ Fx s_before;
+  const int a = accepted_run(p);
+  const int residual = a < p.M - 1;
+  const RowState rs = p.rows[a];
+  // thread t holds chunks k0 .. k1-1 (in order); all their sums are loaded
+  // before any is used
+  constexpr int kPer = kMaxDrawBlocks / kBlock;
+  const int per = (p.nbd + kBlock - 1) / kBlock;
+  const int k0 = min(p.nbd, (int)threadIdx.x * per), k1 = min(p.nbd, k0 + per);
+  Fx cr[kPer], ce[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cr[i] = ce[i] = fx_zero();
+    if (k0 + i < k1) {
+      const u64 *o = p.blk + 4 * (k0 + i);
+      cr[i] = Fx{o[0], o[1]};
+      ce[i] = Fx{o[2], o[3]};
     }
-    const int use_res = residual && fx_nonzero(wres);
-    const Fx W = use_res ? wres : we;
-    const Fx target = to_fx((double)p.u[p.M - 1] * fx_to_double(W));
-    Fx cum = fx_zero();
-    int blk = -1, last_nz = -1;
-    Fx last_before = fx_zero();
-    for (int k = 0; k < p.nb; ++k) {
-      const Fx s = use_res ? sb_res[k] : sb_e[k];
-      const Fx next = fx_sum(cum, s);
-      if (fx_gt(next, target)) { blk = k; break; }
-      if (fx_nonzero(s)) { last_nz = k; last_before = cum; }
-      cum = next;
-    }
-    s_use_res = use_res;
-    s_target = target;
-    s_pick = p.V - 1;
-    if (blk >= 0) {
-      s_mode = 0;            // the crossing lies in block blk
-      s_blk = blk;
-      s_before = cum;
-    } else {
-      s_mode = 1;            // rounding passed the end: last positive entry of that block
-      s_blk = last_nz;
-      s_before = last_before;
-    }
-    p.glob->arrived = 0u;     // ready for the next call
+  }
+  Fx lres = fx_zero(), le = fx_zero();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    fx_add(lres, cr[i]);
+    fx_add(le, ce[i]);
+  }
+  const Fx tres = fx_block_sum(lres, wsum);
+  const Fx te = fx_block_sum(le, wsum);
+  const bool use_res = residual && fx_nonzero(tres);
+  const Fx target = to_fx((double)p.u[p.M - 1] * fx_to_double(use_res ? tres : te));
+  Fx total_unused;
+  Fx cum = fx_block_exclusive(use_res ? lres : le, wsum, total_unused);
+  if (threadIdx.x == 0) {
+    s_blk = 0x7FFFFFFF;
+    s_lastnz = -1;
+    s_pick = -1;
   }
   __syncthreads();
-  const bool exact = s_mode == 0;
-  const int blk = s_blk;
-  if (blk >= 0) {
-    const int j0 = blk * p.chunk, j1 = min(p.V, j0 + p.chunk);
-    const bool use_res = s_use_res != 0;
-    for (int base = j0; base < j1; base += kBlock * kDrawPer) {
-      // thread t holds entries base + kDrawPer*t .. +kDrawPer-1
-      Fx w[kDrawPer];
-      Fx mine = fx_zero();
-      const int jt = base + kDrawPer * threadIdx.x;
+  int found = -1, lastnz = -1;
+  Fx found_before = fx_zero();
 #pragma unroll
-      for (int i = 0; i < kDrawPer; ++i) {
-        Fx wr = fx_zero(), we = fx_zero();
-        if (jt + i < j1) draw_weights(p, rs, a, residual != 0, jt + i, wr, we);
-        w[i] = use_res ? wr : we;
-        fx_add(mine, w[i]);
-      }
+  for (int i = 0; i < kPer; ++i) {
+    const Fx s = use_res ? cr[i] : ce[i];
+    const Fx next = fx_sum(cum, s);
+    if (k0 + i < k1) {
+      if (found < 0 && fx_gt(next, target)) { found = k0 + i; found_before = cum; }
+      if (fx_nonzero(s)) lastnz = k0 + i;
+    }
+    cum = next;
+  }
+  // prefix sums only grow: the first crossing chunk is the least one found
+  if (found >= 0) atomicMin(&s_blk, found);
+  if (lastnz >= 0) atomicMax(&s_lastnz, lastnz);
+  __syncthreads();
+  if (found >= 0 && found == s_blk) s_before = found_before;
+  __syncthreads();
+  const bool exact = s_blk != 0x7FFFFFFF;
+  // exact: the crossing lies in chunk s_blk; otherwise rounding passed the
+  // end and the pick is the last positive entry of the last positive chunk
+  const int blk = exact ? s_blk : s_lastnz;
+  if (blk >= 0) {
+    const int j0 = blk * p.chunkd, j1 = min(p.V, j0 + p.chunkd);
+    for (int base = j0; base < j1; base += kBlock) {
+      // thread t holds entry base + t
+      const int jt = base + (int)threadIdx.x;
+      Fx wr = fx_zero(), we = fx_zero();
+      if (jt < j1) draw_weights(p, rs, a, residual != 0, jt, wr, we);
+      const Fx w = use_res ? wr : we;
       Fx total;
-      const Fx before = fx_sum(s_before, fx_block_exclusive(mine, wsum, total));
+      const Fx before = fx_sum(s_before, fx_block_exclusive(w, wsum, total));
       if (exact) {
-        // the thread whose range crosses the target picks inside it
-        if (!fx_gt(before, s_target) && fx_gt(fx_sum(before, mine), s_target)) {
-          Fx c = before;
-          for (int i = 0; i < kDrawPer; ++i) {
-            fx_add(c, w[i]);
-            if (fx_gt(c, s_target)) { s_pick = jt + i; break; }
-          }
-        }
-      } else {
-        int lastj = -1;
-        for (int i = 0; i < kDrawPer; ++i)
-          if (fx_nonzero(w[i])) lastj = jt + i;
-        if (lastj >= 0) atomicMax(&s_pick, lastj);
+        // the entry whose weight crosses the target is the pick
+        if (!fx_gt(before, target) && fx_gt(fx_sum(before, w), target)) s_pick = jt;
+      } else if (fx_nonzero(w)) {
+        atomicMax(&s_pick, jt);
       }
       __syncthreads();
       if (threadIdx.x == 0) s_before = fx_sum(s_before, total);
@@ -752,7 +784,7 @@ __global__ __launch_bounds__(kBlock) void rej_draw(RejArgs p) {
     }
   }
   __syncthreads();
-  const int pick = s_pick;
+  const int pick = s_pick < 0 ? p.V - 1 : s_pick;   // no positive weight at all: the last id
   if (threadIdx.x < p.M) {
     const int i = threadIdx.x;
     p.tokens[i] = (i < a) ? p.drafts[i] : (i == a ? pick : -1);
@@ -797,6 +829,7 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   p.z = logits; p.ldl = ldl; p.q = q; p.ldq = ldq; p.drafts = drafts; p.u = u;
   p.T = (double)temperature; p.top_p = (double)top_p;
   p.M = M; p.V = V; p.nb = blocks_per_row(V); p.chunk = (V + p.nb - 1) / p.nb;
+  p.nbd = draw_blocks(V); p.chunkd = (V + p.nbd - 1) / p.nbd;
   p.base_len = base_len; p.tokens = tokens; p.counts = counts; p.rollback = rollback;
   p.maxp = reinterpret_cast<float *>(w + L.maxp);
   p.zmax = reinterpret_cast<float *>(w + L.zmax);
@@ -805,7 +838,6 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   p.sel = reinterpret_cast<SelState *>(w + L.sel);
   p.rows = reinterpret_cast<RowState *>(w + L.rows);
   p.acc = reinterpret_cast<AccIn *>(w + L.acc);
-  p.glob = reinterpret_cast<Global *>(w + L.glob);
   p.blk = reinterpret_cast<u64 *>(w + L.blk);
   const dim3 rows_grid(p.nb, M);
   hipLaunchKernelGGL(rej_rowmax, rows_grid, dim3(kBlock), 0, stream, p);
@@ -814,7 +846,8 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   for (int pass = 0; pass < passes; ++pass)
     hipLaunchKernelGGL(rej_pass, rows_grid, dim3(kBlock), 0, stream, p, pass, with_hist);
   hipLaunchKernelGGL(rej_select, dim3(M), dim3(kBlock), 0, stream, p);
-  hipLaunchKernelGGL(rej_draw, dim3(p.nb), dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL(rej_draw_sums, dim3(p.nbd), dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL(rej_draw_pick, dim3(1), dim3(kBlock), 0, stream, p);
   return hipGetLastError();
 }
 

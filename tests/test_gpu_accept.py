@@ -124,6 +124,41 @@ def test_out_of_range_and_zero_probability_drafts():
         check_same(gpu_rej(z, q, d, u, 1.0, 0.5, 0), o, f"drafts {d.tolist()}")
 
 
+def test_draw_at_the_top_of_the_range_picks_the_last_positive_weight():
+    # u = 1 (one past the documented range) puts the draw target at the total
+    # weight: no prefix passes it, and both sides pick the last entry with a
+    # positive weight; the nucleus ends well before the last id
+    rng = np.random.default_rng(13)
+    for trial in range(6):
+        M, V = 4, 3000 + 997 * trial
+        z = rng.standard_normal((M, V)).astype(np.float32)
+        z[:, V // 2:] -= 40.0                       # the upper half is outside the nucleus
+        q = W.rand_dirichlet_rows(rng, M - 1, V, 1.0)
+        d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+        if trial % 2:
+            d[1] = V - 1                            # a rejection: the residual draw
+        u = np.array([0.0, 0.0, 0.0, 1.0], np.float32)
+        o = oracle.accept_rejection(z, q, d, u, 0.7, 0.9, 0)
+        check_same(gpu_rej(z, q, d, u, 0.7, 0.9, 0), o, f"u=1 trial={trial}")
+
+
+@pytest.mark.parametrize("V", [1000, 262144])
+def test_rejection_on_peaked_logits(V):
+    # logits of the spread an LM head produces (std ~300): almost every weight
+    # is below the fixed-point resolution and its exponential is skipped
+    rng = np.random.default_rng(V)
+    M = 8
+    for trial in range(3):
+        z = (rng.standard_normal((M, V)) * 300.0).astype(np.float32)
+        z[:, rng.integers(0, V, 5)] = z.max() - np.float32(0.5)   # a few near the top
+        q = W.rand_dirichlet_rows(rng, M - 1, V, 0.1)
+        d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+        d[trial + 2] = int(rng.integers(0, V))
+        u = W.rand_uniforms(rng, M)
+        o = oracle.accept_rejection(z, q, d, u, 0.6, 0.95, 5, with_margins=True)
+        check_same(gpu_rej(z, q, d, u, 0.6, 0.95, 5), o[:3], f"peaked V={V} trial={trial}", o[3])
+
+
 def test_same_trials_as_the_oracle_law():
     # The GPU reproduces the oracle trial by trial on the uniforms the oracle's
     # chi-square tests use, so the sampling law checked there holds here too.
