@@ -121,6 +121,8 @@ int mtp_verify_gemm(int format, int M, int N, int K, const uint16_t *x, int64_t 
   if (!y && !y_bf16) return fail(MTP_ERR_NULL, "%s: y or y_bf16 is required", who);
   if (ldx < K) return fail(MTP_ERR_SHAPE, "%s: ldx=%lld < K=%d", who, (long long)ldx, K);
   if (ldx % 8 || !aligned(x, 16)) return fail(MTP_ERR_ALIGN, "%s: x must be 16-byte aligned with ldx %% 8 == 0", who);
+  if (((int64_t)(M - 1) * ldx + K) * 2 >= ((int64_t)1 << 31))
+    return fail(MTP_ERR_SHAPE, "%s: the %d activation rows span 2 GiB or more", who, M);
   if (y && ldy < N) return fail(MTP_ERR_SHAPE, "%s: ldy=%lld < N=%d", who, (long long)ldy, N);
   if (y_bf16 && ldyb < N) return fail(MTP_ERR_SHAPE, "%s: ldyb=%lld < N=%d", who, (long long)ldyb, N);
   if (y && !aligned(y, 4)) return fail(MTP_ERR_ALIGN, "%s: y must be 4-byte aligned", who);

@@ -127,6 +127,7 @@ template <> struct Blk<MTP_FMT_Q4_0> {
 using Window = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // 32-bit untyped data, gfx9 family
 constexpr int kLoadNT = 2;               // cache policy: non-temporal
+constexpr uint32_t kXWindow = 0x80000000u;  // activation window bytes (offsets past it read 0)
 
 __device__ __forceinline__ Window block_window(const uint8_t *p, bool valid) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p), 0, valid ? kPairBytes : 0,
@@ -380,18 +381,48 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   const int rstep = nthreads / vpr, vstep = nthreads - rstep * vpr;
   const int xr = __builtin_amdgcn_readfirstlane((M * vpr + nthreads - 1) / nthreads);
   int xm = threadIdx.x / vpr, xvi = threadIdx.x - xm * vpr;
-  auto advance = [&](int &m, int &v) {
-    v += vstep;
-    m += rstep;
-    if (v >= vpr) {
-      v -= vpr;
-      ++m;
+  // The walk keeps, per thread, (m, v) and the vector's byte offsets: in x
+  // (dense rows: from xs.base; a gathered row list computes its row address)
+  // and in LDS.  A round advances them by fixed steps with one wrap check,
+  // and only rounds below xr run at all.  Dense rows are read through a
+  // buffer window whose loads past its range return zeros, so a vector past
+  // K or past the last row needs no separate masking.
+  const bool dense = xs.idx == nullptr;
+  const uint32_t ld2 = (uint32_t)xs.ld * 2u;
+  const uint32_t gstep = (uint32_t)rstep * ld2 + (uint32_t)vstep * 16u;
+  const uint32_t gwrap = ld2 - (uint32_t)vpr * 16u;           // (mod 2^32)
+  const int lstep = rstep * rowb + vstep * 16, lwrap = rowb - vpr * 16;
+  const int vk = min(vpr, (K - k0) / 8);                        // vectors of a row inside K
+  uint32_t goff = (uint32_t)xm * ld2 + (uint32_t)(k0 + 8 * xvi) * 2u;
+  int loff = xm * rowb + xvi * 16;
+  const Window xwin = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(xs.base), 0,
+                                                        (int)kXWindow, kRsrcWord3);
+  auto step = [&]() {
+    xvi += vstep;
+    xm += rstep;
+    goff += gstep;
+    loff += lstep;
+    if (xvi >= vpr) {
+      xvi -= vpr;
+      ++xm;
+      goff += gwrap;
+      loff += lwrap;
     }
   };
-  // one staged vector: LDS store (rows < M) and, for Q4_0, its block sum
-  auto stage = [&](u32x4 v, int m, int vi) {
+  auto load_x = [&]() -> u32x4 {
+    const bool ok = xm < M && xvi < vk;
+    if (dense)
+      return __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(xwin, ok ? goff : kXWindow, 0, 0));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k0 + 8 * xvi);
+    return v;
+  };
+  // one staged vector: LDS store (rows < M; loff < 0 otherwise) and, for
+  // Q4_0, its block sum (c: the accumulator-start index of its block)
+  auto stage = [&](u32x4 v, int lo, int c) {
     const u32x4 val = encode(v);
-    if (m < M) *reinterpret_cast<u32x4 *>(lds + m * rowb + vi * 16) = val;
+    if (lo >= 0) *reinterpret_cast<u32x4 *>(lds + lo) = val;
     if constexpr (FMT == MTP_FMT_Q4_0) {
       float s = (bf16_to_f32(v.x) + bf16_to_f32(v.x >> 16)) +
                 (bf16_to_f32(v.y) + bf16_to_f32(v.y >> 16));
@@ -399,23 +430,21 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
            (bf16_to_f32(v.w) + bf16_to_f32(v.w >> 16));
       s += quad_xor1(s);
       s += quad_xor2(s);
-      if ((lane & 3) == 0 && m < M) cinit[(vi >> 2) * 16 + m] = -136.0f * s;
+      if ((lane & 3) == 0 && lo >= 0) cinit[c] = -136.0f * s;
     }
   };
   // straight-line code for the first kXU rounds (no loop around the loads, so
   // the waits before the stores count only the activation loads)
   u32x4 xv[kXU];
-  const int xm0 = xm, xvi0 = xvi;
+  int xl[kXU], xc[kXU];
 #pragma unroll
   for (int u = 0; u < kXU; ++u) {
-    const int k = k0 + xvi * 8;
-    const bool ok = xm < M && k < K;
-    xv[u] = u32x4{0u, 0u, 0u, 0u};
     if (u < xr) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(xs.row(xm < M ? xm : 0) + (ok ? k : k0));
-      if (ok) xv[u] = v;
+      xv[u] = load_x();
+      xl[u] = xm < M ? loff : -1;
+      xc[u] = (xvi >> 2) * 16 + xm;
+      step();
     }
-    advance(xm, xvi);
   }
   __builtin_amdgcn_sched_barrier(0);
   constexpr int kEarly = PP < kPPShallow ? PP : kPPShallow;
@@ -423,26 +452,18 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
 #pragma unroll
   for (int i = 0; i < kEarly; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
-  {
-    int sm = xm0, sv = xvi0;   // the same walk again for the stores
 #pragma unroll
-    for (int u = 0; u < kXU; ++u) {
-      if (u < xr) stage(xv[u], sm, sv);
-      advance(sm, sv);
-    }
-  }
+  for (int u = 0; u < kXU; ++u)
+    if (u < xr) stage(xv[u], xl[u], xc[u]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = kEarly; i < PP; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
   // rounds beyond kXU (only very long staged rows)
   for (int u = kXU; u < xr; ++u) {
-    const int k = k0 + xvi * 8;
-    const bool ok = xm < M && k < K;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok) v = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k);
-    stage(v, xm, xvi);
-    advance(xm, xvi);
+    const u32x4 v = load_x();
+    stage(v, xm < M ? loff : -1, (xvi >> 2) * 16 + xm);
+    step();
   }
   {
     const bool any = __builtin_amdgcn_ballot_w64(ovf != 0u) != 0ull;

@@ -124,7 +124,8 @@ int mtp_pack_weights(int format, int count, int N, int K, const uint8_t *codes,
  *   format       MTP_FMT_NVFP4 or MTP_FMT_Q4_0
  *   M            1..MTP_MAX_M rows (the committed token plus the drafts)
  *   N, K         output columns (>= 1) and reduction length (multiple of 32)
- *   x, ldx       bf16 [M][ldx], ldx >= K, ldx % 8 == 0, x 16-byte aligned
+ *   x, ldx       bf16 [M][ldx], ldx >= K, ldx % 8 == 0, x 16-byte aligned;
+ *                the M rows span less than 2 GiB ((M - 1) * ldx + K < 2^30)
  *   packed       the weight matrix in the packed layout (mtp_pack_weights),
  *                16-byte aligned
  *   global_scale (host) fp32 multiplier applied to every weight

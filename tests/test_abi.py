@@ -77,6 +77,8 @@ BIG = dict(M=16, N=5120, K=17408, ldx=17408, ldy=5120)   # K split over workgrou
     (dict(ldx=128), -2), (dict(ldx=260), -3), (dict(x=FAKE_ODD), -3),
     (dict(packed=FAKE_ODD), -3), (dict(ldy=10), -2), (BIG, -5),
     (dict(BIG, ws=ctypes.c_void_p(0x100010), wsb=1 << 30), -3),
+    (dict(M=2, ldx=1 << 30), -2),                        # rows span 2 GiB
+    (dict(M=16, ldx=((1 << 30) // 15 + 8) & ~7), -2),
 ])
 def test_gemm_rejects_bad_arguments(kw, code):
     assert gemm(**kw) == code
