@@ -170,7 +170,7 @@ def config3_inputs(seed_offset: int = 0, M: int = 8, K: int = 5376, V: int = 262
                    alpha: float = 0.1) -> dict:
     """LM-head verification + acceptance inputs.  The planted match length L
     and the filler ids are drawn here; turning L into draft ids needs the
-    target's argmax, which the caller takes from the oracle."""
+    target's argmax, which the caller supplies (the oracle's in the tests)."""
     r = streams(3, seed_offset)
     x = rand_bf16(r["x"], (M, K))
     w = rand_weight(FMT_NVFP4, r["codes"], r["scales"], V, K)
