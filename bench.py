@@ -307,8 +307,8 @@ def extra_moe(bv, dev, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this verify-pass build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only (the verify pass here has no multi-GPU "
+              "path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import bit_verify_gemm_amd as bv
     bv.lib()
