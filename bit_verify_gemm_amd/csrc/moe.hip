@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void moe_combine(MoeArgs a) {
 // expert slot share its tg tile groups, so that the grid holds about
 // kWaveTarget waves: a workgroup stages its rows once for several tile
 // groups when there are many slots.
-constexpr int kWaveTarget = 2048;   // 8 waves on each of the 256 CUs
+constexpr int kWaveTarget = 4096;   // 16 waves per CU on 256 CUs; later workgroups wait for a slot
 
 struct MoePlan {
   int TW, J, S, ppj, tg, G, threads;
