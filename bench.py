@@ -7,7 +7,8 @@ call over one batch of activations (this workload's whole pass).
 
 The same run also reports, as context next to the headline, the other
 steps of the verify pass at their own workloads:
-* the Q4_0 projections of one 27B-class decoder layer (M = 8),
+* the Q4_0 projections of one 27B-class decoder layer (M = 8), one by one
+  and with Q|K|V and gate|up fused along N,
 * the 5376 -> 262144 LM head (M = 8) and the greedy and rejection accept
   steps on its logits,
 * the routed MoE pass (8 tokens, 128 experts, top-8, 2048 -> 768 -> 2048),
@@ -233,6 +234,24 @@ def extra_q4_layer(bv, dev, steps, warmup):
         torch.cuda.empty_cache()
     out["layer"] = {"bytes": total_bytes, "us": round(total_us, 3),
                     "gbs": round(total_bytes / (total_us * 1e-6) / 1e9, 1)}
+    # the same layer with the projections that share an input fused along N
+    # (Q|K|V and gate|up), as a decoder runs them
+    P = cfg["proj"]
+    fused_us = out["o"]["us"] + out["down"]["us"]
+    for fname, names in (("qkv_fused", ("q", "k", "v")), ("gate_up_fused", ("gate", "up"))):
+        ws = [P[n]["w"] for n in names]
+        fw = {"format": W.FMT_Q4_0, "K": ws[0]["K"], "N": sum(w["N"] for w in ws), "g": 1.0,
+              "codes": np.concatenate([w["codes"] for w in ws]),
+              "scales": np.concatenate([w["scales"] for w in ws])}
+        gm = gemm_from_host(bv, fw, P[names[0]]["x"], 8, dev)
+        _, ms, _ = time_graph(gm, gm.R, steps, warmup)
+        out[fname] = {"N": gm.N, "K": gm.K, "us": round(ms * 1e3, 3),
+                      "gbs": round(gm.bytes / (ms * 1e-3) / 1e9, 1)}
+        fused_us += ms * 1e3
+        del gm
+        torch.cuda.empty_cache()
+    out["layer_fused"] = {"bytes": total_bytes, "us": round(fused_us, 3),
+                          "gbs": round(total_bytes / (fused_us * 1e-6) / 1e9, 1)}
     return out
 
 
