@@ -83,13 +83,15 @@ inline void allow_large_lds(Kernel *kernel) {
   done.push_back(k);
 }
 
-// Activation rows: row m is base + idx[m] * ld (idx == nullptr: m).
+// Activation rows: row m is base + (idx[m] / div) * ld (idx == nullptr: m).
+// idx may point to global memory or LDS.
 struct XSource {
   const uint16_t *base;
   int64_t ld;
   const int32_t *idx;
+  int div;
   __device__ __forceinline__ const uint16_t *row(int m) const {
-    return base + (int64_t)(idx ? idx[m] : m) * ld;
+    return base + (int64_t)(idx ? idx[m] / div : m) * ld;
   }
 };
 
@@ -288,7 +290,7 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4)
 // Every thread of the workgroup calls run with the same arguments;
 // sync_entry must be true when the workgroup ran the engine before (its LDS
 // may still be in use).
-template <int FMT, int PP, int NT, bool LOCAL, typename TileOf, typename Epi>
+template <int FMT, int PP, int NT, bool LOCAL, bool GATHER, typename TileOf, typename Epi>
 __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
                                     const Plan &pl, const TileOf &tile_of, const Fixup &fx,
                                     uint8_t *lds, bool sync_entry, Epi &&epi) {
@@ -322,16 +324,19 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   // load stream: position si of tile group su is block si / NT of the slice
   // of the wave's tile si % NT; positions past the slice, past the matrix or
   // past the last tile group get empty windows
+  // (the NT tile ids are two plain scalars, not an array: a select between
+  // array elements becomes an indexed private-memory load, whose wait then
+  // drains every weight load in flight)
   int su = 0, si = 0;
-  int stile[NT];
+  int stile0 = -1, stile1 = -1;
   auto tiles_at = [&](int u) {
-#pragma unroll
-    for (int q = 0; q < NT; ++q)
-      stile[q] = __builtin_amdgcn_readfirstlane(tile_of(pl.tg_first + u * pl.tg_step, NT * tw + q));
+    const int tg = pl.tg_first + u * pl.tg_step;
+    stile0 = __builtin_amdgcn_readfirstlane(tile_of(tg, NT * tw));
+    stile1 = NT == 1 ? stile0 : __builtin_amdgcn_readfirstlane(tile_of(tg, NT * tw + NT - 1));
   };
   tiles_at(0);
   auto next_block = [&]() -> Window {
-    const int t = (NT == 1 || si % NT == 0) ? stile[0] : stile[NT - 1];
+    const int t = (NT == 1 || si % NT == 0) ? stile0 : stile1;
     const int pi = si / NT;
     const bool valid = pi < n && t >= 0;
     const int64_t blk = valid ? ((int64_t)t * P + pa + js + pi) : 0;
@@ -382,12 +387,14 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   const int xr = __builtin_amdgcn_readfirstlane((M * vpr + nthreads - 1) / nthreads);
   int xm = threadIdx.x / vpr, xvi = threadIdx.x - xm * vpr;
   // The walk keeps, per thread, (m, v) and the vector's byte offsets: in x
-  // (dense rows: from xs.base; a gathered row list computes its row address)
-  // and in LDS.  A round advances them by fixed steps with one wrap check,
-  // and only rounds below xr run at all.  Dense rows are read through a
-  // buffer window whose loads past its range return zeros, so a vector past
-  // K or past the last row needs no separate masking.
-  const bool dense = xs.idx == nullptr;
+  // (dense rows, from xs.base) and in LDS.  A round advances them by fixed steps with one wrap check,
+  // and only rounds below xr run at all.  Rows are read through a buffer
+  // window whose loads past its range return zeros, so a vector past K or
+  // past the last row needs no separate masking.  Gathered rows (GATHER:
+  // xs.idx lists them) take their index from a table that every wave loads
+  // once (lane m holds row m's), so no index load sits between the loads of
+  // the staging; their byte offsets stay below 2^31 (the callers' row lists
+  // index at most 1024 rows of under 2^16 vectors).
   const uint32_t ld2 = (uint32_t)xs.ld * 2u;
   const uint32_t gstep = (uint32_t)rstep * ld2 + (uint32_t)vstep * 16u;
   const uint32_t gwrap = ld2 - (uint32_t)vpr * 16u;           // (mod 2^32)
@@ -395,6 +402,13 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   const int vk = min(vpr, (K - k0) / 8);                        // vectors of a row inside K
   uint32_t goff = (uint32_t)xm * ld2 + (uint32_t)(k0 + 8 * xvi) * 2u;
   int loff = xm * rowb + xvi * 16;
+  int grow = 0;
+  if constexpr (GATHER) {
+    // (one lane shuffle takes the wait for the table here, in straight-line
+    // code: a first use inside the conditional rounds below would wait for
+    // every load in flight at each of them)
+    grow = __shfl(xs.idx[lane < M ? lane : M - 1] / xs.div, lane);
+  }
   const Window xwin = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(xs.base), 0,
                                                         (int)kXWindow, kRsrcWord3);
   auto step = [&]() {
@@ -411,12 +425,11 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   };
   auto load_x = [&]() -> u32x4 {
     const bool ok = xm < M && xvi < vk;
-    if (dense)
-      return __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(xwin, ok ? goff : kXWindow, 0, 0));
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok) v = *reinterpret_cast<const u32x4 *>(xs.row(xm) + k0 + 8 * xvi);
-    return v;
+    uint32_t off = goff;
+    if constexpr (GATHER)
+      off = (uint32_t)__shfl(grow, ok ? xm : 0) * ld2 + (uint32_t)(k0 + 8 * xvi) * 2u;
+    return __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(xwin, ok ? off : kXWindow, 0, 0));
   };
   // one staged vector: LDS store (rows < M; loff < 0 otherwise) and, for
   // Q4_0, its block sum (c: the accumulator-start index of its block)

@@ -138,9 +138,9 @@ __global__ __launch_bounds__(eng::kMaxThreads) void gemm_kernel(GemmArgs a) {
   pl.tg_first = blockIdx.x / a.KG;
   pl.tg_step = a.G;
   pl.tg_count = (a.TG - pl.tg_first + a.G - 1) / a.G;
-  const eng::XSource xs{a.x, a.ldx, nullptr};
-  eng::run<FMT, PP, 1, false>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx, lds,
-                              false, DenseEpi{&a});
+  const eng::XSource xs{a.x, a.ldx, nullptr, 1};
+  eng::run<FMT, PP, 1, false, false>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx,
+                                     lds, false, DenseEpi{&a});
 }
 
 // Slices of the K range: a function of the shape only (see engine.h).

@@ -8,20 +8,25 @@
 // verify batch (8 tokens, top-8 of 128) sits at 0.5, so here every unique
 // expert is simply read once for all of its rows.
 //
-// Pipeline (all on the device, no host round trip):
-//  1. route:   one workgroup sorts the T*topk (expert, pair) keys, lists the
-//              unique experts and each expert's pairs in pair order.
-//  2. gate_up: grid = (tile groups) x (unique-expert slots); a workgroup
-//              streams gate tiles and the matching up tiles of its expert
-//              through the engine of the dense GEMM (engine.h) for all rows
-//              of that expert and writes h = bf16(silu(gate) * up) per pair.
-//  3. down:    the same for y[pair] = W_d[e] . h[pair].
-//  4. combine: out[t] = sum over slots in slot order of w[t][s] * y[t, s].
+// Pipeline (two kernels, all on the device, no host round trip):
+//  1. gate_up: grid = (G workgroups) x (expert slots).  Every workgroup
+//              first derives the routing from topk_ids itself (see route),
+//              then streams gate tiles and the matching up tiles of its
+//              slot's expert through the engine of the dense GEMM (engine.h)
+//              for all rows of that expert and writes
+//              h = bf16(silu(gate) * up) per pair.
+//  2. down:    the same routing, then y[pair] = W_d[e] . h[pair]; each
+//              (pair, 16-column tile) it finishes counts one arrival for the
+//              pair's token, and the arrival that completes a token's valid
+//              pairs for a tile writes out[t] = sum over slots in slot order
+//              of w[t][s] * y[t, s] for those 16 columns.
 // The grids are sized for the largest possible number of unique experts;
 // slots beyond the actual count exit at once.  The K split of each expert
 // matrix depends only on its shape, so a pair's result does not depend on
 // which other tokens chose the same expert.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "engine.h"
 #include "internal.h"
@@ -30,10 +35,10 @@ namespace mtp {
 namespace {
 
 constexpr int kMaxPairs = 1024;
-constexpr int kInvalidKey = 0x7FFFFFFF - kMaxPairs;  // above e * kMaxPairs + p for e < 2^20
+constexpr int kNoExpert = 0x7FFFFFFF;   // routing key of a pair whose id is outside [0, E)
 
 struct MoeLayout {
-  size_t nuniq, uexp, ustart, ucount, spair, stok, h, y, bytes;
+  size_t cnt, h, y, bytes;
 };
 
 MoeLayout moe_layout(int T, int H, int F, int topk) {
@@ -45,12 +50,7 @@ MoeLayout moe_layout(int T, int H, int F, int topk) {
     o += (n + 255) & ~(size_t)255;
     return at;
   };
-  L.nuniq = take(sizeof(int32_t));
-  L.uexp = take(sizeof(int32_t) * P);
-  L.ustart = take(sizeof(int32_t) * P);
-  L.ucount = take(sizeof(int32_t) * P);
-  L.spair = take(sizeof(int32_t) * P);
-  L.stok = take(sizeof(int32_t) * P);
+  L.cnt = take(sizeof(uint32_t) * T * eng::tiles_of(H));
   L.h = take(sizeof(uint16_t) * P * F);
   L.y = take(sizeof(float) * P * H);
   L.bytes = o;
@@ -70,72 +70,120 @@ struct MoeArgs {
   int T, H, F, E, topk, P;
   int rc;                 // rows per engine pass
   struct { int TW, J, S, ppj, tg; } gu, dn;
-  int32_t *nuniq, *uexp, *ustart, *ucount, *spair, *stok;
-  uint16_t *h;
-  float *y;
+  uint32_t *cnt;          // [token][16-column tile of H]: pairs whose y is stored
+  uint16_t *h;            // [pair][F]
+  float *y;               // [pair][H]
 };
 
-// One workgroup of roundup(P, 64) threads: thread p ranks key p, then
-// position p of the sorted order knows whether it starts an expert; block
-// prefix counts of those starts number the unique experts.
-__global__ __launch_bounds__(kMaxPairs) void moe_route(MoeArgs a) {
-  __shared__ int32_t key[kMaxPairs];
-  __shared__ int32_t sorted[kMaxPairs];
-  __shared__ int32_t ustart[kMaxPairs];
-  __shared__ int32_t wave_starts[kMaxPairs / kWave], wave_valid[kMaxPairs / kWave];
-  const int p = threadIdx.x;
-  const int P = a.P;
-  int e = -1;
-  if (p < P) {
-    e = a.ids[p];
-    if (e < 0 || e >= a.E) e = -1;
-    // distinct keys: invalid pairs sort after every valid one, in pair order
-    key[p] = (e < 0) ? kInvalidKey + p : e * kMaxPairs + p;
+// The routing as one workgroup sees it (LDS).
+struct Route {
+  int32_t key[kMaxPairs];     // expert of pair p, kNoExpert for an id outside [0, E) or p >= P
+  int32_t order[kMaxPairs];   // the pairs ranked by (key, pair)
+  int32_t starts[kMaxPairs / kWave], valid[kMaxPairs / kWave];   // per 64 ranks
+  int32_t e, first, rows;     // the slot: expert (-1: none), ranks first .. first + rows - 1
+};
+
+// Every workgroup derives the routing from topk_ids itself (all of them get
+// the same): the pairs are ranked by (expert, pair index); the unique experts
+// of the valid pairs, in increasing order, are the slots, and slot s holds
+// the pairs of its expert in pair order.  Invalid pairs rank last and belong
+// to no slot.  Called by every thread of the workgroup.
+__device__ void route(const MoeArgs &a, Route &R, int slot) {
+  const int P = a.P, nt = blockDim.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  // keys past P (up to a multiple of 16) are kNoExpert: they rank below no
+  // pair, so the rank loop reads whole groups of 16
+  const int P16 = (P + 15) & ~15;
+  for (int p = threadIdx.x; p < P16; p += nt) {
+    const int e = p < P ? a.ids[p] : -1;
+    R.key[p] = (e >= 0 && e < a.E) ? e : kNoExpert;
   }
   __syncthreads();
-  if (p < P) {
-    int rank = 0;
-    for (int q = 0; q < P; ++q) rank += key[q] < key[p];
-    sorted[rank] = p;
+  for (int p = threadIdx.x; p < P; p += nt) {
+    const int k = R.key[p];
+    int r = 0;
+    for (int q0 = 0; q0 < P16; q0 += 16) {
+      int kq[16];   // all 16 loads in flight before the compares
+#pragma unroll
+      for (int j = 0; j < 16; ++j) kq[j] = R.key[q0 + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        r += (kq[j] < k || (kq[j] == k && q0 + j < p)) ? 1 : 0;
+    }
+    R.order[r] = p;
   }
   __syncthreads();
-  // sorted position p starts an expert when its expert differs from the one
-  // before; invalid pairs sort last and start nothing
-  bool first = false, valid = false;
-  int ke = 0;
-  if (p < P) {
-    const int pp = sorted[p];
-    ke = key[pp];
-    valid = ke < kInvalidKey;
-    first = valid && (p == 0 || key[sorted[p - 1]] / kMaxPairs != ke / kMaxPairs);
-    a.spair[p] = pp;
-    a.stok[p] = pp / a.topk;
-  }
-  const uint64_t fb = __builtin_amdgcn_ballot_w64(first);
-  const uint64_t vb = __builtin_amdgcn_ballot_w64(valid);
-  const int w = p / kWave, l = p % kWave;
-  if (l == 0) {
-    wave_starts[w] = __builtin_popcountll(fb);
-    wave_valid[w] = __builtin_popcountll(vb);
-  }
-  __syncthreads();
-  int u = __builtin_popcountll(fb & ((1ull << l) - 1ull)), nuniq = 0, nvalid = 0;
-  for (int q = 0; q < (int)(blockDim.x / kWave); ++q) {
-    if (q < w) u += wave_starts[q];
-    nuniq += wave_starts[q];
-    nvalid += wave_valid[q];   // the valid positions are a prefix of the order
-  }
-  if (first) {
-    ustart[u] = p;
-    a.uexp[u] = ke / kMaxPairs;
-    a.ustart[u] = p;
+  // rank i starts a slot when its pair is valid and its expert differs from
+  // that of rank i - 1; chunk c covers ranks 64c .. 64c + 63
+  const int nch = (P + kWave - 1) / kWave;
+  auto chunk = [&](int c, uint64_t &vb) -> uint64_t {
+    const int i = c * kWave + lane;
+    bool st = false, vd = false;
+    if (i < P) {
+      const int k = R.key[R.order[i]];
+      vd = k != kNoExpert;
+      st = vd && (i == 0 || R.key[R.order[i - 1]] != k);
+    }
+    vb = __ballot(vd);
+    return __ballot(st);
+  };
+  for (int c = wave; c < nch; c += nt / kWave) {
+    uint64_t vb;
+    const uint64_t sb = chunk(c, vb);
+    if (lane == 0) {
+      R.starts[c] = __popcll(sb);
+      R.valid[c] = __popcll(vb);
+    }
   }
   __syncthreads();
-  if (p < nuniq) a.ucount[p] = (p + 1 < nuniq ? ustart[p + 1] : nvalid) - ustart[p];
-  if (p == 0) *a.nuniq = nuniq;
-  // rows of h for invalid pairs are zero
-  if (a.h_out && p < P && e < 0)
-    for (int f = 0; f < a.F; ++f) a.h_out[(int64_t)p * a.F + f] = 0;
+  if (wave == 0) {
+    // the rank of start number `slot` and of the next start (or the number
+    // of valid pairs: they rank first)
+    int before = 0, nvalid = 0, first = -1, end = -1;
+    for (int c = 0; c < nch; ++c) {
+      const int sc = R.starts[c];
+      nvalid += R.valid[c];
+      for (int want = slot; want <= slot + 1; ++want) {
+        if (want >= before && want < before + sc) {
+          uint64_t vb;
+          uint64_t sb = chunk(c, vb);
+          for (int j = before; j < want; ++j) sb &= sb - 1;   // drop the earlier starts
+          const int pos = c * kWave + __ffsll((long long)sb) - 1;
+          if (want == slot) first = pos;
+          else end = pos;
+        }
+      }
+      before += sc;
+    }
+    if (end < 0) end = nvalid;
+    if (lane == 0) {
+      R.first = first;
+      R.rows = first < 0 ? 0 : end - first;
+      R.e = first < 0 ? -1 : R.key[R.order[first]];
+    }
+  }
+  __syncthreads();
+}
+
+// Set-up of one call, spread over the workgroups of the gate_up kernel (the
+// down kernel runs after it): clears the arrival counters and out (tokens
+// with no valid pair never complete an arrival and keep the zeros), and
+// writes zero rows of h_out for invalid pairs.  Workgroup b of nb takes its
+// share of each.
+__device__ void clear_call_state(const MoeArgs &a, const Route &R) {
+  const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
+  auto share = [&](int n, auto &&f) {
+    const int per = (n + nb - 1) / nb, i1 = min(n, (b + 1) * per);
+    for (int i = b * per + (int)threadIdx.x; i < i1; i += blockDim.x) f(i);
+  };
+  share(a.T * eng::tiles_of(a.H), [&](int i) {
+    __hip_atomic_store(a.cnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
+  share(a.T * a.H, [&](int i) { a.out[i] = 0.0f; });
+  if (a.h_out)
+    for (int p = b; p < a.P; p += nb)
+      if (R.key[p] == kNoExpert)
+        for (int f = threadIdx.x; f < a.F; f += blockDim.x) a.h_out[(int64_t)p * a.F + f] = 0;
 }
 
 // silu(v) = v / (1 + exp(-v)), written so that no intermediate overflows:
@@ -157,8 +205,15 @@ struct GateUpTiles {
 
 struct GateUpEpi {
   const MoeArgs *a;
-  int TWh, nthreads, mc, c0, first;
+  int TWh, nthreads, mc;
+  const int32_t *pairs;   // pair of each row of this pass (LDS)
   float gsc;
+  __device__ __forceinline__ void put(int m, int f, float gate, float up) const {
+    const uint16_t hb = f32_to_bf16_rne(silu(gate) * up);
+    const int pair = pairs[m];
+    a->h[(int64_t)pair * a->F + f] = hb;
+    if (a->h_out) a->h_out[(int64_t)pair * a->F + f] = hb;
+  }
   __device__ __forceinline__ void operator()(int tg, const f32x4 *fin) const {
     const int cols = TWh * 16;
     for (int o = threadIdx.x; o < mc * cols; o += nthreads) {
@@ -166,12 +221,8 @@ struct GateUpEpi {
       const int f = tg * cols + c;
       if (f < a->F) {
         const int q = c >> 4;
-        const float gate = gsc * eng::fin_at(fin, 2 * q, m, c & 15);
-        const float up = gsc * eng::fin_at(fin, 2 * q + 1, m, c & 15);
-        const uint16_t hb = f32_to_bf16_rne(silu(gate) * up);
-        const int pair = a->spair[first + c0 + m];
-        a->h[(int64_t)pair * a->F + f] = hb;
-        if (a->h_out) a->h_out[(int64_t)pair * a->F + f] = hb;
+        put(m, f, gsc * eng::fin_at(fin, 2 * q, m, c & 15),
+            gsc * eng::fin_at(fin, 2 * q + 1, m, c & 15));
       }
     }
   }
@@ -183,13 +234,7 @@ struct GateUpEpi {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = eng::acc_row(lane, i);
-      if (m < mc) {
-        const float gate = gsc * acc[0][i], up = gsc * acc[1][i];
-        const uint16_t hb = f32_to_bf16_rne(silu(gate) * up);
-        const int pair = a->spair[first + c0 + m];
-        a->h[(int64_t)pair * a->F + f] = hb;
-        if (a->h_out) a->h_out[(int64_t)pair * a->F + f] = hb;
-      }
+      if (m < mc) put(m, f, gsc * acc[0][i], gsc * acc[1][i]);
     }
   }
 };
@@ -198,9 +243,13 @@ struct GateUpEpi {
 template <int FMT, int PP, bool PAIRED>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int slot = blockIdx.y;
-  if (slot >= *a.nuniq) return;  // whole workgroup
-  const int e = a.uexp[slot], first = a.ustart[slot], rows = a.ucount[slot];
+  __shared__ Route R;
+  route(a, R, blockIdx.y);
+  clear_call_state(a, R);
+  const int e = __builtin_amdgcn_readfirstlane(R.e);
+  if (e < 0) return;  // a slot past the unique experts (whole workgroup)
+  const int first = __builtin_amdgcn_readfirstlane(R.first);
+  const int rows = __builtin_amdgcn_readfirstlane(R.rows);
   const int P = eng::pairs_of(a.H);
   const uint8_t *w = a.gu_packed + (int64_t)e * eng::packed_bytes(2 * a.F, a.H);
   eng::Plan pl;
@@ -212,24 +261,31 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   const float gsc = a.gu_global ? a.gu_global[e] : 1.0f;
   for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
-    const eng::XSource xs{a.x, a.H, a.stok + first + c0};
-    eng::run<FMT, PP, PAIRED ? 2 : 1, PAIRED>(
+    const int32_t *pairs = R.order + first + c0;
+    const eng::XSource xs{a.x, a.H, pairs, a.topk};   // row of pair p: token p / topk
+    eng::run<FMT, PP, PAIRED ? 2 : 1, PAIRED, true>(
         w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds, c0 > 0,
-        GateUpEpi{&a, TWh, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+        GateUpEpi{&a, TWh, pl.TW * pl.J * kWave, mc, pairs, gsc});
   }
 }
 
+// y rows are stored at agent scope: another workgroup (on another XCD) may
+// add them into out.
 struct DownEpi {
   const MoeArgs *a;
-  int TW, nthreads, mc, c0, first;
+  int TW, nthreads, mc;
+  const int32_t *pairs;
   float gsc;
+  __device__ __forceinline__ void put(int m, int n, float v) const {
+    __hip_atomic_store(a->y + (int64_t)pairs[m] * a->H + n, v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
   __device__ __forceinline__ void operator()(int tg, const f32x4 *fin) const {
     const int cols = TW * 16;
     for (int o = threadIdx.x; o < mc * cols; o += nthreads) {
       const int m = o / cols, c = o - m * cols;
       const int n = tg * cols + c;
-      if (n < a->H)
-        a->y[(int64_t)a->spair[first + c0 + m] * a->H + n] = gsc * eng::fin_at(fin, c >> 4, m, c & 15);
+      if (n < a->H) put(m, n, gsc * eng::fin_at(fin, c >> 4, m, c & 15));
     }
   }
   __device__ __forceinline__ void wave(int tg, int tw, const f32x4 *acc) const {
@@ -239,7 +295,7 @@ struct DownEpi {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = eng::acc_row(lane, i);
-      if (m < mc) a->y[(int64_t)a->spair[first + c0 + m] * a->H + n] = gsc * acc[0][i];
+      if (m < mc) put(m, n, gsc * acc[0][i]);
     }
   }
 };
@@ -252,13 +308,73 @@ struct DownTiles {
   }
 };
 
+// After the down passes of a workgroup (every thread calls it): once all of
+// its y stores are complete, each (row, tile) it produced counts one arrival
+// for the row's token and tile; the arrival that completes the token's
+// valid pairs writes out[t] for the tile's 16 columns, adding the token's
+// slots in slot order.
+__device__ void arrive_and_combine(const MoeArgs &a, const Route &R, const eng::Plan &pl,
+                                   int first, int rows) {
+  __shared__ int done_n;
+  __shared__ int done[eng::kMaxThreads];
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's y stores are complete
+  __syncthreads();                 // ... and every thread's
+  const int ntiles = eng::tiles_of(a.H);
+  const int per = pl.tg_count * pl.TW;   // tile positions of this workgroup
+  const int combos = per * rows;
+  for (int base = 0; base < combos; base += blockDim.x) {
+    if (threadIdx.x == 0) done_n = 0;
+    __syncthreads();
+    const int c = base + threadIdx.x;
+    if (c < combos) {
+      const int m = c / per, s = c - m * per;
+      const int tile = (pl.tg_first + (s / pl.TW) * pl.tg_step) * pl.TW + s % pl.TW;
+      if (tile < ntiles) {
+        const int t = R.order[first + m] / a.topk;
+        uint32_t need = 0;
+        for (int k = 0; k < a.topk; ++k) need += R.key[t * a.topk + k] != kNoExpert ? 1u : 0u;
+        const uint32_t old = __hip_atomic_fetch_add(a.cnt + (int64_t)t * ntiles + tile, 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old + 1u == need) done[atomicAdd(&done_n, 1)] = t * ntiles + tile;
+      }
+    }
+    __syncthreads();
+    const int nd = done_n;
+    for (int i = threadIdx.x; i < nd * 16; i += blockDim.x) {
+      const int d = done[i >> 4], t = d / ntiles;
+      const int n = (d - t * ntiles) * 16 + (i & 15);
+      float s = 0.0f;
+      for (int k0 = 0; k0 < a.topk; k0 += 8) {
+        // eight slots' loads in flight at once (an invalid slot's y is read
+        // but not used), then the sum in slot order
+        float yv[8], wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = t * a.topk + min(k0 + j, a.topk - 1);
+          yv[j] = __hip_atomic_load(a.y + (int64_t)p * a.H + n, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+          wv[j] = a.gw[p];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (k0 + j < a.topk && R.key[t * a.topk + k0 + j] != kNoExpert) s += wv[j] * yv[j];
+      }
+      a.out[(int64_t)t * a.H + n] = s;
+    }
+    __syncthreads();
+  }
+}
+
 // LOCAL: one slice per tile (J == 1), each wave finishes its own tile
 template <int FMT, int PP, bool LOCAL>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int slot = blockIdx.y;
-  if (slot >= *a.nuniq) return;  // whole workgroup
-  const int e = a.uexp[slot], first = a.ustart[slot], rows = a.ucount[slot];
+  __shared__ Route R;
+  route(a, R, blockIdx.y);
+  const int e = __builtin_amdgcn_readfirstlane(R.e);
+  if (e < 0) return;  // a slot past the unique experts (whole workgroup)
+  const int first = __builtin_amdgcn_readfirstlane(R.first);
+  const int rows = __builtin_amdgcn_readfirstlane(R.rows);
   const int P = eng::pairs_of(a.F);
   const uint8_t *w = a.dn_packed + (int64_t)e * eng::packed_bytes(a.H, a.F);
   eng::Plan pl;
@@ -269,31 +385,23 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   const float gsc = a.dn_global ? a.dn_global[e] : 1.0f;
   for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
-    const eng::XSource xs{a.h, a.F, a.spair + first + c0};
-    eng::run<FMT, PP, 1, LOCAL>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds,
-                                c0 > 0, DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, c0, first, gsc});
+    const int32_t *pairs = R.order + first + c0;
+    const eng::XSource xs{a.h, a.F, pairs, 1};
+    eng::run<FMT, PP, 1, LOCAL, true>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr},
+                                      lds, c0 > 0,
+                                      DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, pairs, gsc});
   }
-}
-
-__global__ __launch_bounds__(256) void moe_combine(MoeArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)a.T * a.H) return;
-  const int t = (int)(i / a.H), n = (int)(i - (int64_t)t * a.H);
-  float s = 0.0f;
-  for (int k = 0; k < a.topk; ++k) {
-    const int p = t * a.topk + k;
-    const int e = a.ids[p];
-    if (e >= 0 && e < a.E) s += a.gw[p] * a.y[(int64_t)p * a.H + n];
-  }
-  a.out[i] = s;
+  arrive_and_combine(a, R, pl, first, rows);
 }
 
 // Engine shape of one expert matrix: a single workgroup covers all slices
-// (S of about 8 pairs each); rc rows are staged per pass.  G workgroups per
-// expert slot share its tg tile groups, so that the grid holds about
-// kWaveTarget waves: a workgroup stages its rows once for several tile
-// groups when there are many slots.
-constexpr int kWaveTarget = 4096;   // 16 waves per CU on 256 CUs; later workgroups wait for a slot
+// (S of about 8 pairs each); rc rows are staged per pass.  Workgroups have
+// at most kMoeTiles waves of tiles, so that several share a CU (the kernels
+// hold more than 128 registers per lane, three waves per SIMD).  G
+// workgroups per expert slot share its tg tile groups, as many as the GPU
+// holds at once: a workgroup streams several tile groups (staging its rows
+// once) only when all slots' workgroups would not fit in one round.
+constexpr int kMoeTiles = 4;
 
 struct MoePlan {
   int TW, J, S, ppj, tg, G, threads;
@@ -326,18 +434,44 @@ MoePlan moe_plan(int format, int N, int K, int rc, int tw_max, bool paired) {
   return m;
 }
 
-void moe_spread(MoePlan &m, int slots) {
-  const int per_slot = std::max(1, kWaveTarget / (slots * (m.threads / kWave)));
+// resident: workgroups of the kernel the whole GPU holds at once
+void moe_spread(MoePlan &m, int slots, int resident) {
+  const int per_slot = std::max(1, resident / slots);
   const int rounds = (m.tg + per_slot - 1) / per_slot;   // tile groups per workgroup
   m.G = (m.tg + rounds - 1) / rounds;                     // balanced
+}
+
+// Workgroups of `kernel` (threads, dynamic LDS) resident on the current
+// device at once: per-CU occupancy from the runtime times the CU count.
+template <typename Kernel>
+int resident_workgroups(Kernel *kernel, int threads, size_t lds) {
+  struct Entry { const void *k; int threads; size_t lds; int dev, n; };
+  static std::mutex mu;
+  static std::vector<Entry> seen;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const void *k = reinterpret_cast<const void *>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry &e : seen)
+    if (e.k == k && e.threads == threads && e.lds == lds && e.dev == dev) return e.n;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 1;
+  (void)hipGetLastError();
+  seen.push_back(Entry{k, threads, lds, dev, per_cu * cus});
+  return per_cu * cus;
 }
 
 // Rows staged per pass: up to 16 (and T, which bounds the rows of an expert
 // unless a token repeats an expert), fewer if the staged rows would not fit.
 int moe_rows(int format, int T, int H, int F) {
   int rc = std::min(16, T);
-  while (rc > 1 && (moe_plan(format, 2 * F, H, rc, 4, true).lds > 144 * 1024 ||
-                    moe_plan(format, H, F, rc, 8, false).lds > 144 * 1024))
+  while (rc > 1 && (moe_plan(format, 2 * F, H, rc, kMoeTiles, true).lds > 144 * 1024 ||
+                    moe_plan(format, H, F, rc, kMoeTiles, false).lds > 144 * 1024))
     --rc;
   return rc;
 }
@@ -346,8 +480,8 @@ int moe_rows(int format, int T, int H, int F) {
 
 bool moe_fits(int format, int T, int H, int F) {
   const int rc = moe_rows(format, T, H, F);
-  return moe_plan(format, 2 * F, H, rc, 4, true).lds <= 144 * 1024 &&
-         moe_plan(format, H, F, rc, 8, false).lds <= 144 * 1024;
+  return moe_plan(format, 2 * F, H, rc, kMoeTiles, true).lds <= 144 * 1024 &&
+         moe_plan(format, H, F, rc, kMoeTiles, false).lds <= 144 * 1024;
 }
 
 size_t moe_ws_bytes(int T, int H, int F, int E, int topk) {
@@ -367,35 +501,24 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
   a.dn_packed = dn_packed; a.dn_global = dn_global;
   a.out = out; a.h_out = h_out;
   a.T = T; a.H = H; a.F = F; a.E = E; a.topk = topk; a.P = T * topk;
-  a.nuniq = reinterpret_cast<int32_t *>(w + L.nuniq);
-  a.uexp = reinterpret_cast<int32_t *>(w + L.uexp);
-  a.ustart = reinterpret_cast<int32_t *>(w + L.ustart);
-  a.ucount = reinterpret_cast<int32_t *>(w + L.ucount);
-  a.spair = reinterpret_cast<int32_t *>(w + L.spair);
-  a.stok = reinterpret_cast<int32_t *>(w + L.stok);
+  a.cnt = reinterpret_cast<uint32_t *>(w + L.cnt);
   a.h = reinterpret_cast<uint16_t *>(w + L.h);
   a.y = reinterpret_cast<float *>(w + L.y);
   a.rc = moe_rows(format, T, H, F);
   const int slots = (a.P < E) ? a.P : E;
-  MoePlan gu = moe_plan(format, 2 * F, H, a.rc, 4, true);
-  MoePlan dn = moe_plan(format, H, F, a.rc, 8, false);
-  moe_spread(gu, slots);
-  moe_spread(dn, slots);
+  MoePlan gu = moe_plan(format, 2 * F, H, a.rc, kMoeTiles, true);
+  MoePlan dn = moe_plan(format, H, F, a.rc, kMoeTiles, false);
   a.gu = {gu.TW, gu.J, gu.S, gu.ppj, gu.tg};
   a.dn = {dn.TW, dn.J, dn.S, dn.ppj, dn.tg};
-  const int route_threads = (a.P + kWave - 1) / kWave * kWave;
-  hipLaunchKernelGGL(moe_route, dim3(1), dim3(route_threads), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const dim3 gu_grid(gu.G, slots), dn_grid(dn.G, slots);
   auto go = [&](auto gate_up, auto down) {
     eng::allow_large_lds(gate_up);
     eng::allow_large_lds(down);
-    hipLaunchKernelGGL(gate_up, gu_grid, dim3(gu.threads), gu.lds, stream, a);
-    hipLaunchKernelGGL(down, dn_grid, dim3(dn.threads), dn.lds, stream, a);
+    moe_spread(gu, slots, resident_workgroups(gate_up, gu.threads, gu.lds));
+    moe_spread(dn, slots, resident_workgroups(down, dn.threads, dn.lds));
+    hipLaunchKernelGGL(gate_up, dim3(gu.G, slots), dim3(gu.threads), gu.lds, stream, a);
+    hipLaunchKernelGGL(down, dim3(dn.G, slots), dim3(dn.threads), dn.lds, stream, a);
   };
-  // four blocks per wave in flight: the grid holds about one 8-wave
-  // workgroup per CU
+  // four blocks per wave in flight
   constexpr int kD = eng::kPPDeep, kN = MTP_FMT_NVFP4, kQ = MTP_FMT_Q4_0;
   const bool pg = gu.J == 1, ld = dn.J == 1;
   if (format == kN) {
@@ -409,10 +532,6 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
     else    ld ? go(moe_gate_up<kQ, kD, false>, moe_down<kQ, kD, true>)
                : go(moe_gate_up<kQ, kD, false>, moe_down<kQ, kD, false>);
   }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int64_t TH = (int64_t)T * H;
-  hipLaunchKernelGGL(moe_combine, dim3((unsigned)((TH + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

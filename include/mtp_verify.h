@@ -180,7 +180,7 @@ int mtp_gemm_plan_info(int format, int M, int N, int K, int32_t *info, int n);
  *   gu_global       device fp32 [E] per-expert global scales, or NULL (1.0)
  *   dn_packed/dn_global  the same for the down projections (N = H, K = F),
  *                   expert e at e * mtp_packed_weight_bytes(H, F)
- *   out             fp32 [T][H]
+ *   out             fp32 [T][H] (must not overlap the inputs)
  *   h_out           optional bf16 [T*topk][F] copy of h (pair p = t*topk+s;
  *                   rows of out-of-range ids are zero); may be NULL
  *   ws, ws_bytes    at least mtp_moe_workspace_bytes(T, H, F, E, topk)

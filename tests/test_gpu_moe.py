@@ -106,3 +106,24 @@ def test_moe_128_experts_top8_full_size():
     cfg = W.config4()
     log("C4 unique experts", len(np.unique(cfg["ids"])))
     check(cfg, "C4")
+
+
+def test_many_pairs():
+    # 1024 (token, slot) pairs, the most the call takes: every workgroup ranks
+    # all of them, and an expert's 60-odd rows take several staging passes
+    check(tiny(77, T=128, E=16, topk=8, H=64, F=32), "moe 1024 pairs")
+
+
+def test_token_with_no_valid_expert():
+    cfg = tiny(12, T=3, E=4, topk=2, H=64, F=32)
+    cfg["ids"] = np.array([[0, 1], [-1, 9], [1, 1]], np.int32)
+    out, _ = run_moe(cfg)
+    assert np.all(out[1] == 0.0)
+    check(cfg, "token without a valid expert")
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_NVFP4, W.FMT_Q4_0])
+def test_k_split_over_waves(fmt):
+    # H = 4096 and F = 3072 cut each expert's K into two slices per tile
+    # (gate and up tiles in separate waves, the slice sums meeting in LDS)
+    check(tiny(13, T=2, E=3, topk=2, H=4096, F=3072, fmt=fmt), f"moe {fmt} K split")
