@@ -17,7 +17,7 @@ __all__ = [
     "FMT_NVFP4", "FMT_Q4_0", "MAX_M", "MtpError", "lib", "abi_version",
     "packed_weight_bytes", "pack_weights", "gemm_workspace_bytes", "gemm_workspace",
     "gemm_plan_info",
-    "moe_workspace_bytes", "accept_workspace_bytes",
+    "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -152,6 +152,12 @@ def accept_workspace_bytes(M: int, V: int) -> int:
     return int(lib().mtp_accept_workspace_bytes(M, V))
 
 
+def accept_workspace(M: int, V: int, device) -> torch.Tensor:
+    """A workspace for the accept calls on M x V logits (it may be kept for
+    later calls of either kind and any shape that fits)."""
+    return torch.empty(accept_workspace_bytes(M, V), dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes: int, device, ws):
     if nbytes == 0:
         return ws
@@ -210,7 +216,8 @@ def accept_greedy(logits: torch.Tensor, draft_ids: torch.Tensor | None, base_len
     """Returns (tokens[M] int32, counts[2] int32, rollback[1] int64) on the GPU."""
     M, V = logits.shape
     tok, cnt, rb = _accept_outputs(M, logits.device, outs)
-    ws = _workspace(accept_workspace_bytes(M, V), logits.device, ws)
+    if ws is None or _nbytes(ws) < accept_workspace_bytes(M, V):
+        ws = accept_workspace(M, V, logits.device)
     _check(lib().mtp_accept_greedy(_ptr(logits), M, V, _ld(logits), _ptr(draft_ids),
                                    int(base_len), _ptr(tok), _ptr(cnt), _ptr(rb), _ptr(ws),
                                    _nbytes(ws), _stream(stream)))
@@ -224,7 +231,8 @@ def accept_rejection(logits: torch.Tensor, draft_probs: torch.Tensor | None,
     """Returns (tokens[M] int32, counts[2] int32, rollback[1] int64) on the GPU."""
     M, V = logits.shape
     tok, cnt, rb = _accept_outputs(M, logits.device, outs)
-    ws = _workspace(accept_workspace_bytes(M, V), logits.device, ws)
+    if ws is None or _nbytes(ws) < accept_workspace_bytes(M, V):
+        ws = accept_workspace(M, V, logits.device)
     _check(lib().mtp_accept_rejection(_ptr(logits), M, V, _ld(logits), _ptr(draft_probs),
                                       _ld(draft_probs), _ptr(draft_ids), _ptr(uniforms),
                                       float(temperature), float(top_p), int(base_len), _ptr(tok),

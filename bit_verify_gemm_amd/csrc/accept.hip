@@ -111,15 +111,24 @@ __device__ __forceinline__ double fx_to_double(const Fx &a) {
   return ldexp((double)a.hi, -36) + ldexp((double)a.lo, -100);
 }
 
-__device__ __forceinline__ void fx_atomic_add(u64 *p, Fx v) {
-  if (v.lo) {
-    const u64 old = atomicAdd(p, v.lo);
-    if (old + v.lo < old) v.hi += 1ull;
-  }
-  if (v.hi) atomicAdd(p + 1, v.hi);
+// Sums shared by the blocks of a kernel are kept as three 64-bit limbs,
+// L0 += bits 0..31, L1 += bits 32..63, L2 += bits 64..127 of each
+// contribution, so that the atomic adds need no carry (and no returned
+// value); a limb of at most 2^20 contributions cannot overflow.
+__device__ __forceinline__ void fx_atomic_add3(u64 *p, Fx v) {
+  if (v.lo & 0xFFFFFFFFull) atomicAdd(p, v.lo & 0xFFFFFFFFull);
+  if (v.lo >> 32) atomicAdd(p + 1, v.lo >> 32);
+  if (v.hi) atomicAdd(p + 2, v.hi);
 }
 
-__device__ __forceinline__ Fx fx_load(const u64 *p) { return Fx{p[0], p[1]}; }
+__device__ __forceinline__ Fx fx_from3(u64 l0, u64 l1, u64 l2) {
+  Fx r;
+  r.lo = l0 + (l1 << 32);
+  r.hi = l2 + (l1 >> 32) + (r.lo < l0 ? 1ull : 0ull);
+  return r;
+}
+
+__device__ __forceinline__ Fx fx_load3(const u64 *p) { return fx_from3(p[0], p[1], p[2]); }
 
 __device__ __forceinline__ Fx fx_shfl_xor(const Fx &a, int m) {
   return Fx{(u64)__shfl_xor((long long)a.lo, m), (u64)__shfl_xor((long long)a.hi, m)};
@@ -176,6 +185,8 @@ struct AccIn {
   double px, qx;
 };
 
+constexpr int kMaxRows = 64;
+
 struct Layout {
   size_t maxp, zmax, hist, total, sel, rows, acc, blk, gpart, bytes;
 };
@@ -191,8 +202,8 @@ Layout layout(int M, int V) {
   };
   L.maxp = take(sizeof(float) * M * nb);
   L.zmax = take(sizeof(float) * M);
-  L.hist = take(sizeof(u64) * 3 * kBins * 4 * M);
-  L.total = take(sizeof(u64) * 2 * M);
+  L.hist = take(sizeof(u64) * 4 * kBins * 4 * M);
+  L.total = take(sizeof(u64) * 3 * M);
   L.sel = take(sizeof(SelState) * 4 * M);
   L.rows = take(sizeof(RowState) * M);
   L.acc = take(sizeof(AccIn) * M);
@@ -219,8 +230,8 @@ struct RejArgs {
   int64_t *rollback;
   float *maxp;      // [row][block] partial maxima
   float *zmax;      // [row]
-  u64 *hist;        // [pass][row][bin][lo, hi, count]
-  u64 *total;       // [row][lo, hi]
+  u64 *hist;        // [pass][row][bin][L0, L1, L2, count]
+  u64 *total;       // [row][L0, L1, L2]
   SelState *sel;    // [pass][row]: state after `pass` selections (pass >= 1)
   RowState *rows;
   AccIn *acc;       // [row]: inputs of draft row's acceptance test
@@ -228,7 +239,19 @@ struct RejArgs {
 };
 
 __device__ __forceinline__ u64 *hist_at(const RejArgs &p, int pass, int row) {
-  return p.hist + ((size_t)(pass * p.M + row) * kBins) * 3;
+  return p.hist + ((size_t)(pass * p.M + row) * kBins) * 4;
+}
+
+// Histogram of one row (global, limbs) into LDS as (mass lo, mass hi, count)
+// per bin.
+__device__ void hist_to_lds(const u64 *g, u64 *h) {
+  for (int b = threadIdx.x; b < kBins; b += kBlock) {
+    const u64 *s = g + 4 * b;
+    const Fx m = fx_load3(s);
+    h[3 * b] = m.lo;
+    h[3 * b + 1] = m.hi;
+    h[3 * b + 2] = s[3];
+  }
 }
 
 __device__ __forceinline__ Fx fx_shfl(const Fx &a, int src) {
@@ -338,8 +361,7 @@ __device__ __forceinline__ double e_or_zero(float z, float zmax, double T) {
 
 // Nucleus threshold in fixed point: top_p * S (at least one unit, so that
 // top_p <= 0 keeps exactly the first entry).
-__device__ __forceinline__ Fx threshold(const RejArgs &p, int row) {
-  const double S = fx_to_double(fx_load(p.total + 2 * row));
+__device__ __forceinline__ Fx threshold(const RejArgs &p, double S) {
   Fx t = to_fx(p.top_p > 0.0 ? p.top_p * S : 0.0);
   if (!fx_nonzero(t)) t.lo = 1ull;
   return t;
@@ -415,105 +437,12 @@ __global__ __launch_bounds__(kBlock) void rej_rowmax(RejArgs p) {
     p.maxp[row * p.nb + b] = m;
   }
   // zero this row's histograms (4 passes) and total, spread over the row's blocks
-  const int words = 4 * kBins * 3;
+  const int words = 4 * kBins * 4;
   for (int i = b * kBlock + threadIdx.x; i < words; i += p.nb * kBlock) {
-    const int pass = i / (kBins * 3), w = i - pass * kBins * 3;
+    const int pass = i / (kBins * 4), w = i - pass * kBins * 4;
     hist_at(p, pass, row)[w] = 0ull;
   }
-  if (b == 0 && threadIdx.x < 2) p.total[2 * row + threadIdx.x] = 0ull;
-}
-
-// Radix pass `pass` (0..3).  Pass 0 reduces the row maximum and sums the
-// row's total mass; pass s >= 1 first takes selection step s on histogram
-// s-1 (every block computes the same result, block 0 records it for the
-// next pass).  Then the pass histograms, by key digit, the mass of the
-// entries that match the selected prefix and have non-zero mass.
-__global__ __launch_bounds__(kBlock) void rej_pass(RejArgs p, int pass, int with_hist) {
-  __shared__ u64 sh[kBins * 3];
-  __shared__ u64 hprev[kBins * 3];
-  __shared__ Fx red[kBlock / kWave];
-  __shared__ float s_zmax;
-  __shared__ uint32_t s_prefix;
-  const int b = blockIdx.x, row = blockIdx.y;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  for (int i = threadIdx.x; i < kBins * 3; i += kBlock) sh[i] = 0ull;
-  if (pass == 0) {
-    if (wave == 0) {
-      float m = -__builtin_inff();
-      for (int k = lane; k < p.nb; k += kWave) m = fmaxf(m, p.maxp[row * p.nb + k]);
-      for (int s = kWave / 2; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
-      if (lane == 0) {
-        s_zmax = m;
-        s_prefix = 0;
-        if (b == 0) p.zmax[row] = m;
-      }
-    }
-  } else {
-    const u64 *hp = hist_at(p, pass - 1, row);
-    for (int i = threadIdx.x; i < kBins * 3; i += kBlock) hprev[i] = hp[i];
-    __syncthreads();
-    if (wave == 0) {
-      Fx above = fx_zero();
-      uint32_t prefix = 0;
-      if (pass > 1) {
-        const SelState st = p.sel[(pass - 1) * p.M + row];
-        above = Fx{st.above_lo, st.above_hi};
-        prefix = st.prefix;
-      }
-      const int bin = select_bin_wave(hprev, threshold(p, row), above);
-      prefix = (prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
-      if (lane == 0) {
-        s_prefix = prefix;
-        s_zmax = p.zmax[row];
-        if (b == 0) p.sel[pass * p.M + row] = SelState{above.lo, above.hi, prefix, 0};
-      }
-    }
-  }
-  __syncthreads();
-  const float zmax = s_zmax;
-  const uint32_t prefix = s_prefix;
-  const float *zr = p.z + (int64_t)row * p.ldl;
-  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
-  const int shift = 24 - 8 * pass;
-  Fx tot = fx_zero();
-  for (int base = j0; base < j1; base += kBatch * kBlock) {
-    float v[kBatch];
-    load_batch(zr, base, j1, -__builtin_inff(), v);   // -inf: no mass
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const float zj = v[i];
-      const uint32_t key = fkey(zj);
-      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
-      const Fx e = to_fx(e_or_zero(zj, zmax, p.T));
-      if (!fx_nonzero(e)) continue;     // below the fixed-point resolution: no mass
-      if (pass == 0) fx_add(tot, e);
-      if (with_hist) {
-        const int d = (key >> shift) & 0xFF;
-        u64 *bin = sh + 3 * d;
-        if (e.lo) {
-          const u64 old = atomicAdd(bin, e.lo);
-          atomicAdd(bin + 1, e.hi + ((old + e.lo < old) ? 1ull : 0ull));
-        } else {
-          atomicAdd(bin + 1, e.hi);
-        }
-        atomicAdd(bin + 2, 1ull);
-      }
-    }
-  }
-  if (pass == 0) {
-    tot = fx_block_sum(tot, red);
-    if (threadIdx.x == 0) fx_atomic_add(p.total + 2 * row, tot);
-  }
-  if (with_hist) {
-    __syncthreads();
-    u64 *gh = hist_at(p, pass, row);
-    for (int d = threadIdx.x; d < kBins; d += kBlock) {
-      if (sh[3 * d + 2]) {
-        fx_atomic_add(gh + 3 * d, Fx{sh[3 * d], sh[3 * d + 1]});
-        atomicAdd(gh + 3 * d + 2, sh[3 * d + 2]);
-      }
-    }
-  }
+  if (b == 0 && threadIdx.x < 3) p.total[3 * row + threadIdx.x] = 0ull;
 }
 
 // Index of the t-th (1-based) entry of row `zr` with key == kappa, scanning in
@@ -553,33 +482,47 @@ __device__ __forceinline__ bool in_nucleus(const RowState &rs, float z, int j) {
   return k > rs.kappa || (k == rs.kappa && j <= rs.cutoff);
 }
 
-// One block per row: the last selection step fixes the nucleus (kappa and
-// the tie cut), then the inputs of the row's acceptance test are taken.
+// One block per row, after the last radix pass: the last selection step
+// fixes the nucleus (kappa and the tie cut), then the inputs of the row's
+// acceptance test are taken.  Every load that does not depend on the
+// selection (the draft's own entries, the state of the earlier steps, the
+// histogram) is issued up front.
 __global__ __launch_bounds__(kBlock) void rej_select(RejArgs p) {
-  __shared__ u64 hprev[kBins * 3];
+  __shared__ u64 hbuf[kBins * 3];
   __shared__ RowState s_rs;
+  __shared__ uint32_t s_kappa;
+  __shared__ u64 s_t, s_n;
   const int row = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const float zmax = p.zmax[row];
-  const double S = fx_to_double(fx_load(p.total + 2 * row));
+  int x = -1;
+  float zx = 0.0f;
+  double qx = 0.0;
+  if (threadIdx.x == 0 && row < p.M - 1) {
+    x = p.drafts[row];
+    if (x >= 0 && x < p.V) {
+      zx = p.z[(int64_t)row * p.ldl + x];
+      qx = (double)p.q[(int64_t)row * p.ldq + x];
+    } else {
+      x = -1;
+    }
+  }
+  const double S = fx_to_double(fx_load3(p.total + 3 * row));
   if (p.top_p >= 1.0) {
     if (threadIdx.x == 0) s_rs = RowState{zmax, 0u, p.V, 1, S};
     __syncthreads();
   } else {
-    const u64 *hp = hist_at(p, 3, row);
-    for (int i = threadIdx.x; i < kBins * 3; i += kBlock) hprev[i] = hp[i];
+    const SelState st = p.sel[3 * p.M + row];
+    hist_to_lds(hist_at(p, 3, row), hbuf);
     __syncthreads();
-    __shared__ uint32_t s_kappa;
-    __shared__ u64 s_t, s_n;
-    __shared__ double s_above;
     if (wave == 0) {
-      const SelState st = p.sel[3 * p.M + row];
       Fx above = Fx{st.above_lo, st.above_hi};
-      const Fx thr = threshold(p, row);
-      const int bin = select_bin_wave(hprev, thr, above);
-      const uint32_t kappa = (st.prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
+      const uint32_t prefix = st.prefix;
+      const Fx thr = threshold(p, S);
+      const int bin = select_bin_wave(hbuf, thr, above);
+      const uint32_t kappa = (prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
       if (lane == 0) {
-        const u64 n = hprev[3 * (kappa & 0xFF) + 2];
+        const u64 n = hbuf[3 * (kappa & 0xFF) + 2];
         const double ek = e_of(key_to_float(kappa), zmax, p.T);
         const double above_d = fx_to_double(above);
         const double tt = ceil((fx_to_double(thr) - above_d) / ek);
@@ -587,7 +530,6 @@ __global__ __launch_bounds__(kBlock) void rej_select(RejArgs p) {
         s_kappa = kappa;
         s_t = t;
         s_n = n;
-        s_above = above_d;
         s_rs = RowState{zmax, kappa, p.V, 0, above_d + (double)t * ek};
       }
     }
@@ -598,18 +540,111 @@ __global__ __launch_bounds__(kBlock) void rej_select(RejArgs p) {
       __syncthreads();
     }
   }
-  const RowState rs = s_rs;
   if (threadIdx.x == 0) {
+    const RowState rs = s_rs;
     p.rows[row] = rs;
     if (row < p.M - 1) {
-      const int x = p.drafts[row];
-      double px = 0.0, qx = 0.0;
-      if (x >= 0 && x < p.V) {
-        const float zx = p.z[(int64_t)row * p.ldl + x];
-        if (in_nucleus(rs, zx, x)) px = e_of(zx, rs.zmax, p.T) / rs.mass;
-        qx = (double)p.q[(int64_t)row * p.ldq + x];
+      double px = 0.0;
+      if (x >= 0 && in_nucleus(rs, zx, x)) px = e_of(zx, rs.zmax, p.T) / rs.mass;
+      p.acc[row] = AccIn{px, x >= 0 ? qx : 0.0};
+    }
+  }
+}
+
+// Radix pass `pass` (0..3).  Pass 0 reduces the row maximum and sums the
+// row's total mass; pass s >= 1 first takes selection step s on histogram
+// s-1 (every block computes the same result, block 0 records it for the
+// next pass).  Then the pass histograms, by key digit, the mass of the
+// entries that match the selected prefix and have non-zero mass.  The
+// block's first entries are loaded before the selection step, so that their
+// latency overlaps it.
+__global__ __launch_bounds__(kBlock) void rej_pass(RejArgs p, int pass, int with_hist) {
+  __shared__ u64 sh[kBins * 3];
+  __shared__ u64 hprev[kBins * 3];
+  __shared__ Fx red[kBlock / kWave];
+  __shared__ float s_zmax;
+  __shared__ uint32_t s_prefix;
+  const int b = blockIdx.x, row = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const float *zr = p.z + (int64_t)row * p.ldl;
+  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
+  float v0[kBatch];
+  load_batch(zr, j0, j1, -__builtin_inff(), v0);   // -inf: no mass
+  for (int i = threadIdx.x; i < kBins * 3; i += kBlock) sh[i] = 0ull;
+  if (pass == 0) {
+    if (wave == 0) {
+      float m = -__builtin_inff();
+      for (int k = lane; k < p.nb; k += kWave) m = fmaxf(m, p.maxp[row * p.nb + k]);
+      for (int s = kWave / 2; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
+      if (lane == 0) {
+        s_zmax = m;
+        s_prefix = 0;
+        if (b == 0) p.zmax[row] = m;
       }
-      p.acc[row] = AccIn{px, qx};
+    }
+  } else {
+    const float zm = p.zmax[row];
+    const double S = fx_to_double(fx_load3(p.total + 3 * row));
+    SelState st = SelState{0ull, 0ull, 0u, 0};
+    if (pass > 1) st = p.sel[(pass - 1) * p.M + row];
+    hist_to_lds(hist_at(p, pass - 1, row), hprev);
+    __syncthreads();
+    if (wave == 0) {
+      Fx above = Fx{st.above_lo, st.above_hi};
+      const int bin = select_bin_wave(hprev, threshold(p, S), above);
+      const uint32_t prefix = (st.prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
+      if (lane == 0) {
+        s_prefix = prefix;
+        s_zmax = zm;
+        if (b == 0) p.sel[pass * p.M + row] = SelState{above.lo, above.hi, prefix, 0};
+      }
+    }
+  }
+  __syncthreads();
+  const float zmax = s_zmax;
+  const uint32_t prefix = s_prefix;
+  const int shift = 24 - 8 * pass;
+  Fx tot = fx_zero();
+  auto take = [&](const float (&v)[kBatch]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float zj = v[i];
+      const uint32_t key = fkey(zj);
+      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+      const Fx e = to_fx(e_or_zero(zj, zmax, p.T));
+      if (!fx_nonzero(e)) continue;     // below the fixed-point resolution: no mass
+      if (pass == 0) fx_add(tot, e);
+      if (with_hist) {
+        const int d = (key >> shift) & 0xFF;
+        u64 *bin = sh + 3 * d;
+        if (e.lo) {
+          const u64 old = atomicAdd(bin, e.lo);
+          atomicAdd(bin + 1, e.hi + ((old + e.lo < old) ? 1ull : 0ull));
+        } else {
+          atomicAdd(bin + 1, e.hi);
+        }
+        atomicAdd(bin + 2, 1ull);
+      }
+    }
+  };
+  take(v0);
+  for (int base = j0 + kBatch * kBlock; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(zr, base, j1, -__builtin_inff(), v);
+    take(v);
+  }
+  if (pass == 0) {
+    tot = fx_block_sum(tot, red);
+    if (threadIdx.x == 0) fx_atomic_add3(p.total + 3 * row, tot);
+  }
+  if (with_hist) {
+    __syncthreads();
+    u64 *gh = hist_at(p, pass, row);
+    for (int d = threadIdx.x; d < kBins; d += kBlock) {
+      if (sh[3 * d + 2]) {
+        fx_atomic_add3(gh + 4 * d, Fx{sh[3 * d], sh[3 * d + 1]});
+        atomicAdd(gh + 4 * d + 3, sh[3 * d + 2]);
+      }
     }
   }
 }
@@ -704,11 +739,9 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
   __shared__ Fx wsum[kBlock / kWave];
   __shared__ int s_blk, s_lastnz, s_pick;
   __shared__ Fx s_before;
-  const int a = accepted_run(p);
-  const int residual = a < p.M - 1;
-  const RowState rs = p.rows[a];
-  // thread t holds chunks k0 .. k1-1 (in order); all their sums are loaded
-  // before any is used
+  __shared__ RowState s_rows[kMaxRows];
+  // thread t holds chunks k0 .. k1-1 (in order); their sums and every row's
+  // nucleus are loaded before the accepted run is known (none depends on it)
   constexpr int kPer = kMaxDrawBlocks / kBlock;
   const int per = (p.nbd + kBlock - 1) / kBlock;
   const int k0 = min(p.nbd, (int)threadIdx.x * per), k1 = min(p.nbd, k0 + per);
@@ -722,6 +755,11 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
       ce[i] = Fx{o[2], o[3]};
     }
   }
+  if (threadIdx.x < p.M) s_rows[threadIdx.x] = p.rows[threadIdx.x];
+  const int a = accepted_run(p);
+  const int residual = a < p.M - 1;
+  __syncthreads();
+  const RowState rs = s_rows[a];
   Fx lres = fx_zero(), le = fx_zero();
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {

@@ -209,3 +209,27 @@ def test_repeatable():
     a = gpu_rej(z, q, d, u, 0.6, 0.95, 0)
     for _ in range(3):
         check_same(gpu_rej(z, q, d, u, 0.6, 0.95, 0), a, "repeat")
+
+
+def test_one_workspace_across_calls_and_shapes():
+    # one workspace serves greedy and rejection calls of different shapes in
+    # any order (nothing a call leaves in it may affect the next)
+    rng = np.random.default_rng(77)
+    ws = bv.accept_workspace(8, 262144, DEV)
+    for i, (M, V) in enumerate([(8, 262144), (4, 1000), (8, 262144), (1, 7), (16, 2048),
+                                (8, 4097), (64, 33), (8, 262144)]):
+        z = rng.standard_normal((M, V)).astype(np.float32)
+        d = np.array([oracle.argmax(z[k]) for k in range(M - 1)], np.int32)
+        if M > 2:
+            d[M // 2] = (d[M // 2] + 1) % V
+        dt = dev(d) if M > 1 else None
+        t, c, r = bv.accept_greedy(dev(z), dt, 5, ws=ws)
+        check_same((host(t), host(c), int(host(r)[0])), oracle.accept_greedy(z, d, 5),
+                   f"greedy call {i} M={M} V={V}")
+        q = W.rand_dirichlet_rows(rng, max(M - 1, 1), V, 0.5)[:M - 1]
+        u = rng.random(M).astype(np.float32)
+        t, c, r = bv.accept_rejection(dev(z), dev(q) if M > 1 else None, dt, dev(u), 0.8, 0.9,
+                                      5, ws=ws)
+        check_same((host(t), host(c), int(host(r)[0])),
+                   oracle.accept_rejection(z, q, d, u, 0.8, 0.9, 5),
+                   f"rejection call {i} M={M} V={V}")
