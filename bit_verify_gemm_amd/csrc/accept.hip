@@ -316,24 +316,32 @@ __global__ __launch_bounds__(kBlock) void greedy_partial(const float *z, int64_t
   }
 }
 
-// Row argmax from the block partials (one wave per row), then the prefix
-// match, tokens, counts and rollback.
-__global__ __launch_bounds__(kBlock) void greedy_final(const float *pv, const int *pj, int M, int nb,
-                                                       const int32_t *drafts, int64_t base_len,
-                                                       int32_t *tokens, int32_t *counts,
-                                                       int64_t *rollback) {
+// Row argmax from the block partials (one wave per row, 16 waves), then
+// the prefix match, tokens, counts and rollback.  A wave loads both of its
+// lanes' partials (nb <= 128) before comparing them.
+constexpr int kFinalThreads = 1024;
+static_assert(kMaxBlocksPerRow <= 2 * kWave, "two partials per lane");
+__global__ __launch_bounds__(kFinalThreads) void greedy_final(const float *pv, const int *pj,
+                                                              int M, int nb,
+                                                              const int32_t *drafts,
+                                                              int64_t base_len, int32_t *tokens,
+                                                              int32_t *counts, int64_t *rollback) {
   __shared__ int g[64];
   __shared__ int d[64];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  for (int row = wave; row < M; row += kBlock / kWave) {
-    float bv = __int_as_float(0x7FC00000);
-    int bj = 0x7FFFFFFF;
-    for (int b = lane; b < nb; b += kWave)
-      if (better(pv[row * nb + b], pj[row * nb + b], bv, bj)) { bv = pv[row * nb + b]; bj = pj[row * nb + b]; }
+  if (threadIdx.x < M - 1) d[threadIdx.x] = drafts[threadIdx.x];   // issued with the partials' loads
+  for (int row = wave; row < M; row += kFinalThreads / kWave) {
+    const int b0 = lane, b1 = lane + kWave;
+    const float v0 = b0 < nb ? pv[row * nb + b0] : __int_as_float(0x7FC00000);
+    const int j0 = b0 < nb ? pj[row * nb + b0] : 0x7FFFFFFF;
+    const float v1 = b1 < nb ? pv[row * nb + b1] : __int_as_float(0x7FC00000);
+    const int j1 = b1 < nb ? pj[row * nb + b1] : 0x7FFFFFFF;
+    float bv = v0;
+    int bj = j0;
+    if (better(v1, j1, bv, bj)) { bv = v1; bj = j1; }
     wave_best(bv, bj);
     if (lane == 0) g[row] = (bj == 0x7FFFFFFF) ? 0 : bj;  // all-NaN row: index 0
   }
-  if (threadIdx.x < M - 1) d[threadIdx.x] = drafts[threadIdx.x];
   __syncthreads();
   if (threadIdx.x == 0) {
     int a = 0;
@@ -851,7 +859,7 @@ hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
                      chunk, pv, pj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(greedy_final, dim3(1), dim3(kBlock), 0, stream, pv, pj, M, nb, drafts,
+  hipLaunchKernelGGL(greedy_final, dim3(1), dim3(kFinalThreads), 0, stream, pv, pj, M, nb, drafts,
                      base_len, tokens, counts, rollback);
   return hipGetLastError();
 }
