@@ -73,6 +73,10 @@ def _load():
         lib.orc_argmax.argtypes = [P, ctypes.c_int]
         lib.orc_accept_greedy.restype = ctypes.c_int
         lib.orc_accept_greedy.argtypes = [P, ctypes.c_int, ctypes.c_int, i64, P, i64, P, P, P]
+        lib.orc_accept_sampled.restype = ctypes.c_int
+        lib.orc_accept_sampled.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, i64, P, P,
+                                           i64, P, P, i64, P, P, ctypes.c_int, P, P, P, P, P, P,
+                                           P, P]
         lib.orc_accept_rejection.restype = ctypes.c_int
         lib.orc_accept_rejection.argtypes = [P, ctypes.c_int, ctypes.c_int, i64, P, i64, P, P,
                                              f32, f32, i64, P, P, P, P]
@@ -236,3 +240,79 @@ def accept_rejection(logits: np.ndarray, q: np.ndarray, drafts: np.ndarray, u: n
     if with_margins:
         return tokens, counts, int(rb[0]), margins
     return tokens, counts, int(rb[0])
+
+
+# Sampler parameters of accept_sampled (the fields of orc_sampler, in order).
+SAMPLER_FIELDS = ("temperature", "top_p", "min_p", "top_k", "repeat_penalty",
+                  "presence_penalty", "frequency_penalty", "penalty_last_n")
+SAMPLER_DEFAULTS = dict(temperature=1.0, top_p=1.0, min_p=0.0, top_k=0, repeat_penalty=1.0,
+                        presence_penalty=0.0, frequency_penalty=0.0, penalty_last_n=0)
+
+
+class _Sampler(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("min_p", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("repeat_penalty", ctypes.c_float), ("presence_penalty", ctypes.c_float),
+                ("frequency_penalty", ctypes.c_float), ("penalty_last_n", ctypes.c_int32)]
+
+
+def sampler(**kw) -> dict:
+    s = dict(SAMPLER_DEFAULTS)
+    for k, v in kw.items():
+        if k not in s:
+            raise KeyError(k)
+        s[k] = v
+    return s
+
+
+def accept_sampled(logits: np.ndarray, drafts: np.ndarray, u: np.ndarray, params: dict,
+                   q: np.ndarray | None = None, q_sparse=None, history=None,
+                   base_len=None, with_target: bool = False, with_margins: bool = False):
+    """Sampled acceptance of B sequences (see orc_accept_sampled).
+    logits [B][M][V]; drafts [B][M-1]; u [B][M]; q dense [B][M-1][V] or
+    q_sparse = (ids [B][M-1][K], probs [B][M-1][K]); history: list of B int
+    sequences (or None); base_len [B].  Returns tokens [B][M], counts [B][2],
+    rollback [B] (+ target p' [B][M][V], + margins [B][M+1])."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    B, M, V = logits.shape
+    d = np.ascontiguousarray(drafts if M > 1 else np.zeros((B, 1)), dtype=np.int32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    assert u.shape == (B, M)
+    qd, qi, qp, Kq, ldq = None, None, None, 0, 0
+    if M > 1:
+        if q is not None:
+            qd = np.ascontiguousarray(q, dtype=np.float32)
+            assert qd.shape == (B, M - 1, V)
+            ldq = V
+        else:
+            qi = np.ascontiguousarray(q_sparse[0], dtype=np.int32)
+            qp = np.ascontiguousarray(q_sparse[1], dtype=np.float32)
+            assert qi.shape == qp.shape and qi.shape[:2] == (B, M - 1)
+            Kq = qi.shape[2]
+    hist, hlen, ldh = None, None, 0
+    if history is not None:
+        hlen = np.array([len(h) for h in history], np.int32)
+        ldh = max(1, int(hlen.max()))
+        hist = np.zeros((B, ldh), np.int32)
+        for b, h in enumerate(history):
+            hist[b, :len(h)] = h
+    bl = np.ascontiguousarray(np.zeros(B) if base_len is None else base_len, dtype=np.int64)
+    s = _Sampler(**{k: params[k] for k in SAMPLER_FIELDS})
+    tokens = np.zeros((B, M), np.int32)
+    counts = np.zeros((B, 2), np.int32)
+    rb = np.zeros(B, np.int64)
+    tp = np.zeros((B, M, V), np.float64) if with_target else None
+    margins = np.zeros((B, M + 1), np.float64)
+    rc = lib.orc_accept_sampled(B, M, V, _ptr(logits), V, _ptr(hist), _ptr(hlen), ldh, _ptr(d),
+                                _ptr(qd), ldq, _ptr(qi), _ptr(qp), Kq, _ptr(u),
+                                ctypes.cast(ctypes.pointer(s), ctypes.c_void_p), _ptr(bl),
+                                _ptr(tokens), _ptr(counts), _ptr(rb), _ptr(tp), _ptr(margins))
+    if rc != 0:
+        raise ValueError("orc_accept_sampled rejected its arguments")
+    out = [tokens, counts, rb]
+    if with_target:
+        out.append(tp)
+    if with_margins:
+        out.append(margins)
+    return tuple(out)

@@ -557,3 +557,235 @@ int orc_accept_rejection(const float *logits, int M, int V, int64_t ldl, const f
     free(keys);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* sampled acceptance with the full sampler pipeline                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Ollama mtp.go commit log, the MLX sampler rework: the target distribution
+ * of a row is built by an explicit pipeline -- (1) penalties, (2) top-k,
+ * (3) temperature/softmax, (4) top-p, (5) min-p, (6) normalize,
+ * (7) categorical -- and the common top-k path keeps sparse per-row token
+ * ids and probabilities, which sampled MTP reuses for acceptance, the bonus
+ * draw and the residual draw.  The pages name the steps but not their
+ * formulas; the readings taken here (the usual ones):
+ *
+ *   (1) the penalty window of row i of a sequence is the last penalty_last_n
+ *       tokens of (history ++ drafts[0..i-1]) (none if penalty_last_n <= 0);
+ *       for a token t seen c_t > 0 times in it, in fp32 with every operation
+ *       rounded on its own:
+ *         z = (z > 0) ? z / repeat_penalty : z * repeat_penalty
+ *         z = (z - c_t * frequency_penalty) - presence_penalty
+ *       (the repeat step is skipped when repeat_penalty == 1); ids outside
+ *       [0, V) in the window are ignored.
+ *   (2) top-k keeps the top_k entries first in the order (z desc, index asc)
+ *       (top_k <= 0 or >= V keeps all).
+ *   (3) e_j = exp((z_j - z_max) / T) in fp64 over the kept entries;
+ *       T == 0 makes the target a point mass at the first entry of the order.
+ *   (4) top-p keeps the shortest prefix of the order whose e-mass reaches
+ *       top_p * (sum of e) (top_p >= 1 keeps all, top_p <= 0 the first).
+ *   (5) min-p then drops entries with e_j < min_p (that is, p_j below min_p
+ *       times the largest p); the first entry always stays.
+ *   (6) p'_j = e_j / (e-mass of what is left), 0 elsewhere.
+ *   (7) a draw picks, in index order, the smallest j with
+ *       w_0 + .. + w_j > u * sum(w) (the last j with w_j > 0 if rounding
+ *       passes the end).
+ * Acceptance of draft x_i ~ q_i: accept iff u_i * q_i(x_i) < p'_i(x_i); the
+ * first rejection a draws from max(0, p'_a - q_a) (from p'_a if that is all
+ * zero); if every draft is accepted, a bonus is drawn from p'_{M-1}; both
+ * draws use u_{M-1}.  q_i is dense [V] or sparse (ids, probs; an id not listed
+ * has probability 0, the first listing of an id counts).
+ */
+typedef struct {
+    float temperature, top_p, min_p;
+    int32_t top_k;
+    float repeat_penalty, presence_penalty, frequency_penalty;
+    int32_t penalty_last_n;
+} orc_sampler;
+
+/* Penalised copy of one row (step 1). */
+static void penalise_row(const float *z, int V, const int32_t *window, int W,
+                         const orc_sampler *s, float *zp) {
+    for (int j = 0; j < V; ++j) zp[j] = z[j];
+    for (int w = 0; w < W; ++w) {
+        int32_t t = window[w];
+        if (t < 0 || t >= V) continue;
+        int first = 1;
+        for (int v = 0; v < w; ++v)
+            if (window[v] == t) { first = 0; break; }
+        if (!first) continue;
+        int c = 0;
+        for (int v = 0; v < W; ++v) c += (window[v] == t);
+        volatile float x = z[t];
+        if (s->repeat_penalty != 1.0f) x = (x > 0.0f) ? x / s->repeat_penalty : x * s->repeat_penalty;
+        volatile float cf = (float)c * s->frequency_penalty;
+        x = x - cf;
+        x = x - s->presence_penalty;
+        zp[t] = x;
+    }
+}
+
+/*
+ * Target distribution of one row (steps 2-6) from its penalised logits:
+ * writes p'[V] (0 outside the kept entries) and returns the number kept.
+ * margin: relative distance of the top-p and min-p cuts from their
+ * thresholds.
+ */
+static int sampled_row(const float *zp, int V, const orc_sampler *s, double *p, zkey *keys,
+                       double *margin) {
+    for (int j = 0; j < V; ++j) keys[j].z = zp[j], keys[j].j = j;
+    qsort(keys, (size_t)V, sizeof(zkey), zkey_cmp);
+    int n = (s->top_k > 0 && s->top_k < V) ? s->top_k : V;
+    for (int j = 0; j < V; ++j) p[j] = 0.0;
+    *margin = INFINITY;
+    if (s->temperature == 0.0f) {
+        p[keys[0].j] = 1.0;
+        return 1;
+    }
+    const double T = (double)s->temperature, zm = (double)keys[0].z;
+    double S = 0.0;
+    for (int c = 0; c < n; ++c) {
+        p[keys[c].j] = exp(((double)keys[c].z - zm) / T);
+        S += p[keys[c].j];
+    }
+    int c_p = n;
+    if (s->top_p < 1.0f) {
+        double thr = (double)s->top_p * S, cum = 0.0;
+        c_p = 1;
+        if (s->top_p > 0.0f) {
+            for (c_p = 0; c_p < n;) {
+                double prev = cum;
+                cum += p[keys[c_p].j];
+                ++c_p;
+                if (cum >= thr) {
+                    double m1 = fabs(cum - thr) / S, m0 = fabs(prev - thr) / S;
+                    *margin = m1 < m0 ? m1 : m0;
+                    break;
+                }
+            }
+        }
+    }
+    int c_m = n;
+    if (s->min_p > 0.0f) {
+        for (c_m = 1; c_m < n; ++c_m) {
+            double e = p[keys[c_m].j];
+            double m = fabs(e - (double)s->min_p) / (double)s->min_p;
+            if (m < *margin) *margin = m;
+            if (e < (double)s->min_p) break;
+        }
+    }
+    int kept = c_p < c_m ? c_p : c_m;
+    double Sp = 0.0;
+    for (int c = 0; c < kept; ++c) Sp += p[keys[c].j];
+    for (int c = 0; c < kept; ++c) p[keys[c].j] /= Sp;
+    for (int c = kept; c < n; ++c) p[keys[c].j] = 0.0;
+    return kept;
+}
+
+static double q_of(const float *q, const int32_t *q_ids, const float *q_probs, int Kq, int32_t x) {
+    if (q) return (double)q[x];
+    for (int k = 0; k < Kq; ++k)
+        if (q_ids[k] == x) return (double)q_probs[k];
+    return 0.0;
+}
+
+/*
+ * B sequences of M rows each; row i of sequence b is logits row b*M + i.
+ * history[b][0..history_len[b]-1] (row stride ldh), drafts [B][M-1],
+ * uniforms [B][M], base_len [B]; q dense [B][M-1][ldq] or, if q is NULL,
+ * sparse q_ids / q_probs [B][M-1][Kq].  Outputs tokens [B][M], counts [B][2],
+ * rollback [B].  Optional: target_p [B*M][V] receives every row's p';
+ * margins [B][M+1] as in orc_accept_rejection (acceptance margins per row,
+ * the draw margin, then the smallest cut margin).
+ */
+int orc_accept_sampled(int B, int M, int V, const float *logits, int64_t ldl,
+                       const int32_t *history, const int32_t *history_len, int64_t ldh,
+                       const int32_t *drafts, const float *q, int64_t ldq, const int32_t *q_ids,
+                       const float *q_probs, int Kq, const float *u, const orc_sampler *s,
+                       const int64_t *base_len, int32_t *tokens, int32_t *counts,
+                       int64_t *rollback, double *target_p, double *margins) {
+    if (B < 1 || M < 1 || M > 64 || V < 1 || ldl < V || !(s->temperature >= 0.0f)) return -1;
+    if (M > 1 && !q && (!q_ids || !q_probs || Kq < 1)) return -1;
+    float *zp = (float *)malloc(sizeof(float) * (size_t)V);
+    double *p = (double *)malloc(sizeof(double) * (size_t)V * (size_t)M);
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    zkey *keys = (zkey *)malloc(sizeof(zkey) * (size_t)V);
+    int32_t *window = NULL;
+    int maxw = 0;
+    for (int b = 0; b < B; ++b) {
+        int w = (history ? history_len[b] : 0) + M;
+        if (w > maxw) maxw = w;
+    }
+    window = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxw + 1));
+    if (!zp || !p || !r || !keys || !window) {
+        free(zp); free(p); free(r); free(keys); free(window);
+        return -1;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int Lh = history ? history_len[b] : 0;
+        const int32_t *d = drafts ? drafts + (int64_t)b * (M - 1) : NULL;
+        double *mg = margins ? margins + (int64_t)b * (M + 1) : NULL;
+        double cut_margin = INFINITY, m_cut, m_draw = INFINITY;
+        if (mg)
+            for (int i = 0; i <= M; ++i) mg[i] = INFINITY;
+        for (int i = 0; i < M; ++i) {
+            /* the penalty window: last penalty_last_n of history ++ drafts[0..i-1] */
+            int W = 0;
+            if (s->penalty_last_n > 0) {
+                int total = Lh + i, w0 = total - s->penalty_last_n;
+                if (w0 < 0) w0 = 0;
+                for (int c = w0; c < total; ++c)
+                    window[W++] = (c < Lh) ? history[(int64_t)b * ldh + c] : d[c - Lh];
+            }
+            penalise_row(logits + ((int64_t)b * M + i) * ldl, V, window, W, s, zp);
+            sampled_row(zp, V, s, p + (int64_t)i * V, keys, &m_cut);
+            if (m_cut < cut_margin) cut_margin = m_cut;
+            if (target_p)
+                memcpy(target_p + ((int64_t)b * M + i) * V, p + (int64_t)i * V,
+                       sizeof(double) * (size_t)V);
+        }
+        int32_t run[64];
+        int a = 0;
+        int32_t last = -1;
+        const float *ub = u + (int64_t)b * M;
+        for (;;) {
+            const double *pa = p + (int64_t)a * V;
+            if (a == M - 1) {
+                last = draw(pa, V, (double)ub[M - 1], &m_draw);
+                break;
+            }
+            const int32_t x = d[a];
+            const float *qa = q ? q + ((int64_t)b * (M - 1) + a) * ldq : NULL;
+            const int32_t *qia = q ? NULL : q_ids + ((int64_t)b * (M - 1) + a) * Kq;
+            const float *qpa = q ? NULL : q_probs + ((int64_t)b * (M - 1) + a) * Kq;
+            const double px = (x >= 0 && x < V) ? pa[x] : 0.0;
+            const double qx = (x >= 0 && x < V) ? q_of(qa, qia, qpa, Kq, x) : 0.0;
+            const double lhs = (double)ub[a] * qx;
+            if (mg) mg[a] = (px > 0.0) ? fabs(lhs - px) / px : INFINITY;
+            if (lhs < px) {
+                run[a] = x;
+                ++a;
+                continue;
+            }
+            double Wr = 0.0;
+            for (int j = 0; j < V; ++j) {
+                double dj = pa[j] - (pa[j] > 0.0 ? q_of(qa, qia, qpa, Kq, j) : 0.0);
+                r[j] = dj > 0.0 ? dj : 0.0;
+                Wr += r[j];
+            }
+            last = (Wr > 0.0) ? draw(r, V, (double)ub[M - 1], &m_draw)
+                              : draw(pa, V, (double)ub[M - 1], &m_draw);
+            break;
+        }
+        run[a] = last;
+        write_run(M, run, a, base_len ? base_len[b] : 0, tokens + (int64_t)b * M, counts + 2 * b,
+                  rollback + b);
+        if (mg) {
+            mg[M - 1] = m_draw;
+            mg[M] = cut_margin;
+        }
+    }
+    free(zp); free(p); free(r); free(keys); free(window);
+    return 0;
+}
