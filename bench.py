@@ -9,8 +9,8 @@ The same run also reports, as context next to the headline, the other
 steps of the verify pass at their own workloads:
 * the Q4_0 projections of one 27B-class decoder layer (M = 8), one by one
   and with Q|K|V and gate|up fused along N,
-* the 5376 -> 262144 LM head (M = 8) and the greedy and rejection accept
-  steps on its logits,
+* the 5376 -> 262144 LM head (M = 8) and the greedy, rejection and sampled
+  (full sampler pipeline, sparse top-k) accept steps on its logits,
 * the routed MoE pass (8 tokens, 128 experts, top-8, 2048 -> 768 -> 2048),
   with its unique-expert bytes.
 
@@ -287,11 +287,35 @@ def extra_lm_head_and_accept(bv, dev, steps, warmup):
     # 16 back-to-back calls per graph (the same logits, which stay in the
     # caches as they would right after the LM head), so that the graph's own
     # launch cost is spread as it is for the GEMM timings
+    # the full sampler pipeline on the sparse top-k path (penalties over a
+    # 64-token window of a seeded history, top-k 64, top-p, min-p)
+    sp = bv.Sampler(temperature=c["temperature"], top_p=c["top_p"], min_p=0.01, top_k=64,
+                    repeat_penalty=1.1, penalty_last_n=64)
+    hist = torch.from_numpy(np.random.default_rng(7).integers(0, V, (1, 64)).astype(np.int32)).to(dev)
+    hlen = torch.full((1,), 64, dtype=torch.int32, device=dev)
+    u1 = u.view(1, M)
+    d1 = dd.view(1, M - 1)
+    q1 = q.view(1, M - 1, V)
+    sws = torch.empty(bv.accept_sampled_workspace_bytes(1, M, V, 64, True), dtype=torch.uint8,
+                      device=dev)
+    souts = (torch.empty((1, M), dtype=torch.int32, device=dev),
+             torch.empty((1, 2), dtype=torch.int32, device=dev),
+             torch.empty(1, dtype=torch.int64, device=dev))
+
+    def sampled(i):
+        bv.accept_sampled(logits, d1, u1, sp, draft_probs=q1, history=hist, history_len=hlen,
+                          outs=souts, ws=sws)
+
     _, ms_g, _ = time_graph(greedy, 16, max(64, steps // 4), 32)
     _, ms_r, _ = time_graph(rejection, 16, max(64, steps // 4), 32)
+    _, ms_s, _ = time_graph(sampled, 16, max(64, steps // 4), 32)
     out["accept_greedy"] = {"M": M, "V": V, "us": round(ms_g * 1e3, 3), "planted_L": c["L"]}
     out["accept_rejection"] = {"M": M, "V": V, "us": round(ms_r * 1e3, 3),
                                "temperature": c["temperature"], "top_p": c["top_p"]}
+    out["accept_sampled"] = {"B": 1, "M": M, "V": V, "us": round(ms_s * 1e3, 3),
+                             "temperature": c["temperature"], "top_p": c["top_p"],
+                             "top_k": 64, "min_p": 0.01, "repeat_penalty": 1.1,
+                             "penalty_last_n": 64}
     del gm
     torch.cuda.empty_cache()
     return out

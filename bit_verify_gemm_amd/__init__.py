@@ -18,6 +18,7 @@ __all__ = [
     "packed_weight_bytes", "pack_weights", "gemm_workspace_bytes", "gemm_workspace",
     "gemm_plan_info",
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
+    "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.mtp_accept_rejection.restype = i32
         L.mtp_accept_rejection.argtypes = [P, i32, i32, i64, P, i64, P, P, f32, f32, i64, P, P, P,
                                            P, sz, P]
+        L.mtp_accept_sampled_workspace_bytes.restype = sz
+        L.mtp_accept_sampled_workspace_bytes.argtypes = [i32] * 5
+        L.mtp_accept_sampled.restype = i32
+        L.mtp_accept_sampled.argtypes = [P, i32, i32, i32, i64, P, P, i64, P, P, i64, P, P, i32,
+                                         P, P, P, P, P, P, P, P, P, sz, P]
         _lib = L
         return L
 
@@ -238,4 +244,77 @@ def accept_rejection(logits: torch.Tensor, draft_probs: torch.Tensor | None,
                                       float(temperature), float(top_p), int(base_len), _ptr(tok),
                                       _ptr(cnt), _ptr(rb), _ptr(ws), _nbytes(ws),
                                       _stream(stream)))
+    return tok, cnt, rb
+
+
+class Sampler(ctypes.Structure):
+    """mtp_sampler: the sampler pipeline's parameters (see mtp_verify.h)."""
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("min_p", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("repeat_penalty", ctypes.c_float), ("presence_penalty", ctypes.c_float),
+                ("frequency_penalty", ctypes.c_float), ("penalty_last_n", ctypes.c_int32)]
+
+    def __init__(self, temperature=1.0, top_p=1.0, min_p=0.0, top_k=40, repeat_penalty=1.0,
+                 presence_penalty=0.0, frequency_penalty=0.0, penalty_last_n=0):
+        super().__init__(temperature, top_p, min_p, top_k, repeat_penalty, presence_penalty,
+                         frequency_penalty, penalty_last_n)
+
+    @property
+    def penalties(self) -> bool:
+        return self.penalty_last_n > 0 and (self.repeat_penalty != 1.0 or
+                                            self.presence_penalty != 0.0 or
+                                            self.frequency_penalty != 0.0)
+
+
+def accept_sampled_workspace_bytes(B: int, M: int, V: int, top_k: int, penalties: bool) -> int:
+    return int(lib().mtp_accept_sampled_workspace_bytes(B, M, V, top_k, int(bool(penalties))))
+
+
+def accept_sampled(logits: torch.Tensor, draft_ids: torch.Tensor | None, uniforms: torch.Tensor,
+                   params: Sampler, draft_probs: torch.Tensor | None = None,
+                   draft_topk: tuple | None = None, history: torch.Tensor | None = None,
+                   history_len: torch.Tensor | None = None, base_len: torch.Tensor | None = None,
+                   want_target: bool = False, outs=None, ws: torch.Tensor | None = None,
+                   stream=None):
+    """Sampled acceptance of B sequences.  logits [B][M][V] (or [B*M][V] views
+    with uniforms [B][M] giving B); draft_ids [B][M-1]; draft_probs dense
+    [B][M-1][V] or draft_topk = (ids [B][M-1][Kq], probs [B][M-1][Kq]);
+    history [B][ldh] with history_len [B]; base_len [B] int64.  Returns
+    (tokens [B][M], counts [B][2], rollback [B]) and, with want_target, the
+    targets' sparse ids and probabilities [B][M][K]."""
+    B, M = uniforms.shape
+    V = logits.shape[-1]
+    z = logits.reshape(B * M, V) if logits.dim() == 3 else logits
+    dev = z.device
+    K = min(int(params.top_k), V)
+    if outs is None:
+        outs = (torch.empty((B, M), dtype=torch.int32, device=dev),
+                torch.empty((B, 2), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int64, device=dev))
+    tok, cnt, rb = outs
+    tid = tpr = None
+    if want_target:
+        tid = torch.empty((B, M, K), dtype=torch.int32, device=dev)
+        tpr = torch.empty((B, M, K), dtype=torch.float32, device=dev)
+    need = accept_sampled_workspace_bytes(B, M, V, int(params.top_k), params.penalties)
+    if ws is None or _nbytes(ws) < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    q = qi = qp = None
+    ldq, Kq = 0, 0
+    if M > 1:
+        if draft_probs is not None:
+            q = draft_probs.reshape(B * (M - 1), -1)
+            ldq = _ld(q)
+        else:
+            qi, qp = draft_topk
+            Kq = int(qi.shape[-1])
+    ldh = _ld(history) if history is not None else 0
+    _check(lib().mtp_accept_sampled(_ptr(z), B, M, V, _ld(z), _ptr(history), _ptr(history_len),
+                                    ldh, _ptr(draft_ids), _ptr(q), ldq, _ptr(qi), _ptr(qp), Kq,
+                                    _ptr(uniforms), ctypes.cast(ctypes.pointer(params),
+                                                                ctypes.c_void_p),
+                                    _ptr(base_len), _ptr(tok), _ptr(cnt), _ptr(rb), _ptr(tid),
+                                    _ptr(tpr), _ptr(ws), _nbytes(ws), _stream(stream)))
+    if want_target:
+        return tok, cnt, rb, tid, tpr
     return tok, cnt, rb

@@ -18,6 +18,8 @@
 // function of the inputs.  The top-p nucleus is found by a 4-pass radix
 // select over the order-preserving 32-bit key of each logit, with per-digit
 // mass histograms; ties at the cut are broken by index.
+#include <algorithm>
+
 #include "../../include/mtp_verify.h"
 #include "device.h"
 #include "internal.h"
@@ -842,6 +844,560 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
   }
 }
 
+// ---- sampled acceptance: the full sampler pipeline, sparse top-k path -------
+//
+// Ollama mtp.go commit log, the MLX sampler rework: penalties -> top-k ->
+// temperature/softmax -> top-p -> min-p -> normalize -> categorical, the
+// common top-k path keeping sparse per-row ids and probabilities that sampled
+// MTP reuses for acceptance, bonus and residual draws.  Rows are the B*M
+// (sequence, position) pairs.  Kernels: samp_prep (penalised copy of each
+// row, clears the count histograms), four samp_count radix passes (counts of
+// the order-preserving keys: the top-k cut is the K-th largest key, ties by
+// index), samp_compact_count / samp_compact_write (the K kept entries of each
+// row in index order, placed by per-block counts, no atomics), samp_row (one
+// workgroup per row: sort, softmax in fp64, top-p and min-p cuts on exact
+// fixed-point prefix sums, the row's acceptance inputs) and samp_draw (one
+// workgroup per sequence: the accepted run and the residual or bonus draw).
+
+constexpr int kMaxTopK = 1024;
+constexpr int kRowThreads = 1024;
+constexpr int kMaxPenaltyWindow = 4096;
+
+struct SampArgs {
+  const float *z;
+  int64_t ldl;
+  float *zp;                 // penalised rows [rows][V], or nullptr (no penalties)
+  const int32_t *htok;       // history [B][ldh]
+  const int32_t *hlen;       // [B]
+  int64_t ldh;
+  const int32_t *drafts;     // [B][M-1]
+  const float *q;            // dense [B*(M-1)][ldq], or nullptr
+  int64_t ldq;
+  const int32_t *qi;         // sparse [B*(M-1)][Kq]
+  const float *qp;
+  int Kq;
+  const float *u;            // [B][M]
+  const int64_t *base_len;   // [B] or nullptr
+  double T, top_p, min_p;
+  float rp, pp, fq;          // repeat, presence, frequency penalties
+  int last_n;
+  int B, M, V, K, nb, chunk;
+  int32_t *tokens;
+  int32_t *counts;
+  int64_t *rollback;
+  int32_t *out_ids;          // optional [rows][K]
+  float *out_probs;
+  uint32_t *hcnt;            // [4][rows][kBins]
+  SelState *sel;             // [4][rows]: state after `pass` selections; [0]: the cut
+  uint32_t *bcnt;            // [rows][nb][2]: entries above the cut key, ties at it
+  int32_t *lid;              // [rows][K] kept entries in index order
+  float *lz;
+  int32_t *sid;              // [rows][K] the row's support in index order
+  double *sp;                //   p'
+  double *se;                //   e
+  int32_t *nkept;            // [rows]
+  AccIn *acc;                // [rows]
+};
+
+__device__ __forceinline__ const float *samp_src(const SampArgs &p, int row) {
+  return p.zp ? p.zp + (int64_t)row * p.V : p.z + (int64_t)row * p.ldl;
+}
+
+__device__ __forceinline__ int64_t samp_src_ld(const SampArgs &p) { return p.zp ? p.V : p.ldl; }
+
+// Penalised logit: fp32, every operation rounded on its own.
+__device__ __forceinline__ float penalise(float x, int c, const SampArgs &p) {
+  if (p.rp != 1.0f) x = x > 0.0f ? __fdiv_rn(x, p.rp) : __fmul_rn(x, p.rp);
+  x = __fsub_rn(x, __fmul_rn((float)c, p.fq));
+  return __fsub_rn(x, p.pp);
+}
+
+// grid (nb, rows).  Clears this call's count histograms; with penalties,
+// writes the penalised copy of the row: the window (the last last_n tokens
+// of history ++ drafts before the row) is scanned once per block and its
+// tokens inside the block's range kept in LDS, so each entry counts its
+// occurrences there.
+__global__ __launch_bounds__(kBlock) void samp_prep(SampArgs p) {
+  __shared__ int32_t lt[kMaxPenaltyWindow];
+  __shared__ int nl;
+  const int b = blockIdx.x, row = blockIdx.y, seq = row / p.M, pos = row - seq * p.M;
+  const int rows = p.B * p.M;
+  for (int i = b * kBlock + threadIdx.x; i < 4 * kBins; i += p.nb * kBlock)
+    p.hcnt[(size_t)(i / kBins) * rows * kBins + (size_t)row * kBins + (i % kBins)] = 0u;
+  if (!p.zp) return;
+  const float *zr = p.z + (int64_t)row * p.ldl;
+  float *out = p.zp + (int64_t)row * p.V;
+  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
+  float v0[kBatch];
+  load_batch(zr, j0, j1, 0.0f, v0);
+  if (threadIdx.x == 0) nl = 0;
+  __syncthreads();
+  const int Lh = p.htok ? max(0, min(p.hlen[seq], (int)p.ldh)) : 0;
+  const int total = Lh + pos, w0 = max(0, total - p.last_n);
+  for (int c = w0 + (int)threadIdx.x; c < total; c += kBlock) {
+    const int t = c < Lh ? p.htok[(int64_t)seq * p.ldh + c]
+                         : p.drafts[(int64_t)seq * (p.M - 1) + (c - Lh)];
+    if (t >= j0 && t < j1) lt[atomicAdd(&nl, 1)] = t;
+  }
+  __syncthreads();
+  const int n = nl;
+  auto put = [&](const float (&v)[kBatch], int base) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = base + (int)threadIdx.x + i * kBlock;
+      if (j < j1) {
+        int c = 0;
+        for (int k = 0; k < n; ++k) c += lt[k] == j ? 1 : 0;
+        out[j] = c ? penalise(v[i], c, p) : v[i];
+      }
+    }
+  };
+  put(v0, j0);
+  for (int base = j0 + kBatch * kBlock; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(zr, base, j1, 0.0f, v);
+    put(v, base);
+  }
+}
+
+// The cut state after `pass` selection steps of a row: every block of a pass
+// takes the step itself from the previous pass's counts (count-weighted
+// select_bin_wave: the bin where the count from the top reaches K).
+__device__ void samp_select(const SampArgs &p, int pass, int row, u64 *h, uint32_t &prefix,
+                            Fx &above) {
+  const int rows = p.B * p.M;
+  const uint32_t *g = p.hcnt + ((size_t)(pass - 1) * rows + row) * kBins;
+  SelState st = SelState{0ull, 0ull, 0u, 0};
+  if (pass > 1) st = p.sel[(size_t)(pass - 1) * rows + row];
+  for (int d = threadIdx.x; d < kBins; d += blockDim.x) {
+    const uint32_t c = g[d];
+    h[3 * d] = c;
+    h[3 * d + 1] = 0ull;
+    h[3 * d + 2] = c;
+  }
+  __syncthreads();
+  __shared__ uint32_t s_prefix;
+  __shared__ u64 s_alo, s_ahi;
+  if (threadIdx.x < kWave) {
+    Fx ab = Fx{st.above_lo, st.above_hi};
+    const int bin = select_bin_wave(h, Fx{(u64)p.K, 0ull}, ab);
+    if (threadIdx.x == 0) {
+      s_prefix = (st.prefix << 8) | (uint32_t)(bin < 0 ? 0 : bin);
+      s_alo = ab.lo;
+      s_ahi = ab.hi;
+    }
+  }
+  __syncthreads();
+  prefix = s_prefix;
+  above = Fx{s_alo, s_ahi};
+}
+
+// Radix pass `pass` over the keys of the kept-entry candidates: counts by
+// key digit of the entries matching the selected prefix.
+__global__ __launch_bounds__(kBlock) void samp_count(SampArgs p, int pass) {
+  __shared__ uint32_t sh[kBins];
+  __shared__ u64 hbuf[kBins * 3];
+  const int b = blockIdx.x, row = blockIdx.y, rows = p.B * p.M;
+  const float *src = samp_src(p, row);
+  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
+  float v0[kBatch];
+  load_batch(src, j0, j1, 0.0f, v0);
+  for (int i = threadIdx.x; i < kBins; i += kBlock) sh[i] = 0u;
+  uint32_t prefix = 0;
+  Fx above = fx_zero();
+  if (pass > 0) {
+    samp_select(p, pass, row, hbuf, prefix, above);
+    if (b == 0 && threadIdx.x == 0)
+      p.sel[(size_t)pass * rows + row] = SelState{above.lo, above.hi, prefix, 0};
+  } else {
+    __syncthreads();
+  }
+  const int shift = 24 - 8 * pass;
+  auto take = [&](const float (&v)[kBatch], int base) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = base + (int)threadIdx.x + i * kBlock;
+      const uint32_t key = fkey(v[i]);
+      if (j < j1 && (pass == 0 || (key >> (shift + 8)) == prefix))
+        atomicAdd(&sh[(key >> shift) & 0xFF], 1u);
+    }
+  };
+  take(v0, j0);
+  for (int base = j0 + kBatch * kBlock; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(src, base, j1, 0.0f, v);
+    take(v, base);
+  }
+  __syncthreads();
+  uint32_t *g = p.hcnt + ((size_t)pass * rows + row) * kBins;
+  for (int d = threadIdx.x; d < kBins; d += kBlock)
+    if (sh[d]) atomicAdd(g + d, sh[d]);
+}
+
+// Last selection step (every block), then the block's counts of entries
+// above the cut key and of ties at it.
+__global__ __launch_bounds__(kBlock) void samp_compact_count(SampArgs p) {
+  __shared__ u64 hbuf[kBins * 3];
+  __shared__ uint32_t s_a, s_e;
+  const int b = blockIdx.x, row = blockIdx.y;
+  const float *src = samp_src(p, row);
+  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
+  float v0[kBatch];
+  load_batch(src, j0, j1, 0.0f, v0);
+  if (threadIdx.x == 0) s_a = s_e = 0u;
+  uint32_t kappa;
+  Fx above;
+  samp_select(p, 4, row, hbuf, kappa, above);
+  if (b == 0 && threadIdx.x == 0)   // the cut: key kappa, the first t ties by index are kept
+    p.sel[row] = SelState{above.lo, above.hi, kappa, (int32_t)((u64)p.K - above.lo)};
+  uint32_t na = 0, ne = 0;
+  auto take = [&](const float (&v)[kBatch], int base) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = base + (int)threadIdx.x + i * kBlock;
+      const uint32_t key = fkey(v[i]);
+      if (j < j1) {
+        na += key > kappa ? 1u : 0u;
+        ne += key == kappa ? 1u : 0u;
+      }
+    }
+  };
+  take(v0, j0);
+  for (int base = j0 + kBatch * kBlock; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(src, base, j1, 0.0f, v);
+    take(v, base);
+  }
+  if (na) atomicAdd(&s_a, na);
+  if (ne) atomicAdd(&s_e, ne);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    p.bcnt[((size_t)row * p.nb + b) * 2] = s_a;
+    p.bcnt[((size_t)row * p.nb + b) * 2 + 1] = s_e;
+  }
+}
+
+// Exclusive count of `flag` over the threads of a kBlock block (thread
+// order); the block total in `total`.
+__device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t *wtot, uint32_t &total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const u64 m = __ballot(flag);
+  const uint32_t in_wave = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) wtot[wave] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    if (w < wave) before += wtot[w];
+    total += wtot[w];
+  }
+  return before + in_wave;
+}
+
+// The kept entries of the row, in index order: a block's place follows from
+// the counts of the blocks before it (the first t ties by index are kept).
+__global__ __launch_bounds__(kBlock) void samp_compact_write(SampArgs p) {
+  __shared__ uint32_t s_off, s_tb;
+  __shared__ uint32_t wtot[kBlock / kWave];
+  const int b = blockIdx.x, row = blockIdx.y;
+  const float *src = samp_src(p, row);
+  const int j0 = b * p.chunk, j1 = min(p.V, j0 + p.chunk);
+  float v0[kBatch];
+  load_batch(src, j0, j1, 0.0f, v0);
+  const SelState cut = p.sel[row];
+  const uint32_t kappa = cut.prefix, t = (uint32_t)cut.pad;
+  if (threadIdx.x < kWave) {
+    // ties before this block, and the kept entries before it
+    uint32_t ties = 0, kept = 0;
+    for (int k = threadIdx.x; k < b; k += kWave) {
+      const uint32_t a = p.bcnt[((size_t)row * p.nb + k) * 2];
+      const uint32_t e = p.bcnt[((size_t)row * p.nb + k) * 2 + 1];
+      ties += e;
+      kept += a;
+    }
+    for (int m = kWave / 2; m > 0; m >>= 1) {
+      ties += __shfl_xor(ties, m);
+      kept += __shfl_xor(kept, m);
+    }
+    if (threadIdx.x == 0) {
+      s_tb = ties;
+      s_off = kept + min(ties, t);   // ties before the block are kept in index order up to t
+    }
+  }
+  __syncthreads();
+  uint32_t tb = s_tb, off = s_off;
+  int32_t *lid = p.lid + (size_t)row * p.K;
+  float *lz = p.lz + (size_t)row * p.K;
+  auto put = [&](const float (&v)[kBatch], int base) {
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = base + (int)threadIdx.x + i * kBlock;
+      const uint32_t key = fkey(v[i]);
+      const bool tie = j < j1 && key == kappa;
+      uint32_t ntie;
+      const uint32_t trank = tb + block_excl_count(tie, wtot, ntie);
+      const bool keep = j < j1 && (key > kappa || (tie && trank < t));
+      uint32_t nkeep;
+      const uint32_t at = off + block_excl_count(keep, wtot, nkeep);
+      if (keep && at < (uint32_t)p.K) {   // (always: the counts place exactly K entries)
+        lid[at] = j;
+        lz[at] = v[i];
+      }
+      tb += ntie;
+      off += nkeep;
+    }
+  };
+  put(v0, j0);
+  for (int base = j0 + kBatch * kBlock; base < j1; base += kBatch * kBlock) {
+    float v[kBatch];
+    load_batch(src, base, j1, 0.0f, v);
+    put(v, base);
+  }
+}
+
+// ---- per-row pipeline (one workgroup of kRowThreads per row) ----------------
+
+constexpr int kRowWaves = kRowThreads / kWave;
+
+// Exclusive 128-bit prefix over the kRowThreads threads (thread order).
+__device__ Fx fx_row_exclusive(Fx v, Fx *wsum, Fx &total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  Fx incl = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const Fx o = fx_shfl_up(incl, off);
+    if (lane >= off) fx_add(incl, o);
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  Fx before = fx_zero();
+  total = fx_zero();
+  for (int w = 0; w < kRowWaves; ++w) {
+    if (w < wave) fx_add(before, wsum[w]);
+    fx_add(total, wsum[w]);
+  }
+  return fx_sum(before, fx_sub(incl, v));
+}
+
+// Bitonic sort of n (<= kRowThreads) (key, id) pairs in LDS, thread i owning
+// slot i; `before(a, b)` orders them.  Slots n .. pow2 - 1 must hold entries
+// that order last.
+template <typename Before>
+__device__ void bitonic(float *key, int32_t *id, int n2, Before before) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+      const int i = threadIdx.x, l = i ^ j;
+      if (i < n2 && l > i) {
+        const bool up = (i & k) == 0;
+        const float ki = key[i], kl = key[l];
+        const int32_t ii = id[i], il = id[l];
+        const bool swap = up ? before(kl, il, ki, ii) : before(ki, ii, kl, il);
+        if (swap) {
+          key[i] = kl; key[l] = ki;
+          id[i] = il; id[l] = ii;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// q of draft row r (r = seq * (M-1) + pos) at id x; sparse lists take their
+// first listing of x (staged in LDS: qid/qpr, Kq entries).
+__device__ __forceinline__ double samp_q(const SampArgs &p, int r, int x, const int32_t *qid,
+                                         const float *qpr) {
+  if (p.q) return (double)p.q[(int64_t)r * p.ldq + x];
+  for (int k = 0; k < p.Kq; ++k)
+    if (qid[k] == x) return (double)qpr[k];
+  return 0.0;
+}
+
+__global__ __launch_bounds__(kRowThreads) void samp_row(SampArgs p) {
+  __shared__ float skey[kMaxTopK];
+  __shared__ int32_t sid[kMaxTopK];
+  __shared__ Fx wsum[kRowWaves];
+  __shared__ int32_t qid[kMaxTopK];
+  __shared__ float qpr[kMaxTopK];
+  __shared__ int s_cp, s_cm;
+  __shared__ double s_px;
+  __shared__ int s_qk;
+  const int row = blockIdx.x, seq = row / p.M, pos = row - seq * p.M;
+  const int j = threadIdx.x, K = p.K;
+  const bool draft_row = pos < p.M - 1;
+  const int r = seq * (p.M - 1) + pos;
+  // the draft's sparse list (for q at the draft) is staged with the entries
+  if (draft_row && !p.q)
+    for (int k = j; k < p.Kq; k += kRowThreads) {
+      qid[k] = p.qi[(int64_t)r * p.Kq + k];
+      qpr[k] = p.qp[(int64_t)r * p.Kq + k];
+    }
+  int n2 = 1;
+  while (n2 < K) n2 <<= 1;
+  if (j < n2) {
+    skey[j] = j < K ? p.lz[(size_t)row * K + j] : -__builtin_inff();
+    sid[j] = j < K ? p.lid[(size_t)row * K + j] : 0x7FFFFFFF;
+  }
+  if (j == 0) {
+    s_cp = K;
+    s_cm = K;
+    s_px = 0.0;
+    s_qk = 0x7FFFFFFF;
+  }
+  // order of probability: value descending, index ascending (padding last)
+  bitonic(skey, sid, n2, [](float ka, int32_t ia, float kb, int32_t ib) {
+    return ka > kb || (ka == kb && ia < ib);
+  });
+  double e = 0.0;
+  Fx fe = fx_zero();
+  if (j < K) {
+    e = p.T == 0.0 ? (j == 0 ? 1.0 : 0.0) : exp(((double)skey[j] - (double)skey[0]) / p.T);
+    fe = to_fx(e);
+  }
+  Fx S;
+  const Fx before = fx_row_exclusive(fe, wsum, S);
+  const Fx cum = fx_sum(before, fe);
+  // top-p: the first entry whose cumulative mass reaches top_p * S
+  if (p.T == 0.0) {
+    if (j == 0) s_cp = 1;
+  } else if (p.top_p < 1.0) {
+    Fx thr = to_fx(p.top_p > 0.0 ? p.top_p * fx_to_double(S) : 0.0);
+    if (!fx_nonzero(thr)) thr.lo = 1ull;
+    if (j < K && fx_ge(cum, thr) && !fx_ge(before, thr)) s_cp = j + 1;
+  }
+  // min-p: the first entry (after the first) with e below min_p
+  if (p.min_p > 0.0 && j >= 1 && j < K && e < p.min_p) atomicMin(&s_cm, j);
+  __syncthreads();
+  const int kept = min(s_cp, s_cm);
+  // mass of the kept prefix (exact), then p' = e / mass
+  __shared__ Fx s_mass;
+  if (j == kept - 1) s_mass = cum;
+  __syncthreads();
+  const double mass = fx_to_double(s_mass);
+  const bool in = j < kept;
+  const double pj = in ? e / mass : 0.0;
+  if (p.out_ids) {
+    if (j < K) {
+      p.out_ids[(size_t)row * K + j] = in ? sid[j] : -1;
+      p.out_probs[(size_t)row * K + j] = in ? (float)pj : 0.0f;
+    }
+  }
+  // acceptance inputs of the row's draft
+  if (draft_row) {
+    const int x = p.drafts[(int64_t)r];
+    if (in && sid[j] == x) s_px = pj;
+    if (!p.q)
+      for (int k = j; k < p.Kq; k += kRowThreads)
+        if (qid[k] == x) atomicMin(&s_qk, k);
+  }
+  // the support in index order for the draws: e and p' by id
+  __shared__ double se_s[kMaxTopK], sp_s[kMaxTopK];
+  __syncthreads();
+  if (j < kept) {
+    se_s[j] = e;
+    sp_s[j] = pj;
+    skey[j] = (float)j;   // remembers the slot of each id through the sort
+  }
+  int m2 = 1;
+  while (m2 < kept) m2 <<= 1;
+  if (j >= kept && j < m2) {
+    sid[j] = 0x7FFFFFFF;
+    skey[j] = 0.0f;
+  }
+  bitonic(skey, sid, m2, [](float, int32_t ia, float, int32_t ib) { return ia < ib; });
+  if (j < kept) {
+    const int s = (int)skey[j];
+    p.sid[(size_t)row * K + j] = sid[j];
+    p.se[(size_t)row * K + j] = se_s[s];
+    p.sp[(size_t)row * K + j] = sp_s[s];
+  }
+  if (j == 0) {
+    p.nkept[row] = kept;
+    if (draft_row) {
+      const int x = p.drafts[(int64_t)r];
+      double qx = 0.0;
+      if (x >= 0 && x < p.V) {
+        if (p.q) qx = (double)p.q[(int64_t)r * p.ldq + x];
+        else if (s_qk != 0x7FFFFFFF) qx = (double)qpr[s_qk];
+      }
+      p.acc[row] = AccIn{(x >= 0 && x < p.V) ? s_px : 0.0, qx};
+    }
+  }
+}
+
+// One workgroup per sequence: the accepted run a (first draft with
+// u_i * q_i(x_i) >= p'_i(x_i)), then the draw from the residual
+// max(0, p'_a - q_a) over row a's support (from p'_a if it is all zero), or
+// the bonus from p'_{M-1}, in index order: the smallest id whose cumulative
+// weight exceeds u_{M-1} times the total (the last positive if rounding
+// passes the end).
+__global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
+  __shared__ Fx wsum[kRowWaves];
+  __shared__ int32_t qid[kMaxTopK];
+  __shared__ float qpr[kMaxTopK];
+  __shared__ int s_a, s_pick, s_last;
+  const int seq = blockIdx.x, j = threadIdx.x;
+  if (j < kWave) {
+    bool reject = false;
+    if (j < p.M - 1) {
+      const AccIn in = p.acc[seq * p.M + j];
+      reject = !((double)p.u[(int64_t)seq * p.M + j] * in.qx < in.px);
+    }
+    const u64 rej = __ballot(reject);
+    if (j == 0) {
+      s_a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
+      s_pick = 0x7FFFFFFF;
+      s_last = -1;
+    }
+  }
+  __syncthreads();
+  const int a = s_a, row = seq * p.M + a;
+  const bool residual = a < p.M - 1;
+  const int r = seq * (p.M - 1) + a;
+  if (residual && !p.q)
+    for (int k = j; k < p.Kq; k += kRowThreads) {
+      qid[k] = p.qi[(int64_t)r * p.Kq + k];
+      qpr[k] = p.qp[(int64_t)r * p.Kq + k];
+    }
+  __syncthreads();
+  const int n = p.nkept[row];
+  int32_t id = -1;
+  Fx wr = fx_zero(), we = fx_zero();
+  if (j < n) {
+    id = p.sid[(size_t)row * p.K + j];
+    we = to_fx(p.se[(size_t)row * p.K + j]);
+    if (residual) {
+      const double d = p.sp[(size_t)row * p.K + j] - samp_q(p, r, id, qid, qpr);
+      wr = to_fx(d > 0.0 ? d : 0.0);
+    }
+  }
+  Fx tres;
+  fx_row_exclusive(wr, wsum, tres);
+  const bool use_res = residual && fx_nonzero(tres);
+  const Fx w = use_res ? wr : we;
+  Fx W;
+  const Fx before = fx_row_exclusive(w, wsum, W);
+  const Fx target = to_fx((double)p.u[(int64_t)seq * p.M + p.M - 1] * fx_to_double(W));
+  if (j < n) {
+    const Fx cum = fx_sum(before, w);
+    if (fx_gt(cum, target) && !fx_gt(before, target)) s_pick = id;
+    if (fx_nonzero(w)) atomicMax(&s_last, j);
+  }
+  __syncthreads();
+  if (j == 0 && s_pick == 0x7FFFFFFF)   // rounding passed the end
+    s_pick = s_last >= 0 ? p.sid[(size_t)row * p.K + s_last] : p.V - 1;
+  __syncthreads();
+  if (j < p.M) {
+    const int32_t tok = j < a ? p.drafts[(int64_t)seq * (p.M - 1) + j] : (j == a ? s_pick : -1);
+    p.tokens[(int64_t)seq * p.M + j] = tok;
+  }
+  if (j == 0) {
+    p.counts[2 * seq] = a;
+    p.counts[2 * seq + 1] = a + 1;
+    p.rollback[seq] = (p.base_len ? p.base_len[seq] : 0) + a + 1;
+  }
+}
+
 }  // namespace
 
 size_t accept_ws_bytes(int M, int V) { return layout(M, V).bytes; }
@@ -894,6 +1450,87 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   hipLaunchKernelGGL(rej_select, dim3(M), dim3(kBlock), 0, stream, p);
   hipLaunchKernelGGL(rej_draw_sums, dim3(p.nbd), dim3(kBlock), 0, stream, p);
   hipLaunchKernelGGL(rej_draw_pick, dim3(1), dim3(kBlock), 0, stream, p);
+  return hipGetLastError();
+}
+
+// ---- sampled acceptance: host side -------------------------------------------
+
+namespace {
+
+struct SampLayout {
+  size_t zp, hcnt, sel, bcnt, lid, lz, sid, sp, se, nkept, acc, bytes;
+};
+
+SampLayout samp_layout(int B, int M, int V, int top_k, bool penalties) {
+  const size_t rows = (size_t)B * M, K = (size_t)std::min(top_k, V);
+  const size_t nb = (size_t)blocks_per_row(V);
+  SampLayout L;
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    size_t at = o;
+    o += (n + 255) & ~(size_t)255;
+    return at;
+  };
+  L.zp = take(penalties ? sizeof(float) * rows * V : 0);
+  L.hcnt = take(sizeof(uint32_t) * 4 * rows * kBins);
+  L.sel = take(sizeof(SelState) * 4 * rows);
+  L.bcnt = take(sizeof(uint32_t) * 2 * rows * nb);
+  L.lid = take(sizeof(int32_t) * rows * K);
+  L.lz = take(sizeof(float) * rows * K);
+  L.sid = take(sizeof(int32_t) * rows * K);
+  L.sp = take(sizeof(double) * rows * K);
+  L.se = take(sizeof(double) * rows * K);
+  L.nkept = take(sizeof(int32_t) * rows);
+  L.acc = take(sizeof(AccIn) * rows);
+  L.bytes = o;
+  return L;
+}
+
+}  // namespace
+
+size_t sampled_ws_bytes(int B, int M, int V, int top_k, bool penalties) {
+  return samp_layout(B, M, V, top_k, penalties).bytes;
+}
+
+hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t stream) {
+  const bool pen = c.penalty_last_n > 0 &&
+                   (c.repeat_penalty != 1.0f || c.presence_penalty != 0.0f ||
+                    c.frequency_penalty != 0.0f);
+  const SampLayout L = samp_layout(c.B, c.M, c.V, c.top_k, pen);
+  uint8_t *w = static_cast<uint8_t *>(ws);
+  SampArgs p;
+  p.z = c.logits; p.ldl = c.ldl;
+  p.zp = pen ? reinterpret_cast<float *>(w + L.zp) : nullptr;
+  p.htok = c.history; p.hlen = c.history_len; p.ldh = c.ldh;
+  p.drafts = c.drafts;
+  p.q = c.q; p.ldq = c.ldq; p.qi = c.q_ids; p.qp = c.q_probs; p.Kq = c.Kq;
+  p.u = c.uniforms; p.base_len = c.base_len;
+  p.T = (double)c.temperature; p.top_p = (double)c.top_p; p.min_p = (double)c.min_p;
+  p.rp = c.repeat_penalty; p.pp = c.presence_penalty; p.fq = c.frequency_penalty;
+  p.last_n = c.penalty_last_n;
+  p.B = c.B; p.M = c.M; p.V = c.V; p.K = std::min(c.top_k, c.V);
+  p.nb = blocks_per_row(c.V); p.chunk = (c.V + p.nb - 1) / p.nb;
+  p.tokens = c.tokens; p.counts = c.counts; p.rollback = c.rollback;
+  p.out_ids = c.out_ids; p.out_probs = c.out_probs;
+  p.hcnt = reinterpret_cast<uint32_t *>(w + L.hcnt);
+  p.sel = reinterpret_cast<SelState *>(w + L.sel);
+  p.bcnt = reinterpret_cast<uint32_t *>(w + L.bcnt);
+  p.lid = reinterpret_cast<int32_t *>(w + L.lid);
+  p.lz = reinterpret_cast<float *>(w + L.lz);
+  p.sid = reinterpret_cast<int32_t *>(w + L.sid);
+  p.sp = reinterpret_cast<double *>(w + L.sp);
+  p.se = reinterpret_cast<double *>(w + L.se);
+  p.nkept = reinterpret_cast<int32_t *>(w + L.nkept);
+  p.acc = reinterpret_cast<AccIn *>(w + L.acc);
+  const int rows = c.B * c.M;
+  const dim3 grid(p.nb, rows);
+  hipLaunchKernelGGL(samp_prep, grid, dim3(kBlock), 0, stream, p);
+  for (int pass = 0; pass < 4; ++pass)
+    hipLaunchKernelGGL(samp_count, grid, dim3(kBlock), 0, stream, p, pass);
+  hipLaunchKernelGGL(samp_compact_count, grid, dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL(samp_compact_write, grid, dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL(samp_row, dim3(rows), dim3(kRowThreads), 0, stream, p);
+  hipLaunchKernelGGL(samp_draw, dim3(c.B), dim3(kRowThreads), 0, stream, p);
   return hipGetLastError();
 }
 

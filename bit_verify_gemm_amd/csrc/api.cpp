@@ -52,6 +52,8 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 constexpr int kMaxAcceptRows = 64;
 constexpr int kMaxVocab = 1 << 26;
+constexpr int kMaxSampledSeqs = 1024;
+constexpr int kMaxPenaltyWindow = 4096;
 
 int check_accept_common(const char *who, const float *logits, int M, int V, int64_t ldl,
                         const int32_t *drafts, int32_t *tokens, int32_t *counts,
@@ -229,4 +231,84 @@ int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
                     who);
 }
 
-}  // extern "C"
+size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties) {
+  if (B < 1 || B > kMaxSampledSeqs || M < 1 || M > kMaxAcceptRows || V < 1 || V > kMaxVocab ||
+      top_k < 1 || top_k > MTP_MAX_TOP_K)
+    return 0;
+  return mtp::sampled_ws_bytes(B, M, V, top_k, penalties != 0);
+}
+
+int mtp_accept_sampled(const float *logits, int B, int M, int V, int64_t ldl,
+                       const int32_t *history, const int32_t *history_len, int64_t ldh,
+                       const int32_t *draft_ids, const float *draft_probs, int64_t ldq,
+                       const int32_t *draft_topk_ids, const float *draft_topk_probs, int Kq,
+                       const float *uniforms, const mtp_sampler *params, const int64_t *base_len,
+                       int32_t *out_tokens, int32_t *out_counts, int64_t *out_rollback,
+                       int32_t *out_target_ids, float *out_target_probs, void *ws,
+                       size_t ws_bytes, void *stream) {
+  const char *who = "mtp_accept_sampled";
+  if (!params) return fail(MTP_ERR_NULL, "%s: params are required", who);
+  const mtp_sampler s = *params;
+  if (B < 1 || B > kMaxSampledSeqs)
+    return fail(MTP_ERR_SHAPE, "%s: B=%d out of [1, %d]", who, B, kMaxSampledSeqs);
+  if (M < 1 || M > kMaxAcceptRows) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, %d]", who, M, kMaxAcceptRows);
+  if (V < 1 || V > kMaxVocab) return fail(MTP_ERR_SHAPE, "%s: V=%d out of [1, %d]", who, V, kMaxVocab);
+  if (ldl < V) return fail(MTP_ERR_SHAPE, "%s: ldl=%lld < V=%d", who, (long long)ldl, V);
+  if (!logits || !uniforms || !out_tokens || !out_counts || !out_rollback)
+    return fail(MTP_ERR_NULL, "%s: logits, uniforms and outputs are required", who);
+  if (!aligned(logits, 4)) return fail(MTP_ERR_ALIGN, "%s: logits must be 4-byte aligned", who);
+  if (!(s.temperature >= 0.0f))
+    return fail(MTP_ERR_VALUE, "%s: temperature must be >= 0 (got %g)", who, (double)s.temperature);
+  if (s.top_p != s.top_p || s.min_p != s.min_p || s.repeat_penalty != s.repeat_penalty ||
+      s.presence_penalty != s.presence_penalty || s.frequency_penalty != s.frequency_penalty)
+    return fail(MTP_ERR_VALUE, "%s: NaN sampler parameter", who);
+  if (s.top_k < 1 || s.top_k > MTP_MAX_TOP_K)
+    return fail(MTP_ERR_VALUE, "%s: top_k=%d out of [1, %d] (this path keeps the top-k entries)",
+                who, s.top_k, MTP_MAX_TOP_K);
+  if (!(s.repeat_penalty > 0.0f))
+    return fail(MTP_ERR_VALUE, "%s: repeat_penalty must be > 0", who);
+  if (s.penalty_last_n > kMaxPenaltyWindow)
+    return fail(MTP_ERR_VALUE, "%s: penalty_last_n=%d above %d", who, s.penalty_last_n,
+                kMaxPenaltyWindow);
+  if (history && !history_len) return fail(MTP_ERR_NULL, "%s: history needs history_len", who);
+  if (history && ldh < 1) return fail(MTP_ERR_SHAPE, "%s: ldh=%lld < 1", who, (long long)ldh);
+  if (M > 1) {
+    if (!draft_ids) return fail(MTP_ERR_NULL, "%s: draft_ids required for M > 1", who);
+    if (draft_probs) {
+      if (ldq < V) return fail(MTP_ERR_SHAPE, "%s: ldq=%lld < V=%d", who, (long long)ldq, V);
+    } else {
+      if (!draft_topk_ids || !draft_topk_probs)
+        return fail(MTP_ERR_NULL, "%s: dense or sparse draft distributions required for M > 1",
+                    who);
+      if (Kq < 1 || Kq > MTP_MAX_TOP_K)
+        return fail(MTP_ERR_SHAPE, "%s: Kq=%d out of [1, %d]", who, Kq, MTP_MAX_TOP_K);
+    }
+  }
+  if ((out_target_ids == nullptr) != (out_target_probs == nullptr))
+    return fail(MTP_ERR_NULL, "%s: target ids and probs are written together", who);
+  const bool pen = s.penalty_last_n > 0 &&
+                   (s.repeat_penalty != 1.0f || s.presence_penalty != 0.0f ||
+                    s.frequency_penalty != 0.0f);
+  const size_t need = mtp::sampled_ws_bytes(B, M, V, s.top_k, pen);
+  if (!ws || ws_bytes < need)
+    return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 256)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+  mtp::SampledCall c;
+  c.logits = logits; c.B = B; c.M = M; c.V = V; c.ldl = ldl;
+  c.history = history; c.history_len = history_len; c.ldh = ldh;
+  c.drafts = draft_ids; c.q = draft_probs; c.ldq = ldq;
+  c.q_ids = draft_probs ? nullptr : draft_topk_ids;
+  c.q_probs = draft_probs ? nullptr : draft_topk_probs;
+  c.Kq = draft_probs ? 0 : Kq;
+  c.uniforms = uniforms;
+  c.temperature = s.temperature; c.top_p = s.top_p; c.min_p = s.min_p; c.top_k = s.top_k;
+  c.repeat_penalty = s.repeat_penalty; c.presence_penalty = s.presence_penalty;
+  c.frequency_penalty = s.frequency_penalty; c.penalty_last_n = s.penalty_last_n;
+  c.base_len = base_len;
+  c.tokens = out_tokens; c.counts = out_counts; c.rollback = out_rollback;
+  c.out_ids = out_target_ids; c.out_probs = out_target_probs;
+  return hip_status(mtp::launch_accept_sampled(c, ws, static_cast<hipStream_t>(stream)), who);
+}
+
+}  // extern "C\"

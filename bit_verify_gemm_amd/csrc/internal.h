@@ -40,6 +40,34 @@ hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64
 
 size_t accept_ws_bytes(int M, int V);
 
+// Sampled acceptance of B sequences (mtp_accept_sampled), arguments checked.
+struct SampledCall {
+  const float *logits;
+  int B, M, V;
+  int64_t ldl;
+  const int32_t *history, *history_len;
+  int64_t ldh;
+  const int32_t *drafts;
+  const float *q;
+  int64_t ldq;
+  const int32_t *q_ids;
+  const float *q_probs;
+  int Kq;
+  const float *uniforms;
+  float temperature, top_p, min_p;
+  int top_k;
+  float repeat_penalty, presence_penalty, frequency_penalty;
+  int penalty_last_n;
+  const int64_t *base_len;
+  int32_t *tokens, *counts;
+  int64_t *rollback;
+  int32_t *out_ids;
+  float *out_probs;
+};
+
+size_t sampled_ws_bytes(int B, int M, int V, int top_k, bool penalties);
+hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t stream);
+
 hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
                                 const int32_t *drafts, int64_t base_len, int32_t *tokens,
                                 int32_t *counts, int64_t *rollback, void *ws, hipStream_t stream);

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 2
+#define MTP_ABI_VERSION 3
 
 enum {
   MTP_OK = 0,
@@ -236,6 +236,84 @@ int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
                          void *ws, size_t ws_bytes, void *stream);
 
 size_t mtp_accept_workspace_bytes(int M, int V);
+
+/*
+ * Sampler parameters of mtp_accept_sampled, applied in the order of the
+ * Ollama mtp.go commit log's MLX sampler rework: (1) penalties, (2) top-k,
+ * (3) temperature/softmax, (4) top-p, (5) min-p, (6) normalize,
+ * (7) categorical.  The pages name the steps only; the formulas are the
+ * usual ones:
+ *   (1) for a token seen c > 0 times in the row's penalty window (the last
+ *       penalty_last_n tokens of history ++ the drafts before the row; none
+ *       if penalty_last_n <= 0), in fp32, each operation rounded on its own:
+ *       z = z > 0 ? z / repeat_penalty : z * repeat_penalty (skipped when it
+ *       is 1), then z = (z - c * frequency_penalty) - presence_penalty.
+ *   (2) keep the top_k entries first in the order (z desc, index asc).
+ *   (3) e = exp((z - z_max) / temperature) in fp64 (temperature 0: a point
+ *       mass at the first entry of the order).
+ *   (4) keep the shortest prefix of that order whose e-mass reaches top_p
+ *       times the kept mass (top_p >= 1 keeps all, top_p <= 0 the first).
+ *   (5) drop entries with e < min_p, i.e. p < min_p * max p (min_p <= 0:
+ *       off); the first entry always stays.
+ *   (6) p' = e / (mass of what is left).
+ *   (7) a draw picks the smallest id with cumulative weight > u * total.
+ */
+typedef struct {
+  float temperature;        /* >= 0 */
+  float top_p;
+  float min_p;
+  int32_t top_k;            /* 1 .. MTP_MAX_TOP_K */
+  float repeat_penalty;     /* > 0; 1 = none */
+  float presence_penalty;
+  float frequency_penalty;
+  int32_t penalty_last_n;   /* <= MTP_MAX_PENALTY_WINDOW; <= 0: no penalties */
+} mtp_sampler;
+
+#define MTP_MAX_TOP_K 1024
+#define MTP_MAX_PENALTY_WINDOW 4096
+
+/*
+ * Sampled acceptance (Leviathan/Chen rejection sampling with residual
+ * correction) of B sequences of M verified rows each, on the sparse top-k
+ * path: each row's target p' is built by the sampler pipeline above and kept
+ * as at most top_k (id, probability) pairs on the GPU; acceptance, the
+ * residual draw max(0, p'_a - q_a) (from p'_a if it is all zero) and the
+ * bonus draw from p'_{M-1} reuse them (same article).  Per sequence b, with
+ * u = uniforms[b]: accept draft x_i iff u_i * q_i(x_i) < p'_i(x_i), stop at
+ * the first rejection a; the draws use u_{M-1}.  Outputs per sequence as
+ * for mtp_accept_greedy; rollback[b] = base_len[b] + a + 1.
+ *   logits, ldl      fp32 [B*M][ldl], row b*M + i (finite values)
+ *   history, ldh     int32 [B][ldh] committed tokens, oldest first, or NULL;
+ *   history_len      int32 [B] (device), clamped to [0, ldh]
+ *   draft_ids        int32 [B][M-1]
+ *   draft_probs, ldq dense fp32 [B*(M-1)][ldq], or NULL and then
+ *   draft_topk_ids / draft_topk_probs: sparse [B*(M-1)][Kq] (an id not listed
+ *                    has probability 0; the first listing of an id counts)
+ *   uniforms         fp32 [B][M] in [0, 1)
+ *   params           (host) the sampler
+ *   base_len         int64 [B] (device), or NULL (0)
+ *   out_tokens [B][M], out_counts [B][2], out_rollback [B]
+ *   out_target_ids / out_target_probs  optional int32 / fp32 [B*M][K],
+ *                    K = min(top_k, V): each row's p' in order of
+ *                    probability, -1 / 0 past its support
+ *   ws, ws_bytes     at least mtp_accept_sampled_workspace_bytes(B, M, V,
+ *                    top_k, penalties on); calls sharing it must not overlap
+ * Errors: MTP_ERR_VALUE for temperature < 0 or NaN, a NaN parameter, top_k
+ * outside [1, MTP_MAX_TOP_K], repeat_penalty <= 0 or a window above
+ * MTP_MAX_PENALTY_WINDOW; 1 <= B <= 1024, 1 <= M <= 64.
+ */
+int mtp_accept_sampled(const float *logits, int B, int M, int V, int64_t ldl,
+                       const int32_t *history, const int32_t *history_len, int64_t ldh,
+                       const int32_t *draft_ids, const float *draft_probs, int64_t ldq,
+                       const int32_t *draft_topk_ids, const float *draft_topk_probs, int Kq,
+                       const float *uniforms, const mtp_sampler *params, const int64_t *base_len,
+                       int32_t *out_tokens, int32_t *out_counts, int64_t *out_rollback,
+                       int32_t *out_target_ids, float *out_target_probs, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* penalties: nonzero when penalty_last_n > 0 and a penalty differs from its
+ * neutral value (the penalised rows then take a workspace copy). */
+size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties);
 
 /* Thread-local message for the last non-zero status of this thread. */
 const char *mtp_last_error(void);

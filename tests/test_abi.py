@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bv.abi_version() == 2
+    assert bv.abi_version() == 3
 
 
 def test_packed_sizes():
@@ -152,3 +152,41 @@ def test_moe_rejects_bad_arguments():
     assert call(gu=None) == -1
     assert call(dn=FAKE_ODD) == -3
     assert call(wsb=need - 1) == -5
+
+
+def test_accept_sampled_rejects_bad_arguments():
+    L = bv.lib()
+    B, M, V = 2, 4, 100
+    need = bv.accept_sampled_workspace_bytes(B, M, V, 40, False)
+    assert need > 0 and bv.accept_sampled_workspace_bytes(B, M, V, 0, False) == 0
+    assert bv.accept_sampled_workspace_bytes(B, M, V, 40, True) > need   # penalised copies
+    ws = ctypes.c_void_p(0x100000)
+
+    def call(params, B=B, M=M, V=V, drafts=FAKE, q=FAKE, qi=None, qp=None, Kq=0, ws_bytes=need,
+             uniforms=FAKE, tid=None, tpr=None):
+        return L.mtp_accept_sampled(FAKE, B, M, V, V, None, None, 0, drafts, q, V, qi, qp, Kq,
+                                    uniforms, ctypes.cast(ctypes.pointer(params), ctypes.c_void_p),
+                                    None, FAKE, FAKE, FAKE, tid, tpr, ws, ws_bytes, None)
+
+    ok = bv.Sampler(temperature=0.6, top_k=40)
+    assert call(bv.Sampler(temperature=-1.0, top_k=40)) == -7
+    assert call(bv.Sampler(temperature=float("nan"), top_k=40)) == -7
+    assert call(bv.Sampler(top_p=float("nan"), top_k=40)) == -7
+    assert call(bv.Sampler(top_k=0)) == -7
+    assert call(bv.Sampler(top_k=1025)) == -7
+    assert call(bv.Sampler(top_k=40, repeat_penalty=0.0)) == -7
+    assert call(bv.Sampler(top_k=40, penalty_last_n=4097)) == -7
+    assert call(ok, B=0) == -2
+    assert call(ok, B=1025) == -2
+    assert call(ok, M=65) == -2
+    assert call(ok, drafts=None) == -1
+    assert call(ok, q=None) == -1                        # neither dense nor sparse q
+    assert call(ok, q=None, qi=FAKE, qp=FAKE, Kq=0) == -2
+    assert call(ok, q=None, qi=FAKE, qp=FAKE, Kq=1025) == -2
+    assert call(ok, uniforms=None) == -1
+    assert call(ok, tid=FAKE) == -1                      # ids without probs
+    assert call(ok, ws_bytes=need - 1) == -5
+    assert L.mtp_accept_sampled(FAKE, B, M, V, V, None, None, 0, FAKE, FAKE, V, None, None, 0,
+                                FAKE, None, None, FAKE, FAKE, FAKE, None, None, ws, need,
+                                None) == -1              # no params
+    assert bv.lib().mtp_last_error()
