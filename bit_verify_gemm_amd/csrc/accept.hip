@@ -1099,6 +1099,7 @@ __device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t *wtot, 
 // the counts of the blocks before it (the first t ties by index are kept).
 __global__ __launch_bounds__(kBlock) void samp_compact_write(SampArgs p) {
   __shared__ uint32_t s_off, s_tb;
+  __shared__ bool s_none;
   __shared__ uint32_t wtot[kBlock / kWave];
   const int b = blockIdx.x, row = blockIdx.y;
   const float *src = samp_src(p, row);
@@ -1123,9 +1124,14 @@ __global__ __launch_bounds__(kBlock) void samp_compact_write(SampArgs p) {
     if (threadIdx.x == 0) {
       s_tb = ties;
       s_off = kept + min(ties, t);   // ties before the block are kept in index order up to t
+      // nothing to place: no entry above the cut and no tie still kept
+      const uint32_t a = p.bcnt[((size_t)row * p.nb + b) * 2];
+      const uint32_t e = p.bcnt[((size_t)row * p.nb + b) * 2 + 1];
+      s_none = a == 0u && (e == 0u || ties >= t);
     }
   }
   __syncthreads();
+  if (s_none) return;
   uint32_t tb = s_tb, off = s_off;
   int32_t *lid = p.lid + (size_t)row * p.K;
   float *lz = p.lz + (size_t)row * p.K;
@@ -1159,8 +1165,9 @@ __global__ __launch_bounds__(kBlock) void samp_compact_write(SampArgs p) {
 
 constexpr int kRowWaves = kRowThreads / kWave;
 
-// Exclusive 128-bit prefix over the kRowThreads threads (thread order).
+// Exclusive 128-bit prefix over the threads of the workgroup (thread order).
 __device__ Fx fx_row_exclusive(Fx v, Fx *wsum, Fx &total) {
+  const int nw = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   Fx incl = v;
   for (int off = 1; off < kWave; off <<= 1) {
@@ -1172,15 +1179,15 @@ __device__ Fx fx_row_exclusive(Fx v, Fx *wsum, Fx &total) {
   __syncthreads();
   Fx before = fx_zero();
   total = fx_zero();
-  for (int w = 0; w < kRowWaves; ++w) {
+  for (int w = 0; w < nw; ++w) {
     if (w < wave) fx_add(before, wsum[w]);
     fx_add(total, wsum[w]);
   }
   return fx_sum(before, fx_sub(incl, v));
 }
 
-// Bitonic sort of n (<= kRowThreads) (key, id) pairs in LDS, thread i owning
-// slot i; `before(a, b)` orders them.  Slots n .. pow2 - 1 must hold entries
+// Bitonic sort of n2 (a power of two, at most the workgroup size) (key, id)
+// pairs in LDS, thread i owning slot i; `before(a, b)` orders them.  Slots n .. pow2 - 1 must hold entries
 // that order last.
 template <typename Before>
 __device__ void bitonic(float *key, int32_t *id, int n2, Before before) {
@@ -1223,12 +1230,19 @@ __global__ __launch_bounds__(kRowThreads) void samp_row(SampArgs p) {
   __shared__ double s_px;
   __shared__ int s_qk;
   const int row = blockIdx.x, seq = row / p.M, pos = row - seq * p.M;
-  const int j = threadIdx.x, K = p.K;
+  const int j = threadIdx.x, K = p.K, nt = blockDim.x;
   const bool draft_row = pos < p.M - 1;
   const int r = seq * (p.M - 1) + pos;
-  // the draft's sparse list (for q at the draft) is staged with the entries
+  // the draft and its dense q are loaded first (they do not depend on the
+  // cuts); a sparse list is staged with the entries
+  int x = -1;
+  double qx_dense = 0.0;
+  if (draft_row) {
+    x = p.drafts[(int64_t)r];
+    if (p.q && j == 0 && x >= 0 && x < p.V) qx_dense = (double)p.q[(int64_t)r * p.ldq + x];
+  }
   if (draft_row && !p.q)
-    for (int k = j; k < p.Kq; k += kRowThreads) {
+    for (int k = j; k < p.Kq; k += nt) {
       qid[k] = p.qi[(int64_t)r * p.Kq + k];
       qpr[k] = p.qp[(int64_t)r * p.Kq + k];
     }
@@ -1284,10 +1298,9 @@ __global__ __launch_bounds__(kRowThreads) void samp_row(SampArgs p) {
   }
   // acceptance inputs of the row's draft
   if (draft_row) {
-    const int x = p.drafts[(int64_t)r];
     if (in && sid[j] == x) s_px = pj;
     if (!p.q)
-      for (int k = j; k < p.Kq; k += kRowThreads)
+      for (int k = j; k < p.Kq; k += nt)
         if (qid[k] == x) atomicMin(&s_qk, k);
   }
   // the support in index order for the draws: e and p' by id
@@ -1314,12 +1327,8 @@ __global__ __launch_bounds__(kRowThreads) void samp_row(SampArgs p) {
   if (j == 0) {
     p.nkept[row] = kept;
     if (draft_row) {
-      const int x = p.drafts[(int64_t)r];
       double qx = 0.0;
-      if (x >= 0 && x < p.V) {
-        if (p.q) qx = (double)p.q[(int64_t)r * p.ldq + x];
-        else if (s_qk != 0x7FFFFFFF) qx = (double)qpr[s_qk];
-      }
+      if (x >= 0 && x < p.V) qx = p.q ? qx_dense : (s_qk != 0x7FFFFFFF ? (double)qpr[s_qk] : 0.0);
       p.acc[row] = AccIn{(x >= 0 && x < p.V) ? s_px : 0.0, qx};
     }
   }
@@ -1336,7 +1345,9 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
   __shared__ int32_t qid[kMaxTopK];
   __shared__ float qpr[kMaxTopK];
   __shared__ int s_a, s_pick, s_last;
-  const int seq = blockIdx.x, j = threadIdx.x;
+  const int seq = blockIdx.x, j = threadIdx.x, nt = blockDim.x;
+  // the drafts (committed as they are up to the run) do not depend on it
+  const int32_t dj = j < p.M - 1 ? p.drafts[(int64_t)seq * (p.M - 1) + j] : -1;
   if (j < kWave) {
     bool reject = false;
     if (j < p.M - 1) {
@@ -1355,7 +1366,7 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
   const bool residual = a < p.M - 1;
   const int r = seq * (p.M - 1) + a;
   if (residual && !p.q)
-    for (int k = j; k < p.Kq; k += kRowThreads) {
+    for (int k = j; k < p.Kq; k += nt) {
       qid[k] = p.qi[(int64_t)r * p.Kq + k];
       qpr[k] = p.qp[(int64_t)r * p.Kq + k];
     }
@@ -1388,7 +1399,7 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
     s_pick = s_last >= 0 ? p.sid[(size_t)row * p.K + s_last] : p.V - 1;
   __syncthreads();
   if (j < p.M) {
-    const int32_t tok = j < a ? p.drafts[(int64_t)seq * (p.M - 1) + j] : (j == a ? s_pick : -1);
+    const int32_t tok = j < a ? dj : (j == a ? s_pick : -1);
     p.tokens[(int64_t)seq * p.M + j] = tok;
   }
   if (j == 0) {
@@ -1529,8 +1540,11 @@ hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t str
     hipLaunchKernelGGL(samp_count, grid, dim3(kBlock), 0, stream, p, pass);
   hipLaunchKernelGGL(samp_compact_count, grid, dim3(kBlock), 0, stream, p);
   hipLaunchKernelGGL(samp_compact_write, grid, dim3(kBlock), 0, stream, p);
-  hipLaunchKernelGGL(samp_row, dim3(rows), dim3(kRowThreads), 0, stream, p);
-  hipLaunchKernelGGL(samp_draw, dim3(c.B), dim3(kRowThreads), 0, stream, p);
+  // one thread per kept entry (a power of two, at least a wave)
+  int nt = kWave;
+  while (nt < p.K) nt <<= 1;
+  hipLaunchKernelGGL(samp_row, dim3(rows), dim3(nt), 0, stream, p);
+  hipLaunchKernelGGL(samp_draw, dim3(c.B), dim3(nt), 0, stream, p);
   return hipGetLastError();
 }
 
