@@ -350,6 +350,24 @@ def extra_moe(bv, dev, steps, warmup):
             "m1_gemv_bytes": topk * per_expert, "no_dedup_bytes": T * topk * per_expert}
 
 
+def depth_controller(bv, sweep):
+    """The draft depth the controller picks on this run's measured cost of
+    one verify pass per width (M = 1, 2, 4, 8; linear in between) plus a
+    drafter costing a tenth of the M = 1 pass per draft token, for constant
+    per-position acceptance rates."""
+    ms = sorted(int(m) for m in sweep)
+    us = [sweep[str(m)]["us_per_call"] for m in ms]
+    verify = np.interp(np.arange(1, 9), ms, us)
+    cost = verify + 0.1 * us[0] * np.arange(8)
+    out = {"cost_us_per_step": [round(float(c), 3) for c in cost],
+           "draft_us_per_token": round(0.1 * us[0], 3)}
+    for a in (0.5, 0.7, 0.9):
+        d, rate = bv.choose_draft_depth(np.full(7, a), cost)
+        out[f"accept_{a}"] = {"depth": d, "tokens_per_us": round(float(rate[d]), 4),
+                              "speedup_vs_plain": round(float(rate[d] / rate[0]), 3)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -426,6 +444,7 @@ def main():
         out["m_sweep"] = sweep
         if "1" in sweep and "8" in sweep:
             out["m8_over_m1_time"] = round(sweep["8"]["us_per_call"] / sweep["1"]["us_per_call"], 4)
+            out["depth_controller"] = depth_controller(bv, sweep)
     if extra:
         out["other_workloads"] = extra
     if not args.no_cpu and not args.only_headline:

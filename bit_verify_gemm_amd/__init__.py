@@ -19,6 +19,7 @@ __all__ = [
     "gemm_plan_info",
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
     "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
+    "choose_draft_depth", "DepthStats",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -80,6 +81,13 @@ def lib() -> ctypes.CDLL:
         L.mtp_accept_sampled.restype = i32
         L.mtp_accept_sampled.argtypes = [P, i32, i32, i32, i64, P, P, i64, P, P, i64, P, P, i32,
                                          P, P, P, P, P, P, P, P, P, sz, P]
+        D = ctypes.c_double
+        L.mtp_choose_draft_depth.restype = i32
+        L.mtp_choose_draft_depth.argtypes = [P, P, i32, P]
+        L.mtp_depth_observe.restype = i32
+        L.mtp_depth_observe.argtypes = [P, P, i32, i32, i32, D]
+        L.mtp_depth_estimate.restype = i32
+        L.mtp_depth_estimate.argtypes = [P, P, i32, P]
         _lib = L
         return L
 
@@ -318,3 +326,43 @@ def accept_sampled(logits: torch.Tensor, draft_ids: torch.Tensor | None, uniform
     if want_target:
         return tok, cnt, rb, tid, tpr
     return tok, cnt, rb
+
+
+def _host_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def choose_draft_depth(accept_prob, cost):
+    """(d, rates): the draft depth with the most expected committed tokens per
+    unit of cost (mtp_choose_draft_depth).  accept_prob [dmax], cost [dmax+1]."""
+    import numpy as np
+    c = np.ascontiguousarray(cost, dtype=np.float64)
+    dmax = len(c) - 1
+    a = np.ascontiguousarray(accept_prob, dtype=np.float64)[:dmax]
+    rate = np.zeros(dmax + 1, np.float64)
+    d = int(lib().mtp_choose_draft_depth(_host_ptr(a) if dmax else None, _host_ptr(c), dmax,
+                                         _host_ptr(rate)))
+    if d < 0:
+        raise MtpError(d, "mtp_choose_draft_depth: bad arguments")
+    return d, rate
+
+
+class DepthStats:
+    """Live per-position acceptance (mtp_depth_observe / mtp_depth_estimate)."""
+
+    def __init__(self, dmax: int, keep: float = 1.0):
+        import numpy as np
+        self.dmax, self.keep = int(dmax), float(keep)
+        self.reached = np.zeros(self.dmax, np.float64)
+        self.accepted = np.zeros(self.dmax, np.float64)
+
+    def observe(self, depth: int, n_accepted: int):
+        _check(lib().mtp_depth_observe(_host_ptr(self.reached), _host_ptr(self.accepted),
+                                       self.dmax, int(depth), int(n_accepted), self.keep))
+
+    def estimate(self):
+        import numpy as np
+        prob = np.zeros(self.dmax, np.float64)
+        _check(lib().mtp_depth_estimate(_host_ptr(self.reached), _host_ptr(self.accepted),
+                                        self.dmax, _host_ptr(prob)))
+        return prob

@@ -315,6 +315,35 @@ int mtp_accept_sampled(const float *logits, int B, int M, int V, int64_t ldl,
  * neutral value (the penalised rows then take a workspace copy). */
 size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties);
 
+/*
+ * Draft-depth controller (host functions; no GPU work).  Ollama mtp.go
+ * commit log: the depth drafted is the one that maximises committed tokens
+ * per wall-clock, from live per-position acceptance and the measured forward
+ * cost per width, with no depth cap; MTPLX blog post: plain decoding stays
+ * the baseline.  A step of depth d verifies M = d + 1 rows and commits
+ * E(d) = 1 + sum_{i=1..d} prod_{j<=i} accept_prob[j-1] tokens in
+ * expectation.
+ *
+ * mtp_choose_draft_depth: returns the d in [0, dmax] with the largest
+ *   E(d) / cost[d] (the smallest d on a tie; d = 0 is plain decoding) and
+ *   writes E(d) / cost[d] to rate[0..dmax] if rate is not NULL.
+ *   accept_prob [dmax] in [0, 1]; cost [dmax + 1] > 0 (e.g. microseconds of
+ *   the verify pass at M = d + 1 plus drafting d tokens); dmax in [0, 63].
+ *   Errors: MTP_ERR_NULL, MTP_ERR_SHAPE (dmax), MTP_ERR_VALUE (a cost <= 0
+ *   or NaN, a probability outside [0, 1]).
+ * mtp_depth_observe: after a step of depth `depth` that accepted n_accepted
+ *   drafts, positions 1..min(n_accepted + 1, depth) were reached and
+ *   1..n_accepted accepted; reached[] and accepted[] (length dmax, caller
+ *   owned, start at 0) are multiplied by keep in [0, 1] (1: plain counts),
+ *   then counted.
+ * mtp_depth_estimate: prob[i] = (accepted[i] + 1) / (reached[i] + 2)
+ *   (Laplace's rule: 1/2 before any evidence).
+ */
+int mtp_choose_draft_depth(const double *accept_prob, const double *cost, int dmax, double *rate);
+int mtp_depth_observe(double *reached, double *accepted, int dmax, int depth, int n_accepted,
+                      double keep);
+int mtp_depth_estimate(const double *reached, const double *accepted, int dmax, double *prob);
+
 /* Thread-local message for the last non-zero status of this thread. */
 const char *mtp_last_error(void);
 

@@ -77,6 +77,13 @@ def _load():
         lib.orc_accept_sampled.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, i64, P, P,
                                            i64, P, P, i64, P, P, ctypes.c_int, P, P, P, P, P, P,
                                            P, P]
+        lib.orc_choose_draft_depth.restype = ctypes.c_int
+        lib.orc_choose_draft_depth.argtypes = [P, P, ctypes.c_int, P]
+        lib.orc_depth_observe.restype = None
+        lib.orc_depth_observe.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_double]
+        lib.orc_depth_estimate.restype = None
+        lib.orc_depth_estimate.argtypes = [P, P, ctypes.c_int, P]
         lib.orc_accept_rejection.restype = ctypes.c_int
         lib.orc_accept_rejection.argtypes = [P, ctypes.c_int, ctypes.c_int, i64, P, i64, P, P,
                                              f32, f32, i64, P, P, P, P]
@@ -316,3 +323,29 @@ def accept_sampled(logits: np.ndarray, drafts: np.ndarray, u: np.ndarray, params
     if with_margins:
         out.append(margins)
     return tuple(out)
+
+
+def choose_draft_depth(accept_prob, cost):
+    """(d, rates): the depth maximising E(d) / cost[d] (see oracle.c)."""
+    lib = _load()
+    a = np.ascontiguousarray(accept_prob, dtype=np.float64)
+    c = np.ascontiguousarray(cost, dtype=np.float64)
+    dmax = len(c) - 1
+    assert len(a) >= dmax
+    rate = np.zeros(dmax + 1, np.float64)
+    d = lib.orc_choose_draft_depth(_ptr(a if len(a) else np.zeros(1)), _ptr(c), dmax, _ptr(rate))
+    if d < 0:
+        raise ValueError("orc_choose_draft_depth rejected its arguments")
+    return int(d), rate
+
+
+def depth_observe(reached, accepted, d, a, keep=1.0):
+    lib = _load()
+    lib.orc_depth_observe(_ptr(reached), _ptr(accepted), len(reached), int(d), int(a), float(keep))
+
+
+def depth_estimate(reached, accepted):
+    lib = _load()
+    prob = np.zeros(len(reached), np.float64)
+    lib.orc_depth_estimate(_ptr(reached), _ptr(accepted), len(reached), _ptr(prob))
+    return prob

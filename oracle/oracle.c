@@ -789,3 +789,67 @@ int orc_accept_sampled(int B, int M, int V, const float *logits, int64_t ldl,
     free(zp); free(p); free(r); free(keys); free(window);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* draft-depth controller                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Ollama mtp.go commit log (the controller that replaced the heuristic
+ * schedule): draft the depth that maximises committed tokens per unit of
+ * wall-clock, from live per-position acceptance and the measured forward
+ * cost per width, with no cap on the depth; MTPLX blog post, "Why it is
+ * interesting on a Mac specifically": plain decoding stays the baseline.
+ *
+ * With a_i the probability that draft i (1-based) is accepted given drafts
+ * 1..i-1 were, a step of depth d commits E(d) = 1 + sum_{i=1..d} prod_{j<=i}
+ * a_j tokens in expectation (the accepted run plus the correction or bonus
+ * token) and costs cost[d] (the verify pass at M = d + 1 rows, plus drafting
+ * d tokens); the chosen depth maximises E(d) / cost[d], the smallest d on a
+ * tie, d = 0 (plain decoding, one token per step) included.
+ */
+int orc_choose_draft_depth(const double *accept_prob, const double *cost, int dmax,
+                           double *rate) {
+    if (dmax < 0 || dmax > 63) return -1;
+    for (int d = 0; d <= dmax; ++d)
+        if (!(cost[d] > 0.0)) return -1;
+    for (int i = 0; i < dmax; ++i)
+        if (!(accept_prob[i] >= 0.0 && accept_prob[i] <= 1.0)) return -1;
+    int best = 0;
+    double best_rate = 0.0;
+    for (int d = 0; d <= dmax; ++d) {
+        double e = 1.0;
+        for (int i = 1; i <= d; ++i) {
+            double prod = 1.0;
+            for (int j = 1; j <= i; ++j) prod *= accept_prob[j - 1];
+            e += prod;
+        }
+        double r = e / cost[d];
+        if (rate) rate[d] = r;
+        if (d == 0 || r > best_rate) {
+            best = d;
+            best_rate = r;
+        }
+    }
+    return best;
+}
+
+/*
+ * Live per-position acceptance: after a step of depth d that accepted a
+ * drafts, positions i = 1..min(a + 1, d) were reached and positions 1..a
+ * accepted; counts decay by `keep` per step (1 = plain counts).  The estimate
+ * a_i = (accepted_i + 1) / (reached_i + 2) (Laplace's rule, 1/2 before any
+ * evidence).
+ */
+void orc_depth_observe(double *reached, double *accepted, int dmax, int d, int a, double keep) {
+    for (int i = 1; i <= dmax; ++i) {
+        reached[i - 1] *= keep;
+        accepted[i - 1] *= keep;
+        if (i <= d && i <= a + 1) reached[i - 1] += 1.0;
+        if (i <= d && i <= a) accepted[i - 1] += 1.0;
+    }
+}
+
+void orc_depth_estimate(const double *reached, const double *accepted, int dmax, double *prob) {
+    for (int i = 0; i < dmax; ++i) prob[i] = (accepted[i] + 1.0) / (reached[i] + 2.0);
+}
