@@ -12,7 +12,9 @@ steps of the verify pass at their own workloads:
 * the 5376 -> 262144 LM head (M = 8) and the greedy, rejection and sampled
   (full sampler pipeline, sparse top-k) accept steps on its logits,
 * the routed MoE pass (8 tokens, 128 experts, top-8, 2048 -> 768 -> 2048),
-  with its unique-expert bytes.
+  with its unique-expert bytes,
+* multi-row verify attention: 8 rows over a 32768-key prefix (32 query heads
+  on 8 KV heads of dim 128), with the KV bytes it reads.
 
 Method:
 * weights are packed once (mtp_pack_weights, outside the timed region);
@@ -350,6 +352,38 @@ def extra_moe(bv, dev, steps, warmup):
             "m1_gemv_bytes": topk * per_expert, "no_dedup_bytes": T * topk * per_expert}
 
 
+def extra_verify_attention(bv, dev, steps, warmup):
+    """Causal attention of 8 verify rows over a 32768-key prefix: 32 query
+    heads on 8 KV heads of dim 128 (bf16), each KV head read once for all
+    8 x 4 query rows; rotating copies of the cache (>= 1 GiB)."""
+    M, Hq, Hkv, D, L = 8, 32, 8, 128, 32768 - 8
+    rng = np.random.default_rng(31)
+    q = dev_bits(W.to_bf16_bits(rng.standard_normal((M, Hq, D)).astype(np.float32)), dev)
+    kv_bytes = 2 * Hkv * (L + M) * D * 2
+    R = max(2, -(-ROTATE_BYTES // kv_bytes))
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    caches = []
+    for _ in range(R):
+        k = torch.randn((Hkv, L + M, D), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((Hkv, L + M, D), generator=g, device=dev).to(torch.bfloat16)
+        caches.append((k.view(torch.int16), v.view(torch.int16)))
+    out = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(bv.attention_workspace_bytes(M, Hq, Hkv, D, L), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        k, v = caches[i % R]
+        bv.verify_attention(q, k, v, L, out=out, ws=ws)
+
+    _, ms, _ = time_graph(call, R, max(64, steps // 8), max(16, warmup // 8))
+    res = {"M": M, "Hq": Hq, "Hkv": Hkv, "D": D, "keys": L + M, "kv_bytes": kv_bytes,
+           "us": round(ms * 1e3, 3), "gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}
+    res["frac_of_hbm_peak"] = round(res["gbs"] / PEAK_HBM_GBS, 4)
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
 def depth_controller(bv, sweep):
     """The draft depth the controller picks on this run's measured cost of
     one verify pass per width (M = 1, 2, 4, 8; linear in between) plus a
@@ -413,6 +447,7 @@ def main():
         extra["lm_head_5376x262144_m8"] = extra_lm_head_and_accept(bv, dev, args.steps,
                                                                    args.warmup)
         extra["moe_8tok_128x_top8"] = extra_moe(bv, dev, args.steps, args.warmup)
+        extra["verify_attention_32k"] = extra_verify_attention(bv, dev, args.steps, args.warmup)
 
     if args.copy_calibration:
         copy_calibration(dev)

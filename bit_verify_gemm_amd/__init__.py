@@ -19,7 +19,7 @@ __all__ = [
     "gemm_plan_info",
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
     "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
-    "choose_draft_depth", "DepthStats",
+    "choose_draft_depth", "DepthStats", "verify_attention", "attention_workspace_bytes",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.mtp_accept_sampled.restype = i32
         L.mtp_accept_sampled.argtypes = [P, i32, i32, i32, i64, P, P, i64, P, P, i64, P, P, i32,
                                          P, P, P, P, P, P, P, P, P, sz, P]
+        L.mtp_verify_attention_workspace_bytes.restype = sz
+        L.mtp_verify_attention_workspace_bytes.argtypes = [i32] * 5
+        L.mtp_verify_attention.restype = i32
+        L.mtp_verify_attention.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, f32, P, P, sz, P]
         D = ctypes.c_double
         L.mtp_choose_draft_depth.restype = i32
         L.mtp_choose_draft_depth.argtypes = [P, P, i32, P]
@@ -366,3 +370,28 @@ class DepthStats:
         _check(lib().mtp_depth_estimate(_host_ptr(self.reached), _host_ptr(self.accepted),
                                         self.dmax, _host_ptr(prob)))
         return prob
+
+
+def attention_workspace_bytes(M: int, Hq: int, Hkv: int, D: int, L: int) -> int:
+    return int(lib().mtp_verify_attention_workspace_bytes(M, Hq, Hkv, D, L))
+
+
+def verify_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, L: int,
+                     scale: float | None = None, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal attention of the M verify rows q [M][Hq][D] (bf16) over the
+    cache k_cache / v_cache [Hkv][ldk][D] (bf16; positions 0 .. L+M-1 hold
+    keys, the verify tokens' own at L ..).  Returns out [M][Hq][D] fp32."""
+    M, Hq, D = q.shape
+    Hkv, ldk, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((M, Hq, D), dtype=torch.float32, device=q.device)
+    need = attention_workspace_bytes(M, Hq, Hkv, D, L)
+    if ws is None or _nbytes(ws) < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().mtp_verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), ldk, M, Hq, Hkv, D,
+                                      int(L), float(scale), _ptr(out), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)))
+    return out

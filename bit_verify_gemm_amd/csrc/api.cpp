@@ -231,6 +231,48 @@ int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
                     who);
 }
 
+static int check_attention(const char *who, int M, int Hq, int Hkv, int D, int L) {
+  if (M < 1 || M > 16) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, 16]", who, M);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(MTP_ERR_SHAPE, "%s: head dim %d is not 64, 128 or 256", who, D);
+  if (Hkv < 1 || Hq < Hkv || Hq % Hkv)
+    return fail(MTP_ERR_SHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", who, Hq, Hkv);
+  if ((int64_t)M * (Hq / Hkv) > 128)
+    return fail(MTP_ERR_SHAPE, "%s: M * Hq / Hkv = %lld query rows per KV head above 128", who,
+                (long long)M * (Hq / Hkv));
+  if (L < 0 || (int64_t)(L + M) * D * 2 >= ((int64_t)1 << 31))
+    return fail(MTP_ERR_SHAPE, "%s: L=%d out of range", who, L);
+  if (Hkv > 65535) return fail(MTP_ERR_SHAPE, "%s: Hkv=%d above 65535", who, Hkv);
+  return MTP_OK;
+}
+
+size_t mtp_verify_attention_workspace_bytes(int M, int Hq, int Hkv, int D, int L) {
+  if (check_attention("mtp_verify_attention_workspace_bytes", M, Hq, Hkv, D, L)) return 0;
+  return mtp::attention_ws_bytes(M, Hq, Hkv, D, L);
+}
+
+int mtp_verify_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                         int64_t ldk, int M, int Hq, int Hkv, int D, int L, float scale,
+                         float *out, void *ws, size_t ws_bytes, void *stream) {
+  const char *who = "mtp_verify_attention";
+  if (int rc = check_attention(who, M, Hq, Hkv, D, L)) return rc;
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(MTP_ERR_NULL, "%s: q, caches and out are required", who);
+  if (ldk < (int64_t)L + M)
+    return fail(MTP_ERR_SHAPE, "%s: ldk=%lld < L + M=%d", who, (long long)ldk, L + M);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(MTP_ERR_ALIGN, "%s: q, caches and out must be 16-byte aligned", who);
+  if (!(scale == scale)) return fail(MTP_ERR_VALUE, "%s: scale is NaN", who);
+  const size_t need = mtp::attention_ws_bytes(M, Hq, Hkv, D, L);
+  if (!ws || ws_bytes < need)
+    return fail(MTP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 256)) return fail(MTP_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+  return hip_status(mtp::launch_verify_attention(q, k_cache, v_cache, ldk, M, Hq, Hkv, D, L, scale,
+                                                 out, ws, static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties) {
   if (B < 1 || B > kMaxSampledSeqs || M < 1 || M > kMaxAcceptRows || V < 1 || V > kMaxVocab ||
       top_k < 1 || top_k > MTP_MAX_TOP_K)

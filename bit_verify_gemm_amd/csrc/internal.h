@@ -66,6 +66,13 @@ struct SampledCall {
 };
 
 size_t sampled_ws_bytes(int B, int M, int V, int top_k, bool penalties);
+
+// ---- multi-row verify attention ---------------------------------------------
+
+size_t attention_ws_bytes(int M, int Hq, int Hkv, int D, int L);
+hipError_t launch_verify_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   int64_t ldk, int M, int Hq, int Hkv, int D, int L, float scale,
+                                   float *out, void *ws, hipStream_t stream);
 hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t stream);
 
 hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,

@@ -316,6 +316,33 @@ int mtp_accept_sampled(const float *logits, int B, int M, int V, int64_t ldl,
 size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties);
 
 /*
+ * Multi-row verify attention over a shared KV prefix.  Qiita roofline
+ * article, §2-3: at long context the KV reads also take bandwidth, but the
+ * candidates of one verify pass look at the same prefix, so one KV read
+ * serves all of them (as with the weights).  For the M verify rows of one
+ * sequence, row i (absolute position L + i) of query head h attends
+ * causally to keys 0 .. L + i of KV head h / (Hq / Hkv):
+ *   out[i][h] = softmax_j(scale * q[i][h] . k[h/G][j]) . v[h/G][j]
+ * Each KV head's keys are read once for all M * Hq/Hkv query rows.  The M
+ * verify tokens' own K and V must already be in the cache at positions
+ * L .. L + M - 1.  Arithmetic: bf16 products with fp32 accumulation on the
+ * matrix cores, fp32 online softmax, the probabilities rounded to bf16 for
+ * the product with V (|error| <= 2^-8 * sum_j p_j |v_j| from that rounding).
+ *   q            bf16 [M][Hq][D], 16-byte aligned
+ *   k_cache,
+ *   v_cache, ldk bf16 [Hkv][ldk][D] (ldk >= L + M), 16-byte aligned
+ *   M            1..16; D 64, 128 or 256; Hq a multiple of Hkv with
+ *                M * Hq / Hkv <= 128
+ *   scale        the score scale (e.g. 1 / sqrt(D))
+ *   out          fp32 [M][Hq][D]
+ *   ws, ws_bytes at least mtp_verify_attention_workspace_bytes(...)
+ */
+int mtp_verify_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                         int64_t ldk, int M, int Hq, int Hkv, int D, int L, float scale,
+                         float *out, void *ws, size_t ws_bytes, void *stream);
+size_t mtp_verify_attention_workspace_bytes(int M, int Hq, int Hkv, int D, int L);
+
+/*
  * Draft-depth controller (host functions; no GPU work).  Ollama mtp.go
  * commit log: the depth drafted is the one that maximises committed tokens
  * per wall-clock, from live per-position acceptance and the measured forward

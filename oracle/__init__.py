@@ -77,6 +77,9 @@ def _load():
         lib.orc_accept_sampled.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, i64, P, P,
                                            i64, P, P, i64, P, P, ctypes.c_int, P, P, P, P, P, P,
                                            P, P]
+        lib.orc_verify_attention.restype = ctypes.c_int
+        lib.orc_verify_attention.argtypes = [ctypes.c_int] * 5 + [i64, P, P, P, ctypes.c_double,
+                                                                   P, P, ctypes.c_int]
         lib.orc_choose_draft_depth.restype = ctypes.c_int
         lib.orc_choose_draft_depth.argtypes = [P, P, ctypes.c_int, P]
         lib.orc_depth_observe.restype = None
@@ -349,3 +352,23 @@ def depth_estimate(reached, accepted):
     prob = np.zeros(len(reached), np.float64)
     lib.orc_depth_estimate(_ptr(reached), _ptr(accepted), len(reached), _ptr(prob))
     return prob
+
+
+def verify_attention(q, k, v, L, scale=None, nthreads=None):
+    """(out, bound): causal attention of the M verify rows (see oracle.c).
+    q uint16 (bf16 bits) [M][Hq][D]; k, v [Hkv][ldk][D]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    M, Hq, D = q.shape
+    Hkv, ldk, _ = k.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.zeros((M, Hq, D), np.float64)
+    ob = np.zeros((M, Hq, D), np.float64)
+    rc = lib.orc_verify_attention(M, Hq, Hkv, D, int(L), ldk, _ptr(q), _ptr(k), _ptr(v),
+                                  float(scale), _ptr(o), _ptr(ob), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("orc_verify_attention rejected its arguments")
+    return o, ob

@@ -853,3 +853,94 @@ void orc_depth_observe(double *reached, double *accepted, int dmax, int d, int a
 void orc_depth_estimate(const double *reached, const double *accepted, int dmax, double *prob) {
     for (int i = 0; i < dmax; ++i) prob[i] = (accepted[i] + 1.0) / (reached[i] + 2.0);
 }
+
+/* ------------------------------------------------------------------------ */
+/* multi-row verify attention over a shared KV prefix                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Qiita roofline article, §2-3: at long context the KV reads also take
+ * bandwidth, but the K candidates of a verify pass look at the same prefix,
+ * so one KV read serves all of them, as with the weights.  The oracle is the
+ * plain definition of causal attention for the M verify rows of one
+ * sequence (grouped heads: query head h reads KV head h / G):
+ *   row i sits at position L + i and sees keys 0 .. L + i (the prefix and
+ *   the verify tokens up to itself, whose K and V are already in the cache);
+ *   s_j = scale * sum_d q[i][h][d] * k[h/G][j][d]; p = softmax(s);
+ *   o[i][h][d] = sum_j p_j * v[h/G][j][d];
+ * in fp64 from the bf16 inputs.  ob[i][h][d] = sum_j p_j |v[h/G][j][d]| is
+ * the error scale of the result.
+ */
+static void *attn_worker(void *arg);
+typedef struct {
+    int M, Hq, Hkv, D, L;
+    int64_t ldk;
+    const uint16_t *q, *k, *v;
+    double scale;
+    double *o, *ob;
+    int h0, h1;
+} attn_job;
+
+static void *attn_worker(void *arg) {
+    attn_job *J = (attn_job *)arg;
+    const int G = J->Hq / J->Hkv, D = J->D;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(J->L + J->M));
+    if (!s) return NULL;
+    for (int h = J->h0; h < J->h1; ++h) {
+        const int kh = h / G;
+        const uint16_t *K = J->k + (int64_t)kh * J->ldk * D;
+        const uint16_t *V = J->v + (int64_t)kh * J->ldk * D;
+        for (int i = 0; i < J->M; ++i) {
+            const uint16_t *q = J->q + ((int64_t)i * J->Hq + h) * D;
+            const int n = J->L + i + 1;
+            double mx = -INFINITY;
+            for (int j = 0; j < n; ++j) {
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d)
+                    acc += orc_bf16(q[d]) * orc_bf16(K[(int64_t)j * D + d]);
+                s[j] = J->scale * acc;
+                if (s[j] > mx) mx = s[j];
+            }
+            double l = 0.0;
+            for (int j = 0; j < n; ++j) {
+                s[j] = exp(s[j] - mx);
+                l += s[j];
+            }
+            double *o = J->o + ((int64_t)i * J->Hq + h) * D;
+            double *ob = J->ob + ((int64_t)i * J->Hq + h) * D;
+            for (int d = 0; d < D; ++d) o[d] = ob[d] = 0.0;
+            for (int j = 0; j < n; ++j) {
+                const double p = s[j] / l;
+                for (int d = 0; d < D; ++d) {
+                    const double vv = orc_bf16(V[(int64_t)j * D + d]);
+                    o[d] += p * vv;
+                    ob[d] += p * fabs(vv);
+                }
+            }
+        }
+    }
+    free(s);
+    return NULL;
+}
+
+/* q [M][Hq][D], k and v [Hkv][ldk][D] (positions 0 .. L+M-1 hold keys),
+ * o and ob [M][Hq][D]. */
+int orc_verify_attention(int M, int Hq, int Hkv, int D, int L, int64_t ldk, const uint16_t *q,
+                         const uint16_t *k, const uint16_t *v, double scale, double *o,
+                         double *ob, int nthreads) {
+    if (M < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || D < 1 || L < 0 || ldk < (int64_t)L + M)
+        return -1;
+    tables_init();
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > Hq) nthreads = Hq;
+    pthread_t th[64];
+    attn_job jobs[64];
+    if (nthreads > 64) nthreads = 64;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (attn_job){M, Hq, Hkv, D, L, ldk, q, k, v, scale, o, ob,
+                             (int)((int64_t)Hq * t / nthreads), (int)((int64_t)Hq * (t + 1) / nthreads)};
+        pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
