@@ -209,23 +209,66 @@ __global__ __launch_bounds__(kMaxRowWaves * kWave) void vattn_partial(AttnArgs a
 }
 
 // One workgroup of D threads per (query row, KV head): merges the chunks in
-// chunk order, out = sum_c O_c e^(m_c - m) / sum_c l_c e^(m_c - m).
+// chunk order, out = sum_c O_c e^(m_c - m) / sum_c l_c e^(m_c - m).  The
+// chunk weights are computed once into LDS; each thread then sums its
+// column with eight chunks' loads in flight.
+constexpr int kMaxChunks = 512;
+
 template <int D>
 __global__ __launch_bounds__(256) void vattn_combine(AttnArgs a) {
+  __shared__ float wc[kMaxChunks];
+  __shared__ float red[256 / kWave];
+  __shared__ float s_mx, s_l;
   const int r = blockIdx.x, kh = blockIdx.y, d = threadIdx.x;
+  const int lane = d & (kWave - 1), wave = d / kWave, nw = D / kWave;
   const int R16 = (a.R + 15) / 16 * 16;
+  const size_t base = (size_t)kh * a.nch * R16 + r;   // slot of chunk c: base + c * R16
+  // row maximum over the chunks
   float mx = -__builtin_inff();
-  for (int c = 0; c < a.nch; ++c) mx = fmaxf(mx, a.ml[2 * (((size_t)kh * a.nch + c) * R16 + r)]);
-  float lsum = 0.0f, acc = 0.0f;
-  for (int c = 0; c < a.nch; ++c) {
-    const size_t slot = ((size_t)kh * a.nch + c) * R16 + r;
-    const float mc = a.ml[2 * slot];
-    const float w = mc == -__builtin_inff() ? 0.0f : __expf(mc - mx);
-    lsum += a.ml[2 * slot + 1] * w;
-    acc += a.part[slot * D + d] * w;
+  for (int c = d; c < a.nch; c += D) {
+    const float mc = a.ml[2 * (base + (size_t)c * R16)];
+    wc[c] = mc;
+    mx = fmaxf(mx, mc);
   }
+  for (int s = kWave / 2; s > 0; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  if (d == 0) {
+    float m = red[0];
+    for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+    s_mx = m;
+  }
+  __syncthreads();
+  const float m = s_mx;
+  // chunk weights and each chunk's weighted sum, then the normaliser in
+  // chunk order
+  __shared__ float lc[kMaxChunks];
+  for (int c = d; c < a.nch; c += D) {
+    const float mc = wc[c];
+    const float w = mc == -__builtin_inff() ? 0.0f : __expf(mc - m);
+    wc[c] = w;
+    lc[c] = a.ml[2 * (base + (size_t)c * R16) + 1] * w;
+  }
+  __syncthreads();
+  if (d == 0) {
+    float l = 0.0f;
+    for (int c = 0; c < a.nch; ++c) l += lc[c];
+    s_l = l;
+  }
+  float acc = 0.0f;
+  const float *col = a.part + base * D + d;
+  int c = 0;
+  for (; c + 8 <= a.nch; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = col[(size_t)(c + u) * R16 * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u] * wc[c + u];
+  }
+  for (; c < a.nch; ++c) acc += col[(size_t)c * R16 * D] * wc[c];
+  __syncthreads();
   const int qi = r / a.G, h = kh * a.G + r % a.G;
-  a.out[((int64_t)qi * a.Hq + h) * D + d] = acc / lsum;
+  a.out[((int64_t)qi * a.Hq + h) * D + d] = acc / s_l;
 }
 
 struct AttnPlan {
@@ -237,9 +280,9 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int L) {
   AttnPlan p;
   const int total = L + M, G = Hq / Hkv, R = M * G;
   p.R16 = (R + 15) / 16 * 16;
-  // about two workgroups per CU, chunks of at least 64 positions
-  int nch = (512 + Hkv - 1) / Hkv;
-  nch = std::max(1, std::min(nch, (total + 63) / 64));
+  // about four workgroups per CU, chunks of at least 64 positions
+  int nch = (1024 + Hkv - 1) / Hkv;
+  nch = std::max(1, std::min(std::min(nch, kMaxChunks), (total + 63) / 64));
   p.ch = ((total + nch - 1) / nch + kSub - 1) / kSub * kSub;
   p.nch = (total + p.ch - 1) / p.ch;
   const size_t slots = (size_t)Hkv * p.nch * p.R16;
