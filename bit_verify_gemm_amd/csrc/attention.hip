@@ -103,10 +103,16 @@ __global__ __launch_bounds__(kMaxRowWaves * kWave) void vattn_partial(AttnArgs a
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m = -__builtin_inff(), l = 0.0f;
 
-  // register staging of one step: pieces p = t, t + nt, ... of K and of V
-  // (a workgroup has at least kMinWaves waves)
+  // register staging of one step (a workgroup has at least kMinWaves
+  // waves): K in 16-byte pieces (p = t, t + nt, ...) stored as they are;
+  // V in blocks of 4 positions x 4 columns (four 8-byte loads), transposed
+  // in registers so that each column's 4 positions go to LDS in one 8-byte
+  // store
   constexpr int kPer = (kChunks + kMinWaves * kWave - 1) / (kMinWaves * kWave);
-  u32x4 kr[kPer], vr[kPer];
+  constexpr int kVBlocks = (kSub / 4) * (D / 4);
+  constexpr int kVPer = (kVBlocks + kMinWaves * kWave - 1) / (kMinWaves * kWave);
+  u32x4 kr[kPer];
+  u32x2 vr[kVPer][4];
   auto load_step = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -115,7 +121,18 @@ __global__ __launch_bounds__(kMaxRowWaves * kWave) void vattn_partial(AttnArgs a
         const int pos = base + pc / (D / 8), d0 = (pc % (D / 8)) * 8;
         const int off = pos < c1 ? (pos * D + d0) * 2 : (int)bytes;   // past the chunk: zeros
         kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kw, off, 0, 0));
-        vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vw, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int b = (int)threadIdx.x + u * nt;
+      if (b < kVBlocks) {
+        const int p0 = base + 4 * (b / (D / 4)), d0 = 4 * (b % (D / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int off = p0 + r < c1 ? ((p0 + r) * D + d0) * 2 : (int)bytes;
+          vr[u][r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vw, off, 0, 0));
+        }
       }
     }
   };
@@ -126,10 +143,28 @@ __global__ __launch_bounds__(kMaxRowWaves * kWave) void vattn_partial(AttnArgs a
       if (pc < kChunks) {
         const int p = pc / (D / 8), d0 = (pc % (D / 8)) * 8;
         *reinterpret_cast<u32x4 *>(&s.k[p * Lds<D>::kRow + d0]) = kr[u];
-        const uint32_t w[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      }
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s.vt[(d0 + e) * Lds<D>::vRow + p] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    for (int u = 0; u < kVPer; ++u) {
+      const int b = (int)threadIdx.x + u * nt;
+      if (b < kVBlocks) {
+        const int p = 4 * (b / (D / 4)), d0 = 4 * (b % (D / 4));
+        // vr[u][r] = columns d0..d0+3 of position p + r (.x: d0, d0+1; .y: d0+2, d0+3);
+        // column d0 + c takes the halves c of the four positions
+        const uint32_t lo = 0x05040100u, hi = 0x07060302u;   // low / high halves of two words
+        const u32x2 c0 = {__builtin_amdgcn_perm(vr[u][1].x, vr[u][0].x, lo),
+                          __builtin_amdgcn_perm(vr[u][3].x, vr[u][2].x, lo)};
+        const u32x2 c1v = {__builtin_amdgcn_perm(vr[u][1].x, vr[u][0].x, hi),
+                           __builtin_amdgcn_perm(vr[u][3].x, vr[u][2].x, hi)};
+        const u32x2 c2 = {__builtin_amdgcn_perm(vr[u][1].y, vr[u][0].y, lo),
+                          __builtin_amdgcn_perm(vr[u][3].y, vr[u][2].y, lo)};
+        const u32x2 c3 = {__builtin_amdgcn_perm(vr[u][1].y, vr[u][0].y, hi),
+                          __builtin_amdgcn_perm(vr[u][3].y, vr[u][2].y, hi)};
+        *reinterpret_cast<u32x2 *>(&s.vt[(d0 + 0) * Lds<D>::vRow + p]) = c0;
+        *reinterpret_cast<u32x2 *>(&s.vt[(d0 + 1) * Lds<D>::vRow + p]) = c1v;
+        *reinterpret_cast<u32x2 *>(&s.vt[(d0 + 2) * Lds<D>::vRow + p]) = c2;
+        *reinterpret_cast<u32x2 *>(&s.vt[(d0 + 3) * Lds<D>::vRow + p]) = c3;
       }
     }
   };
