@@ -243,24 +243,26 @@ __global__ __launch_bounds__(kMaxRowWaves * kWave) void vattn_partial(AttnArgs a
   }
 }
 
-// One workgroup of D threads per (query row, KV head): merges the chunks in
-// chunk order, out = sum_c O_c e^(m_c - m) / sum_c l_c e^(m_c - m).  The
-// chunk weights are computed once into LDS; each thread then sums its
-// column with eight chunks' loads in flight.
+// One workgroup of 1024 threads per (query row, KV head) merges the chunks:
+// out = sum_c O_c e^(m_c - m) / sum_c l_c e^(m_c - m).  The chunk weights
+// are computed once into LDS; 1024 / D groups of threads each add every
+// (1024/D)-th chunk of a column with eight loads in flight, and the group
+// sums are added in a fixed order.
 constexpr int kMaxChunks = 512;
 
 template <int D>
-__global__ __launch_bounds__(256) void vattn_combine(AttnArgs a) {
+__global__ __launch_bounds__(1024) void vattn_combine(AttnArgs a) {
+  constexpr int kCG = 1024 / D;   // chunk groups
   __shared__ float wc[kMaxChunks];
-  __shared__ float red[256 / kWave];
+  __shared__ float red[1024 / kWave];
   __shared__ float s_mx, s_l;
-  const int r = blockIdx.x, kh = blockIdx.y, d = threadIdx.x;
-  const int lane = d & (kWave - 1), wave = d / kWave, nw = D / kWave;
+  const int r = blockIdx.x, kh = blockIdx.y, t = threadIdx.x, d = t % D;
+  const int lane = t & (kWave - 1), wave = t / kWave, nw = 1024 / kWave;
   const int R16 = (a.R + 15) / 16 * 16;
   const size_t base = (size_t)kh * a.nch * R16 + r;   // slot of chunk c: base + c * R16
   // row maximum over the chunks
   float mx = -__builtin_inff();
-  for (int c = d; c < a.nch; c += D) {
+  for (int c = t; c < a.nch; c += 1024) {
     const float mc = a.ml[2 * (base + (size_t)c * R16)];
     wc[c] = mc;
     mx = fmaxf(mx, mc);
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(256) void vattn_combine(AttnArgs a) {
   for (int s = kWave / 2; s > 0; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  if (d == 0) {
+  if (t == 0) {
     float m = red[0];
     for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
     s_mx = m;
@@ -278,30 +280,38 @@ __global__ __launch_bounds__(256) void vattn_combine(AttnArgs a) {
   // chunk weights and each chunk's weighted sum, then the normaliser in
   // chunk order
   __shared__ float lc[kMaxChunks];
-  for (int c = d; c < a.nch; c += D) {
+  for (int c = t; c < a.nch; c += 1024) {
     const float mc = wc[c];
     const float w = mc == -__builtin_inff() ? 0.0f : __expf(mc - m);
     wc[c] = w;
     lc[c] = a.ml[2 * (base + (size_t)c * R16) + 1] * w;
   }
   __syncthreads();
-  if (d == 0) {
+  if (t == 0) {
     float l = 0.0f;
     for (int c = 0; c < a.nch; ++c) l += lc[c];
     s_l = l;
   }
+  // thread (cg, d) adds chunks cg, cg + kCG, ... of column d (eight loads in
+  // flight), then the kCG sums are added in cg order
+  const int cg = threadIdx.x / D;
   float acc = 0.0f;
   const float *col = a.part + base * D + d;
-  int c = 0;
-  for (; c + 8 <= a.nch; c += 8) {
+  int c = cg;
+  for (; c + 7 * kCG < a.nch; c += 8 * kCG) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = col[(size_t)(c + u) * R16 * D];
+    for (int u = 0; u < 8; ++u) v[u] = col[(size_t)(c + u * kCG) * R16 * D];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u] * wc[c + u];
+    for (int u = 0; u < 8; ++u) acc += v[u] * wc[c + u * kCG];
   }
-  for (; c < a.nch; ++c) acc += col[(size_t)c * R16 * D] * wc[c];
+  for (; c < a.nch; c += kCG) acc += col[(size_t)c * R16 * D] * wc[c];
+  __shared__ float part_sum[kCG][D];
+  part_sum[cg][d] = acc;
   __syncthreads();
+  if (cg != 0) return;
+  acc = part_sum[0][d];
+  for (int k = 1; k < kCG; ++k) acc += part_sum[k][d];
   const int qi = r / a.G, h = kh * a.G + r % a.G;
   a.out[((int64_t)qi * a.Hq + h) * D + d] = acc / s_l;
 }
@@ -350,15 +360,15 @@ hipError_t launch_verify_attention(const uint16_t *q, const uint16_t *k, const u
   switch (D) {
     case 64:
       hipLaunchKernelGGL(vattn_partial<64>, grid, block, 0, stream, a);
-      hipLaunchKernelGGL(vattn_combine<64>, cgrid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(vattn_combine<64>, cgrid, dim3(1024), 0, stream, a);
       break;
     case 128:
       hipLaunchKernelGGL(vattn_partial<128>, grid, block, 0, stream, a);
-      hipLaunchKernelGGL(vattn_combine<128>, cgrid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL(vattn_combine<128>, cgrid, dim3(1024), 0, stream, a);
       break;
     default:
       hipLaunchKernelGGL(vattn_partial<256>, grid, block, 0, stream, a);
-      hipLaunchKernelGGL(vattn_combine<256>, cgrid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(vattn_combine<256>, cgrid, dim3(1024), 0, stream, a);
       break;
   }
   return hipGetLastError();
