@@ -52,6 +52,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        lib.orc_kv_write.restype = None
+        lib.orc_kv_write.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, i64, P, i64, ctypes.c_int]
         lib.orc_e2m1.restype = ctypes.c_double
         lib.orc_e2m1.argtypes = [ctypes.c_uint32]
         lib.orc_e4m3.restype = ctypes.c_double
@@ -372,3 +374,33 @@ def verify_attention(q, k, v, L, scale=None, nthreads=None):
     if rc != 0:
         raise ValueError("orc_verify_attention rejected its arguments")
     return o, ob
+
+
+def kv_commit(cache: np.ndarray, new_rows: np.ndarray, base, rollback, ring: int) -> np.ndarray:
+    """The cache after a verify write of M rows at base[b] committed to
+    rollback[b] (Ollama mtp.go commit log, snapshot rework): a copy of
+    ``cache`` [NL][B][Hkv][cap][D] (uint16 bf16 bits) that received only the
+    first rollback[b] - base[b] rows of ``new_rows`` [NL][B][M][Hkv][D].
+    ``rollback`` is clamped into [base, base + M] as the library does."""
+    out = np.array(cache, dtype=np.uint16, copy=True, order="C")
+    NL, B, Hkv, cap, D = out.shape
+    rows = np.ascontiguousarray(new_rows, dtype=np.uint16)
+    M = rows.shape[2]
+    lib = _load()
+    for b in range(B):
+        n = int(min(max(int(rollback[b]) - int(base[b]), 0), M))
+        for l in range(NL):
+            for h in range(Hkv):
+                head = out[l, b, h]
+                src = np.ascontiguousarray(rows[l, b, :, h, :])
+                lib.orc_kv_write(_ptr(head), cap, D, ring, int(base[b]), _ptr(src), D, n)
+    return out
+
+
+def kv_live_rows(cap: int, ring: int, length: int) -> dict:
+    """Row -> position of every live position of a cache holding positions
+    0 .. length-1: all of them for a linear cache, the last cap for a
+    rotating one."""
+    lo = max(0, length - cap) if ring else 0
+    hi = length if ring else min(length, cap)
+    return {(p % cap if ring else p): p for p in range(lo, hi)}

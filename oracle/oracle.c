@@ -29,6 +29,10 @@
  *     gives a point mass, so rejection acceptance reduces to argmax match).
  *   - Ollama news item, fifth paragraph: a rollback point before each
  *     proposal; a rejection rewinds to the last accepted token.
+ *   - Ollama mtp.go commit log, the snapshot rework: the runner commits a
+ *     verify batch by restoring the caches to the accepted count.  The
+ *     oracle is what that restore must produce: the cache as if only the
+ *     accepted rows had ever been written (orc_kv_write of those rows).
  *
  * Element formats (the pages only name "nvfp4" and "Q4"; the readings used):
  *   E2M1 nibble: bit3 sign, bits2..1 exponent (bias 1), bit0 mantissa.
@@ -943,4 +947,34 @@ int orc_verify_attention(int M, int Hq, int Hkv, int D, int L, int64_t ldk, cons
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV-cache commit                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Ollama mtp.go commit log, the snapshot rework: restoring a cache to the
+ * accepted count must leave it as if the rejected rows had never been
+ * written.  The plain definition of a write: position p of one head goes to
+ * row p of a linear cache (ring = 0; positions at or past cap are not
+ * stored) or row p mod cap of a rotating one (ring = 1), replacing what was
+ * there.  Writing n rows of D elements, rows[m * ld + d], one position at a
+ * time from base upwards.  Called with n = accepted count on a copy of the
+ * cache taken before the verify write, it gives the committed cache.
+ */
+void orc_kv_write(uint16_t *cache, int64_t cap, int D, int ring, int64_t base,
+                  const uint16_t *rows, int64_t ld, int n) {
+  for (int m = 0; m < n; m++) {
+    int64_t p = base + m;
+    if (p < 0) continue;
+    int64_t row;
+    if (ring) {
+      row = p % cap;
+    } else {
+      if (p >= cap) continue;
+      row = p;
+    }
+    for (int d = 0; d < D; d++) cache[row * D + d] = rows[(int64_t)m * ld + d];
+  }
 }
