@@ -384,6 +384,47 @@ def extra_verify_attention(bv, dev, steps, warmup):
     return res
 
 
+def extra_kv_rollback(bv, dev, steps, warmup):
+    """Verify-step cache writes and the commit of a rotating-cache stack:
+    52 sliding-window layers (a 1024-key window on a 1031-row ring), 16 KV
+    heads of dim 128, 8 verify rows written past the wrap (every write
+    destroys a live row, so every one is copied out).  append: one layer's
+    write, as the forward issues it per layer; restore: one call over all 52
+    layers with every draft rejected (7 of 8 rows given back per head)."""
+    NL, Hkv, D, M, cap = 52, 16, 128, 8, 1031
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    kc = torch.randint(-32768, 32767, (NL, 1, Hkv, cap, D), generator=g, dtype=torch.int16,
+                       device=dev)
+    vc = torch.randint_like(kc, -32768, 32767)
+    kn = torch.randint(-32768, 32767, (NL, 1, M, Hkv * D), generator=g, dtype=torch.int16,
+                       device=dev)
+    vn = torch.randint_like(kn, -32768, 32767)
+    snap = bv.kv_snapshot(kc, M)
+    base = torch.tensor([5000], dtype=torch.int64, device=dev)
+    roll = torch.tensor([5001], dtype=torch.int64, device=dev)
+    layer_snap = [(snap[0][i:i + 1], snap[1][i:i + 1]) for i in range(NL)]
+
+    def append(i):
+        bv.kv_append(kc[i:i + 1], vc[i:i + 1], kn[i:i + 1], vn[i:i + 1], base, True, layer_snap[i])
+
+    def restore(i):
+        bv.kv_restore(kc, vc, M, base, roll, True, snap)
+
+    _, ms_a, _ = time_graph(append, NL, max(NL, steps // 4), max(NL, warmup // 4))
+    _, ms_r, _ = time_graph(restore, 8, max(64, steps // 16), max(16, warmup // 16))
+    row = D * 2
+    a_bytes = 2 * Hkv * M * row * 4          # read new + old, write snapshot + cache, K and V
+    r_bytes = NL * 2 * Hkv * (M - 1) * row * 2
+    res = {"layers": NL, "Hkv": Hkv, "D": D, "M": M, "ring_rows": cap,
+           "append_us_per_layer": round(ms_a * 1e3, 3), "append_bytes": a_bytes,
+           "restore_us": round(ms_r * 1e3, 3), "restore_bytes": r_bytes,
+           "restore_gbs": round(r_bytes / (ms_r * 1e-3) / 1e9, 1)}
+    del kc, vc, kn, vn, snap, layer_snap
+    torch.cuda.empty_cache()
+    return res
+
+
 def depth_controller(bv, sweep):
     """The draft depth the controller picks on this run's measured cost of
     one verify pass per width (M = 1, 2, 4, 8; linear in between) plus a
@@ -448,6 +489,7 @@ def main():
                                                                    args.warmup)
         extra["moe_8tok_128x_top8"] = extra_moe(bv, dev, args.steps, args.warmup)
         extra["verify_attention_32k"] = extra_verify_attention(bv, dev, args.steps, args.warmup)
+        extra["kv_rollback_52x16x128"] = extra_kv_rollback(bv, dev, args.steps, args.warmup)
 
     if args.copy_calibration:
         copy_calibration(dev)

@@ -20,6 +20,7 @@ __all__ = [
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
     "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
     "choose_draft_depth", "DepthStats", "verify_attention", "attention_workspace_bytes",
+    "kv_snapshot", "kv_append", "kv_restore",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -85,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.mtp_verify_attention_workspace_bytes.argtypes = [i32] * 5
         L.mtp_verify_attention.restype = i32
         L.mtp_verify_attention.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, f32, P, P, sz, P]
+        L.mtp_kv_append.restype = i32
+        L.mtp_kv_append.argtypes = [P, P, i32, i32, i32, i64, i32, i32, P, P, i64, i32, P, P, P,
+                                    P, P]
+        L.mtp_kv_restore.restype = i32
+        L.mtp_kv_restore.argtypes = [P, P, i32, i32, i32, i64, i32, i32, i32, P, P, P, P, P, P]
         D = ctypes.c_double
         L.mtp_choose_draft_depth.restype = i32
         L.mtp_choose_draft_depth.argtypes = [P, P, i32, P]
@@ -374,6 +380,46 @@ class DepthStats:
 
 def attention_workspace_bytes(M: int, Hq: int, Hkv: int, D: int, L: int) -> int:
     return int(lib().mtp_verify_attention_workspace_bytes(M, Hq, Hkv, D, L))
+
+
+def kv_snapshot(k_cache: torch.Tensor, M: int):
+    """Snapshot buffers (K, V) [NL][B][Hkv][M][D] for a rotating cache
+    k_cache [NL][B][Hkv][cap][D]; only rows a verify write destroys are
+    ever written into them."""
+    NL, B, Hkv, _, D = k_cache.shape
+    return (torch.empty((NL, B, Hkv, M, D), dtype=k_cache.dtype, device=k_cache.device),
+            torch.empty((NL, B, Hkv, M, D), dtype=k_cache.dtype, device=k_cache.device))
+
+
+def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, base_len: torch.Tensor, ring: bool, snapshot=None,
+              err: torch.Tensor | None = None, stream=None):
+    """Write the M verify rows k_new / v_new ([NL][B][M] rows of Hkv * D bf16,
+    rows ld_new = k_new.stride(2) elements apart) into k_cache / v_cache
+    [NL][B][Hkv][cap][D] at positions base_len[b] .. (device int64 [B]),
+    copying out of a rotating cache only the rows that the write destroys."""
+    NL, B, Hkv, cap, D = k_cache.shape
+    M = k_new.shape[2]
+    ld = int(k_new.stride(2))
+    if k_new.stride(1) != M * ld or k_new.stride(0) != B * M * ld or v_new.stride() != k_new.stride():
+        raise ValueError("k_new and v_new must be [NL][B][M] rows ld_new apart")
+    sk, sv = snapshot if snapshot is not None else (None, None)
+    _check(lib().mtp_kv_append(_ptr(k_cache), _ptr(v_cache), NL, B, Hkv, cap, D, int(bool(ring)),
+                               _ptr(k_new), _ptr(v_new), ld, M, _ptr(base_len), _ptr(sk),
+                               _ptr(sv), _ptr(err), _stream(stream)))
+
+
+def kv_restore(k_cache: torch.Tensor, v_cache: torch.Tensor, M: int, base_len: torch.Tensor,
+               rollback: torch.Tensor, ring: bool, snapshot=None,
+               err: torch.Tensor | None = None, stream=None):
+    """Commit the last kv_append to rollback[b] (device int64 [B], e.g. an
+    accept call's out_rollback): a rotating cache gets back the rows that
+    the dropped positions overwrote; a linear cache needs no work."""
+    NL, B, Hkv, cap, D = k_cache.shape
+    sk, sv = snapshot if snapshot is not None else (None, None)
+    _check(lib().mtp_kv_restore(_ptr(k_cache), _ptr(v_cache), NL, B, Hkv, cap, D,
+                                int(bool(ring)), int(M), _ptr(base_len), _ptr(rollback),
+                                _ptr(sk), _ptr(sv), _ptr(err), _stream(stream)))
 
 
 def verify_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, L: int,

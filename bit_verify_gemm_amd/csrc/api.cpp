@@ -273,6 +273,58 @@ int mtp_verify_attention(const uint16_t *q, const uint16_t *k_cache, const uint1
                     who);
 }
 
+static int check_kv(const char *who, const void *k, const void *v, int NL, int B, int Hkv,
+                    int64_t cap, int D, int ring, int M, const int64_t *base, const void *sk,
+                    const void *sv) {
+  if (NL < 1 || B < 1 || Hkv < 1 || (int64_t)NL * B * Hkv > ((int64_t)1 << 24))
+    return fail(MTP_ERR_SHAPE, "%s: NL=%d, B=%d, Hkv=%d (each >= 1, product <= 2^24)", who, NL, B,
+                Hkv);
+  if (D < 8 || D > 512 || D % 8) return fail(MTP_ERR_SHAPE, "%s: D=%d (8..512, a multiple of 8)", who, D);
+  if (M < 1 || M > kMaxAcceptRows) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, %d]", who, M, kMaxAcceptRows);
+  if (cap < M) return fail(MTP_ERR_SHAPE, "%s: cap=%lld below M=%d", who, (long long)cap, M);
+  if (ring != 0 && ring != 1) return fail(MTP_ERR_VALUE, "%s: ring=%d is not 0 or 1", who, ring);
+  if (!k || !v || !base) return fail(MTP_ERR_NULL, "%s: caches and base_len are required", who);
+  if (ring && (!sk || !sv)) return fail(MTP_ERR_NULL, "%s: a rotating cache needs snapshots", who);
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(sk, 16) || !aligned(sv, 16) ||
+      !aligned(base, 8))
+    return fail(MTP_ERR_ALIGN, "%s: caches and snapshots must be 16-byte aligned", who);
+  return MTP_OK;
+}
+
+int mtp_kv_append(uint16_t *k_cache, uint16_t *v_cache, int NL, int B, int Hkv, int64_t cap,
+                  int D, int ring, const uint16_t *k_new, const uint16_t *v_new, int64_t ld_new,
+                  int M, const int64_t *base_len, uint16_t *snap_k, uint16_t *snap_v,
+                  int32_t *err, void *stream) {
+  const char *who = "mtp_kv_append";
+  if (int rc = check_kv(who, k_cache, v_cache, NL, B, Hkv, cap, D, ring, M, base_len, snap_k, snap_v))
+    return rc;
+  if (!k_new || !v_new) return fail(MTP_ERR_NULL, "%s: k_new and v_new are required", who);
+  if (ld_new < (int64_t)Hkv * D || ld_new % 8)
+    return fail(MTP_ERR_SHAPE, "%s: ld_new=%lld (>= Hkv * D = %d, a multiple of 8)", who,
+                (long long)ld_new, Hkv * D);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(MTP_ERR_ALIGN, "%s: k_new and v_new must be 16-byte aligned", who);
+  return hip_status(mtp::launch_kv_append(k_cache, v_cache, NL, B, Hkv, cap, D, ring, k_new, v_new,
+                                          ld_new, M, base_len, snap_k, snap_v, err,
+                                          static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+int mtp_kv_restore(uint16_t *k_cache, uint16_t *v_cache, int NL, int B, int Hkv, int64_t cap,
+                   int D, int ring, int M, const int64_t *base_len, const int64_t *rollback,
+                   const uint16_t *snap_k, const uint16_t *snap_v, int32_t *err, void *stream) {
+  const char *who = "mtp_kv_restore";
+  if (int rc = check_kv(who, k_cache, v_cache, NL, B, Hkv, cap, D, ring, M, base_len, snap_k, snap_v))
+    return rc;
+  if (!rollback) return fail(MTP_ERR_NULL, "%s: rollback is required", who);
+  if (!aligned(rollback, 8)) return fail(MTP_ERR_ALIGN, "%s: rollback must be 8-byte aligned", who);
+  if (rollback == base_len) return fail(MTP_ERR_VALUE, "%s: rollback aliases base_len", who);
+  return hip_status(mtp::launch_kv_restore(k_cache, v_cache, NL, B, Hkv, cap, D, ring, M, base_len,
+                                           rollback, snap_k, snap_v, err,
+                                           static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties) {
   if (B < 1 || B > kMaxSampledSeqs || M < 1 || M > kMaxAcceptRows || V < 1 || V > kMaxVocab ||
       top_k < 1 || top_k > MTP_MAX_TOP_K)

@@ -85,6 +85,17 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
                                    int64_t base_len, int32_t *tokens, int32_t *counts,
                                    int64_t *rollback, void *ws, hipStream_t stream);
 
+// ---- KV-cache rollback ------------------------------------------------------
+
+hipError_t launch_kv_append(uint16_t *k, uint16_t *v, int NL, int B, int Hkv, int64_t cap, int D,
+                            int ring, const uint16_t *kn, const uint16_t *vn, int64_t ld_new,
+                            int M, const int64_t *base, uint16_t *sk, uint16_t *sv, int32_t *err,
+                            hipStream_t stream);
+hipError_t launch_kv_restore(uint16_t *k, uint16_t *v, int NL, int B, int Hkv, int64_t cap, int D,
+                             int ring, int M, const int64_t *base, const int64_t *roll,
+                             const uint16_t *sk, const uint16_t *sv, int32_t *err,
+                             hipStream_t stream);
+
 // ---- MoE -------------------------------------------------------------------
 
 size_t moe_ws_bytes(int T, int H, int F, int E, int topk);

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 3
+#define MTP_ABI_VERSION 4
 
 enum {
   MTP_OK = 0,
@@ -341,6 +341,58 @@ int mtp_verify_attention(const uint16_t *q, const uint16_t *k_cache, const uint1
                          int64_t ldk, int M, int Hq, int Hkv, int D, int L, float scale,
                          float *out, void *ws, size_t ws_bytes, void *stream);
 size_t mtp_verify_attention_workspace_bytes(int M, int Hq, int Hkv, int D, int L);
+
+/*
+ * KV-cache rollback with lazy snapshots.  Ollama mtp.go commit log, the
+ * snapshot rework: a cache snapshots itself as a verify write crosses each
+ * offset and the runner commits a batch by restoring to the accepted count;
+ * a KV or rotating capture points into the live buffer and holds no copy of
+ * its own until a destructive write forces one, so rejecting costs nothing.
+ * Ollama news item, fifth paragraph: the restore point is the rollback index
+ * that the accept calls emit (out_rollback = base_len + a + 1).
+ *
+ * Layout.  One call covers NL layers of the same shape: a cache is
+ *   k_cache, v_cache  bf16 [NL][B][Hkv][cap][D] (contiguous, 16-byte aligned)
+ * for B sequences.  A LINEAR cache (ring = 0) keeps position p in row p and
+ * must have room for it (p < cap).  A ROTATING cache (ring = 1) keeps
+ * position p in row p mod cap; writing p >= cap destroys position p - cap,
+ * which is the one write that takes a copy.  (A rotating cache that serves a
+ * sliding window of W keys to M verify rows at once needs cap >= W + M - 1.)
+ *
+ * mtp_kv_append: writes the M verify rows of every sequence b at positions
+ *   base_len[b] .. base_len[b] + M - 1.  Before a rotating-cache row that
+ *   holds a live position is overwritten, its old contents are copied to
+ *   snap_k/snap_v [NL][B][Hkv][M][D] at index m = p - base_len[b]; no other
+ *   snapshot row is touched, and a linear cache copies nothing (its snapshot
+ *   is base_len itself; snap_k and snap_v may be NULL).
+ *     k_new, v_new  bf16; row m of sequence b of layer l starts at element
+ *                   ((l * B + b) * M + m) * ld_new, and holds head h at
+ *                   h * D .. h * D + D - 1 (ld_new >= Hkv * D, a multiple
+ *                   of 8), so a fused projection's K or V columns can be
+ *                   passed in place
+ *     base_len      int64 [B] (device): the cache length before the write
+ *                   (e.g. the previous step's out_rollback)
+ * mtp_kv_restore: commits to rollback[b] (device int64 [B], clamped into
+ *   [base_len[b], base_len[b] + M]): the positions rollback[b] .. base_len[b]
+ *   + M - 1 are dropped, and every rotating-cache row they overwrote gets its
+ *   snapshot back, so the cache equals one that only ever received the first
+ *   rollback[b] - base_len[b] rows.  For a linear cache nothing is launched
+ *   and nothing is read: the new length is rollback[b] itself.  base_len, M and the snapshot must
+ *   be those of the append being undone; base_len must not alias rollback.
+ *   Run it after the append and before the next write to the same cache.
+ * err (device int32, may be NULL): set to a nonzero value (never cleared) if
+ *   a position was negative, did not fit a linear cache (that row is not
+ *   written), or a rollback lay outside its range (it is clamped).
+ * Limits: 1 <= M <= 64, M <= cap, 1 <= D <= 512 a multiple of 8,
+ *   NL * B * Hkv <= 2^24.
+ */
+int mtp_kv_append(uint16_t *k_cache, uint16_t *v_cache, int NL, int B, int Hkv, int64_t cap,
+                  int D, int ring, const uint16_t *k_new, const uint16_t *v_new, int64_t ld_new,
+                  int M, const int64_t *base_len, uint16_t *snap_k, uint16_t *snap_v,
+                  int32_t *err, void *stream);
+int mtp_kv_restore(uint16_t *k_cache, uint16_t *v_cache, int NL, int B, int Hkv, int64_t cap,
+                   int D, int ring, int M, const int64_t *base_len, const int64_t *rollback,
+                   const uint16_t *snap_k, const uint16_t *snap_v, int32_t *err, void *stream);
 
 /*
  * Draft-depth controller (host functions; no GPU work).  Ollama mtp.go

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bv.abi_version() == 3
+    assert bv.abi_version() == 4
 
 
 def test_packed_sizes():
@@ -190,3 +190,31 @@ def test_accept_sampled_rejects_bad_arguments():
                                 FAKE, None, None, FAKE, FAKE, FAKE, None, None, ws, need,
                                 None) == -1              # no params
     assert bv.lib().mtp_last_error()
+
+
+def test_kv_calls_reject_bad_arguments():
+    L = bv.lib()
+
+    def app(NL=2, B=1, Hkv=4, cap=64, D=128, ring=1, kn=FAKE, ld=512, M=8, base=FAKE, sk=FAKE,
+            k=FAKE):
+        return L.mtp_kv_append(k, FAKE, NL, B, Hkv, cap, D, ring, kn, FAKE, ld, M, base, sk, FAKE,
+                               None, None)
+
+    def res(M=8, roll=ctypes.c_void_p(0x20000), base=FAKE, ring=1, sk=FAKE, D=128):
+        return L.mtp_kv_restore(FAKE, FAKE, 2, 1, 4, 64, D, ring, M, base, roll, sk, FAKE, None,
+                                None)
+
+    assert app(NL=0) == -2
+    assert app(NL=1 << 12, B=1 << 12, Hkv=2) == -2       # more than 2^24 heads
+    assert app(D=0) == -2 and app(D=12) == -2 and app(D=520) == -2
+    assert app(M=0) == -2 and app(M=65) == -2
+    assert app(cap=7) == -2                               # cap below M
+    assert app(ring=2) == -7
+    assert app(k=None) == -1 and app(base=None) == -1 and app(kn=None) == -1
+    assert app(sk=None) == -1                             # a ring needs its snapshots
+    assert app(ld=511) == -2 and app(ld=500) == -2        # below Hkv * D, not a multiple of 8
+    assert app(kn=FAKE_ODD) == -3 and app(k=FAKE_ODD) == -3
+    assert res(roll=None) == -1
+    assert res(roll=FAKE) == -7                           # rollback aliases base_len
+    assert res(sk=None) == -1 and res(M=0) == -2 and res(D=4) == -2
+    assert "mtp_kv_restore" in bv.lib().mtp_last_error().decode()
