@@ -400,9 +400,13 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
     copying out of a rotating cache only the rows that the write destroys."""
     NL, B, Hkv, cap, D = k_cache.shape
     M = k_new.shape[2]
-    ld = int(k_new.stride(2))
-    if k_new.stride(1) != M * ld or k_new.stride(0) != B * M * ld or v_new.stride() != k_new.stride():
-        raise ValueError("k_new and v_new must be [NL][B][M] rows ld_new apart")
+    ld = int(k_new.stride(2)) if M > 1 else Hkv * D
+    for t in (k_new, v_new):
+        if (tuple(t.shape[:3]) != (NL, B, M) or t.shape[3] < Hkv * D or t.stride(3) != 1
+                or (M > 1 and t.stride(2) != ld) or (B > 1 and t.stride(1) != M * ld)
+                or (NL > 1 and t.stride(0) != B * M * ld)):
+            raise ValueError("k_new and v_new must be [NL][B][M] rows of >= Hkv * D elements, "
+                             "the rows ld_new apart with the same strides")
     sk, sv = snapshot if snapshot is not None else (None, None)
     _check(lib().mtp_kv_append(_ptr(k_cache), _ptr(v_cache), NL, B, Hkv, cap, D, int(bool(ring)),
                                _ptr(k_new), _ptr(v_new), ld, M, _ptr(base_len), _ptr(sk),

@@ -318,7 +318,8 @@ int mtp_kv_restore(uint16_t *k_cache, uint16_t *v_cache, int NL, int B, int Hkv,
     return rc;
   if (!rollback) return fail(MTP_ERR_NULL, "%s: rollback is required", who);
   if (!aligned(rollback, 8)) return fail(MTP_ERR_ALIGN, "%s: rollback must be 8-byte aligned", who);
-  if (rollback == base_len) return fail(MTP_ERR_VALUE, "%s: rollback aliases base_len", who);
+  if (rollback < base_len + B && base_len < rollback + B)
+    return fail(MTP_ERR_VALUE, "%s: rollback overlaps base_len", who);
   return hip_status(mtp::launch_kv_restore(k_cache, v_cache, NL, B, Hkv, cap, D, ring, M, base_len,
                                            rollback, snap_k, snap_v, err,
                                            static_cast<hipStream_t>(stream)),

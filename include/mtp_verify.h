@@ -378,7 +378,7 @@ size_t mtp_verify_attention_workspace_bytes(int M, int Hq, int Hkv, int D, int L
  *   snapshot back, so the cache equals one that only ever received the first
  *   rollback[b] - base_len[b] rows.  For a linear cache nothing is launched
  *   and nothing is read: the new length is rollback[b] itself.  base_len, M and the snapshot must
- *   be those of the append being undone; base_len must not alias rollback.
+ *   be those of the append being undone; base_len must not overlap rollback.
  *   Run it after the append and before the next write to the same cache.
  * err (device int32, may be NULL): set to a nonzero value (never cleared) if
  *   a position was negative, did not fit a linear cache (that row is not

@@ -216,5 +216,7 @@ def test_kv_calls_reject_bad_arguments():
     assert app(kn=FAKE_ODD) == -3 and app(k=FAKE_ODD) == -3
     assert res(roll=None) == -1
     assert res(roll=FAKE) == -7                           # rollback aliases base_len
+    assert L.mtp_kv_restore(FAKE, FAKE, 2, 3, 4, 64, 128, 1, 8, FAKE,
+                            ctypes.c_void_p(0x10000 + 16), FAKE, FAKE, None, None) == -7  # partial overlap
     assert res(sk=None) == -1 and res(M=0) == -2 and res(D=4) == -2
     assert "mtp_kv_restore" in bv.lib().mtp_last_error().decode()
