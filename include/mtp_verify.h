@@ -25,6 +25,12 @@
  *    softmax, top-p, normalise, categorical; at temperature 0 acceptance is
  *    argmax matching.  Ollama news item, fifth paragraph: a rollback point is
  *    recorded so that a rejection rewinds to the last accepted token.
+ *  - Around the pass: the full sampler (penalties, top-k, top-p, min-p) in
+ *    the acceptance of B sequences (Ollama mtp.go commit log, MLX sampler
+ *    rework); the draft-depth controller (same log, controller message);
+ *    multi-row verify attention over a shared KV prefix (Qiita roofline
+ *    article, §2-3); cache rollback with lazy snapshots (same log, snapshot
+ *    rework).
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
