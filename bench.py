@@ -425,6 +425,35 @@ def extra_kv_rollback(bv, dev, steps, warmup):
     return res
 
 
+def read_ceiling(bv, dev, steps, warmup):
+    """The read rate one launch reaches on this GPU: a plain read of every
+    byte (mtp_read_probe, the best of its launch shapes), timed like the
+    verify GEMMs (graph replays over rotating copies) on buffers of the C1
+    matrix's size, the LM head's size and 2 GiB."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nb in (("33mb", W.weight_bytes(14336, 4096)), ("793mb", W.weight_bytes(262144, 5376)),
+                     ("2gib", 2 << 30)):
+        nb = (nb + 15) // 16 * 16
+        R = max(1, -(-ROTATE_BYTES // nb))   # >= 1 GiB of copies (2 GiB: one)
+        bufs = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(R)]
+
+        best = None
+        for shape in range(bv.read_probe_shapes()):
+            def call(i, shape=shape):
+                bv.read_probe(bufs[i % R], sink, shape)
+
+            _, ms, _ = time_graph(call, R, max(R, steps // 8), max(R, warmup // 8))
+            if best is None or ms < best[0]:
+                best = (ms, shape)
+        ms, shape = best
+        out[name] = {"bytes": nb, "copies": R, "best_shape": shape, "us": round(ms * 1e3, 3),
+                     "gbs": round(nb / (ms * 1e-3) / 1e9, 1)}
+        del bufs
+        torch.cuda.empty_cache()
+    return out
+
+
 def depth_controller(bv, sweep):
     """The draft depth the controller picks on this run's measured cost of
     one verify pass per width (M = 1, 2, 4, 8; linear in between) plus a
@@ -491,6 +520,11 @@ def main():
         extra["verify_attention_32k"] = extra_verify_attention(bv, dev, args.steps, args.warmup)
         extra["kv_rollback_52x16x128"] = extra_kv_rollback(bv, dev, args.steps, args.warmup)
 
+    ceiling = None
+    if not args.no_extra and not args.only_headline:
+        ceiling = read_ceiling(bv, dev, args.steps, args.warmup)
+        ceiling["c1_frac_of_33mb_ceiling"] = round(achieved / ceiling["33mb"]["gbs"], 4)
+
     if args.copy_calibration:
         copy_calibration(dev)
 
@@ -524,6 +558,8 @@ def main():
             out["depth_controller"] = depth_controller(bv, sweep)
     if extra:
         out["other_workloads"] = extra
+    if ceiling:
+        out["read_ceiling"] = ceiling
     if not args.no_cpu and not args.only_headline:
         out["cpu_baseline"] = cpu_baseline(cfg, M)
     print(json.dumps(out), flush=True)

@@ -20,7 +20,8 @@ __all__ = [
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
     "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
     "choose_draft_depth", "DepthStats", "verify_attention", "attention_workspace_bytes",
-    "kv_snapshot", "kv_append", "kv_restore",
+    "kv_snapshot", "kv_append", "kv_restore", "read_probe",
+    "read_probe_shapes",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
 ]
 
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
                                     P, P]
         L.mtp_kv_restore.restype = i32
         L.mtp_kv_restore.argtypes = [P, P, i32, i32, i32, i64, i32, i32, i32, P, P, P, P, P, P]
+        L.mtp_read_probe.restype = i32
+        L.mtp_read_probe.argtypes = [P, sz, P, i32, P]
         D = ctypes.c_double
         L.mtp_choose_draft_depth.restype = i32
         L.mtp_choose_draft_depth.argtypes = [P, P, i32, P]
@@ -424,6 +427,18 @@ def kv_restore(k_cache: torch.Tensor, v_cache: torch.Tensor, M: int, base_len: t
     _check(lib().mtp_kv_restore(_ptr(k_cache), _ptr(v_cache), NL, B, Hkv, cap, D,
                                 int(bool(ring)), int(M), _ptr(base_len), _ptr(rollback),
                                 _ptr(sk), _ptr(sv), _ptr(err), _stream(stream)))
+
+
+def read_probe_shapes() -> int:
+    """Number of launch shapes of the read-bandwidth probe."""
+    return int(lib().mtp_read_probe(None, 0, None, -1, None))
+
+
+def read_probe(src: torch.Tensor, sink: torch.Tensor, shape: int = 0, stream=None):
+    """Read every byte of the contiguous device tensor ``src`` once in launch
+    shape ``shape`` (a bandwidth measurement aid); ``sink`` is a device
+    int32 tensor."""
+    _check(lib().mtp_read_probe(_ptr(src), _nbytes(src), _ptr(sink), int(shape), _stream(stream)))
 
 
 def verify_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, L: int,

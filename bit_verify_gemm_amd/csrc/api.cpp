@@ -326,6 +326,18 @@ int mtp_kv_restore(uint16_t *k_cache, uint16_t *v_cache, int NL, int B, int Hkv,
                     who);
 }
 
+int mtp_read_probe(const void *src, size_t bytes, uint32_t *sink, int shape, void *stream) {
+  const char *who = "mtp_read_probe";
+  if (shape < 0) return mtp::read_probe_shapes();
+  if (shape >= mtp::read_probe_shapes())
+    return fail(MTP_ERR_VALUE, "%s: shape %d out of [0, %d)", who, shape, mtp::read_probe_shapes());
+  if (!src || !sink) return fail(MTP_ERR_NULL, "%s: src and sink are required", who);
+  if (!aligned(src, 16) || bytes % 16 || !aligned(sink, 4))
+    return fail(MTP_ERR_ALIGN, "%s: src and bytes must be multiples of 16", who);
+  return hip_status(
+      mtp::launch_read_probe(src, bytes, sink, shape, static_cast<hipStream_t>(stream)), who);
+}
+
 size_t mtp_accept_sampled_workspace_bytes(int B, int M, int V, int top_k, int penalties) {
   if (B < 1 || B > kMaxSampledSeqs || M < 1 || M > kMaxAcceptRows || V < 1 || V > kMaxVocab ||
       top_k < 1 || top_k > MTP_MAX_TOP_K)

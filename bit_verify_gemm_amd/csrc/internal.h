@@ -85,6 +85,12 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
                                    int64_t base_len, int32_t *tokens, int32_t *counts,
                                    int64_t *rollback, void *ws, hipStream_t stream);
 
+// ---- read-bandwidth probe (measurement aid) -------------------------------
+
+int read_probe_shapes();
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int shape,
+                             hipStream_t stream);
+
 // ---- KV-cache rollback ------------------------------------------------------
 
 hipError_t launch_kv_append(uint16_t *k, uint16_t *v, int NL, int B, int Hkv, int64_t cap, int D,

@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 4
+#define MTP_ABI_VERSION 5
 
 enum {
   MTP_OK = 0,
@@ -428,6 +428,20 @@ int mtp_choose_draft_depth(const double *accept_prob, const double *cost, int dm
 int mtp_depth_observe(double *reached, double *accepted, int dmax, int depth, int n_accepted,
                       double keep);
 int mtp_depth_estimate(const double *reached, const double *accepted, int dmax, double *prob);
+
+/*
+ * Read-bandwidth probe (a measurement aid, not a step of the verify pass):
+ * reads every 16-byte piece of src[0 .. bytes) once with non-temporal vector
+ * loads in launch shape `shape` (0 .. n-1: loads in flight per thread and
+ * grid size) and folds them so that no load can be dropped; *sink (device,
+ * 4-byte aligned) is written only when the fold equals one fixed value.
+ * Timed on buffers of a verify matrix's size, the best shape gives the read
+ * rate a launch of that size reaches: the ceiling the verify GEMM is
+ * compared with.  shape < 0 returns n (the number of shapes).
+ * Errors: MTP_ERR_VALUE (shape >= n), MTP_ERR_NULL, MTP_ERR_ALIGN (src not
+ * 16-byte aligned, bytes not a multiple of 16).
+ */
+int mtp_read_probe(const void *src, size_t bytes, uint32_t *sink, int shape, void *stream);
 
 /* Thread-local message for the last non-zero status of this thread. */
 const char *mtp_last_error(void);

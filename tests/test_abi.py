@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bv.abi_version() == 4
+    assert bv.abi_version() == 5
 
 
 def test_packed_sizes():
@@ -220,3 +220,14 @@ def test_kv_calls_reject_bad_arguments():
                             ctypes.c_void_p(0x10000 + 16), FAKE, FAKE, None, None) == -7  # partial overlap
     assert res(sk=None) == -1 and res(M=0) == -2 and res(D=4) == -2
     assert "mtp_kv_restore" in bv.lib().mtp_last_error().decode()
+
+
+def test_read_probe_rejects_bad_arguments():
+    L = bv.lib()
+    n = bv.read_probe_shapes()
+    assert n >= 1
+    assert L.mtp_read_probe(FAKE, 16, FAKE, n, None) == -7
+    assert L.mtp_read_probe(None, 16, FAKE, 0, None) == -1
+    assert L.mtp_read_probe(FAKE, 16, None, 0, None) == -1
+    assert L.mtp_read_probe(FAKE_ODD, 16, FAKE, 0, None) == -3
+    assert L.mtp_read_probe(FAKE, 17, FAKE, 0, None) == -3
