@@ -84,23 +84,31 @@ __device__ __forceinline__ u32x4 nvfp4_decode8_f16(uint32_t codes, f16x2 s2) {
 }
 
 // Eight bf16 values -> eight fp16 values (conversion toward zero).  Exact for
-// every bf16 value of magnitude in [2^-17, 65280], for zeros, infinities and
-// NaNs; smaller magnitudes lose at most 2^-24.  `ovf` is set when a finite
-// value lies beyond the fp16 range (|x| >= 65536).
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v, uint32_t &ovf) {
+// every bf16 value of magnitude in [2^-17, 65280] and for zeros; smaller
+// magnitudes lose at most 2^-24.  `mag` keeps, per 16-bit half, the largest
+// bf16 magnitude pattern seen (a packed unsigned maximum, one instruction
+// per two values); f16_unsafe(mag) then tells whether any value lay beyond
+// the fp16 range (|x| >= 65536) or was not finite.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v, uint32_t &mag) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, mag);
   u32x4 r;
-  uint32_t bad = 0;
-#define MTP_CVT_DWORD(c)                                                                    \
-  {                                                                                         \
-    const uint32_t lo = (v.c & 0x7FFFu) - 0x4780u, hi = ((v.c >> 16) & 0x7FFFu) - 0x4780u;  \
-    bad |= (uint32_t)(lo < 0x3800u) | (uint32_t)(hi < 0x3800u);                             \
+#define MTP_CVT_DWORD(c)                                                                     \
+  {                                                                                          \
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.c & 0x7FFF7FFFu));          \
     r.c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v.c << 16), \
                                                                  __uint_as_float(v.c & 0xFFFF0000u))); \
   }
   MTP_CVT_DWORD(x) MTP_CVT_DWORD(y) MTP_CVT_DWORD(z) MTP_CVT_DWORD(w)
 #undef MTP_CVT_DWORD
-  ovf |= bad;
+  mag = __builtin_bit_cast(uint32_t, m);
   return r;
+}
+
+// Whether a magnitude pattern kept by bf16x8_to_f16x8 reaches 65536
+// (0x4780), an infinity or a NaN in either half.
+__device__ __forceinline__ bool f16_unsafe(uint32_t mag) {
+  return (mag & 0xFFFFu) >= 0x4780u || (mag >> 16) >= 0x4780u;
 }
 
 // Eight offset-binary int4 codes u (element i in nibble i) -> eight bf16

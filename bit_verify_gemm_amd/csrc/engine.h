@@ -357,12 +357,12 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
 
   // Activations are staged as fp16 for nvfp4 (exact for the bf16 values met
   // in practice; see bf16x8_to_f16x8) and as bf16 in MFMA slot order for
-  // Q4_0.  If any staged nvfp4 activation exceeds the fp16 range the
-  // workgroup stages bf16 instead and takes the bf16 path.
-  uint32_t ovf = 0;
+  // Q4_0.  If any staged nvfp4 activation exceeds the fp16 range or is not
+  // finite, the workgroup stages bf16 instead and takes the bf16 path.
+  uint32_t xmag = 0;
   auto encode = [&](u32x4 v) -> u32x4 {
     if constexpr (FMT == MTP_FMT_Q4_0) return interleave_halves(v);
-    else return bf16x8_to_f16x8(v, ovf);
+    else return bf16x8_to_f16x8(v, xmag);
   };
 
   // 1) activation loads, 2) the first kPPShallow weight blocks, 3) activation
@@ -479,7 +479,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     step();
   }
   {
-    const bool any = __builtin_amdgcn_ballot_w64(ovf != 0u) != 0ull;
+    const bool any = __builtin_amdgcn_ballot_w64(f16_unsafe(xmag)) != 0ull;
     if (lane == 0) wave_ovf[wave] = any ? 1u : 0u;
   }
   for (int i = threadIdx.x; i < M * 32; i += nthreads) {   // zero slot of every row

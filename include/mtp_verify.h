@@ -145,6 +145,10 @@ int mtp_pack_weights(int format, int count, int N, int K, const uint8_t *codes,
  *                again.  Between GEMM calls nothing else may write it, and
  *                calls sharing it must be ordered on one stream.
  * Accuracy: |y - exact| <= 1e-3 * sum_k |x * w| + 1e-5 (fp32 accumulation).
+ * An infinity or NaN in x[m] makes every output of row m non-finite: nvfp4
+ * follows IEEE products and sums (+-inf, NaN where an infinity meets a zero
+ * weight); Q4_0 gives NaN (its per-block offset correction subtracts the
+ * infinite block sum).
  * Results are deterministic, and row m's result depends only on x[m] and W
  * (not on M or the other rows): the K split is a function of (N, K) alone.
  */

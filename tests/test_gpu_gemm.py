@@ -159,6 +159,32 @@ def test_strides_scale_and_bf16_output(fmt):
     assert np.array_equal(yb, expect)
 
 
+@pytest.mark.parametrize("fmt", [W.FMT_NVFP4, W.FMT_Q4_0])
+def test_non_finite_activations(fmt):
+    # an infinity in row 0 and a NaN in row 2.  nvfp4 (whose workgroups then
+    # take the bf16 path) follows IEEE products and sums: +-inf where the
+    # weight is nonzero, NaN where it is zero (inf * 0).  Q4_0 gives NaN in
+    # every output of such a row (its per-block offset correction subtracts
+    # the infinite block sum).  The other rows stay within the usual bound.
+    N, K, M = 200, 1024, 4
+    w = weight(fmt, N, K, seed=14)
+    rng = np.random.default_rng(15)
+    xf = rng.normal(size=(M, K)).astype(np.float32)
+    xf[0, 77] = np.inf
+    xf[2, 300] = np.nan
+    x = W.to_bf16_bits(xf)
+    y = gemm_gpu(bv, w, x)
+    y_ref, b_ref = oracle.gemm(w, x)
+    if fmt == W.FMT_NVFP4:
+        assert np.array_equal(np.isnan(y), np.isnan(y_ref)), "NaN pattern"
+        assert np.array_equal(np.isposinf(y), np.isposinf(y_ref)), "+inf pattern"
+        assert np.array_equal(np.isneginf(y), np.isneginf(y_ref)), "-inf pattern"
+    else:
+        assert np.isnan(y[0]).all()
+    assert np.isnan(y[2]).all() and not np.isfinite(y[0]).any()
+    assert_gemm_close(y[[1, 3]], y_ref[[1, 3]], b_ref[[1, 3]], "finite rows")
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_nvfp4_activations_outside_fp16_range(M):
     # nvfp4 activations are staged as fp16 when every value fits; a value
