@@ -365,11 +365,13 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     else return bf16x8_to_f16x8(v, xmag);
   };
 
-  // 1) activation loads, 2) the first kPPShallow weight blocks, 3) activation
-  // stores to LDS (waiting for the activation loads only), 4) the rest of the
+  // 1) activation loads, 2) the first weight block, 3) activation stores to
+  // LDS (waiting for the activation loads only), 4) the rest of the
   // prefetch: the activation bytes do not queue behind the weight stream, and
-  // the weight stream starts before the staging ends.  (More loads before
-  // the stores only stall the stores behind a full memory queue.)
+  // the weight stream starts before the staging ends.  (More blocks before
+  // the stores only stall the stores behind a full memory queue: with two,
+  // three or four the M = 8 launch measured 0.15-0.5 us slower, with none
+  // 0.7 us slower.)
   // Vector i = u * nthreads + tid of the staged rows is (m, v) = divmod(i,
   // vpr); (m, v) advance incrementally so that no division sits between the
   // loads.  Only the rounds that hold staged vectors load (xr, the same for
@@ -460,7 +462,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int kEarly = PP < kPPShallow ? PP : kPPShallow;
+  constexpr int kEarly = 1;
   Blk<FMT> buf[PP];
 #pragma unroll
   for (int i = 0; i < kEarly; ++i) load_blk(buf[i], next_block(), lane);
