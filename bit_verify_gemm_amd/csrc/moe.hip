@@ -91,26 +91,42 @@ struct Route {
 __device__ void route(const MoeArgs &a, Route &R, int slot) {
   const int P = a.P, nt = blockDim.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  // keys past P (up to a multiple of 16) are kNoExpert: they rank below no
-  // pair, so the rank loop reads whole groups of 16
+  // The rank order (expert, pair) is that of the distinct combined keys
+  // expert * kMaxPairs + pair (an invalid pair's expert reads as E; E <=
+  // 2^20 keeps them below 2^31), so ranking takes one compare per pair; the
+  // combined keys sit in R.order until every rank is known.  Keys past P (up
+  // to a multiple of 16) are the largest int: they rank below no pair, so
+  // the rank loop reads whole groups of 16.
   const int P16 = (P + 15) & ~15;
   for (int p = threadIdx.x; p < P16; p += nt) {
     const int e = p < P ? a.ids[p] : -1;
-    R.key[p] = (e >= 0 && e < a.E) ? e : kNoExpert;
+    const bool ok = e >= 0 && e < a.E;
+    R.key[p] = ok ? e : kNoExpert;
+    R.order[p] = p < P ? (ok ? e : a.E) * kMaxPairs + p : 0x7FFFFFFF;
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += nt) {
-    const int k = R.key[p];
-    int r = 0;
-    for (int q0 = 0; q0 < P16; q0 += 16) {
-      int kq[16];   // all 16 loads in flight before the compares
+  constexpr int kMaxPerThread = kMaxPairs / kWave;   // workgroups have >= 64 threads
+  int rank[kMaxPerThread];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) kq[j] = R.key[q0 + j];
+  for (int u = 0; u < kMaxPerThread; ++u) {
+    const int p = threadIdx.x + u * nt;
+    rank[u] = 0;
+    if (p < P) {
+      const int ck = R.order[p];
+      for (int q0 = 0; q0 < P16; q0 += 16) {
+        int kq[16];   // all 16 loads in flight before the compares
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        r += (kq[j] < k || (kq[j] == k && q0 + j < p)) ? 1 : 0;
+        for (int j = 0; j < 16; ++j) kq[j] = R.order[q0 + j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rank[u] += kq[j] < ck ? 1 : 0;
+      }
     }
-    R.order[r] = p;
+  }
+  __syncthreads();   // every combined key is read
+#pragma unroll
+  for (int u = 0; u < kMaxPerThread; ++u) {
+    const int p = threadIdx.x + u * nt;
+    if (p < P) R.order[rank[u]] = p;
   }
   __syncthreads();
   // rank i starts a slot when its pair is valid and its expert differs from
@@ -143,15 +159,15 @@ __device__ void route(const MoeArgs &a, Route &R, int slot) {
     for (int c = 0; c < nch; ++c) {
       const int sc = R.starts[c];
       nvalid += R.valid[c];
-      for (int want = slot; want <= slot + 1; ++want) {
-        if (want >= before && want < before + sc) {
-          uint64_t vb;
-          uint64_t sb = chunk(c, vb);
-          for (int j = before; j < want; ++j) sb &= sb - 1;   // drop the earlier starts
-          const int pos = c * kWave + __ffsll((long long)sb) - 1;
-          if (want == slot) first = pos;
-          else end = pos;
-        }
+      if (slot < before + sc && slot + 1 >= before) {   // start `slot` or `slot + 1` is here
+        uint64_t vb;
+        const uint64_t sb = chunk(c, vb);
+        // the start number of this lane's rank: starts below it in the chunk
+        const int num = before + __popcll(sb & ((1ull << lane) - 1ull));
+        const bool st = (sb >> lane) & 1ull;
+        const uint64_t h0 = __ballot(st && num == slot), h1 = __ballot(st && num == slot + 1);
+        if (h0) first = c * kWave + __ffsll((long long)h0) - 1;
+        if (h1) end = c * kWave + __ffsll((long long)h1) - 1;
       }
       before += sc;
     }
