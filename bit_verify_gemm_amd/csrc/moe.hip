@@ -80,6 +80,7 @@ struct Route {
   int32_t key[kMaxPairs];     // expert of pair p, kNoExpert for an id outside [0, E) or p >= P
   int32_t order[kMaxPairs];   // the pairs ranked by (key, pair)
   int32_t starts[kMaxPairs / kWave], valid[kMaxPairs / kWave];   // per 64 ranks
+  int32_t part[4][kWave];     // partial ranks (up to 64 pairs, four waves)
   int32_t e, first, rows;     // the slot: expert (-1: none), ranks first .. first + rows - 1
 };
 
@@ -105,30 +106,50 @@ __device__ void route(const MoeArgs &a, Route &R, int slot) {
     R.order[p] = p < P ? (ok ? e : a.E) * kMaxPairs + p : 0x7FFFFFFF;
   }
   __syncthreads();
-  constexpr int kMaxPerThread = kMaxPairs / kWave;   // workgroups have >= 64 threads
-  int rank[kMaxPerThread];
+  if (P16 <= kWave && nt >= 4 * kWave) {
+    // up to 64 pairs: each of four waves counts one quarter of the keys for
+    // every pair (lane = pair), then the four counts are added
+    if (wave < 4) {
+      const int q0 = wave * (P16 / 4);
+      int r = 0;
+      if (lane < P) {
+        const int ck = R.order[lane];
+        for (int j = 0; j < P16 / 4; ++j) r += R.order[q0 + j] < ck ? 1 : 0;
+      }
+      R.part[wave][lane] = r;
+    }
+    __syncthreads();   // every combined key is read
+    if (threadIdx.x < P) {
+      const int p = threadIdx.x;
+      R.order[R.part[0][p] + R.part[1][p] + R.part[2][p] + R.part[3][p]] = p;
+    }
+    __syncthreads();
+  } else {
+    constexpr int kMaxPerThread = kMaxPairs / kWave;   // workgroups have >= 64 threads
+    int rank[kMaxPerThread];
 #pragma unroll
-  for (int u = 0; u < kMaxPerThread; ++u) {
-    const int p = threadIdx.x + u * nt;
-    rank[u] = 0;
-    if (p < P) {
-      const int ck = R.order[p];
-      for (int q0 = 0; q0 < P16; q0 += 16) {
-        int kq[16];   // all 16 loads in flight before the compares
+    for (int u = 0; u < kMaxPerThread; ++u) {
+      const int p = threadIdx.x + u * nt;
+      rank[u] = 0;
+      if (p < P) {
+        const int ck = R.order[p];
+        for (int q0 = 0; q0 < P16; q0 += 16) {
+          int kq[16];   // all 16 loads in flight before the compares
 #pragma unroll
-        for (int j = 0; j < 16; ++j) kq[j] = R.order[q0 + j];
+          for (int j = 0; j < 16; ++j) kq[j] = R.order[q0 + j];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) rank[u] += kq[j] < ck ? 1 : 0;
+          for (int j = 0; j < 16; ++j) rank[u] += kq[j] < ck ? 1 : 0;
+        }
       }
     }
-  }
-  __syncthreads();   // every combined key is read
+    __syncthreads();   // every combined key is read
 #pragma unroll
-  for (int u = 0; u < kMaxPerThread; ++u) {
-    const int p = threadIdx.x + u * nt;
-    if (p < P) R.order[rank[u]] = p;
+    for (int u = 0; u < kMaxPerThread; ++u) {
+      const int p = threadIdx.x + u * nt;
+      if (p < P) R.order[rank[u]] = p;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // rank i starts a slot when its pair is valid and its expert differs from
   // that of rank i - 1; chunk c covers ranks 64c .. 64c + 63
   const int nch = (P + kWave - 1) / kWave;
