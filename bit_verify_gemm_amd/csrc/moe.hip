@@ -164,25 +164,28 @@ __device__ void route(const MoeArgs &a, Route &R, int slot) {
     vb = __ballot(vd);
     return __ballot(st);
   };
-  for (int c = wave; c < nch; c += nt / kWave) {
-    uint64_t vb;
-    const uint64_t sb = chunk(c, vb);
-    if (lane == 0) {
-      R.starts[c] = __popcll(sb);
-      R.valid[c] = __popcll(vb);
+  if (nch > 1) {   // (one chunk: the search below takes its counts itself)
+    for (int c = wave; c < nch; c += nt / kWave) {
+      uint64_t vb;
+      const uint64_t sb = chunk(c, vb);
+      if (lane == 0) {
+        R.starts[c] = __popcll(sb);
+        R.valid[c] = __popcll(vb);
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   if (wave == 0) {
     // the rank of start number `slot` and of the next start (or the number
     // of valid pairs: they rank first)
     int before = 0, nvalid = 0, first = -1, end = -1;
     for (int c = 0; c < nch; ++c) {
-      const int sc = R.starts[c];
-      nvalid += R.valid[c];
+      uint64_t vb = 0, sb = 0;
+      if (nch == 1) sb = chunk(0, vb);
+      const int sc = nch == 1 ? __popcll(sb) : R.starts[c];
+      nvalid += nch == 1 ? __popcll(vb) : R.valid[c];
       if (slot < before + sc && slot + 1 >= before) {   // start `slot` or `slot + 1` is here
-        uint64_t vb;
-        const uint64_t sb = chunk(c, vb);
+        if (nch > 1) sb = chunk(c, vb);
         // the start number of this lane's rank: starts below it in the chunk
         const int num = before + __popcll(sb & ((1ull << lane) - 1ull));
         const bool st = (sb >> lane) & 1ull;
