@@ -189,6 +189,11 @@ struct AccIn {
 
 constexpr int kMaxRows = 64;
 
+// Per draw block: residual sum (lo, hi), e sum (lo, hi), and the first index
+// whose residual, resp. e, is positive in fp64 (kNone: none).
+constexpr int kBlkWords = 6;
+constexpr int kNone = 0x7FFFFFFF;
+
 struct Layout {
   size_t maxp, zmax, hist, total, sel, rows, acc, blk, gpart, bytes;
 };
@@ -209,7 +214,7 @@ Layout layout(int M, int V) {
   L.sel = take(sizeof(SelState) * 4 * M);
   L.rows = take(sizeof(RowState) * M);
   L.acc = take(sizeof(AccIn) * M);
-  L.blk = take(sizeof(u64) * 4 * (size_t)draw_blocks(V));
+  L.blk = take(sizeof(u64) * kBlkWords * (size_t)draw_blocks(V));
   L.gpart = take(sizeof(float) * 2 * M * nb);
   L.bytes = o;
   return L;
@@ -237,7 +242,7 @@ struct RejArgs {
   SelState *sel;    // [pass][row]: state after `pass` selections (pass >= 1)
   RowState *rows;
   AccIn *acc;       // [row]: inputs of draft row's acceptance test
-  u64 *blk;         // [block][res lo, res hi, e lo, e hi]
+  u64 *blk;         // [block][res lo, res hi, e lo, e hi, first res > 0, first e > 0]
 };
 
 __device__ __forceinline__ u64 *hist_at(const RejArgs &p, int pass, int row) {
@@ -672,21 +677,100 @@ __device__ __forceinline__ int accepted_run(const RejArgs &p) {
   return rej ? __ffsll((long long)rej) - 1 : p.M - 1;
 }
 
-// Weights of the final draw for entry j of row `row`.
+// Weights of the final draw for entry j of row `row`, in fixed point, and
+// whether each is positive in fp64 (pe: e > 0, pres: e / mass - q > 0).  The
+// fixed-point weights drop values below 2^-100; the flags do not, so that a
+// draw whose target is below that resolution (u = 0 picks the first positive
+// weight) still follows the fp64 weights.  (rs.mass >= 1, the row maximum's
+// own weight.)
 __device__ __forceinline__ void draw_weights(const RejArgs &p, const RowState &rs, int row,
-                                             bool residual, int j, Fx &wres, Fx &we) {
+                                             bool residual, int j, Fx &wres, Fx &we, bool &pres,
+                                             bool &pe) {
   const float zj = p.z[(int64_t)row * p.ldl + j];
-  // (rs.mass >= 1, the row maximum's own weight, so a weight that is 0 in
-  // fixed point also gives a residual of 0)
-  double e = 0.0;
-  if (in_nucleus(rs, zj, j)) e = e_or_zero(zj, rs.zmax, p.T);
+  double e = 0.0, x = 0.0;
+  pe = false;
+  const bool in = in_nucleus(rs, zj, j);
+  if (in) {
+    x = ((double)zj - (double)rs.zmax) / p.T;
+    e = x < -70.5 ? 0.0 : exp(x);            // as e_or_zero
+    pe = x > -744.0 || exp(x) > 0.0;         // exp(-744) ~ 1e-323 is still positive
+  }
   we = to_fx(e);
+  pres = false;
   if (residual) {
-    const double d = e / rs.mass - (double)p.q[(int64_t)row * p.ldq + j];
+    const double qj = (double)p.q[(int64_t)row * p.ldq + j];
+    const double d = e / rs.mass - qj;
     wres = to_fx(d > 0.0 ? d : 0.0);
+    pres = d > 0.0;
+    // e skipped below 2^-100: positive residual only where q is smaller still
+    if (in && e == 0.0 && qj < 0x1p-100) pres = exp(x) / rs.mass - qj > 0.0;
   } else {
     wres = fx_zero();
   }
+}
+
+// The same weight in fp64, as the definition reads (no skipped exponential):
+// e inside the nucleus, or max(0, e / mass - q).
+__device__ __forceinline__ double draw_weight_f64(const RejArgs &p, const RowState &rs, int row,
+                                                  bool residual, int j) {
+  const float zj = p.z[(int64_t)row * p.ldl + j];
+  const double e = in_nucleus(rs, zj, j) ? exp(((double)zj - (double)rs.zmax) / p.T) : 0.0;
+  if (!residual) return e;
+  const double d = e / rs.mass - (double)p.q[(int64_t)row * p.ldq + j];
+  return d > 0.0 ? d : 0.0;
+}
+
+// A draw whose target u * W lies below the fixed-point resolution, in fp64
+// and index order as the definition reads: W = w_0 + .. + w_{V-1} summed in
+// order, then the smallest j whose running sum exceeds u * W (the last
+// positive weight if rounding passes the end).  The block computes 256
+// weights at a time; thread 0 adds them in order.  Slow (a sequential pass
+// over the row), but reached only by u = 0-like targets that the first
+// positive index does not settle, or by residuals whose every positive
+// weight is below 2^-100.
+__device__ int draw_f64_sequential(const RejArgs &p, const RowState &rs, int row, bool residual,
+                                   double u) {
+  __shared__ double sw[kBlock];
+  __shared__ double s_t;
+  __shared__ int s_found, s_last;
+  double W = 0.0;
+  int last = -1;
+  for (int base = 0; base < p.V; base += kBlock) {
+    const int j = base + (int)threadIdx.x;
+    sw[threadIdx.x] = j < p.V ? draw_weight_f64(p, rs, row, residual, j) : 0.0;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int i = 0; i < kBlock && base + i < p.V; ++i) {
+        W += sw[i];
+        if (sw[i] > 0.0) last = base + i;
+      }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    s_t = u * W;
+    s_found = -1;
+    s_last = last;
+  }
+  __syncthreads();
+  double cum = 0.0;
+  for (int base = 0; base < p.V; base += kBlock) {
+    const int j = base + (int)threadIdx.x;
+    sw[threadIdx.x] = j < p.V ? draw_weight_f64(p, rs, row, residual, j) : 0.0;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int i = 0; i < kBlock && base + i < p.V; ++i) {
+        cum += sw[i];
+        if (cum > s_t) {
+          s_found = base + i;
+          break;
+        }
+      }
+    __syncthreads();
+    if (s_found >= 0) break;
+  }
+  const int r = s_found >= 0 ? s_found : (s_last >= 0 ? s_last : p.V - 1);
+  __syncthreads();
+  return r;
 }
 
 // Exclusive 128-bit prefix sums over the threads of the block (thread order);
@@ -722,32 +806,46 @@ __device__ Fx fx_block_exclusive(Fx v, Fx *wsum, Fx &total) {
 // serialises their arrivals.)
 __global__ __launch_bounds__(kBlock) void rej_draw_sums(RejArgs p) {
   __shared__ Fx wsum[kBlock / kWave];
+  __shared__ int s_fr, s_fe;
   const int a = accepted_run(p);
   const int residual = a < p.M - 1;
   const RowState rs = p.rows[a];
   const int b = blockIdx.x;
   const int j0 = b * p.chunkd, j1 = min(p.V, j0 + p.chunkd);
+  if (threadIdx.x == 0) {
+    s_fr = kNone;
+    s_fe = kNone;
+  }
+  __syncthreads();
   Fx sr = fx_zero(), se = fx_zero();
+  int fr = kNone, fe = kNone;   // this thread's first positive entries (j rises)
   for (int j = j0 + threadIdx.x; j < j1; j += kBlock) {
     Fx wr, we;
-    draw_weights(p, rs, a, residual != 0, j, wr, we);
+    bool pr, pe;
+    draw_weights(p, rs, a, residual != 0, j, wr, we, pr, pe);
     fx_add(sr, wr);
     fx_add(se, we);
+    if (pr && fr == kNone) fr = j;
+    if (pe && fe == kNone) fe = j;
   }
-  sr = fx_block_sum(sr, wsum);
+  if (fr != kNone) atomicMin(&s_fr, fr);
+  if (fe != kNone) atomicMin(&s_fe, fe);
+  sr = fx_block_sum(sr, wsum);   // (its barriers also order the minima above)
   se = fx_block_sum(se, wsum);
   if (threadIdx.x == 0) {
-    u64 *o = p.blk + 4 * b;
+    u64 *o = p.blk + kBlkWords * b;
     o[0] = sr.lo;
     o[1] = sr.hi;
     o[2] = se.lo;
     o[3] = se.hi;
+    o[4] = (u64)s_fr;
+    o[5] = (u64)s_fe;
   }
 }
 
 __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
   __shared__ Fx wsum[kBlock / kWave];
-  __shared__ int s_blk, s_lastnz, s_pick;
+  __shared__ int s_blk, s_lastnz, s_pick, s_fr, s_fe;
   __shared__ Fx s_before;
   __shared__ RowState s_rows[kMaxRows];
   // thread t holds chunks k0 .. k1-1 (in order); their sums and every row's
@@ -756,19 +854,28 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
   const int per = (p.nbd + kBlock - 1) / kBlock;
   const int k0 = min(p.nbd, (int)threadIdx.x * per), k1 = min(p.nbd, k0 + per);
   Fx cr[kPer], ce[kPer];
+  int fr = kNone, fe = kNone;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     cr[i] = ce[i] = fx_zero();
     if (k0 + i < k1) {
-      const u64 *o = p.blk + 4 * (k0 + i);
+      const u64 *o = p.blk + kBlkWords * (k0 + i);
       cr[i] = Fx{o[0], o[1]};
       ce[i] = Fx{o[2], o[3]};
+      fr = min(fr, (int)o[4]);
+      fe = min(fe, (int)o[5]);
     }
   }
   if (threadIdx.x < p.M) s_rows[threadIdx.x] = p.rows[threadIdx.x];
+  if (threadIdx.x == 0) {
+    s_fr = kNone;
+    s_fe = kNone;
+  }
   const int a = accepted_run(p);
   const int residual = a < p.M - 1;
   __syncthreads();
+  if (fr != kNone) atomicMin(&s_fr, fr);
+  if (fe != kNone) atomicMin(&s_fe, fe);
   const RowState rs = s_rows[a];
   Fx lres = fx_zero(), le = fx_zero();
 #pragma unroll
@@ -776,10 +883,35 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
     fx_add(lres, cr[i]);
     fx_add(le, ce[i]);
   }
-  const Fx tres = fx_block_sum(lres, wsum);
+  const Fx tres = fx_block_sum(lres, wsum);   // (its barriers also order the minima)
   const Fx te = fx_block_sum(le, wsum);
-  const bool use_res = residual && fx_nonzero(tres);
-  const Fx target = to_fx((double)p.u[p.M - 1] * fx_to_double(use_res ? tres : te));
+  // the residual is used when any of its fp64 weights is positive (its sum
+  // in fp64 is then positive), even if all of them are below 2^-100
+  const bool use_res = residual && s_fr != kNone;
+  const double u = (double)p.u[p.M - 1];
+  const Fx target = to_fx(u * fx_to_double(use_res ? tres : te));
+  if (!fx_nonzero(target)) {
+    // below the fixed-point resolution: u = 0 takes the first positive weight
+    // (the first index whose running sum exceeds 0); any other target is
+    // settled in fp64 by the sequential definition
+    int pick;
+    if (u == 0.0) {
+      const int f = use_res ? s_fr : s_fe;
+      pick = f != kNone ? f : p.V - 1;
+    } else {
+      pick = draw_f64_sequential(p, rs, a, use_res, u);
+    }
+    if (threadIdx.x < p.M) {
+      const int i = threadIdx.x;
+      p.tokens[i] = (i < a) ? p.drafts[i] : (i == a ? pick : -1);
+    }
+    if (threadIdx.x == 0) {
+      p.counts[0] = a;
+      p.counts[1] = a + 1;
+      *p.rollback = p.base_len + a + 1;
+    }
+    return;
+  }
   Fx total_unused;
   Fx cum = fx_block_exclusive(use_res ? lres : le, wsum, total_unused);
   if (threadIdx.x == 0) {
@@ -816,7 +948,8 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
       // thread t holds entry base + t
       const int jt = base + (int)threadIdx.x;
       Fx wr = fx_zero(), we = fx_zero();
-      if (jt < j1) draw_weights(p, rs, a, residual != 0, jt, wr, we);
+      bool pr, pe;
+      if (jt < j1) draw_weights(p, rs, a, residual != 0, jt, wr, we, pr, pe);
       const Fx w = use_res ? wr : we;
       Fx total;
       const Fx before = fx_sum(s_before, fx_block_exclusive(w, wsum, total));
@@ -1291,9 +1424,10 @@ __global__ __launch_bounds__(kRowThreads) void samp_row(SampArgs p) {
   const bool in = j < kept;
   const double pj = in ? e / mass : 0.0;
   if (p.out_ids) {
-    if (j < K) {
-      p.out_ids[(size_t)row * K + j] = in ? sid[j] : -1;
-      p.out_probs[(size_t)row * K + j] = in ? (float)pj : 0.0f;
+    if (j < K) {   // the support: kept entries whose p' is positive in fp64
+      const bool sup = in && pj > 0.0;
+      p.out_ids[(size_t)row * K + j] = sup ? sid[j] : -1;
+      p.out_probs[(size_t)row * K + j] = sup ? (float)pj : 0.0f;
     }
   }
   // acceptance inputs of the row's draft
@@ -1374,22 +1508,72 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
   const int n = p.nkept[row];
   int32_t id = -1;
   Fx wr = fx_zero(), we = fx_zero();
+  double dres = 0.0, dp = 0.0;   // fp64 residual and p'
   if (j < n) {
     id = p.sid[(size_t)row * p.K + j];
     we = to_fx(p.se[(size_t)row * p.K + j]);
+    dp = p.sp[(size_t)row * p.K + j];
     if (residual) {
-      const double d = p.sp[(size_t)row * p.K + j] - samp_q(p, r, id, qid, qpr);
-      wr = to_fx(d > 0.0 ? d : 0.0);
+      const double d = dp - samp_q(p, r, id, qid, qpr);
+      dres = d > 0.0 ? d : 0.0;
+      wr = to_fx(dres);
     }
   }
+  // first support slot (id order) with a positive fp64 residual, resp. p'
+  __shared__ int s_fr, s_fp;
+  if (j == 0) {
+    s_fr = 0x7FFFFFFF;
+    s_fp = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  if (dres > 0.0) atomicMin(&s_fr, j);
+  if (dp > 0.0) atomicMin(&s_fp, j);
   Fx tres;
-  fx_row_exclusive(wr, wsum, tres);
-  const bool use_res = residual && fx_nonzero(tres);
+  fx_row_exclusive(wr, wsum, tres);   // (its barriers also order the minima)
+  // the residual is used when any of its fp64 weights is positive, even if
+  // all of them are below the fixed-point resolution
+  const bool use_res = residual && s_fr != 0x7FFFFFFF;
   const Fx w = use_res ? wr : we;
   Fx W;
   const Fx before = fx_row_exclusive(w, wsum, W);
-  const Fx target = to_fx((double)p.u[(int64_t)seq * p.M + p.M - 1] * fx_to_double(W));
-  if (j < n) {
+  const double u = (double)p.u[(int64_t)seq * p.M + p.M - 1];
+  const Fx target = to_fx(u * fx_to_double(W));
+  if (!fx_nonzero(target)) {
+    // below 2^-100: u = 0 takes the first positive weight (the first slot
+    // whose running sum exceeds 0); another target follows the fp64
+    // definition in index order (the residual, or p' itself), summed by one
+    // thread over the support
+    if (j == 0) {
+      const int f = use_res ? s_fr : s_fp;
+      int slot = f;
+      if (u != 0.0) {
+        auto wgt = [&](int k) {
+          const double pk = p.sp[(size_t)row * p.K + k];
+          if (!use_res) return pk;
+          const double d = pk - samp_q(p, r, p.sid[(size_t)row * p.K + k], qid, qpr);
+          return d > 0.0 ? d : 0.0;
+        };
+        double Wd = 0.0;
+        int last = -1;
+        for (int k = 0; k < n; ++k) {
+          const double wk = wgt(k);
+          Wd += wk;
+          if (wk > 0.0) last = k;
+        }
+        const double t = u * Wd;
+        double cum = 0.0;
+        slot = last;
+        for (int k = 0; k < n; ++k) {
+          cum += wgt(k);
+          if (cum > t) {
+            slot = k;
+            break;
+          }
+        }
+      }
+      s_pick = (slot >= 0 && slot < n) ? p.sid[(size_t)row * p.K + slot] : p.V - 1;
+    }
+  } else if (j < n) {
     const Fx cum = fx_sum(before, w);
     if (fx_gt(cum, target) && !fx_gt(before, target)) s_pick = id;
     if (fx_nonzero(w)) atomicMax(&s_last, j);

@@ -84,31 +84,61 @@ __device__ __forceinline__ u32x4 nvfp4_decode8_f16(uint32_t codes, f16x2 s2) {
 }
 
 // Eight bf16 values -> eight fp16 values (conversion toward zero).  Exact for
-// every bf16 value of magnitude in [2^-17, 65280] and for zeros; smaller
-// magnitudes lose at most 2^-24.  `mag` keeps, per 16-bit half, the largest
-// bf16 magnitude pattern seen (a packed unsigned maximum, one instruction
-// per two values); f16_unsafe(mag) then tells whether any value lay beyond
-// the fp16 range (|x| >= 65536) or was not finite.
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v, uint32_t &mag) {
+// zeros and for every bf16 value of magnitude in [2^-17, 65280]: a bf16 value
+// has 8 significant bits, so from 2^-17 up its lowest bit is at least 2^-24,
+// the spacing of fp16 subnormals.  Per 16-bit half, `mag` keeps the largest
+// bf16 magnitude pattern seen and `mnz` the smallest of (magnitude pattern -
+// 1) mod 2^16, so a zero leaves it at 0xFFFF (packed unsigned maximum,
+// subtract and minimum: three instructions per two values);
+// f16_unsafe(mag, mnz) then tells whether any value was not finite, reached
+// 65536 or was nonzero below 2^-17.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v, uint32_t &mag, uint32_t &mnz) {
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
   u16x2 m = __builtin_bit_cast(u16x2, mag);
+  u16x2 n = __builtin_bit_cast(u16x2, mnz);
+  const u16x2 one = {1, 1};
   u32x4 r;
 #define MTP_CVT_DWORD(c)                                                                     \
   {                                                                                          \
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.c & 0x7FFF7FFFu));          \
+    const u16x2 a = __builtin_bit_cast(u16x2, v.c & 0x7FFF7FFFu);                            \
+    m = __builtin_elementwise_max(m, a);                                                     \
+    n = __builtin_elementwise_min(n, a - one);                                               \
     r.c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v.c << 16), \
                                                                  __uint_as_float(v.c & 0xFFFF0000u))); \
   }
   MTP_CVT_DWORD(x) MTP_CVT_DWORD(y) MTP_CVT_DWORD(z) MTP_CVT_DWORD(w)
 #undef MTP_CVT_DWORD
   mag = __builtin_bit_cast(uint32_t, m);
+  mnz = __builtin_bit_cast(uint32_t, n);
   return r;
 }
 
-// Whether a magnitude pattern kept by bf16x8_to_f16x8 reaches 65536
-// (0x4780), an infinity or a NaN in either half.
-__device__ __forceinline__ bool f16_unsafe(uint32_t mag) {
-  return (mag & 0xFFFFu) >= 0x4780u || (mag >> 16) >= 0x4780u;
+// Whether the patterns kept by bf16x8_to_f16x8 show, in either half, a
+// magnitude of 65536 (0x4780) or more, an infinity or NaN, or a nonzero
+// magnitude below 2^-17 (0x3700).
+__device__ __forceinline__ bool f16_unsafe(uint32_t mag, uint32_t mnz) {
+  return (mag & 0xFFFFu) >= 0x4780u || (mag >> 16) >= 0x4780u || (mnz & 0xFFFFu) < 0x36FFu ||
+         (mnz >> 16) < 0x36FFu;
+}
+
+// Binary exponent e of a nonzero finite bf16 magnitude pattern p:
+// 2^e <= value < 2^(e+1) (subnormals included).
+__device__ __forceinline__ int bf16_exponent(uint32_t p) {
+  return p >= 0x80u ? (int)(p >> 7) - 127 : (31 - __builtin_clz(p)) - 133;
+}
+
+// Eight bf16 values times 2^s (a power of two given as fp32 `sc`) -> eight
+// fp16 values, exact whenever every nonzero |x| * 2^s lies in [2^-17, 2^16)
+// (the product is exact in fp32 and has at most 8 significant bits).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 v, float sc) {
+  u32x4 r;
+#define MTP_CVT_DWORD(c)                                                                   \
+  r.c = __builtin_bit_cast(uint32_t,                                                       \
+                           __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v.c << 16) * sc,     \
+                                                      __uint_as_float(v.c & 0xFFFF0000u) * sc));
+  MTP_CVT_DWORD(x) MTP_CVT_DWORD(y) MTP_CVT_DWORD(z) MTP_CVT_DWORD(w)
+#undef MTP_CVT_DWORD
+  return r;
 }
 
 // Eight offset-binary int4 codes u (element i in nibble i) -> eight bf16

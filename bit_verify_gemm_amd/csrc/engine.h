@@ -46,7 +46,7 @@ constexpr int kSlotBytes = 512;   // one pair of one activation row in LDS (256 
 constexpr int kPPShallow = 2;     // blocks in flight per wave: workgroups with many tile groups
 constexpr int kPPDeep = 4;        // ... one tile group per workgroup (one 8-wave workgroup per CU)
 constexpr int kMaxWaves = 16;         // waves of all workgroups on one CU (<= 128 VGPRs)
-constexpr int kWgWaves = 8;           // waves of one workgroup at most
+constexpr int kWgWaves = 8;           // compute waves of one workgroup at most
 constexpr int kMaxThreads = kWgWaves * kWave;
 constexpr int kXU = 12;           // activation staging rounds in flight at once
 constexpr int kMaxLds = 160 * 1024;
@@ -290,6 +290,7 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4)
 // Every thread of the workgroup calls run with the same arguments;
 // sync_entry must be true when the workgroup ran the engine before (its LDS
 // may still be in use).
+
 template <int FMT, int PP, int NT, bool LOCAL, bool GATHER, typename TileOf, typename Epi>
 __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
                                     const Plan &pl, const TileOf &tile_of, const Fixup &fx,
@@ -355,14 +356,19 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
 
   if (sync_entry) __syncthreads();  // LDS may still be read by a previous call's epilogue
 
-  // Activations are staged as fp16 for nvfp4 (exact for the bf16 values met
-  // in practice; see bf16x8_to_f16x8) and as bf16 in MFMA slot order for
-  // Q4_0.  If any staged nvfp4 activation exceeds the fp16 range or is not
-  // finite, the workgroup stages bf16 instead and takes the bf16 path.
-  uint32_t xmag = 0;
+  // Activations are staged as fp16 for nvfp4 and as bf16 in MFMA slot order
+  // for Q4_0.  The fp16 copy is exact when every nonzero staged magnitude
+  // lies in [2^-17, 65280] (see bf16x8_to_f16x8).  Otherwise the workgroup
+  // restages its activations times a power of two 2^s that brings its
+  // largest magnitude just below 2^16, and scales its sums back by 2^-s
+  // (every product and partial sum then carries the factor exactly, so the
+  // result is that of the unscaled products); if even then a nonzero value
+  // would fall below 2^-17, or a value is not finite, it stages bf16 and
+  // takes the bf16 path.
+  uint32_t xmag = 0, xmnz = 0xFFFFFFFFu;
   auto encode = [&](u32x4 v) -> u32x4 {
     if constexpr (FMT == MTP_FMT_Q4_0) return interleave_halves(v);
-    else return bf16x8_to_f16x8(v, xmag);
+    else return bf16x8_to_f16x8(v, xmag, xmnz);
   };
 
   // 1) activation loads, 2) the first weight block, 3) activation stores to
@@ -481,7 +487,7 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     step();
   }
   {
-    const bool any = __builtin_amdgcn_ballot_w64(f16_unsafe(xmag)) != 0ull;
+    const bool any = __builtin_amdgcn_ballot_w64(f16_unsafe(xmag, xmnz)) != 0ull;
     if (lane == 0) wave_ovf[wave] = any ? 1u : 0u;
   }
   for (int i = threadIdx.x; i < M * 32; i += nthreads) {   // zero slot of every row
@@ -537,14 +543,41 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   if (FMT == MTP_FMT_NVFP4)
     for (int q = 0; q < nthreads / kWave; ++q) x_ovf |= wave_ovf[q];
   bool use_f16 = FMT == MTP_FMT_NVFP4;
+  float xinv = 1.0f;   // 2^-s: takes the staging scale back out of the sums
   if (FMT == MTP_FMT_NVFP4 && __builtin_amdgcn_readfirstlane(x_ovf)) {
-    use_f16 = false;
+    // workgroup extremes: the largest magnitude pattern and the smallest
+    // nonzero one minus 1 (0xFFFF: all zero)
+    uint32_t hi = max(xmag & 0xFFFFu, xmag >> 16), lo = min(xmnz & 0xFFFFu, xmnz >> 16);
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    }
+    __shared__ uint32_t wave_ext[kWgWaves];
+    if (lane == 0) wave_ext[wave] = hi | (lo << 16);
+    __syncthreads();
+    hi = 0u;
+    lo = 0xFFFFu;
+    for (int q = 0; q < nthreads / kWave; ++q) {
+      hi = max(hi, wave_ext[q] & 0xFFFFu);
+      lo = min(lo, wave_ext[q] >> 16);
+    }
+    // s puts the largest magnitude in [2^15, 2^16); 2^s and 2^-s stay normal
+    int s = 0;
+    bool scaled = false;
+    if (hi < 0x7F80u) {
+      s = min(126, 15 - bf16_exponent(hi));
+      scaled = lo == 0xFFFFu || bf16_exponent(lo + 1u) + s >= -17;
+    }
+    use_f16 = scaled;
+    const float sc = __builtin_ldexpf(1.0f, s);
+    xinv = __builtin_ldexpf(1.0f, -s);
     for (int i = threadIdx.x; i < M * vpr; i += nthreads) {
       const int m = i / vpr, v = i - m * vpr;
       const int k = k0 + v * 8;
       u32x4 val = {0u, 0u, 0u, 0u};
       if (k < K) val = *reinterpret_cast<const u32x4 *>(xs.row(m) + k);
-      *reinterpret_cast<u32x4 *>(lds + m * rowb + v * 16) = val;
+      *reinterpret_cast<u32x4 *>(lds + m * rowb + v * 16) =
+          scaled ? bf16x8_to_f16x8_scaled(val, sc) : val;
     }
     __syncthreads();
   }
@@ -573,6 +606,10 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
           load_blk(buf[i], next_block(), lane);
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      if constexpr (kF16) {
+#pragma unroll
+        for (int q = 0; q < NT; ++q) acc[q] *= xinv;
       }
       if constexpr (LOCAL) epi.wave(tg, tw, acc);
       else finish_group(tg, acc[0]);

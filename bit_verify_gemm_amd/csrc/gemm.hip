@@ -164,6 +164,19 @@ void slices(int T, int P, int &S, int &ppj) {
   S = (P + ppj - 1) / ppj;
 }
 
+// Workspace of a K-split plan: the arrival counters (one per tile group,
+// indexed below T) in a header of at least kCounterHeader bytes, then the
+// slice partials.  Matrices of up to kCounterHeader / 4 tiles all put their
+// partials past the same fixed header, so the partial sums one shape leaves
+// behind never lie where another shape looks for its (zero) counters.
+constexpr size_t kCounterHeader = 256 * 1024;
+
+size_t counter_bytes(int T) {
+  return std::max(kCounterHeader, ((size_t)T * 4 + 255) & ~(size_t)255);
+}
+
+size_t split_ws_bytes(int T, int S) { return counter_bytes(T) + (size_t)T * S * kWave * 16; }
+
 }  // namespace
 
 size_t packed_weight_bytes(int N, int K) { return eng::packed_bytes(N, K); }
@@ -187,7 +200,7 @@ size_t gemm_ws_bytes(int N, int K) {
   int S, ppj;
   slices(T, P, S, ppj);
   if (S == 1) return 0;
-  return (((size_t)T * 4 + 255) & ~(size_t)255) + (size_t)T * S * kWave * 16;
+  return split_ws_bytes(T, S);
 }
 
 GemmPlan gemm_plan(int format, int M, int N, int K) {
@@ -237,9 +250,7 @@ GemmPlan finish_plan(GemmPlan pl) {
     pl.PP = per_cu == 1 ? deep : eng::kPPShallow;
   }
   pl.grid = pl.G * pl.KG;
-  pl.ws_bytes = pl.KG > 1 ? (((size_t)pl.T * 4 + 255) & ~(size_t)255) +
-                                (size_t)pl.T * pl.S * kWave * 16
-                          : 0;
+  pl.ws_bytes = pl.KG > 1 ? split_ws_bytes(pl.T, pl.S) : 0;
   return pl;
 }
 
@@ -253,7 +264,7 @@ hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64
   a.TW = pl.TW; a.J = pl.J; a.S = pl.S; a.ppj = pl.ppj; a.KG = pl.KG; a.TG = pl.TG; a.G = pl.G;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   a.fx.cnt = reinterpret_cast<uint32_t *>(w8);
-  a.fx.part = reinterpret_cast<f32x4 *>(w8 ? w8 + (((size_t)pl.T * 4 + 255) & ~(size_t)255) : nullptr);
+  a.fx.part = reinterpret_cast<f32x4 *>(w8 ? w8 + counter_bytes(pl.T) : nullptr);
   auto go = [&](auto kernel) {
     eng::allow_large_lds(kernel);
     hipLaunchKernelGGL(kernel, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);

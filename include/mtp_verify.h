@@ -139,11 +139,16 @@ int mtp_pack_weights(int format, int count, int N, int K, const uint8_t *codes,
  *   y_bf16,ldyb  optional bf16 copy of y (round to nearest even) [M][ldyb];
  *                may be NULL.  At least one of y and y_bf16 must be non-NULL.
  *   ws, ws_bytes workspace of at least mtp_gemm_workspace_bytes(N, K) bytes
- *                (NULL allowed when that is 0), 256-byte aligned.  It holds
- *                arrival counters that must be ZERO before its first use
- *                (fill it with zeros once); every call leaves them zero
- *                again.  Between GEMM calls nothing else may write it, and
- *                calls sharing it must be ordered on one stream.
+ *                (NULL allowed when that is 0), 256-byte aligned.  Its first
+ *                max(256 KiB, 4 * ceil(N/16)) bytes hold arrival counters
+ *                that must be ZERO before its first use (fill it with zeros
+ *                once); every call leaves them zero again, and the partial
+ *                sums follow them.  One workspace (of the largest size
+ *                needed) may serve any sequence of matrices with N <=
+ *                1048576; a matrix with more rows needs one of its own (or
+ *                a refill with zeros before and after it).  Between GEMM
+ *                calls nothing else may write it, and calls sharing it must
+ *                be ordered on one stream.
  * Accuracy: |y - exact| <= 1e-3 * sum_k |x * w| + 1e-5 (fp32 accumulation).
  * An infinity or NaN in x[m] makes every output of row m non-finite: nvfp4
  * follows IEEE products and sums (+-inf, NaN where an infinity meets a zero

@@ -159,6 +159,42 @@ def test_rejection_on_peaked_logits(V):
         check_same(gpu_rej(z, q, d, u, 0.6, 0.95, 5), o[:3], f"peaked V={V} trial={trial}", o[3])
 
 
+def u_zero_case(path, trial):
+    """Std-300 logits (an LM head's spread) with u_{M-1} = 0: at T = 0.6 every
+    weight below the top one lies far under 2^-100 but is positive in fp64
+    (logit gaps below about 446), so the pick, the smallest index with a
+    positive weight, is usually not the argmax."""
+    rng = np.random.default_rng(900 + 10 * trial + (path == "residual"))
+    M, V = 8, 262144
+    z = (rng.standard_normal((M, V)) * 300.0).astype(np.float32)
+    q = W.rand_dirichlet_rows(rng, M - 1, V, 0.1)
+    d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+    if path == "residual":
+        a = trial + 1
+        d[a] = int(rng.integers(0, V))              # p'(x) ~ 0 < u * q(x): rejected
+        # a draft that gives no mass to a few ids the target still reaches:
+        # their residual is p' itself, positive but far below 2^-100
+        near = np.flatnonzero((z[a].max() - z[a]) < 300.0)
+        q[a, near[:3]] = 0.0
+    u = W.rand_uniforms(rng, M)
+    u[:M - 1] = 0.5
+    u[M - 1] = 0.0
+    return z, q, d, u
+
+
+@pytest.mark.parametrize("path", ["bonus", "residual"])
+def test_draw_with_u_zero_takes_the_first_positive_weight(path):
+    picks_off_argmax = 0
+    for trial in range(3):
+        z, q, d, u = u_zero_case(path, trial)
+        o = oracle.accept_rejection(z, q, d, u, 0.6, 1.0, 9, with_margins=True)
+        a = int(o[1][0])
+        assert (a < len(d)) == (path == "residual")
+        picks_off_argmax += int(o[0][a] != oracle.argmax(z[a]))
+        check_same(gpu_rej(z, q, d, u, 0.6, 1.0, 9), o[:3], f"u=0 {path} trial={trial}", o[3])
+    assert picks_off_argmax > 0     # the case exercises weights below 2^-100
+
+
 def test_same_trials_as_the_oracle_law():
     # The GPU reproduces the oracle trial by trial on the uniforms the oracle's
     # chi-square tests use, so the sampling law checked there holds here too.

@@ -209,6 +209,95 @@ def test_nvfp4_activations_outside_fp16_range(M):
     assert_gemm_close(y, y_ref, b_ref, "tiny activations")
 
 
+def positive_nvfp4(N, K, seed):
+    """nvfp4 weights with positive codes only (E2M1 0.5 .. 6), so that the
+    products of same-signed activations never cancel."""
+    rng = np.random.default_rng(seed)
+    nib = rng.integers(1, 8, size=(N, K))
+    sc = W.to_e4m3_bits(np.exp2(rng.uniform(-4, 2, size=(N, K // 16))).astype(np.float32))
+    return {"format": W.FMT_NVFP4, "N": N, "K": K, "codes": pack_nibbles(nib), "scales": sc,
+            "g": 1.0}
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_nvfp4_tiny_same_signed_activations(M):
+    # bf16 magnitudes below 2^-17 have bits below the fp16 subnormal spacing
+    # (2^-24).  Same-signed rows against positive weights add every
+    # truncation error with one sign, so a lossy fp16 copy misses the bound
+    # by several times; the staging must keep them exact.
+    N, K = 160, 4096
+    w = positive_nvfp4(N, K, seed=41)
+    rng = np.random.default_rng(42)
+    xf = np.empty((M, K), np.float32)
+    xf[0] = 1.0078125 * 2.0 ** -18                       # 2^-18 + 2^-25
+    if M > 1:
+        xf[1:] = np.exp2(rng.uniform(-24, -17, size=(M - 1, K)))   # uniform in exponent
+        xf[2:4] = rng.uniform(2.0 ** -24, 2.0 ** -17, size=(2, K))
+        xf[4:] *= -1.0
+    x = W.to_bf16_bits(xf)
+    y = gemm_gpu(bv, w, x)
+    y_ref, b_ref = oracle.gemm(w, x)
+    assert_gemm_close(y, y_ref, b_ref, "tiny same-signed activations")
+
+
+def test_nvfp4_tiny_one_hot_reads_largest_weight_exactly():
+    # one activation (1 + 2^-7) * 2^-20 against weight 6 * 448 = 2688 (code 7,
+    # scale 0x7E): the product is exact in fp32, so the result must be too
+    N, K = 32, 512
+    nib = np.full((N, K), 7)
+    sc = np.full((N, K // 16), 0x7E, np.uint8)
+    w = {"format": W.FMT_NVFP4, "N": N, "K": K, "codes": pack_nibbles(nib), "scales": sc,
+         "g": 1.0}
+    xf = np.zeros((4, K), np.float32)
+    for m, k in enumerate((0, 129, 300, 511)):
+        xf[m, k] = (1.0 + 2.0 ** -7) * 2.0 ** -20 * (-1.0 if m % 2 else 1.0)
+    x = W.to_bf16_bits(xf)
+    y = gemm_gpu(bv, w, x)
+    y_ref, _ = oracle.gemm(w, x)
+    assert np.array_equal(y, y_ref)
+    assert y_ref[0, 0] == 2688.0 * (1.0 + 2.0 ** -7) * 2.0 ** -20
+
+
+@pytest.mark.parametrize("scale_exp", [-40, -20, 18, 60])
+@pytest.mark.parametrize("M", [1, 8])
+def test_nvfp4_scaled_exact_regime_bitwise(scale_exp, M):
+    # integer activations times 2^scale_exp with power-of-two weight scales:
+    # every product and partial sum is exact in fp32, so the GPU must match
+    # the oracle bit for bit when the activations lie outside the fp16 window
+    # (below 2^-17 or from 65536 up) as well as inside it
+    N, K = 96, 2048
+    rng = np.random.default_rng(43 + M)
+    xf = rng.integers(-4, 5, size=(M, K)).astype(np.float64) * 2.0 ** scale_exp
+    x = W.to_bf16_bits(xf.astype(np.float32))
+    nib = rng.integers(0, 16, size=(N, K))
+    sc = W.to_e4m3_bits(np.exp2(rng.integers(-1, 3, size=(N, K // 16))).astype(np.float32))
+    w = {"format": W.FMT_NVFP4, "N": N, "K": K, "codes": pack_nibbles(nib), "scales": sc,
+         "g": 1.0}
+    y = gemm_gpu(bv, w, x)
+    y_ref, _ = oracle.gemm(w, x)
+    assert np.array_equal(y, y_ref)
+
+
+def test_nvfp4_subnormal_and_mixed_range_activations():
+    # bf16 subnormals (below 2^-126) alone, and rows spanning more than the
+    # 33 binades one fp16 scale can hold (1e4 next to 1e-7: bf16 path)
+    N, K, M = 200, 1024, 4
+    w = weight(W.FMT_NVFP4, N, K, seed=44)
+    rng = np.random.default_rng(45)
+    xf = rng.integers(-4, 5, size=(M, K)).astype(np.float32) * np.float32(2.0 ** -130)
+    x = W.to_bf16_bits(xf)
+    y = gemm_gpu(bv, w, x)
+    y_ref, b_ref = oracle.gemm(w, x)
+    assert_gemm_close(y, y_ref, b_ref, "subnormal activations")
+    xf = rng.normal(size=(M, K)).astype(np.float32)
+    xf[:, 3] = 1.0e4
+    xf[:, 10:200] = 1.0e-7 * rng.normal(size=(M, 190))
+    x = W.to_bf16_bits(xf)
+    y = gemm_gpu(bv, w, x)
+    y_ref, b_ref = oracle.gemm(w, x)
+    assert_gemm_close(y, y_ref, b_ref, "mixed-range activations")
+
+
 def test_deterministic_across_calls():
     N, K, M = 5120, 17408, 8          # K split over workgroups
     assert bv.gemm_plan_info(W.FMT_Q4_0, M, N, K)["KG"] > 1
@@ -226,6 +315,28 @@ def test_deterministic_across_calls():
     y1 = ys[0]
     y_ref, b_ref = oracle.gemm(w, x, cols=np.arange(0, N, 7))
     assert_gemm_close(y1[:, ::7], y_ref, b_ref, "q4 down")
+
+
+def test_one_workspace_serves_several_shapes():
+    # K-split plans of different shapes in turn on one zeroed workspace: the
+    # partial sums one shape leaves behind must not act as another shape's
+    # arrival counters (small T first, then a larger T, then back)
+    shapes = [(W.FMT_Q4_0, 512, 17408), (W.FMT_Q4_0, 5120, 17408), (W.FMT_NVFP4, 1024, 17408),
+              (W.FMT_Q4_0, 512, 17408)]
+    M = 4
+    for fmt, N, K in shapes:
+        assert bv.gemm_plan_info(fmt, M, N, K)["KG"] > 1, (N, K)
+    need = max(bv.gemm_workspace_bytes(N, K) for _, N, K in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, (fmt, N, K) in enumerate(shapes):
+        log("shared workspace", i, FNAME[fmt], N, K)
+        w = weight(fmt, N, K, seed=50 + i)
+        x = W.rand_bf16(np.random.default_rng(60 + i), (M, K))
+        y, _ = bv.verify_gemm(fmt, dev(x), pack_gpu(bv, w), N, K, ws=ws)
+        cols = np.arange(0, N, 5)
+        y_ref, b_ref = oracle.gemm(w, x, cols=cols)
+        assert_gemm_close(host(y).astype(np.float64)[:, cols], y_ref, b_ref, f"shape {i}")
+    assert not host(ws)[:256 * 1024].any()
 
 
 # ---------------------------------------------------------------------------

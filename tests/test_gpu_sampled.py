@@ -58,7 +58,8 @@ def check(z, drafts, u, par, what, **kw):
             if not (np.array_equal(got[:n], order) and np.all(got[n:] == -1)):
                 raise AssertionError(f"{what}: row ({b},{i}) kept {got[:n + 2].tolist()} "
                                      f"oracle {order[:n + 2].tolist()} margins {om[b].tolist()}")
-            assert np.allclose(gp[b, i, :n], p[order], rtol=2e-6, atol=0), what
+            # (fp32 output: below its subnormal range a probability reads 0)
+            assert np.allclose(gp[b, i, :n], p[order], rtol=2e-6, atol=2.0 ** -149), what
             assert np.all(gp[b, i, n:] == 0) and n <= K
     ok = np.array_equal(gt, ot) and np.array_equal(gc, oc) and np.array_equal(gr, orb)
     if not ok:
@@ -122,6 +123,37 @@ def test_sampled_matches_oracle(B, M, V, par):
             check(z, d, u, par, f"dense q trial {trial}", q=q if M > 1 else None,
                   q_sparse=None if M > 1 else (np.zeros((B, 0, 1), np.int32),) * 2,
                   history=hist, base_len=bl)
+
+
+@pytest.mark.parametrize("path", ["bonus", "residual"])
+def test_sampled_draw_with_u_zero_takes_the_first_positive_weight(path):
+    # u_{M-1} = 0: the pick is the kept id of smallest index whose weight is
+    # positive in fp64.  Std-100 logits at T = 0.6 with the top 1024 kept put
+    # nearly every kept weight far below 2^-100 while still positive.
+    par = oracle.sampler(temperature=0.6, top_k=1024)
+    off = 0
+    for trial in range(3):
+        rng = np.random.default_rng(700 + 10 * trial + (path == "residual"))
+        B, M, V = 2, 8, 65536
+        z = (rng.standard_normal((B, M, V)) * 100.0).astype(np.float32)
+        d = np.argmax(z[:, :M - 1], axis=2).astype(np.int32)
+        if path == "residual":
+            d[:, trial + 1] = rng.integers(0, V, B)
+        q = np.stack([W.rand_dirichlet_rows(rng, M - 1, V, 0.1) for _ in range(B)])
+        if path == "residual":
+            # no draft mass on the three smallest kept ids: their residual is
+            # p' itself, positive but far below 2^-100
+            for b in range(B):
+                kept = np.argsort(-z[b, trial + 1], kind="stable")[:1024]
+                q[b, trial + 1, np.sort(kept)[:3]] = 0.0
+        u = np.full((B, M), 0.5, np.float32)
+        u[:, M - 1] = 0.0
+        o = oracle.accept_sampled(z, d, u, par, q=q)
+        for b in range(B):
+            a = int(o[1][b][0])
+            off += int(o[0][b][a] != np.argmax(z[b, a]))
+        check(z, d, u, par, f"u=0 {path} trial {trial}", q=q)
+    assert off > 0
 
 
 def test_draft_ids_out_of_range_are_rejected():
