@@ -20,14 +20,20 @@ Method:
 * weights are packed once (mtp_pack_weights, outside the timed region);
 * R rotating copies of the weights (R * bytes >= 1 GiB, four times the
   256 MiB Infinity Cache) so every call streams its weights from HBM;
-* the calls are captured once in a HIP graph (torch.cuda.CUDAGraph) and
-  replayed; K timed steps are bracketed by torch.cuda.synchronize();
-* HIP events recorded on the launch stream around the timed replays give
-  the average duration per launch (including the gaps between launches);
+* the headline captures exactly W warm-up calls and exactly K timed calls
+  (--warmup, --steps) in two HIP graphs (torch.cuda.CUDAGraph); the timed
+  graph is replayed once, bracketed by torch.cuda.synchronize(), and HIP
+  events recorded on the launch stream around it give the time of the K
+  calls (including the gaps between launches).  `value`, `ms_per_step` and
+  `roofline.achieved` all come from that one clock; a sustained figure over
+  at least 20 ms of back-to-back calls is reported beside it, and the
+  in-kernel average of the committed rocprofv3 trace of the same kernel;
 * effective GB/s = algorithmic weight bytes (4-bit codes + block scales,
   9/16 byte per weight) / time;
-* the CPU oracle (fp64, 16 host threads at most) runs repeated passes of
-  the same workload for a bounded sample as the baseline.
+* the CPU oracle (fp64) runs repeated whole passes of the same workload for
+  a bounded sample as the baseline, on the host threads this process may
+  use (the OMP_NUM_THREADS share where it is set, else every core of its
+  affinity mask); os.cpu_count() is reported beside it.
 """
 from __future__ import annotations
 
@@ -50,6 +56,9 @@ import workloads as W  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nvfp4_4096x14336_m8_pmc.md")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nvfp4_4096x14336_m8_kernel_trace.md")
+SUSTAIN_S = 0.020                 # the sustained figure's timed region, at least
+ONLY = ("all", "headline", "sweep", "c0", "c2", "c3", "moe", "attn", "kv", "ceiling")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_verify_gemm_amd", "csrc", f)
                   for f in ("engine.h", "device.h", "gemm.hip")]
 
@@ -57,15 +66,20 @@ KERNEL_SOURCES = [os.path.join(ROOT, "bit_verify_gemm_amd", "csrc", f)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=2400,
+                    help="headline calls timed (exactly this many; 2400 take about 22 ms)")
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--m", type=int, default=8, help="rows of the headline pass")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1/2/4 sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (Q4_0 layer, LM head + accept, MoE)")
     ap.add_argument("--only-headline", action="store_true",
-                    help="time the headline GEMM only (for profiler runs)")
+                    help="time the headline GEMM only (for profiler runs; = --only headline)")
+    ap.add_argument("--only", choices=ONLY, default="all",
+                    help="the headline and one other workload (for profiler runs)")
+    ap.add_argument("--sustain-ms", type=float, default=SUSTAIN_S * 1e3,
+                    help="timed region of the sustained figure (0: skip it, for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for PMC scaling)")
     return ap.parse_args()
@@ -108,6 +122,47 @@ class Graphed:
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * self.R)
+
+
+def capture(calls, idx):
+    """A HIP graph of calls(i) for i in idx (the launch path warmed first)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in idx[:4]:
+            calls(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in idx:
+            calls(i)
+    return g
+
+
+def time_exact(calls, R, steps, warmup):
+    """Exactly `warmup` untimed calls, then exactly `steps` timed calls, each
+    set captured in one graph; call i uses rotating copy i mod R, and the
+    warm-up takes the copies just before copy 0 so that the timed calls
+    start on the least recently read ones.  Returns (seconds by HIP events
+    on the replay stream, wall seconds), both around the one timed replay."""
+    gw = capture(calls, [(R - warmup % R + i) % R for i in range(warmup)]) if warmup else None
+    gk = capture(calls, [i % R for i in range(steps)])
+    for i in range(R):                     # every copy read once, in order
+        calls(i)
+    if gw is not None:
+        gw.replay()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    gk.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) * 1e-3, wall
 
 
 def time_graph(calls, R, steps, warmup):
@@ -165,13 +220,23 @@ def gemm_from_host(bv, w, x, M, dev):
                 w["K"], dev_bits(x[:M], dev), dev, float(w.get("g", 1.0)))
 
 
+def host_threads():
+    """The host threads this process may use: its OMP_NUM_THREADS share
+    where one is set (the GPU hosts give each GPU a share of their cores),
+    else every core of its affinity mask."""
+    aff = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(omp) if omp.isdigit() and int(omp) > 0 else aff
+    return max(1, min(n, aff)), aff
+
+
 def cpu_baseline(cfg, M, budget_s=1.5):
     """The oracle as it stands, on repeated whole passes of the workload
-    until about budget_s of wall time (16 host threads at most)."""
+    until about budget_s of wall time, on host_threads() threads."""
     import oracle
     w = cfg["w"]
     x = cfg["x"][:M]
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, aff = host_threads()
     oracle.gemm(w, x, nthreads=threads)                # load and warm
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -184,7 +249,10 @@ def cpu_baseline(cfg, M, budget_s=1.5):
             "cores": threads, "kind": "oracle",
             "sample": f"{reps} whole passes of the workload (M={M}, K={w['K']}, N={w['N']}, "
                       f"fp64 sums with the |x*w| bound) in {t:.2f} s wall on {threads} threads "
-                      f"(about {t * threads:.0f} CPU-seconds)"}
+                      f"(about {t * threads:.0f} CPU-seconds; the process may use {aff} cores, "
+                      f"OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', 'unset')}, "
+                      f"os.cpu_count()={os.cpu_count()})",
+            "host_cpu_count": os.cpu_count(), "affinity_cores": aff}
 
 
 def kernel_source_hash():
@@ -193,6 +261,20 @@ def kernel_source_hash():
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def trace_average_ns():
+    """The headline kernel's average duration in the committed rocprofv3
+    kernel trace, if it was taken on the current kernel sources; else None."""
+    try:
+        text = open(TRACE_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"headline_kernel_average_ns:\s*([0-9.]+)", text)
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return float(m.group(1))
 
 
 def pmc_traffic():
@@ -257,6 +339,85 @@ def extra_q4_layer(bv, dev, steps, warmup):
     return out
 
 
+def extra_c0_chain(bv, dev, steps, warmup):
+    """The tiny verify pass end to end: x[4][2048] -> nvfp4 2048x2048 (bf16
+    output) -> nvfp4 head 2048 -> 1024 -> greedy acceptance of 3 drafts, as
+    one chain of launches per call, over rotating copies of both matrices."""
+    c = W.config0()
+    M, V = c["M"], c["V"]
+    b1, b2 = W.weight_bytes(2048, 2048), W.weight_bytes(V, 2048)
+    R = max(2, -(-ROTATE_BYTES // (b1 + b2)))
+    p1 = bv.pack_weights(bv.FMT_NVFP4, dev_bits(c["w1"]["codes"], dev),
+                         dev_bits(c["w1"]["scales"], dev), 2048, 2048)
+    p2 = bv.pack_weights(bv.FMT_NVFP4, dev_bits(c["head"]["codes"], dev),
+                         dev_bits(c["head"]["scales"], dev), V, 2048)
+    w1s = [p1] + [p1.clone() for _ in range(R - 1)]
+    w2s = [p2] + [p2.clone() for _ in range(R - 1)]
+    x = dev_bits(c["x"], dev)
+    yb = torch.empty((M, 2048), dtype=torch.int16, device=dev)
+    z = torch.empty((M, V), dtype=torch.float32, device=dev)
+    d = torch.from_numpy(c["drafts"]).to(dev)
+    outs = (torch.empty(M, dtype=torch.int32, device=dev),
+            torch.empty(2, dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int64, device=dev))
+    ws = bv.accept_workspace(M, V, dev)
+
+    def chain(i):
+        bv.verify_gemm(bv.FMT_NVFP4, x, w1s[i % R], 2048, 2048, 1.0, y_bf16=yb, want_fp32=False)
+        bv.verify_gemm(bv.FMT_NVFP4, yb, w2s[i % R], V, 2048, 1.0, y=z)
+        bv.accept_greedy(z, d, 100, outs=outs, ws=ws)
+
+    _, ms, n = time_graph(chain, R, max(R, steps // 4), max(R, warmup // 4))
+    res = {"M": M, "K": 2048, "N": 2048, "V": V, "weight_bytes": b1 + b2,
+           "us_per_pass": round(ms * 1e3, 3), "gbs": round((b1 + b2) / (ms * 1e-3) / 1e9, 1),
+           "launches_per_pass": 4, "passes_timed": n}
+    del w1s, w2s
+    torch.cuda.empty_cache()
+    return res
+
+
+def extra_q4_layer_sweep(bv, dev, steps, warmup):
+    """The 27B-class Q4_0 layer as a decoder runs it (Q|K|V and gate|up fused
+    along N: four launches), one graph per row count M = 1, 2, 4, 8, over
+    rotating copies of the whole layer."""
+    cfg = W.config2(M=8)
+    P = cfg["proj"]
+    mats = []
+    for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        ws = [P[n]["w"] for n in names]
+        fw = {"format": W.FMT_Q4_0, "K": ws[0]["K"], "N": sum(w["N"] for w in ws),
+              "codes": np.concatenate([w["codes"] for w in ws]),
+              "scales": np.concatenate([w["scales"] for w in ws])}
+        mats.append((fw, P[names[0]]["x"]))
+    layer_bytes = sum(W.weight_bytes(fw["N"], fw["K"]) for fw, _ in mats)
+    R = max(2, -(-ROTATE_BYTES // layer_bytes))
+    packed = []
+    for fw, _ in mats:
+        pk = bv.pack_weights(W.FMT_Q4_0, dev_bits(fw["codes"], dev), dev_bits(fw["scales"], dev),
+                             fw["N"], fw["K"])
+        packed.append([pk] + [pk.clone() for _ in range(R - 1)])
+    wss = [bv.gemm_workspace(fw["N"], fw["K"], dev) for fw, _ in mats]
+    out = {"bytes": layer_bytes, "launches": 4}
+    for M in (1, 2, 4, 8):
+        xs = [dev_bits(x[:M], dev) for _, x in mats]
+        ys = [torch.empty((M, fw["N"]), dtype=torch.float32, device=dev) for fw, _ in mats]
+
+        def layer(i, xs=xs, ys=ys):
+            for j, (fw, _) in enumerate(mats):
+                bv.verify_gemm(W.FMT_Q4_0, xs[j], packed[j][i % R], fw["N"], fw["K"], 1.0,
+                               y=ys[j], ws=wss[j])
+
+        _, ms, _ = time_graph(layer, R, max(4 * R, steps // 16), max(R, warmup // 16))
+        out[str(M)] = {"us": round(ms * 1e3, 3),
+                       "gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                       "plans": [{k: bv.gemm_plan_info(W.FMT_Q4_0, M, fw["N"], fw["K"])[k]
+                                  for k in ("S", "J", "KG", "TW", "grid")} for fw, _ in mats]}
+    out["m8_over_m1_time"] = round(out["8"]["us"] / out["1"]["us"], 4)
+    del packed
+    torch.cuda.empty_cache()
+    return out
+
+
 def extra_lm_head_and_accept(bv, dev, steps, warmup):
     c = W.config3_inputs(M=8)
     M, V = c["M"], c["V"]
@@ -308,12 +469,26 @@ def extra_lm_head_and_accept(bv, dev, steps, warmup):
         bv.accept_sampled(logits, d1, u1, sp, draft_probs=q1, history=hist, history_len=hlen,
                           outs=souts, ws=sws)
 
+    # the same step on logits ~ N(0,1) (a nucleus of many thousand tokens,
+    # unlike the head's own logits, whose nucleus is mostly one token)
+    zs = torch.from_numpy(W.spread_logits(3, M, V)).to(dev)
+    ams = np.argmax(W.spread_logits(3, M, V), axis=1).astype(np.int32)
+    dds = torch.from_numpy(W.plant_drafts(ams, c["L"], c["filler"], c["miss"], V)).to(dev)
+
+    def rejection_spread(i):
+        bv.accept_rejection(zs, q, dds, u, c["temperature"], c["top_p"], 100, outs=outs, ws=ws)
+
     _, ms_g, _ = time_graph(greedy, 16, max(64, steps // 4), 32)
     _, ms_r, _ = time_graph(rejection, 16, max(64, steps // 4), 32)
+    _, ms_rs, _ = time_graph(rejection_spread, 16, max(64, steps // 4), 32)
     _, ms_s, _ = time_graph(sampled, 16, max(64, steps // 4), 32)
     out["accept_greedy"] = {"M": M, "V": V, "us": round(ms_g * 1e3, 3), "planted_L": c["L"]}
     out["accept_rejection"] = {"M": M, "V": V, "us": round(ms_r * 1e3, 3),
                                "temperature": c["temperature"], "top_p": c["top_p"]}
+    out["accept_rejection_spread_logits"] = {"M": M, "V": V, "us": round(ms_rs * 1e3, 3),
+                                             "logits": "N(0,1)",
+                                             "temperature": c["temperature"],
+                                             "top_p": c["top_p"]}
     out["accept_sampled"] = {"B": 1, "M": M, "V": V, "us": round(ms_s * 1e3, 3),
                              "temperature": c["temperature"], "top_p": c["top_p"],
                              "top_k": 64, "min_p": 0.01, "repeat_penalty": 1.1,
@@ -344,12 +519,23 @@ def extra_moe(bv, dev, steps, warmup):
     def call(i):
         bv.verify_moe(gu["format"], x, ids, gw, gups[i % R], dnps[i % R], E, F, out=out_t, ws=ws)
 
+    # the M = 1 baseline: the first token alone (its 8 experts)
+    ws1 = torch.empty(bv.moe_workspace_bytes(1, H, F, E, topk), dtype=torch.uint8, device=dev)
+    out1 = torch.empty((1, H), dtype=torch.float32, device=dev)
+
+    def call1(i):
+        bv.verify_moe(gu["format"], x[:1], ids[:1], gw[:1], gups[i % R], dnps[i % R], E, F,
+                      out=out1, ws=ws1)
+
     _, ms, _ = time_graph(call, R, max(40, steps // 10), 10)
+    _, ms1, _ = time_graph(call1, R, max(40, steps // 10), 10)
     uniq = len(np.unique(c["ids"]))
     ub = uniq * per_expert
     return {"T": T, "E": E, "topk": topk, "H": H, "F": F, "unique_experts": uniq,
             "unique_bytes": ub, "us": round(ms * 1e3, 3), "gbs": round(ub / (ms * 1e-3) / 1e9, 1),
-            "m1_gemv_bytes": topk * per_expert, "no_dedup_bytes": T * topk * per_expert}
+            "m1_gemv_bytes": topk * per_expert, "m1_us": round(ms1 * 1e3, 3),
+            "m1_gbs": round(topk * per_expert / (ms1 * 1e-3) / 1e9, 1),
+            "t8_over_m1_time": round(ms / ms1, 4), "no_dedup_bytes": T * topk * per_expert}
 
 
 def extra_verify_attention(bv, dev, steps, warmup):
@@ -478,79 +664,119 @@ def main():
         print("bench.py measures one GPU only (the verify pass here has no multi-GPU "
               "path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    only = "headline" if args.only_headline else args.only
+    want = lambda name: only == name or (only == "all" and not args.no_extra)  # noqa: E731
     import bit_verify_gemm_amd as bv
     bv.lib()
     dev = torch.device("cuda:0")
     cfg = W.config1(M=8)
     M = args.m
 
+    # headline: exactly --steps calls, one HIP-event clock
     head = gemm_from_host(bv, cfg["w"], cfg["x"], M, dev)
-    wall, per_call_ms, ncalls = time_graph(head, head.R, args.steps, args.warmup)
+    t_ev, t_wall = time_exact(head, head.R, args.steps, args.warmup)
     bytes_call = head.bytes
-    value = bytes_call * ncalls / wall / 1e9
-    achieved = bytes_call / (per_call_ms * 1e-3) / 1e9
+    value = bytes_call * args.steps / t_ev / 1e9
     plan = bv.gemm_plan_info(bv.FMT_NVFP4, M, cfg["w"]["N"], cfg["w"]["K"])
+    # beside it: at least 20 ms of back-to-back calls (whole replays of the
+    # rotating copies)
+    per = t_ev / args.steps
+    sustained = None
+    if args.sustain_ms > 0:
+        g = Graphed(head, head.R)
+        g.ms_per_call(head.R)
+        n_sus = max(head.R, int(args.sustain_ms * 1e-3 / per) + 1)
+        ms_sus = g.ms_per_call(n_sus)
+        n_sus = -(-n_sus // head.R) * head.R
+        sustained = {"calls": n_sus, "timed_ms": round(ms_sus * n_sus, 3),
+                     "us_per_call": round(ms_sus * 1e3, 3),
+                     "gbs": round(bytes_call / (ms_sus * 1e-3) / 1e9, 1)}
+        del g
 
     # M sweep: the row counts take turns in 5 rounds and each reports its
     # median, so that clock drift between separate measurements does not
     # enter the ratios between them
     sweep = {}
-    if not args.no_sweep and not args.only_headline:
+    if only in ("all", "sweep") and not args.no_sweep:
         ms_of = {m: [] for m in (1, 2, 4, 8)}
         runners = {m: gemm_from_host(bv, cfg["w"], cfg["x"], m, dev) for m in ms_of}
         graphs = {m: Graphed(r, r.R) for m, r in runners.items()}
-        for g in graphs.values():
-            g.ms_per_call(args.warmup)
+        for gm in graphs.values():
+            gm.ms_per_call(gm.R)
+        n_each = max(runners[1].R, int(SUSTAIN_S / per / 4) + 1)
         for _ in range(5):
-            for m, g in graphs.items():
-                ms_of[m].append(g.ms_per_call(max(1, args.steps // 4)))
+            for m, gm in graphs.items():
+                ms_of[m].append(gm.ms_per_call(n_each))
         for m, v in ms_of.items():
             ms = float(np.median(v))
             sweep[str(m)] = {"us_per_call": round(ms * 1e3, 3),
-                             "gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1)}
+                             "gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1),
+                             "frac_of_hbm_peak": round(bytes_call / (ms * 1e-3) / 1e9
+                                                       / PEAK_HBM_GBS, 4)}
         del graphs, runners
         torch.cuda.empty_cache()
 
+    steps_x, warm_x = 2000, 2000      # call counts of the other workloads' timings
     extra = {}
-    if not args.no_extra and not args.only_headline:
-        extra["q4_0_layer_27b_m8"] = extra_q4_layer(bv, dev, args.steps, args.warmup)
-        extra["lm_head_5376x262144_m8"] = extra_lm_head_and_accept(bv, dev, args.steps,
-                                                                   args.warmup)
-        extra["moe_8tok_128x_top8"] = extra_moe(bv, dev, args.steps, args.warmup)
-        extra["verify_attention_32k"] = extra_verify_attention(bv, dev, args.steps, args.warmup)
-        extra["kv_rollback_52x16x128"] = extra_kv_rollback(bv, dev, args.steps, args.warmup)
+    if want("c0"):
+        extra["c0_tiny_chained_pass"] = extra_c0_chain(bv, dev, steps_x, warm_x)
+    if want("c2"):
+        extra["q4_0_layer_27b_m8"] = extra_q4_layer(bv, dev, steps_x, warm_x)
+        extra["q4_0_layer_27b_fused_m_sweep"] = extra_q4_layer_sweep(bv, dev, steps_x, warm_x)
+    if want("c3"):
+        extra["lm_head_5376x262144_m8"] = extra_lm_head_and_accept(bv, dev, steps_x, warm_x)
+    if want("moe"):
+        extra["moe_8tok_128x_top8"] = extra_moe(bv, dev, steps_x, warm_x)
+    if want("attn"):
+        extra["verify_attention_32k"] = extra_verify_attention(bv, dev, steps_x, warm_x)
+    if want("kv"):
+        extra["kv_rollback_52x16x128"] = extra_kv_rollback(bv, dev, steps_x, warm_x)
 
     ceiling = None
-    if not args.no_extra and not args.only_headline:
-        ceiling = read_ceiling(bv, dev, args.steps, args.warmup)
-        ceiling["c1_frac_of_33mb_ceiling"] = round(achieved / ceiling["33mb"]["gbs"], 4)
+    if want("ceiling"):
+        ceiling = read_ceiling(bv, dev, steps_x, warm_x)
+        ceiling["c1_frac_of_33mb_ceiling"] = round(value / ceiling["33mb"]["gbs"], 4)
+        if sustained:
+            ceiling["c1_sustained_frac_of_33mb_ceiling"] = round(sustained["gbs"]
+                                                                 / ceiling["33mb"]["gbs"], 4)
 
     if args.copy_calibration:
         copy_calibration(dev)
 
     traffic = pmc_traffic()
+    trace_ns = trace_average_ns()
     out = {
         "metric": "effective weight GB/s (% of HBM peak) for nvfp4 verify GEMM at M=1/2/4/8",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": ncalls,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / ncalls * 1e3, 6),
+        "ms_per_step": round(t_ev / args.steps * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": f"nvfp4 verify GEMM, dense FFN-up K=4096 -> N=14336, M={M} "
-                               f"bf16 rows (staged as fp16, exact), fp32 accumulate",
+                               f"bf16 rows (staged exactly as fp16), fp32 accumulate",
                    "M": M, "K": 4096, "N": 14336, "weight_bytes_per_call": bytes_call,
                    "rotating_weight_copies": head.R, "graph_replay": True,
+                   "timed_region_ms_hip_events": round(t_ev * 1e3, 4),
+                   "timed_region_ms_wall": round(t_wall * 1e3, 4),
                    "plan": {k: plan[k] for k in ("S", "J", "KG", "TW", "grid", "threads")}},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
     }
+    if sustained:
+        out["sustained"] = sustained
+    if trace_ns:
+        out["roofline"]["kernel_trace_avg_ns"] = trace_ns
+        out["roofline"]["kernel_trace_achieved"] = round(bytes_call / trace_ns, 1)
     if sweep:
         out["m_sweep"] = sweep
         if "1" in sweep and "8" in sweep:
@@ -560,7 +786,7 @@ def main():
         out["other_workloads"] = extra
     if ceiling:
         out["read_ceiling"] = ceiling
-    if not args.no_cpu and not args.only_headline:
+    if not args.no_cpu and only == "all":
         out["cpu_baseline"] = cpu_baseline(cfg, M)
     print(json.dumps(out), flush=True)
 
