@@ -22,7 +22,8 @@ __all__ = [
     "choose_draft_depth", "DepthStats", "verify_attention", "attention_workspace_bytes",
     "kv_snapshot", "kv_append", "kv_restore", "read_probe",
     "read_probe_shapes",
-    "verify_gemm", "verify_moe", "accept_greedy", "accept_rejection", "LIB_PATH",
+    "verify_gemm", "verify_moe", "accept_greedy", "accept_greedy_static", "accept_rejection",
+    "LIB_PATH",
 ]
 
 FMT_NVFP4 = 1
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.mtp_accept_workspace_bytes.argtypes = [i32, i32]
         L.mtp_accept_greedy.restype = i32
         L.mtp_accept_greedy.argtypes = [P, i32, i32, i64, P, i64, P, P, P, P, sz, P]
+        L.mtp_accept_greedy_static.restype = i32
+        L.mtp_accept_greedy_static.argtypes = [P, i32, i32, i64, P, i64, P, P, P, P]
         L.mtp_accept_rejection.restype = i32
         L.mtp_accept_rejection.argtypes = [P, i32, i32, i64, P, i64, P, P, f32, f32, i64, P, P, P,
                                            P, sz, P]
@@ -248,6 +251,18 @@ def accept_greedy(logits: torch.Tensor, draft_ids: torch.Tensor | None, base_len
     _check(lib().mtp_accept_greedy(_ptr(logits), M, V, _ld(logits), _ptr(draft_ids),
                                    int(base_len), _ptr(tok), _ptr(cnt), _ptr(rb), _ptr(ws),
                                    _nbytes(ws), _stream(stream)))
+    return tok, cnt, rb
+
+
+def accept_greedy_static(logits: torch.Tensor, draft_ids: torch.Tensor | None,
+                         base_len: int = 0, outs=None, stream=None):
+    """mtp_accept_greedy on the library's static scratch (no workspace).
+    Returns (tokens[M] int32, counts[2] int32, rollback[1] int64) on the GPU."""
+    M, V = logits.shape
+    tok, cnt, rb = _accept_outputs(M, logits.device, outs)
+    _check(lib().mtp_accept_greedy_static(_ptr(logits), M, V, _ld(logits), _ptr(draft_ids),
+                                          int(base_len), _ptr(tok), _ptr(cnt), _ptr(rb),
+                                          _stream(stream)))
     return tok, cnt, rb
 
 

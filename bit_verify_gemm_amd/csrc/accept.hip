@@ -19,6 +19,7 @@
 // select over the order-preserving 32-bit key of each logit, with per-digit
 // mass histograms; ties at the cut are broken by index.
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/mtp_verify.h"
 #include "device.h"
@@ -1597,15 +1598,15 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
 
 size_t accept_ws_bytes(int M, int V) { return layout(M, V).bytes; }
 
-hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
-                                const int32_t *drafts, int64_t base_len, int32_t *tokens,
-                                int32_t *counts, int64_t *rollback, void *ws, hipStream_t stream) {
-  const Layout L = layout(M, V);
+namespace {
+
+// The two greedy kernels on the per-block partial maxima pv/pj (M x nb each).
+hipError_t launch_greedy_parts(const float *logits, int M, int V, int64_t ldl,
+                               const int32_t *drafts, int64_t base_len, int32_t *tokens,
+                               int32_t *counts, int64_t *rollback, float *pv, int *pj,
+                               hipStream_t stream) {
   const int nb = blocks_per_row(V);
   const int chunk = (V + nb - 1) / nb;
-  uint8_t *w = static_cast<uint8_t *>(ws);
-  float *pv = reinterpret_cast<float *>(w + L.gpart);
-  int *pj = reinterpret_cast<int *>(pv + (size_t)M * nb);
   hipLaunchKernelGGL(greedy_partial, dim3(nb, M), dim3(kBlock), 0, stream, logits, ldl, V, nb,
                      chunk, pv, pj);
   hipError_t e = hipGetLastError();
@@ -1613,6 +1614,68 @@ hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
   hipLaunchKernelGGL(greedy_final, dim3(1), dim3(kFinalThreads), 0, stream, pv, pj, M, nb, drafts,
                      base_len, tokens, counts, rollback);
   return hipGetLastError();
+}
+
+// ---- greedy acceptance without a caller workspace ----------------------------
+//
+// For callers that cannot allocate (graph capture, fixed serving loops): the
+// partial maxima live in this file-scope device array, one copy per GPU, kept
+// until the process ends; every call on a GPU overwrites its copy before
+// reading it, so nothing needs clearing, and calls that overlap on one GPU
+// race on it.  In host code the array's name stands for a host-side shadow,
+// not a device address: its device address is looked up once per device
+// (with that device current) and only that address reaches the kernels.
+constexpr size_t kStaticScratchBytes = 2 * sizeof(float) * kMaxRows * kMaxBlocksPerRow;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
+                                const int32_t *drafts, int64_t base_len, int32_t *tokens,
+                                int32_t *counts, int64_t *rollback, void *ws, hipStream_t stream) {
+  const Layout L = layout(M, V);
+  const int nb = blocks_per_row(V);
+  uint8_t *w = static_cast<uint8_t *>(ws);
+  float *pv = reinterpret_cast<float *>(w + L.gpart);
+  int *pj = reinterpret_cast<int *>(pv + (size_t)M * nb);
+  return launch_greedy_parts(logits, M, V, ldl, drafts, base_len, tokens, counts, rollback, pv,
+                             pj, stream);
+}
+
+size_t greedy_static_bytes(int M, int V) { return 2 * sizeof(float) * (size_t)M * blocks_per_row(V); }
+
+size_t greedy_static_max_bytes() { return kStaticScratchBytes; }
+
+hipError_t launch_accept_greedy_static(const float *logits, int M, int V, int64_t ldl,
+                                       const int32_t *drafts, int64_t base_len, int32_t *tokens,
+                                       int32_t *counts, int64_t *rollback, hipStream_t stream) {
+  if (greedy_static_bytes(M, V) > kStaticScratchBytes) return hipErrorInvalidValue;
+  void *p = nullptr;
+  const hipError_t e = scratch_address(&p);
+  if (e != hipSuccess) return e;
+  float *pv = static_cast<float *>(p);
+  int *pj = reinterpret_cast<int *>(pv + (size_t)M * blocks_per_row(V));
+  return launch_greedy_parts(logits, M, V, ldl, drafts, base_len, tokens, counts, rollback, pv,
+                             pj, stream);
 }
 
 hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ldl,

@@ -205,6 +205,27 @@ int mtp_accept_greedy(const float *logits, int M, int V, int64_t ldl, const int3
                     who);
 }
 
+int mtp_accept_greedy_static(const float *logits, int M, int V, int64_t ldl,
+                             const int32_t *draft_ids, int64_t base_len, int32_t *out_tokens,
+                             int32_t *out_counts, int64_t *out_rollback, void *stream) {
+  const char *who = "mtp_accept_greedy_static";
+  if (M < 1 || M > kMaxAcceptRows) return fail(MTP_ERR_SHAPE, "%s: M=%d out of [1, %d]", who, M, kMaxAcceptRows);
+  if (V < 1 || V > kMaxVocab) return fail(MTP_ERR_SHAPE, "%s: V=%d out of [1, %d]", who, V, kMaxVocab);
+  if (ldl < V) return fail(MTP_ERR_SHAPE, "%s: ldl=%lld < V=%d", who, (long long)ldl, V);
+  if (!logits || !out_tokens || !out_counts || !out_rollback)
+    return fail(MTP_ERR_NULL, "%s: logits and outputs are required", who);
+  if (M > 1 && !draft_ids) return fail(MTP_ERR_NULL, "%s: draft_ids required for M > 1", who);
+  if (!aligned(logits, 4)) return fail(MTP_ERR_ALIGN, "%s: logits must be 4-byte aligned", who);
+  const size_t need = mtp::greedy_static_bytes(M, V), have = mtp::greedy_static_max_bytes();
+  if (need > have)
+    return fail(MTP_ERR_SHAPE, "%s: M=%d, V=%d needs %zu bytes of scratch, the library holds %zu",
+                who, M, V, need, have);
+  return hip_status(mtp::launch_accept_greedy_static(logits, M, V, ldl, draft_ids, base_len,
+                                                     out_tokens, out_counts, out_rollback,
+                                                     static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
                          const float *draft_probs, int64_t ldq, const int32_t *draft_ids,
                          const float *uniforms, float temperature, float top_p, int64_t base_len,

@@ -79,6 +79,13 @@ hipError_t launch_accept_greedy(const float *logits, int M, int V, int64_t ldl,
                                 const int32_t *drafts, int64_t base_len, int32_t *tokens,
                                 int32_t *counts, int64_t *rollback, void *ws, hipStream_t stream);
 
+// Greedy acceptance on the library's own static device scratch (no workspace).
+size_t greedy_static_bytes(int M, int V);
+size_t greedy_static_max_bytes();
+hipError_t launch_accept_greedy_static(const float *logits, int M, int V, int64_t ldl,
+                                       const int32_t *drafts, int64_t base_len, int32_t *tokens,
+                                       int32_t *counts, int64_t *rollback, hipStream_t stream);
+
 hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ldl,
                                    const float *q, int64_t ldq, const int32_t *drafts,
                                    const float *u, float temperature, float top_p,

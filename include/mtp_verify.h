@@ -253,6 +253,24 @@ int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
 size_t mtp_accept_workspace_bytes(int M, int V);
 
 /*
+ * mtp_accept_greedy without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, fixed serving loops, harnesses
+ * that forbid allocation).  Same computation, outputs and argument rules as
+ * mtp_accept_greedy (1 <= M <= 64, 1 <= V <= 2^26, ldl >= V); its scratch
+ * (the per-block partial maxima, at most 64 KiB: 8 bytes per row per block
+ * of the row, 128 blocks per row at most) is a static device array inside
+ * the library, one per GPU, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no library allocator); a shape whose
+ * scratch would exceed the array is MTP_ERR_SHAPE.  Every call on a GPU
+ * writes that GPU's array before reading it, so nothing needs clearing, but
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and must be ordered by the caller.
+ */
+int mtp_accept_greedy_static(const float *logits, int M, int V, int64_t ldl,
+                             const int32_t *draft_ids, int64_t base_len, int32_t *out_tokens,
+                             int32_t *out_counts, int64_t *out_rollback, void *stream);
+
+/*
  * Sampler parameters of mtp_accept_sampled, applied in the order of the
  * Ollama mtp.go commit log's MLX sampler rework: (1) penalties, (2) top-k,
  * (3) temperature/softmax, (4) top-p, (5) min-p, (6) normalize,

@@ -128,6 +128,22 @@ def test_accept_rejects_bad_arguments():
                                   FAKE, FAKE, ws, need, None) == -1
 
 
+def test_accept_greedy_static_rejects_bad_arguments():
+    L = bv.lib()
+    FAKE = ctypes.c_void_p(0x1000)
+    args = lambda M=4, V=100, ldl=100, logits=FAKE, d=FAKE, t=FAKE: (  # noqa: E731
+        logits, M, V, ldl, d, 0, t, FAKE, FAKE, None)
+    assert L.mtp_accept_greedy_static(*args(M=0)) == -2
+    assert L.mtp_accept_greedy_static(*args(M=65)) == -2
+    assert L.mtp_accept_greedy_static(*args(V=0)) == -2
+    assert L.mtp_accept_greedy_static(*args(ldl=99)) == -2
+    assert L.mtp_accept_greedy_static(*args(logits=None)) == -1
+    assert L.mtp_accept_greedy_static(*args(d=None)) == -1
+    assert L.mtp_accept_greedy_static(*args(t=None)) == -1
+    assert L.mtp_accept_greedy_static(*args(logits=ctypes.c_void_p(0x1002))) == -3
+    assert b"mtp_accept_greedy_static" in L.mtp_last_error()
+
+
 def test_moe_rejects_bad_arguments():
     L = bv.lib()
     ws = ctypes.c_void_p(0x100000)
