@@ -58,7 +58,7 @@ ROTATE_BYTES = 1 << 30
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nvfp4_4096x14336_m8_pmc.md")
 TRACE_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nvfp4_4096x14336_m8_kernel_trace.md")
 SUSTAIN_S = 0.020                 # the sustained figure's timed region, at least
-ONLY = ("all", "headline", "sweep", "c0", "c2", "c3", "moe", "attn", "kv", "ceiling")
+ONLY = ("all", "headline", "sweep", "c0", "c2", "c3", "lmhead", "moe", "attn", "kv", "ceiling")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_verify_gemm_amd", "csrc", f)
                   for f in ("engine.h", "device.h", "gemm.hip")]
 
@@ -418,13 +418,15 @@ def extra_q4_layer_sweep(bv, dev, steps, warmup):
     return out
 
 
-def extra_lm_head_and_accept(bv, dev, steps, warmup):
+def extra_lm_head_and_accept(bv, dev, steps, warmup, gemm_only=False):
     c = W.config3_inputs(M=8)
     M, V = c["M"], c["V"]
     gm = gemm_from_host(bv, c["w"], c["x"], M, dev)
     _, ms, _ = time_graph(gm, gm.R, max(20, steps // 20), max(4, warmup // 20))
     out = {"lm_head": {"N": V, "K": c["K"], "us": round(ms * 1e3, 3),
                        "gbs": round(gm.bytes / (ms * 1e-3) / 1e9, 1)}}
+    if gemm_only:
+        return out
     gm(0)
     torch.cuda.synchronize()
     logits = gm.y
@@ -728,6 +730,9 @@ def main():
         extra["q4_0_layer_27b_fused_m_sweep"] = extra_q4_layer_sweep(bv, dev, steps_x, warm_x)
     if want("c3"):
         extra["lm_head_5376x262144_m8"] = extra_lm_head_and_accept(bv, dev, steps_x, warm_x)
+    elif only == "lmhead":      # the LM-head GEMM alone (for counter runs)
+        extra["lm_head_5376x262144_m8"] = extra_lm_head_and_accept(bv, dev, steps_x, warm_x,
+                                                                   gemm_only=True)
     if want("moe"):
         extra["moe_8tok_128x_top8"] = extra_moe(bv, dev, steps_x, warm_x)
     if want("attn"):

@@ -183,9 +183,9 @@ def accept_workspace_bytes(M: int, V: int) -> int:
 
 
 def accept_workspace(M: int, V: int, device) -> torch.Tensor:
-    """A workspace for the accept calls on M x V logits (it may be kept for
-    later calls of either kind and any shape that fits)."""
-    return torch.empty(accept_workspace_bytes(M, V), dtype=torch.uint8, device=device)
+    """A zero-filled workspace for the accept calls on M x V logits (it may
+    be kept for later calls of either kind and any shape that fits)."""
+    return torch.zeros(accept_workspace_bytes(M, V), dtype=torch.uint8, device=device)
 
 
 def _workspace(nbytes: int, device, ws):

@@ -196,11 +196,80 @@ constexpr int kBlkWords = 6;
 constexpr int kNone = 0x7FFFFFFF;
 
 struct Layout {
-  size_t maxp, zmax, hist, total, sel, rows, acc, blk, gpart, bytes;
+  size_t hdr, maxp, zmax, hist, total, sel, rows, acc, blk, gpart, ahist, above, ccount,
+      cand, wsum, bytes;
 };
+
+// The one-launch rejection kernel (rej_one): workgroups of kOneThreads, each
+// holding up to kOneChunk entries of one row in LDS; used when every row fits
+// in at most kMaxOneBlocks workgroups altogether (all resident at once, one
+// per compute unit).
+constexpr int kOneThreads = 1024;
+constexpr int kOneChunk = 8192;
+constexpr int kMaxOneBlocks = 256;
+constexpr int kXBins = 1024;          // approximate mass bins of the cut search
+// Workspace header (offset 0, the same for every shape): one 4 KiB page per
+// row and one for the call, so that the words workgroups wait on lie apart.
+// Row page: arrival counters of the mass pass, the candidate step and the
+// draw step; the row's tagged candidate-bin and state words; its
+// workgroups' tagged chunk maxima.  Call page: the count of rows whose draw
+// sums are in, an error word, the generation number of the last call.  Zero
+// before first use; every call of the one-launch kernel leaves the counters
+// zero and advances the generation number (the tagged words need no reset).
+constexpr int kPageWords = 512;
+constexpr int kRowCnt = 0, kRowCand = 1, kRowDraw = 2, kRowBins = 64, kRowState = 128,
+              kRowSlots = 256;
+constexpr int kCallRows = 0, kCallErr = 1, kCallGen = 2;
+constexpr int kHdrWords = (kMaxRows + 1) * kPageWords;
+static_assert(kRowSlots + kMaxOneBlocks <= kPageWords, "slots fit the row page");
+
+// LDS of rej_one for chunks of C entries: logits, e values, approximate bins.
+__host__ __device__ constexpr int one_e_offset(int C) { return (4 * C + 15) & ~15; }
+__host__ __device__ constexpr int one_b_offset(int C) { return one_e_offset(C) + 8 * C; }
+__host__ __device__ constexpr int one_lds_bytes(int C) { return one_b_offset(C) + 2 * C; }
+// Dynamic LDS of rej_one: the chunk, or (in the workgroup that resolves a
+// row's cut, once it no longer needs its chunk) one_cand_room candidates as
+// (key << 32 | index, e) pairs.
+constexpr int kCandLdsBytes = 96 * 1024;
+__host__ __device__ constexpr int one_dyn_bytes(int C) {
+  return one_lds_bytes(C) > kCandLdsBytes ? one_lds_bytes(C) : kCandLdsBytes;
+}
+__host__ __device__ constexpr int one_cand_room(int C) { return one_dyn_bytes(C) / 16; }
+
+// Workgroups per row of rej_one, or 0 where it does not apply: enough to
+// spread the rows over the compute units (at least 1024 entries each), with
+// at most kOneChunk entries each.
+int one_blocks_per_row(int M, int V) {
+  int G = std::max((V + kOneChunk - 1) / kOneChunk, std::min(kMaxOneBlocks / M, (V + 1023) / 1024));
+  if (G < 1) G = 1;
+  const int C = (V + G - 1) / G;
+  G = (V + C - 1) / C;   // no empty chunk
+  if (C > kOneChunk || (int64_t)M * G > kMaxOneBlocks) return 0;
+  return G;
+}
+
+// Room for rej_one's per-call regions at any row count up to M (so that a
+// workspace sized for M rows serves every smaller M): candidate entries,
+// workgroups and rows.
+struct OneRoom {
+  size_t cand, blocks, rows;
+};
+
+OneRoom one_room(int M, int V) {
+  OneRoom r{0, 0, 0};
+  for (int m = 1; m <= M; ++m) {
+    const int G = one_blocks_per_row(m, V);
+    if (!G) continue;
+    r.cand = std::max(r.cand, (size_t)m * G * (size_t)((V + G - 1) / G));
+    r.blocks = std::max(r.blocks, (size_t)m * G);
+    r.rows = (size_t)m;
+  }
+  return r;
+}
 
 Layout layout(int M, int V) {
   const size_t nb = (size_t)blocks_per_row(V);
+  const OneRoom one = one_room(M, V);
   Layout L;
   size_t o = 0;
   auto take = [&](size_t n) {
@@ -208,6 +277,7 @@ Layout layout(int M, int V) {
     o += (n + 255) & ~(size_t)255;
     return at;
   };
+  L.hdr = take(sizeof(u64) * kHdrWords);
   L.maxp = take(sizeof(float) * M * nb);
   L.zmax = take(sizeof(float) * M);
   L.hist = take(sizeof(u64) * 4 * kBins * 4 * M);
@@ -215,8 +285,13 @@ Layout layout(int M, int V) {
   L.sel = take(sizeof(SelState) * 4 * M);
   L.rows = take(sizeof(RowState) * M);
   L.acc = take(sizeof(AccIn) * M);
-  L.blk = take(sizeof(u64) * kBlkWords * (size_t)draw_blocks(V));
+  L.blk = take(sizeof(u64) * kBlkWords * (size_t)std::max(draw_blocks(V), kMaxOneBlocks));
   L.gpart = take(sizeof(float) * 2 * M * nb);
+  L.ahist = take(sizeof(double) * kXBins * one.rows);
+  L.above = take(sizeof(u64) * 3 * M);
+  L.ccount = take(sizeof(int32_t) * one.blocks);
+  L.cand = take(sizeof(u64) * one.cand);
+  L.wsum = take(one.blocks ? sizeof(u64) * 4 * kMaxOneBlocks * (kOneThreads / kWave) : 0);
   L.bytes = o;
   return L;
 }
@@ -244,6 +319,13 @@ struct RejArgs {
   RowState *rows;
   AccIn *acc;       // [row]: inputs of draft row's acceptance test
   u64 *blk;         // [block][res lo, res hi, e lo, e hi, first res > 0, first e > 0]
+  u64 *hdr;         // rej_one: counters (see kHdrWords)
+  double *ahist;    // rej_one: [row][kXBins] approximate mass histogram
+  u64 *above;       // rej_one: [row][L0, L1, L2] exact mass above the candidate bins
+  int32_t *ccount;  // rej_one: [row][workgroup] candidates
+  u64 *cand;        // rej_one: [row][workgroup][C] candidates (key << 32 | index)
+  u64 *wsum;        // rej_one: [res lo, res hi, e lo, e hi][row][workgroup][wave] draw range sums
+  int G, C;         // rej_one: workgroups per row, entries per workgroup
 };
 
 __device__ __forceinline__ u64 *hist_at(const RejArgs &p, int pass, int row) {
@@ -729,19 +811,20 @@ __device__ __forceinline__ double draw_weight_f64(const RejArgs &p, const RowSta
 // over the row), but reached only by u = 0-like targets that the first
 // positive index does not settle, or by residuals whose every positive
 // weight is below 2^-100.
+template <int NT>
 __device__ int draw_f64_sequential(const RejArgs &p, const RowState &rs, int row, bool residual,
                                    double u) {
-  __shared__ double sw[kBlock];
+  __shared__ double sw[NT];
   __shared__ double s_t;
   __shared__ int s_found, s_last;
   double W = 0.0;
   int last = -1;
-  for (int base = 0; base < p.V; base += kBlock) {
+  for (int base = 0; base < p.V; base += NT) {
     const int j = base + (int)threadIdx.x;
     sw[threadIdx.x] = j < p.V ? draw_weight_f64(p, rs, row, residual, j) : 0.0;
     __syncthreads();
     if (threadIdx.x == 0)
-      for (int i = 0; i < kBlock && base + i < p.V; ++i) {
+      for (int i = 0; i < NT && base + i < p.V; ++i) {
         W += sw[i];
         if (sw[i] > 0.0) last = base + i;
       }
@@ -754,12 +837,12 @@ __device__ int draw_f64_sequential(const RejArgs &p, const RowState &rs, int row
   }
   __syncthreads();
   double cum = 0.0;
-  for (int base = 0; base < p.V; base += kBlock) {
+  for (int base = 0; base < p.V; base += NT) {
     const int j = base + (int)threadIdx.x;
     sw[threadIdx.x] = j < p.V ? draw_weight_f64(p, rs, row, residual, j) : 0.0;
     __syncthreads();
     if (threadIdx.x == 0)
-      for (int i = 0; i < kBlock && base + i < p.V; ++i) {
+      for (int i = 0; i < NT && base + i < p.V; ++i) {
         cum += sw[i];
         if (cum > s_t) {
           s_found = base + i;
@@ -900,7 +983,7 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
       const int f = use_res ? s_fr : s_fe;
       pick = f != kNone ? f : p.V - 1;
     } else {
-      pick = draw_f64_sequential(p, rs, a, use_res, u);
+      pick = draw_f64_sequential<kBlock>(p, rs, a, use_res, u);
     }
     if (threadIdx.x < p.M) {
       const int i = threadIdx.x;
@@ -976,6 +1059,1107 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
     p.counts[1] = a + 1;
     *p.rollback = p.base_len + a + 1;
   }
+}
+
+// ---- rejection acceptance in one launch --------------------------------------
+//
+// The steps of the kernels above in one launch of G workgroups per row.  Each
+// workgroup holds a chunk of up to kOneChunk entries of its row in LDS, with
+// the entries' e values, for the whole call.  Rows never wait for each
+// other, and a workgroup waits only on words in its own row's page of the
+// workspace header:
+//   (1) the row maximum: each workgroup publishes its chunk maximum in a
+//       slot tagged with the call's generation number and waits until every
+//       slot of its row carries this call's tag;
+//   (2) the mass pass: the exact row total and an approximate fp64 mass
+//       histogram over kXBins bins of x = (z - zmax) / T are summed over the
+//       row.  x is a monotone function of z, so each bin is an interval of
+//       keys, and these bins spread a row far more evenly than the leading
+//       bits of its keys (the histogram's LDS atomics rarely collide).  The
+//       last workgroup of the row to arrive derives, from the fp64 prefix
+//       sums and a bound on their rounding, the range of bins that must hold
+//       the nucleus cut, and publishes it in a tagged word;
+//   (3) each workgroup adds the exact mass of its entries above that range
+//       and writes its entries inside it (the candidates, in index order) to
+//       its own segment of the workspace; the last to arrive resolves the cut
+//       alone (an exact pass over fine bins of x, then an exact sort of the
+//       fine bin that holds the cut), then publishes the row's state and
+//       acceptance input behind a tagged word;
+//   (4) every workgroup sums its chunk's draw weights for its own row before
+//       the accepted run is known (the residual for a draft row, p' for
+//       every row), per wave over contiguous ranges;
+//   (5) the last workgroup of the last row to finish derives the accepted
+//       run a from every row's acceptance input and picks the token from row
+//       a's workgroup and range sums, then resets the counters and advances
+//       the generation number.
+// Every decision is taken on exact fixed-point sums, as in the kernels above,
+// so the outputs are theirs.  A wait that runs past its bound sets the error
+// word and goes on (no wave is left spinning).
+
+constexpr int kSpinLimit = 1 << 21;
+constexpr int kOneWaves = kOneThreads / kWave;
+constexpr int kKPer = kOneChunk / kOneThreads;    // chunk entries per thread
+constexpr int kResPer = 8;                        // candidate loads each thread keeps in flight
+constexpr double kXScale = (double)kXBins / 70.5;
+constexpr int kSortMax = kXBins / 4;              // entries of a fine bin sorted directly
+static_assert(kXBins == kOneThreads, "one approximate bin per thread");
+static_assert(kKPer * kOneThreads == kOneChunk, "whole entries per thread");
+static_assert(kKPer * kOneWaves == 2 * kWave, "two compaction counts per lane");
+
+// Draw ranges: each wave of a workgroup of the drawing row covers one_range(C)
+// consecutive entries of the chunk; a thread of the picking workgroup holds
+// at most kMaxRangesPerThread range sums.
+__host__ __device__ constexpr int one_range(int C) { return (C + kOneWaves - 1) / kOneWaves; }
+constexpr int kRanges = kMaxOneBlocks * kOneWaves;
+constexpr int kMaxRangesPerThread = kRanges / kOneThreads;
+static_assert(one_range(kOneChunk) <= kKPer * kWave, "a wave's range fits its registers");
+static_assert(one_range(kOneChunk) <= kOneThreads, "a range fits one entry per thread");
+
+__device__ __forceinline__ int wave_min(int v) {
+  for (int s = kWave / 2; s > 0; s >>= 1) v = min(v, __shfl_xor(v, s));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+  for (int s = kWave / 2; s > 0; s >>= 1) v = max(v, __shfl_xor(v, s));
+  return v;
+}
+
+// Approximate bin of an entry with non-zero fixed-point mass (x in [-70.5, 0]).
+__device__ __forceinline__ int xbin(double x) {
+  const int b = (int)(-x * kXScale);
+  return b < kXBins - 1 ? b : kXBins - 1;
+}
+
+__device__ __forceinline__ u64 ld_ag(const u64 *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_ag(u64 *p, u64 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agi(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agi(int32_t *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agd(const double *p) {
+  return __longlong_as_double((long long)ld_ag(reinterpret_cast<const u64 *>(p)));
+}
+
+// Data crossing workgroups is only ever written by agent-scope atomic
+// stores and read-modify-writes and read by agent-scope atomic loads, which
+// all act at the coherence point beyond the per-XCD caches; so ordering needs
+// no cache-wide fences (an agent-scope acquire or release would write back
+// or invalidate the whole L2), only completion: every thread waits for its
+// own writes (s_waitcnt) before the arrival that publishes them is counted,
+// and a reader issues its loads only after it has seen that arrival.
+
+// The calling lane waits until slot s carries tag in its high word and
+// returns it (bounded: past kSpinLimit polls the error word is set and the
+// wait ends).
+__device__ u64 wait_slot(const u64 *s, uint32_t tag, u64 *err) {
+  u64 v = ld_ag(s);
+  int it = 0;
+  while ((uint32_t)(v >> 32) != tag) {
+    if (++it > kSpinLimit) {
+      st_ag(err, 1ull);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = ld_ag(s);
+  }
+  return v;
+}
+
+// Workgroup-wide exact sum (all kOneThreads threads); valid in every thread.
+__device__ Fx fx_sum_one(Fx a, Fx *red) {
+  a = fx_wave_sum(a);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = a;
+  __syncthreads();
+  Fx s = fx_zero();
+  for (int i = 0; i < kOneWaves; ++i) fx_add(s, red[i]);
+  return s;
+}
+
+// Exclusive exact prefix over the threads (thread order) and the total.
+__device__ Fx fx_excl_one(Fx v, Fx *red, Fx &total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  Fx incl = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const Fx o = fx_shfl_up(incl, off);
+    if (lane >= off) fx_add(incl, o);
+  }
+  __syncthreads();
+  if (lane == kWave - 1) red[wave] = incl;
+  __syncthreads();
+  Fx before = fx_zero();
+  total = fx_zero();
+  for (int w = 0; w < kOneWaves; ++w) {
+    if (w < wave) fx_add(before, red[w]);
+    fx_add(total, red[w]);
+  }
+  return fx_sum(before, fx_sub(incl, v));
+}
+
+// Inclusive fp64 prefix over the threads in one fixed order of additions (so
+// every workgroup that runs it on the same values gets the same sums).
+__device__ double dscan_one(double v, double *dred) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  double incl = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) dred[wave] = incl;
+  __syncthreads();
+  double before = 0.0;
+  for (int w = 0; w < wave; ++w) before += dred[w];
+  return before + incl;
+}
+
+// Workgroup-wide count of `flag` and the exclusive count before this thread.
+__device__ int count_one(bool flag, int &before, int *wcnt) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const u64 b = __ballot(flag);
+  __syncthreads();
+  if (lane == 0) wcnt[wave] = __popcll(b);
+  __syncthreads();
+  int tot = 0, pre = 0;
+  for (int w = 0; w < kOneWaves; ++w) {
+    if (w < wave) pre += wcnt[w];
+    tot += wcnt[w];
+  }
+  before = pre + __popcll(b & ((1ull << lane) - 1ull));
+  return tot;
+}
+
+// Adds mass e (non-zero) with one count to LDS bin d (lo with carry, hi).
+__device__ __forceinline__ void hist_add(u64 *sh, int d, const Fx &e) {
+  u64 *bin = sh + 3 * d;
+  if (e.lo) {
+    const u64 old = atomicAdd(bin, e.lo);
+    atomicAdd(bin + 1, e.hi + ((old + e.lo < old) ? 1ull : 0ull));
+  } else {
+    atomicAdd(bin + 1, e.hi);
+  }
+  atomicAdd(bin + 2, 1ull);
+}
+
+// The draw weights of entry j (as draw_weights) from its logit zj and draft
+// probability qj at hand; e_all is its e_or_zero value when have_e, else it
+// is computed here (inside the nucleus only).  The exponential is taken at
+// most twice: e itself, and exp(x) again only where e is not positive (the
+// flags then need the unskipped value).
+__device__ __forceinline__ void draw_weights_v(const RowState &rs, double T, bool residual, int j,
+                                               float zj, double qj, bool have_e, double e_all,
+                                               Fx &wres, Fx &we, bool &pres, bool &pe) {
+  const bool in = in_nucleus(rs, zj, j);
+  double e = 0.0, x = 0.0, ex = 0.0;
+  if (in) {
+    x = ((double)zj - (double)rs.zmax) / T;
+    if (!have_e) e_all = x < -70.5 ? 0.0 : exp(x);
+    e = e_all;
+    ex = e > 0.0 ? e : exp(x);
+  }
+  pe = in && (e > 0.0 || x > -744.0 || ex > 0.0);
+  we = to_fx(e);
+  pres = false;
+  wres = fx_zero();
+  if (residual) {
+    const double d = e / rs.mass - qj;
+    wres = to_fx(d > 0.0 ? d : 0.0);
+    pres = d > 0.0;
+    if (in && e == 0.0 && qj < 0x1p-100) pres = ex / rs.mass - qj > 0.0;
+  }
+}
+
+__device__ __forceinline__ void store_row_state(RowState *dst, const RowState &rs) {
+  u64 w[3];
+  __builtin_memcpy(w, &rs, sizeof(w));
+  u64 *d = reinterpret_cast<u64 *>(dst);
+  for (int i = 0; i < 3; ++i) st_ag(d + i, w[i]);
+}
+
+__device__ __forceinline__ RowState row_state_of(const u64 *w) {
+  RowState rs;
+  __builtin_memcpy(&rs, w, sizeof(rs));
+  return rs;
+}
+
+// Acceptance input of a draft row: p'(x) under nucleus rs and q(x), for a
+// draft x whose logit zx and draft probability qx are at hand (valid: x in
+// [0, V)).
+__device__ __forceinline__ void publish_acc(const RejArgs &p, int row, const RowState &rs, int x,
+                                            bool valid, float zx, float qx) {
+  double px = 0.0, qd = 0.0;
+  if (valid) {
+    if (in_nucleus(rs, zx, x)) px = e_of(zx, rs.zmax, p.T) / rs.mass;
+    qd = (double)qx;
+  }
+  u64 *o = reinterpret_cast<u64 *>(p.acc + row);
+  st_ag(o, (u64)__double_as_longlong(px));
+  st_ag(o + 1, (u64)__double_as_longlong(qd));
+}
+
+// Loads the draft of row `row` (< M-1), its logit and draft probability.
+__device__ __forceinline__ void load_draft(const RejArgs &p, int row, int &x, bool &valid,
+                                           float &zx, float &qx) {
+  x = p.drafts[row];
+  valid = x >= 0 && x < p.V;
+  zx = valid ? p.z[(int64_t)row * p.ldl + x] : 0.0f;
+  qx = valid ? p.q[(int64_t)row * p.ldq + x] : 0.0f;
+}
+
+__global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  const int C = p.C;
+  float *zc = reinterpret_cast<float *>(dyn);                          // [C] logits
+  double *ec = reinterpret_cast<double *>(dyn + one_e_offset(C));      // [C] e_or_zero
+  uint16_t *bc = reinterpret_cast<uint16_t *>(dyn + one_b_offset(C));  // [C] bin or 0xFFFF
+  __shared__ double ah[kXBins];
+  __shared__ u64 sh[kBins * 3];
+  __shared__ Fx red[kOneWaves], wred[kOneWaves];
+  __shared__ double dred[kOneWaves];
+  __shared__ int wcnt[kOneWaves];
+  __shared__ int koff[kKPer * kOneWaves + 1];
+  __shared__ int segoff[kMaxOneBlocks];
+  __shared__ float s_f[kOneWaves];
+  __shared__ u64 s_gen, s_abv_lo, s_abv_hi, s_nk;
+  __shared__ u64 s_w[6];
+  __shared__ float s_zmax, s_zx, s_qx;
+  __shared__ uint32_t s_kmin, s_kmax, s_prefix;
+  __shared__ int s_blo, s_bhi, s_last, s_flag, s_nc, s_cut, s_a, s_x;
+  __shared__ int s_pick, s_blk, s_lastnz, s_fr, s_fe;
+  __shared__ Fx s_before;
+  const int G = p.G, row = blockIdx.x / G, g = blockIdx.x - row * G;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int j0 = g * C, n = min(C, p.V - j0);
+  u64 *const rp = p.hdr + (size_t)row * kPageWords;            // this row's page
+  u64 *const cp = p.hdr + (size_t)kMaxRows * kPageWords;       // the call's page
+  u64 *const err = cp + kCallErr;
+  const bool nucleus = !(p.top_p >= 1.0);
+  const double T = p.T;
+  bool chunk_lost = false;   // this workgroup's LDS holds candidates, not its chunk
+
+  // (1) the chunk into LDS and its maximum; this row's sums are cleared
+  // (shared out over the row's workgroups) before the maximum is published
+  if (tid == 0) s_gen = ld_ag(cp + kCallGen) + 1ull;
+  const float *zr = p.z + (int64_t)row * p.ldl + j0;
+  {
+    float v[kKPer];
+#pragma unroll
+    for (int k = 0; k < kKPer; ++k) {
+      const int i = k * kOneThreads + tid;
+      v[k] = i < n ? zr[i] : -__builtin_inff();
+    }
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < kKPer; ++k) {
+      const int i = k * kOneThreads + tid;
+      if (i < n) zc[i] = v[k];
+      m = fmaxf(m, v[k]);
+    }
+    if (nucleus)
+      for (int w = g * kOneThreads + tid; w < kXBins; w += G * kOneThreads)
+        st_ag(reinterpret_cast<u64 *>(p.ahist + (size_t)row * kXBins) + w, 0ull);
+    if (g == 0 && tid < 3) {
+      st_ag(p.total + 3 * row + tid, 0ull);
+      st_ag(p.above + 3 * row + tid, 0ull);
+    }
+    for (int s = kWave / 2; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
+    if (lane == 0) s_f[wave] = m;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t tag = (uint32_t)s_gen;
+      if (lane == 0) {
+        for (int w = 1; w < kOneWaves; ++w) m = fmaxf(m, s_f[w]);
+        st_ag(rp + kRowSlots + g, ((u64)tag << 32) | fkey(m));
+      }
+      uint32_t best = fkey(-__builtin_inff());
+      for (int q = lane; q < G; q += kWave)
+        best = max(best, (uint32_t)wait_slot(rp + kRowSlots + q, tag, err));
+      for (int s = kWave / 2; s > 0; s >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, s));
+      if (lane == 0) s_zmax = key_to_float(best);
+    }
+    __syncthreads();
+  }
+  const uint32_t tag = (uint32_t)s_gen;
+  const float zmax = s_zmax;
+
+  // (2) e of every entry (kept in LDS), the row's exact mass and, with
+  // top_p < 1, its approximate histogram over x
+  if (nucleus) ah[tid] = 0.0;
+  __syncthreads();
+  {
+    Fx tot = fx_zero();
+    for (int i = tid; i < n; i += kOneThreads) {
+      const double x = ((double)zc[i] - (double)zmax) / T;
+      const double e = x < -70.5 ? 0.0 : exp(x);     // as e_or_zero
+      ec[i] = e;
+      const Fx f = to_fx(e);
+      uint16_t b = 0xFFFF;
+      if (fx_nonzero(f)) {
+        fx_add(tot, f);
+        b = (uint16_t)xbin(x);
+        if (nucleus)
+          __hip_atomic_fetch_add(&ah[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      bc[i] = b;
+    }
+    tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram)
+    if (tid == 0 && fx_nonzero(tot)) fx_atomic_add3(p.total + 3 * row, tot);
+    if (nucleus && ah[tid] != 0.0) unsafeAtomicAdd(p.ahist + (size_t)row * kXBins + tid, ah[tid]);
+  }
+  // arrival; the last workgroup of the row reads the row's sums
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_flag = __hip_atomic_fetch_add(rp + kRowCnt, 1ull, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
+  __syncthreads();
+  const bool last2 = s_flag;
+
+  if (!nucleus) {
+    // the whole row is the nucleus: the last workgroup publishes the row's
+    // state (its mass) and the acceptance input
+    if (last2 && tid == 0) {
+      const u64 *tr = p.total + 3 * row;
+      const Fx S = fx_from3(ld_ag(tr), ld_ag(tr + 1), ld_ag(tr + 2));
+      const RowState rs = RowState{zmax, 0u, p.V, 1, fx_to_double(S)};
+      store_row_state(p.rows + row, rs);
+      if (row < p.M - 1) {
+        int x;
+        bool valid;
+        float zx, qx;
+        load_draft(p, row, x, valid, zx, qx);
+        publish_acc(p, row, rs, x, valid, zx, qx);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      st_ag(rp + kRowState, (u64)tag << 32);
+    }
+  } else {
+    // (2b) the range [blo, bhi] of approximate bins that holds the cut, found
+    // by the last workgroup of the row and published in a tagged word.  The
+    // fp64 sums carry a relative error below (C + G + 32) * 2^-53 (the
+    // longest chain of additions behind any of them: within a chunk, over
+    // the chunks, the prefix), and fixed point drops below V * 2^-100; E
+    // bounds both with room to spare.  No bin before blo reaches the
+    // threshold, bin bhi does (or bhi is the last occupied bin).
+    if (last2) {
+      if (tid == 0) {
+        const u64 *tr = p.total + 3 * row;
+        for (int w = 0; w < 3; ++w) s_w[w] = ld_ag(tr + w);
+        s_blo = kXBins;
+        s_bhi = kXBins;
+        s_last = -1;
+      }
+      const double v = ld_agd(p.ahist + (size_t)row * kXBins + tid);
+      const double cum = dscan_one(v, dred);    // (its barriers publish s_w)
+      const double Sd = fx_to_double(fx_from3(s_w[0], s_w[1], s_w[2]));
+      const double thr_d = fx_to_double(threshold(p, Sd));
+      const double E = (double)(C + G + 64) * 0x1p-51 * (Sd + 1.0) + (double)p.V * 0x1p-98;
+      {   // first thread of each condition, last occupied bin: one LDS atomic per wave
+        const u64 b0 = __ballot(cum >= thr_d - E), b1 = __ballot(cum >= thr_d + E);
+        const u64 b2 = __ballot(v > 0.0);
+        if (lane == 0) {
+          if (b0) atomicMin(&s_blo, wave * kWave + __ffsll((long long)b0) - 1);
+          if (b1) atomicMin(&s_bhi, wave * kWave + __ffsll((long long)b1) - 1);
+          if (b2) atomicMax(&s_last, wave * kWave + 63 - __clzll((long long)b2));
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        s_blo = min(s_blo, s_last);
+        s_bhi = min(s_bhi, s_last);
+        st_ag(rp + kRowBins,
+              ((u64)tag << 32) | ((u64)(s_blo + 1) << 16) | (u64)(s_bhi + 1));
+      }
+    } else if (tid == 0) {
+      const u64 w = wait_slot(rp + kRowBins, tag, err);
+      s_blo = (int)((w >> 16) & 0xFFFF) - 1;
+      s_bhi = (int)(w & 0xFFFF) - 1;
+    }
+    __syncthreads();
+    const int blo = s_blo, bhi = s_bhi;
+
+    // (3) the exact mass above the range, and the candidates in index order
+    // (entry k * kOneThreads + t is thread t's k-th)
+    {
+      Fx ab = fx_zero();
+      u64 bal[kKPer];
+#pragma unroll
+      for (int k = 0; k < kKPer; ++k) {
+        const int i = k * kOneThreads + tid;
+        const int b = i < n ? (int)bc[i] : 0xFFFF;
+        if (b < blo) fx_add(ab, to_fx(ec[i]));
+        bal[k] = __ballot(b >= blo && b <= bhi);
+        if (lane == 0) koff[k * kOneWaves + wave] = __popcll(bal[k]);
+      }
+      ab = fx_sum_one(ab, red);     // (its barriers also publish koff)
+      if (tid == 0 && fx_nonzero(ab)) fx_atomic_add3(p.above + 3 * row, ab);
+      if (wave == 0) {
+        const int c0 = koff[2 * lane], c1 = koff[2 * lane + 1];
+        int incl = c0 + c1;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        const int before = incl - c0 - c1;
+        koff[2 * lane] = before;
+        koff[2 * lane + 1] = before + c0;
+        if (lane == kWave - 1) koff[kKPer * kOneWaves] = incl;
+      }
+      __syncthreads();
+      u64 *seg = p.cand + (size_t)(row * G + g) * C;
+#pragma unroll
+      for (int k = 0; k < kKPer; ++k) {
+        if ((bal[k] >> lane) & 1ull) {
+          const int i = k * kOneThreads + tid;
+          const int pos = koff[k * kOneWaves + wave] + __popcll(bal[k] & ((1ull << lane) - 1ull));
+          st_ag(seg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
+        }
+      }
+      if (tid == 0) st_agi(p.ccount + row * G + g, koff[kKPer * kOneWaves]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_flag = __hip_atomic_fetch_add(rp + kRowCand, 1ull, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
+    __syncthreads();
+
+    chunk_lost = s_flag;
+    if (s_flag) {
+      // (3b) the last workgroup of the row resolves the cut.  Independent
+      // loads first: segment sizes (wave 0), the row's sums (thread 64),
+      // the draft (thread 128).
+      if (wave == 0) {
+        int c[4], loc = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = 4 * lane + r;
+          c[r] = q < G ? ld_agi(p.ccount + row * G + q) : 0;
+          loc += c[r];
+        }
+        int incl = loc;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        int o = incl - loc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          segoff[4 * lane + r] = o;
+          o += c[r];
+        }
+        if (lane == kWave - 1) s_nc = incl;
+      } else if (tid == 64) {
+        const u64 *abr = p.above + 3 * row, *tr = p.total + 3 * row;
+        for (int w = 0; w < 3; ++w) {
+          s_w[w] = ld_ag(abr + w);
+          s_w[3 + w] = ld_ag(tr + w);
+        }
+      } else if (tid == 128 && row < p.M - 1) {
+        int x;
+        bool valid;
+        float zx, qx;
+        load_draft(p, row, x, valid, zx, qx);
+        s_x = valid ? x : -1;
+        s_zx = zx;
+        s_qx = qx;
+      }
+      __syncthreads();
+      const int nc = s_nc;
+      const Fx A = fx_from3(s_w[0], s_w[1], s_w[2]);
+      const double Sd = fx_to_double(fx_from3(s_w[3], s_w[4], s_w[5]));
+      const Fx thr = threshold(p, Sd);
+      const double thr_d = fx_to_double(thr);
+      auto seg_of = [&](int c) {   // the last segment starting at or before c
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (segoff[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+      };
+      auto cand_load = [&](int c) {
+        const int q = seg_of(c);
+        return ld_ag(p.cand + (size_t)(row * G + q) * C + (c - segoff[q]));
+      };
+      auto e_of_key = [&](u64 v) {   // e of a candidate, as step (2) computed it
+        return e_of(key_to_float((uint32_t)(v >> 32)), zmax, T);
+      };
+      // the candidates into LDS, over this workgroup's chunk (reloaded from
+      // the logits if this row draws); any beyond the room stay in the
+      // workspace and are loaded again where needed
+      const int room = one_cand_room(C), nl = min(nc, room);
+      u64 *lk = reinterpret_cast<u64 *>(dyn);
+      double *le = reinterpret_cast<double *>(dyn + (size_t)room * 8);
+      for (int base = 0; base < nl; base += kResPer * kOneThreads) {
+        int sq[kResPer];
+        u64 v[kResPer];
+#pragma unroll
+        for (int k = 0; k < kResPer; ++k) {
+          const int c = base + k * kOneThreads + tid;
+          sq[k] = c < nl ? seg_of(c) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kResPer; ++k) {
+          const int c = base + k * kOneThreads + tid;
+          v[k] = c < nl ? ld_ag(p.cand + (size_t)(row * G + sq[k]) * C + (c - segoff[sq[k]]))
+                        : 0ull;
+        }
+#pragma unroll
+        for (int k = 0; k < kResPer; ++k) {
+          const int c = base + k * kOneThreads + tid;
+          if (c < nl) {
+            lk[c] = v[k];
+            le[c] = e_of_key(v[k]);
+          }
+        }
+      }
+      __syncthreads();
+      auto each = [&](auto &&f) {   // every candidate once
+        for (int c = tid; c < nl; c += kOneThreads) f(lk[c], le[c]);
+        for (int c = room + tid; c < nc; c += kOneThreads) {
+          const u64 v = cand_load(c);
+          f(v, e_of_key(v));
+        }
+      };
+      // (3c) one exact pass over fine bins of x: fb(z) = (t - blo) * 256 /
+      // (bhi - blo + 1) with t = -x * kXScale (x as step (2) computes it) is a
+      // monotone function of z like the bins themselves, so the selection
+      // over fine bins is exact, and it spreads the candidates evenly (few
+      // LDS atomics collide).  Digit 255 - fb puts larger logits in higher
+      // bins, as select_bin_wave expects.
+      const double S2 = 256.0 / (double)(bhi - blo + 1);
+      auto fbin = [&](u64 v) {
+        const double x = ((double)key_to_float((uint32_t)(v >> 32)) - (double)zmax) / T;
+        const int b = (int)((-x * kXScale - (double)blo) * S2);
+        return 255 - (b < 0 ? 0 : (b > 255 ? 255 : b));
+      };
+      // (few candidates skip it: they are all sorted directly)
+      const bool few = nc <= kWave;
+      if (!few) {
+        for (int i = tid; i < kBins * 3; i += kOneThreads) sh[i] = 0ull;
+        __syncthreads();
+        each([&](u64 v, double e) { hist_add(sh, fbin(v), to_fx(e)); });
+        __syncthreads();
+        if (wave == 0) {
+          Fx a2 = A;
+          int bin = select_bin_wave(sh, thr, a2);
+          if (bin < 0) bin = 0;
+          if (lane == 0) {
+            s_prefix = (uint32_t)bin;
+            s_abv_lo = a2.lo;
+            s_abv_hi = a2.hi;
+            s_nk = sh[3 * bin + 2];
+            s_nc = 0;
+          }
+        }
+        __syncthreads();
+      }
+      const int fsel = few ? 0 : (int)s_prefix, n2 = few ? nc : (int)s_nk;
+      Fx above = few ? A : Fx{s_abv_lo, s_abv_hi};
+      uint32_t kappa = 0u;
+      u64 nk = 0ull;
+      int cut_pos = -1;   // where the cut group starts among the sorted entries
+      // the fine bin's entries, gathered and sorted by (key descending, index
+      // ascending) in the LDS of the step (2) histogram, when they fit
+      u64 *gk = reinterpret_cast<u64 *>(ah), *sk = gk + kSortMax;
+      double *ge = ah + 2 * kSortMax, *se2 = ah + 3 * kSortMax;
+      const bool small = n2 <= kSortMax;
+      // one wave sorts up to kWave entries (from the candidates themselves
+      // when they are few, else from the gathered fine bin) and finds the cut
+      // group in them with wave-level scans
+      auto wave_cut = [&](const u64 *srck, const double *srce) {
+        if (wave == 0) {
+          auto skey = [](u64 v) {
+            return (v & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (v & 0xFFFFFFFFull));
+          };
+          const bool valid = lane < n2;
+          const u64 v0 = valid ? srck[lane] : 0ull;
+          const double e0 = valid ? srce[lane] : 0.0;
+          const u64 mine = skey(v0);
+          int rank = 0;
+          for (int j = 0; j < n2; ++j) rank += skey(srck[j]) > mine;
+          if (valid) {
+            sk[rank] = v0;
+            se2[rank] = e0;
+          }
+          __builtin_amdgcn_s_waitcnt(0);
+          __builtin_amdgcn_wave_barrier();
+          const u64 v = valid ? sk[lane] : 0ull;
+          const Fx f = valid ? to_fx(se2[lane]) : fx_zero();
+          Fx incl = f;
+          for (int off = 1; off < kWave; off <<= 1) {
+            const Fx o = fx_shfl_up(incl, off);
+            if (lane >= off) fx_add(incl, o);
+          }
+          const Fx excl = fx_sum(above, fx_sub(incl, f));
+          const uint32_t key = (uint32_t)(v >> 32);
+          const bool gend = valid && (lane == n2 - 1 || (uint32_t)(sk[lane + 1] >> 32) != key);
+          const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
+          const int gl = hit ? __ffsll((long long)hit) - 1 : n2 - 1;
+          const uint32_t kap = (uint32_t)__shfl((int)key, gl);
+          const u64 first = __ballot(valid && key == kap);
+          const int gs = __ffsll((long long)first) - 1;
+          const Fx ab = fx_shfl(excl, gs);
+          if (lane == 0) {
+            s_prefix = kap;
+            s_abv_lo = ab.lo;
+            s_abv_hi = ab.hi;
+            s_nk = (u64)(gl - gs + 1);
+            s_cut = gs;
+          }
+        }
+        __syncthreads();
+        kappa = s_prefix;
+        above = Fx{s_abv_lo, s_abv_hi};
+        nk = s_nk;
+        cut_pos = s_cut;
+      };
+      if (nc > 0 && few) {
+        wave_cut(lk, le);
+      } else if (nc > 0 && small) {
+        each([&](u64 v, double e) {
+          if (fbin(v) == fsel) {
+            const int pos = atomicAdd(&s_nc, 1);
+            gk[pos] = v;
+            ge[pos] = e;
+          }
+        });
+        __syncthreads();
+        if (n2 <= kWave) {
+          wave_cut(gk, ge);
+        } else {
+        // rank = entries before this one in the order; the sort key
+        // (key << 32 | ~index) is distinct and descends in that order
+        auto skey = [](u64 v) {
+          return (v & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (v & 0xFFFFFFFFull));
+        };
+        if (tid < n2) {
+          const u64 mine = skey(gk[tid]);
+          int rank = 0;
+          for (int j = 0; j < n2; ++j) rank += skey(gk[j]) > mine;
+          sk[rank] = gk[tid];
+          se2[rank] = ge[tid];
+        }
+        __syncthreads();
+        // exclusive prefix in the order; the cut is the first key whose group
+        // reaches the threshold (else the last group)
+        const u64 v = tid < n2 ? sk[tid] : 0ull;
+        const Fx f = tid < n2 ? to_fx(se2[tid]) : fx_zero();
+        Fx tot_unused;
+        const Fx excl = fx_sum(above, fx_excl_one(f, red, tot_unused));
+        const uint32_t key = (uint32_t)(v >> 32);
+        const bool gend = tid < n2 && (tid == n2 - 1 || (uint32_t)(sk[tid + 1] >> 32) != key);
+        if (tid == 0) {
+          s_blk = 0x7FFFFFFF;
+          s_lastnz = 0x7FFFFFFF;
+        }
+        __syncthreads();
+        {
+          const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
+          if (lane == 0 && hit) atomicMin(&s_blk, wave * kWave + __ffsll((long long)hit) - 1);
+        }
+        __syncthreads();
+        const int gl = s_blk != 0x7FFFFFFF ? s_blk : n2 - 1;   // the cut group's last entry
+        kappa = (uint32_t)(sk[gl] >> 32);
+        {
+          const u64 first = __ballot(tid < n2 && key == kappa);
+          if (lane == 0 && first)
+            atomicMin(&s_lastnz, wave * kWave + __ffsll((long long)first) - 1);
+        }
+        __syncthreads();
+        const int gs = s_lastnz;   // the cut group's first entry
+        if (tid == gs) {
+          s_abv_lo = excl.lo;
+          s_abv_hi = excl.hi;
+        }
+        __syncthreads();
+        above = Fx{s_abv_lo, s_abv_hi};
+        nk = (u64)(gl - gs + 1);
+        cut_pos = gs;
+        }
+      } else if (nc > 0) {
+        // a large fine bin (many equal or nearly equal logits): radix passes
+        // over the keys of its entries
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+        each([&](u64 v, double) {
+          if (fbin(v) != fsel) return;
+          const uint32_t k = (uint32_t)(v >> 32);
+          kmn = min(kmn, k);
+          kmx = max(kmx, k);
+        });
+        for (int s2 = kWave / 2; s2 > 0; s2 >>= 1) {
+          kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, s2));
+          kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, s2));
+        }
+        if (tid == 0) {
+          s_kmin = 0xFFFFFFFFu;
+          s_kmax = 0u;
+        }
+        __syncthreads();
+        if (lane == 0) {
+          atomicMin(&s_kmin, kmn);
+          atomicMax(&s_kmax, kmx);
+        }
+        __syncthreads();
+        kmn = s_kmin;
+        kmx = s_kmax;
+        int lo_bit = kmn == kmx ? 0 : 32 - __clz((int)(kmn ^ kmx));
+        uint32_t prefix = lo_bit == 32 ? 0u : (kmn >> lo_bit);
+        nk = (u64)n2;
+        while (lo_bit > 0) {
+          const int db = min(8, lo_bit), shift = lo_bit - db;
+          for (int i = tid; i < kBins * 3; i += kOneThreads) sh[i] = 0ull;
+          __syncthreads();
+          each([&](u64 v, double e) {
+            const uint32_t k = (uint32_t)(v >> 32);
+            if (fbin(v) != fsel || (lo_bit < 32 && (k >> lo_bit) != prefix)) return;
+            hist_add(sh, (int)((k >> shift) & ((1u << db) - 1u)), to_fx(e));
+          });
+          __syncthreads();
+          if (wave == 0) {
+            Fx a2 = above;
+            int bin = select_bin_wave(sh, thr, a2);
+            if (bin < 0) bin = 0;
+            if (lane == 0) {
+              s_prefix = (prefix << db) | (uint32_t)bin;
+              s_abv_lo = a2.lo;
+              s_abv_hi = a2.hi;
+              s_nk = sh[3 * bin + 2];
+            }
+          }
+          __syncthreads();
+          prefix = s_prefix;
+          above = Fx{s_abv_lo, s_abv_hi};
+          nk = s_nk;
+          lo_bit = shift;
+          __syncthreads();
+        }
+        kappa = prefix;
+      }
+      const double ek = e_of(key_to_float(kappa), zmax, T);
+      const double above_d = fx_to_double(above);
+      const double tt = ceil((thr_d - above_d) / ek);
+      const u64 t = (tt < 1.0) ? 1ull : (tt >= (double)nk ? nk : (u64)tt);
+      int cutoff = p.V;
+      if (t < nk && cut_pos >= 0) {
+        // the group is sorted by index: its t-th entry is the last inside
+        cutoff = (int)(uint32_t)sk[cut_pos + (int)t - 1];
+      } else if (t < nk) {
+        // ties at the cut: the first t in index order (the candidates' order)
+        // are inside
+        if (tid == 0) s_cut = p.V;
+        int seen = 0;
+        auto round = [&](bool valid, u64 v) {
+          const bool f = valid && (uint32_t)(v >> 32) == kappa;
+          int pre;
+          const int tot_r = count_one(f, pre, wcnt);
+          if (f && (u64)(seen + pre + 1) == t) s_cut = (int)(uint32_t)v;
+          seen += tot_r;
+          return (u64)seen >= t;
+        };
+        bool done = false;
+        for (int base = 0; !done && base < nc; base += kOneThreads) {
+          const int c = base + tid;
+          done = round(c < nc, c < nl ? lk[c] : (c < nc ? cand_load(c) : 0ull));
+        }
+        __syncthreads();
+        cutoff = s_cut;
+      }
+      if (tid == 0) {
+        const RowState rs = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
+        store_row_state(p.rows + row, rs);
+        if (row < p.M - 1) publish_acc(p, row, rs, s_x, s_x >= 0, s_zx, s_qx);
+        __builtin_amdgcn_s_waitcnt(0);
+        st_ag(rp + kRowState, (u64)tag << 32);
+      }
+    }
+  }
+
+  // (4) the draw weights of this row, before the accepted run is known:
+  // the residual max(0, p' - q) for a draft row (drawn if its draft is the
+  // first rejected), p' itself (drawn by the last row, or where a residual
+  // is all zero).  Wave w sums a contiguous range of the chunk (entries w*L
+  // .. w*L+L-1).  Then the arrivals are counted per row and over the rows;
+  // the very last workgroup derives the accepted run a and picks the token
+  // from row a's range sums.
+  {
+    const bool residual = row < p.M - 1;
+    const int L = one_range(C), rb = wave * L;
+    if (tid == 0) {
+      wait_slot(rp + kRowState, tag, err);
+      const u64 *rw = reinterpret_cast<const u64 *>(p.rows + row);
+      for (int w = 0; w < 3; ++w) s_w[w] = ld_ag(rw + w);
+      s_fr = kNone;
+      s_fe = kNone;
+    }
+    float qv[kKPer], zv[kKPer];
+#pragma unroll
+    for (int r = 0; r < kKPer; ++r) {
+      const int i = rb + r * kWave + lane;
+      const bool ok = r * kWave + lane < L && i < n;
+      qv[r] = (ok && residual) ? p.q[(int64_t)row * p.ldq + j0 + i] : 0.0f;
+      zv[r] = (ok && chunk_lost) ? zr[i] : 0.0f;
+    }
+    __syncthreads();
+    const RowState rs = row_state_of(s_w);
+    Fx sr = fx_zero(), se = fx_zero();
+    int fr = kNone, fe = kNone;
+#pragma unroll
+    for (int r = 0; r < kKPer; ++r) {
+      const int i = rb + r * kWave + lane;
+      if (r * kWave + lane < L && i < n) {
+        Fx wr, we;
+        bool pr, pe;
+        draw_weights_v(rs, T, residual, j0 + i, chunk_lost ? zv[r] : zc[i], (double)qv[r],
+                       !chunk_lost, chunk_lost ? 0.0 : ec[i], wr, we, pr, pe);
+        fx_add(sr, wr);
+        fx_add(se, we);
+        if (pr && fr == kNone) fr = j0 + i;
+        if (pe && fe == kNone) fe = j0 + i;
+      }
+    }
+    sr = fx_wave_sum(sr);
+    se = fx_wave_sum(se);
+    fr = wave_min(fr);
+    fe = wave_min(fe);
+    if (lane == 0) {
+      u64 *o = p.wsum + (size_t)blockIdx.x * kOneWaves + wave;
+      st_ag(o, sr.lo);
+      st_ag(o + kRanges, sr.hi);
+      st_ag(o + 2 * kRanges, se.lo);
+      st_ag(o + 3 * kRanges, se.hi);
+      red[wave] = sr;
+      wred[wave] = se;
+      if (fr != kNone) atomicMin(&s_fr, fr);
+      if (fe != kNone) atomicMin(&s_fe, fe);
+    }
+    __syncthreads();
+    if (wave == 0) {   // the workgroup's sums (lanes 0..15 hold the waves')
+      Fx br = lane < kOneWaves ? red[lane] : fx_zero();
+      Fx be = lane < kOneWaves ? wred[lane] : fx_zero();
+      br = fx_wave_sum(br);
+      be = fx_wave_sum(be);
+      if (lane == 0) {
+        u64 *o = p.blk + kBlkWords * blockIdx.x;
+        st_ag(o, br.lo);
+        st_ag(o + 1, br.hi);
+        st_ag(o + 2, be.lo);
+        st_ag(o + 3, be.hi);
+        st_ag(o + 4, (u64)s_fr);
+        st_ag(o + 5, (u64)s_fe);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      bool last = __hip_atomic_fetch_add(rp + kRowDraw, 1ull, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
+      if (last)
+        last = __hip_atomic_fetch_add(cp + kCallRows, 1ull, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (u64)(p.M - 1);
+      s_flag = last;
+    }
+    __syncthreads();
+    if (s_flag) {
+      // (5) the last workgroup of the call: the accepted run, then the draw
+      // from row a (every row's state, acceptance input and sums are in).
+      // Wave 0 finds the workgroup and the range of the crossing from the
+      // workgroup and range sums (wave-level scans, no block barriers); then
+      // the whole workgroup scans that range.
+      if (wave == 0) {
+        bool reject = false;
+        if (lane < p.M - 1) {
+          const u64 *o = reinterpret_cast<const u64 *>(p.acc + lane);
+          const double px = __longlong_as_double((long long)ld_ag(o));
+          const double qx = __longlong_as_double((long long)ld_ag(o + 1));
+          reject = !((double)p.u[lane] * qx < px);
+        }
+        const u64 rej = __ballot(reject);
+        const int a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
+        const bool residual = a < p.M - 1;
+        Fx br[kMaxOneBlocks / kWave], be[kMaxOneBlocks / kWave];
+        int bfr = kNone, bfe = kNone;
+#pragma unroll
+        for (int c = 0; c < kMaxOneBlocks / kWave; ++c) {
+          const int q = c * kWave + lane;
+          br[c] = be[c] = fx_zero();
+          if (q < G) {
+            const u64 *o = p.blk + kBlkWords * (a * G + q);
+            br[c] = Fx{ld_ag(o), ld_ag(o + 1)};
+            be[c] = Fx{ld_ag(o + 2), ld_ag(o + 3)};
+            bfr = min(bfr, (int)ld_ag(o + 4));
+            bfe = min(bfe, (int)ld_ag(o + 5));
+          }
+        }
+        Fx lr = fx_zero(), le = fx_zero();
+#pragma unroll
+        for (int c = 0; c < kMaxOneBlocks / kWave; ++c) {
+          fx_add(lr, br[c]);
+          fx_add(le, be[c]);
+        }
+        const Fx tres = fx_wave_sum(lr), te = fx_wave_sum(le);
+        bfr = wave_min(bfr);
+        bfe = wave_min(bfe);
+        const bool use_res = residual && bfr != kNone;
+        const double u = (double)p.u[p.M - 1];
+        const Fx target = to_fx(u * fx_to_double(use_res ? tres : te));
+        int mode = 0, pick = -1, blk = -1, rng = -1;   // mode 0: range rng holds the pick
+        Fx before = fx_zero();
+        if (!fx_nonzero(target)) {
+          // below the fixed-point resolution (see rej_draw_pick): u = 0 takes
+          // the first positive weight, any other target the fp64 sequence
+          if (u == 0.0) {
+            const int f = use_res ? bfr : bfe;
+            mode = 1;
+            pick = f != kNone ? f : p.V - 1;
+          } else {
+            mode = 2;
+          }
+        } else {
+          // the workgroup of the crossing (workgroups in index order: c-major)
+          Fx cum = fx_zero();
+          bool exact = false;
+          int lastnz = -1;
+#pragma unroll
+          for (int c = 0; c < kMaxOneBlocks / kWave; ++c) {
+            const int q = c * kWave + lane;
+            const Fx w = use_res ? br[c] : be[c];
+            Fx incl = w;
+            for (int off = 1; off < kWave; off <<= 1) {
+              const Fx o = fx_shfl_up(incl, off);
+              if (lane >= off) fx_add(incl, o);
+            }
+            const Fx bef = fx_sum(cum, fx_sub(incl, w));
+            const u64 hit = __ballot(!exact && q < G && !fx_gt(bef, target) &&
+                                     fx_gt(fx_sum(bef, w), target));
+            if (hit) {
+              const int l = __ffsll((long long)hit) - 1;
+              exact = true;
+              blk = c * kWave + l;
+              before = fx_shfl(bef, l);
+            }
+            const u64 nz = __ballot(q < G && fx_nonzero(w));
+            if (nz) lastnz = c * kWave + 63 - __clzll((long long)nz);
+            fx_add(cum, fx_shfl(incl, kWave - 1));
+          }
+          if (!exact) {
+            blk = lastnz;
+            before = fx_zero();
+          }
+          if (blk >= 0) {
+            // the range of the crossing inside workgroup blk (lane w < 16 holds
+            // range w), or its last positive range
+            const size_t rq = ((size_t)a * G + blk) * kOneWaves + lane;
+            Fx w = fx_zero();
+            if (lane < kOneWaves) {
+              const u64 *o = p.wsum + rq + (use_res ? 0 : 2 * kRanges);
+              w = Fx{ld_ag(o), ld_ag(o + kRanges)};
+            }
+            Fx incl = w;
+            for (int off = 1; off < kWave; off <<= 1) {
+              const Fx o = fx_shfl_up(incl, off);
+              if (lane >= off) fx_add(incl, o);
+            }
+            const Fx bef = fx_sum(before, fx_sub(incl, w));
+            if (exact) {
+              const u64 hit = __ballot(lane < kOneWaves && !fx_gt(bef, target) &&
+                                       fx_gt(fx_sum(bef, w), target));
+              const int l = hit ? __ffsll((long long)hit) - 1 : 0;
+              rng = l;
+              before = fx_shfl(bef, l);
+            } else {
+              const u64 nz = __ballot(lane < kOneWaves && fx_nonzero(w));
+              rng = nz ? 63 - __clzll((long long)nz) : 0;
+            }
+            mode = exact ? 0 : 3;
+          } else {
+            mode = 1;
+            pick = p.V - 1;   // no positive weight at all: the last id
+          }
+        }
+        if (lane == 0) {
+          s_a = a;
+          s_flag = mode;
+          s_pick = pick;
+          s_blk = blk;
+          s_lastnz = rng;
+          s_before = before;
+          s_fr = use_res ? 1 : 0;
+          const u64 *rw = reinterpret_cast<const u64 *>(p.rows + a);
+          for (int w = 0; w < 3; ++w) s_w[3 + w] = ld_ag(rw + w);
+          s_abv_lo = target.lo;
+          s_abv_hi = target.hi;
+        }
+      }
+      __syncthreads();
+      const int a = s_a, mode = s_flag;
+      const bool residual = a < p.M - 1, use_res = s_fr != 0;
+      const RowState rs = row_state_of(s_w + 3);
+      int pick = s_pick;
+      if (mode == 2) {
+        pick = draw_f64_sequential<kOneThreads>(p, rs, a, use_res, (double)p.u[p.M - 1]);
+      } else if (mode == 0 || mode == 3) {
+        // the range's entries, thread t holding entry t: exact, the entry whose
+        // weight crosses the target; else the last positive one
+        const Fx target = Fx{s_abv_lo, s_abv_hi};
+        const int gb = s_blk, s0 = s_lastnz * L;
+        const int len = max(0, min(L, min(C, p.V - gb * C) - s0));
+        const int jt = gb * C + s0 + tid;
+        Fx w = fx_zero();
+        if (tid < len) {
+          const float zt = p.z[(int64_t)a * p.ldl + jt];
+          const float qt = residual ? p.q[(int64_t)a * p.ldq + jt] : 0.0f;
+          Fx wr, we;
+          bool pr, pe;
+          draw_weights_v(rs, T, residual, jt, zt, (double)qt, false, 0.0, wr, we, pr, pe);
+          w = use_res ? wr : we;
+        }
+        if (tid == 0) s_pick = -1;
+        Fx tot2;
+        Fx bef = fx_excl_one(w, red, tot2);   // (its barriers also publish s_pick)
+        if (mode == 0) bef = fx_sum(s_before, bef);
+        int lastw = -1;
+        if (tid < len) {
+          if (mode == 0) {
+            if (!fx_gt(bef, target) && fx_gt(fx_sum(bef, w), target)) s_pick = jt;   // one entry
+          } else if (fx_nonzero(w)) {
+            lastw = jt;
+          }
+        }
+        lastw = wave_max(lastw);
+        if (lane == 0 && lastw >= 0) atomicMax(&s_pick, lastw);
+        __syncthreads();
+        pick = s_pick < 0 ? p.V - 1 : s_pick;
+      }
+      if (tid < p.M) p.tokens[tid] = (tid < a) ? p.drafts[tid] : (tid == a ? pick : -1);
+      if (tid == 0) {
+        p.counts[0] = a;
+        p.counts[1] = a + 1;
+        *p.rollback = p.base_len + a + 1;
+      }
+      // (6) every other workgroup has left: the counters are reset and the
+      // generation advances for the next call
+      if (tid < p.M) {
+        u64 *r = p.hdr + (size_t)tid * kPageWords;
+        st_ag(r + kRowCnt, 0ull);
+        st_ag(r + kRowCand, 0ull);
+        st_ag(r + kRowDraw, 0ull);
+      }
+      if (tid == 0) {
+        st_ag(cp + kCallRows, 0ull);
+        st_ag(cp + kCallGen, s_gen);
+      }
+    }
+  }
+
 }
 
 // ---- sampled acceptance: the full sampler pipeline, sparse top-k path -------
@@ -1699,6 +2883,28 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   p.rows = reinterpret_cast<RowState *>(w + L.rows);
   p.acc = reinterpret_cast<AccIn *>(w + L.acc);
   p.blk = reinterpret_cast<u64 *>(w + L.blk);
+  p.hdr = reinterpret_cast<u64 *>(w + L.hdr);
+  p.ahist = reinterpret_cast<double *>(w + L.ahist);
+  p.above = reinterpret_cast<u64 *>(w + L.above);
+  p.ccount = reinterpret_cast<int32_t *>(w + L.ccount);
+  p.cand = reinterpret_cast<u64 *>(w + L.cand);
+  p.wsum = reinterpret_cast<u64 *>(w + L.wsum);
+  p.G = one_blocks_per_row(M, V);
+  p.C = p.G ? (V + p.G - 1) / p.G : 0;
+  if (p.G > 0) {
+    // one launch: every row's chunks resident in LDS, the steps separated by
+    // per-row meeting points (rej_one)
+    static std::once_flag lds_once;
+    std::call_once(lds_once, [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(rej_one),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                one_dyn_bytes(kOneChunk));
+      (void)hipGetLastError();   // a refusal shows up as the launch's own error
+    });
+    hipLaunchKernelGGL(rej_one, dim3(M * p.G), dim3(kOneThreads), (size_t)one_dyn_bytes(p.C),
+                       stream, p);
+    return hipGetLastError();
+  }
   const dim3 rows_grid(p.nb, M);
   hipLaunchKernelGGL(rej_rowmax, rows_grid, dim3(kBlock), 0, stream, p);
   const int with_hist = (p.top_p < 1.0) ? 1 : 0;

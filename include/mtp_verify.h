@@ -219,9 +219,12 @@ size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk);
  *   out_rollback     = base_len + a + 1 (cache length to restore to)
  *   logits, ldl      fp32 [M][ldl], 1 <= M <= 64, 1 <= V <= ldl
  *   draft_ids        int32 [M-1] (may be NULL when M == 1)
- *   ws, ws_bytes     at least mtp_accept_workspace_bytes(M, V); no contents
- *                    are kept between calls.  Calls that share one workspace
- *                    must not overlap in time.
+ *   ws, ws_bytes     at least mtp_accept_workspace_bytes(M, V), zero-filled
+ *                    before its first use.  Its first 260 KiB hold counters
+ *                    and tags that mtp_accept_rejection leaves ready for the
+ *                    next call (of either kind and any shape that fits);
+ *                    nothing else is kept between calls.  Calls that share
+ *                    one workspace must not overlap in time.
  */
 int mtp_accept_greedy(const float *logits, int M, int V, int64_t ldl, const int32_t *draft_ids,
                       int64_t base_len, int32_t *out_tokens, int32_t *out_counts,

@@ -269,3 +269,65 @@ def test_one_workspace_across_calls_and_shapes():
         check_same((host(t), host(c), int(host(r)[0])),
                    oracle.accept_rejection(z, q, d, u, 0.8, 0.9, 5),
                    f"rejection call {i} M={M} V={V}")
+
+
+ONE_LAUNCH_CASES = [
+    # name, M, V, logits: the one-launch path's branches and the shapes past it
+    ("flat rows (every entry a candidate, ties beyond the LDS room)", 2, 262144, "flat"),
+    ("integer logits (a fine bin too large to sort directly)", 4, 262144, "int"),
+    ("peaked rows (a handful of candidates)", 8, 262144, "peaked"),
+    ("N(0,1) rows (thousands of candidates)", 8, 262144, "normal"),
+    ("one row over 256 workgroups", 1, 262144, "normal"),
+    ("rows of every kind at once", 6, 65536, "mixed"),
+    ("too many workgroups for one launch (the chained kernels)", 16, 262144, "normal"),
+]
+
+
+@pytest.mark.parametrize("name,M,V,kind", ONE_LAUNCH_CASES)
+def test_rejection_one_launch_paths(name, M, V, kind):
+    rng = np.random.default_rng(M * 131 + V % 977 + len(kind))
+    log("rejection path:", name)
+    for trial in range(2):
+        if kind == "flat":
+            z = np.full((M, V), 0.75, np.float32)
+        elif kind == "int":
+            z = rng.integers(-3, 4, size=(M, V)).astype(np.float32)
+        elif kind == "peaked":
+            z = (rng.standard_normal((M, V)) * 300.0).astype(np.float32)
+        elif kind == "normal":
+            z = rng.standard_normal((M, V)).astype(np.float32)
+        else:
+            z = rng.standard_normal((M, V)).astype(np.float32)
+            z[1] *= np.float32(300.0)
+            z[2] = np.float32(1.25)
+            z[3] = rng.integers(-2, 3, size=V).astype(np.float32)
+        q = W.rand_dirichlet_rows(rng, max(M - 1, 1), V, 0.3)[:M - 1]
+        d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+        if M > 2:
+            d[M // 2] = int(rng.integers(0, V))
+        u = W.rand_uniforms(rng, M)
+        top_p = (0.95, 0.5)[trial]
+        o = oracle.accept_rejection(z, q, d, u, 0.6, top_p, 3, with_margins=True)
+        check_same(gpu_rej(z, q, d, u, 0.6, top_p, 3), o[:3], f"{name} trial={trial}", o[3])
+
+
+def test_rejection_back_to_back_calls_on_one_workspace():
+    # counters and tags left in the workspace by one call must serve the next:
+    # the same inputs forty times, then other inputs, all on one workspace
+    rng = np.random.default_rng(21)
+    M, V = 8, 262144
+    ws = bv.accept_workspace(M, V, DEV)
+    z = rng.standard_normal((M, V)).astype(np.float32)
+    q = W.rand_dirichlet_rows(rng, M - 1, V, 0.3)
+    d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+    d[4] = 11
+    u = W.rand_uniforms(rng, M)
+    o = oracle.accept_rejection(z, q, d, u, 0.6, 0.95, 1)
+    zt, qt, dt, ut = dev(z), dev(q), dev(d), dev(u)
+    outs = [bv.accept_rejection(zt, qt, dt, ut, 0.6, 0.95, 1, ws=ws) for _ in range(40)]
+    for i, (t, c, r) in enumerate(outs):
+        check_same((host(t), host(c), int(host(r)[0])), o, f"call {i}")
+    z2 = (rng.standard_normal((M, V)) * 300.0).astype(np.float32)
+    o2 = oracle.accept_rejection(z2, q, d, u, 0.6, 0.95, 1)
+    t, c, r = bv.accept_rejection(dev(z2), qt, dt, ut, 0.6, 0.95, 1, ws=ws)
+    check_same((host(t), host(c), int(host(r)[0])), o2, "other inputs")
