@@ -19,7 +19,7 @@ __all__ = [
     "gemm_plan_info",
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
     "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
-    "choose_draft_depth", "DepthStats", "verify_attention", "attention_workspace_bytes",
+    "choose_draft_depth", "DepthStats", "DepthStatsDevice", "verify_attention", "attention_workspace_bytes",
     "kv_snapshot", "kv_append", "kv_restore", "read_probe",
     "read_probe_shapes",
     "verify_gemm", "verify_moe", "accept_greedy", "accept_greedy_static", "accept_rejection",
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.mtp_depth_observe.argtypes = [P, P, i32, i32, i32, D]
         L.mtp_depth_estimate.restype = i32
         L.mtp_depth_estimate.argtypes = [P, P, i32, P]
+        L.mtp_depth_observe_device.restype = i32
+        L.mtp_depth_observe_device.argtypes = [P, P, i32, i32, P, D, P, P, P, P, P]
         _lib = L
         return L
 
@@ -394,6 +396,29 @@ class DepthStats:
         _check(lib().mtp_depth_estimate(_host_ptr(self.reached), _host_ptr(self.accepted),
                                         self.dmax, _host_ptr(prob)))
         return prob
+
+
+class DepthStatsDevice:
+    """Live per-position acceptance kept on the GPU (mtp_depth_observe_device):
+    observe() enqueues the update from an accept call's counts and the next
+    depth choice on the stream; nothing is read back unless asked for."""
+
+    def __init__(self, dmax: int, cost, device, keep: float = 1.0):
+        self.dmax, self.keep = int(dmax), float(keep)
+        self.reached = torch.zeros(self.dmax, dtype=torch.float64, device=device)
+        self.accepted = torch.zeros(self.dmax, dtype=torch.float64, device=device)
+        self.prob = torch.zeros(self.dmax, dtype=torch.float64, device=device)
+        self.cost = torch.as_tensor(cost, dtype=torch.float64).to(device).contiguous()
+        if self.cost.numel() != self.dmax + 1:
+            raise ValueError("cost needs dmax + 1 entries")
+        self.choice = torch.zeros(1, dtype=torch.int32, device=device)
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def observe(self, depth: int, counts: torch.Tensor, stream=None):
+        _check(lib().mtp_depth_observe_device(
+            _ptr(self.reached), _ptr(self.accepted), self.dmax, int(depth), _ptr(counts),
+            self.keep, _ptr(self.cost), _ptr(self.choice), _ptr(self.prob), _ptr(self.err),
+            _stream(stream)))
 
 
 def attention_workspace_bytes(M: int, Hq: int, Hkv: int, D: int, L: int) -> int:

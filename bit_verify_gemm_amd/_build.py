@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "controller.cpp", "gemm.hip", "accept.hip", "moe.hip", "attention.hip",
-           "kvcache.hip", "probe.hip"]
+           "kvcache.hip", "probe.hip", "depth.hip"]
 HEADERS = ["device.h", "engine.h", "internal.h"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -226,6 +226,23 @@ int mtp_accept_greedy_static(const float *logits, int M, int V, int64_t ldl,
                     who);
 }
 
+int mtp_depth_observe_device(double *reached, double *accepted, int dmax, int depth,
+                             const int32_t *counts, double keep, const double *cost,
+                             int32_t *choice, double *prob, int32_t *err, void *stream) {
+  const char *who = "mtp_depth_observe_device";
+  if (!reached || !accepted || !counts)
+    return fail(MTP_ERR_NULL, "%s: reached, accepted and counts are required", who);
+  if (choice && !cost) return fail(MTP_ERR_NULL, "%s: cost is required with choice", who);
+  if (dmax < 1 || dmax > 63) return fail(MTP_ERR_SHAPE, "%s: dmax=%d out of [1, 63]", who, dmax);
+  if (depth < 0) return fail(MTP_ERR_SHAPE, "%s: depth=%d < 0", who, depth);
+  if (!(keep >= 0.0 && keep <= 1.0))
+    return fail(MTP_ERR_VALUE, "%s: keep=%g out of [0, 1]", who, keep);
+  return hip_status(mtp::launch_depth_observe(reached, accepted, dmax, depth, counts, keep, cost,
+                                              choice, prob, err,
+                                              static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 int mtp_accept_rejection(const float *logits, int M, int V, int64_t ldl,
                          const float *draft_probs, int64_t ldq, const int32_t *draft_ids,
                          const float *uniforms, float temperature, float top_p, int64_t base_len,

@@ -121,4 +121,9 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
                       const float *gu_global, const uint8_t *dn_packed, const float *dn_global,
                       float *out, uint16_t *h_out, void *ws, hipStream_t stream);
 
+// depth.hip
+hipError_t launch_depth_observe(double *reached, double *accepted, int dmax, int depth,
+                                const int32_t *counts, double keep, const double *cost,
+                                int32_t *choice, double *prob, int32_t *err, hipStream_t stream);
+
 }  // namespace mtp

@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 5
+#define MTP_ABI_VERSION 6
 
 enum {
   MTP_OK = 0,
@@ -458,6 +458,32 @@ int mtp_choose_draft_depth(const double *accept_prob, const double *cost, int dm
 int mtp_depth_observe(double *reached, double *accepted, int dmax, int depth, int n_accepted,
                       double keep);
 int mtp_depth_estimate(const double *reached, const double *accepted, int dmax, double *prob);
+
+/*
+ * The same controller on the device, enqueued on `stream` after the accept
+ * call of a step of depth `depth`, so that the host reads nothing per step
+ * ("Faster Gemma 4 on MLX with multi-token prediction", fourth and fifth
+ * paragraphs: the runtime tunes the depth from acceptance and verify
+ * timings, with no return to the CPU).  With n = counts[0] (the accepted
+ * count the accept call wrote, device int32):
+ *   reached, accepted   device fp64 [dmax], updated as mtp_depth_observe
+ *                       updates them (the same fp64 operations, so the two
+ *                       agree bit for bit);
+ *   prob (optional)     device fp64 [dmax]: mtp_depth_estimate of the update;
+ *   choice (optional)   device int32 [1]: mtp_choose_draft_depth of prob and
+ *                       cost (device fp64 [dmax + 1], required with choice).
+ * The host may read choice whenever it likes (for instance with an
+ * asynchronous copy behind an event), or a drafting kernel may read it on
+ * the device.  Device-side errors go to err (optional, device int32 [1]):
+ * 0 ok; 1 counts[0] outside [0, depth] (the statistics are left as they
+ * were); 2 a cost <= 0 or NaN (choice 0).  Host errors, returned before
+ * anything is enqueued: MTP_ERR_NULL (reached, accepted or counts; cost with
+ * choice), MTP_ERR_SHAPE (dmax outside [1, 63], depth < 0), MTP_ERR_VALUE
+ * (keep outside [0, 1]).
+ */
+int mtp_depth_observe_device(double *reached, double *accepted, int dmax, int depth,
+                             const int32_t *counts, double keep, const double *cost,
+                             int32_t *choice, double *prob, int32_t *err, void *stream);
 
 /*
  * Read-bandwidth probe (a measurement aid, not a step of the verify pass):

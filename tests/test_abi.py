@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bv.abi_version() == 5
+    assert bv.abi_version() == 6
 
 
 def test_packed_sizes():
@@ -247,3 +247,21 @@ def test_read_probe_rejects_bad_arguments():
     assert L.mtp_read_probe(FAKE, 16, None, 0, None) == -1
     assert L.mtp_read_probe(FAKE_ODD, 16, FAKE, 0, None) == -3
     assert L.mtp_read_probe(FAKE, 17, FAKE, 0, None) == -3
+
+
+def test_depth_observe_device_rejects_bad_arguments_on_the_host():
+    # every check below fails before anything is enqueued (no GPU needed)
+    L = bv.lib()
+    buf = (ctypes.c_double * 64)()
+    cnt = (ctypes.c_int32 * 2)()
+    P = ctypes.cast
+    r = P(buf, ctypes.c_void_p)
+    c = P(cnt, ctypes.c_void_p)
+    f = L.mtp_depth_observe_device
+    assert f(None, r, 4, 1, c, 1.0, None, None, None, None, None) == -1
+    assert f(r, r, 4, 1, None, 1.0, None, None, None, None, None) == -1
+    assert f(r, r, 4, 1, c, 1.0, None, c, None, None, None) == -1      # choice needs cost
+    assert f(r, r, 0, 1, c, 1.0, None, None, None, None, None) == -2
+    assert f(r, r, 64, 1, c, 1.0, None, None, None, None, None) == -2
+    assert f(r, r, 4, -1, c, 1.0, None, None, None, None, None) == -2
+    assert f(r, r, 4, 1, c, 1.5, None, None, None, None, None) == -7
