@@ -15,7 +15,7 @@
 // Per 32-position step a wave (16 query rows) computes S^T = K Q^T
 // (positions x rows) with K from LDS and Q^T held in registers, updates the
 // running row maxima and sums (online softmax, fp32), and adds
-// O^T += V^T P^T with V^T from LDS and P^T (bf16) taken straight from the
+// O^T += V^T P^T with V^T from LDS and P^T (two bf16 parts) taken straight from the
 // S^T accumulator: the reduction slots of the second product are the
 // positions 4g..4g+3 and 16+4g..16+4g+3 that lane group g already holds, so
 // no transpose is needed.  Chunks of the KV range run in separate
@@ -215,18 +215,30 @@ __global__ __launch_bounds__(kMaxRowWaves * kWave) void vattn_partial(AttnArgs a
       for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
       m = mn;
     }
-    u32x4 pb;
-    pb.x = (uint32_t)f32_to_bf16_rne(pv[0]) | ((uint32_t)f32_to_bf16_rne(pv[1]) << 16);
-    pb.y = (uint32_t)f32_to_bf16_rne(pv[2]) | ((uint32_t)f32_to_bf16_rne(pv[3]) << 16);
-    pb.z = (uint32_t)f32_to_bf16_rne(pv[4]) | ((uint32_t)f32_to_bf16_rne(pv[5]) << 16);
-    pb.w = (uint32_t)f32_to_bf16_rne(pv[6]) | ((uint32_t)f32_to_bf16_rne(pv[7]) << 16);
+    // P as two bf16 parts, ph = bf16(p) and pl = bf16(p - ph) (the
+    // difference is exact in fp32): ph + pl holds p to 16 significant bits
+    // (relative error below 2^-17), and both products with V are exact in
+    // the fp32 accumulation of the MFMA
+    uint16_t ph[8], pl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ph[i] = f32_to_bf16_rne(pv[i]);
+      pl[i] = f32_to_bf16_rne(pv[i] - __uint_as_float((uint32_t)ph[i] << 16));
+    }
+    auto pack = [](const uint16_t *h) {
+      return u32x4{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                   (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16)};
+    };
+    const u32x4 pbh = pack(ph), pbl = pack(pl);
     // O^T += V^T P^T: V^T rows d = 16dt + n, slots = the same eight positions
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const uint16_t *vrow = &s.vt[(16 * dt + n) * Lds<D>::vRow];
       const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 4 * g);
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 + 4 * g);
-      o[dt] = mfma_16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, o[dt]);
+      const u32x4 vt = u32x4{lo.x, lo.y, hi.x, hi.y};
+      o[dt] = mfma_16x16x32(vt, pbh, o[dt]);
+      o[dt] = mfma_16x16x32(vt, pbl, o[dt]);
     }
   }
   // partials of this chunk: lane (n, g) holds d = 16dt + 4g + i of row r

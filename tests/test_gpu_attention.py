@@ -1,9 +1,11 @@
 """GPU parity of mtp_verify_attention against the oracle.
 
-Bar, per element: |out - oracle| <= 2^-7 * sum_j p_j |v_j| + 1e-6.  The GPU
-rounds the probabilities to bf16 for the product with V (relative error at
-most 2^-8 each, so at most 2^-8 of that sum); fp32 scores, softmax and
-accumulation add far less.  The factor two is the margin."""
+Bar, per element: |out - oracle| <= 1e-3 * sum_j p_j |v_j| + 1e-6, the
+accuracy the verify GEMMs are held to (1e-3 of the magnitude sum of the
+products), set by that requirement rather than by the kernel.  (The kernel
+holds each probability as two bf16 parts, 16 significant bits, so its
+products carry relative errors below 2^-17; its fp32 scores, softmax and
+accumulation stay far inside the bar.)"""
 import numpy as np
 import pytest
 import torch
@@ -30,8 +32,9 @@ def check(q, k, v, L, what, scale=None):
     o = host(bv.verify_attention(dev(q), dev(k), dev(v), L, scale))
     ro, rb = oracle.verify_attention(q, k, v, L, scale)
     err = np.abs(o - ro)
-    bad = err > 2.0 ** -7 * rb + 1e-6
-    log(what, "max err / bound", float((err / (2.0 ** -7 * rb + 1e-6)).max()))
+    bar = 1e-3 * rb + 1e-6
+    bad = err > bar
+    log(what, "max err / bound", float((err / bar).max()))
     assert not bad.any(), f"{what}: {np.argwhere(bad)[:4].tolist()} gpu {o[bad][:4]} oracle {ro[bad][:4]}"
 
 
