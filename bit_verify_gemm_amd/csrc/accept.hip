@@ -1275,16 +1275,37 @@ __device__ __forceinline__ void draw_weights_v(const RowState &rs, double T, boo
   }
 }
 
-__device__ __forceinline__ void store_row_state(RowState *dst, const RowState &rs) {
-  u64 w[3];
-  __builtin_memcpy(w, &rs, sizeof(w));
-  u64 *d = reinterpret_cast<u64 *>(dst);
-  for (int i = 0; i < 3; ++i) st_ag(d + i, w[i]);
+// A row's state in six tagged words of its page (tag << 32 | 32 bits):
+// kappa, cutoff, all, the two halves of mass, and zmax.  Each word carries
+// the tag, so a reader that sees all six tags has the whole state in one
+// round trip, whatever order the stores landed in.
+constexpr int kStateWords = 6;
+
+__device__ __forceinline__ void publish_state(u64 *rp, uint32_t tag, const RowState &rs) {
+  const u64 mb = (u64)__double_as_longlong(rs.mass);
+  const uint32_t v[kStateWords] = {rs.kappa, (uint32_t)rs.cutoff, (uint32_t)rs.all, (uint32_t)mb,
+                                   (uint32_t)(mb >> 32), __float_as_uint(rs.zmax)};
+  for (int i = 0; i < kStateWords; ++i) st_ag(rp + kRowState + i, ((u64)tag << 32) | v[i]);
 }
 
 __device__ __forceinline__ RowState row_state_of(const u64 *w) {
   RowState rs;
   __builtin_memcpy(&rs, w, sizeof(rs));
+  return rs;
+}
+
+// Called by a whole wave: lanes 0..5 wait for their word; the state is
+// returned in every lane.
+__device__ __forceinline__ RowState wait_state(const u64 *rp, uint32_t tag, u64 *err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t w = lane < kStateWords ? (uint32_t)wait_slot(rp + kRowState + lane, tag, err) : 0u;
+  RowState rs;
+  rs.zmax = __uint_as_float((uint32_t)__shfl((int)w, 5));
+  rs.kappa = (uint32_t)__shfl((int)w, 0);
+  rs.cutoff = __shfl((int)w, 1);
+  rs.all = __shfl((int)w, 2);
+  const u64 mb = (u64)(uint32_t)__shfl((int)w, 3) | ((u64)(uint32_t)__shfl((int)w, 4) << 32);
+  rs.mass = __longlong_as_double((long long)mb);
   return rs;
 }
 
@@ -1429,7 +1450,6 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       const u64 *tr = p.total + 3 * row;
       const Fx S = fx_from3(ld_ag(tr), ld_ag(tr + 1), ld_ag(tr + 2));
       const RowState rs = RowState{zmax, 0u, p.V, 1, fx_to_double(S)};
-      store_row_state(p.rows + row, rs);
       if (row < p.M - 1) {
         int x;
         bool valid;
@@ -1437,8 +1457,8 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         load_draft(p, row, x, valid, zx, qx);
         publish_acc(p, row, rs, x, valid, zx, qx);
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      st_ag(rp + kRowState, (u64)tag << 32);
+      __builtin_amdgcn_s_waitcnt(0);   // the acceptance input before the state
+      publish_state(rp, tag, rs);
     }
   } else {
     // (2b) the range [blo, bhi] of approximate bins that holds the cut, found
@@ -1875,10 +1895,9 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       }
       if (tid == 0) {
         const RowState rs = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
-        store_row_state(p.rows + row, rs);
         if (row < p.M - 1) publish_acc(p, row, rs, s_x, s_x >= 0, s_zx, s_qx);
-        __builtin_amdgcn_s_waitcnt(0);
-        st_ag(rp + kRowState, (u64)tag << 32);
+        __builtin_amdgcn_s_waitcnt(0);   // the acceptance input before the state
+        publish_state(rp, tag, rs);
       }
     }
   }
@@ -1893,12 +1912,13 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   {
     const bool residual = row < p.M - 1;
     const int L = one_range(C), rb = wave * L;
-    if (tid == 0) {
-      wait_slot(rp + kRowState, tag, err);
-      const u64 *rw = reinterpret_cast<const u64 *>(p.rows + row);
-      for (int w = 0; w < 3; ++w) s_w[w] = ld_ag(rw + w);
-      s_fr = kNone;
-      s_fe = kNone;
+    if (wave == 0) {
+      const RowState rs0 = wait_state(rp, tag, err);
+      if (lane == 0) {
+        __builtin_memcpy(s_w, &rs0, sizeof(rs0));
+        s_fr = kNone;
+        s_fe = kNone;
+      }
     }
     float qv[kKPer], zv[kKPer];
 #pragma unroll
@@ -1985,12 +2005,17 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         const u64 rej = __ballot(reject);
         const int a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
         const bool residual = a < p.M - 1;
+        {   // row a's state (its words are all in: every row arrived after them)
+          const RowState rsa = wait_state(p.hdr + (size_t)a * kPageWords, tag, err);
+          if (lane == 0) __builtin_memcpy(s_w + 3, &rsa, sizeof(rsa));
+        }
         Fx br[kMaxOneBlocks / kWave], be[kMaxOneBlocks / kWave];
         int bfr = kNone, bfe = kNone;
 #pragma unroll
         for (int c = 0; c < kMaxOneBlocks / kWave; ++c) {
           const int q = c * kWave + lane;
           br[c] = be[c] = fx_zero();
+          if (c * kWave >= G) continue;
           if (q < G) {
             const u64 *o = p.blk + kBlkWords * (a * G + q);
             br[c] = Fx{ld_ag(o), ld_ag(o + 1)};
@@ -2030,6 +2055,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           int lastnz = -1;
 #pragma unroll
           for (int c = 0; c < kMaxOneBlocks / kWave; ++c) {
+            if (c * kWave >= G) break;   // (uniform)
             const int q = c * kWave + lane;
             const Fx w = use_res ? br[c] : be[c];
             Fx incl = w;
@@ -2093,8 +2119,6 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           s_lastnz = rng;
           s_before = before;
           s_fr = use_res ? 1 : 0;
-          const u64 *rw = reinterpret_cast<const u64 *>(p.rows + a);
-          for (int w = 0; w < 3; ++w) s_w[3 + w] = ld_ag(rw + w);
           s_abv_lo = target.lo;
           s_abv_hi = target.hi;
         }
