@@ -15,7 +15,8 @@
 //              slot's expert through the engine of the dense GEMM (engine.h)
 //              for all rows of that expert and writes
 //              h = bf16(silu(gate) * up) per pair.
-//  2. down:    the same routing, then y[pair] = W_d[e] . h[pair]; each
+//  2. down:    the routing gate_up published in the workspace (no second
+//              ranking), then y[pair] = W_d[e] . h[pair]; each
 //              (pair, 16-column tile) it finishes counts one arrival for the
 //              pair's token, and the arrival that completes a token's valid
 //              pairs for a tile writes out[t] = sum over slots in slot order
@@ -38,7 +39,7 @@ constexpr int kMaxPairs = 1024;
 constexpr int kNoExpert = 0x7FFFFFFF;   // routing key of a pair whose id is outside [0, E)
 
 struct MoeLayout {
-  size_t cnt, h, y, bytes;
+  size_t cnt, h, y, route, bytes;
 };
 
 MoeLayout moe_layout(int T, int H, int F, int topk) {
@@ -53,6 +54,7 @@ MoeLayout moe_layout(int T, int H, int F, int topk) {
   L.cnt = take(sizeof(uint32_t) * T * eng::tiles_of(H));
   L.h = take(sizeof(uint16_t) * P * F);
   L.y = take(sizeof(float) * P * H);
+  L.route = take(sizeof(int32_t) * (2 * P + 3 * P));   // order, key, then (e, first, rows) per slot
   L.bytes = o;
   return L;
 }
@@ -73,6 +75,7 @@ struct MoeArgs {
   uint32_t *cnt;          // [token][16-column tile of H]: pairs whose y is stored
   uint16_t *h;            // [pair][F]
   float *y;               // [pair][H]
+  int32_t *route;         // the routing gate_up derived: order [P], key [P], slots [P][3]
 };
 
 // The routing as one workgroup sees it (LDS).
@@ -226,6 +229,39 @@ __device__ void clear_call_state(const MoeArgs &a, const Route &R) {
         for (int f = threadIdx.x; f < a.F; f += blockDim.x) a.h_out[(int64_t)p * a.F + f] = 0;
 }
 
+// The routing for the down kernel (which runs after this one): workgroup
+// (0, 0) writes the ranked pairs and their keys, the first workgroup of
+// each slot its (expert, first rank, rows).
+__device__ void publish_route(const MoeArgs &a, const Route &R) {
+  if (blockIdx.x != 0) return;
+  if (blockIdx.y == 0)
+    for (int p = threadIdx.x; p < a.P; p += blockDim.x) {
+      a.route[p] = R.order[p];
+      a.route[a.P + p] = R.key[p];
+    }
+  if (threadIdx.x == 0) {
+    int32_t *sl = a.route + 2 * a.P + 3 * blockIdx.y;
+    sl[0] = R.e;
+    sl[1] = R.first;
+    sl[2] = R.rows;
+  }
+}
+
+// The down kernel's view of the routing, read from what gate_up published.
+__device__ void load_route(const MoeArgs &a, Route &R, int slot) {
+  for (int p = threadIdx.x; p < a.P; p += blockDim.x) {
+    R.order[p] = a.route[p];
+    R.key[p] = a.route[a.P + p];
+  }
+  if (threadIdx.x == 0) {
+    const int32_t *sl = a.route + 2 * a.P + 3 * slot;
+    R.e = sl[0];
+    R.first = sl[1];
+    R.rows = sl[2];
+  }
+  __syncthreads();
+}
+
 // silu(v) = v / (1 + exp(-v)), written so that no intermediate overflows:
 // for v < 0 it is v * e / (1 + e) with e = exp(v) (gradual underflow).
 __device__ __forceinline__ float silu(float v) {
@@ -286,6 +322,7 @@ __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   __shared__ Route R;
   route(a, R, blockIdx.y);
   clear_call_state(a, R);
+  publish_route(a, R);
   const int e = __builtin_amdgcn_readfirstlane(R.e);
   if (e < 0) return;  // a slot past the unique experts (whole workgroup)
   const int first = __builtin_amdgcn_readfirstlane(R.first);
@@ -410,7 +447,7 @@ template <int FMT, int PP, bool LOCAL>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ Route R;
-  route(a, R, blockIdx.y);
+  load_route(a, R, blockIdx.y);
   const int e = __builtin_amdgcn_readfirstlane(R.e);
   if (e < 0) return;  // a slot past the unique experts (whole workgroup)
   const int first = __builtin_amdgcn_readfirstlane(R.first);
@@ -544,6 +581,7 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
   a.cnt = reinterpret_cast<uint32_t *>(w + L.cnt);
   a.h = reinterpret_cast<uint16_t *>(w + L.h);
   a.y = reinterpret_cast<float *>(w + L.y);
+  a.route = reinterpret_cast<int32_t *>(w + L.route);
   a.rc = moe_rows(format, T, H, F);
   const int slots = (a.P < E) ? a.P : E;
   MoePlan gu = moe_plan(format, 2 * F, H, a.rc, kMoeTiles, true);
