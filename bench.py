@@ -461,7 +461,7 @@ def extra_lm_head_and_accept(bv, dev, steps, warmup, gemm_only=False):
     u1 = u.view(1, M)
     d1 = dd.view(1, M - 1)
     q1 = q.view(1, M - 1, V)
-    sws = torch.empty(bv.accept_sampled_workspace_bytes(1, M, V, 64, True), dtype=torch.uint8,
+    sws = torch.zeros(bv.accept_sampled_workspace_bytes(1, M, V, 64, True), dtype=torch.uint8,
                       device=dev)
     souts = (torch.empty((1, M), dtype=torch.int32, device=dev),
              torch.empty((1, 2), dtype=torch.int32, device=dev),

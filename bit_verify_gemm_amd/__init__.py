@@ -18,7 +18,7 @@ __all__ = [
     "packed_weight_bytes", "pack_weights", "gemm_workspace_bytes", "gemm_workspace",
     "gemm_plan_info",
     "moe_workspace_bytes", "accept_workspace_bytes", "accept_workspace",
-    "Sampler", "accept_sampled", "accept_sampled_workspace_bytes",
+    "Sampler", "accept_sampled", "accept_sampled_workspace", "accept_sampled_workspace_bytes",
     "choose_draft_depth", "DepthStats", "DepthStatsDevice", "verify_attention", "attention_workspace_bytes",
     "kv_snapshot", "kv_append", "kv_restore", "read_probe",
     "read_probe_shapes",
@@ -308,6 +308,14 @@ def accept_sampled_workspace_bytes(B: int, M: int, V: int, top_k: int, penalties
     return int(lib().mtp_accept_sampled_workspace_bytes(B, M, V, top_k, int(bool(penalties))))
 
 
+def accept_sampled_workspace(B: int, M: int, V: int, top_k: int, penalties: bool,
+                             device) -> torch.Tensor:
+    """A zero-filled workspace for mtp_accept_sampled (its head holds counters
+    that each call leaves zero)."""
+    return torch.zeros(max(accept_sampled_workspace_bytes(B, M, V, top_k, penalties), 1),
+                       dtype=torch.uint8, device=device)
+
+
 def accept_sampled(logits: torch.Tensor, draft_ids: torch.Tensor | None, uniforms: torch.Tensor,
                    params: Sampler, draft_probs: torch.Tensor | None = None,
                    draft_topk: tuple | None = None, history: torch.Tensor | None = None,
@@ -336,7 +344,7 @@ def accept_sampled(logits: torch.Tensor, draft_ids: torch.Tensor | None, uniform
         tpr = torch.empty((B, M, K), dtype=torch.float32, device=dev)
     need = accept_sampled_workspace_bytes(B, M, V, int(params.top_k), params.penalties)
     if ws is None or _nbytes(ws) < need:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     q = qi = qp = None
     ldq, Kq = 0, 0
     if M > 1:

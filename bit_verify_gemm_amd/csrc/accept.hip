@@ -2239,6 +2239,13 @@ struct SampArgs {
   double *se;                //   e
   int32_t *nkept;            // [rows]
   AccIn *acc;                // [rows]
+  // samp_one
+  uint32_t *rowcnt;          // [rows] arrivals (workspace head, zero between calls)
+  uint32_t *seqcnt;          // [B] rows done
+  u64 *info;                 // [rows][G] (smallest candidate key << 32) | candidate count
+  u64 *cand;                 // [rows][G][C] candidates (key << 32 | index), index order
+  u64 *res;                  // [rows] (draft rejected << 31) | token this row would draw
+  int G, C, pen;
 };
 
 __device__ __forceinline__ const float *samp_src(const SampArgs &p, int row) {
@@ -2802,6 +2809,695 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
   }
 }
 
+// ---- sampled acceptance in one launch ----------------------------------------
+//
+// The pipeline above in one launch of G workgroups per row, with no
+// workgroup ever waiting for another.  Each workgroup penalises its chunk
+// of up to kOneChunk entries in registers, bins it by d = chunk max - z
+// (sbin), and takes as candidates its entries in the bins up to the first
+// whose count from the top reaches K: a superset of the chunk's own top K.
+// It writes them in index order to its own segment of the workspace,
+// publishes their number and smallest key (0 when the chunk holds fewer
+// than K entries, all of them candidates), and arrives on the row's
+// counter.  The last workgroup of the row to arrive resolves the row alone:
+//   - kappa = the largest published key.  The workgroup that published it
+//     holds at least K entries with keys >= kappa, and every workgroup's
+//     entries with keys >= kappa are among its candidates, so the set S of
+//     candidates with keys >= kappa holds the row's top K;
+//   - a histogram of S over bins of d = row max - z finds the bin where the
+//     count from the top reaches K; the entries of S up to that bin are
+//     sorted (key descending, index ascending) and the first K are the
+//     row's top K in the order of probability.  When that bin is too full
+//     to sort (heavy ties) a radix select finds the K-th key instead, and
+//     the ties at it are taken in index order;
+//   - softmax, top-p and min-p on exact fixed-point prefix sums, p', the
+//     row's acceptance input, and the draw the row would make if the
+//     accepted run stopped at it (the residual for a draft row, the bonus
+//     for the last), in index order over its support, as samp_row and
+//     samp_draw do;
+//   - the row's verdict and token go to the workspace; the last row of the
+//     sequence to finish derives the accepted run and writes the outputs.
+// Data crossing workgroups follows the rules of rej_one (agent-scope
+// atomic stores and loads, each writer's stores complete before it
+// arrives).  The counters live in the workspace head; each call leaves
+// them zero.
+
+constexpr int kSHB = 2048;              // bins of d: exponent and 5 mantissa bits
+constexpr int kSBinBase = 3072;         // bin 0 takes every d below 2^-31
+constexpr int kSRoom = 8192;            // entries of S the resolver keeps in LDS
+constexpr int kSSortMax = 2048;         // entries the resolver sorts
+constexpr int kSMaxG = 256;
+constexpr int kSMaxRows = 4096;
+constexpr int kSMaxSeqs = 1024;
+constexpr int kSCandBudget = 16384;     // expected candidates per row the launch rule allows
+constexpr int kSOffL = 0;                           // u64 [kSRoom]: S (first the penalty window)
+constexpr int kSOffSort = kSOffL + 8 * kSRoom;      // u64 [kSSortMax]: entries to sort
+constexpr int kSOffE = kSOffSort + 8 * kSSortMax;   // fp64 [kMaxTopK]: e by rank
+constexpr int kSOffP = kSOffE + 8 * kMaxTopK;       //   p' by rank
+constexpr int kSOffQ = kSOffP + 8 * kMaxTopK;       //   q(id) by rank
+constexpr int kSOffId = kSOffQ + 8 * kMaxTopK;      // int32 [kMaxTopK]: id by rank
+constexpr int kSOffQid = kSOffId + 4 * kMaxTopK;    // the sparse draft list
+constexpr int kSOffQpr = kSOffQid + 4 * kMaxTopK;
+constexpr int kSDyn = kSOffQpr + 4 * kMaxTopK;
+static_assert(4 * kMaxPenaltyWindow <= 8 * kSRoom, "the penalty window fits where S goes");
+static_assert(kSHB == 2 * kOneThreads, "two bins per thread");
+static_assert(kSSortMax == 2 * kOneThreads, "one compare-exchange per thread and step");
+static_assert(kMaxTopK <= kOneThreads && kMaxTopK <= kSSortMax, "one kept entry per thread");
+static_assert(kSMaxG <= 4 * kWave, "four segments per lane");
+static_assert(kWave == 64, "the accepted run takes one lane per row");
+
+// Bin of z below zmax (a key >= z's): the exponent and leading 5 mantissa
+// bits of d = zmax - z, shifted and clamped, so bins are about 3% of d wide.
+// d is monotone in z, so each bin is an interval of keys.
+__device__ __forceinline__ int sbin(float zmax, float z) {
+  const int b = (int)(__float_as_uint(zmax - z) >> 18) - kSBinBase;
+  return b < 0 ? 0 : (b < kSHB ? b : kSHB - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  for (int s = kWave / 2; s > 0; s >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, s));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  for (int s = kWave / 2; s > 0; s >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, s));
+  return v;
+}
+
+// Inclusive prefix of v over the threads (thread order), and the total.
+__device__ int iscan_one(int v, int *wsum, int &total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int incl = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < kOneWaves; ++w) {
+    if (w < wave) before += wsum[w];
+    total += wsum[w];
+  }
+  return before + incl;
+}
+
+// Place in an LDS list for the lanes with `flag` (one atomic per wave on the
+// list's count; order within the list unspecified).  Whole waves call it.
+__device__ __forceinline__ int wave_append(bool flag, int *count) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const u64 b = __ballot(flag);
+  int base = 0;
+  if (lane == 0 && b) base = atomicAdd(count, __popcll(b));
+  base = __shfl(base, 0);
+  return base + __popcll(b & ((1ull << lane) - 1ull));
+}
+
+// Sorts the n (<= kSSortMax) distinct non-zero values of a (LDS, room for
+// kSSortMax) in descending order and returns where they are: in b (room for
+// n) for n <= 256, ranked by counting with 1024 / n2 lanes per value, else
+// in a by a bitonic network.  The whole workgroup calls it.
+__device__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
+  const int tid = threadIdx.x;
+  int n2 = 16;
+  while (n2 < n) n2 <<= 1;
+  __syncthreads();
+  if (n2 <= 256) {
+    const int P = kOneThreads / n2, e = tid / P, part = tid - e * P;
+    const u64 mine = e < n ? a[e] : 0ull;
+    int rank = 0;
+    if (e < n)
+      for (int k = part; k < n; k += P) rank += a[k] > mine ? 1 : 0;
+    for (int s = P / 2; s > 0; s >>= 1) rank += __shfl_xor(rank, s);
+    if (e < n && part == 0) b[rank] = mine;
+    __syncthreads();
+    return b;
+  }
+  for (int i = n + tid; i < n2; i += kOneThreads) a[i] = 0ull;
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+      if (tid < n2 / 2) {
+        const int i = ((tid & ~(j - 1)) << 1) | (tid & (j - 1)), l = i | j;
+        const u64 x = a[i], y = a[l];
+        if ((i & k) == 0 ? x < y : x > y) {
+          a[i] = y;
+          a[l] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return a;
+}
+
+__device__ __forceinline__ uint32_t add_ag32(uint32_t *c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void clear_ag32(uint32_t *c) {
+  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// grid (rows * G), kOneThreads threads, kSDyn bytes of dynamic LDS.
+__global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  __shared__ uint32_t hs[kSHB];
+  __shared__ int koff[kKPer * kOneWaves + 1];
+  __shared__ int wcnt[kOneWaves];
+  __shared__ uint32_t wkey[kOneWaves];
+  __shared__ Fx red[kOneWaves];
+  __shared__ int segoff[kSMaxG + 1];
+  __shared__ Fx s_mass;
+  __shared__ double s_px;
+  __shared__ uint32_t s_kmax, s_kap;
+  __shared__ int s_nl, s_bst, s_A, s_n2, s_last, s_ns, s_m, s_dig, s_abv;
+  __shared__ int s_cp, s_cm, s_qk, s_fr, s_fp, s_pick, s_lastw;
+  const int G = p.G, C = p.C, row = blockIdx.x / G, g = blockIdx.x - row * G;
+  const int seq = row / p.M, pos = row - seq * p.M;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int j0 = g * C, n = min(C, p.V - j0), K = p.K;
+
+  // (1) the chunk, penalised in registers: entry k * kOneThreads + t is
+  // thread t's k-th
+  const float *zr = p.z + (int64_t)row * p.ldl + j0;
+  float v[kKPer];
+#pragma unroll
+  for (int k = 0; k < kKPer; ++k) {
+    const int i = k * kOneThreads + tid;
+    v[k] = i < n ? zr[i] : 0.0f;
+  }
+  for (int i = tid; i < kSHB; i += kOneThreads) hs[i] = 0u;
+  if (p.pen) {
+    // the window's tokens inside the chunk, then each entry's count
+    int32_t *lt = reinterpret_cast<int32_t *>(dyn + kSOffL);
+    if (tid == 0) s_nl = 0;
+    __syncthreads();
+    const int Lh = p.htok ? max(0, min(p.hlen[seq], (int)p.ldh)) : 0;
+    const int total = Lh + pos, w0 = max(0, total - p.last_n);
+    for (int c = w0 + tid; c < total; c += kOneThreads) {
+      const int t = c < Lh ? p.htok[(int64_t)seq * p.ldh + c]
+                           : p.drafts[(int64_t)seq * (p.M - 1) + (c - Lh)];
+      if (t >= j0 && t < j0 + n) lt[atomicAdd(&s_nl, 1)] = t;
+    }
+    __syncthreads();
+    const int nl = s_nl;
+#pragma unroll
+    for (int k = 0; k < kKPer; ++k) {
+      const int i = k * kOneThreads + tid;
+      int c = 0;
+      for (int q = 0; q < nl; ++q) c += lt[q] == j0 + i ? 1 : 0;
+      if (c && i < n) v[k] = penalise(v[k], c, p);
+    }
+  }
+  // the chunk maximum by key (+0 above -0), then the count histogram
+  uint32_t km = 0u;
+#pragma unroll
+  for (int k = 0; k < kKPer; ++k)
+    if (k * kOneThreads + tid < n) km = max(km, fkey(v[k]));
+  km = wave_umax(km);
+  if (lane == 0) wkey[wave] = km;
+  __syncthreads();
+  km = 0u;
+  for (int w = 0; w < kOneWaves; ++w) km = max(km, wkey[w]);
+  const float mg = key_to_float(km);
+  int bk[kKPer];
+#pragma unroll
+  for (int k = 0; k < kKPer; ++k) {
+    bk[k] = kSHB;
+    if (k * kOneThreads + tid < n) {
+      bk[k] = sbin(mg, v[k]);
+      atomicAdd(&hs[bk[k]], 1u);
+    }
+  }
+  if (tid == 0) s_bst = -1;
+  __syncthreads();
+  {
+    const int h0 = (int)hs[2 * tid], h1 = (int)hs[2 * tid + 1];
+    int tot;
+    const int inc = iscan_one(h0 + h1, wcnt, tot);
+    const int exc = inc - h0 - h1;
+    if (exc < K && inc >= K) s_bst = exc + h0 >= K ? 2 * tid : 2 * tid + 1;
+  }
+  __syncthreads();
+  const int bst0 = s_bst;   // -1: the chunk holds fewer than K entries, all candidates
+  // the candidates, in index order, and their smallest key
+  {
+    u64 bal[kKPer];
+    uint32_t kmn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int k = 0; k < kKPer; ++k) {
+      const bool c = k * kOneThreads + tid < n && (bst0 < 0 || bk[k] <= bst0);
+      bal[k] = __ballot(c);
+      if (lane == 0) koff[k * kOneWaves + wave] = __popcll(bal[k]);
+      if (c) kmn = min(kmn, fkey(v[k]));
+    }
+    kmn = wave_umin(kmn);
+    if (lane == 0) wkey[wave] = kmn;
+    __syncthreads();
+    if (wave == 0) {
+      const int c0 = koff[2 * lane], c1 = koff[2 * lane + 1];
+      int incl = c0 + c1;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const int before = incl - c0 - c1;
+      koff[2 * lane] = before;
+      koff[2 * lane + 1] = before + c0;
+      if (lane == kWave - 1) koff[kKPer * kOneWaves] = incl;
+    }
+    __syncthreads();
+    u64 *seg = p.cand + (size_t)(row * G + g) * C;
+#pragma unroll
+    for (int k = 0; k < kKPer; ++k) {
+      if ((bal[k] >> lane) & 1ull) {
+        const int i = k * kOneThreads + tid;
+        const int at = koff[k * kOneWaves + wave] + __popcll(bal[k] & ((1ull << lane) - 1ull));
+        st_ag(seg + at, ((u64)fkey(v[k]) << 32) | (uint32_t)(j0 + i));
+      }
+    }
+    if (tid == 0) {
+      uint32_t kg = 0u;
+      if (bst0 >= 0) {
+        kg = 0xFFFFFFFFu;
+        for (int w = 0; w < kOneWaves; ++w) kg = min(kg, wkey[w]);
+      }
+      st_ag(p.info + row * G + g, ((u64)kg << 32) | (u64)(uint32_t)koff[kKPer * kOneWaves]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_last = add_ag32(p.rowcnt + row) == (uint32_t)(G - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // (2) the last workgroup of the row resolves it.  Independent loads
+  // first: the draft, its dense q, the sparse draft list, the draw's u.
+  if (tid == 0) clear_ag32(p.rowcnt + row);
+  const bool draft_row = pos < p.M - 1;
+  const int r = seq * (p.M - 1) + pos;
+  const double T = p.T;
+  int32_t *qid = reinterpret_cast<int32_t *>(dyn + kSOffQid);
+  float *qpr = reinterpret_cast<float *>(dyn + kSOffQpr);
+  if (draft_row && !p.q)
+    for (int k = tid; k < p.Kq; k += kOneThreads) {
+      qid[k] = p.qi[(int64_t)r * p.Kq + k];
+      qpr[k] = p.qp[(int64_t)r * p.Kq + k];
+    }
+  const int x = draft_row ? p.drafts[r] : -1;
+  const bool xvalid = x >= 0 && x < p.V;
+  float qx_dense = 0.0f;
+  if (tid == 0 && draft_row && p.q && xvalid) qx_dense = p.q[(int64_t)r * p.ldq + x];
+  const double ub = (double)p.u[(int64_t)seq * p.M + p.M - 1];
+  // segment offsets and kappa
+  if (wave == 0) {
+    int c[4], s = 0;
+    uint32_t kap = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sg = 4 * lane + q;
+      c[q] = 0;
+      if (sg < G) {
+        const u64 w = ld_ag(p.info + row * G + sg);
+        c[q] = (int)(uint32_t)w;
+        kap = max(kap, (uint32_t)(w >> 32));
+      }
+      s += c[q];
+    }
+    int incl = s;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    int before = incl - s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (4 * lane + q < G) segoff[4 * lane + q] = before;
+      before += c[q];
+    }
+    if (lane == kWave - 1) segoff[G] = incl;
+    kap = wave_umax(kap);
+    if (lane == 0) {
+      s_kap = kap;
+      s_ns = 0;
+      s_kmax = 0u;
+    }
+  }
+  __syncthreads();
+  const int nc = segoff[G];
+  const uint32_t kap = s_kap;
+  // candidate i of the row (index order): segment by binary search
+  auto cand_at = [&](int i) -> u64 {
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (segoff[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    return ld_ag(p.cand + (size_t)(row * G + lo) * C + (i - segoff[lo]));
+  };
+  // f(i, w) for every candidate in rounds of kOneThreads * kResPer (loads
+  // in flight), the same number of calls in every thread (i >= nc: padding)
+  auto for_cands = [&](auto &&f) {
+    for (int base = 0; base < nc; base += kOneThreads * kResPer) {
+      u64 vv[kResPer];
+#pragma unroll
+      for (int t = 0; t < kResPer; ++t) {
+        const int i = base + t * kOneThreads + tid;
+        vv[t] = i < nc ? cand_at(i) : 0ull;
+      }
+#pragma unroll
+      for (int t = 0; t < kResPer; ++t) f(base + t * kOneThreads + tid, vv[t]);
+    }
+  };
+  // S into LDS (while it fits) and the row maximum
+  u64 *Ls = reinterpret_cast<u64 *>(dyn + kSOffL);
+  {
+    uint32_t kmx = 0u;
+    for_cands([&](int i, u64 w) {
+      const uint32_t key = (uint32_t)(w >> 32);
+      const bool f = i < nc && key >= kap;
+      const int at = wave_append(f, &s_ns);
+      if (f) {
+        if (at < kSRoom) Ls[at] = w;
+        kmx = max(kmx, key);
+      }
+    });
+    kmx = wave_umax(kmx);
+    if (lane == 0) atomicMax(&s_kmax, kmx);
+  }
+  for (int i = tid; i < kSHB; i += kOneThreads) hs[i] = 0u;
+  if (tid == 0) {
+    s_bst = kSHB - 1;
+    s_A = 0;
+    s_n2 = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  const int ns = s_ns;
+  const bool inl = ns <= kSRoom;
+  const float zmax = key_to_float(s_kmax);
+  // histogram of S by d = zmax - z; the bin where the count reaches K
+  if (inl) {
+    for (int i = tid; i < ns; i += kOneThreads)
+      atomicAdd(&hs[sbin(zmax, key_to_float((uint32_t)(Ls[i] >> 32)))], 1u);
+  } else {
+    for_cands([&](int i, u64 w) {
+      const uint32_t key = (uint32_t)(w >> 32);
+      if (i < nc && key >= kap) atomicAdd(&hs[sbin(zmax, key_to_float(key))], 1u);
+    });
+  }
+  __syncthreads();
+  {
+    const int h0 = (int)hs[2 * tid], h1 = (int)hs[2 * tid + 1];
+    int tot;
+    const int inc = iscan_one(h0 + h1, wcnt, tot);
+    const int exc = inc - h0 - h1;
+    if (exc < K && inc >= K) {
+      const bool first = exc + h0 >= K;
+      s_bst = first ? 2 * tid : 2 * tid + 1;
+      s_A = first ? exc : exc + h0;
+      s_n2 = first ? h0 : h1;
+    }
+    if (tid == 0) s_m = 0;
+  }
+  __syncthreads();
+  const int bst = s_bst;
+  u64 *Sa = reinterpret_cast<u64 *>(dyn + kSOffSort);
+  // an entry to sort, keyed (key << 32 | ~index): descending order is key
+  // descending, index ascending
+  auto put = [&](bool f, u64 w) {
+    const int at = wave_append(f, &s_m);
+    if (f && at < kSSortMax)
+      Sa[at] = (w & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (w & 0xFFFFFFFFull));
+  };
+  if ((int64_t)s_A + s_n2 <= kSSortMax) {
+    // S up to the bin of the cut
+    if (inl) {
+      for (int base = 0; base < ns; base += kOneThreads) {
+        const int i = base + tid;
+        const u64 w = i < ns ? Ls[i] : 0ull;
+        put(i < ns && sbin(zmax, key_to_float((uint32_t)(w >> 32))) <= bst, w);
+      }
+    } else {
+      for_cands([&](int i, u64 w) {
+        const uint32_t key = (uint32_t)(w >> 32);
+        put(i < nc && key >= kap && sbin(zmax, key_to_float(key)) <= bst, w);
+      });
+    }
+  } else {
+    // radix select of the K-th key of S, 8 bits a pass; then the entries
+    // above it and the first ties at it in index order
+    uint32_t prefix = 0u;
+    int above = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < kBins; i += kOneThreads) hs[i] = 0u;
+      if (tid == 0) {
+        s_dig = 0;
+        s_abv = above;
+      }
+      __syncthreads();
+      for_cands([&](int i, u64 w) {
+        const uint32_t key = (uint32_t)(w >> 32);
+        if (i < nc && key >= kap && (pass == 0 || (key >> (shift + 8)) == prefix))
+          atomicAdd(&hs[(key >> shift) & 0xFFu], 1u);
+      });
+      __syncthreads();
+      if (wave == 0) {
+        int c[4], s = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = (int)hs[255 - 4 * lane - q];
+          s += c[q];
+        }
+        int incl = s;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        int acc = above + incl - s;
+        if (acc < K && acc + s >= K) {
+          for (int q = 0; q < 4; ++q) {
+            if (acc + c[q] >= K) {
+              s_dig = 255 - 4 * lane - q;
+              s_abv = acc;
+              break;
+            }
+            acc += c[q];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << 8) | (uint32_t)s_dig;
+      above = s_abv;
+      __syncthreads();
+    }
+    const uint32_t kst = prefix;
+    const int t = K - above;
+    int seen = 0;
+    for_cands([&](int i, u64 w) {
+      const uint32_t key = (uint32_t)(w >> 32);
+      const bool tie = i < nc && key == kst;
+      int pre;
+      const int nt = count_one(tie, pre, wcnt);
+      put((i < nc && key > kst) || (tie && seen + pre < t), w);
+      seen += nt;
+    });
+  }
+  __syncthreads();
+  const u64 *top = sort_desc(Sa, Ls, min(s_m, kSSortMax));
+
+  // (3) the row's target over its top K (thread j holds rank j): e, the
+  // top-p and min-p cuts, p'; as samp_row
+  const int j = tid;
+  double *eR = reinterpret_cast<double *>(dyn + kSOffE);
+  double *pR = reinterpret_cast<double *>(dyn + kSOffP);
+  double *qR = reinterpret_cast<double *>(dyn + kSOffQ);
+  int32_t *idR = reinterpret_cast<int32_t *>(dyn + kSOffId);
+  int idj = -1;
+  double e = 0.0;
+  Fx fe = fx_zero();
+  {
+    const float z0 = key_to_float((uint32_t)(top[0] >> 32));
+    if (j < K) {
+      const u64 w = top[j];
+      idj = (int)(0xFFFFFFFFu - (uint32_t)w);
+      e = T == 0.0 ? (j == 0 ? 1.0 : 0.0)
+                   : exp(((double)key_to_float((uint32_t)(w >> 32)) - (double)z0) / T);
+      fe = to_fx(e);
+    }
+  }
+  if (tid == 0) {
+    s_cp = K;
+    s_cm = K;
+    s_px = 0.0;
+    s_qk = kNone;
+    s_fr = kNone;
+    s_fp = kNone;
+    s_pick = kNone;
+    s_lastw = -1;
+  }
+  Fx Ssum;
+  const Fx before = fx_excl_one(fe, red, Ssum);
+  const Fx cum = fx_sum(before, fe);
+  if (T == 0.0) {
+    if (j == 0) s_cp = 1;
+  } else if (p.top_p < 1.0) {
+    Fx thr = to_fx(p.top_p > 0.0 ? p.top_p * fx_to_double(Ssum) : 0.0);
+    if (!fx_nonzero(thr)) thr.lo = 1ull;
+    if (j < K && fx_ge(cum, thr) && !fx_ge(before, thr)) s_cp = j + 1;
+  }
+  if (p.min_p > 0.0) {
+    const u64 b = __ballot(j >= 1 && j < K && e < p.min_p);
+    if (lane == 0 && b) atomicMin(&s_cm, wave * kWave + __ffsll((long long)b) - 1);
+  }
+  __syncthreads();
+  const int kept = min(s_cp, s_cm);
+  if (j == kept - 1) s_mass = cum;
+  __syncthreads();
+  const bool in = j < kept;
+  const double pj = in ? e / fx_to_double(s_mass) : 0.0;
+  if (p.out_ids && j < K) {   // the support: kept entries whose p' is positive in fp64
+    const bool sup = in && pj > 0.0;
+    p.out_ids[(size_t)row * K + j] = sup ? idj : -1;
+    p.out_probs[(size_t)row * K + j] = sup ? (float)pj : 0.0f;
+  }
+  if (draft_row) {
+    if (in && idj == x) s_px = pj;
+    if (!p.q)
+      for (int k = tid; k < p.Kq; k += kOneThreads)
+        if (qid[k] == x) atomicMin(&s_qk, k);
+  }
+  // (4) the draw this row would make, in index order over its support: the
+  // residual max(0, p' - q) for a draft row (p' if that is all zero), else
+  // p'; as samp_draw
+  const bool residual = draft_row;
+  if (in) {
+    double qj = 0.0;
+    if (residual) {
+      if (p.q) {
+        if (idj >= 0 && idj < p.V) qj = (double)p.q[(int64_t)r * p.ldq + idj];
+      } else {
+        for (int k = 0; k < p.Kq; ++k)
+          if (qid[k] == idj) {
+            qj = (double)qpr[k];
+            break;
+          }
+      }
+    }
+    eR[j] = e;
+    pR[j] = pj;
+    qR[j] = qj;
+    idR[j] = idj;
+    Sa[j] = ((u64)(0xFFFFFFFFu - (uint32_t)idj) << 32) | (uint32_t)j;
+  }
+  const u64 *byid = sort_desc(Sa, Ls, kept);
+  const int s = tid;
+  int ids = -1;
+  double dres = 0.0, dp = 0.0;
+  Fx wr = fx_zero(), we = fx_zero();
+  if (s < kept) {
+    const int jj = (int)(uint32_t)byid[s];
+    ids = idR[jj];
+    dp = pR[jj];
+    we = to_fx(eR[jj]);
+    if (residual) {
+      const double d = dp - qR[jj];
+      dres = d > 0.0 ? d : 0.0;
+      wr = to_fx(dres);
+    }
+  }
+  {
+    const u64 b0 = __ballot(dres > 0.0), b1 = __ballot(dp > 0.0);
+    if (lane == 0) {
+      if (b0) atomicMin(&s_fr, wave * kWave + __ffsll((long long)b0) - 1);
+      if (b1) atomicMin(&s_fp, wave * kWave + __ffsll((long long)b1) - 1);
+    }
+  }
+  __syncthreads();
+  // the residual is used when any of its fp64 weights is positive, even if
+  // all of them are below the fixed-point resolution
+  const bool use_res = residual && s_fr != kNone;
+  const Fx w = use_res ? wr : we;
+  Fx W;
+  const Fx bef = fx_excl_one(w, red, W);
+  const Fx target = to_fx(ub * fx_to_double(W));
+  if (!fx_nonzero(target)) {
+    // below 2^-100: u = 0 takes the first positive weight; another target
+    // follows the fp64 definition in index order, summed by one thread
+    if (tid == 0) {
+      int slot = use_res ? s_fr : s_fp;
+      if (ub != 0.0) {
+        auto wgt = [&](int k) {
+          const int jj = (int)(uint32_t)byid[k];
+          if (!use_res) return pR[jj];
+          const double d = pR[jj] - qR[jj];
+          return d > 0.0 ? d : 0.0;
+        };
+        double Wd = 0.0;
+        int last = -1;
+        for (int k = 0; k < kept; ++k) {
+          const double wk = wgt(k);
+          Wd += wk;
+          if (wk > 0.0) last = k;
+        }
+        const double tt = ub * Wd;
+        double cm = 0.0;
+        slot = last;
+        for (int k = 0; k < kept; ++k) {
+          cm += wgt(k);
+          if (cm > tt) {
+            slot = k;
+            break;
+          }
+        }
+      }
+      s_pick = (slot >= 0 && slot < kept) ? idR[(int)(uint32_t)byid[slot]] : p.V - 1;
+    }
+  } else {
+    if (s < kept && fx_gt(fx_sum(bef, w), target) && !fx_gt(bef, target)) s_pick = ids;
+    const u64 b = __ballot(s < kept && fx_nonzero(w));
+    if (lane == 0 && b) atomicMax(&s_lastw, wave * kWave + 63 - __clzll((long long)b));
+  }
+  __syncthreads();
+  // (5) the row's verdict and token; the last row of the sequence to finish
+  // writes the sequence's outputs
+  if (tid == 0) {
+    int pick = s_pick;
+    if (pick == kNone)   // rounding passed the end: the last positive weight
+      pick = s_lastw >= 0 ? idR[(int)(uint32_t)byid[s_lastw]] : p.V - 1;
+    bool reject = false;
+    if (draft_row) {
+      double qx = 0.0;
+      if (xvalid) qx = p.q ? (double)qx_dense : (s_qk != kNone ? (double)qpr[s_qk] : 0.0);
+      const double px = xvalid ? s_px : 0.0;
+      reject = !((double)p.u[(int64_t)seq * p.M + pos] * qx < px);
+    }
+    st_ag(p.res + row, ((u64)(reject ? 1u : 0u) << 31) | (u64)(uint32_t)pick);
+    __builtin_amdgcn_s_waitcnt(0);
+    s_last = add_ag32(p.seqcnt + seq) == (uint32_t)(p.M - 1);
+  }
+  __syncthreads();
+  if (!s_last || wave != 0) return;
+  {
+    const int i = lane;
+    const u64 rw = i < p.M ? ld_ag(p.res + (size_t)seq * p.M + i) : 0ull;
+    const u64 rej = __ballot(i < p.M - 1 && ((rw >> 31) & 1ull));
+    const int a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
+    const int tok = __shfl((int)(rw & 0x7FFFFFFFull), a);
+    if (i < p.M)
+      p.tokens[(int64_t)seq * p.M + i] =
+          i < a ? p.drafts[(int64_t)seq * (p.M - 1) + i] : (i == a ? tok : -1);
+    if (i == 0) {
+      p.counts[2 * seq] = a;
+      p.counts[2 * seq + 1] = a + 1;
+      p.rollback[seq] = (p.base_len ? p.base_len[seq] : 0) + a + 1;
+      clear_ag32(p.seqcnt + seq);
+    }
+  }
+}
+
 }  // namespace
 
 size_t accept_ws_bytes(int M, int V) { return layout(M, V).bytes; }
@@ -2946,30 +3642,61 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
 namespace {
 
 struct SampLayout {
-  size_t zp, hcnt, sel, bcnt, lid, lz, sid, sp, se, nkept, acc, bytes;
+  int G, C;   // samp_one's workgroups per row and chunk (G == 0: the chained kernels)
+  size_t zp, hcnt, sel, bcnt, lid, lz, sid, sp, se, nkept, acc, info, cand, res, bytes;
 };
+
+// Workgroups per row of samp_one, or 0 for the chained kernels: the rows
+// spread over the compute units as for rej_one (chunks of at most
+// kOneChunk entries), while the rows' expected candidates (about K + 16 a
+// workgroup) stay within kSCandBudget and the counters fit the head.
+int samp_one_blocks(int B, int M, int V, int K) {
+  const int64_t rows = (int64_t)B * M;
+  if (rows > kSMaxRows || B > kSMaxSeqs || M > kWave) return 0;
+  int G = std::max((V + kOneChunk - 1) / kOneChunk,
+                   std::min(std::max(1, kMaxOneBlocks / (int)rows), (V + 1023) / 1024));
+  const int C = (V + G - 1) / G;
+  G = (V + C - 1) / C;   // no empty chunk
+  if (G > kSMaxG || (int64_t)G * (K + 16) > kSCandBudget) return 0;
+  return G;
+}
+
+// Head (offset 0, the same for every shape): samp_one's row and sequence
+// counters, zero before first use and after every call.  The per-call
+// regions of samp_one and of the chained kernels follow it (one or the
+// other).
+constexpr size_t kSHeadBytes = sizeof(uint32_t) * (kSMaxRows + kSMaxSeqs);
+static_assert(kSHeadBytes % 256 == 0, "regions stay 256-byte aligned");
 
 SampLayout samp_layout(int B, int M, int V, int top_k, bool penalties) {
   const size_t rows = (size_t)B * M, K = (size_t)std::min(top_k, V);
   const size_t nb = (size_t)blocks_per_row(V);
-  SampLayout L;
-  size_t o = 0;
+  SampLayout L{};
+  L.G = samp_one_blocks(B, M, V, (int)K);
+  L.C = L.G ? (V + L.G - 1) / L.G : 0;
+  size_t o = kSHeadBytes;
   auto take = [&](size_t n) {
     size_t at = o;
     o += (n + 255) & ~(size_t)255;
     return at;
   };
-  L.zp = take(penalties ? sizeof(float) * rows * V : 0);
-  L.hcnt = take(sizeof(uint32_t) * 4 * rows * kBins);
-  L.sel = take(sizeof(SelState) * 4 * rows);
-  L.bcnt = take(sizeof(uint32_t) * 2 * rows * nb);
-  L.lid = take(sizeof(int32_t) * rows * K);
-  L.lz = take(sizeof(float) * rows * K);
-  L.sid = take(sizeof(int32_t) * rows * K);
-  L.sp = take(sizeof(double) * rows * K);
-  L.se = take(sizeof(double) * rows * K);
-  L.nkept = take(sizeof(int32_t) * rows);
-  L.acc = take(sizeof(AccIn) * rows);
+  if (L.G) {
+    L.info = take(sizeof(u64) * rows * L.G);
+    L.cand = take(sizeof(u64) * rows * L.G * L.C);
+    L.res = take(sizeof(u64) * rows);
+  } else {
+    L.zp = take(penalties ? sizeof(float) * rows * V : 0);
+    L.hcnt = take(sizeof(uint32_t) * 4 * rows * kBins);
+    L.sel = take(sizeof(SelState) * 4 * rows);
+    L.bcnt = take(sizeof(uint32_t) * 2 * rows * nb);
+    L.lid = take(sizeof(int32_t) * rows * K);
+    L.lz = take(sizeof(float) * rows * K);
+    L.sid = take(sizeof(int32_t) * rows * K);
+    L.sp = take(sizeof(double) * rows * K);
+    L.se = take(sizeof(double) * rows * K);
+    L.nkept = take(sizeof(int32_t) * rows);
+    L.acc = take(sizeof(AccIn) * rows);
+  }
   L.bytes = o;
   return L;
 }
@@ -3000,6 +3727,25 @@ hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t str
   p.nb = blocks_per_row(c.V); p.chunk = (c.V + p.nb - 1) / p.nb;
   p.tokens = c.tokens; p.counts = c.counts; p.rollback = c.rollback;
   p.out_ids = c.out_ids; p.out_probs = c.out_probs;
+  const int rows = c.B * c.M;
+  if (L.G) {
+    p.G = L.G;
+    p.C = L.C;
+    p.pen = pen ? 1 : 0;
+    p.zp = nullptr;
+    p.rowcnt = reinterpret_cast<uint32_t *>(w);
+    p.seqcnt = p.rowcnt + kSMaxRows;
+    p.info = reinterpret_cast<u64 *>(w + L.info);
+    p.cand = reinterpret_cast<u64 *>(w + L.cand);
+    p.res = reinterpret_cast<u64 *>(w + L.res);
+    static std::once_flag samp_once;
+    std::call_once(samp_once, [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(samp_one),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kSDyn);
+    });
+    hipLaunchKernelGGL(samp_one, dim3(rows * L.G), dim3(kOneThreads), kSDyn, stream, p);
+    return hipGetLastError();
+  }
   p.hcnt = reinterpret_cast<uint32_t *>(w + L.hcnt);
   p.sel = reinterpret_cast<SelState *>(w + L.sel);
   p.bcnt = reinterpret_cast<uint32_t *>(w + L.bcnt);
@@ -3010,7 +3756,6 @@ hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t str
   p.se = reinterpret_cast<double *>(w + L.se);
   p.nkept = reinterpret_cast<int32_t *>(w + L.nkept);
   p.acc = reinterpret_cast<AccIn *>(w + L.acc);
-  const int rows = c.B * c.M;
   const dim3 grid(p.nb, rows);
   hipLaunchKernelGGL(samp_prep, grid, dim3(kBlock), 0, stream, p);
   for (int pass = 0; pass < 4; ++pass)

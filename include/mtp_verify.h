@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 6
+#define MTP_ABI_VERSION 7
 
 enum {
   MTP_OK = 0,
@@ -333,7 +333,11 @@ typedef struct {
  *                    K = min(top_k, V): each row's p' in order of
  *                    probability, -1 / 0 past its support
  *   ws, ws_bytes     at least mtp_accept_sampled_workspace_bytes(B, M, V,
- *                    top_k, penalties on); calls sharing it must not overlap
+ *                    top_k, penalties on), zero-filled before its first use.
+ *                    Its first 20 KiB hold row and sequence counters that
+ *                    every call leaves zero for the next (of any shape);
+ *                    nothing else is kept between calls.  Calls sharing it
+ *                    must not overlap in time.
  * Errors: MTP_ERR_VALUE for temperature < 0 or NaN, a NaN parameter, top_k
  * outside [1, MTP_MAX_TOP_K], repeat_penalty <= 0 or a window above
  * MTP_MAX_PENALTY_WINDOW; 1 <= B <= 1024, 1 <= M <= 64.

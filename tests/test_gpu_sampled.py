@@ -90,6 +90,11 @@ CASES = [
                         penalty_last_n=64)),
     (2, 6, 777, dict(temperature=0.7, top_k=1, repeat_penalty=1.5, penalty_last_n=8)),
     (1, 5, 500, dict(temperature=2.0, top_p=0.0, top_k=50)),
+    # 64 rows over 2048 workgroups of the one-launch kernel
+    (8, 8, 262144, dict(temperature=0.6, top_p=0.95, min_p=0.01, top_k=64)),
+    # top_k 600 over 262144 entries: the chained kernels
+    (1, 4, 262144, dict(temperature=0.8, top_p=0.9, top_k=600, repeat_penalty=1.2,
+                        penalty_last_n=32)),
 ]
 
 
@@ -178,3 +183,32 @@ def test_sampled_on_lm_head_logits():
                          repeat_penalty=1.1, penalty_last_n=64)
     check(z, d, c["u"][None], par, "LM head", q=c["q"][None], history=[[1, 2, 3]],
           base_len=[100])
+
+
+def test_sampled_calls_share_one_workspace():
+    # one workspace through one-launch and chained calls of several shapes:
+    # each call must leave the head's counters ready for the next
+    rng = np.random.default_rng(41)
+    shapes = [(1, 8, 262144, 64), (2, 4, 262144, 600), (3, 5, 4099, 40), (1, 8, 262144, 64),
+              (2, 3, 777, 1)]
+    need = max(bv.accept_sampled_workspace_bytes(B, M, V, k, True) for B, M, V, k in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for rep, (B, M, V, k) in enumerate(shapes):
+        par = oracle.sampler(temperature=0.7, top_p=0.9, top_k=k, repeat_penalty=1.1,
+                             penalty_last_n=16)
+        z = (rng.standard_normal((B, M, V)) * 2.0).astype(np.float32)
+        d = drafts_for(rng, z, par, rep % 2 == 0)
+        u = rng.random((B, M)).astype(np.float32)
+        q = rng.dirichlet(np.full(V, 0.3), size=(B, M - 1)).astype(np.float32)
+        hist = [list(rng.integers(0, V, 20)) for _ in range(B)]
+        log("shared workspace", rep, B, M, V, k)
+        ldh = max(len(h) for h in hist)
+        harr = np.array([h + [0] * (ldh - len(h)) for h in hist], np.int32)
+        g = bv.accept_sampled(dev(z), dev(d), dev(u), bv.Sampler(**par), draft_probs=dev(q),
+                              history=dev(harr), history_len=dev(np.array([len(h) for h in hist],
+                                                                           np.int32)), ws=ws)
+        g = [host(t) for t in g]
+        o = oracle.accept_sampled(z, d, u, par, q=q, history=hist)
+        assert np.array_equal(g[0], o[0]) and np.array_equal(g[1], o[1]), (rep, g, o[:2])
+    # the head is back to zero
+    assert int(ws[:20480].count_nonzero()) == 0
