@@ -2245,7 +2245,7 @@ struct SampArgs {
   u64 *info;                 // [rows][G] (smallest candidate key << 32) | candidate count
   u64 *cand;                 // [rows][G][C] candidates (key << 32 | index), index order
   u64 *res;                  // [rows] (draft rejected << 31) | token this row would draw
-  int G, C, pen;
+  int G, C, pen, lkc;        // lkc: log2 of the candidate slots read in the first round
 };
 
 __device__ __forceinline__ const float *samp_src(const SampArgs &p, int row) {
@@ -2837,10 +2837,13 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
 //     samp_draw do;
 //   - the row's verdict and token go to the workspace; the last row of the
 //     sequence to finish derives the accepted run and writes the outputs.
-// Data crossing workgroups follows the rules of rej_one (agent-scope
-// atomic stores and loads, each writer's stores complete before it
-// arrives).  The counters live in the workspace head; each call leaves
-// them zero.
+// The resolver's steps are short chains on one workgroup, so each runs on
+// as few waves as its data needs (the others wait at the next barrier),
+// and wave-wide sums and extrema move data between lanes with DPP rather
+// than through LDS.  Data crossing workgroups follows the rules of rej_one
+// (agent-scope atomic stores and loads, each writer's stores complete
+// before it arrives).  The counters live in the workspace head; each call
+// leaves them zero.
 
 constexpr int kSHB = 2048;              // bins of d: exponent and 5 mantissa bits
 constexpr int kSBinBase = 3072;         // bin 0 takes every d below 2^-31
@@ -2850,6 +2853,7 @@ constexpr int kSMaxG = 256;
 constexpr int kSMaxRows = 4096;
 constexpr int kSMaxSeqs = 1024;
 constexpr int kSCandBudget = 16384;     // expected candidates per row the launch rule allows
+constexpr int kSSlotPer = 8;            // first-round candidate slots per resolver thread
 constexpr int kSOffL = 0;                           // u64 [kSRoom]: S (first the penalty window)
 constexpr int kSOffSort = kSOffL + 8 * kSRoom;      // u64 [kSSortMax]: entries to sort
 constexpr int kSOffE = kSOffSort + 8 * kSSortMax;   // fp64 [kMaxTopK]: e by rank
@@ -2860,7 +2864,7 @@ constexpr int kSOffQid = kSOffId + 4 * kMaxTopK;    // the sparse draft list
 constexpr int kSOffQpr = kSOffQid + 4 * kMaxTopK;
 constexpr int kSDyn = kSOffQpr + 4 * kMaxTopK;
 static_assert(4 * kMaxPenaltyWindow <= 8 * kSRoom, "the penalty window fits where S goes");
-static_assert(kSHB == 2 * kOneThreads, "two bins per thread");
+static_assert(kSHB == 32 * kWave, "32 bins per lane of one wave");
 static_assert(kSSortMax == 2 * kOneThreads, "one compare-exchange per thread and step");
 static_assert(kMaxTopK <= kOneThreads && kMaxTopK <= kSSortMax, "one kept entry per thread");
 static_assert(kSMaxG <= 4 * kWave, "four segments per lane");
@@ -2874,33 +2878,125 @@ __device__ __forceinline__ int sbin(float zmax, float z) {
   return b < 0 ? 0 : (b < kSHB ? b : kSHB - 1);
 }
 
-__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
-  for (int s = kWave / 2; s > 0; s >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, s));
-  return v;
+// DPP moves: lane i reads a lane of its own row of 16 within the same
+// instruction.  dpp0: a shift or broadcast (row_shr:n reads lane i - n,
+// row_bcast:15 and :31 the last lane of the row before, resp. of row 1;
+// lanes without a source, and rows outside row_mask, read 0).  dppp: a
+// permutation within each row.
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118,
+              kDppBcast15 = 0x142, kDppBcast31 = 0x143, kDppSwap1 = 0xB1, kDppSwap2 = 0x4E,
+              kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, row_mask, 0xF, false);
 }
-__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
-  for (int s = kWave / 2; s > 0; s >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, s));
-  return v;
+template <int ctrl>
+__device__ __forceinline__ uint32_t dppp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, 0xF, 0xF, false);
 }
 
-// Inclusive prefix of v over the threads (thread order), and the total.
-__device__ int iscan_one(int v, int *wsum, int &total) {
+// Inclusive sum over the lanes of the wave.
+__device__ __forceinline__ int dpp_incl(int x) {
+  x += (int)dpp0<kDppShr1>((uint32_t)x);
+  x += (int)dpp0<kDppShr2>((uint32_t)x);
+  x += (int)dpp0<kDppShr4>((uint32_t)x);
+  x += (int)dpp0<kDppShr8>((uint32_t)x);
+  x += (int)dpp0<kDppBcast15, 0xA>((uint32_t)x);
+  x += (int)dpp0<kDppBcast31, 0xC>((uint32_t)x);
+  return x;
+}
+
+// Wave-wide extrema (the same value in every lane).
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t x) {
+  x = max(x, dppp<kDppSwap1>(x));
+  x = max(x, dppp<kDppSwap2>(x));
+  x = max(x, dppp<kDppHalfMirror>(x));
+  x = max(x, dppp<kDppMirror>(x));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(r0, r1), max(r2, r3));   // unsigned: keys use all 32 bits
+}
+__device__ __forceinline__ uint32_t dpp_umin(uint32_t x) {
+  x = min(x, dppp<kDppSwap1>(x));
+  x = min(x, dppp<kDppSwap2>(x));
+  x = min(x, dppp<kDppHalfMirror>(x));
+  x = min(x, dppp<kDppMirror>(x));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ Fx dpp0_fx(const Fx &a) {
+  Fx r;
+  r.lo = (u64)dpp0<ctrl, row_mask>((uint32_t)a.lo) |
+         ((u64)dpp0<ctrl, row_mask>((uint32_t)(a.lo >> 32)) << 32);
+  r.hi = (u64)dpp0<ctrl, row_mask>((uint32_t)a.hi) |
+         ((u64)dpp0<ctrl, row_mask>((uint32_t)(a.hi >> 32)) << 32);
+  return r;
+}
+
+// Inclusive exact sum over the lanes of the wave.
+__device__ __forceinline__ Fx dpp_fx_incl(Fx x) {
+  fx_add(x, dpp0_fx<kDppShr1>(x));
+  fx_add(x, dpp0_fx<kDppShr2>(x));
+  fx_add(x, dpp0_fx<kDppShr4>(x));
+  fx_add(x, dpp0_fx<kDppShr8>(x));
+  fx_add(x, dpp0_fx<kDppBcast15, 0xA>(x));
+  fx_add(x, dpp0_fx<kDppBcast31, 0xC>(x));
+  return x;
+}
+
+// Exclusive exact prefix of v over the threads of the first W waves (thread
+// order; the other threads must pass zero) and their total.  The whole
+// workgroup calls it.
+__device__ Fx fx_excl_w(Fx v, Fx *red, Fx &total, int W) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  int incl = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  Fx incl = v;
+  if (wave < W) incl = dpp_fx_incl(v);
   __syncthreads();
-  if (lane == kWave - 1) wsum[wave] = incl;
+  if (wave < W && lane == kWave - 1) red[wave] = incl;
   __syncthreads();
-  int before = 0;
-  total = 0;
-  for (int w = 0; w < kOneWaves; ++w) {
-    if (w < wave) before += wsum[w];
-    total += wsum[w];
+  Fx before = fx_zero();
+  total = fx_zero();
+  for (int w = 0; w < W; ++w) {
+    if (w < wave) fx_add(before, red[w]);
+    fx_add(total, red[w]);
   }
-  return before + incl;
+  return fx_sum(before, fx_sub(incl, v));
+}
+
+// One wave: the first bin of h[0 .. kSHB) where the count from bin 0 reaches
+// K, the count before it and its own (the same in every lane); bin -1 when
+// the total stays below K.
+__device__ void first_bin_reaching(const uint32_t *h, int K, int &bin, int &before, int &cnt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint4 *h4 = reinterpret_cast<const uint4 *>(h + 32 * lane);
+  int s = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 c = h4[q];
+    s += (int)(c.x + c.y + c.z + c.w);
+  }
+  const int incl = dpp_incl(s);
+  const u64 b = __ballot(incl - s < K && incl >= K);
+  bin = -1;
+  before = 0;
+  cnt = 0;
+  if (!b) return;
+  const int L = __ffsll((long long)b) - 1;
+  const int base = __builtin_amdgcn_readlane(incl - s, L);
+  const int hv = lane < 32 ? (int)h[32 * L + lane] : 0;
+  const int inc2 = base + dpp_incl(hv);
+  const u64 b2 = __ballot(lane < 32 && inc2 >= K && inc2 - hv < K);
+  const int l2 = __ffsll((long long)b2) - 1;
+  bin = 32 * L + l2;
+  before = __builtin_amdgcn_readlane(inc2 - hv, l2);
+  cnt = __builtin_amdgcn_readlane(hv, l2);
 }
 
 // Place in an LDS list for the lanes with `flag` (one atomic per wave on the
@@ -2910,14 +3006,15 @@ __device__ __forceinline__ int wave_append(bool flag, int *count) {
   const u64 b = __ballot(flag);
   int base = 0;
   if (lane == 0 && b) base = atomicAdd(count, __popcll(b));
-  base = __shfl(base, 0);
+  base = __builtin_amdgcn_readfirstlane(base);   // every lane is active here
   return base + __popcll(b & ((1ull << lane) - 1ull));
 }
 
 // Sorts the n (<= kSSortMax) distinct non-zero values of a (LDS, room for
 // kSSortMax) in descending order and returns where they are: in b (room for
-// n) for n <= 256, ranked by counting with 1024 / n2 lanes per value, else
-// in a by a bitonic network.  The whole workgroup calls it.
+// n) for n <= 256, ranked by counting (1024 / n2 lanes a value, four loads
+// in flight a lane), else in a by a bitonic network.  The whole workgroup
+// calls it.
 __device__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
   const int tid = threadIdx.x;
   int n2 = 16;
@@ -2926,9 +3023,19 @@ __device__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
   if (n2 <= 256) {
     const int P = kOneThreads / n2, e = tid / P, part = tid - e * P;
     const u64 mine = e < n ? a[e] : 0ull;
-    int rank = 0;
-    if (e < n)
-      for (int k = part; k < n; k += P) rank += a[k] > mine ? 1 : 0;
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    if (e < n) {
+      int k = part;
+      for (; k + 3 * P < n; k += 4 * P) {
+        const u64 x0 = a[k], x1 = a[k + P], x2 = a[k + 2 * P], x3 = a[k + 3 * P];
+        r0 += x0 > mine ? 1 : 0;
+        r1 += x1 > mine ? 1 : 0;
+        r2 += x2 > mine ? 1 : 0;
+        r3 += x3 > mine ? 1 : 0;
+      }
+      for (; k < n; k += P) r0 += a[k] > mine ? 1 : 0;
+    }
+    int rank = (r0 + r1) + (r2 + r3);
     for (int s = P / 2; s > 0; s >>= 1) rank += __shfl_xor(rank, s);
     if (e < n && part == 0) b[rank] = mine;
     __syncthreads();
@@ -2962,14 +3069,14 @@ __device__ __forceinline__ void clear_ag32(uint32_t *c) {
 // grid (rows * G), kOneThreads threads, kSDyn bytes of dynamic LDS.
 __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  __shared__ uint32_t hs[kSHB];
+  __shared__ __attribute__((aligned(16))) uint32_t hs[kSHB];
   __shared__ int koff[kKPer * kOneWaves + 1];
   __shared__ int wcnt[kOneWaves];
   __shared__ uint32_t wkey[kOneWaves];
   __shared__ Fx red[kOneWaves];
-  __shared__ int segoff[kSMaxG + 1];
+  __shared__ int segoff[kSMaxG + 1], segcnt[kSMaxG], remoff[kSMaxG + 1];
   __shared__ Fx s_mass;
-  __shared__ double s_px;
+  __shared__ double s_px, s_qx;
   __shared__ uint32_t s_kmax, s_kap;
   __shared__ int s_nl, s_bst, s_A, s_n2, s_last, s_ns, s_m, s_dig, s_abv;
   __shared__ int s_cp, s_cm, s_qk, s_fr, s_fp, s_pick, s_lastw;
@@ -3010,12 +3117,13 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       if (c && i < n) v[k] = penalise(v[k], c, p);
     }
   }
-  // the chunk maximum by key (+0 above -0), then the count histogram
+  // the chunk maximum by key (+0 above -0), then the count histogram and
+  // (wave 0) the first bin where the count from the top reaches K
   uint32_t km = 0u;
 #pragma unroll
   for (int k = 0; k < kKPer; ++k)
     if (k * kOneThreads + tid < n) km = max(km, fkey(v[k]));
-  km = wave_umax(km);
+  km = dpp_umax(km);
   if (lane == 0) wkey[wave] = km;
   __syncthreads();
   km = 0u;
@@ -3030,14 +3138,11 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       atomicAdd(&hs[bk[k]], 1u);
     }
   }
-  if (tid == 0) s_bst = -1;
   __syncthreads();
-  {
-    const int h0 = (int)hs[2 * tid], h1 = (int)hs[2 * tid + 1];
-    int tot;
-    const int inc = iscan_one(h0 + h1, wcnt, tot);
-    const int exc = inc - h0 - h1;
-    if (exc < K && inc >= K) s_bst = exc + h0 >= K ? 2 * tid : 2 * tid + 1;
+  if (wave == 0) {
+    int bin, before, cnt;
+    first_bin_reaching(hs, K, bin, before, cnt);
+    if (lane == 0) s_bst = bin;
   }
   __syncthreads();
   const int bst0 = s_bst;   // -1: the chunk holds fewer than K entries, all candidates
@@ -3052,16 +3157,12 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       if (lane == 0) koff[k * kOneWaves + wave] = __popcll(bal[k]);
       if (c) kmn = min(kmn, fkey(v[k]));
     }
-    kmn = wave_umin(kmn);
+    kmn = dpp_umin(kmn);
     if (lane == 0) wkey[wave] = kmn;
     __syncthreads();
     if (wave == 0) {
       const int c0 = koff[2 * lane], c1 = koff[2 * lane + 1];
-      int incl = c0 + c1;
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
+      const int incl = dpp_incl(c0 + c1);
       const int before = incl - c0 - c1;
       koff[2 * lane] = before;
       koff[2 * lane + 1] = before + c0;
@@ -3092,12 +3193,23 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   __syncthreads();
   if (!s_last) return;
 
-  // (2) the last workgroup of the row resolves it.  Independent loads
-  // first: the draft, its dense q, the sparse draft list, the draw's u.
+  // (2) the last workgroup of the row resolves it.  One round of loads:
+  // the first Kc slots of every segment (valid or not: Kc is a power of two
+  // <= C, so they stay inside the segment), the segments' words (wave 0),
+  // the draft and its dense q (last wave), the sparse draft list.
   if (tid == 0) clear_ag32(p.rowcnt + row);
   const bool draft_row = pos < p.M - 1;
   const int r = seq * (p.M - 1) + pos;
   const double T = p.T;
+  const int W = (K + kWave - 1) / kWave;   // waves of the per-rank steps
+  const int lk = p.lkc, Kc = 1 << lk, nslot = G << lk;
+  u64 vs[kSSlotPer];
+#pragma unroll
+  for (int t = 0; t < kSSlotPer; ++t) {
+    const int sl = t * kOneThreads + tid;
+    vs[t] = sl < nslot ? ld_ag(p.cand + (size_t)(row * G + (sl >> lk)) * C + (sl & (Kc - 1)))
+                       : 0ull;
+  }
   int32_t *qid = reinterpret_cast<int32_t *>(dyn + kSOffQid);
   float *qpr = reinterpret_cast<float *>(dyn + kSOffQpr);
   if (draft_row && !p.q)
@@ -3105,14 +3217,16 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       qid[k] = p.qi[(int64_t)r * p.Kq + k];
       qpr[k] = p.qp[(int64_t)r * p.Kq + k];
     }
+  if (tid == kOneThreads - kWave) {
+    const int x = draft_row ? p.drafts[r] : -1;
+    s_qx = (draft_row && p.q && x >= 0 && x < p.V) ? (double)p.q[(int64_t)r * p.ldq + x] : 0.0;
+  }
   const int x = draft_row ? p.drafts[r] : -1;
   const bool xvalid = x >= 0 && x < p.V;
-  float qx_dense = 0.0f;
-  if (tid == 0 && draft_row && p.q && xvalid) qx_dense = p.q[(int64_t)r * p.ldq + x];
   const double ub = (double)p.u[(int64_t)seq * p.M + p.M - 1];
-  // segment offsets and kappa
   if (wave == 0) {
-    int c[4], s = 0;
+    // counts, offsets, kappa; counts past Kc are left for a second round
+    int c[4], ex[4], s = 0, e = 0;
     uint32_t kap = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -3123,21 +3237,28 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
         c[q] = (int)(uint32_t)w;
         kap = max(kap, (uint32_t)(w >> 32));
       }
+      ex[q] = max(0, c[q] - Kc);
       s += c[q];
+      e += ex[q];
     }
-    int incl = s;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    int before = incl - s;
+    const int incl = dpp_incl(s), einc = dpp_incl(e);
+    int before = incl - s, ebefore = einc - e;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (4 * lane + q < G) segoff[4 * lane + q] = before;
+      const int sg = 4 * lane + q;
+      if (sg < G) {
+        segoff[sg] = before;
+        segcnt[sg] = c[q];
+        remoff[sg] = ebefore;
+      }
       before += c[q];
+      ebefore += ex[q];
     }
-    if (lane == kWave - 1) segoff[G] = incl;
-    kap = wave_umax(kap);
+    if (lane == kWave - 1) {
+      segoff[G] = incl;
+      remoff[G] = einc;
+    }
+    kap = dpp_umax(kap);
     if (lane == 0) {
       s_kap = kap;
       s_ns = 0;
@@ -3145,7 +3266,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
     }
   }
   __syncthreads();
-  const int nc = segoff[G];
+  const int nc = segoff[G], nrem = remoff[G];
   const uint32_t kap = s_kap;
   // candidate i of the row (index order): segment by binary search
   auto cand_at = [&](int i) -> u64 {
@@ -3171,33 +3292,54 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       for (int t = 0; t < kResPer; ++t) f(base + t * kOneThreads + tid, vv[t]);
     }
   };
-  // S into LDS (while it fits) and the row maximum
+  // S into LDS (while it fits) and the row maximum: the loaded slots, then
+  // the candidates past Kc
   u64 *Ls = reinterpret_cast<u64 *>(dyn + kSOffL);
   {
     uint32_t kmx = 0u;
-    for_cands([&](int i, u64 w) {
+    auto take = [&](bool valid, u64 w) {
       const uint32_t key = (uint32_t)(w >> 32);
-      const bool f = i < nc && key >= kap;
+      const bool f = valid && key >= kap;
       const int at = wave_append(f, &s_ns);
       if (f) {
         if (at < kSRoom) Ls[at] = w;
         kmx = max(kmx, key);
       }
-    });
-    kmx = wave_umax(kmx);
+    };
+#pragma unroll
+    for (int t = 0; t < kSSlotPer; ++t) {
+      if (t * kOneThreads >= nslot) break;   // (uniform)
+      const int sl = t * kOneThreads + tid;
+      take(sl < nslot && (sl & (Kc - 1)) < segcnt[min(sl >> lk, G - 1)], vs[t]);
+    }
+    for (int base = 0; base < nrem; base += kOneThreads * kResPer) {
+      u64 vv[kResPer];
+#pragma unroll
+      for (int t = 0; t < kResPer; ++t) {
+        const int i = base + t * kOneThreads + tid;
+        vv[t] = 0ull;
+        if (i < nrem) {
+          int lo = 0, hi = G;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (remoff[mid] <= i) lo = mid;
+            else hi = mid;
+          }
+          vv[t] = ld_ag(p.cand + (size_t)(row * G + lo) * C + Kc + (i - remoff[lo]));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kResPer; ++t) take(base + t * kOneThreads + tid < nrem, vv[t]);
+    }
+    kmx = dpp_umax(kmx);
     if (lane == 0) atomicMax(&s_kmax, kmx);
   }
   for (int i = tid; i < kSHB; i += kOneThreads) hs[i] = 0u;
-  if (tid == 0) {
-    s_bst = kSHB - 1;
-    s_A = 0;
-    s_n2 = 0x7FFFFFFF;
-  }
   __syncthreads();
   const int ns = s_ns;
   const bool inl = ns <= kSRoom;
   const float zmax = key_to_float(s_kmax);
-  // histogram of S by d = zmax - z; the bin where the count reaches K
+  // histogram of S by d = zmax - z; (wave 0) the bin where the count reaches K
   if (inl) {
     for (int i = tid; i < ns; i += kOneThreads)
       atomicAdd(&hs[sbin(zmax, key_to_float((uint32_t)(Ls[i] >> 32)))], 1u);
@@ -3208,18 +3350,15 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
     });
   }
   __syncthreads();
-  {
-    const int h0 = (int)hs[2 * tid], h1 = (int)hs[2 * tid + 1];
-    int tot;
-    const int inc = iscan_one(h0 + h1, wcnt, tot);
-    const int exc = inc - h0 - h1;
-    if (exc < K && inc >= K) {
-      const bool first = exc + h0 >= K;
-      s_bst = first ? 2 * tid : 2 * tid + 1;
-      s_A = first ? exc : exc + h0;
-      s_n2 = first ? h0 : h1;
+  if (wave == 0) {
+    int bin, before, cnt;
+    first_bin_reaching(hs, K, bin, before, cnt);
+    if (lane == 0) {
+      s_bst = bin;
+      s_A = before;
+      s_n2 = bin < 0 ? 0x7FFFFFFF : cnt;
+      s_m = 0;
     }
-    if (tid == 0) s_m = 0;
   }
   __syncthreads();
   const int bst = s_bst;
@@ -3271,11 +3410,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
           c[q] = (int)hs[255 - 4 * lane - q];
           s += c[q];
         }
-        int incl = s;
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
-        }
+        const int incl = dpp_incl(s);
         int acc = above + incl - s;
         if (acc < K && acc + s >= K) {
           for (int q = 0; q < 4; ++q) {
@@ -3308,8 +3443,8 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   __syncthreads();
   const u64 *top = sort_desc(Sa, Ls, min(s_m, kSSortMax));
 
-  // (3) the row's target over its top K (thread j holds rank j): e, the
-  // top-p and min-p cuts, p'; as samp_row
+  // (3) the row's target over its top K (thread j of the first W waves
+  // holds rank j): e, the top-p and min-p cuts, p'; as samp_row
   const int j = tid;
   double *eR = reinterpret_cast<double *>(dyn + kSOffE);
   double *pR = reinterpret_cast<double *>(dyn + kSOffP);
@@ -3317,16 +3452,16 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   int32_t *idR = reinterpret_cast<int32_t *>(dyn + kSOffId);
   int idj = -1;
   double e = 0.0;
+  float qpre = 0.0f;   // the draft's dense q at this rank's id, loaded early
   Fx fe = fx_zero();
-  {
+  if (j < K) {
     const float z0 = key_to_float((uint32_t)(top[0] >> 32));
-    if (j < K) {
-      const u64 w = top[j];
-      idj = (int)(0xFFFFFFFFu - (uint32_t)w);
-      e = T == 0.0 ? (j == 0 ? 1.0 : 0.0)
-                   : exp(((double)key_to_float((uint32_t)(w >> 32)) - (double)z0) / T);
-      fe = to_fx(e);
-    }
+    const u64 w = top[j];
+    idj = (int)(0xFFFFFFFFu - (uint32_t)w);
+    if (draft_row && p.q && idj >= 0 && idj < p.V) qpre = p.q[(int64_t)r * p.ldq + idj];
+    e = T == 0.0 ? (j == 0 ? 1.0 : 0.0)
+                 : exp(((double)key_to_float((uint32_t)(w >> 32)) - (double)z0) / T);
+    fe = to_fx(e);
   }
   if (tid == 0) {
     s_cp = K;
@@ -3339,16 +3474,16 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
     s_lastw = -1;
   }
   Fx Ssum;
-  const Fx before = fx_excl_one(fe, red, Ssum);
+  const Fx before = fx_excl_w(fe, red, Ssum, W);
   const Fx cum = fx_sum(before, fe);
   if (T == 0.0) {
     if (j == 0) s_cp = 1;
-  } else if (p.top_p < 1.0) {
+  } else if (p.top_p < 1.0 && j < K) {
     Fx thr = to_fx(p.top_p > 0.0 ? p.top_p * fx_to_double(Ssum) : 0.0);
     if (!fx_nonzero(thr)) thr.lo = 1ull;
-    if (j < K && fx_ge(cum, thr) && !fx_ge(before, thr)) s_cp = j + 1;
+    if (fx_ge(cum, thr) && !fx_ge(before, thr)) s_cp = j + 1;
   }
-  if (p.min_p > 0.0) {
+  if (p.min_p > 0.0 && wave < W) {
     const u64 b = __ballot(j >= 1 && j < K && e < p.min_p);
     if (lane == 0 && b) atomicMin(&s_cm, wave * kWave + __ffsll((long long)b) - 1);
   }
@@ -3377,7 +3512,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
     double qj = 0.0;
     if (residual) {
       if (p.q) {
-        if (idj >= 0 && idj < p.V) qj = (double)p.q[(int64_t)r * p.ldq + idj];
+        qj = (double)qpre;
       } else {
         for (int k = 0; k < p.Kq; ++k)
           if (qid[k] == idj) {
@@ -3408,7 +3543,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       wr = to_fx(dres);
     }
   }
-  {
+  if (wave < W) {
     const u64 b0 = __ballot(dres > 0.0), b1 = __ballot(dp > 0.0);
     if (lane == 0) {
       if (b0) atomicMin(&s_fr, wave * kWave + __ffsll((long long)b0) - 1);
@@ -3420,9 +3555,9 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   // all of them are below the fixed-point resolution
   const bool use_res = residual && s_fr != kNone;
   const Fx w = use_res ? wr : we;
-  Fx W;
-  const Fx bef = fx_excl_one(w, red, W);
-  const Fx target = to_fx(ub * fx_to_double(W));
+  Fx Wt;
+  const Fx bef = fx_excl_w(w, red, Wt, W);
+  const Fx target = to_fx(ub * fx_to_double(Wt));
   if (!fx_nonzero(target)) {
     // below 2^-100: u = 0 takes the first positive weight; another target
     // follows the fp64 definition in index order, summed by one thread
@@ -3455,7 +3590,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
       }
       s_pick = (slot >= 0 && slot < kept) ? idR[(int)(uint32_t)byid[slot]] : p.V - 1;
     }
-  } else {
+  } else if (wave < W) {
     if (s < kept && fx_gt(fx_sum(bef, w), target) && !fx_gt(bef, target)) s_pick = ids;
     const u64 b = __ballot(s < kept && fx_nonzero(w));
     if (lane == 0 && b) atomicMax(&s_lastw, wave * kWave + 63 - __clzll((long long)b));
@@ -3470,7 +3605,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
     bool reject = false;
     if (draft_row) {
       double qx = 0.0;
-      if (xvalid) qx = p.q ? (double)qx_dense : (s_qk != kNone ? (double)qpr[s_qk] : 0.0);
+      if (xvalid) qx = p.q ? s_qx : (s_qk != kNone ? (double)qpr[s_qk] : 0.0);
       const double px = xvalid ? s_px : 0.0;
       reject = !((double)p.u[(int64_t)seq * p.M + pos] * qx < px);
     }
@@ -3738,6 +3873,15 @@ hipError_t launch_accept_sampled(const SampledCall &c, void *ws, hipStream_t str
     p.info = reinterpret_cast<u64 *>(w + L.info);
     p.cand = reinterpret_cast<u64 *>(w + L.cand);
     p.res = reinterpret_cast<u64 *>(w + L.res);
+    // first-round slots per segment: a power of two, at most C, all G
+    // segments' slots within kSSlotPer loads a thread, room for K and more
+    int kc = 1, lkc = 0;
+    while (kc * 2 <= L.C && (int64_t)L.G * kc * 2 <= kSSlotPer * kOneThreads &&
+           kc < p.K + 64) {
+      kc *= 2;
+      ++lkc;
+    }
+    p.lkc = lkc;
     static std::once_flag samp_once;
     std::call_once(samp_once, [] {
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(samp_one),
