@@ -3066,6 +3066,212 @@ __device__ __forceinline__ void clear_ag32(uint32_t *c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ Fx fx_readlane(const Fx &a, int l) {
+  Fx r;
+  r.lo = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.lo, l) |
+         ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.lo >> 32), l) << 32);
+  r.hi = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.hi, l) |
+         ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.hi >> 32), l) << 32);
+  return r;
+}
+__device__ __forceinline__ double dbl_readlane(double v, int l) {
+  const u64 b = (u64)__double_as_longlong(v);
+  const u64 r = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l) |
+                ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l) << 32);
+  return __longlong_as_double((long long)r);
+}
+
+// Wave 0 of the last row of a sequence to finish: the accepted run a (the
+// first rejected draft row, else M-1) and the sequence's outputs.
+__device__ void samp_commit(const SampArgs &p, int seq) {
+  const int i = threadIdx.x & (kWave - 1);
+  const u64 rw = i < p.M ? ld_ag(p.res + (size_t)seq * p.M + i) : 0ull;
+  const u64 rej = __ballot(i < p.M - 1 && ((rw >> 31) & 1ull));
+  const int a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
+  const int tok = __shfl((int)(rw & 0x7FFFFFFFull), a);
+  if (i < p.M)
+    p.tokens[(int64_t)seq * p.M + i] =
+        i < a ? p.drafts[(int64_t)seq * (p.M - 1) + i] : (i == a ? tok : -1);
+  if (i == 0) {
+    p.counts[2 * seq] = a;
+    p.counts[2 * seq + 1] = a + 1;
+    p.rollback[seq] = (p.base_len ? p.base_len[seq] : 0) + a + 1;
+    clear_ag32(p.seqcnt + seq);
+  }
+}
+
+// Steps (3)-(5) for K <= 64 on wave 0 alone (the other waves have left):
+// lane j holds rank j; every prefix is a DPP scan, every cut, first and
+// last a ballot, the index order a count over readlane, and the weights
+// reach index order through LDS within the wave, so no workgroup barrier
+// is needed.  Same decisions, in the same arithmetic, as the general path.
+__device__ void samp_small(const SampArgs &p, const u64 *top, int row, int seq, int pos,
+                           double qx_dense, const int32_t *qid, const float *qpr, double ub,
+                           unsigned char *scratch) {
+  const int lane = threadIdx.x & (kWave - 1), K = p.K;
+  const double T = p.T;
+  const bool draft_row = pos < p.M - 1;
+  const int r = seq * (p.M - 1) + pos;
+  const int x = draft_row ? p.drafts[r] : -1;
+  const bool xvalid = x >= 0 && x < p.V;
+  const bool act = lane < K;
+  int idj = -1;
+  double e = 0.0;
+  float qpre = 0.0f;
+  if (act) {
+    const float z0 = key_to_float((uint32_t)(top[0] >> 32));
+    const u64 w = top[lane];
+    idj = (int)(0xFFFFFFFFu - (uint32_t)w);
+    if (draft_row && p.q && idj >= 0 && idj < p.V) qpre = p.q[(int64_t)r * p.ldq + idj];
+    e = T == 0.0 ? (lane == 0 ? 1.0 : 0.0)
+                 : exp(((double)key_to_float((uint32_t)(w >> 32)) - (double)z0) / T);
+  }
+  // softmax mass, top-p and min-p cuts, p'
+  const Fx fe = to_fx(e);
+  const Fx incl = dpp_fx_incl(fe);
+  const Fx before = fx_sub(incl, fe);
+  int cp = K;
+  if (T == 0.0) {
+    cp = 1;
+  } else if (p.top_p < 1.0) {
+    Fx thr = to_fx(p.top_p > 0.0 ? p.top_p * fx_to_double(fx_readlane(incl, kWave - 1)) : 0.0);
+    if (!fx_nonzero(thr)) thr.lo = 1ull;
+    const u64 b = __ballot(act && fx_ge(incl, thr) && !fx_ge(before, thr));
+    if (b) cp = __ffsll((long long)b);
+  }
+  int cm = K;
+  if (p.min_p > 0.0) {
+    const u64 b = __ballot(act && lane >= 1 && e < p.min_p);
+    if (b) cm = __ffsll((long long)b) - 1;
+  }
+  const int kept = min(cp, cm);
+  const bool in = lane < kept;
+  const double pj = in ? e / fx_to_double(fx_readlane(incl, kept - 1)) : 0.0;
+  if (p.out_ids && act) {   // the support: kept entries whose p' is positive in fp64
+    const bool sup = in && pj > 0.0;
+    p.out_ids[(size_t)row * K + lane] = sup ? idj : -1;
+    p.out_probs[(size_t)row * K + lane] = sup ? (float)pj : 0.0f;
+  }
+  // the acceptance input of the row's draft
+  double px = 0.0, qx = 0.0;
+  if (draft_row && xvalid) {
+    const u64 bx = __ballot(in && idj == x);
+    if (bx) px = dbl_readlane(pj, __ffsll((long long)bx) - 1);
+    if (p.q) {
+      qx = qx_dense;
+    } else {
+      for (int k0 = 0; k0 < p.Kq; k0 += kWave) {
+        const u64 bq = __ballot(k0 + lane < p.Kq && qid[k0 + lane] == x);
+        if (bq) {
+          qx = (double)qpr[k0 + __ffsll((long long)bq) - 1];
+          break;
+        }
+      }
+    }
+  }
+  // the draw this row would make: weights at rank order, then index order
+  const bool residual = draft_row;
+  double qj = 0.0;
+  if (residual && in) {
+    if (p.q) {
+      qj = (double)qpre;
+    } else {
+      for (int k = 0; k < p.Kq; ++k)
+        if (qid[k] == idj) {
+          qj = (double)qpr[k];
+          break;
+        }
+    }
+  }
+  double dres = 0.0;
+  Fx wr = fx_zero();
+  if (residual && in) {
+    const double d = pj - qj;
+    dres = d > 0.0 ? d : 0.0;
+    wr = to_fx(dres);
+  }
+  // the residual is used when any of its fp64 weights is positive, even if
+  // all of them are below the fixed-point resolution
+  const bool use_res = residual && __ballot(in && dres > 0.0) != 0ull;
+  const Fx w = use_res ? wr : (in ? fe : fx_zero());
+  int rid = 0;   // place in index order among the kept ids (distinct)
+  for (int k = 0; k < kept; ++k) rid += __builtin_amdgcn_readlane(idj, k) < idj ? 1 : 0;
+  Fx *wS = reinterpret_cast<Fx *>(scratch);
+  int32_t *idS = reinterpret_cast<int32_t *>(scratch + sizeof(Fx) * kWave);
+  double *pS = reinterpret_cast<double *>(scratch + (sizeof(Fx) + 4) * kWave);
+  double *qS = reinterpret_cast<double *>(scratch + (sizeof(Fx) + 12) * kWave);
+  if (in) {
+    wS[rid] = w;
+    idS[rid] = idj;
+    pS[rid] = pj;
+    qS[rid] = qj;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const bool sv = lane < kept;   // lane s now holds index-order slot s
+  const Fx ws = sv ? wS[lane] : fx_zero();
+  const int ids = sv ? idS[lane] : -1;
+  const double dps = sv ? pS[lane] : 0.0;
+  double dress = 0.0;
+  if (residual && sv) {
+    const double d = dps - qS[lane];
+    dress = d > 0.0 ? d : 0.0;
+  }
+  const u64 bfr = __ballot(dress > 0.0), bfp = __ballot(dps > 0.0);
+  const Fx wincl = dpp_fx_incl(ws);
+  const Fx bef = fx_sub(wincl, ws);
+  const Fx target = to_fx(ub * fx_to_double(fx_readlane(wincl, kWave - 1)));
+  int pick;
+  if (!fx_nonzero(target)) {
+    // below 2^-100: u = 0 takes the first positive weight; another target
+    // follows the fp64 definition in index order (every lane alike)
+    int slot = use_res ? (bfr ? __ffsll((long long)bfr) - 1 : kNone)
+                       : (bfp ? __ffsll((long long)bfp) - 1 : kNone);
+    if (ub != 0.0) {
+      auto wgt = [&](int k) {
+        if (!use_res) return pS[k];
+        const double d = pS[k] - qS[k];
+        return d > 0.0 ? d : 0.0;
+      };
+      double Wd = 0.0;
+      int last = -1;
+      for (int k = 0; k < kept; ++k) {
+        const double wk = wgt(k);
+        Wd += wk;
+        if (wk > 0.0) last = k;
+      }
+      const double tt = ub * Wd;
+      double cm2 = 0.0;
+      slot = last;
+      for (int k = 0; k < kept; ++k) {
+        cm2 += wgt(k);
+        if (cm2 > tt) {
+          slot = k;
+          break;
+        }
+      }
+    }
+    pick = (slot >= 0 && slot < kept) ? idS[slot] : p.V - 1;
+  } else {
+    const u64 bp = __ballot(sv && fx_gt(wincl, target) && !fx_gt(bef, target));
+    if (bp) {
+      pick = __builtin_amdgcn_readlane(ids, __ffsll((long long)bp) - 1);
+    } else {   // rounding passed the end: the last positive weight
+      const u64 bl = __ballot(sv && fx_nonzero(ws));
+      pick = bl ? __builtin_amdgcn_readlane(ids, 63 - __clzll((long long)bl)) : p.V - 1;
+    }
+  }
+  // the row's verdict and token; the last row of the sequence commits it
+  bool reject = false;
+  if (draft_row) reject = !((double)p.u[(int64_t)seq * p.M + pos] * qx < px);
+  int last = 0;
+  if (lane == 0) {
+    st_ag(p.res + row, ((u64)(reject ? 1u : 0u) << 31) | (u64)(uint32_t)pick);
+    __builtin_amdgcn_s_waitcnt(0);
+    last = add_ag32(p.seqcnt + seq) == (uint32_t)(p.M - 1) ? 1 : 0;
+  }
+  if (__builtin_amdgcn_readfirstlane(last)) samp_commit(p, seq);
+}
+
 // grid (rows * G), kOneThreads threads, kSDyn bytes of dynamic LDS.
 __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
@@ -3442,6 +3648,10 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
   }
   __syncthreads();
   const u64 *top = sort_desc(Sa, Ls, min(s_m, kSSortMax));
+  if (K <= kWave) {   // one wave from here on
+    if (wave == 0) samp_small(p, top, row, seq, pos, s_qx, qid, qpr, ub, dyn + kSOffE);
+    return;
+  }
 
   // (3) the row's target over its top K (thread j of the first W waves
   // holds rank j): e, the top-p and min-p cuts, p'; as samp_row
@@ -3614,23 +3824,7 @@ __global__ __launch_bounds__(kOneThreads) void samp_one(SampArgs p) {
     s_last = add_ag32(p.seqcnt + seq) == (uint32_t)(p.M - 1);
   }
   __syncthreads();
-  if (!s_last || wave != 0) return;
-  {
-    const int i = lane;
-    const u64 rw = i < p.M ? ld_ag(p.res + (size_t)seq * p.M + i) : 0ull;
-    const u64 rej = __ballot(i < p.M - 1 && ((rw >> 31) & 1ull));
-    const int a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
-    const int tok = __shfl((int)(rw & 0x7FFFFFFFull), a);
-    if (i < p.M)
-      p.tokens[(int64_t)seq * p.M + i] =
-          i < a ? p.drafts[(int64_t)seq * (p.M - 1) + i] : (i == a ? tok : -1);
-    if (i == 0) {
-      p.counts[2 * seq] = a;
-      p.counts[2 * seq + 1] = a + 1;
-      p.rollback[seq] = (p.base_len ? p.base_len[seq] : 0) + a + 1;
-      clear_ag32(p.seqcnt + seq);
-    }
-  }
+  if (s_last && wave == 0) samp_commit(p, seq);
 }
 
 }  // namespace

@@ -130,12 +130,15 @@ def test_sampled_matches_oracle(B, M, V, par):
                   history=hist, base_len=bl)
 
 
+@pytest.mark.parametrize("top_k", [1024, 256, 64])
 @pytest.mark.parametrize("path", ["bonus", "residual"])
-def test_sampled_draw_with_u_zero_takes_the_first_positive_weight(path):
+def test_sampled_draw_with_u_zero_takes_the_first_positive_weight(path, top_k):
     # u_{M-1} = 0: the pick is the kept id of smallest index whose weight is
-    # positive in fp64.  Std-100 logits at T = 0.6 with the top 1024 kept put
-    # nearly every kept weight far below 2^-100 while still positive.
-    par = oracle.sampler(temperature=0.6, top_k=1024)
+    # positive in fp64.  Std-100 logits at T = 0.6 with the top 1024 (the
+    # chained kernels), 256 (one launch) or 64 (one launch, one wave per row
+    # after the sort) kept put nearly every kept weight far below 2^-100
+    # while still positive.
+    par = oracle.sampler(temperature=0.6, top_k=top_k)
     off = 0
     for trial in range(3):
         rng = np.random.default_rng(700 + 10 * trial + (path == "residual"))
@@ -149,7 +152,7 @@ def test_sampled_draw_with_u_zero_takes_the_first_positive_weight(path):
             # no draft mass on the three smallest kept ids: their residual is
             # p' itself, positive but far below 2^-100
             for b in range(B):
-                kept = np.argsort(-z[b, trial + 1], kind="stable")[:1024]
+                kept = np.argsort(-z[b, trial + 1], kind="stable")[:top_k]
                 q[b, trial + 1, np.sort(kept)[:3]] = 0.0
         u = np.full((B, M), 0.5, np.float32)
         u[:, M - 1] = 0.0
