@@ -133,14 +133,144 @@ __device__ __forceinline__ Fx fx_from3(u64 l0, u64 l1, u64 l2) {
 
 __device__ __forceinline__ Fx fx_load3(const u64 *p) { return fx_from3(p[0], p[1], p[2]); }
 
-__device__ __forceinline__ Fx fx_shfl_xor(const Fx &a, int m) {
-  return Fx{(u64)__shfl_xor((long long)a.lo, m), (u64)__shfl_xor((long long)a.hi, m)};
+// DPP moves: lane i reads a lane of its own row of 16 within the same
+// instruction.  dpp0: a shift or broadcast (row_shr:n reads lane i - n,
+// row_bcast:15 and :31 the last lane of the row before, resp. of row 1;
+// lanes without a source, and rows outside row_mask, read 0).  dppp: a
+// permutation within each row.
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118,
+              kDppBcast15 = 0x142, kDppBcast31 = 0x143, kDppSwap1 = 0xB1, kDppSwap2 = 0x4E,
+              kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, row_mask, 0xF, false);
+}
+template <int ctrl>
+__device__ __forceinline__ uint32_t dppp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, 0xF, 0xF, false);
 }
 
-// Exact wave-wide sum (integer adds commute).
-__device__ __forceinline__ Fx fx_wave_sum(Fx a) {
-  for (int m = kWave / 2; m > 0; m >>= 1) fx_add(a, fx_shfl_xor(a, m));
-  return a;
+// Inclusive sum over the lanes of the wave.
+__device__ __forceinline__ int dpp_incl(int x) {
+  x += (int)dpp0<kDppShr1>((uint32_t)x);
+  x += (int)dpp0<kDppShr2>((uint32_t)x);
+  x += (int)dpp0<kDppShr4>((uint32_t)x);
+  x += (int)dpp0<kDppShr8>((uint32_t)x);
+  x += (int)dpp0<kDppBcast15, 0xA>((uint32_t)x);
+  x += (int)dpp0<kDppBcast31, 0xC>((uint32_t)x);
+  return x;
+}
+
+// Wave-wide extrema (the same value in every lane).
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t x) {
+  x = max(x, dppp<kDppSwap1>(x));
+  x = max(x, dppp<kDppSwap2>(x));
+  x = max(x, dppp<kDppHalfMirror>(x));
+  x = max(x, dppp<kDppMirror>(x));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(r0, r1), max(r2, r3));   // unsigned: keys use all 32 bits
+}
+__device__ __forceinline__ uint32_t dpp_umin(uint32_t x) {
+  x = min(x, dppp<kDppSwap1>(x));
+  x = min(x, dppp<kDppSwap2>(x));
+  x = min(x, dppp<kDppHalfMirror>(x));
+  x = min(x, dppp<kDppMirror>(x));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ Fx dpp0_fx(const Fx &a) {
+  Fx r;
+  r.lo = (u64)dpp0<ctrl, row_mask>((uint32_t)a.lo) |
+         ((u64)dpp0<ctrl, row_mask>((uint32_t)(a.lo >> 32)) << 32);
+  r.hi = (u64)dpp0<ctrl, row_mask>((uint32_t)a.hi) |
+         ((u64)dpp0<ctrl, row_mask>((uint32_t)(a.hi >> 32)) << 32);
+  return r;
+}
+
+// Inclusive exact sum over the lanes of the wave.
+__device__ __forceinline__ Fx dpp_fx_incl(Fx x) {
+  fx_add(x, dpp0_fx<kDppShr1>(x));
+  fx_add(x, dpp0_fx<kDppShr2>(x));
+  fx_add(x, dpp0_fx<kDppShr4>(x));
+  fx_add(x, dpp0_fx<kDppShr8>(x));
+  fx_add(x, dpp0_fx<kDppBcast15, 0xA>(x));
+  fx_add(x, dpp0_fx<kDppBcast31, 0xC>(x));
+  return x;
+}
+
+__device__ __forceinline__ Fx fx_readlane(const Fx &a, int l) {
+  Fx r;
+  r.lo = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.lo, l) |
+         ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.lo >> 32), l) << 32);
+  r.hi = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.hi, l) |
+         ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.hi >> 32), l) << 32);
+  return r;
+}
+__device__ __forceinline__ double dbl_readlane(double v, int l) {
+  const u64 b = (u64)__double_as_longlong(v);
+  const u64 r = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l) |
+                ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l) << 32);
+  return __longlong_as_double((long long)r);
+}
+
+// Exact wave-wide sum (integer adds commute), in every lane.  Whole waves
+// call it.
+__device__ __forceinline__ Fx fx_wave_sum(Fx a) { return fx_readlane(dpp_fx_incl(a), kWave - 1); }
+
+// Signed wave-wide extrema, in every lane.  Whole waves call them.
+__device__ __forceinline__ int dpp_imin(int x) {
+  x = min(x, (int)dppp<kDppSwap1>((uint32_t)x));
+  x = min(x, (int)dppp<kDppSwap2>((uint32_t)x));
+  x = min(x, (int)dppp<kDppHalfMirror>((uint32_t)x));
+  x = min(x, (int)dppp<kDppMirror>((uint32_t)x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __forceinline__ int dpp_imax(int x) {
+  x = max(x, (int)dppp<kDppSwap1>((uint32_t)x));
+  x = max(x, (int)dppp<kDppSwap2>((uint32_t)x));
+  x = max(x, (int)dppp<kDppHalfMirror>((uint32_t)x));
+  x = max(x, (int)dppp<kDppMirror>((uint32_t)x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __forceinline__ float dpp_fmax(float x) {
+  x = fmaxf(x, __uint_as_float(dppp<kDppSwap1>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dppp<kDppSwap2>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dppp<kDppHalfMirror>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dppp<kDppMirror>(__float_as_uint(x))));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// An fp64 DPP shift (as dpp0, each half moved alike).
+template <int ctrl, int row_mask = 0xF>
+__device__ __forceinline__ double dpp0_d(double v) {
+  const u64 b = (u64)__double_as_longlong(v);
+  return __longlong_as_double((long long)((u64)dpp0<ctrl, row_mask>((uint32_t)b) |
+                                          ((u64)dpp0<ctrl, row_mask>((uint32_t)(b >> 32)) << 32)));
+}
+
+// Inclusive fp64 sum over the lanes of the wave (a fixed order of additions).
+__device__ __forceinline__ double dpp_dincl(double x) {
+  x += dpp0_d<kDppShr1>(x);
+  x += dpp0_d<kDppShr2>(x);
+  x += dpp0_d<kDppShr4>(x);
+  x += dpp0_d<kDppShr8>(x);
+  x += dpp0_d<kDppBcast15, 0xA>(x);
+  x += dpp0_d<kDppBcast31, 0xC>(x);
+  return x;
 }
 
 // Block-wide sum; result valid in every thread.  `red` holds kBlock/kWave Fx.
@@ -344,14 +474,6 @@ __device__ void hist_to_lds(const u64 *g, u64 *h) {
   }
 }
 
-__device__ __forceinline__ Fx fx_shfl(const Fx &a, int src) {
-  return Fx{(u64)__shfl((long long)a.lo, src), (u64)__shfl((long long)a.hi, src)};
-}
-
-__device__ __forceinline__ Fx fx_shfl_up(const Fx &a, int d) {
-  return Fx{(u64)__shfl_up((long long)a.lo, d), (u64)__shfl_up((long long)a.hi, d)};
-}
-
 __device__ __forceinline__ Fx fx_sub(Fx a, const Fx &b) {
   const u64 lo = a.lo - b.lo;
   a.hi = a.hi - b.hi - (a.lo < b.lo ? 1ull : 0ull);
@@ -483,11 +605,7 @@ __device__ int select_bin_wave(const u64 *h, const Fx &thr, Fx &above) {
     c[i] = h[3 * b + 2];
     fx_add(lsum, m[i]);
   }
-  Fx incl = lsum;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const Fx o = fx_shfl_up(incl, off);
-    if (lane >= off) fx_add(incl, o);
-  }
+  Fx incl = dpp_fx_incl(lsum);
   Fx cum = fx_sum(above, fx_sub(incl, lsum));   // mass of all higher bins
   int found = -1, last = -1;
   Fx found_above = fx_zero(), last_above = fx_zero();
@@ -504,13 +622,13 @@ __device__ int select_bin_wave(const u64 *h, const Fx &thr, Fx &above) {
   const u64 hit = __ballot(found >= 0);
   if (hit) {
     const int src = __ffsll((long long)hit) - 1;
-    above = fx_shfl(found_above, src);
+    above = fx_readlane(found_above, src);
     return __shfl(found, src);
   }
   const u64 occ = __ballot(last >= 0);
   if (!occ) return -1;
   const int src = 63 - __clzll((long long)occ);
-  above = fx_shfl(last_above, src);
+  above = fx_readlane(last_above, src);
   return __shfl(last, src);
 }
 
@@ -861,11 +979,7 @@ __device__ int draw_f64_sequential(const RejArgs &p, const RowState &rs, int row
 // also returns the block total.  `wsum` holds kBlock/kWave Fx.
 __device__ Fx fx_block_exclusive(Fx v, Fx *wsum, Fx &total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  Fx incl = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const Fx o = fx_shfl_up(incl, off);
-    if (lane >= off) fx_add(incl, o);
-  }
+  Fx incl = dpp_fx_incl(v);
   __syncthreads();
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
@@ -1115,14 +1229,8 @@ constexpr int kMaxRangesPerThread = kRanges / kOneThreads;
 static_assert(one_range(kOneChunk) <= kKPer * kWave, "a wave's range fits its registers");
 static_assert(one_range(kOneChunk) <= kOneThreads, "a range fits one entry per thread");
 
-__device__ __forceinline__ int wave_min(int v) {
-  for (int s = kWave / 2; s > 0; s >>= 1) v = min(v, __shfl_xor(v, s));
-  return v;
-}
-__device__ __forceinline__ int wave_max(int v) {
-  for (int s = kWave / 2; s > 0; s >>= 1) v = max(v, __shfl_xor(v, s));
-  return v;
-}
+__device__ __forceinline__ int wave_min(int v) { return dpp_imin(v); }
+__device__ __forceinline__ int wave_max(int v) { return dpp_imax(v); }
 
 // Approximate bin of an entry with non-zero fixed-point mass (x in [-70.5, 0]).
 __device__ __forceinline__ int xbin(double x) {
@@ -1185,11 +1293,7 @@ __device__ Fx fx_sum_one(Fx a, Fx *red) {
 // Exclusive exact prefix over the threads (thread order) and the total.
 __device__ Fx fx_excl_one(Fx v, Fx *red, Fx &total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  Fx incl = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const Fx o = fx_shfl_up(incl, off);
-    if (lane >= off) fx_add(incl, o);
-  }
+  const Fx incl = dpp_fx_incl(v);
   __syncthreads();
   if (lane == kWave - 1) red[wave] = incl;
   __syncthreads();
@@ -1206,11 +1310,7 @@ __device__ Fx fx_excl_one(Fx v, Fx *red, Fx &total) {
 // every workgroup that runs it on the same values gets the same sums).
 __device__ double dscan_one(double v, double *dred) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  double incl = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const double incl = dpp_dincl(v);
   __syncthreads();
   if (lane == kWave - 1) dred[wave] = incl;
   __syncthreads();
@@ -1300,11 +1400,12 @@ __device__ __forceinline__ RowState wait_state(const u64 *rp, uint32_t tag, u64 
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t w = lane < kStateWords ? (uint32_t)wait_slot(rp + kRowState + lane, tag, err) : 0u;
   RowState rs;
-  rs.zmax = __uint_as_float((uint32_t)__shfl((int)w, 5));
-  rs.kappa = (uint32_t)__shfl((int)w, 0);
-  rs.cutoff = __shfl((int)w, 1);
-  rs.all = __shfl((int)w, 2);
-  const u64 mb = (u64)(uint32_t)__shfl((int)w, 3) | ((u64)(uint32_t)__shfl((int)w, 4) << 32);
+  rs.zmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)w, 5));
+  rs.kappa = (uint32_t)__builtin_amdgcn_readlane((int)w, 0);
+  rs.cutoff = __builtin_amdgcn_readlane((int)w, 1);
+  rs.all = __builtin_amdgcn_readlane((int)w, 2);
+  const u64 mb = (u64)(uint32_t)__builtin_amdgcn_readlane((int)w, 3) |
+                 ((u64)(uint32_t)__builtin_amdgcn_readlane((int)w, 4) << 32);
   rs.mass = __longlong_as_double((long long)mb);
   return rs;
 }
@@ -1389,7 +1490,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       st_ag(p.total + 3 * row + tid, 0ull);
       st_ag(p.above + 3 * row + tid, 0ull);
     }
-    for (int s = kWave / 2; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
+    m = dpp_fmax(m);
     if (lane == 0) s_f[wave] = m;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1402,7 +1503,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       uint32_t best = fkey(-__builtin_inff());
       for (int q = lane; q < G; q += kWave)
         best = max(best, (uint32_t)wait_slot(rp + kRowSlots + q, tag, err));
-      for (int s = kWave / 2; s > 0; s >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, s));
+      best = dpp_umax(best);
       if (lane == 0) s_zmax = key_to_float(best);
     }
     __syncthreads();
@@ -1522,11 +1623,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       if (tid == 0 && fx_nonzero(ab)) fx_atomic_add3(p.above + 3 * row, ab);
       if (wave == 0) {
         const int c0 = koff[2 * lane], c1 = koff[2 * lane + 1];
-        int incl = c0 + c1;
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
-        }
+        const int incl = dpp_incl(c0 + c1);
         const int before = incl - c0 - c1;
         koff[2 * lane] = before;
         koff[2 * lane + 1] = before + c0;
@@ -1564,11 +1661,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           c[r] = q < G ? ld_agi(p.ccount + row * G + q) : 0;
           loc += c[r];
         }
-        int incl = loc;
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
-        }
+        int incl = dpp_incl(loc);
         int o = incl - loc;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1714,20 +1807,16 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           __builtin_amdgcn_wave_barrier();
           const u64 v = valid ? sk[lane] : 0ull;
           const Fx f = valid ? to_fx(se2[lane]) : fx_zero();
-          Fx incl = f;
-          for (int off = 1; off < kWave; off <<= 1) {
-            const Fx o = fx_shfl_up(incl, off);
-            if (lane >= off) fx_add(incl, o);
-          }
+          Fx incl = dpp_fx_incl(f);
           const Fx excl = fx_sum(above, fx_sub(incl, f));
           const uint32_t key = (uint32_t)(v >> 32);
           const bool gend = valid && (lane == n2 - 1 || (uint32_t)(sk[lane + 1] >> 32) != key);
           const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
           const int gl = hit ? __ffsll((long long)hit) - 1 : n2 - 1;
-          const uint32_t kap = (uint32_t)__shfl((int)key, gl);
+          const uint32_t kap = (uint32_t)__builtin_amdgcn_readlane((int)key, gl);
           const u64 first = __ballot(valid && key == kap);
           const int gs = __ffsll((long long)first) - 1;
-          const Fx ab = fx_shfl(excl, gs);
+          const Fx ab = fx_readlane(excl, gs);
           if (lane == 0) {
             s_prefix = kap;
             s_abv_lo = ab.lo;
@@ -2058,11 +2147,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
             if (c * kWave >= G) break;   // (uniform)
             const int q = c * kWave + lane;
             const Fx w = use_res ? br[c] : be[c];
-            Fx incl = w;
-            for (int off = 1; off < kWave; off <<= 1) {
-              const Fx o = fx_shfl_up(incl, off);
-              if (lane >= off) fx_add(incl, o);
-            }
+            Fx incl = dpp_fx_incl(w);
             const Fx bef = fx_sum(cum, fx_sub(incl, w));
             const u64 hit = __ballot(!exact && q < G && !fx_gt(bef, target) &&
                                      fx_gt(fx_sum(bef, w), target));
@@ -2070,11 +2155,11 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
               const int l = __ffsll((long long)hit) - 1;
               exact = true;
               blk = c * kWave + l;
-              before = fx_shfl(bef, l);
+              before = fx_readlane(bef, l);
             }
             const u64 nz = __ballot(q < G && fx_nonzero(w));
             if (nz) lastnz = c * kWave + 63 - __clzll((long long)nz);
-            fx_add(cum, fx_shfl(incl, kWave - 1));
+            fx_add(cum, fx_readlane(incl, kWave - 1));
           }
           if (!exact) {
             blk = lastnz;
@@ -2089,18 +2174,14 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
               const u64 *o = p.wsum + rq + (use_res ? 0 : 2 * kRanges);
               w = Fx{ld_ag(o), ld_ag(o + kRanges)};
             }
-            Fx incl = w;
-            for (int off = 1; off < kWave; off <<= 1) {
-              const Fx o = fx_shfl_up(incl, off);
-              if (lane >= off) fx_add(incl, o);
-            }
+            Fx incl = dpp_fx_incl(w);
             const Fx bef = fx_sum(before, fx_sub(incl, w));
             if (exact) {
               const u64 hit = __ballot(lane < kOneWaves && !fx_gt(bef, target) &&
                                        fx_gt(fx_sum(bef, w), target));
               const int l = hit ? __ffsll((long long)hit) - 1 : 0;
               rng = l;
-              before = fx_shfl(bef, l);
+              before = fx_readlane(bef, l);
             } else {
               const u64 nz = __ballot(lane < kOneWaves && fx_nonzero(w));
               rng = nz ? 63 - __clzll((long long)nz) : 0;
@@ -2518,11 +2599,7 @@ constexpr int kRowWaves = kRowThreads / kWave;
 __device__ Fx fx_row_exclusive(Fx v, Fx *wsum, Fx &total) {
   const int nw = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  Fx incl = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const Fx o = fx_shfl_up(incl, off);
-    if (lane >= off) fx_add(incl, o);
-  }
+  const Fx incl = dpp_fx_incl(v);
   __syncthreads();
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
@@ -2878,79 +2955,6 @@ __device__ __forceinline__ int sbin(float zmax, float z) {
   return b < 0 ? 0 : (b < kSHB ? b : kSHB - 1);
 }
 
-// DPP moves: lane i reads a lane of its own row of 16 within the same
-// instruction.  dpp0: a shift or broadcast (row_shr:n reads lane i - n,
-// row_bcast:15 and :31 the last lane of the row before, resp. of row 1;
-// lanes without a source, and rows outside row_mask, read 0).  dppp: a
-// permutation within each row.
-constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118,
-              kDppBcast15 = 0x142, kDppBcast31 = 0x143, kDppSwap1 = 0xB1, kDppSwap2 = 0x4E,
-              kDppHalfMirror = 0x141, kDppMirror = 0x140;
-template <int ctrl, int row_mask = 0xF>
-__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, row_mask, 0xF, false);
-}
-template <int ctrl>
-__device__ __forceinline__ uint32_t dppp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, 0xF, 0xF, false);
-}
-
-// Inclusive sum over the lanes of the wave.
-__device__ __forceinline__ int dpp_incl(int x) {
-  x += (int)dpp0<kDppShr1>((uint32_t)x);
-  x += (int)dpp0<kDppShr2>((uint32_t)x);
-  x += (int)dpp0<kDppShr4>((uint32_t)x);
-  x += (int)dpp0<kDppShr8>((uint32_t)x);
-  x += (int)dpp0<kDppBcast15, 0xA>((uint32_t)x);
-  x += (int)dpp0<kDppBcast31, 0xC>((uint32_t)x);
-  return x;
-}
-
-// Wave-wide extrema (the same value in every lane).
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t x) {
-  x = max(x, dppp<kDppSwap1>(x));
-  x = max(x, dppp<kDppSwap2>(x));
-  x = max(x, dppp<kDppHalfMirror>(x));
-  x = max(x, dppp<kDppMirror>(x));
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
-  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
-  return max(max(r0, r1), max(r2, r3));   // unsigned: keys use all 32 bits
-}
-__device__ __forceinline__ uint32_t dpp_umin(uint32_t x) {
-  x = min(x, dppp<kDppSwap1>(x));
-  x = min(x, dppp<kDppSwap2>(x));
-  x = min(x, dppp<kDppHalfMirror>(x));
-  x = min(x, dppp<kDppMirror>(x));
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
-  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
-  return min(min(r0, r1), min(r2, r3));
-}
-
-template <int ctrl, int row_mask = 0xF>
-__device__ __forceinline__ Fx dpp0_fx(const Fx &a) {
-  Fx r;
-  r.lo = (u64)dpp0<ctrl, row_mask>((uint32_t)a.lo) |
-         ((u64)dpp0<ctrl, row_mask>((uint32_t)(a.lo >> 32)) << 32);
-  r.hi = (u64)dpp0<ctrl, row_mask>((uint32_t)a.hi) |
-         ((u64)dpp0<ctrl, row_mask>((uint32_t)(a.hi >> 32)) << 32);
-  return r;
-}
-
-// Inclusive exact sum over the lanes of the wave.
-__device__ __forceinline__ Fx dpp_fx_incl(Fx x) {
-  fx_add(x, dpp0_fx<kDppShr1>(x));
-  fx_add(x, dpp0_fx<kDppShr2>(x));
-  fx_add(x, dpp0_fx<kDppShr4>(x));
-  fx_add(x, dpp0_fx<kDppShr8>(x));
-  fx_add(x, dpp0_fx<kDppBcast15, 0xA>(x));
-  fx_add(x, dpp0_fx<kDppBcast31, 0xC>(x));
-  return x;
-}
-
 // Exclusive exact prefix of v over the threads of the first W waves (thread
 // order; the other threads must pass zero) and their total.  The whole
 // workgroup calls it.
@@ -3064,21 +3068,6 @@ __device__ __forceinline__ uint32_t add_ag32(uint32_t *c) {
 }
 __device__ __forceinline__ void clear_ag32(uint32_t *c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ Fx fx_readlane(const Fx &a, int l) {
-  Fx r;
-  r.lo = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.lo, l) |
-         ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.lo >> 32), l) << 32);
-  r.hi = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.hi, l) |
-         ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.hi >> 32), l) << 32);
-  return r;
-}
-__device__ __forceinline__ double dbl_readlane(double v, int l) {
-  const u64 b = (u64)__double_as_longlong(v);
-  const u64 r = (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l) |
-                ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l) << 32);
-  return __longlong_as_double((long long)r);
 }
 
 // Wave 0 of the last row of a sequence to finish: the accepted run a (the
