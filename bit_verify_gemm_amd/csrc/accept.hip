@@ -340,10 +340,11 @@ constexpr int kMaxOneBlocks = 256;
 constexpr int kXBins = 1024;          // approximate mass bins of the cut search
 // Workspace header (offset 0, the same for every shape): one 4 KiB page per
 // row and one for the call, so that the words workgroups wait on lie apart.
-// Row page: arrival counters of the mass pass, the candidate step and the
-// draw step; the row's tagged candidate-bin and state words; its
-// workgroups' tagged chunk maxima.  Call page: the count of rows whose draw
-// sums are in, an error word, the generation number of the last call.  Zero
+// Row page: arrival counters of the mass pass and the candidate step (a
+// third word is kept zero); the row's tagged candidate-bin and state words;
+// its workgroups' tagged chunk maxima.  Call page: the count of workgroups
+// whose draw sums are in, an error word, the generation number of the last
+// call.  Zero
 // before first use; every call of the one-launch kernel leaves the counters
 // zero and advances the generation number (the tagged words need no reset).
 constexpr int kPageWords = 512;
@@ -1440,7 +1441,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   float *zc = reinterpret_cast<float *>(dyn);                          // [C] logits
   double *ec = reinterpret_cast<double *>(dyn + one_e_offset(C));      // [C] e_or_zero
   uint16_t *bc = reinterpret_cast<uint16_t *>(dyn + one_b_offset(C));  // [C] bin or 0xFFFF
-  __shared__ double ah[kXBins];
+  __shared__ u64 hx[3 * kXBins];   // exact bin masses, three carry-free limbs (fx_atomic_add3)
   __shared__ u64 sh[kBins * 3];
   __shared__ Fx red[kOneWaves], wred[kOneWaves];
   __shared__ double dred[kOneWaves];
@@ -1512,8 +1513,10 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   const float zmax = s_zmax;
 
   // (2) e of every entry (kept in LDS), the row's exact mass and, with
-  // top_p < 1, its approximate histogram over x
-  if (nucleus) ah[tid] = 0.0;
+  // top_p < 1, the chunk's exact mass per bin of x (kept for step 3) and the
+  // row's approximate histogram
+  if (nucleus)
+    for (int i = tid; i < 3 * kXBins; i += kOneThreads) hx[i] = 0ull;
   __syncthreads();
   {
     Fx tot = fx_zero();
@@ -1526,14 +1529,21 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       if (fx_nonzero(f)) {
         fx_add(tot, f);
         b = (uint16_t)xbin(x);
-        if (nucleus)
-          __hip_atomic_fetch_add(&ah[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (nucleus) {
+          u64 *h = hx + 3 * b;
+          if (f.lo & 0xFFFFFFFFull) atomicAdd(h, f.lo & 0xFFFFFFFFull);
+          if (f.lo >> 32) atomicAdd(h + 1, f.lo >> 32);
+          if (f.hi) atomicAdd(h + 2, f.hi);
+        }
       }
       bc[i] = b;
     }
     tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram)
     if (tid == 0 && fx_nonzero(tot)) fx_atomic_add3(p.total + 3 * row, tot);
-    if (nucleus && ah[tid] != 0.0) unsafeAtomicAdd(p.ahist + (size_t)row * kXBins + tid, ah[tid]);
+    if (nucleus) {
+      const Fx m = fx_load3(hx + 3 * tid);
+      if (fx_nonzero(m)) unsafeAtomicAdd(p.ahist + (size_t)row * kXBins + tid, fx_to_double(m));
+    }
   }
   // arrival; the last workgroup of the row reads the row's sums
   __builtin_amdgcn_s_waitcnt(0);
@@ -1606,16 +1616,16 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     __syncthreads();
     const int blo = s_blo, bhi = s_bhi;
 
-    // (3) the exact mass above the range, and the candidates in index order
-    // (entry k * kOneThreads + t is thread t's k-th)
+    // (3) the exact mass above the range (the chunk's bins before blo, one a
+    // thread), and the candidates in index order (entry k * kOneThreads + t
+    // is thread t's k-th)
     {
-      Fx ab = fx_zero();
+      Fx ab = tid < blo ? fx_load3(hx + 3 * tid) : fx_zero();
       u64 bal[kKPer];
 #pragma unroll
       for (int k = 0; k < kKPer; ++k) {
         const int i = k * kOneThreads + tid;
         const int b = i < n ? (int)bc[i] : 0xFFFF;
-        if (b < blo) fx_add(ab, to_fx(ec[i]));
         bal[k] = __ballot(b >= blo && b <= bhi);
         if (lane == 0) koff[k * kOneWaves + wave] = __popcll(bal[k]);
       }
@@ -1781,9 +1791,9 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       u64 nk = 0ull;
       int cut_pos = -1;   // where the cut group starts among the sorted entries
       // the fine bin's entries, gathered and sorted by (key descending, index
-      // ascending) in the LDS of the step (2) histogram, when they fit
-      u64 *gk = reinterpret_cast<u64 *>(ah), *sk = gk + kSortMax;
-      double *ge = ah + 2 * kSortMax, *se2 = ah + 3 * kSortMax;
+      // ascending) in the LDS of the step (2) bin masses, when they fit
+      u64 *gk = hx, *sk = gk + kSortMax;   // (hx is free once step 3 has read it)
+      double *ge = reinterpret_cast<double *>(hx + 2 * kSortMax), *se2 = ge + kSortMax;
       const bool small = n2 <= kSortMax;
       // one wave sorts up to kWave entries (from the candidates themselves
       // when they are few, else from the gathered fine bin) and finds the cut
@@ -2001,6 +2011,14 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   {
     const bool residual = row < p.M - 1;
     const int L = one_range(C), rb = wave * L;
+    float qv[kKPer], zv[kKPer];   // (loaded before the wait, which they do not need)
+#pragma unroll
+    for (int r = 0; r < kKPer; ++r) {
+      const int i = rb + r * kWave + lane;
+      const bool ok = r * kWave + lane < L && i < n;
+      qv[r] = (ok && residual) ? p.q[(int64_t)row * p.ldq + j0 + i] : 0.0f;
+      zv[r] = (ok && chunk_lost) ? zr[i] : 0.0f;
+    }
     if (wave == 0) {
       const RowState rs0 = wait_state(rp, tag, err);
       if (lane == 0) {
@@ -2008,14 +2026,6 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         s_fr = kNone;
         s_fe = kNone;
       }
-    }
-    float qv[kKPer], zv[kKPer];
-#pragma unroll
-    for (int r = 0; r < kKPer; ++r) {
-      const int i = rb + r * kWave + lane;
-      const bool ok = r * kWave + lane < L && i < n;
-      qv[r] = (ok && residual) ? p.q[(int64_t)row * p.ldq + j0 + i] : 0.0f;
-      zv[r] = (ok && chunk_lost) ? zr[i] : 0.0f;
     }
     __syncthreads();
     const RowState rs = row_state_of(s_w);
@@ -2068,14 +2078,9 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-      bool last = __hip_atomic_fetch_add(rp + kRowDraw, 1ull, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
-      if (last)
-        last = __hip_atomic_fetch_add(cp + kCallRows, 1ull, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == (u64)(p.M - 1);
-      s_flag = last;
-    }
+    if (tid == 0)   // one count over the call's workgroups
+      s_flag = __hip_atomic_fetch_add(cp + kCallRows, 1ull, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (u64)(p.M * G - 1);
     __syncthreads();
     if (s_flag) {
       // (5) the last workgroup of the call: the accepted run, then the draw
