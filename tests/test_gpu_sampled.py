@@ -215,3 +215,40 @@ def test_sampled_calls_share_one_workspace():
         assert np.array_equal(g[0], o[0]) and np.array_equal(g[1], o[1]), (rep, g, o[:2])
     # the head is back to zero
     assert int(ws[:20480].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "few_values", "masked", "ragged_k_over_chunk",
+                                  "spike_in_one_chunk"])
+def test_sampled_one_launch_edge_rows(kind):
+    # rows that take the one-launch kernel's slow paths: a cut bin too full
+    # to sort (all equal, few distinct values), candidate sets larger than
+    # the resolver keeps in LDS, a last chunk shorter than top_k, all the
+    # large logits in one chunk, rows of -1e30 with a few finite entries
+    rng = np.random.default_rng(sum(map(ord, kind)))   # (a fixed seed per case)
+    B, M, V = 2, 4, 40000
+    K = 64
+    if kind == "ragged_k_over_chunk":
+        V, K = 5000 + 37, 1024         # chunks of 1008 (the last 1005): none holds K
+    par = oracle.sampler(temperature=0.8, top_p=0.9, min_p=0.01, top_k=K, repeat_penalty=1.2,
+                         penalty_last_n=16)
+    if kind == "all_equal":
+        z = np.full((B, M, V), 1.5, np.float32)
+    elif kind == "few_values":
+        z = rng.integers(0, 3, size=(B, M, V)).astype(np.float32) * 0.5
+    elif kind == "masked":
+        z = np.full((B, M, V), -1e30, np.float32)
+        for b in range(B):
+            for i in range(M):
+                keep = rng.choice(V, 100, replace=False)
+                z[b, i, keep] = rng.standard_normal(100).astype(np.float32) * 2
+    elif kind == "spike_in_one_chunk":
+        z = rng.standard_normal((B, M, V)).astype(np.float32)
+        z[:, :, 2000:2500] += 6.0
+    else:
+        z = (rng.standard_normal((B, M, V)) * 3).astype(np.float32)
+    d = drafts_for(rng, z, par, True)
+    u = rng.random((B, M)).astype(np.float32)
+    q = rng.dirichlet(np.full(V, 0.3), size=(B, M - 1)).astype(np.float32)
+    hist = [list(rng.integers(0, V, 10)) for _ in range(B)]
+    log("sampled edge", kind, B, M, V, K)
+    check(z, d, u, par, kind, q=q, history=hist)
