@@ -301,7 +301,8 @@ struct RowState {
   float zmax;
   uint32_t kappa;   // key of the last nucleus value (all keys >= kappa)
   int32_t cutoff;   // entries with key == kappa and index <= cutoff are inside
-  int32_t all;      // 1: the nucleus is the whole row
+  int32_t all;      // bit 0: the nucleus is the whole row; bit 1 (rej_one): the
+                    // row's resolving workgroup drew the row's token itself
   double mass;      // nucleus mass S' (sum of e over the nucleus)
 };
 
@@ -326,7 +327,8 @@ constexpr int kBlkWords = 6;
 constexpr int kNone = 0x7FFFFFFF;
 
 struct Layout {
-  size_t hdr, maxp, zmax, hist, total, sel, rows, acc, blk, gpart, ahist, above, ccount,
+  size_t hdr, maxp, zmax, hist, total, sel, rows, acc, blk, gpart, ahist, above, ccount, acount,
+      asec,
       cand, wsum, bytes;
 };
 
@@ -351,6 +353,10 @@ constexpr int kPageWords = 512;
 constexpr int kRowCnt = 0, kRowCand = 1, kRowDraw = 2, kRowBins = 64, kRowState = 128,
               kRowSlots = 256;
 constexpr int kCallRows = 0, kCallErr = 1, kCallGen = 2;
+constexpr int kRowPick = 192;   // rej_one: the row's tagged token when its resolver drew it
+// rej_one: a workgroup hands its entries above the candidate bins to the
+// row's resolver when it has at most kAboveCap of them
+constexpr int kAboveCap = 256;
 constexpr int kHdrWords = (kMaxRows + 1) * kPageWords;
 static_assert(kRowSlots + kMaxOneBlocks <= kPageWords, "slots fit the row page");
 
@@ -421,6 +427,8 @@ Layout layout(int M, int V) {
   L.ahist = take(sizeof(double) * kXBins * one.rows);
   L.above = take(sizeof(u64) * 3 * M);
   L.ccount = take(sizeof(int32_t) * one.blocks);
+  L.acount = take(sizeof(int32_t) * one.blocks);
+  L.asec = take(sizeof(u64) * kAboveCap * one.blocks);
   L.cand = take(sizeof(u64) * one.cand);
   L.wsum = take(one.blocks ? sizeof(u64) * 4 * kMaxOneBlocks * (kOneThreads / kWave) : 0);
   L.bytes = o;
@@ -454,6 +462,8 @@ struct RejArgs {
   double *ahist;    // rej_one: [row][kXBins] approximate mass histogram
   u64 *above;       // rej_one: [row][L0, L1, L2] exact mass above the candidate bins
   int32_t *ccount;  // rej_one: [row][workgroup] candidates
+  int32_t *acount;  // rej_one: [row][workgroup] entries above the candidate bins, -1: > kAboveCap
+  u64 *asec;        // rej_one: [row][workgroup][kAboveCap] those entries (key << 32 | index)
   u64 *cand;        // rej_one: [row][workgroup][C] candidates (key << 32 | index)
   u64 *wsum;        // rej_one: [res lo, res hi, e lo, e hi][row][workgroup][wave] draw range sums
   int G, C;         // rej_one: workgroups per row, entries per workgroup
@@ -694,7 +704,7 @@ __device__ int find_tth_tie(const float *zr, int V, uint32_t kappa, int t) {
 }
 
 __device__ __forceinline__ bool in_nucleus(const RowState &rs, float z, int j) {
-  if (rs.all) return true;
+  if (rs.all & 1) return true;
   const uint32_t k = fkey(z);
   return k > rs.kappa || (k == rs.kappa && j <= rs.cutoff);
 }
@@ -1176,6 +1186,68 @@ __global__ __launch_bounds__(kBlock) void rej_draw_pick(RejArgs p) {
   }
 }
 
+constexpr int kSSortMax = 2048;   // entries the one-launch resolvers sort at most
+
+// Place in an LDS list for the lanes with `flag` (one atomic per wave on the
+// list's count; order within the list unspecified).  Whole waves call it.
+__device__ __forceinline__ int wave_append(bool flag, int *count) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const u64 b = __ballot(flag);
+  int base = 0;
+  if (lane == 0 && b) base = atomicAdd(count, __popcll(b));
+  base = __builtin_amdgcn_readfirstlane(base);   // every lane is active here
+  return base + __popcll(b & ((1ull << lane) - 1ull));
+}
+
+// Sorts the n (<= kSSortMax) distinct non-zero values of a (LDS, room for
+// kSSortMax) in descending order and returns where they are: in b (room for
+// n) for n <= 256, ranked by counting (1024 / n2 lanes a value, four loads
+// in flight a lane), else in a by a bitonic network.  The whole workgroup
+// calls it.
+__device__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
+  const int tid = threadIdx.x;
+  int n2 = 16;
+  while (n2 < n) n2 <<= 1;
+  __syncthreads();
+  if (n2 <= 256) {
+    const int P = kOneThreads / n2, e = tid / P, part = tid - e * P;
+    const u64 mine = e < n ? a[e] : 0ull;
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    if (e < n) {
+      int k = part;
+      for (; k + 3 * P < n; k += 4 * P) {
+        const u64 x0 = a[k], x1 = a[k + P], x2 = a[k + 2 * P], x3 = a[k + 3 * P];
+        r0 += x0 > mine ? 1 : 0;
+        r1 += x1 > mine ? 1 : 0;
+        r2 += x2 > mine ? 1 : 0;
+        r3 += x3 > mine ? 1 : 0;
+      }
+      for (; k < n; k += P) r0 += a[k] > mine ? 1 : 0;
+    }
+    int rank = (r0 + r1) + (r2 + r3);
+    for (int s = P / 2; s > 0; s >>= 1) rank += __shfl_xor(rank, s);
+    if (e < n && part == 0) b[rank] = mine;
+    __syncthreads();
+    return b;
+  }
+  for (int i = n + tid; i < n2; i += kOneThreads) a[i] = 0ull;
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+      if (tid < n2 / 2) {
+        const int i = ((tid & ~(j - 1)) << 1) | (tid & (j - 1)), l = i | j;
+        const u64 x = a[i], y = a[l];
+        if ((i & k) == 0 ? x < y : x > y) {
+          a[i] = y;
+          a[l] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return a;
+}
+
 // ---- rejection acceptance in one launch --------------------------------------
 //
 // The steps of the kernels above in one launch of G workgroups per row.  Each
@@ -1446,8 +1518,8 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   __shared__ Fx red[kOneWaves], wred[kOneWaves];
   __shared__ double dred[kOneWaves];
   __shared__ int wcnt[kOneWaves];
-  __shared__ int koff[kKPer * kOneWaves + 1];
-  __shared__ int segoff[kMaxOneBlocks];
+  __shared__ int koff[kKPer * kOneWaves + 1], koffa[kKPer * kOneWaves + 1];
+  __shared__ int segoff[kMaxOneBlocks], aoff[kMaxOneBlocks];
   __shared__ float s_f[kOneWaves];
   __shared__ u64 s_gen, s_abv_lo, s_abv_hi, s_nk;
   __shared__ u64 s_w[6];
@@ -1455,6 +1527,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   __shared__ uint32_t s_kmin, s_kmax, s_prefix;
   __shared__ int s_blo, s_bhi, s_last, s_flag, s_nc, s_cut, s_a, s_x;
   __shared__ int s_pick, s_blk, s_lastnz, s_fr, s_fe;
+  __shared__ int s_an, s_nin, s_drew, s_lastw, s_nc2;
   __shared__ Fx s_before;
   const int G = p.G, row = blockIdx.x / G, g = blockIdx.x - row * G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -1468,7 +1541,10 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
 
   // (1) the chunk into LDS and its maximum; this row's sums are cleared
   // (shared out over the row's workgroups) before the maximum is published
-  if (tid == 0) s_gen = ld_ag(cp + kCallGen) + 1ull;
+  if (tid == 0) {
+    s_gen = ld_ag(cp + kCallGen) + 1ull;
+    s_drew = 0;
+  }
   const float *zr = p.z + (int64_t)row * p.ldl + j0;
   {
     float v[kKPer];
@@ -1619,25 +1695,33 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     // (3) the exact mass above the range (the chunk's bins before blo, one a
     // thread), and the candidates in index order (entry k * kOneThreads + t
     // is thread t's k-th)
+    // Entries above the range (in the nucleus whatever the cut) also go to
+    // the workspace when there are at most kAboveCap of them, so that a
+    // resolver whose nucleus is small can draw the row's token alone.
     {
       Fx ab = tid < blo ? fx_load3(hx + 3 * tid) : fx_zero();
-      u64 bal[kKPer];
+      u64 bal[kKPer], abl[kKPer];
 #pragma unroll
       for (int k = 0; k < kKPer; ++k) {
         const int i = k * kOneThreads + tid;
         const int b = i < n ? (int)bc[i] : 0xFFFF;
         bal[k] = __ballot(b >= blo && b <= bhi);
-        if (lane == 0) koff[k * kOneWaves + wave] = __popcll(bal[k]);
+        abl[k] = __ballot(b < blo);
+        if (lane == 0) {
+          koff[k * kOneWaves + wave] = __popcll(bal[k]);
+          koffa[k * kOneWaves + wave] = __popcll(abl[k]);
+        }
       }
-      ab = fx_sum_one(ab, red);     // (its barriers also publish koff)
+      ab = fx_sum_one(ab, red);     // (its barriers also publish koff and koffa)
       if (tid == 0 && fx_nonzero(ab)) fx_atomic_add3(p.above + 3 * row, ab);
-      if (wave == 0) {
-        const int c0 = koff[2 * lane], c1 = koff[2 * lane + 1];
+      if (wave < 2) {
+        int *ko = wave == 0 ? koff : koffa;
+        const int c0 = ko[2 * lane], c1 = ko[2 * lane + 1];
         const int incl = dpp_incl(c0 + c1);
         const int before = incl - c0 - c1;
-        koff[2 * lane] = before;
-        koff[2 * lane + 1] = before + c0;
-        if (lane == kWave - 1) koff[kKPer * kOneWaves] = incl;
+        ko[2 * lane] = before;
+        ko[2 * lane + 1] = before + c0;
+        if (lane == kWave - 1) ko[kKPer * kOneWaves] = incl;
       }
       __syncthreads();
       u64 *seg = p.cand + (size_t)(row * G + g) * C;
@@ -1649,7 +1733,22 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           st_ag(seg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
         }
       }
-      if (tid == 0) st_agi(p.ccount + row * G + g, koff[kKPer * kOneWaves]);
+      const int na = koffa[kKPer * kOneWaves];
+      if (na <= kAboveCap) {
+        u64 *aseg = p.asec + (size_t)(row * G + g) * kAboveCap;
+#pragma unroll
+        for (int k = 0; k < kKPer; ++k) {
+          if ((abl[k] >> lane) & 1ull) {
+            const int i = k * kOneThreads + tid;
+            const int pos = koffa[k * kOneWaves + wave] + __popcll(abl[k] & ((1ull << lane) - 1ull));
+            st_ag(aseg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
+          }
+        }
+      }
+      if (tid == 0) {
+        st_agi(p.ccount + row * G + g, koff[kKPer * kOneWaves]);
+        st_agi(p.acount + row * G + g, na <= kAboveCap ? na : -1);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1664,21 +1763,36 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       // loads first: segment sizes (wave 0), the row's sums (thread 64),
       // the draft (thread 128).
       if (wave == 0) {
-        int c[4], loc = 0;
+        // candidates, and entries above the range (-1: not handed over), a
+        // workgroup at a time
+        int c[4], ca[4], loc = 0, loca = 0;
+        bool over = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int q = 4 * lane + r;
           c[r] = q < G ? ld_agi(p.ccount + row * G + q) : 0;
-          loc += c[r];
+          ca[r] = q < G ? ld_agi(p.acount + row * G + q) : 0;
         }
-        int incl = dpp_incl(loc);
-        int o = incl - loc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          loc += c[r];
+          over = over || ca[r] < 0;
+          loca += max(ca[r], 0);
+        }
+        int incl = dpp_incl(loc), incla = dpp_incl(loca);
+        int o = incl - loc, oa = incla - loca;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           segoff[4 * lane + r] = o;
+          aoff[4 * lane + r] = oa;
           o += c[r];
+          oa += max(ca[r], 0);
         }
-        if (lane == kWave - 1) s_nc = incl;
+        const bool any_over = __ballot(over) != 0ull;
+        if (lane == kWave - 1) {
+          s_nc = incl;
+          s_an = any_over ? -1 : incla;
+        }
       } else if (tid == 64) {
         const u64 *abr = p.above + 3 * row, *tr = p.total + 3 * row;
         for (int w = 0; w < 3; ++w) {
@@ -1992,11 +2106,113 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         __syncthreads();
         cutoff = s_cut;
       }
+      // (3e) a small nucleus: when every workgroup handed over its entries
+      // above the range and the nucleus holds at most kOneThreads entries,
+      // this workgroup draws the row's token itself (the draw row a would
+      // make, as the picker below does it) and the row's other workgroups
+      // leave as soon as they see the state
+      const RowState rs0 = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
+      if (tid == 0) s_nin = 0;
+      __syncthreads();
+      if (s_an >= 0) {   // (uniform)
+        int nin = 0;
+        each([&](u64 v, double) {
+          nin += in_nucleus(rs0, key_to_float((uint32_t)(v >> 32)), (int)(uint32_t)v) ? 1 : 0;
+        });
+        nin = __builtin_amdgcn_readlane(dpp_incl(nin), kWave - 1);
+        if (lane == 0 && nin) atomicAdd(&s_nin, nin);
+      }
+      __syncthreads();
+      const bool tiny = s_an >= 0 && s_an + s_nin <= kOneThreads;
       if (tid == 0) {
-        const RowState rs = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
-        if (row < p.M - 1) publish_acc(p, row, rs, s_x, s_x >= 0, s_zx, s_qx);
+        RowState rs = rs0;
+        if (tiny) rs.all = 2;
+        if (row < p.M - 1) publish_acc(p, row, rs0, s_x, s_x >= 0, s_zx, s_qx);
         __builtin_amdgcn_s_waitcnt(0);   // the acceptance input before the state
         publish_state(rp, tag, rs);
+      }
+      if (tiny) {
+        // the nucleus in index order: entries keyed (~index << 32 | key)
+        u64 *nuc = hx;   // (free: the fine-bin sort is done)
+        const int na = s_an;
+        for (int i = tid; i < na; i += kOneThreads) {
+          int lo = 0, hi = G - 1;   // the last workgroup whose entries start at or before i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (aoff[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          const u64 v = ld_ag(p.asec + (size_t)(row * G + lo) * kAboveCap + (i - aoff[lo]));
+          nuc[i] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (v >> 32);
+        }
+        if (tid == 0) {
+          s_nc2 = na;
+          s_fr = kNone;
+          s_fe = kNone;
+          s_pick = -1;
+          s_lastw = -1;
+        }
+        __syncthreads();
+        for (int base = 0; base < nc; base += kOneThreads) {   // (uniform rounds)
+          const int c = base + tid;
+          const u64 v = c < nl ? lk[c] : (c < nc ? cand_load(c) : 0ull);
+          const bool f =
+              c < nc && in_nucleus(rs0, key_to_float((uint32_t)(v >> 32)), (int)(uint32_t)v);
+          const int at = wave_append(f, &s_nc2);
+          if (f && at < kOneThreads) nuc[at] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (v >> 32);
+        }
+        __syncthreads();
+        const int N = min(s_nc2, kOneThreads);
+        const u64 *srt = sort_desc(nuc, hx + kOneThreads, N);
+        const bool residual = row < p.M - 1;
+        int jt = -1;
+        Fx wr = fx_zero(), we = fx_zero();
+        bool pr = false, pe = false;
+        if (tid < N) {
+          const u64 v = srt[tid];
+          jt = (int)(0xFFFFFFFFu - (uint32_t)(v >> 32));
+          const float qt = residual ? p.q[(int64_t)row * p.ldq + jt] : 0.0f;
+          draw_weights_v(rs0, T, residual, jt, key_to_float((uint32_t)v), (double)qt, false, 0.0,
+                         wr, we, pr, pe);
+        }
+        {   // the first index with a positive fp64 residual, resp. p'
+          const int fr = wave_min(pr ? jt : kNone), fe = wave_min(pe ? jt : kNone);
+          if (lane == 0) {
+            if (fr != kNone) atomicMin(&s_fr, fr);
+            if (fe != kNone) atomicMin(&s_fe, fe);
+          }
+        }
+        __syncthreads();
+        const bool use_res = residual && s_fr != kNone;
+        const Fx w = use_res ? wr : we;
+        Fx tot;
+        const Fx bef = fx_excl_one(w, red, tot);   // (its barriers also publish s_fr, s_fe)
+        const double u = (double)p.u[p.M - 1];
+        const Fx target = to_fx(u * fx_to_double(tot));
+        int pick;
+        if (!fx_nonzero(target)) {
+          if (u == 0.0) {
+            const int f = use_res ? s_fr : s_fe;
+            pick = f != kNone ? f : p.V - 1;
+          } else {
+            pick = draw_f64_sequential<kOneThreads>(p, rs0, row, use_res, u);
+          }
+        } else {
+          if (tid < N && !fx_gt(bef, target) && fx_gt(fx_sum(bef, w), target)) s_pick = jt;
+          const int lw = wave_max(tid < N && fx_nonzero(w) ? jt : -1);
+          if (lane == 0 && lw >= 0) atomicMax(&s_lastw, lw);
+          __syncthreads();
+          pick = s_pick >= 0 ? s_pick : (s_lastw >= 0 ? s_lastw : p.V - 1);
+        }
+        // the row's token, then the arrivals of all of its workgroups at once
+        if (tid == 0) {
+          st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
+          __builtin_amdgcn_s_waitcnt(0);
+          s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
+          s_drew = 1;
+        }
+        __syncthreads();
       }
     }
   }
@@ -2011,6 +2227,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   {
     const bool residual = row < p.M - 1;
     const int L = one_range(C), rb = wave * L;
+    if (!s_drew) {   // (uniform; a resolver that drew its row has arrived already)
     float qv[kKPer], zv[kKPer];   // (loaded before the wait, which they do not need)
 #pragma unroll
     for (int r = 0; r < kKPer; ++r) {
@@ -2029,6 +2246,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     }
     __syncthreads();
     const RowState rs = row_state_of(s_w);
+    if (rs.all & 2) return;   // this row's resolver drew its token: nothing to sum
     Fx sr = fx_zero(), se = fx_zero();
     int fr = kNone, fe = kNone;
 #pragma unroll
@@ -2082,6 +2300,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       s_flag = __hip_atomic_fetch_add(cp + kCallRows, 1ull, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT) == (u64)(p.M * G - 1);
     __syncthreads();
+    }
     if (s_flag) {
       // (5) the last workgroup of the call: the accepted run, then the draw
       // from row a (every row's state, acceptance input and sums are in).
@@ -2099,10 +2318,20 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         const u64 rej = __ballot(reject);
         const int a = rej ? __ffsll((long long)rej) - 1 : p.M - 1;
         const bool residual = a < p.M - 1;
+        bool drawn;
         {   // row a's state (its words are all in: every row arrived after them)
           const RowState rsa = wait_state(p.hdr + (size_t)a * kPageWords, tag, err);
           if (lane == 0) __builtin_memcpy(s_w + 3, &rsa, sizeof(rsa));
+          drawn = (rsa.all & 2) != 0;
         }
+        if (drawn) {   // row a's resolver drew its token (it stored it before arriving)
+          const u64 wp = wait_slot(p.hdr + (size_t)a * kPageWords + kRowPick, tag, err);
+          if (lane == 0) {
+            s_a = a;
+            s_flag = 1;
+            s_pick = (int)(uint32_t)wp;
+          }
+        } else {
         Fx br[kMaxOneBlocks / kWave], be[kMaxOneBlocks / kWave];
         int bfr = kNone, bfe = kNone;
 #pragma unroll
@@ -2207,6 +2436,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           s_fr = use_res ? 1 : 0;
           s_abv_lo = target.lo;
           s_abv_hi = target.hi;
+        }
         }
       }
       __syncthreads();
@@ -2930,7 +3160,6 @@ __global__ __launch_bounds__(kRowThreads) void samp_draw(SampArgs p) {
 constexpr int kSHB = 2048;              // bins of d: exponent and 5 mantissa bits
 constexpr int kSBinBase = 3072;         // bin 0 takes every d below 2^-31
 constexpr int kSRoom = 8192;            // entries of S the resolver keeps in LDS
-constexpr int kSSortMax = 2048;         // entries the resolver sorts
 constexpr int kSMaxG = 256;
 constexpr int kSMaxRows = 4096;
 constexpr int kSMaxSeqs = 1024;
@@ -3006,66 +3235,6 @@ __device__ void first_bin_reaching(const uint32_t *h, int K, int &bin, int &befo
   bin = 32 * L + l2;
   before = __builtin_amdgcn_readlane(inc2 - hv, l2);
   cnt = __builtin_amdgcn_readlane(hv, l2);
-}
-
-// Place in an LDS list for the lanes with `flag` (one atomic per wave on the
-// list's count; order within the list unspecified).  Whole waves call it.
-__device__ __forceinline__ int wave_append(bool flag, int *count) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const u64 b = __ballot(flag);
-  int base = 0;
-  if (lane == 0 && b) base = atomicAdd(count, __popcll(b));
-  base = __builtin_amdgcn_readfirstlane(base);   // every lane is active here
-  return base + __popcll(b & ((1ull << lane) - 1ull));
-}
-
-// Sorts the n (<= kSSortMax) distinct non-zero values of a (LDS, room for
-// kSSortMax) in descending order and returns where they are: in b (room for
-// n) for n <= 256, ranked by counting (1024 / n2 lanes a value, four loads
-// in flight a lane), else in a by a bitonic network.  The whole workgroup
-// calls it.
-__device__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
-  const int tid = threadIdx.x;
-  int n2 = 16;
-  while (n2 < n) n2 <<= 1;
-  __syncthreads();
-  if (n2 <= 256) {
-    const int P = kOneThreads / n2, e = tid / P, part = tid - e * P;
-    const u64 mine = e < n ? a[e] : 0ull;
-    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-    if (e < n) {
-      int k = part;
-      for (; k + 3 * P < n; k += 4 * P) {
-        const u64 x0 = a[k], x1 = a[k + P], x2 = a[k + 2 * P], x3 = a[k + 3 * P];
-        r0 += x0 > mine ? 1 : 0;
-        r1 += x1 > mine ? 1 : 0;
-        r2 += x2 > mine ? 1 : 0;
-        r3 += x3 > mine ? 1 : 0;
-      }
-      for (; k < n; k += P) r0 += a[k] > mine ? 1 : 0;
-    }
-    int rank = (r0 + r1) + (r2 + r3);
-    for (int s = P / 2; s > 0; s >>= 1) rank += __shfl_xor(rank, s);
-    if (e < n && part == 0) b[rank] = mine;
-    __syncthreads();
-    return b;
-  }
-  for (int i = n + tid; i < n2; i += kOneThreads) a[i] = 0ull;
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      __syncthreads();
-      if (tid < n2 / 2) {
-        const int i = ((tid & ~(j - 1)) << 1) | (tid & (j - 1)), l = i | j;
-        const u64 x = a[i], y = a[l];
-        if ((i & k) == 0 ? x < y : x > y) {
-          a[i] = y;
-          a[l] = x;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  return a;
 }
 
 __device__ __forceinline__ uint32_t add_ag32(uint32_t *c) {
@@ -3930,6 +4099,8 @@ hipError_t launch_accept_rejection(const float *logits, int M, int V, int64_t ld
   p.ahist = reinterpret_cast<double *>(w + L.ahist);
   p.above = reinterpret_cast<u64 *>(w + L.above);
   p.ccount = reinterpret_cast<int32_t *>(w + L.ccount);
+  p.acount = reinterpret_cast<int32_t *>(w + L.acount);
+  p.asec = reinterpret_cast<u64 *>(w + L.asec);
   p.cand = reinterpret_cast<u64 *>(w + L.cand);
   p.wsum = reinterpret_cast<u64 *>(w + L.wsum);
   p.G = one_blocks_per_row(M, V);

@@ -195,6 +195,39 @@ def test_draw_with_u_zero_takes_the_first_positive_weight(path):
     assert picks_off_argmax > 0     # the case exercises weights below 2^-100
 
 
+@pytest.mark.parametrize("path", ["bonus", "residual"])
+def test_small_nucleus_draw_with_u_zero(path):
+    # top_p < 1 on std-300 logits with a few entries planted near the top: the
+    # nucleus holds a handful of entries, so the workgroup that resolves a
+    # row's cut draws its token itself; u_{M-1} = 0 takes the smallest kept
+    # index with a positive weight (rarely the argmax), the residual path
+    # also with no draft mass on some of them
+    off = 0
+    for trial in range(3):
+        rng = np.random.default_rng(1300 + 10 * trial + (path == "residual"))
+        M, V = 8, 262144
+        z = (rng.standard_normal((M, V)) * 300.0).astype(np.float32)
+        for i in range(M):
+            near = rng.integers(0, V, 6)
+            z[i, near] = z[i].max() - np.float32(0.5) * np.arange(1, 7, dtype=np.float32)
+        q = W.rand_dirichlet_rows(rng, M - 1, V, 0.1)
+        d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+        if path == "residual":
+            a = trial + 1
+            d[a] = int(rng.integers(0, V))
+            kept = np.argsort(-z[a], kind="stable")[:4]
+            q[a, kept[1:3]] = 0.0
+        u = W.rand_uniforms(rng, M)
+        u[:M - 1] = 0.5
+        u[M - 1] = 0.0
+        o = oracle.accept_rejection(z, q, d, u, 0.6, 0.95, 2, with_margins=True)
+        a = int(o[1][0])
+        assert (a < M - 1) == (path == "residual")
+        off += int(o[0][a] != oracle.argmax(z[a]))
+        check_same(gpu_rej(z, q, d, u, 0.6, 0.95, 2), o[:3], f"small u=0 {path} {trial}", o[3])
+    assert off > 0
+
+
 def test_same_trials_as_the_oracle_law():
     # The GPU reproduces the oracle trial by trial on the uniforms the oracle's
     # chi-square tests use, so the sampling law checked there holds here too.
