@@ -1527,7 +1527,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   __shared__ uint32_t s_kmin, s_kmax, s_prefix;
   __shared__ int s_blo, s_bhi, s_last, s_flag, s_nc, s_cut, s_a, s_x;
   __shared__ int s_pick, s_blk, s_lastnz, s_fr, s_fe;
-  __shared__ int s_an, s_nin, s_drew, s_lastw, s_nc2;
+  __shared__ int s_an, s_drew, s_lastw, s_nc2;
   __shared__ Fx s_before;
   const int G = p.G, row = blockIdx.x / G, g = blockIdx.x - row * G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -1859,6 +1859,28 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         }
       }
       __syncthreads();
+      // What a small nucleus would draw from, fetched while the cut is
+      // resolved (none of it depends on the cut): with every workgroup's
+      // entries above the range handed over and room for them and all the
+      // candidates in one workgroup (pre), the entries above the range and,
+      // for a draft row, the draft's q at every candidate; held in registers
+      // until the draw (the q at the entries above follows in step 3e)
+      const bool pre = s_an >= 0 && s_an + nc <= kOneThreads;
+      const bool draft_row = row < p.M - 1;
+      u64 pv = 0ull;
+      float pqc = 0.0f;
+      if (pre) {
+        if (tid < s_an) {
+          int lo = 0, hi = G - 1;   // the last workgroup whose entries start at or before tid
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (aoff[mid] <= tid) lo = mid;
+            else hi = mid - 1;
+          }
+          pv = ld_ag(p.asec + (size_t)(row * G + lo) * kAboveCap + (tid - aoff[lo]));
+        }
+        if (draft_row && tid < nc) pqc = p.q[(int64_t)row * p.ldq + (int)(uint32_t)lk[tid]];
+      }
       auto each = [&](auto &&f) {   // every candidate once
         for (int c = tid; c < nl; c += kOneThreads) f(lk[c], le[c]);
         for (int c = room + tid; c < nc; c += kOneThreads) {
@@ -2106,24 +2128,14 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         __syncthreads();
         cutoff = s_cut;
       }
-      // (3e) a small nucleus: when every workgroup handed over its entries
-      // above the range and the nucleus holds at most kOneThreads entries,
-      // this workgroup draws the row's token itself (the draw row a would
-      // make, as the picker below does it) and the row's other workgroups
-      // leave as soon as they see the state
+      // (3e) a small nucleus (pre: at most kOneThreads entries in the
+      // nucleus, all of them at hand): this workgroup draws the row's token
+      // itself (the draw row a would make, as the picker below does it) and
+      // the row's other workgroups leave as soon as they see the state
       const RowState rs0 = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
-      if (tid == 0) s_nin = 0;
-      __syncthreads();
-      if (s_an >= 0) {   // (uniform)
-        int nin = 0;
-        each([&](u64 v, double) {
-          nin += in_nucleus(rs0, key_to_float((uint32_t)(v >> 32)), (int)(uint32_t)v) ? 1 : 0;
-        });
-        nin = __builtin_amdgcn_readlane(dpp_incl(nin), kWave - 1);
-        if (lane == 0 && nin) atomicAdd(&s_nin, nin);
-      }
-      __syncthreads();
-      const bool tiny = s_an >= 0 && s_an + s_nin <= kOneThreads;
+      const bool tiny = pre;
+      float pqa = 0.0f;
+      if (tiny && draft_row && tid < s_an) pqa = p.q[(int64_t)row * p.ldq + (int)(uint32_t)pv];
       if (tid == 0) {
         RowState rs = rs0;
         if (tiny) rs.all = 2;
@@ -2132,19 +2144,20 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         publish_state(rp, tag, rs);
       }
       if (tiny) {
-        // the nucleus in index order: entries keyed (~index << 32 | key)
+        // the nucleus in index order: entries keyed (~index << 32 | slot),
+        // slot i < kOneThreads the i-th entry above the range, kOneThreads + c
+        // candidate c
         u64 *nuc = hx;   // (free: the fine-bin sort is done)
+        u64 *abv = reinterpret_cast<u64 *>(dyn + 16384);   // (the candidates use
+        float *qa = reinterpret_cast<float *>(dyn + 8192);  // at most 8 KiB of lk)
+        float *qc = qa + kOneThreads;
         const int na = s_an;
-        for (int i = tid; i < na; i += kOneThreads) {
-          int lo = 0, hi = G - 1;   // the last workgroup whose entries start at or before i
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (aoff[mid] <= i) lo = mid;
-            else hi = mid - 1;
-          }
-          const u64 v = ld_ag(p.asec + (size_t)(row * G + lo) * kAboveCap + (i - aoff[lo]));
-          nuc[i] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (v >> 32);
+        if (tid < na) {
+          abv[tid] = pv;
+          qa[tid] = pqa;
+          nuc[tid] = ((u64)(0xFFFFFFFFu - (uint32_t)pv) << 32) | (uint32_t)tid;
         }
+        if (tid < nc) qc[tid] = pqc;
         if (tid == 0) {
           s_nc2 = na;
           s_fr = kNone;
@@ -2153,17 +2166,18 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           s_lastw = -1;
         }
         __syncthreads();
-        for (int base = 0; base < nc; base += kOneThreads) {   // (uniform rounds)
-          const int c = base + tid;
-          const u64 v = c < nl ? lk[c] : (c < nc ? cand_load(c) : 0ull);
+        {   // the candidates inside the cut (nc <= kOneThreads - na: one round)
+          const int c = tid;
+          const u64 v = c < nc ? lk[c] : 0ull;
           const bool f =
               c < nc && in_nucleus(rs0, key_to_float((uint32_t)(v >> 32)), (int)(uint32_t)v);
           const int at = wave_append(f, &s_nc2);
-          if (f && at < kOneThreads) nuc[at] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (v >> 32);
+          if (f && at < kOneThreads)
+            nuc[at] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (uint32_t)(kOneThreads + c);
         }
         __syncthreads();
         const int N = min(s_nc2, kOneThreads);
-        const u64 *srt = sort_desc(nuc, hx + kOneThreads, N);
+        const u64 *srt = sort_desc(nuc, hx + 2 * kOneThreads, N);
         const bool residual = row < p.M - 1;
         int jt = -1;
         Fx wr = fx_zero(), we = fx_zero();
@@ -2171,9 +2185,12 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         if (tid < N) {
           const u64 v = srt[tid];
           jt = (int)(0xFFFFFFFFu - (uint32_t)(v >> 32));
-          const float qt = residual ? p.q[(int64_t)row * p.ldq + jt] : 0.0f;
-          draw_weights_v(rs0, T, residual, jt, key_to_float((uint32_t)v), (double)qt, false, 0.0,
-                         wr, we, pr, pe);
+          const int sl = (int)(uint32_t)v;
+          const bool ab = sl < kOneThreads;
+          const u64 e0 = ab ? abv[sl] : lk[sl - kOneThreads];
+          const float qt = residual ? (ab ? qa[sl] : qc[sl - kOneThreads]) : 0.0f;
+          draw_weights_v(rs0, T, residual, jt, key_to_float((uint32_t)(e0 >> 32)), (double)qt,
+                         false, 0.0, wr, we, pr, pe);
         }
         {   // the first index with a positive fp64 residual, resp. p'
           const int fr = wave_min(pr ? jt : kNone), fe = wave_min(pe ? jt : kNone);
