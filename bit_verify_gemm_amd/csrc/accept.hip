@@ -1507,6 +1507,64 @@ __device__ __forceinline__ void load_draft(const RejArgs &p, int row, int &x, bo
   qx = valid ? p.q[(int64_t)row * p.ldq + x] : 0.0f;
 }
 
+// The token of a row whose nucleus is at hand, as the picker of rej_one
+// draws it when the accepted run stops at the row: the residual
+// max(0, p' - q) for a draft row (p' if that is all zero), else p', in index
+// order, with u_{M-1}.  srt holds the N <= kOneThreads nucleus entries in
+// index order as (~index << 32 | slot); at(slot, z, q) gives an entry's
+// logit and the draft's q at it.  The whole workgroup calls it; every thread
+// gets the token.
+template <typename At>
+__device__ int rej_nucleus_draw(const RejArgs &p, const RowState &rs, int row, const u64 *srt,
+                                int N, const At &at, Fx *red) {
+  __shared__ int s_fr, s_fe, s_pick, s_lastw;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const bool residual = row < p.M - 1;
+  if (tid == 0) {
+    s_fr = kNone;
+    s_fe = kNone;
+    s_pick = -1;
+    s_lastw = -1;
+  }
+  __syncthreads();
+  int jt = -1;
+  Fx wr = fx_zero(), we = fx_zero();
+  bool pr = false, pe = false;
+  if (tid < N) {
+    const u64 v = srt[tid];
+    jt = (int)(0xFFFFFFFFu - (uint32_t)(v >> 32));
+    float zt, qt;
+    at((int)(uint32_t)v, zt, qt);
+    draw_weights_v(rs, p.T, residual, jt, zt, (double)qt, false, 0.0, wr, we, pr, pe);
+  }
+  {   // the first index with a positive fp64 residual, resp. p'
+    const int fr = wave_min(pr ? jt : kNone), fe = wave_min(pe ? jt : kNone);
+    if (lane == 0) {
+      if (fr != kNone) atomicMin(&s_fr, fr);
+      if (fe != kNone) atomicMin(&s_fe, fe);
+    }
+  }
+  __syncthreads();
+  const bool use_res = residual && s_fr != kNone;
+  const Fx w = use_res ? wr : we;
+  Fx tot;
+  const Fx bef = fx_excl_one(w, red, tot);   // (its barriers also publish s_fr, s_fe)
+  const double u = (double)p.u[p.M - 1];
+  const Fx target = to_fx(u * fx_to_double(tot));
+  if (!fx_nonzero(target)) {
+    if (u == 0.0) {
+      const int f = use_res ? s_fr : s_fe;
+      return f != kNone ? f : p.V - 1;
+    }
+    return draw_f64_sequential<kOneThreads>(p, rs, row, use_res, u);
+  }
+  if (tid < N && !fx_gt(bef, target) && fx_gt(fx_sum(bef, w), target)) s_pick = jt;
+  const int lw = wave_max(tid < N && fx_nonzero(w) ? jt : -1);
+  if (lane == 0 && lw >= 0) atomicMax(&s_lastw, lw);
+  __syncthreads();
+  return s_pick >= 0 ? s_pick : (s_lastw >= 0 ? s_lastw : p.V - 1);
+}
+
 __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   const int C = p.C;
@@ -2158,13 +2216,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           nuc[tid] = ((u64)(0xFFFFFFFFu - (uint32_t)pv) << 32) | (uint32_t)tid;
         }
         if (tid < nc) qc[tid] = pqc;
-        if (tid == 0) {
-          s_nc2 = na;
-          s_fr = kNone;
-          s_fe = kNone;
-          s_pick = -1;
-          s_lastw = -1;
-        }
+        if (tid == 0) s_nc2 = na;
         __syncthreads();
         {   // the candidates inside the cut (nc <= kOneThreads - na: one round)
           const int c = tid;
@@ -2178,49 +2230,15 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
         __syncthreads();
         const int N = min(s_nc2, kOneThreads);
         const u64 *srt = sort_desc(nuc, hx + 2 * kOneThreads, N);
-        const bool residual = row < p.M - 1;
-        int jt = -1;
-        Fx wr = fx_zero(), we = fx_zero();
-        bool pr = false, pe = false;
-        if (tid < N) {
-          const u64 v = srt[tid];
-          jt = (int)(0xFFFFFFFFu - (uint32_t)(v >> 32));
-          const int sl = (int)(uint32_t)v;
-          const bool ab = sl < kOneThreads;
-          const u64 e0 = ab ? abv[sl] : lk[sl - kOneThreads];
-          const float qt = residual ? (ab ? qa[sl] : qc[sl - kOneThreads]) : 0.0f;
-          draw_weights_v(rs0, T, residual, jt, key_to_float((uint32_t)(e0 >> 32)), (double)qt,
-                         false, 0.0, wr, we, pr, pe);
-        }
-        {   // the first index with a positive fp64 residual, resp. p'
-          const int fr = wave_min(pr ? jt : kNone), fe = wave_min(pe ? jt : kNone);
-          if (lane == 0) {
-            if (fr != kNone) atomicMin(&s_fr, fr);
-            if (fe != kNone) atomicMin(&s_fe, fe);
-          }
-        }
-        __syncthreads();
-        const bool use_res = residual && s_fr != kNone;
-        const Fx w = use_res ? wr : we;
-        Fx tot;
-        const Fx bef = fx_excl_one(w, red, tot);   // (its barriers also publish s_fr, s_fe)
-        const double u = (double)p.u[p.M - 1];
-        const Fx target = to_fx(u * fx_to_double(tot));
-        int pick;
-        if (!fx_nonzero(target)) {
-          if (u == 0.0) {
-            const int f = use_res ? s_fr : s_fe;
-            pick = f != kNone ? f : p.V - 1;
-          } else {
-            pick = draw_f64_sequential<kOneThreads>(p, rs0, row, use_res, u);
-          }
-        } else {
-          if (tid < N && !fx_gt(bef, target) && fx_gt(fx_sum(bef, w), target)) s_pick = jt;
-          const int lw = wave_max(tid < N && fx_nonzero(w) ? jt : -1);
-          if (lane == 0 && lw >= 0) atomicMax(&s_lastw, lw);
-          __syncthreads();
-          pick = s_pick >= 0 ? s_pick : (s_lastw >= 0 ? s_lastw : p.V - 1);
-        }
+        const int pick = rej_nucleus_draw(
+            p, rs0, row, srt, N,
+            [&](int sl, float &zt, float &qt) {
+              const bool ab = sl < kOneThreads;
+              const u64 e0 = ab ? abv[sl] : lk[sl - kOneThreads];
+              zt = key_to_float((uint32_t)(e0 >> 32));
+              qt = draft_row ? (ab ? qa[sl] : qc[sl - kOneThreads]) : 0.0f;
+            },
+            red);
         // the row's token, then the arrivals of all of its workgroups at once
         if (tid == 0) {
           st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
