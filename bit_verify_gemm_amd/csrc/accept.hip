@@ -357,7 +357,13 @@ constexpr int kRowPick = 192;   // rej_one: the row's tagged token when its reso
 // rej_one: a workgroup hands its entries above the candidate bins to the
 // row's resolver when it has at most kAboveCap of them
 constexpr int kAboveCap = 256;
-constexpr int kHdrWords = (kMaxRows + 1) * kPageWords;
+// rej_one's exchange area after the pages: kXW tagged words per workgroup
+// (row * G + g): its chunk maximum, its approximate mass, the key of its
+// (kTopK + 1)-th largest entry and its kTopK largest entries (key, index).
+constexpr int kTopK = 2;
+constexpr int kXW = 3 + 2 * kTopK;
+constexpr int kXchg = (kMaxRows + 1) * kPageWords;
+constexpr int kHdrWords = kXchg + kMaxOneBlocks * kXW;
 static_assert(kRowSlots + kMaxOneBlocks <= kPageWords, "slots fit the row page");
 
 // LDS of rej_one for chunks of C entries: logits, e values, approximate bins.
@@ -604,7 +610,7 @@ __device__ __forceinline__ Fx threshold(const RejArgs &p, double S) {
 // the mass to `thr`; if rounding never gets there, the lowest occupied bin.
 // `above` enters as the mass above the histogram's range and leaves as the
 // mass strictly above the chosen bin.  Lane L covers bins 255-4L .. 252-4L.
-__device__ int select_bin_wave(const u64 *h, const Fx &thr, Fx &above) {
+__device__ __forceinline__ int select_bin_wave(const u64 *h, const Fx &thr, Fx &above) {
   const int lane = threadIdx.x & (kWave - 1);
   Fx m[4];
   u64 c[4];
@@ -941,8 +947,8 @@ __device__ __forceinline__ double draw_weight_f64(const RejArgs &p, const RowSta
 // positive index does not settle, or by residuals whose every positive
 // weight is below 2^-100.
 template <int NT>
-__device__ int draw_f64_sequential(const RejArgs &p, const RowState &rs, int row, bool residual,
-                                   double u) {
+__device__ __forceinline__ int draw_f64_sequential(const RejArgs &p, const RowState &rs, int row,
+                                                   bool residual, double u) {
   __shared__ double sw[NT];
   __shared__ double s_t;
   __shared__ int s_found, s_last;
@@ -1204,7 +1210,7 @@ __device__ __forceinline__ int wave_append(bool flag, int *count) {
 // n) for n <= 256, ranked by counting (1024 / n2 lanes a value, four loads
 // in flight a lane), else in a by a bitonic network.  The whole workgroup
 // calls it.
-__device__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
+__device__ __forceinline__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
   const int tid = threadIdx.x;
   int n2 = 16;
   while (n2 < n) n2 <<= 1;
@@ -1338,7 +1344,7 @@ __device__ __forceinline__ double ld_agd(const double *p) {
 // The calling lane waits until slot s carries tag in its high word and
 // returns it (bounded: past kSpinLimit polls the error word is set and the
 // wait ends).
-__device__ u64 wait_slot(const u64 *s, uint32_t tag, u64 *err) {
+__device__ __forceinline__ u64 wait_slot(const u64 *s, uint32_t tag, u64 *err) {
   u64 v = ld_ag(s);
   int it = 0;
   while ((uint32_t)(v >> 32) != tag) {
@@ -1364,7 +1370,7 @@ __device__ Fx fx_sum_one(Fx a, Fx *red) {
 }
 
 // Exclusive exact prefix over the threads (thread order) and the total.
-__device__ Fx fx_excl_one(Fx v, Fx *red, Fx &total) {
+__device__ __forceinline__ Fx fx_excl_one(Fx v, Fx *red, Fx &total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const Fx incl = dpp_fx_incl(v);
   __syncthreads();
@@ -1515,7 +1521,7 @@ __device__ __forceinline__ void load_draft(const RejArgs &p, int row, int &x, bo
 // logit and the draft's q at it.  The whole workgroup calls it; every thread
 // gets the token.
 template <typename At>
-__device__ int rej_nucleus_draw(const RejArgs &p, const RowState &rs, int row, const u64 *srt,
+__device__ __forceinline__ int rej_nucleus_draw(const RejArgs &p, const RowState &rs, int row, const u64 *srt,
                                 int N, const At &at, Fx *red) {
   __shared__ int s_fr, s_fe, s_pick, s_lastw;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -1565,6 +1571,182 @@ __device__ int rej_nucleus_draw(const RejArgs &p, const RowState &rs, int row, c
   return s_pick >= 0 ? s_pick : (s_lastw >= 0 ? s_lastw : p.V - 1);
 }
 
+// ---- rej_one: rows whose cut the top entries settle ------------------------
+//
+// Step (1b) of rej_one.  Every workgroup of a row with top_p < 1 hands over,
+// with its chunk maximum, an approximate mass of its chunk and its kTopK
+// largest entries; every workgroup of the row then reads all of them and
+// takes the same decision, on the same words in the same order.  The top set
+// is every entry of the row whose key exceeds ks, the largest of the
+// workgroups' (kTopK + 1)-th keys (a workgroup hands over all its entries
+// above its own), so it is a prefix of the row in nucleus order.  Sa, the
+// sum of the chunks' approximate masses, differs from the exact mass S of
+// step 2 (fixed point, below V 2^-100 lost) by a relative error below 2^-14:
+// its terms are fp32 exponentials of arguments below 2^8 in magnitude (one
+// ulp each, plus the argument's three roundings), summed eight at a time in
+// fp32 and in fp64 beyond.  So the threshold lies between the thresholds of
+// Sa (1 -+ 2^-9) -+ V 2^-98, and the cut is settled when, over the top set in
+// nucleus order, the first group of equal keys whose exact prefix reaches
+// the upper threshold is the first to reach the lower one, and the count of
+// its ties inside is the same under both.  The row's state then is the one
+// steps 2 and 3 would find.
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// (key << 32 | index) -> a value that descends in nucleus order (key
+// descending, index ascending)
+__device__ __forceinline__ u64 order_key(u64 e) {
+  return (e & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (e & 0xFFFFFFFFull));
+}
+
+__device__ __forceinline__ uint32_t lane_push(int to, uint32_t v) {   // v to lane `to`
+  return (uint32_t)__builtin_amdgcn_ds_permute(to * 4, (int)v);
+}
+
+// Run by one whole wave.  xw: the row's exchange words (payloads), workgroup
+// b's at xw + b * kXW; lst: kWave entries of LDS scratch.  Returns the row
+// maximum in zmax and whether the cut is settled; if so, the row's state in
+// rs and, in lanes < n (the nucleus, in nucleus order), the entries (key << 32
+// | index), their e (as step 2 computes it) and, when want_q, the draft's q.
+// The top sets tried grow: entries above the largest of the workgroups' r-th
+// keys for r = 1, ..., kTopK (a workgroup handed over all of its entries
+// above its own r-th key, its (kTopK + 1)-th in word 2, so each is a prefix of
+// the row), until one holds a group that reaches the lower threshold.
+__device__ __forceinline__ bool rej_top_settle(const RejArgs &p, int row, int G, const uint32_t *xw,
+                                               u64 *lst, bool want_q, float &zmax, RowState &rs,
+                                               u64 &ent, double &ee, float &qe, int &n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double T = p.T;
+  const float L2 = (float)(kLog2e / T);
+  uint32_t best = fkey(-__builtin_inff());
+  for (int b = lane; b < G; b += kWave) best = max(best, xw[b * kXW]);
+  best = dpp_umax(best);
+  zmax = key_to_float(best);
+  double sa = 0.0;   // (the chunks' masses scaled by fp32 exponentials too)
+  for (int b = lane; b < G; b += kWave) {
+    const float sg = __uint_as_float(xw[b * kXW + 1]);
+    if (sg > 0.0f)
+      sa += (double)sg * (double)__builtin_amdgcn_exp2f((key_to_float(xw[b * kXW]) - zmax) * L2);
+  }
+  sa = dbl_readlane(dpp_dincl(sa), kWave - 1);
+  n = 0;
+  if (!(fabsf(zmax) <= 3.4e38f) || !(sa >= 0.5 && sa <= 1e300)) return false;
+  const double slo = fmax(0.0, sa * (1.0 - 0x1p-9) - (double)p.V * 0x1p-98);
+  const double shi = sa * (1.0 + 0x1p-9) + (double)p.V * 0x1p-98;
+  const Fx thl = threshold(p, slo), thh = threshold(p, shi);
+  if (fx_gt(thl, to_fx((double)(G * kTopK)))) return false;   // (every e is at most 1)
+#pragma unroll 1
+  for (int r = 1; r <= kTopK; ++r) {
+    const int wk = r == kTopK ? 2 : 3 + 2 * r;
+    uint32_t ks = 0u;
+    for (int b = lane; b < G; b += kWave) ks = max(ks, xw[b * kXW + wk]);
+    ks = dpp_umax(ks);
+    int nt = 0;
+    for (int c0 = 0; c0 < G * kTopK; c0 += kWave) {
+      const int c = c0 + lane;
+      bool f = false;
+      u64 e = 0ull;
+      if (c < G * kTopK) {
+        const int b = c / kTopK, i = c - b * kTopK;
+        const uint32_t key = xw[b * kXW + 3 + 2 * i];
+        f = key > ks;
+        e = ((u64)key << 32) | xw[b * kXW + 4 + 2 * i];
+      }
+      const u64 bal = __ballot(f);
+      const int pos = nt + __popcll(bal & ((1ull << lane) - 1ull));
+      if (f && pos < kWave) lst[pos] = e;
+      nt += __popcll(bal);
+    }
+    if (nt > kWave) return false;
+    if (nt == 0 || fx_gt(thl, to_fx((double)nt))) continue;   // (every e is at most 1)
+    __builtin_amdgcn_wave_barrier();
+    const bool val = lane < nt;
+    const u64 te = val ? lst[lane] : 0ull;
+    if (__ballot(val && (uint32_t)te >= (uint32_t)p.V)) return false;   // (never: indices of the row)
+    float tq = 0.0f;
+    if (want_q && val) tq = p.q[(int64_t)row * p.ldq + (int)(uint32_t)te];   // (used at the end)
+    // nucleus order: each entry's rank, then entry r to lane r
+    const u64 ok = order_key(te);
+    int rank = val ? 0 : lane;
+    for (int k = 0; k < nt; ++k) {
+      const u64 o = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(ok >> 32), k) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ok, k);
+      rank += (val && o > ok) ? 1 : 0;
+    }
+    const uint32_t skey = lane_push(rank, (uint32_t)(te >> 32));
+    const uint32_t sidx = lane_push(rank, (uint32_t)te);
+    // exact prefix masses (e as step 2 computes it) and the cut group
+    const double e = val ? e_or_zero(key_to_float(skey), zmax, T) : 0.0;
+    const Fx f = to_fx(e);
+    const Fx incl = dpp_fx_incl(f);
+    const uint32_t nkey =
+        (uint32_t)__builtin_amdgcn_ds_bpermute(((lane + 1) & (kWave - 1)) * 4, (int)skey);
+    const bool gend = val && (lane == nt - 1 || nkey != skey);
+    const u64 hh = __ballot(gend && fx_ge(incl, thh)), hl = __ballot(gend && fx_ge(incl, thl));
+    if (!hl) continue;   // the cut lies beyond this set
+    if (!hh || __ffsll((long long)hh) != __ffsll((long long)hl)) return false;
+    const int gl = __ffsll((long long)hh) - 1;   // the cut group's last entry
+    const uint32_t kappa = (uint32_t)__builtin_amdgcn_readlane((int)skey, gl);
+    const int gs = __ffsll((long long)__ballot(val && skey == kappa)) - 1;   // its first
+    const double above_d = fx_to_double(fx_readlane(fx_sub(incl, f), gs));
+    const int nk = gl - gs + 1;
+    const double ek = dbl_readlane(e, gs);   // (e_of at kappa: its x is above -70.5)
+    auto ties_in = [&](const Fx &th) {   // as steps 2 and 3 count them
+      const double tt = ceil((fx_to_double(th) - above_d) / ek);
+      return tt < 1.0 ? 1 : (tt >= (double)nk ? nk : (int)tt);
+    };
+    const int t = ties_in(thl);
+    if (t != ties_in(thh)) return false;
+    const int cutoff = t < nk ? __builtin_amdgcn_readlane((int)sidx, gs + t - 1) : p.V;
+    rs = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
+    n = gs + t;
+    ent = ((u64)skey << 32) | sidx;
+    ee = e;
+    qe = __uint_as_float(lane_push(rank, __float_as_uint(tq)));
+    return true;
+  }
+  return false;
+}
+
+// rej_nucleus_draw by one wave, for n <= kWave nucleus entries held by lanes
+// < n (key << 32 | index, e as step 2 computes it, draft q) in any order.  Returns the token, or -2
+// when u > 0 and the target falls below the fixed-point resolution (the
+// fp64 sequence over the row then decides); use_res as it drew.
+__device__ __forceinline__ int wave_nucleus_draw(const RejArgs &p, const RowState &rs, int row,
+                                                 u64 ent, double ee, float qe, int n, double u,
+                                                 bool &use_res) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool residual = row < p.M - 1, val = lane < n;
+  const int j = val ? (int)(uint32_t)ent : kNone;
+  int rank = val ? 0 : lane;   // index order
+  for (int k = 0; k < n; ++k) rank += (val && __builtin_amdgcn_readlane(j, k) < j) ? 1 : 0;
+  const int jt = (int)lane_push(rank, (uint32_t)j);
+  const float zt = key_to_float(lane_push(rank, (uint32_t)(ent >> 32)));
+  const float qt = __uint_as_float(lane_push(rank, __float_as_uint(qe)));
+  const u64 eb = (u64)__double_as_longlong(ee);
+  const double et = __longlong_as_double(
+      (long long)(((u64)lane_push(rank, (uint32_t)(eb >> 32)) << 32) | lane_push(rank, (uint32_t)eb)));
+  Fx wr = fx_zero(), we = fx_zero();
+  bool pr = false, pe = false;
+  if (val) draw_weights_v(rs, p.T, residual, jt, zt, (double)qt, true, et, wr, we, pr, pe);
+  const int fr = wave_min(pr ? jt : kNone), fe = wave_min(pe ? jt : kNone);
+  use_res = residual && fr != kNone;
+  const Fx w = use_res ? wr : we;
+  const Fx incl = dpp_fx_incl(w);
+  const Fx target = to_fx(u * fx_to_double(fx_readlane(incl, kWave - 1)));
+  if (!fx_nonzero(target)) {
+    if (u == 0.0) {
+      const int f = use_res ? fr : fe;
+      return f != kNone ? f : p.V - 1;
+    }
+    return -2;
+  }
+  const u64 hit = __ballot(val && !fx_gt(fx_sub(incl, w), target) && fx_gt(incl, target));
+  if (hit) return __builtin_amdgcn_readlane(jt, __ffsll((long long)hit) - 1);
+  const int lw = wave_max(val && fx_nonzero(w) ? jt : -1);
+  return lw >= 0 ? lw : p.V - 1;
+}
+
 __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   const int C = p.C;
@@ -1586,6 +1768,9 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   __shared__ int s_blo, s_bhi, s_last, s_flag, s_nc, s_cut, s_a, s_x;
   __shared__ int s_pick, s_blk, s_lastnz, s_fr, s_fe;
   __shared__ int s_an, s_drew, s_lastw, s_nc2;
+  __shared__ int s_fast;
+  __shared__ double s_sw[kOneWaves];
+  __shared__ u64 s_tk[kOneWaves * (kTopK + 1)], s_lst[kWave];
   __shared__ Fx s_before;
   const int G = p.G, row = blockIdx.x / G, g = blockIdx.x - row * G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -1598,12 +1783,16 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   bool chunk_lost = false;   // this workgroup's LDS holds candidates, not its chunk
 
   // (1) the chunk into LDS and its maximum; this row's sums are cleared
-  // (shared out over the row's workgroups) before the maximum is published
+  // (shared out over the row's workgroups) before the maximum is published.
+  // With top_p < 1 each workgroup then also hands over its chunk's
+  // approximate mass and top entries (1b), read and judged in step 2.
   if (tid == 0) {
     s_gen = ld_ag(cp + kCallGen) + 1ull;
     s_drew = 0;
+    s_fast = 0;
   }
   const float *zr = p.z + (int64_t)row * p.ldl + j0;
+  u64 *const xg = p.hdr + kXchg + (size_t)row * G * kXW;   // the row's exchange words
   {
     float v[kKPer];
 #pragma unroll
@@ -1625,21 +1814,102 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       st_ag(p.total + 3 * row + tid, 0ull);
       st_ag(p.above + 3 * row + tid, 0ull);
     }
+    const float mt = m;   // this thread's maximum
     m = dpp_fmax(m);
     if (lane == 0) s_f[wave] = m;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (wave == 0) {
-      const uint32_t tag = (uint32_t)s_gen;
-      if (lane == 0) {
-        for (int w = 1; w < kOneWaves; ++w) m = fmaxf(m, s_f[w]);
-        st_ag(rp + kRowSlots + g, ((u64)tag << 32) | fkey(m));
-      }
+    const uint32_t tag = (uint32_t)s_gen;
+    const float mg = dpp_fmax(lane < kOneWaves ? s_f[lane] : -__builtin_inff());
+    if (wave == 0) {   // this chunk's maximum out, the row's in
+      if (lane == 0)
+        st_ag(nucleus ? xg + (size_t)g * kXW : rp + kRowSlots + g, ((u64)tag << 32) | fkey(mg));
+      const u64 *sl = nucleus ? xg : rp + kRowSlots;
+      const int st = nucleus ? kXW : 1;
       uint32_t best = fkey(-__builtin_inff());
-      for (int q = lane; q < G; q += kWave)
-        best = max(best, (uint32_t)wait_slot(rp + kRowSlots + q, tag, err));
+      for (int q = lane; q < G; q += kWave) {
+        u64 w = ld_ag(sl + (size_t)q * st);
+        if ((uint32_t)(w >> 32) != tag) w = wait_slot(sl + (size_t)q * st, tag, err);
+        best = max(best, (uint32_t)w);
+      }
       best = dpp_umax(best);
       if (lane == 0) s_zmax = key_to_float(best);
+    }
+    if (nucleus) {
+      // (1b) each wave's mass relative to the chunk maximum (fp32
+      // exponentials) and its kTopK + 1 largest keys with multiplicity (the
+      // winning lane of a round takes its next largest); then wave 0 merges
+      // them into this chunk's words
+      const float L2 = (float)(kLog2e / T);
+      float sw = 0.0f;
+      if (mg > -__builtin_inff()) {
+#pragma unroll
+        for (int k = 0; k < kKPer; ++k) sw += __builtin_amdgcn_exp2f((v[k] - mg) * L2);
+      }
+      const double swd = dbl_readlane(dpp_dincl((double)sw), kWave - 1);
+      // only a wave with at most kTopK wave maxima above its own can hold
+      // one of the chunk's kTopK + 1 largest entries: the others' entries lie
+      // below the chunk's (kTopK + 1)-th key and are left out
+      const bool part =
+          __popcll(__ballot(lane < kOneWaves && s_f[lane & (kOneWaves - 1)] > m)) <= kTopK;
+      uint32_t kk[kKPer];
+#pragma unroll
+      for (int k = 0; k < kKPer; ++k) kk[k] = fkey(v[k]);
+      uint32_t bv = fkey(mt);
+      int bk = 0;
+#pragma unroll
+      for (int k = kKPer - 1; k >= 0; --k) bk = kk[k] == bv ? k : bk;
+      uint32_t taken = 0u;
+      if (!part && lane <= kTopK) s_tk[wave * (kTopK + 1) + lane] = 0ull;
+#pragma unroll 1
+      for (int r = 0; part && r <= kTopK; ++r) {
+        const uint32_t wm = dpp_umax(bv);
+        const int wl = __ffsll((long long)__ballot(bv == wm)) - 1;
+        const int wi = __builtin_amdgcn_readlane(j0 + bk * kOneThreads + tid, wl);
+        if (lane == 0) s_tk[wave * (kTopK + 1) + r] = ((u64)wm << 32) | (uint32_t)wi;
+        if (r < kTopK && lane == wl) {   // the winner's next largest
+          taken |= 1u << bk;
+          bv = 0u;   // (every key of a number is above 0)
+#pragma unroll
+          for (int k = 0; k < kKPer; ++k) {
+            if (!((taken >> k) & 1u) && kk[k] > bv) {
+              bv = kk[k];
+              bk = k;
+            }
+          }
+        }
+      }
+      if (lane == 0) s_sw[wave] = swd;
+      __syncthreads();
+      if (wave == 0) {
+        // this chunk's words 1..: its approximate mass relative to its
+        // maximum, the (kTopK + 1)-th key, the kTopK largest entries
+        const double sg = dbl_readlane(dpp_dincl(lane < kOneWaves ? s_sw[lane] : 0.0), kWave - 1);
+        constexpr int kCand = kOneWaves * (kTopK + 1);
+        static_assert(kCand <= 2 * kWave, "two wave candidates a lane");
+        u64 c0 = lane < kCand ? s_tk[lane] : 0ull;
+        u64 c1 = lane + kWave < kCand ? s_tk[lane + kWave] : 0ull;
+        uint32_t pl = lane == 1 ? __float_as_uint((float)sg) : 0u;
+#pragma unroll 1
+        for (int r = 0; r <= kTopK; ++r) {
+          const bool hi = (uint32_t)(c1 >> 32) > (uint32_t)(c0 >> 32);
+          const uint32_t cv = (uint32_t)((hi ? c1 : c0) >> 32);
+          const uint32_t wm = dpp_umax(cv);
+          const int wl = __ffsll((long long)__ballot(cv == wm)) - 1;
+          const uint32_t wi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(hi ? c1 : c0), wl);
+          if (lane == wl) {
+            if (hi) c1 = 0ull;
+            else c0 = 0ull;
+          }
+          if (r < kTopK) {
+            if (lane == 3 + 2 * r) pl = wm;
+            if (lane == 4 + 2 * r) pl = wi;
+          } else if (lane == 2) {
+            pl = wm;
+          }
+        }
+        if (lane >= 1 && lane < kXW) st_ag(xg + (size_t)g * kXW + lane, ((u64)tag << 32) | pl);
+      }
     }
     __syncthreads();
   }
@@ -1648,9 +1918,33 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
 
   // (2) e of every entry (kept in LDS), the row's exact mass and, with
   // top_p < 1, the chunk's exact mass per bin of x (kept for step 3) and the
-  // row's approximate histogram
+  // row's approximate histogram; meanwhile the row's exchange words are
+  // loaded (into sh, or past the chunk when they do not fit there; with no
+  // room for them the row is never settled), then judged (2a)
   if (nucleus)
     for (int i = tid; i < 3 * kXBins; i += kOneThreads) hx[i] = 0ull;
+  uint32_t *const xw =
+      !nucleus ? nullptr
+      : G * kXW <= kBins * 3 * 2 ? reinterpret_cast<uint32_t *>(sh)
+      : ((one_lds_bytes(C) + 15) & ~15) + G * kXW * 4 <= one_dyn_bytes(C)
+          ? reinterpret_cast<uint32_t *>(dyn + ((one_lds_bytes(C) + 15) & ~15))
+          : nullptr;
+  constexpr int kWR = (kMaxOneBlocks * kXW + kOneThreads - 1) / kOneThreads;
+  u64 xv[kWR];
+#pragma unroll
+  for (int r = 0; r < kWR; ++r) {
+    const int i = tid + r * kOneThreads;
+    xv[r] = xw && i < G * kXW ? ld_ag(xg + i) : 0ull;
+  }
+  const bool draw = xw && g == 0 && wave == 0, draft_row = row < p.M - 1;
+  double u_last = 0.0;
+  int dx = -1;
+  bool dvalid = false;
+  float dzx = 0.0f, dqx = 0.0f;
+  if (draw) {   // what workgroup 0 of a settled row needs last, loaded first
+    u_last = (double)p.u[p.M - 1];
+    if (draft_row) load_draft(p, row, dx, dvalid, dzx, dqx);
+  }
   __syncthreads();
   {
     Fx tot = fx_zero();
@@ -1672,582 +1966,638 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       }
       bc[i] = b;
     }
-    tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram)
+#pragma unroll
+    for (int r = 0; r < kWR; ++r) {
+      const int i = tid + r * kOneThreads;
+      if (xw && i < G * kXW) {
+        u64 w = xv[r];
+        if ((uint32_t)(w >> 32) != tag) w = wait_slot(xg + i, tag, err);
+        xw[i] = (uint32_t)w;
+      }
+    }
+    tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram and xw)
     if (tid == 0 && fx_nonzero(tot)) fx_atomic_add3(p.total + 3 * row, tot);
     if (nucleus) {
       const Fx m = fx_load3(hx + 3 * tid);
       if (fx_nonzero(m)) unsafeAtomicAdd(p.ahist + (size_t)row * kXBins + tid, fx_to_double(m));
     }
   }
-  // arrival; the last workgroup of the row reads the row's sums
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_flag = __hip_atomic_fetch_add(rp + kRowCnt, 1ull, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
-  __syncthreads();
-  const bool last2 = s_flag;
-
-  if (!nucleus) {
-    // the whole row is the nucleus: the last workgroup publishes the row's
-    // state (its mass) and the acceptance input
-    if (last2 && tid == 0) {
-      const u64 *tr = p.total + 3 * row;
-      const Fx S = fx_from3(ld_ag(tr), ld_ag(tr + 1), ld_ag(tr + 2));
-      const RowState rs = RowState{zmax, 0u, p.V, 1, fx_to_double(S)};
-      if (row < p.M - 1) {
-        int x;
-        bool valid;
-        float zx, qx;
-        load_draft(p, row, x, valid, zx, qx);
-        publish_acc(p, row, rs, x, valid, zx, qx);
-      }
-      __builtin_amdgcn_s_waitcnt(0);   // the acceptance input before the state
-      publish_state(rp, tag, rs);
-    }
-  } else {
-    // (2b) the range [blo, bhi] of approximate bins that holds the cut, found
-    // by the last workgroup of the row and published in a tagged word.  The
-    // fp64 sums carry a relative error below (C + G + 32) * 2^-53 (the
-    // longest chain of additions behind any of them: within a chunk, over
-    // the chunks, the prefix), and fixed point drops below V * 2^-100; E
-    // bounds both with room to spare.  No bin before blo reaches the
-    // threshold, bin bhi does (or bhi is the last occupied bin).
-    if (last2) {
-      if (tid == 0) {
-        const u64 *tr = p.total + 3 * row;
-        for (int w = 0; w < 3; ++w) s_w[w] = ld_ag(tr + w);
-        s_blo = kXBins;
-        s_bhi = kXBins;
-        s_last = -1;
-      }
-      const double v = ld_agd(p.ahist + (size_t)row * kXBins + tid);
-      const double cum = dscan_one(v, dred);    // (its barriers publish s_w)
-      const double Sd = fx_to_double(fx_from3(s_w[0], s_w[1], s_w[2]));
-      const double thr_d = fx_to_double(threshold(p, Sd));
-      const double E = (double)(C + G + 64) * 0x1p-51 * (Sd + 1.0) + (double)p.V * 0x1p-98;
-      {   // first thread of each condition, last occupied bin: one LDS atomic per wave
-        const u64 b0 = __ballot(cum >= thr_d - E), b1 = __ballot(cum >= thr_d + E);
-        const u64 b2 = __ballot(v > 0.0);
+  if (xw) {
+    // (2a) do the top entries settle the cut?  Every workgroup of the row
+    // judges the same words alike; if so, workgroup 0 draws the row's token
+    // and arrives for all, and the others leave
+    if (wave == 0) {
+      float zm;
+      RowState rs0;
+      u64 ent = 0ull;
+      double ee = 0.0;
+      float qe = 0.0f;
+      int nn = 0;
+      const bool settled =
+          rej_top_settle(p, row, G, xw, s_lst, draw && draft_row, zm, rs0, ent, ee, qe, nn);
+      if (settled && draw) {
+        bool use_res = false;
+        const int pick = wave_nucleus_draw(p, rs0, row, ent, ee, qe, nn, u_last, use_res);
         if (lane == 0) {
-          if (b0) atomicMin(&s_blo, wave * kWave + __ffsll((long long)b0) - 1);
-          if (b1) atomicMin(&s_bhi, wave * kWave + __ffsll((long long)b1) - 1);
-          if (b2) atomicMax(&s_last, wave * kWave + 63 - __clzll((long long)b2));
+          __builtin_memcpy(s_w, &rs0, sizeof(rs0));
+          s_pick = pick;
+          s_fr = use_res ? 1 : 0;
+          if (draft_row) publish_acc(p, row, rs0, dx, dvalid, dzx, dqx);
         }
       }
-      __syncthreads();
-      if (tid == 0) {
-        s_blo = min(s_blo, s_last);
-        s_bhi = min(s_bhi, s_last);
-        st_ag(rp + kRowBins,
-              ((u64)tag << 32) | ((u64)(s_blo + 1) << 16) | (u64)(s_bhi + 1));
-      }
-    } else if (tid == 0) {
-      const u64 w = wait_slot(rp + kRowBins, tag, err);
-      s_blo = (int)((w >> 16) & 0xFFFF) - 1;
-      s_bhi = (int)(w & 0xFFFF) - 1;
+      if (lane == 0) s_fast = settled ? 1 : 0;
     }
     __syncthreads();
-    const int blo = s_blo, bhi = s_bhi;
-
-    // (3) the exact mass above the range (the chunk's bins before blo, one a
-    // thread), and the candidates in index order (entry k * kOneThreads + t
-    // is thread t's k-th)
-    // Entries above the range (in the nucleus whatever the cut) also go to
-    // the workspace when there are at most kAboveCap of them, so that a
-    // resolver whose nucleus is small can draw the row's token alone.
-    {
-      Fx ab = tid < blo ? fx_load3(hx + 3 * tid) : fx_zero();
-      u64 bal[kKPer], abl[kKPer];
-#pragma unroll
-      for (int k = 0; k < kKPer; ++k) {
-        const int i = k * kOneThreads + tid;
-        const int b = i < n ? (int)bc[i] : 0xFFFF;
-        bal[k] = __ballot(b >= blo && b <= bhi);
-        abl[k] = __ballot(b < blo);
-        if (lane == 0) {
-          koff[k * kOneWaves + wave] = __popcll(bal[k]);
-          koffa[k * kOneWaves + wave] = __popcll(abl[k]);
-        }
-      }
-      ab = fx_sum_one(ab, red);     // (its barriers also publish koff and koffa)
-      if (tid == 0 && fx_nonzero(ab)) fx_atomic_add3(p.above + 3 * row, ab);
-      if (wave < 2) {
-        int *ko = wave == 0 ? koff : koffa;
-        const int c0 = ko[2 * lane], c1 = ko[2 * lane + 1];
-        const int incl = dpp_incl(c0 + c1);
-        const int before = incl - c0 - c1;
-        ko[2 * lane] = before;
-        ko[2 * lane + 1] = before + c0;
-        if (lane == kWave - 1) ko[kKPer * kOneWaves] = incl;
+    if (s_fast) {
+      if (g != 0) return;
+      const RowState rs0 = row_state_of(s_w);
+      int pick = s_pick;
+      if (pick == -2)   // below the fixed-point resolution with u > 0
+        pick = draw_f64_sequential<kOneThreads>(p, rs0, row, s_fr != 0, (double)p.u[p.M - 1]);
+      if (tid == 0) {
+        RowState rs = rs0;
+        rs.all = 2;
+        publish_state(rp, tag, rs);
+        st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
+        __builtin_amdgcn_s_waitcnt(0);   // acceptance input, state and token before the count
+        s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
+        s_drew = 1;
       }
       __syncthreads();
-      u64 *seg = p.cand + (size_t)(row * G + g) * C;
-#pragma unroll
-      for (int k = 0; k < kKPer; ++k) {
-        if ((bal[k] >> lane) & 1ull) {
-          const int i = k * kOneThreads + tid;
-          const int pos = koff[k * kOneWaves + wave] + __popcll(bal[k] & ((1ull << lane) - 1ull));
-          st_ag(seg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
-        }
-      }
-      const int na = koffa[kKPer * kOneWaves];
-      if (na <= kAboveCap) {
-        u64 *aseg = p.asec + (size_t)(row * G + g) * kAboveCap;
-#pragma unroll
-        for (int k = 0; k < kKPer; ++k) {
-          if ((abl[k] >> lane) & 1ull) {
-            const int i = k * kOneThreads + tid;
-            const int pos = koffa[k * kOneWaves + wave] + __popcll(abl[k] & ((1ull << lane) - 1ull));
-            st_ag(aseg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
-          }
-        }
-      }
-      if (tid == 0) {
-        st_agi(p.ccount + row * G + g, koff[kKPer * kOneWaves]);
-        st_agi(p.acount + row * G + g, na <= kAboveCap ? na : -1);
-      }
     }
+  }
+  if (!s_drew) {   // (uniform: a row drawn in step 2a goes to step 5)
+    // arrival; the last workgroup of the row reads the row's sums
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      s_flag = __hip_atomic_fetch_add(rp + kRowCand, 1ull, __ATOMIC_RELAXED,
+      s_flag = __hip_atomic_fetch_add(rp + kRowCnt, 1ull, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
     __syncthreads();
+    const bool last2 = s_flag;
 
-    chunk_lost = s_flag;
-    if (s_flag) {
-      // (3b) the last workgroup of the row resolves the cut.  Independent
-      // loads first: segment sizes (wave 0), the row's sums (thread 64),
-      // the draft (thread 128).
-      if (wave == 0) {
-        // candidates, and entries above the range (-1: not handed over), a
-        // workgroup at a time
-        int c[4], ca[4], loc = 0, loca = 0;
-        bool over = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 4 * lane + r;
-          c[r] = q < G ? ld_agi(p.ccount + row * G + q) : 0;
-          ca[r] = q < G ? ld_agi(p.acount + row * G + q) : 0;
+    if (!nucleus) {
+      // the whole row is the nucleus: the last workgroup publishes the row's
+      // state (its mass) and the acceptance input
+      if (last2 && tid == 0) {
+        const u64 *tr = p.total + 3 * row;
+        const Fx S = fx_from3(ld_ag(tr), ld_ag(tr + 1), ld_ag(tr + 2));
+        const RowState rs = RowState{zmax, 0u, p.V, 1, fx_to_double(S)};
+        if (row < p.M - 1) {
+          int x;
+          bool valid;
+          float zx, qx;
+          load_draft(p, row, x, valid, zx, qx);
+          publish_acc(p, row, rs, x, valid, zx, qx);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          loc += c[r];
-          over = over || ca[r] < 0;
-          loca += max(ca[r], 0);
-        }
-        int incl = dpp_incl(loc), incla = dpp_incl(loca);
-        int o = incl - loc, oa = incla - loca;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          segoff[4 * lane + r] = o;
-          aoff[4 * lane + r] = oa;
-          o += c[r];
-          oa += max(ca[r], 0);
-        }
-        const bool any_over = __ballot(over) != 0ull;
-        if (lane == kWave - 1) {
-          s_nc = incl;
-          s_an = any_over ? -1 : incla;
-        }
-      } else if (tid == 64) {
-        const u64 *abr = p.above + 3 * row, *tr = p.total + 3 * row;
-        for (int w = 0; w < 3; ++w) {
-          s_w[w] = ld_ag(abr + w);
-          s_w[3 + w] = ld_ag(tr + w);
-        }
-      } else if (tid == 128 && row < p.M - 1) {
-        int x;
-        bool valid;
-        float zx, qx;
-        load_draft(p, row, x, valid, zx, qx);
-        s_x = valid ? x : -1;
-        s_zx = zx;
-        s_qx = qx;
-      }
-      __syncthreads();
-      const int nc = s_nc;
-      const Fx A = fx_from3(s_w[0], s_w[1], s_w[2]);
-      const double Sd = fx_to_double(fx_from3(s_w[3], s_w[4], s_w[5]));
-      const Fx thr = threshold(p, Sd);
-      const double thr_d = fx_to_double(thr);
-      auto seg_of = [&](int c) {   // the last segment starting at or before c
-        int lo = 0, hi = G - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (segoff[mid] <= c) lo = mid; else hi = mid - 1;
-        }
-        return lo;
-      };
-      auto cand_load = [&](int c) {
-        const int q = seg_of(c);
-        return ld_ag(p.cand + (size_t)(row * G + q) * C + (c - segoff[q]));
-      };
-      auto e_of_key = [&](u64 v) {   // e of a candidate, as step (2) computed it
-        return e_of(key_to_float((uint32_t)(v >> 32)), zmax, T);
-      };
-      // the candidates into LDS, over this workgroup's chunk (reloaded from
-      // the logits if this row draws); any beyond the room stay in the
-      // workspace and are loaded again where needed
-      const int room = one_cand_room(C), nl = min(nc, room);
-      u64 *lk = reinterpret_cast<u64 *>(dyn);
-      double *le = reinterpret_cast<double *>(dyn + (size_t)room * 8);
-      for (int base = 0; base < nl; base += kResPer * kOneThreads) {
-        int sq[kResPer];
-        u64 v[kResPer];
-#pragma unroll
-        for (int k = 0; k < kResPer; ++k) {
-          const int c = base + k * kOneThreads + tid;
-          sq[k] = c < nl ? seg_of(c) : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < kResPer; ++k) {
-          const int c = base + k * kOneThreads + tid;
-          v[k] = c < nl ? ld_ag(p.cand + (size_t)(row * G + sq[k]) * C + (c - segoff[sq[k]]))
-                        : 0ull;
-        }
-#pragma unroll
-        for (int k = 0; k < kResPer; ++k) {
-          const int c = base + k * kOneThreads + tid;
-          if (c < nl) {
-            lk[c] = v[k];
-            le[c] = e_of_key(v[k]);
-          }
-        }
-      }
-      __syncthreads();
-      // What a small nucleus would draw from, fetched while the cut is
-      // resolved (none of it depends on the cut): with every workgroup's
-      // entries above the range handed over and room for them and all the
-      // candidates in one workgroup (pre), the entries above the range and,
-      // for a draft row, the draft's q at every candidate; held in registers
-      // until the draw (the q at the entries above follows in step 3e)
-      const bool pre = s_an >= 0 && s_an + nc <= kOneThreads;
-      const bool draft_row = row < p.M - 1;
-      u64 pv = 0ull;
-      float pqc = 0.0f;
-      if (pre) {
-        if (tid < s_an) {
-          int lo = 0, hi = G - 1;   // the last workgroup whose entries start at or before tid
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (aoff[mid] <= tid) lo = mid;
-            else hi = mid - 1;
-          }
-          pv = ld_ag(p.asec + (size_t)(row * G + lo) * kAboveCap + (tid - aoff[lo]));
-        }
-        if (draft_row && tid < nc) pqc = p.q[(int64_t)row * p.ldq + (int)(uint32_t)lk[tid]];
-      }
-      auto each = [&](auto &&f) {   // every candidate once
-        for (int c = tid; c < nl; c += kOneThreads) f(lk[c], le[c]);
-        for (int c = room + tid; c < nc; c += kOneThreads) {
-          const u64 v = cand_load(c);
-          f(v, e_of_key(v));
-        }
-      };
-      // (3c) one exact pass over fine bins of x: fb(z) = (t - blo) * 256 /
-      // (bhi - blo + 1) with t = -x * kXScale (x as step (2) computes it) is a
-      // monotone function of z like the bins themselves, so the selection
-      // over fine bins is exact, and it spreads the candidates evenly (few
-      // LDS atomics collide).  Digit 255 - fb puts larger logits in higher
-      // bins, as select_bin_wave expects.
-      const double S2 = 256.0 / (double)(bhi - blo + 1);
-      auto fbin = [&](u64 v) {
-        const double x = ((double)key_to_float((uint32_t)(v >> 32)) - (double)zmax) / T;
-        const int b = (int)((-x * kXScale - (double)blo) * S2);
-        return 255 - (b < 0 ? 0 : (b > 255 ? 255 : b));
-      };
-      // (few candidates skip it: they are all sorted directly)
-      const bool few = nc <= kWave;
-      if (!few) {
-        for (int i = tid; i < kBins * 3; i += kOneThreads) sh[i] = 0ull;
-        __syncthreads();
-        each([&](u64 v, double e) { hist_add(sh, fbin(v), to_fx(e)); });
-        __syncthreads();
-        if (wave == 0) {
-          Fx a2 = A;
-          int bin = select_bin_wave(sh, thr, a2);
-          if (bin < 0) bin = 0;
-          if (lane == 0) {
-            s_prefix = (uint32_t)bin;
-            s_abv_lo = a2.lo;
-            s_abv_hi = a2.hi;
-            s_nk = sh[3 * bin + 2];
-            s_nc = 0;
-          }
-        }
-        __syncthreads();
-      }
-      const int fsel = few ? 0 : (int)s_prefix, n2 = few ? nc : (int)s_nk;
-      Fx above = few ? A : Fx{s_abv_lo, s_abv_hi};
-      uint32_t kappa = 0u;
-      u64 nk = 0ull;
-      int cut_pos = -1;   // where the cut group starts among the sorted entries
-      // the fine bin's entries, gathered and sorted by (key descending, index
-      // ascending) in the LDS of the step (2) bin masses, when they fit
-      u64 *gk = hx, *sk = gk + kSortMax;   // (hx is free once step 3 has read it)
-      double *ge = reinterpret_cast<double *>(hx + 2 * kSortMax), *se2 = ge + kSortMax;
-      const bool small = n2 <= kSortMax;
-      // one wave sorts up to kWave entries (from the candidates themselves
-      // when they are few, else from the gathered fine bin) and finds the cut
-      // group in them with wave-level scans
-      auto wave_cut = [&](const u64 *srck, const double *srce) {
-        if (wave == 0) {
-          auto skey = [](u64 v) {
-            return (v & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (v & 0xFFFFFFFFull));
-          };
-          const bool valid = lane < n2;
-          const u64 v0 = valid ? srck[lane] : 0ull;
-          const double e0 = valid ? srce[lane] : 0.0;
-          const u64 mine = skey(v0);
-          int rank = 0;
-          for (int j = 0; j < n2; ++j) rank += skey(srck[j]) > mine;
-          if (valid) {
-            sk[rank] = v0;
-            se2[rank] = e0;
-          }
-          __builtin_amdgcn_s_waitcnt(0);
-          __builtin_amdgcn_wave_barrier();
-          const u64 v = valid ? sk[lane] : 0ull;
-          const Fx f = valid ? to_fx(se2[lane]) : fx_zero();
-          Fx incl = dpp_fx_incl(f);
-          const Fx excl = fx_sum(above, fx_sub(incl, f));
-          const uint32_t key = (uint32_t)(v >> 32);
-          const bool gend = valid && (lane == n2 - 1 || (uint32_t)(sk[lane + 1] >> 32) != key);
-          const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
-          const int gl = hit ? __ffsll((long long)hit) - 1 : n2 - 1;
-          const uint32_t kap = (uint32_t)__builtin_amdgcn_readlane((int)key, gl);
-          const u64 first = __ballot(valid && key == kap);
-          const int gs = __ffsll((long long)first) - 1;
-          const Fx ab = fx_readlane(excl, gs);
-          if (lane == 0) {
-            s_prefix = kap;
-            s_abv_lo = ab.lo;
-            s_abv_hi = ab.hi;
-            s_nk = (u64)(gl - gs + 1);
-            s_cut = gs;
-          }
-        }
-        __syncthreads();
-        kappa = s_prefix;
-        above = Fx{s_abv_lo, s_abv_hi};
-        nk = s_nk;
-        cut_pos = s_cut;
-      };
-      if (nc > 0 && few) {
-        wave_cut(lk, le);
-      } else if (nc > 0 && small) {
-        each([&](u64 v, double e) {
-          if (fbin(v) == fsel) {
-            const int pos = atomicAdd(&s_nc, 1);
-            gk[pos] = v;
-            ge[pos] = e;
-          }
-        });
-        __syncthreads();
-        if (n2 <= kWave) {
-          wave_cut(gk, ge);
-        } else {
-        // rank = entries before this one in the order; the sort key
-        // (key << 32 | ~index) is distinct and descends in that order
-        auto skey = [](u64 v) {
-          return (v & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (v & 0xFFFFFFFFull));
-        };
-        if (tid < n2) {
-          const u64 mine = skey(gk[tid]);
-          int rank = 0;
-          for (int j = 0; j < n2; ++j) rank += skey(gk[j]) > mine;
-          sk[rank] = gk[tid];
-          se2[rank] = ge[tid];
-        }
-        __syncthreads();
-        // exclusive prefix in the order; the cut is the first key whose group
-        // reaches the threshold (else the last group)
-        const u64 v = tid < n2 ? sk[tid] : 0ull;
-        const Fx f = tid < n2 ? to_fx(se2[tid]) : fx_zero();
-        Fx tot_unused;
-        const Fx excl = fx_sum(above, fx_excl_one(f, red, tot_unused));
-        const uint32_t key = (uint32_t)(v >> 32);
-        const bool gend = tid < n2 && (tid == n2 - 1 || (uint32_t)(sk[tid + 1] >> 32) != key);
-        if (tid == 0) {
-          s_blk = 0x7FFFFFFF;
-          s_lastnz = 0x7FFFFFFF;
-        }
-        __syncthreads();
-        {
-          const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
-          if (lane == 0 && hit) atomicMin(&s_blk, wave * kWave + __ffsll((long long)hit) - 1);
-        }
-        __syncthreads();
-        const int gl = s_blk != 0x7FFFFFFF ? s_blk : n2 - 1;   // the cut group's last entry
-        kappa = (uint32_t)(sk[gl] >> 32);
-        {
-          const u64 first = __ballot(tid < n2 && key == kappa);
-          if (lane == 0 && first)
-            atomicMin(&s_lastnz, wave * kWave + __ffsll((long long)first) - 1);
-        }
-        __syncthreads();
-        const int gs = s_lastnz;   // the cut group's first entry
-        if (tid == gs) {
-          s_abv_lo = excl.lo;
-          s_abv_hi = excl.hi;
-        }
-        __syncthreads();
-        above = Fx{s_abv_lo, s_abv_hi};
-        nk = (u64)(gl - gs + 1);
-        cut_pos = gs;
-        }
-      } else if (nc > 0) {
-        // a large fine bin (many equal or nearly equal logits): radix passes
-        // over the keys of its entries
-        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-        each([&](u64 v, double) {
-          if (fbin(v) != fsel) return;
-          const uint32_t k = (uint32_t)(v >> 32);
-          kmn = min(kmn, k);
-          kmx = max(kmx, k);
-        });
-        for (int s2 = kWave / 2; s2 > 0; s2 >>= 1) {
-          kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, s2));
-          kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, s2));
-        }
-        if (tid == 0) {
-          s_kmin = 0xFFFFFFFFu;
-          s_kmax = 0u;
-        }
-        __syncthreads();
-        if (lane == 0) {
-          atomicMin(&s_kmin, kmn);
-          atomicMax(&s_kmax, kmx);
-        }
-        __syncthreads();
-        kmn = s_kmin;
-        kmx = s_kmax;
-        int lo_bit = kmn == kmx ? 0 : 32 - __clz((int)(kmn ^ kmx));
-        uint32_t prefix = lo_bit == 32 ? 0u : (kmn >> lo_bit);
-        nk = (u64)n2;
-        while (lo_bit > 0) {
-          const int db = min(8, lo_bit), shift = lo_bit - db;
-          for (int i = tid; i < kBins * 3; i += kOneThreads) sh[i] = 0ull;
-          __syncthreads();
-          each([&](u64 v, double e) {
-            const uint32_t k = (uint32_t)(v >> 32);
-            if (fbin(v) != fsel || (lo_bit < 32 && (k >> lo_bit) != prefix)) return;
-            hist_add(sh, (int)((k >> shift) & ((1u << db) - 1u)), to_fx(e));
-          });
-          __syncthreads();
-          if (wave == 0) {
-            Fx a2 = above;
-            int bin = select_bin_wave(sh, thr, a2);
-            if (bin < 0) bin = 0;
-            if (lane == 0) {
-              s_prefix = (prefix << db) | (uint32_t)bin;
-              s_abv_lo = a2.lo;
-              s_abv_hi = a2.hi;
-              s_nk = sh[3 * bin + 2];
-            }
-          }
-          __syncthreads();
-          prefix = s_prefix;
-          above = Fx{s_abv_lo, s_abv_hi};
-          nk = s_nk;
-          lo_bit = shift;
-          __syncthreads();
-        }
-        kappa = prefix;
-      }
-      const double ek = e_of(key_to_float(kappa), zmax, T);
-      const double above_d = fx_to_double(above);
-      const double tt = ceil((thr_d - above_d) / ek);
-      const u64 t = (tt < 1.0) ? 1ull : (tt >= (double)nk ? nk : (u64)tt);
-      int cutoff = p.V;
-      if (t < nk && cut_pos >= 0) {
-        // the group is sorted by index: its t-th entry is the last inside
-        cutoff = (int)(uint32_t)sk[cut_pos + (int)t - 1];
-      } else if (t < nk) {
-        // ties at the cut: the first t in index order (the candidates' order)
-        // are inside
-        if (tid == 0) s_cut = p.V;
-        int seen = 0;
-        auto round = [&](bool valid, u64 v) {
-          const bool f = valid && (uint32_t)(v >> 32) == kappa;
-          int pre;
-          const int tot_r = count_one(f, pre, wcnt);
-          if (f && (u64)(seen + pre + 1) == t) s_cut = (int)(uint32_t)v;
-          seen += tot_r;
-          return (u64)seen >= t;
-        };
-        bool done = false;
-        for (int base = 0; !done && base < nc; base += kOneThreads) {
-          const int c = base + tid;
-          done = round(c < nc, c < nl ? lk[c] : (c < nc ? cand_load(c) : 0ull));
-        }
-        __syncthreads();
-        cutoff = s_cut;
-      }
-      // (3e) a small nucleus (pre: at most kOneThreads entries in the
-      // nucleus, all of them at hand): this workgroup draws the row's token
-      // itself (the draw row a would make, as the picker below does it) and
-      // the row's other workgroups leave as soon as they see the state
-      const RowState rs0 = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
-      const bool tiny = pre;
-      float pqa = 0.0f;
-      if (tiny && draft_row && tid < s_an) pqa = p.q[(int64_t)row * p.ldq + (int)(uint32_t)pv];
-      if (tid == 0) {
-        RowState rs = rs0;
-        if (tiny) rs.all = 2;
-        if (row < p.M - 1) publish_acc(p, row, rs0, s_x, s_x >= 0, s_zx, s_qx);
         __builtin_amdgcn_s_waitcnt(0);   // the acceptance input before the state
         publish_state(rp, tag, rs);
       }
-      if (tiny) {
-        // the nucleus in index order: entries keyed (~index << 32 | slot),
-        // slot i < kOneThreads the i-th entry above the range, kOneThreads + c
-        // candidate c
-        u64 *nuc = hx;   // (free: the fine-bin sort is done)
-        u64 *abv = reinterpret_cast<u64 *>(dyn + 16384);   // (the candidates use
-        float *qa = reinterpret_cast<float *>(dyn + 8192);  // at most 8 KiB of lk)
-        float *qc = qa + kOneThreads;
-        const int na = s_an;
-        if (tid < na) {
-          abv[tid] = pv;
-          qa[tid] = pqa;
-          nuc[tid] = ((u64)(0xFFFFFFFFu - (uint32_t)pv) << 32) | (uint32_t)tid;
-        }
-        if (tid < nc) qc[tid] = pqc;
-        if (tid == 0) s_nc2 = na;
-        __syncthreads();
-        {   // the candidates inside the cut (nc <= kOneThreads - na: one round)
-          const int c = tid;
-          const u64 v = c < nc ? lk[c] : 0ull;
-          const bool f =
-              c < nc && in_nucleus(rs0, key_to_float((uint32_t)(v >> 32)), (int)(uint32_t)v);
-          const int at = wave_append(f, &s_nc2);
-          if (f && at < kOneThreads)
-            nuc[at] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (uint32_t)(kOneThreads + c);
-        }
-        __syncthreads();
-        const int N = min(s_nc2, kOneThreads);
-        const u64 *srt = sort_desc(nuc, hx + 2 * kOneThreads, N);
-        const int pick = rej_nucleus_draw(
-            p, rs0, row, srt, N,
-            [&](int sl, float &zt, float &qt) {
-              const bool ab = sl < kOneThreads;
-              const u64 e0 = ab ? abv[sl] : lk[sl - kOneThreads];
-              zt = key_to_float((uint32_t)(e0 >> 32));
-              qt = draft_row ? (ab ? qa[sl] : qc[sl - kOneThreads]) : 0.0f;
-            },
-            red);
-        // the row's token, then the arrivals of all of its workgroups at once
+    } else {
+      // (2b) the range [blo, bhi] of approximate bins that holds the cut, found
+      // by the last workgroup of the row and published in a tagged word.  The
+      // fp64 sums carry a relative error below (C + G + 32) * 2^-53 (the
+      // longest chain of additions behind any of them: within a chunk, over
+      // the chunks, the prefix), and fixed point drops below V * 2^-100; E
+      // bounds both with room to spare.  No bin before blo reaches the
+      // threshold, bin bhi does (or bhi is the last occupied bin).
+      if (last2) {
         if (tid == 0) {
-          st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
-          __builtin_amdgcn_s_waitcnt(0);
-          s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
-          s_drew = 1;
+          const u64 *tr = p.total + 3 * row;
+          for (int w = 0; w < 3; ++w) s_w[w] = ld_ag(tr + w);
+          s_blo = kXBins;
+          s_bhi = kXBins;
+          s_last = -1;
+        }
+        const double v = ld_agd(p.ahist + (size_t)row * kXBins + tid);
+        const double cum = dscan_one(v, dred);    // (its barriers publish s_w)
+        const double Sd = fx_to_double(fx_from3(s_w[0], s_w[1], s_w[2]));
+        const double thr_d = fx_to_double(threshold(p, Sd));
+        const double E = (double)(C + G + 64) * 0x1p-51 * (Sd + 1.0) + (double)p.V * 0x1p-98;
+        {   // first thread of each condition, last occupied bin: one LDS atomic per wave
+          const u64 b0 = __ballot(cum >= thr_d - E), b1 = __ballot(cum >= thr_d + E);
+          const u64 b2 = __ballot(v > 0.0);
+          if (lane == 0) {
+            if (b0) atomicMin(&s_blo, wave * kWave + __ffsll((long long)b0) - 1);
+            if (b1) atomicMin(&s_bhi, wave * kWave + __ffsll((long long)b1) - 1);
+            if (b2) atomicMax(&s_last, wave * kWave + 63 - __clzll((long long)b2));
+          }
         }
         __syncthreads();
+        if (tid == 0) {
+          s_blo = min(s_blo, s_last);
+          s_bhi = min(s_bhi, s_last);
+          st_ag(rp + kRowBins,
+                ((u64)tag << 32) | ((u64)(s_blo + 1) << 16) | (u64)(s_bhi + 1));
+        }
+      } else if (tid == 0) {
+        const u64 w = wait_slot(rp + kRowBins, tag, err);
+        s_blo = (int)((w >> 16) & 0xFFFF) - 1;
+        s_bhi = (int)(w & 0xFFFF) - 1;
+      }
+      __syncthreads();
+      const int blo = s_blo, bhi = s_bhi;
+
+      // (3) the exact mass above the range (the chunk's bins before blo, one a
+      // thread), and the candidates in index order (entry k * kOneThreads + t
+      // is thread t's k-th)
+      // Entries above the range (in the nucleus whatever the cut) also go to
+      // the workspace when there are at most kAboveCap of them, so that a
+      // resolver whose nucleus is small can draw the row's token alone.
+      {
+        Fx ab = tid < blo ? fx_load3(hx + 3 * tid) : fx_zero();
+        u64 bal[kKPer], abl[kKPer];
+#pragma unroll
+        for (int k = 0; k < kKPer; ++k) {
+          const int i = k * kOneThreads + tid;
+          const int b = i < n ? (int)bc[i] : 0xFFFF;
+          bal[k] = __ballot(b >= blo && b <= bhi);
+          abl[k] = __ballot(b < blo);
+          if (lane == 0) {
+            koff[k * kOneWaves + wave] = __popcll(bal[k]);
+            koffa[k * kOneWaves + wave] = __popcll(abl[k]);
+          }
+        }
+        ab = fx_sum_one(ab, red);     // (its barriers also publish koff and koffa)
+        if (tid == 0 && fx_nonzero(ab)) fx_atomic_add3(p.above + 3 * row, ab);
+        if (wave < 2) {
+          int *ko = wave == 0 ? koff : koffa;
+          const int c0 = ko[2 * lane], c1 = ko[2 * lane + 1];
+          const int incl = dpp_incl(c0 + c1);
+          const int before = incl - c0 - c1;
+          ko[2 * lane] = before;
+          ko[2 * lane + 1] = before + c0;
+          if (lane == kWave - 1) ko[kKPer * kOneWaves] = incl;
+        }
+        __syncthreads();
+        u64 *seg = p.cand + (size_t)(row * G + g) * C;
+#pragma unroll
+        for (int k = 0; k < kKPer; ++k) {
+          if ((bal[k] >> lane) & 1ull) {
+            const int i = k * kOneThreads + tid;
+            const int pos = koff[k * kOneWaves + wave] + __popcll(bal[k] & ((1ull << lane) - 1ull));
+            st_ag(seg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
+          }
+        }
+        const int na = koffa[kKPer * kOneWaves];
+        if (na <= kAboveCap) {
+          u64 *aseg = p.asec + (size_t)(row * G + g) * kAboveCap;
+#pragma unroll
+          for (int k = 0; k < kKPer; ++k) {
+            if ((abl[k] >> lane) & 1ull) {
+              const int i = k * kOneThreads + tid;
+              const int pos = koffa[k * kOneWaves + wave] + __popcll(abl[k] & ((1ull << lane) - 1ull));
+              st_ag(aseg + pos, ((u64)fkey(zc[i]) << 32) | (uint32_t)(j0 + i));
+            }
+          }
+        }
+        if (tid == 0) {
+          st_agi(p.ccount + row * G + g, koff[kKPer * kOneWaves]);
+          st_agi(p.acount + row * G + g, na <= kAboveCap ? na : -1);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        s_flag = __hip_atomic_fetch_add(rp + kRowCand, 1ull, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (u64)(G - 1);
+      __syncthreads();
+
+      chunk_lost = s_flag;
+      if (s_flag) {
+        // (3b) the last workgroup of the row resolves the cut.  Independent
+        // loads first: segment sizes (wave 0), the row's sums (thread 64),
+        // the draft (thread 128).
+        if (wave == 0) {
+          // candidates, and entries above the range (-1: not handed over), a
+          // workgroup at a time
+          int c[4], ca[4], loc = 0, loca = 0;
+          bool over = false;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = 4 * lane + r;
+            c[r] = q < G ? ld_agi(p.ccount + row * G + q) : 0;
+            ca[r] = q < G ? ld_agi(p.acount + row * G + q) : 0;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            loc += c[r];
+            over = over || ca[r] < 0;
+            loca += max(ca[r], 0);
+          }
+          int incl = dpp_incl(loc), incla = dpp_incl(loca);
+          int o = incl - loc, oa = incla - loca;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            segoff[4 * lane + r] = o;
+            aoff[4 * lane + r] = oa;
+            o += c[r];
+            oa += max(ca[r], 0);
+          }
+          const bool any_over = __ballot(over) != 0ull;
+          if (lane == kWave - 1) {
+            s_nc = incl;
+            s_an = any_over ? -1 : incla;
+          }
+        } else if (tid == 64) {
+          const u64 *abr = p.above + 3 * row, *tr = p.total + 3 * row;
+          for (int w = 0; w < 3; ++w) {
+            s_w[w] = ld_ag(abr + w);
+            s_w[3 + w] = ld_ag(tr + w);
+          }
+        } else if (tid == 128 && row < p.M - 1) {
+          int x;
+          bool valid;
+          float zx, qx;
+          load_draft(p, row, x, valid, zx, qx);
+          s_x = valid ? x : -1;
+          s_zx = zx;
+          s_qx = qx;
+        }
+        __syncthreads();
+        const int nc = s_nc;
+        const Fx A = fx_from3(s_w[0], s_w[1], s_w[2]);
+        const double Sd = fx_to_double(fx_from3(s_w[3], s_w[4], s_w[5]));
+        const Fx thr = threshold(p, Sd);
+        const double thr_d = fx_to_double(thr);
+        auto seg_of = [&](int c) {   // the last segment starting at or before c
+          int lo = 0, hi = G - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (segoff[mid] <= c) lo = mid; else hi = mid - 1;
+          }
+          return lo;
+        };
+        auto cand_load = [&](int c) {
+          const int q = seg_of(c);
+          return ld_ag(p.cand + (size_t)(row * G + q) * C + (c - segoff[q]));
+        };
+        auto e_of_key = [&](u64 v) {   // e of a candidate, as step (2) computed it
+          return e_of(key_to_float((uint32_t)(v >> 32)), zmax, T);
+        };
+        // the candidates into LDS, over this workgroup's chunk (reloaded from
+        // the logits if this row draws); any beyond the room stay in the
+        // workspace and are loaded again where needed
+        const int room = one_cand_room(C), nl = min(nc, room);
+        u64 *lk = reinterpret_cast<u64 *>(dyn);
+        double *le = reinterpret_cast<double *>(dyn + (size_t)room * 8);
+        for (int base = 0; base < nl; base += kResPer * kOneThreads) {
+          int sq[kResPer];
+          u64 v[kResPer];
+#pragma unroll
+          for (int k = 0; k < kResPer; ++k) {
+            const int c = base + k * kOneThreads + tid;
+            sq[k] = c < nl ? seg_of(c) : 0;
+          }
+#pragma unroll
+          for (int k = 0; k < kResPer; ++k) {
+            const int c = base + k * kOneThreads + tid;
+            v[k] = c < nl ? ld_ag(p.cand + (size_t)(row * G + sq[k]) * C + (c - segoff[sq[k]]))
+                          : 0ull;
+          }
+#pragma unroll
+          for (int k = 0; k < kResPer; ++k) {
+            const int c = base + k * kOneThreads + tid;
+            if (c < nl) {
+              lk[c] = v[k];
+              le[c] = e_of_key(v[k]);
+            }
+          }
+        }
+        __syncthreads();
+        // What a small nucleus would draw from, fetched while the cut is
+        // resolved (none of it depends on the cut): with every workgroup's
+        // entries above the range handed over and room for them and all the
+        // candidates in one workgroup (pre), the entries above the range and,
+        // for a draft row, the draft's q at every candidate; held in registers
+        // until the draw (the q at the entries above follows in step 3e)
+        const bool pre = s_an >= 0 && s_an + nc <= kOneThreads;
+        const bool draft_row = row < p.M - 1;
+        u64 pv = 0ull;
+        float pqc = 0.0f;
+        if (pre) {
+          if (tid < s_an) {
+            int lo = 0, hi = G - 1;   // the last workgroup whose entries start at or before tid
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (aoff[mid] <= tid) lo = mid;
+              else hi = mid - 1;
+            }
+            pv = ld_ag(p.asec + (size_t)(row * G + lo) * kAboveCap + (tid - aoff[lo]));
+          }
+          if (draft_row && tid < nc) pqc = p.q[(int64_t)row * p.ldq + (int)(uint32_t)lk[tid]];
+        }
+        auto each = [&](auto &&f) {   // every candidate once
+          for (int c = tid; c < nl; c += kOneThreads) f(lk[c], le[c]);
+          for (int c = room + tid; c < nc; c += kOneThreads) {
+            const u64 v = cand_load(c);
+            f(v, e_of_key(v));
+          }
+        };
+        // (3c) one exact pass over fine bins of x: fb(z) = (t - blo) * 256 /
+        // (bhi - blo + 1) with t = -x * kXScale (x as step (2) computes it) is a
+        // monotone function of z like the bins themselves, so the selection
+        // over fine bins is exact, and it spreads the candidates evenly (few
+        // LDS atomics collide).  Digit 255 - fb puts larger logits in higher
+        // bins, as select_bin_wave expects.
+        const double S2 = 256.0 / (double)(bhi - blo + 1);
+        auto fbin = [&](u64 v) {
+          const double x = ((double)key_to_float((uint32_t)(v >> 32)) - (double)zmax) / T;
+          const int b = (int)((-x * kXScale - (double)blo) * S2);
+          return 255 - (b < 0 ? 0 : (b > 255 ? 255 : b));
+        };
+        // (few candidates skip it: they are all sorted directly)
+        const bool few = nc <= kWave;
+        if (!few) {
+          for (int i = tid; i < kBins * 3; i += kOneThreads) sh[i] = 0ull;
+          __syncthreads();
+          each([&](u64 v, double e) { hist_add(sh, fbin(v), to_fx(e)); });
+          __syncthreads();
+          if (wave == 0) {
+            Fx a2 = A;
+            int bin = select_bin_wave(sh, thr, a2);
+            if (bin < 0) bin = 0;
+            if (lane == 0) {
+              s_prefix = (uint32_t)bin;
+              s_abv_lo = a2.lo;
+              s_abv_hi = a2.hi;
+              s_nk = sh[3 * bin + 2];
+              s_nc = 0;
+            }
+          }
+          __syncthreads();
+        }
+        const int fsel = few ? 0 : (int)s_prefix, n2 = few ? nc : (int)s_nk;
+        Fx above = few ? A : Fx{s_abv_lo, s_abv_hi};
+        uint32_t kappa = 0u;
+        u64 nk = 0ull;
+        int cut_pos = -1;   // where the cut group starts among the sorted entries
+        // the fine bin's entries, gathered and sorted by (key descending, index
+        // ascending) in the LDS of the step (2) bin masses, when they fit
+        u64 *gk = hx, *sk = gk + kSortMax;   // (hx is free once step 3 has read it)
+        double *ge = reinterpret_cast<double *>(hx + 2 * kSortMax), *se2 = ge + kSortMax;
+        const bool small = n2 <= kSortMax;
+        // one wave sorts up to kWave entries (from the candidates themselves
+        // when they are few, else from the gathered fine bin) and finds the cut
+        // group in them with wave-level scans
+        auto wave_cut = [&](const u64 *srck, const double *srce) {
+          if (wave == 0) {
+            auto skey = [](u64 v) {
+              return (v & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (v & 0xFFFFFFFFull));
+            };
+            const bool valid = lane < n2;
+            const u64 v0 = valid ? srck[lane] : 0ull;
+            const double e0 = valid ? srce[lane] : 0.0;
+            const u64 mine = skey(v0);
+            int rank = 0;
+            for (int j = 0; j < n2; ++j) rank += skey(srck[j]) > mine;
+            if (valid) {
+              sk[rank] = v0;
+              se2[rank] = e0;
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+            const u64 v = valid ? sk[lane] : 0ull;
+            const Fx f = valid ? to_fx(se2[lane]) : fx_zero();
+            Fx incl = dpp_fx_incl(f);
+            const Fx excl = fx_sum(above, fx_sub(incl, f));
+            const uint32_t key = (uint32_t)(v >> 32);
+            const bool gend = valid && (lane == n2 - 1 || (uint32_t)(sk[lane + 1] >> 32) != key);
+            const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
+            const int gl = hit ? __ffsll((long long)hit) - 1 : n2 - 1;
+            const uint32_t kap = (uint32_t)__builtin_amdgcn_readlane((int)key, gl);
+            const u64 first = __ballot(valid && key == kap);
+            const int gs = __ffsll((long long)first) - 1;
+            const Fx ab = fx_readlane(excl, gs);
+            if (lane == 0) {
+              s_prefix = kap;
+              s_abv_lo = ab.lo;
+              s_abv_hi = ab.hi;
+              s_nk = (u64)(gl - gs + 1);
+              s_cut = gs;
+            }
+          }
+          __syncthreads();
+          kappa = s_prefix;
+          above = Fx{s_abv_lo, s_abv_hi};
+          nk = s_nk;
+          cut_pos = s_cut;
+        };
+        if (nc > 0 && few) {
+          wave_cut(lk, le);
+        } else if (nc > 0 && small) {
+          each([&](u64 v, double e) {
+            if (fbin(v) == fsel) {
+              const int pos = atomicAdd(&s_nc, 1);
+              gk[pos] = v;
+              ge[pos] = e;
+            }
+          });
+          __syncthreads();
+          if (n2 <= kWave) {
+            wave_cut(gk, ge);
+          } else {
+          // rank = entries before this one in the order; the sort key
+          // (key << 32 | ~index) is distinct and descends in that order
+          auto skey = [](u64 v) {
+            return (v & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFull - (v & 0xFFFFFFFFull));
+          };
+          if (tid < n2) {
+            const u64 mine = skey(gk[tid]);
+            int rank = 0;
+            for (int j = 0; j < n2; ++j) rank += skey(gk[j]) > mine;
+            sk[rank] = gk[tid];
+            se2[rank] = ge[tid];
+          }
+          __syncthreads();
+          // exclusive prefix in the order; the cut is the first key whose group
+          // reaches the threshold (else the last group)
+          const u64 v = tid < n2 ? sk[tid] : 0ull;
+          const Fx f = tid < n2 ? to_fx(se2[tid]) : fx_zero();
+          Fx tot_unused;
+          const Fx excl = fx_sum(above, fx_excl_one(f, red, tot_unused));
+          const uint32_t key = (uint32_t)(v >> 32);
+          const bool gend = tid < n2 && (tid == n2 - 1 || (uint32_t)(sk[tid + 1] >> 32) != key);
+          if (tid == 0) {
+            s_blk = 0x7FFFFFFF;
+            s_lastnz = 0x7FFFFFFF;
+          }
+          __syncthreads();
+          {
+            const u64 hit = __ballot(gend && fx_ge(fx_sum(excl, f), thr));
+            if (lane == 0 && hit) atomicMin(&s_blk, wave * kWave + __ffsll((long long)hit) - 1);
+          }
+          __syncthreads();
+          const int gl = s_blk != 0x7FFFFFFF ? s_blk : n2 - 1;   // the cut group's last entry
+          kappa = (uint32_t)(sk[gl] >> 32);
+          {
+            const u64 first = __ballot(tid < n2 && key == kappa);
+            if (lane == 0 && first)
+              atomicMin(&s_lastnz, wave * kWave + __ffsll((long long)first) - 1);
+          }
+          __syncthreads();
+          const int gs = s_lastnz;   // the cut group's first entry
+          if (tid == gs) {
+            s_abv_lo = excl.lo;
+            s_abv_hi = excl.hi;
+          }
+          __syncthreads();
+          above = Fx{s_abv_lo, s_abv_hi};
+          nk = (u64)(gl - gs + 1);
+          cut_pos = gs;
+          }
+        } else if (nc > 0) {
+          // a large fine bin (many equal or nearly equal logits): radix passes
+          // over the keys of its entries
+          uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+          each([&](u64 v, double) {
+            if (fbin(v) != fsel) return;
+            const uint32_t k = (uint32_t)(v >> 32);
+            kmn = min(kmn, k);
+            kmx = max(kmx, k);
+          });
+          for (int s2 = kWave / 2; s2 > 0; s2 >>= 1) {
+            kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, s2));
+            kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, s2));
+          }
+          if (tid == 0) {
+            s_kmin = 0xFFFFFFFFu;
+            s_kmax = 0u;
+          }
+          __syncthreads();
+          if (lane == 0) {
+            atomicMin(&s_kmin, kmn);
+            atomicMax(&s_kmax, kmx);
+          }
+          __syncthreads();
+          kmn = s_kmin;
+          kmx = s_kmax;
+          int lo_bit = kmn == kmx ? 0 : 32 - __clz((int)(kmn ^ kmx));
+          uint32_t prefix = lo_bit == 32 ? 0u : (kmn >> lo_bit);
+          nk = (u64)n2;
+          while (lo_bit > 0) {
+            const int db = min(8, lo_bit), shift = lo_bit - db;
+            for (int i = tid; i < kBins * 3; i += kOneThreads) sh[i] = 0ull;
+            __syncthreads();
+            each([&](u64 v, double e) {
+              const uint32_t k = (uint32_t)(v >> 32);
+              if (fbin(v) != fsel || (lo_bit < 32 && (k >> lo_bit) != prefix)) return;
+              hist_add(sh, (int)((k >> shift) & ((1u << db) - 1u)), to_fx(e));
+            });
+            __syncthreads();
+            if (wave == 0) {
+              Fx a2 = above;
+              int bin = select_bin_wave(sh, thr, a2);
+              if (bin < 0) bin = 0;
+              if (lane == 0) {
+                s_prefix = (prefix << db) | (uint32_t)bin;
+                s_abv_lo = a2.lo;
+                s_abv_hi = a2.hi;
+                s_nk = sh[3 * bin + 2];
+              }
+            }
+            __syncthreads();
+            prefix = s_prefix;
+            above = Fx{s_abv_lo, s_abv_hi};
+            nk = s_nk;
+            lo_bit = shift;
+            __syncthreads();
+          }
+          kappa = prefix;
+        }
+        const double ek = e_of(key_to_float(kappa), zmax, T);
+        const double above_d = fx_to_double(above);
+        const double tt = ceil((thr_d - above_d) / ek);
+        const u64 t = (tt < 1.0) ? 1ull : (tt >= (double)nk ? nk : (u64)tt);
+        int cutoff = p.V;
+        if (t < nk && cut_pos >= 0) {
+          // the group is sorted by index: its t-th entry is the last inside
+          cutoff = (int)(uint32_t)sk[cut_pos + (int)t - 1];
+        } else if (t < nk) {
+          // ties at the cut: the first t in index order (the candidates' order)
+          // are inside
+          if (tid == 0) s_cut = p.V;
+          int seen = 0;
+          auto round = [&](bool valid, u64 v) {
+            const bool f = valid && (uint32_t)(v >> 32) == kappa;
+            int pre;
+            const int tot_r = count_one(f, pre, wcnt);
+            if (f && (u64)(seen + pre + 1) == t) s_cut = (int)(uint32_t)v;
+            seen += tot_r;
+            return (u64)seen >= t;
+          };
+          bool done = false;
+          for (int base = 0; !done && base < nc; base += kOneThreads) {
+            const int c = base + tid;
+            done = round(c < nc, c < nl ? lk[c] : (c < nc ? cand_load(c) : 0ull));
+          }
+          __syncthreads();
+          cutoff = s_cut;
+        }
+        // (3e) a small nucleus (pre: at most kOneThreads entries in the
+        // nucleus, all of them at hand): this workgroup draws the row's token
+        // itself (the draw row a would make, as the picker below does it) and
+        // the row's other workgroups leave as soon as they see the state
+        const RowState rs0 = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
+        const bool tiny = pre;
+        float pqa = 0.0f;
+        if (tiny && draft_row && tid < s_an) pqa = p.q[(int64_t)row * p.ldq + (int)(uint32_t)pv];
+        if (tid == 0) {
+          RowState rs = rs0;
+          if (tiny) rs.all = 2;
+          if (row < p.M - 1) publish_acc(p, row, rs0, s_x, s_x >= 0, s_zx, s_qx);
+          __builtin_amdgcn_s_waitcnt(0);   // the acceptance input before the state
+          publish_state(rp, tag, rs);
+        }
+        if (tiny) {
+          // the nucleus in index order: entries keyed (~index << 32 | slot),
+          // slot i < kOneThreads the i-th entry above the range, kOneThreads + c
+          // candidate c
+          u64 *nuc = hx;   // (free: the fine-bin sort is done)
+          u64 *abv = reinterpret_cast<u64 *>(dyn + 16384);   // (the candidates use
+          float *qa = reinterpret_cast<float *>(dyn + 8192);  // at most 8 KiB of lk)
+          float *qc = qa + kOneThreads;
+          const int na = s_an;
+          if (tid < na) {
+            abv[tid] = pv;
+            qa[tid] = pqa;
+            nuc[tid] = ((u64)(0xFFFFFFFFu - (uint32_t)pv) << 32) | (uint32_t)tid;
+          }
+          if (tid < nc) qc[tid] = pqc;
+          if (tid == 0) s_nc2 = na;
+          __syncthreads();
+          {   // the candidates inside the cut (nc <= kOneThreads - na: one round)
+            const int c = tid;
+            const u64 v = c < nc ? lk[c] : 0ull;
+            const bool f =
+                c < nc && in_nucleus(rs0, key_to_float((uint32_t)(v >> 32)), (int)(uint32_t)v);
+            const int at = wave_append(f, &s_nc2);
+            if (f && at < kOneThreads)
+              nuc[at] = ((u64)(0xFFFFFFFFu - (uint32_t)v) << 32) | (uint32_t)(kOneThreads + c);
+          }
+          __syncthreads();
+          const int N = min(s_nc2, kOneThreads);
+          const u64 *srt = sort_desc(nuc, hx + 2 * kOneThreads, N);
+          const int pick = rej_nucleus_draw(
+              p, rs0, row, srt, N,
+              [&](int sl, float &zt, float &qt) {
+                const bool ab = sl < kOneThreads;
+                const u64 e0 = ab ? abv[sl] : lk[sl - kOneThreads];
+                zt = key_to_float((uint32_t)(e0 >> 32));
+                qt = draft_row ? (ab ? qa[sl] : qc[sl - kOneThreads]) : 0.0f;
+              },
+              red);
+          // the row's token, then the arrivals of all of its workgroups at once
+          if (tid == 0) {
+            st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
+            __builtin_amdgcn_s_waitcnt(0);
+            s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
+            s_drew = 1;
+          }
+          __syncthreads();
+        }
       }
     }
   }

@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 7
+#define MTP_ABI_VERSION 8
 
 enum {
   MTP_OK = 0,
@@ -220,7 +220,7 @@ size_t mtp_moe_workspace_bytes(int T, int H, int F, int E, int topk);
  *   logits, ldl      fp32 [M][ldl], 1 <= M <= 64, 1 <= V <= ldl
  *   draft_ids        int32 [M-1] (may be NULL when M == 1)
  *   ws, ws_bytes     at least mtp_accept_workspace_bytes(M, V), zero-filled
- *                    before its first use.  Its first 260 KiB hold counters
+ *                    before its first use.  Its first 282 KiB hold counters
  *                    and tags that mtp_accept_rejection leaves ready for the
  *                    next call (of either kind and any shape that fits);
  *                    nothing else is kept between calls.  Calls that share

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bv.abi_version() == 7
+    assert bv.abi_version() == 8
 
 
 def test_packed_sizes():

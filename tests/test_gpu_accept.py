@@ -364,3 +364,59 @@ def test_rejection_back_to_back_calls_on_one_workspace():
     o2 = oracle.accept_rejection(z2, q, d, u, 0.6, 0.95, 1)
     t, c, r = bv.accept_rejection(dev(z2), qt, dt, ut, 0.6, 0.95, 1, ws=ws)
     check_same((host(t), host(c), int(host(r)[0])), o2, "other inputs")
+
+
+SETTLE_CASES = [
+    # name, M, V: rows whose cut the workgroups' top entries may settle
+    ("threshold on a prefix (the bracket straddles it: steps 2 and 3 decide)", 4, 262144),
+    ("ties in the cut group (t below the group size)", 4, 262144),
+    ("five maxima in one chunk (the top set is not complete)", 4, 262144),
+    ("more top entries than a wave holds", 4, 262144),
+    ("u below the fixed-point resolution", 8, 262144),
+    ("a short last chunk", 5, 70001),
+    ("one row over 256 workgroups", 1, 262144),
+]
+
+
+@pytest.mark.parametrize("name,M,V", SETTLE_CASES)
+def test_rejection_settled_by_top_entries(name, M, V):
+    rng = np.random.default_rng(sum(map(ord, name)))
+    log("settle:", name)
+    T = 0.6
+    for trial in range(3):
+        z = (rng.standard_normal((M, V)) * 300.0).astype(np.float32)
+        zt = z.max(axis=1)
+        top_p = 0.95
+        u = W.rand_uniforms(rng, M)
+        if name.startswith("threshold"):
+            # two entries at the top: S = 1 + e1 (+ far less), and top_p puts
+            # the threshold on the first prefix, just below or above it
+            e1 = 0.25 + 0.1 * trial
+            for i in range(M):
+                j = int(rng.integers(0, V))
+                z[i, j] = zt[i] + np.float32(T * np.log(e1))
+            S = 1.0 + 0.25 + 0.1 * trial
+            top_p = (1.0 / S) * (1.0 + (-1e-7, 0.0, 1e-7)[trial])
+        elif name.startswith("ties"):
+            for i in range(M):
+                z[i, rng.choice(V, 3, replace=False)] = zt[i] + np.float32(1.0)
+            top_p = (0.5, 0.34, 0.9)[trial]
+        elif name.startswith("five"):
+            for i in range(M):
+                z[i, 100 + 512 * np.arange(5)] = zt[i] + np.float32(1.0)   # (chunks of 4096)
+        elif name.startswith("more"):
+            # 4 distinct near-top entries in each of the 64 chunks of 4096
+            for i in range(M):
+                for c in range(64):
+                    z[i, c * 4096 + 7 * np.arange(4)] = zt[i] - np.float32(0.01) * (4 * c + np.arange(4))
+            top_p = 0.9
+        elif name.startswith("u below"):
+            u[M - 1] = np.float32((1e-33, 1e-40, 3e-31)[trial])
+            if trial == 1:
+                u[:M - 1] = 0.999                                # residual path
+        q = W.rand_dirichlet_rows(rng, max(M - 1, 1), V, 0.1)[:M - 1]
+        d = np.array([oracle.argmax(z[i]) for i in range(M - 1)], np.int32)
+        if M > 2:
+            d[M // 2] = int(rng.integers(0, V))
+        o = oracle.accept_rejection(z, q, d, u, T, top_p, 4, with_margins=True)
+        check_same(gpu_rej(z, q, d, u, T, top_p, 4), o[:3], f"{name} trial={trial}", o[3])
