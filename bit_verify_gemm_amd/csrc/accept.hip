@@ -1918,9 +1918,10 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
 
   // (2) e of every entry (kept in LDS), the row's exact mass and, with
   // top_p < 1, the chunk's exact mass per bin of x (kept for step 3) and the
-  // row's approximate histogram; meanwhile the row's exchange words are
-  // loaded (into sh, or past the chunk when they do not fit there; with no
-  // room for them the row is never settled), then judged (2a)
+  // row's approximate histogram.  With top_p < 1 and room for the row's
+  // exchange words (in sh, or past the chunk when they do not fit there),
+  // wave 0 takes no exponentials: it loads those words and judges them (2a)
+  // meanwhile, and the other waves stop early when the cut is settled.
   if (nucleus)
     for (int i = tid; i < 3 * kXBins; i += kOneThreads) hx[i] = 0ull;
   uint32_t *const xw =
@@ -1929,26 +1930,76 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       : ((one_lds_bytes(C) + 15) & ~15) + G * kXW * 4 <= one_dyn_bytes(C)
           ? reinterpret_cast<uint32_t *>(dyn + ((one_lds_bytes(C) + 15) & ~15))
           : nullptr;
-  constexpr int kWR = (kMaxOneBlocks * kXW + kOneThreads - 1) / kOneThreads;
-  u64 xv[kWR];
-#pragma unroll
-  for (int r = 0; r < kWR; ++r) {
-    const int i = tid + r * kOneThreads;
-    xv[r] = xw && i < G * kXW ? ld_ag(xg + i) : 0ull;
-  }
-  const bool draw = xw && g == 0 && wave == 0, draft_row = row < p.M - 1;
-  double u_last = 0.0;
-  int dx = -1;
-  bool dvalid = false;
-  float dzx = 0.0f, dqx = 0.0f;
-  if (draw) {   // what workgroup 0 of a settled row needs last, loaded first
-    u_last = (double)p.u[p.M - 1];
-    if (draft_row) load_draft(p, row, dx, dvalid, dzx, dqx);
-  }
+  const bool solo = xw != nullptr;
+  volatile int *const fast_flag = &s_fast;
   __syncthreads();
-  {
-    Fx tot = fx_zero();
-    for (int i = tid; i < n; i += kOneThreads) {
+  Fx tot = fx_zero();
+  if (solo && wave == 0) {
+    // (2a) do the top entries settle the cut?  Every workgroup of the row
+    // judges the same words alike; if so, workgroup 0 draws the row's token,
+    // publishes it with the row's state and arrives for the whole row, and
+    // the others leave
+    const bool draw = g == 0, draft_row = row < p.M - 1;
+    double u_last = 0.0;
+    int dx = -1;
+    bool dvalid = false;
+    float dzx = 0.0f, dqx = 0.0f;
+    if (draw) {   // (loaded first, used last)
+      u_last = (double)p.u[p.M - 1];
+      if (draft_row) load_draft(p, row, dx, dvalid, dzx, dqx);
+    }
+    constexpr int kWB = 8;   // loads in flight a lane
+    for (int i0 = 0; i0 < G * kXW; i0 += kWB * kWave) {
+      u64 w[kWB];
+#pragma unroll
+      for (int r = 0; r < kWB; ++r) {
+        const int i = i0 + r * kWave + lane;
+        w[r] = i < G * kXW ? ld_ag(xg + i) : 0ull;
+      }
+#pragma unroll
+      for (int r = 0; r < kWB; ++r) {
+        const int i = i0 + r * kWave + lane;
+        if (i < G * kXW) {
+          u64 v = w[r];
+          if ((uint32_t)(v >> 32) != tag) v = wait_slot(xg + i, tag, err);
+          xw[i] = (uint32_t)v;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float zm;
+    RowState rs0;
+    u64 ent = 0ull;
+    double ee = 0.0;
+    float qe = 0.0f;
+    int nn = 0;
+    const bool settled =
+        rej_top_settle(p, row, G, xw, s_lst, draw && draft_row, zm, rs0, ent, ee, qe, nn);
+    if (settled && draw) {
+      bool use_res = false;
+      const int pick = wave_nucleus_draw(p, rs0, row, ent, ee, qe, nn, u_last, use_res);
+      if (lane == 0) {
+        if (draft_row) publish_acc(p, row, rs0, dx, dvalid, dzx, dqx);
+        __builtin_memcpy(s_w, &rs0, sizeof(rs0));
+        s_fr = use_res ? 1 : 0;
+        s_pick = pick;
+        if (pick != -2) {   // (else the fp64 sequence below, by the whole workgroup)
+          RowState rs = rs0;
+          rs.all = 2;
+          publish_state(rp, tag, rs);
+          st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
+          __builtin_amdgcn_s_waitcnt(0);   // acceptance input, state and token before the count
+          s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
+          s_drew = 1;
+        }
+      }
+    }
+    if (lane == 0 && settled) *fast_flag = 1;
+  } else {
+    const int t0 = solo ? tid - kWave : tid, nth = solo ? kOneThreads - kWave : kOneThreads;
+    for (int i = t0; i < n; i += nth) {
+      if (solo && *fast_flag) break;   // (the row is settled: these sums go unused)
       const double x = ((double)zc[i] - (double)zmax) / T;
       const double e = x < -70.5 ? 0.0 : exp(x);     // as e_or_zero
       ec[i] = e;
@@ -1966,65 +2017,31 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       }
       bc[i] = b;
     }
-#pragma unroll
-    for (int r = 0; r < kWR; ++r) {
-      const int i = tid + r * kOneThreads;
-      if (xw && i < G * kXW) {
-        u64 w = xv[r];
-        if ((uint32_t)(w >> 32) != tag) w = wait_slot(xg + i, tag, err);
-        xw[i] = (uint32_t)w;
-      }
-    }
-    tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram and xw)
-    if (tid == 0 && fx_nonzero(tot)) fx_atomic_add3(p.total + 3 * row, tot);
-    if (nucleus) {
-      const Fx m = fx_load3(hx + 3 * tid);
-      if (fx_nonzero(m)) unsafeAtomicAdd(p.ahist + (size_t)row * kXBins + tid, fx_to_double(m));
-    }
   }
-  if (xw) {
-    // (2a) do the top entries settle the cut?  Every workgroup of the row
-    // judges the same words alike; if so, workgroup 0 draws the row's token
-    // and arrives for all, and the others leave
-    if (wave == 0) {
-      float zm;
-      RowState rs0;
-      u64 ent = 0ull;
-      double ee = 0.0;
-      float qe = 0.0f;
-      int nn = 0;
-      const bool settled =
-          rej_top_settle(p, row, G, xw, s_lst, draw && draft_row, zm, rs0, ent, ee, qe, nn);
-      if (settled && draw) {
-        bool use_res = false;
-        const int pick = wave_nucleus_draw(p, rs0, row, ent, ee, qe, nn, u_last, use_res);
-        if (lane == 0) {
-          __builtin_memcpy(s_w, &rs0, sizeof(rs0));
-          s_pick = pick;
-          s_fr = use_res ? 1 : 0;
-          if (draft_row) publish_acc(p, row, rs0, dx, dvalid, dzx, dqx);
-        }
-      }
-      if (lane == 0) s_fast = settled ? 1 : 0;
-    }
-    __syncthreads();
-    if (s_fast) {
-      if (g != 0) return;
+  tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram and publish 2a)
+  if (s_fast) {   // (uniform)
+    if (g != 0) return;
+    if (!s_drew) {   // the token below the fixed-point resolution with u > 0
       const RowState rs0 = row_state_of(s_w);
-      int pick = s_pick;
-      if (pick == -2)   // below the fixed-point resolution with u > 0
-        pick = draw_f64_sequential<kOneThreads>(p, rs0, row, s_fr != 0, (double)p.u[p.M - 1]);
+      const int pick =
+          draw_f64_sequential<kOneThreads>(p, rs0, row, s_fr != 0, (double)p.u[p.M - 1]);
       if (tid == 0) {
         RowState rs = rs0;
         rs.all = 2;
         publish_state(rp, tag, rs);
         st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
-        __builtin_amdgcn_s_waitcnt(0);   // acceptance input, state and token before the count
+        __builtin_amdgcn_s_waitcnt(0);
         s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
         s_drew = 1;
       }
       __syncthreads();
+    }
+  } else {
+    if (tid == 0 && fx_nonzero(tot)) fx_atomic_add3(p.total + 3 * row, tot);
+    if (nucleus) {
+      const Fx m = fx_load3(hx + 3 * tid);
+      if (fx_nonzero(m)) unsafeAtomicAdd(p.ahist + (size_t)row * kXBins + tid, fx_to_double(m));
     }
   }
   if (!s_drew) {   // (uniform: a row drawn in step 2a goes to step 5)
