@@ -362,6 +362,7 @@ constexpr int kAboveCap = 256;
 // (kTopK + 1)-th largest entry and its kTopK largest entries (key, index).
 constexpr int kTopK = 2;
 constexpr int kXW = 3 + 2 * kTopK;
+static_assert(kTopK >= 2, "word 5 holds a workgroup's second key");
 constexpr int kXchg = (kMaxRows + 1) * kPageWords;
 constexpr int kHdrWords = kXchg + kMaxOneBlocks * kXW;
 static_assert(kRowSlots + kMaxOneBlocks <= kPageWords, "slots fit the row page");
@@ -1634,7 +1635,35 @@ __device__ __forceinline__ bool rej_top_settle(const RejArgs &p, int row, int G,
   const double slo = fmax(0.0, sa * (1.0 - 0x1p-9) - (double)p.V * 0x1p-98);
   const double shi = sa * (1.0 + 0x1p-9) + (double)p.V * 0x1p-98;
   const Fx thl = threshold(p, slo), thh = threshold(p, shi);
-  if (fx_gt(thl, to_fx((double)(G * kTopK)))) return false;   // (every e is at most 1)
+  auto fx_int = [](int k) { return Fx{0ull, (u64)k << 36}; };   // k in fixed point (1 = 2^100)
+  if (fx_gt(thl, fx_int(G * kTopK))) return false;   // (every e is at most 1)
+  {
+    // the common case first: the row maximum alone reaches the upper
+    // threshold (its e is exactly 1) and no other entry ties with it (it is
+    // the only handed-over entry with its key, and every workgroup's second
+    // key lies below it); then the nucleus is that entry, as the general
+    // steps below would find
+    uint32_t k2 = 0u;
+    for (int b = lane; b < G; b += kWave) k2 = max(k2, xw[b * kXW + 5]);
+    k2 = dpp_umax(k2);
+    int at = -1, cnt = 0;
+    for (int c0 = 0; c0 < G * kTopK; c0 += kWave) {
+      const int c = c0 + lane, b = c / kTopK, i = c - b * kTopK;
+      const bool f = c < G * kTopK && xw[b * kXW + 3 + 2 * i] == best;
+      const u64 bal = __ballot(f);
+      if (bal && at < 0) at = __builtin_amdgcn_readlane(c < G * kTopK ? (int)xw[b * kXW + 4 + 2 * i] : 0,
+                                                        __ffsll((long long)bal) - 1);
+      cnt += __popcll(bal);
+    }
+    if (k2 < best && cnt == 1 && !fx_gt(thh, fx_int(1)) && (uint32_t)at < (uint32_t)p.V) {
+      rs = RowState{zmax, best, p.V, 0, 1.0};
+      n = 1;
+      ent = ((u64)best << 32) | (uint32_t)at;
+      ee = 1.0;
+      qe = want_q && lane == 0 ? p.q[(int64_t)row * p.ldq + at] : 0.0f;
+      return true;
+    }
+  }
 #pragma unroll 1
   for (int r = 1; r <= kTopK; ++r) {
     const int wk = r == kTopK ? 2 : 3 + 2 * r;
@@ -1658,7 +1687,7 @@ __device__ __forceinline__ bool rej_top_settle(const RejArgs &p, int row, int G,
       nt += __popcll(bal);
     }
     if (nt > kWave) return false;
-    if (nt == 0 || fx_gt(thl, to_fx((double)nt))) continue;   // (every e is at most 1)
+    if (nt == 0 || fx_gt(thl, fx_int(nt))) continue;   // (every e is at most 1)
     __builtin_amdgcn_wave_barrier();
     const bool val = lane < nt;
     const u64 te = val ? lst[lane] : 0ull;
@@ -1695,8 +1724,8 @@ __device__ __forceinline__ bool rej_top_settle(const RejArgs &p, int row, int G,
       const double tt = ceil((fx_to_double(th) - above_d) / ek);
       return tt < 1.0 ? 1 : (tt >= (double)nk ? nk : (int)tt);
     };
-    const int t = ties_in(thl);
-    if (t != ties_in(thh)) return false;
+    const int t = nk == 1 ? 1 : ties_in(thl);
+    if (nk > 1 && t != ties_in(thh)) return false;
     const int cutoff = t < nk ? __builtin_amdgcn_readlane((int)sidx, gs + t - 1) : p.V;
     rs = RowState{zmax, kappa, cutoff, 0, above_d + (double)t * ek};
     n = gs + t;
@@ -1718,14 +1747,19 @@ __device__ __forceinline__ int wave_nucleus_draw(const RejArgs &p, const RowStat
   const int lane = threadIdx.x & (kWave - 1);
   const bool residual = row < p.M - 1, val = lane < n;
   const int j = val ? (int)(uint32_t)ent : kNone;
-  int rank = val ? 0 : lane;   // index order
-  for (int k = 0; k < n; ++k) rank += (val && __builtin_amdgcn_readlane(j, k) < j) ? 1 : 0;
-  const int jt = (int)lane_push(rank, (uint32_t)j);
-  const float zt = key_to_float(lane_push(rank, (uint32_t)(ent >> 32)));
-  const float qt = __uint_as_float(lane_push(rank, __float_as_uint(qe)));
-  const u64 eb = (u64)__double_as_longlong(ee);
-  const double et = __longlong_as_double(
-      (long long)(((u64)lane_push(rank, (uint32_t)(eb >> 32)) << 32) | lane_push(rank, (uint32_t)eb)));
+  int jt = j;
+  float zt = key_to_float((uint32_t)(ent >> 32)), qt = qe;
+  double et = ee;
+  if (n > 1) {   // index order
+    int rank = val ? 0 : lane;
+    for (int k = 0; k < n; ++k) rank += (val && __builtin_amdgcn_readlane(j, k) < j) ? 1 : 0;
+    jt = (int)lane_push(rank, (uint32_t)j);
+    zt = key_to_float(lane_push(rank, (uint32_t)(ent >> 32)));
+    qt = __uint_as_float(lane_push(rank, __float_as_uint(qe)));
+    const u64 eb = (u64)__double_as_longlong(ee);
+    et = __longlong_as_double((long long)(((u64)lane_push(rank, (uint32_t)(eb >> 32)) << 32) |
+                                          lane_push(rank, (uint32_t)eb)));
+  }
   Fx wr = fx_zero(), we = fx_zero();
   bool pr = false, pe = false;
   if (val) draw_weights_v(rs, p.T, residual, jt, zt, (double)qt, true, et, wr, we, pr, pe);
@@ -1745,6 +1779,61 @@ __device__ __forceinline__ int wave_nucleus_draw(const RejArgs &p, const RowStat
   if (hit) return __builtin_amdgcn_readlane(jt, __ffsll((long long)hit) - 1);
   const int lw = wave_max(val && fx_nonzero(w) ? jt : -1);
   return lw >= 0 ? lw : p.V - 1;
+}
+
+// Step 5 of rej_one by one wave (of the last workgroup to arrive) when the
+// accepted run ends at a row that drew its own token: every row's acceptance
+// input, state word `all` and token word are loaded at once, then the run a
+// (the first rejected draft, else M - 1) and row a's token give the outputs,
+// and the counters are reset for the next call.  Returns false, writing
+// nothing, when row a's token is left to the workgroup's draw.
+__device__ __forceinline__ bool rej_pick_drawn(const RejArgs &p, uint32_t tag, u64 gen, u64 *err) {
+  const int lane = threadIdx.x & (kWave - 1), M = p.M;
+  u64 ax = 0ull, aq = 0ull, ws = 0ull, wp = 0ull;
+  float ul = 0.0f;
+  if (lane < M - 1) {
+    const u64 *o = reinterpret_cast<const u64 *>(p.acc + lane);
+    ax = ld_ag(o);
+    aq = ld_ag(o + 1);
+    ul = p.u[lane];
+  }
+  if (lane < M) {
+    const u64 *r = p.hdr + (size_t)lane * kPageWords;
+    ws = ld_ag(r + kRowState + 2);
+    wp = ld_ag(r + kRowPick);
+  }
+  const double px = __longlong_as_double((long long)ax), qx = __longlong_as_double((long long)aq);
+  const u64 rej = __ballot(lane < M - 1 && !((double)ul * qx < px));
+  const int a = rej ? __ffsll((long long)rej) - 1 : M - 1;
+  auto lane_u64 = [&](u64 v) {
+    return ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), a) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, a);
+  };
+  u64 wsa = lane_u64(ws);
+  if ((uint32_t)(wsa >> 32) != tag) wsa = wait_slot(p.hdr + (size_t)a * kPageWords + kRowState + 2, tag, err);
+  if (!((uint32_t)wsa & 2u)) return false;
+  u64 wpa = lane_u64(wp);
+  if ((uint32_t)(wpa >> 32) != tag) wpa = wait_slot(p.hdr + (size_t)a * kPageWords + kRowPick, tag, err);
+  const int pick = (int)(uint32_t)wpa;
+  if (lane < M) p.tokens[lane] = lane < a ? p.drafts[lane] : (lane == a ? pick : -1);
+  if (lane == 0) {
+    p.counts[0] = a;
+    p.counts[1] = a + 1;
+    *p.rollback = p.base_len + a + 1;
+  }
+  // every other workgroup is done with the counters: reset them, advance the generation
+  if (lane < M) {
+    u64 *r = p.hdr + (size_t)lane * kPageWords;
+    st_ag(r + kRowCnt, 0ull);
+    st_ag(r + kRowCand, 0ull);
+    st_ag(r + kRowDraw, 0ull);
+  }
+  if (lane == 0) {
+    u64 *cp = p.hdr + (size_t)kMaxRows * kPageWords;
+    st_ag(cp + kCallRows, 0ull);
+    st_ag(cp + kCallGen, gen);
+  }
+  return true;
 }
 
 __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
@@ -1938,7 +2027,9 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     // (2a) do the top entries settle the cut?  Every workgroup of the row
     // judges the same words alike; if so, workgroup 0 draws the row's token,
     // publishes it with the row's state and arrives for the whole row, and
-    // the others leave
+    // the others leave.  (Wave 0 issues first on its SIMD meanwhile: its
+    // chain is serial, the exponentials are not.)
+    __builtin_amdgcn_s_setprio(3);
     const bool draw = g == 0, draft_row = row < p.M - 1;
     double u_last = 0.0;
     int dx = -1;
@@ -1975,9 +2066,11 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     int nn = 0;
     const bool settled =
         rej_top_settle(p, row, G, xw, s_lst, draw && draft_row, zm, rs0, ent, ee, qe, nn);
+    if (lane == 0 && settled) *fast_flag = 1;   // (the other waves stop)
     if (settled && draw) {
       bool use_res = false;
       const int pick = wave_nucleus_draw(p, rs0, row, ent, ee, qe, nn, u_last, use_res);
+      u64 before = 0ull;
       if (lane == 0) {
         if (draft_row) publish_acc(p, row, rs0, dx, dvalid, dzx, dqx);
         __builtin_memcpy(s_w, &rs0, sizeof(rs0));
@@ -1989,13 +2082,23 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           publish_state(rp, tag, rs);
           st_ag(rp + kRowPick, ((u64)tag << 32) | (uint32_t)pick);
           __builtin_amdgcn_s_waitcnt(0);   // acceptance input, state and token before the count
-          s_flag = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) + (u64)G == (u64)p.M * G;
+          before = __hip_atomic_fetch_add(cp + kCallRows, (u64)G, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (pick != -2) {
+        before = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(before >> 32), 0) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)before, 0);
+        // the last to arrive: step 5 here, unless row a's token needs the workgroup
+        const bool last = before + (u64)G == (u64)p.M * G;
+        const bool done = last && rej_pick_drawn(p, tag, s_gen, err);
+        if (lane == 0) {
+          s_flag = last && !done;
           s_drew = 1;
         }
       }
     }
-    if (lane == 0 && settled) *fast_flag = 1;
+    __builtin_amdgcn_s_setprio(0);
   } else {
     const int t0 = solo ? tid - kWave : tid, nth = solo ? kOneThreads - kWave : kOneThreads;
     for (int i = t0; i < n; i += nth) {
