@@ -1857,7 +1857,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   __shared__ int s_blo, s_bhi, s_last, s_flag, s_nc, s_cut, s_a, s_x;
   __shared__ int s_pick, s_blk, s_lastnz, s_fr, s_fe;
   __shared__ int s_an, s_drew, s_lastw, s_nc2;
-  __shared__ int s_fast;
+  __shared__ int s_fast, s_next;
   __shared__ double s_sw[kOneWaves];
   __shared__ u64 s_tk[kOneWaves * (kTopK + 1)], s_lst[kWave];
   __shared__ Fx s_before;
@@ -2021,8 +2021,39 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
           : nullptr;
   const bool solo = xw != nullptr;
   volatile int *const fast_flag = &s_fast;
+  if (tid == 0) s_next = 0;
   __syncthreads();
   Fx tot = fx_zero();
+  // the exponentials: with wave 0 judging, the waves take kWave entries at a
+  // time from a shared count (wave 0 joins when the row is not settled) and
+  // stop once it is; else thread t takes entries t, t + kOneThreads, ...
+  auto e_pass = [&](int i) {
+    const double x = ((double)zc[i] - (double)zmax) / T;
+    const double e = x < -70.5 ? 0.0 : exp(x);     // as e_or_zero
+    ec[i] = e;
+    const Fx f = to_fx(e);
+    uint16_t b = 0xFFFF;
+    if (fx_nonzero(f)) {
+      fx_add(tot, f);
+      b = (uint16_t)xbin(x);
+      if (nucleus) {
+        u64 *h = hx + 3 * b;
+        if (f.lo & 0xFFFFFFFFull) atomicAdd(h, f.lo & 0xFFFFFFFFull);
+        if (f.lo >> 32) atomicAdd(h + 1, f.lo >> 32);
+        if (f.hi) atomicAdd(h + 2, f.hi);
+      }
+    }
+    bc[i] = b;
+  };
+  auto shared_pass = [&]() {
+    for (;;) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_next, kWave);
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (base >= n || *fast_flag) break;   // (a settled row leaves these sums unused)
+      if (base + lane < n) e_pass(base + lane);
+    }
+  };
   if (solo && wave == 0) {
     // (2a) do the top entries settle the cut?  Every workgroup of the row
     // judges the same words alike; if so, workgroup 0 draws the row's token,
@@ -2067,6 +2098,10 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
     const bool settled =
         rej_top_settle(p, row, G, xw, s_lst, draw && draft_row, zm, rs0, ent, ee, qe, nn);
     if (lane == 0 && settled) *fast_flag = 1;   // (the other waves stop)
+    if (!settled) {
+      __builtin_amdgcn_s_setprio(0);
+      shared_pass();
+    }
     if (settled && draw) {
       bool use_res = false;
       const int pick = wave_nucleus_draw(p, rs0, row, ent, ee, qe, nn, u_last, use_res);
@@ -2099,27 +2134,10 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
+  } else if (solo) {
+    shared_pass();
   } else {
-    const int t0 = solo ? tid - kWave : tid, nth = solo ? kOneThreads - kWave : kOneThreads;
-    for (int i = t0; i < n; i += nth) {
-      if (solo && *fast_flag) break;   // (the row is settled: these sums go unused)
-      const double x = ((double)zc[i] - (double)zmax) / T;
-      const double e = x < -70.5 ? 0.0 : exp(x);     // as e_or_zero
-      ec[i] = e;
-      const Fx f = to_fx(e);
-      uint16_t b = 0xFFFF;
-      if (fx_nonzero(f)) {
-        fx_add(tot, f);
-        b = (uint16_t)xbin(x);
-        if (nucleus) {
-          u64 *h = hx + 3 * b;
-          if (f.lo & 0xFFFFFFFFull) atomicAdd(h, f.lo & 0xFFFFFFFFull);
-          if (f.lo >> 32) atomicAdd(h + 1, f.lo >> 32);
-          if (f.hi) atomicAdd(h + 2, f.hi);
-        }
-      }
-      bc[i] = b;
-    }
+    for (int i = tid; i < n; i += kOneThreads) e_pass(i);
   }
   tot = fx_sum_one(tot, red);     // (its barriers also complete the histogram and publish 2a)
   if (s_fast) {   // (uniform)
