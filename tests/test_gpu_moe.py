@@ -127,3 +127,23 @@ def test_k_split_over_waves(fmt):
     # H = 4096 and F = 3072 cut each expert's K into two slices per tile
     # (gate and up tiles in separate waves, the slice sums meeting in LDS)
     check(tiny(13, T=2, E=3, topk=2, H=4096, F=3072, fmt=fmt), f"moe {fmt} K split")
+
+
+def test_one_workspace_across_calls_and_shapes():
+    # calls of different token counts and shapes in a row on one workspace
+    # (each call sets up its own counters), each matched with the oracle,
+    # then the first again
+    cfgs = [tiny(71, T=8, E=16, topk=4, H=256, F=128), tiny(72, T=1, E=16, topk=4, H=256, F=128),
+            tiny(73, T=5, E=9, topk=3, H=128, F=64), tiny(71, T=8, E=16, topk=4, H=256, F=128)]
+    need = max(bv.moe_workspace_bytes(c["T"], c["H"], c["F"], c["E"], c["topk"]) for c in cfgs)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, cfg in enumerate(cfgs):
+        T, H, F, E = cfg["T"], cfg["H"], cfg["F"], cfg["E"]
+        gu, dn = cfg["gate_up"], cfg["down"]
+        gup = bv.pack_weights(gu["format"], dev(gu["codes"]), dev(gu["scales"]), 2 * F, H, count=E)
+        dnp = bv.pack_weights(dn["format"], dev(dn["codes"]), dev(dn["scales"]), H, F, count=E)
+        out, _ = bv.verify_moe(gu["format"], dev(cfg["x"]), dev(cfg["ids"]), dev(cfg["gw"]),
+                               gup, dnp, E, F, gu_global=dev(gu["g"]), dn_global=dev(dn["g"]),
+                               ws=ws)
+        o_out, o_b, _ = oracle.moe(cfg)[:3]
+        assert_gemm_close(host(out).astype(np.float64), o_out, o_b, f"call {i} (T={T})")
