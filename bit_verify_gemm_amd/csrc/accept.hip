@@ -1260,11 +1260,18 @@ __device__ __forceinline__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
 // The steps of the kernels above in one launch of G workgroups per row.  Each
 // workgroup holds a chunk of up to kOneChunk entries of its row in LDS, with
 // the entries' e values, for the whole call.  Rows never wait for each
-// other, and a workgroup waits only on words in its own row's page of the
+// other, and a workgroup waits only on words of its own row in the
 // workspace header:
 //   (1) the row maximum: each workgroup publishes its chunk maximum in a
 //       slot tagged with the call's generation number and waits until every
-//       slot of its row carries this call's tag;
+//       slot of its row carries this call's tag; with top_p < 1 it also hands
+//       over its chunk's approximate mass and largest entries (exchange
+//       words, see rej_top_settle);
+//   (2a) with top_p < 1, wave 0 of every workgroup judges the row's exchange
+//       words while the other waves start step 2: when they settle the cut,
+//       workgroup 0 draws the row's token in one wave, publishes it with the
+//       row's state and arrives for the whole row, and steps 2 to 4 are
+//       skipped;
 //   (2) the mass pass: the exact row total and an approximate fp64 mass
 //       histogram over kXBins bins of x = (z - zmax) / T are summed over the
 //       row.  x is a monotone function of z, so each bin is an interval of
@@ -1284,8 +1291,9 @@ __device__ __forceinline__ const u64 *sort_desc(u64 *a, u64 *b, int n) {
 //       every row), per wave over contiguous ranges;
 //   (5) the last workgroup of the last row to finish derives the accepted
 //       run a from every row's acceptance input and picks the token from row
-//       a's workgroup and range sums, then resets the counters and advances
-//       the generation number.
+//       a's workgroup and range sums (or takes the token row a drew itself,
+//       in one wave), then resets the counters and advances the generation
+//       number.
 // Every decision is taken on exact fixed-point sums, as in the kernels above,
 // so the outputs are theirs.  A wait that runs past its bound sets the error
 // word and goes on (no wave is left spinning).
@@ -1574,23 +1582,23 @@ __device__ __forceinline__ int rej_nucleus_draw(const RejArgs &p, const RowState
 
 // ---- rej_one: rows whose cut the top entries settle ------------------------
 //
-// Step (1b) of rej_one.  Every workgroup of a row with top_p < 1 hands over,
-// with its chunk maximum, an approximate mass of its chunk and its kTopK
-// largest entries; every workgroup of the row then reads all of them and
-// takes the same decision, on the same words in the same order.  The top set
-// is every entry of the row whose key exceeds ks, the largest of the
-// workgroups' (kTopK + 1)-th keys (a workgroup hands over all its entries
-// above its own), so it is a prefix of the row in nucleus order.  Sa, the
-// sum of the chunks' approximate masses, differs from the exact mass S of
-// step 2 (fixed point, below V 2^-100 lost) by a relative error below 2^-14:
-// its terms are fp32 exponentials of arguments below 2^8 in magnitude (one
-// ulp each, plus the argument's three roundings), summed eight at a time in
-// fp32 and in fp64 beyond.  So the threshold lies between the thresholds of
-// Sa (1 -+ 2^-9) -+ V 2^-98, and the cut is settled when, over the top set in
-// nucleus order, the first group of equal keys whose exact prefix reaches
-// the upper threshold is the first to reach the lower one, and the count of
-// its ties inside is the same under both.  The row's state then is the one
-// steps 2 and 3 would find.
+// Steps (1) and (2a) of rej_one.  Every workgroup of a row with top_p < 1
+// hands over, with its chunk maximum, an approximate mass of its chunk, its
+// kTopK largest entries and its (kTopK + 1)-th key; every workgroup of the
+// row then reads all of them and takes the same decision, on the same words
+// in the same order.  A workgroup hands over all of its entries above its
+// own r-th key (r <= kTopK), so the entries above the largest of the
+// workgroups' r-th keys are a prefix of the row in nucleus order (a top
+// set).  Sa, the sum of the chunks' approximate masses, differs from the
+// exact mass S of step 2 (fixed point, below V 2^-100 lost) by a relative
+// error below 2^-14: its terms are fp32 exponentials of arguments below 2^8
+// in magnitude (one ulp each, plus the argument's three roundings), summed
+// eight at a time in fp32 and in fp64 beyond.  So the threshold lies between
+// the thresholds of Sa (1 -+ 2^-9) -+ V 2^-98, and the cut is settled when,
+// over a top set in nucleus order, the first group of equal keys whose exact
+// prefix reaches the upper threshold is the first to reach the lower one,
+// and the count of its ties inside is the same under both.  The row's state
+// then is the one steps 2 and 3 would find.
 
 constexpr double kLog2e = 1.4426950408889634;
 
@@ -1874,7 +1882,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
   // (1) the chunk into LDS and its maximum; this row's sums are cleared
   // (shared out over the row's workgroups) before the maximum is published.
   // With top_p < 1 each workgroup then also hands over its chunk's
-  // approximate mass and top entries (1b), read and judged in step 2.
+  // approximate mass and top entries, read and judged in step 2a.
   if (tid == 0) {
     s_gen = ld_ag(cp + kCallGen) + 1ull;
     s_drew = 0;
@@ -1925,7 +1933,7 @@ __global__ __launch_bounds__(kOneThreads) void rej_one(RejArgs p) {
       if (lane == 0) s_zmax = key_to_float(best);
     }
     if (nucleus) {
-      // (1b) each wave's mass relative to the chunk maximum (fp32
+      // each wave's mass relative to the chunk maximum (fp32
       // exponentials) and its kTopK + 1 largest keys with multiplicity (the
       // winning lane of a round takes its next largest); then wave 0 merges
       // them into this chunk's words
