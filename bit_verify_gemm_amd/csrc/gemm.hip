@@ -227,23 +227,31 @@ GemmPlan gemm_plan(int format, int M, int N, int K) {
   return finish_plan(pl);
 }
 
+constexpr int kDeepPP[] = {3, 4, 5, 6, 8};   // blocks in flight a wave, one workgroup per CU
+
 GemmPlan finish_plan(GemmPlan pl) {
   // Workgroups resident on 256 CUs by LDS and wave slots; when every tile
   // group has its own workgroup, one round; otherwise a persistent loop whose
   // load stream runs on across the tile groups of a workgroup.  A wave's
   // positions per tile group are rounded up to whole rounds of PP blocks in
-  // flight (padding positions load empty windows and skip the arithmetic),
-  // so PP is kPPDeep - 1 or kPPDeep, whichever pads less (the deeper on a
-  // tie); two workgroups on one CU take kPPShallow, whose registers leave
-  // room for both.
+  // flight (padding positions load empty windows and skip the arithmetic).
+  // One round of workgroups (one tile group each) takes kPPDeep - 1 or
+  // kPPDeep, whichever pads less (the deeper on a tie): deeper bursts only
+  // queue behind the activation loads.  A persistent workgroup alone on its
+  // CU (its 8 waves may hold up to 256 registers each) takes the depth of
+  // kDeepPP that pads least, the deeper on a tie: up to a whole slice of 8
+  // blocks in flight across its tile groups.  Two workgroups on one CU take
+  // kPPShallow, whose registers leave room for both.
   int per_cu = (int)(eng::kMaxLds / std::max<size_t>(pl.lds + 1024, 1));
   per_cu = std::max(1, std::min(per_cu, eng::kMaxWaves / (pl.threads / kWave)));
   const int64_t one_round = std::max<int64_t>(1, 256 / pl.KG);
   auto pad = [&](int pp) { return (pl.ppj + pp - 1) / pp * pp - pl.ppj; };
-  const int deep = pad(eng::kPPDeep - 1) < pad(eng::kPPDeep) ? eng::kPPDeep - 1 : eng::kPPDeep;
+  int deep = kDeepPP[0];
+  for (int pp : kDeepPP)
+    if (pad(pp) <= pad(deep)) deep = pp;
   if (pl.TG <= one_round) {
     pl.G = pl.TG;
-    pl.PP = deep;
+    pl.PP = pad(eng::kPPDeep - 1) < pad(eng::kPPDeep) ? eng::kPPDeep - 1 : eng::kPPDeep;
   } else {
     const int64_t cap = std::max<int64_t>(1, (int64_t)256 * per_cu / pl.KG);
     pl.G = (int)std::min<int64_t>(pl.TG, cap);
@@ -269,14 +277,19 @@ hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64
     eng::allow_large_lds(kernel);
     hipLaunchKernelGGL(kernel, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
   };
-  // one kernel per (format, blocks in flight 2..4)
+  // one kernel per (format, blocks in flight: kPPShallow or one of kDeepPP)
   auto pick = [&](auto fmt_tag) {
     constexpr int F = decltype(fmt_tag)::value;
-    if (pl.PP == 2) go(gemm_kernel<F, 2>);
-    else if (pl.PP == 3) go(gemm_kernel<F, 3>);
-    else go(gemm_kernel<F, 4>);
+    switch (pl.PP) {
+      case 2: go(gemm_kernel<F, 2>); break;
+      case 3: go(gemm_kernel<F, 3>); break;
+      case 4: go(gemm_kernel<F, 4>); break;
+      case 5: go(gemm_kernel<F, 5>); break;
+      case 6: go(gemm_kernel<F, 6>); break;
+      default: go(gemm_kernel<F, 8>); break;
+    }
   };
-  static_assert(eng::kPPShallow == 2 && eng::kPPDeep == 4, "kernels exist for 2..4 blocks in flight");
+  static_assert(eng::kPPShallow == 2, "a kernel exists for the shallow depth");
   if (format == MTP_FMT_NVFP4) pick(std::integral_constant<int, MTP_FMT_NVFP4>{});
   else pick(std::integral_constant<int, MTP_FMT_Q4_0>{});
   return hipGetLastError();
