@@ -43,13 +43,20 @@ def test_plan_invariants(fmt, N, K):
         assert p["ws_bytes"] <= bv.gemm_workspace_bytes(N, K)
         assert (p["ws_bytes"] > 0) == (KG > 1)
         # blocks in flight: 2 when two persistent workgroups share a CU (their
-        # registers must fit together); otherwise 3 or 4, whichever pads a
-        # wave's positions per tile group less, 4 on a tie
+        # registers must fit together); one round of workgroups takes 3 or 4,
+        # whichever pads a wave's positions per tile group less, 4 on a tie; a
+        # persistent workgroup alone on its CU takes whichever of 3, 4, 5, 6, 8
+        # pads least, the deeper on a tie
         one_round = p["grid"] <= 256 and p["G"] == p["TG"]
-        pad = {pp: -(-ppj // pp) * pp - ppj for pp in (3, 4)}
-        deep = 3 if pad[3] < pad[4] else 4
+        pad = {pp: -(-ppj // pp) * pp - ppj for pp in (3, 4, 5, 6, 8)}
         per_cu = min(MAX_LDS // (p["lds"] + 1024), 16 // waves)
-        assert p["PP"] == (2 if not one_round and per_cu >= 2 else deep)
+        if one_round:
+            want = 3 if pad[3] < pad[4] else 4
+        elif per_cu >= 2:
+            want = 2
+        else:
+            want = min((pad[pp], -pp) for pp in (3, 4, 5, 6, 8))[1] * -1
+        assert p["PP"] == want
         slices.add((S, ppj))
     assert len(slices) == 1, "the K split must not depend on M"
 
