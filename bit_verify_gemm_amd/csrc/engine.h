@@ -301,7 +301,8 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4, r = lane & 15;
-  const int tw = wave % pl.TW, j = wave / pl.TW;
+  // TW is a power of two (every caller's plan)
+  const int tw = wave & (pl.TW - 1), j = wave >> __builtin_ctz(pl.TW);
   const int pa = pl.kg * pl.J * pl.ppj;               // first pair of the workgroup
   const int np = min(pl.J * pl.ppj, P - pa);          // pairs staged
   const int rowb = row_bytes(np);
@@ -419,17 +420,13 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   }
   const Window xwin = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(xs.base), 0,
                                                         (int)kXWindow, kRsrcWord3);
-  auto step = [&]() {
+  auto step = [&]() {   // (selects, not a branch: lanes wrap at different rounds)
     xvi += vstep;
-    xm += rstep;
-    goff += gstep;
-    loff += lstep;
-    if (xvi >= vpr) {
-      xvi -= vpr;
-      ++xm;
-      goff += gwrap;
-      loff += lwrap;
-    }
+    const bool wrap = xvi >= vpr;
+    xvi -= wrap ? vpr : 0;
+    xm += rstep + (wrap ? 1 : 0);
+    goff += gstep + (wrap ? gwrap : 0u);
+    loff += lstep + (wrap ? lwrap : 0);
   };
   auto load_x = [&]() -> u32x4 {
     const bool ok = xm < M && xvi < vk;

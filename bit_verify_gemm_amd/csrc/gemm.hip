@@ -100,6 +100,7 @@ struct GemmArgs {
   float gscale;
   int M, N, K, T, P;
   int TW, J, S, ppj, KG, TG, G;
+  int tg_base, tg_rem;   // TG = tg_base * G + tg_rem: tile groups per workgroup without a division
   eng::Fixup fx;
 };
 
@@ -134,10 +135,11 @@ __global__ __launch_bounds__(eng::kMaxThreads) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   eng::Plan pl;
   pl.TW = a.TW; pl.J = a.J; pl.S = a.S; pl.ppj = a.ppj; pl.KG = a.KG;
-  pl.kg = blockIdx.x % a.KG;
-  pl.tg_first = blockIdx.x / a.KG;
+  // grid (KG, G): the K group runs fastest in launch order
+  pl.kg = blockIdx.x;
+  pl.tg_first = blockIdx.y;
   pl.tg_step = a.G;
-  pl.tg_count = (a.TG - pl.tg_first + a.G - 1) / a.G;
+  pl.tg_count = a.tg_base + (pl.tg_first < a.tg_rem ? 1 : 0);
   const eng::XSource xs{a.x, a.ldx, nullptr, 1};
   eng::run<FMT, PP, 1, false, false>(a.w, a.P, a.K, a.M, xs, pl, DenseTiles{a.TW, a.T}, a.fx,
                                      lds, false, DenseEpi{&a});
@@ -270,12 +272,13 @@ hipError_t launch_gemm(int format, int M, int N, int K, const uint16_t *x, int64
   a.y = y; a.ldy = ldy; a.yb = yb; a.ldyb = ldyb;
   a.gscale = gscale; a.M = M; a.N = N; a.K = K; a.T = pl.T; a.P = pl.P;
   a.TW = pl.TW; a.J = pl.J; a.S = pl.S; a.ppj = pl.ppj; a.KG = pl.KG; a.TG = pl.TG; a.G = pl.G;
+  a.tg_base = pl.TG / pl.G; a.tg_rem = pl.TG % pl.G;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   a.fx.cnt = reinterpret_cast<uint32_t *>(w8);
   a.fx.part = reinterpret_cast<f32x4 *>(w8 ? w8 + counter_bytes(pl.T) : nullptr);
   auto go = [&](auto kernel) {
     eng::allow_large_lds(kernel);
-    hipLaunchKernelGGL(kernel, dim3(pl.grid), dim3(pl.threads), pl.lds, stream, a);
+    hipLaunchKernelGGL(kernel, dim3(pl.KG, pl.G), dim3(pl.threads), pl.lds, stream, a);
   };
   // one kernel per (format, blocks in flight: kPPShallow or one of kDeepPP)
   auto pick = [&](auto fmt_tag) {

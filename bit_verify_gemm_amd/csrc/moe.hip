@@ -586,6 +586,8 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
   const int slots = (a.P < E) ? a.P : E;
   MoePlan gu = moe_plan(format, 2 * F, H, a.rc, kMoeTiles, true);
   MoePlan dn = moe_plan(format, H, F, a.rc, kMoeTiles, false);
+  // the engine splits a workgroup's waves into (tile, slice) by shifts
+  if ((gu.TW & (gu.TW - 1)) || (dn.TW & (dn.TW - 1))) return hipErrorInvalidValue;
   a.gu = {gu.TW, gu.J, gu.S, gu.ppj, gu.tg};
   a.dn = {dn.TW, dn.J, dn.S, dn.ppj, dn.tg};
   auto go = [&](auto gate_up, auto down) {

@@ -35,7 +35,7 @@ def test_plan_invariants(fmt, N, K):
         assert 1 <= ppj <= 16 and S * ppj >= P and (S - 1) * ppj < P
         assert 1 <= J <= 16 and J * KG >= S and (KG - 1) * J < S
         waves = TW * J
-        assert TW >= 1 and waves <= 8 and p["threads"] == waves * 64
+        assert TW >= 1 and TW & (TW - 1) == 0 and waves <= 8 and p["threads"] == waves * 64
         assert p["TG"] == -(-T // TW) and p["grid"] == p["G"] * KG and 1 <= p["G"] <= p["TG"]
         np_ = min(J * ppj, P)
         lds = M * row_bytes(np_) + (fmt == W.FMT_Q4_0) * (np_ + 1) * 128 * 4 + waves * 1024
