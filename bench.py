@@ -20,14 +20,15 @@ Method:
 * weights are packed once (mtp_pack_weights, outside the timed region);
 * R rotating copies of the weights (R * bytes >= 1 GiB, four times the
   256 MiB Infinity Cache) so every call streams its weights from HBM;
-* the headline captures exactly W warm-up calls and exactly K timed calls
-  (--warmup, --steps) in two HIP graphs (torch.cuda.CUDAGraph); the timed
-  graph is replayed once, bracketed by torch.cuda.synchronize(), and HIP
-  events recorded on the launch stream around it give the time of the K
-  calls (including the gaps between launches).  `value`, `ms_per_step` and
-  `roofline.achieved` all come from that one clock; a sustained figure over
-  at least 20 ms of back-to-back calls is reported beside it, and the
-  in-kernel average of the committed rocprofv3 trace of the same kernel;
+* the headline runs exactly W untimed warm-up calls, then exactly K timed
+  calls (--warmup, --steps) launched directly on one stream behind a
+  GPU-side lead (a bounded spin kernel recorded before the first event, long
+  enough for the host to enqueue all K); HIP events on that stream around
+  the K calls give their GPU time, gaps between launches included.
+  `value`, `ms_per_step` and `roofline.achieved` all come from that one
+  clock; a sustained figure over at least 20 ms of back-to-back calls (HIP
+  graph replays) is reported beside it, and the in-kernel average of the
+  committed rocprofv3 trace of the same kernel;
 * effective GB/s = algorithmic weight bytes (4-bit codes + block scales,
   9/16 byte per weight) / time;
 * the CPU oracle (fp64) runs repeated whole passes of the same workload for
@@ -124,45 +125,56 @@ class Graphed:
         return e0.elapsed_time(e1) / (reps * self.R)
 
 
-def capture(calls, idx):
-    """A HIP graph of calls(i) for i in idx (the launch path warmed first)."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in idx[:4]:
-            calls(i)
-    torch.cuda.current_stream().wait_stream(s)
+LEAD_FIXED_MS = 2.0        # GPU-side lead before the headline's timed calls ...
+LEAD_PER_CALL_MS = 0.04    # ... plus this per call (about 4x the host's enqueue cost)
+
+
+def sleep_cycles_per_ms() -> float:
+    """Rate of torch.cuda._sleep (a bounded spin on the GPU clock), measured
+    on its own: it paces nothing but the lead below."""
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in idx:
-            calls(i)
-    return g
+    n = 2_000_000
+    e0.record(stream)
+    torch.cuda._sleep(n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return n / max(e0.elapsed_time(e1), 1e-3)
 
 
 def time_exact(calls, R, steps, warmup):
-    """Exactly `warmup` untimed calls, then exactly `steps` timed calls, each
-    set captured in one graph; call i uses rotating copy i mod R, and the
-    warm-up takes the copies just before copy 0 so that the timed calls
-    start on the least recently read ones.  Returns (seconds by HIP events
-    on the replay stream, wall seconds), both around the one timed replay."""
-    gw = capture(calls, [(R - warmup % R + i) % R for i in range(warmup)]) if warmup else None
-    gk = capture(calls, [i % R for i in range(steps)])
-    for i in range(R):                     # every copy read once, in order
-        calls(i)
-    if gw is not None:
-        gw.replay()
+    """Exactly `warmup` untimed calls, then exactly `steps` timed calls,
+    launched directly on the current stream; call i uses rotating copy
+    i mod R, and the warm-up takes the copies just before copy 0 so that the
+    timed calls start on the least recently read ones.  The timed calls sit
+    behind a GPU-side lead (a bounded spin kernel, before the first event) of
+    LEAD_FIXED_MS + steps * LEAD_PER_CALL_MS, so the host has enqueued them
+    all before the GPU reaches them and they run back to back: the two HIP
+    events bracket the GPU time of exactly those calls.  (A freshly
+    instantiated graph of the same calls runs 0.4-1.5 us per call slower on
+    its first replay, and a graph cannot be warmed without extra calls.)
+    Returns (seconds by HIP events, host seconds to enqueue the timed calls,
+    lead in ms); the enqueue time must stay below the lead."""
+    for i in range(warmup):
+        calls((R - warmup % R + i) % R)
+    cyc = sleep_cycles_per_ms()
+    lead_ms = LEAD_FIXED_MS + steps * LEAD_PER_CALL_MS
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    torch.cuda._sleep(int(lead_ms * cyc))
     e0.record(stream)
-    gk.replay()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls(i % R)
+    enqueue = time.perf_counter() - t0
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) * 1e-3, wall
+    return e0.elapsed_time(e1) * 1e-3, enqueue, lead_ms
 
 
 def time_graph(calls, R, steps, warmup):
@@ -679,7 +691,7 @@ def main():
 
     # headline: exactly --steps calls, one HIP-event clock
     head = gemm_from_host(bv, cfg["w"], cfg["x"], M, dev)
-    t_ev, t_wall = time_exact(head, head.R, args.steps, args.warmup)
+    t_ev, t_enq, lead_ms = time_exact(head, head.R, args.steps, args.warmup)
     bytes_call = head.bytes
     value = bytes_call * args.steps / t_ev / 1e9
     plan = bv.gemm_plan_info(bv.FMT_NVFP4, M, cfg["w"]["N"], cfg["w"]["K"])
@@ -771,7 +783,9 @@ def main():
                    "M": M, "K": 4096, "N": 14336, "weight_bytes_per_call": bytes_call,
                    "rotating_weight_copies": head.R, "graph_replay": True,
                    "timed_region_ms_hip_events": round(t_ev * 1e3, 4),
-                   "timed_region_ms_wall": round(t_wall * 1e3, 4),
+                   "launch": "direct, behind a GPU-side lead",
+                   "lead_ms": round(lead_ms, 3), "enqueue_ms": round(t_enq * 1e3, 3),
+                   "enqueue_within_lead": bool(t_enq * 1e3 < lead_ms),
                    "plan": {k: plan[k] for k in ("S", "J", "KG", "TW", "grid", "threads")}},
         "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),

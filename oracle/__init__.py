@@ -8,9 +8,13 @@ The arithmetic lives in ``oracle.c`` (plain C, serial fp64 sums, pthreads over
 output columns); this module only marshals numpy arrays through ctypes.  See
 the header of ``oracle.c`` for the definitions and the passages they follow.
 
-Parity unpinned (no page fixes them; they are internally consistent readings):
-the SiLU activation and the bf16 rounding of the MoE intermediate, and the
-bf16 rounding of the first product in the tiny chained verify pass.
+Readings the pages leave open (they name neither): the SiLU activation and
+the bf16 rounding of the MoE intermediate, and the bf16 rounding of the first
+product in the tiny chained verify pass.  The oracle's arithmetic for them is
+pinned all the same: the MoE against an independent composition (library
+element decoders, numpy products, a bf16 rounding checked against brute-force
+nearest-even) and invariants; the chained pass is a composition of the
+pinned GEMM, bf16-rounding and greedy oracles.
 """
 from __future__ import annotations
 

@@ -5,8 +5,8 @@ The MoE oracle is checked against an independent composition written here
 against structural invariants: slot-order combine, deduplication not
 changing results, duplicated experts counted twice, out-of-range ids
 contributing nothing.  The choice of SiLU and of the bf16 rounding of the
-intermediate is a reading of the pages, not something they fix ("parity
-unpinned" for that choice).
+intermediate is a reading of the pages, not something they fix; what is
+pinned here is the oracle's arithmetic for that reading.
 """
 import numpy as np
 import pytest
