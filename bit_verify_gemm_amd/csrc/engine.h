@@ -291,39 +291,10 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4)
 // sync_entry must be true when the workgroup ran the engine before (its LDS
 // may still be in use).
 
-// The first PP blocks of the stream that run() loads first (positions 0 ..
-// PP - 1 of tile group pl.tg_first), issued ahead of run() by a caller that
-// knows the matrix before it can stage the activations; that caller then
-// passes them to run() (PRE).  Called by every thread of the workgroup with
-// the plan and tile_of that run() gets.
-template <int FMT, int PP, int NT, typename TileOf>
-__device__ __forceinline__ void issue_first(const uint8_t *w, int P, const Plan &pl,
-                                            const TileOf &tile_of, Blk<FMT> (&buf)[PP]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int tw = wave & (pl.TW - 1), j = wave >> __builtin_ctz(pl.TW);
-  const int pa = pl.kg * pl.J * pl.ppj;
-  const int np = min(pl.J * pl.ppj, P - pa);
-  const int js = min(np, j * pl.ppj);
-  const int n = min(np, js + pl.ppj) - js;
-  const int t0 = __builtin_amdgcn_readfirstlane(tile_of(pl.tg_first, NT * tw));
-  const int t1 = NT == 1 ? t0 : __builtin_amdgcn_readfirstlane(tile_of(pl.tg_first, NT * tw + NT - 1));
-#pragma unroll
-  for (int i = 0; i < PP; ++i) {   // (PP <= the positions of one tile group)
-    const int t = (NT == 1 || i % NT == 0) ? t0 : t1;
-    const int pi = i / NT;
-    const bool valid = pi < n && t >= 0;
-    const int64_t blk = valid ? ((int64_t)t * P + pa + js + pi) : 0;
-    load_blk(buf[i], block_window(w + blk * kPairBytes, valid), lane);
-  }
-}
-
-template <int FMT, int PP, int NT, bool LOCAL, bool GATHER, bool PRE = false, typename TileOf,
-          typename Epi>
+template <int FMT, int PP, int NT, bool LOCAL, bool GATHER, typename TileOf, typename Epi>
 __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const XSource &xs,
                                     const Plan &pl, const TileOf &tile_of, const Fixup &fx,
-                                    uint8_t *lds, bool sync_entry, Epi &&epi,
-                                    const Blk<FMT> *pre = nullptr) {
+                                    uint8_t *lds, bool sync_entry, Epi &&epi) {
   const int nthreads = pl.TW * pl.J * kWave;
   // wave-uniform values are pinned to scalar registers so that branches on
   // them stay scalar branches (no exec-masked both-ways execution)
@@ -494,17 +465,8 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int kEarly = PRE ? 0 : 1;
+  constexpr int kEarly = 1;
   Blk<FMT> buf[PP];
-  if constexpr (PRE) {
-    // the caller issued positions 0 .. PP - 1 (issue_first); the stream
-    // moves past them
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      buf[i] = pre[i];
-      (void)next_block();
-    }
-  }
 #pragma unroll
   for (int i = 0; i < kEarly; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -512,10 +474,8 @@ __device__ __forceinline__ void run(const uint8_t *w, int P, int K, int M, const
   for (int u = 0; u < kXU; ++u)
     if (u < xr) stage(xv[u], xl[u], xc[u]);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!PRE) {
 #pragma unroll
-    for (int i = kEarly; i < PP; ++i) load_blk(buf[i], next_block(), lane);
-  }
+  for (int i = kEarly; i < PP; ++i) load_blk(buf[i], next_block(), lane);
   __builtin_amdgcn_sched_barrier(0);
   // rounds beyond kXU (only very long staged rows)
   for (int u = kXU; u < xr; ++u) {

@@ -27,7 +27,6 @@
 // which other tokens chose the same expert.
 #include <algorithm>
 #include <mutex>
-#include <type_traits>
 #include <vector>
 
 #include "engine.h"
@@ -79,12 +78,6 @@ struct MoeArgs {
   int32_t *route;         // the routing gate_up derived: order [P], key [P], slots [P][3]
 };
 
-// Threads of a gate_up and of a down workgroup, from the plans in the
-// arguments (a scalar value: no load of the dispatch packet's block size,
-// which could queue behind weight loads already issued).
-__device__ __forceinline__ int gu_threads(const MoeArgs &a) { return a.gu.TW * a.gu.J * kWave; }
-__device__ __forceinline__ int dn_threads(const MoeArgs &a) { return a.dn.TW * a.dn.J * kWave; }
-
 // The routing as one workgroup sees it (LDS).
 struct Route {
   int32_t key[kMaxPairs];     // expert of pair p, kNoExpert for an id outside [0, E) or p >= P
@@ -99,11 +92,8 @@ struct Route {
 // of the valid pairs, in increasing order, are the slots, and slot s holds
 // the pairs of its expert in pair order.  Invalid pairs rank last and belong
 // to no slot.  Called by every thread of the workgroup.
-// ID_REG: the ids come from `id_reg` (lane l holds pair l's id; up to 64
-// pairs), so no memory load sits behind weight loads issued earlier.
-template <bool ID_REG = false>
-__device__ void route(const MoeArgs &a, Route &R, int slot, int id_reg = -1) {
-  const int P = a.P, nt = gu_threads(a);
+__device__ void route(const MoeArgs &a, Route &R, int slot) {
+  const int P = a.P, nt = blockDim.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   // The rank order (expert, pair) is that of the distinct combined keys
   // expert * kMaxPairs + pair (an invalid pair's expert reads as E; E <=
@@ -113,7 +103,7 @@ __device__ void route(const MoeArgs &a, Route &R, int slot, int id_reg = -1) {
   // the rank loop reads whole groups of 16.
   const int P16 = (P + 15) & ~15;
   for (int p = threadIdx.x; p < P16; p += nt) {
-    const int e = p < P ? (ID_REG ? id_reg : a.ids[p]) : -1;
+    const int e = p < P ? a.ids[p] : -1;
     const bool ok = e >= 0 && e < a.E;
     R.key[p] = ok ? e : kNoExpert;
     R.order[p] = p < P ? (ok ? e : a.E) * kMaxPairs + p : 0x7FFFFFFF;
@@ -218,44 +208,6 @@ __device__ void route(const MoeArgs &a, Route &R, int slot, int id_reg = -1) {
   __syncthreads();
 }
 
-// The expert of slot `slot` (the slot-th smallest distinct valid expert of
-// topk_ids, as route() finds it) read straight from topk_ids, without
-// ranking the pairs, or -1 past the unique experts.  Every wave finds it
-// alone with a flag table of its own (`flags`: 64 words, one byte per
-// expert), for up to 64 pairs and kQuickExperts experts; `id` gets the id of
-// the lane's pair (-1 past the pairs).
-constexpr int kQuickExperts = 256;
-
-__device__ __forceinline__ int slot_expert_quick(const MoeArgs &a, int slot, uint32_t *flags,
-                                                 int &id) {
-  const int lane = threadIdx.x & (kWave - 1);
-  flags[lane] = 0u;
-  id = lane < a.P ? a.ids[lane] : -1;
-  // (one wave's LDS accesses run in order; the byte stores may alias the words)
-  if (id >= 0 && id < a.E) reinterpret_cast<uint8_t *>(flags)[id] = 1;
-  const uint32_t f = flags[lane];   // flags of experts 4 lane .. 4 lane + 3
-  const int c = __builtin_popcount(f & 0x01010101u);
-  // experts flagged in the lanes below: the prefix of c (0..4) from its bits
-  const uint64_t lt = (1ull << lane) - 1ull;
-  int before = 0;
-#pragma unroll
-  for (int b = 0; b < 3; ++b) before += __popcll(__ballot((c >> b) & 1) & lt) << b;
-  const bool mine = slot >= before && slot < before + c;
-  int e = -1;
-  if (mine) {
-    int k = slot - before;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if ((f >> (8 * i)) & 1u) {
-        if (k == 0 && e < 0) e = 4 * lane + i;
-        --k;
-      }
-  }
-  const uint64_t m = __ballot(mine);
-  if (!m) return -1;
-  return __builtin_amdgcn_readlane(e, __ffsll((long long)m) - 1);
-}
-
 // Set-up of one call, spread over the workgroups of the gate_up kernel (the
 // down kernel runs after it): clears the arrival counters and out (tokens
 // with no valid pair never complete an arrival and keep the zeros), and
@@ -265,7 +217,7 @@ __device__ void clear_call_state(const MoeArgs &a, const Route &R) {
   const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
   auto share = [&](int n, auto &&f) {
     const int per = (n + nb - 1) / nb, i1 = min(n, (b + 1) * per);
-    for (int i = b * per + (int)threadIdx.x; i < i1; i += gu_threads(a)) f(i);
+    for (int i = b * per + (int)threadIdx.x; i < i1; i += blockDim.x) f(i);
   };
   share(a.T * eng::tiles_of(a.H), [&](int i) {
     __hip_atomic_store(a.cnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -274,7 +226,7 @@ __device__ void clear_call_state(const MoeArgs &a, const Route &R) {
   if (a.h_out)
     for (int p = b; p < a.P; p += nb)
       if (R.key[p] == kNoExpert)
-        for (int f = threadIdx.x; f < a.F; f += gu_threads(a)) a.h_out[(int64_t)p * a.F + f] = 0;
+        for (int f = threadIdx.x; f < a.F; f += blockDim.x) a.h_out[(int64_t)p * a.F + f] = 0;
 }
 
 // The routing for the down kernel (which runs after this one): workgroup
@@ -283,7 +235,7 @@ __device__ void clear_call_state(const MoeArgs &a, const Route &R) {
 __device__ void publish_route(const MoeArgs &a, const Route &R) {
   if (blockIdx.x != 0) return;
   if (blockIdx.y == 0)
-    for (int p = threadIdx.x; p < a.P; p += gu_threads(a)) {
+    for (int p = threadIdx.x; p < a.P; p += blockDim.x) {
       a.route[p] = R.order[p];
       a.route[a.P + p] = R.key[p];
     }
@@ -295,41 +247,9 @@ __device__ void publish_route(const MoeArgs &a, const Route &R) {
   }
 }
 
-// The routing gate_up published, for up to one pair per thread: loaded
-// into registers (before any weight load, so that the stores to LDS do not
-// wait for those), then stored by store_route.
-struct RouteRegs {
-  int order, key, e, first, rows;
-};
-
-__device__ __forceinline__ RouteRegs load_route_regs(const MoeArgs &a, int slot) {
-  const int p = threadIdx.x;
-  RouteRegs r;
-  r.order = p < a.P ? a.route[p] : 0;
-  r.key = p < a.P ? a.route[a.P + p] : 0;
-  const int32_t *sl = a.route + 2 * a.P + 3 * slot;
-  r.e = __builtin_amdgcn_readfirstlane(sl[0]);
-  r.first = __builtin_amdgcn_readfirstlane(sl[1]);
-  r.rows = __builtin_amdgcn_readfirstlane(sl[2]);
-  return r;
-}
-
-__device__ __forceinline__ void store_route(const MoeArgs &a, Route &R, const RouteRegs &r) {
-  if ((int)threadIdx.x < a.P) {
-    R.order[threadIdx.x] = r.order;
-    R.key[threadIdx.x] = r.key;
-  }
-  if (threadIdx.x == 0) {
-    R.e = r.e;
-    R.first = r.first;
-    R.rows = r.rows;
-  }
-  __syncthreads();
-}
-
 // The down kernel's view of the routing, read from what gate_up published.
 __device__ void load_route(const MoeArgs &a, Route &R, int slot) {
-  for (int p = threadIdx.x; p < a.P; p += dn_threads(a)) {
+  for (int p = threadIdx.x; p < a.P; p += blockDim.x) {
     R.order[p] = a.route[p];
     R.key[p] = a.route[a.P + p];
   }
@@ -395,50 +315,35 @@ struct GateUpEpi {
   }
 };
 
-// PAIRED: one wave streams a gate tile and its up tile together (J == 1).
-// PRE (up to 64 pairs and kQuickExperts experts): each wave finds its slot's
-// expert from topk_ids alone and issues its first weight blocks before the
-// ranking, so that the weight stream runs during the routing.
-template <int FMT, int PP, bool PAIRED, bool PRE>
+// PAIRED: one wave streams a gate tile and its up tile together (J == 1)
+template <int FMT, int PP, bool PAIRED>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_gate_up(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ Route R;
-  constexpr int NT = PAIRED ? 2 : 1;
-  const int P = eng::pairs_of(a.H);
-  eng::Plan pl;
-  pl.TW = a.gu.TW; pl.J = a.gu.J; pl.S = a.gu.S; pl.ppj = a.gu.ppj; pl.KG = 1; pl.kg = 0;
-  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x;
-  pl.tg_count = (a.gu.tg - pl.tg_first + gridDim.x - 1) / gridDim.x;
-  const int TWh = PAIRED ? pl.TW : pl.TW / 2;
-  const GateUpTiles tiles{TWh, a.F / 16};
-  const size_t mat = eng::packed_bytes(2 * a.F, a.H);
-  eng::Blk<FMT> pre[PP];
-  int id = -1;
-  if constexpr (PRE) {
-    __shared__ uint32_t qflags[eng::kWgWaves][kWave];
-    const int eq = slot_expert_quick(a, blockIdx.y, qflags[threadIdx.x / kWave], id);
-    if (eq >= 0) eng::issue_first<FMT, PP, NT>(a.gu_packed + (int64_t)eq * mat, P, pl, tiles, pre);
-  }
-  route<PRE>(a, R, blockIdx.y, id);
+  route(a, R, blockIdx.y);
   clear_call_state(a, R);
   publish_route(a, R);
   const int e = __builtin_amdgcn_readfirstlane(R.e);
   if (e < 0) return;  // a slot past the unique experts (whole workgroup)
   const int first = __builtin_amdgcn_readfirstlane(R.first);
   const int rows = __builtin_amdgcn_readfirstlane(R.rows);
-  const uint8_t *w = a.gu_packed + (int64_t)e * mat;
+  const int P = eng::pairs_of(a.H);
+  const uint8_t *w = a.gu_packed + (int64_t)e * eng::packed_bytes(2 * a.F, a.H);
+  eng::Plan pl;
+  pl.TW = a.gu.TW; pl.J = a.gu.J; pl.S = a.gu.S; pl.ppj = a.gu.ppj; pl.KG = 1; pl.kg = 0;
+  pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x;
+  pl.tg_count = (a.gu.tg - pl.tg_first + gridDim.x - 1) / gridDim.x;
+  const int TWh = PAIRED ? pl.TW : pl.TW / 2;
+  const GateUpTiles tiles{TWh, a.F / 16};
   const float gsc = a.gu_global ? a.gu_global[e] : 1.0f;
-  auto pass = [&](int c0, auto pre_tag) {
-    constexpr bool kPre = decltype(pre_tag)::value;
+  for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
     const int32_t *pairs = R.order + first + c0;
     const eng::XSource xs{a.x, a.H, pairs, a.topk};   // row of pair p: token p / topk
-    eng::run<FMT, PP, NT, PAIRED, true, kPre>(
+    eng::run<FMT, PP, PAIRED ? 2 : 1, PAIRED, true>(
         w, P, a.H, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr}, lds, c0 > 0,
-        GateUpEpi{&a, TWh, pl.TW * pl.J * kWave, mc, pairs, gsc}, pre);
-  };
-  pass(0, eng::BoolTag<PRE>{});
-  for (int c0 = a.rc; c0 < rows; c0 += a.rc) pass(c0, eng::BoolTag<false>{});
+        GateUpEpi{&a, TWh, pl.TW * pl.J * kWave, mc, pairs, gsc});
+  }
 }
 
 // y rows are stored at agent scope: another workgroup (on another XCD) may
@@ -494,7 +399,7 @@ __device__ void arrive_and_combine(const MoeArgs &a, const Route &R, const eng::
   const int ntiles = eng::tiles_of(a.H);
   const int per = pl.tg_count * pl.TW;   // tile positions of this workgroup
   const int combos = per * rows;
-  for (int base = 0; base < combos; base += dn_threads(a)) {
+  for (int base = 0; base < combos; base += blockDim.x) {
     if (threadIdx.x == 0) done_n = 0;
     __syncthreads();
     const int c = base + threadIdx.x;
@@ -512,7 +417,7 @@ __device__ void arrive_and_combine(const MoeArgs &a, const Route &R, const eng::
     }
     __syncthreads();
     const int nd = done_n;
-    for (int i = threadIdx.x; i < nd * 16; i += dn_threads(a)) {
+    for (int i = threadIdx.x; i < nd * 16; i += blockDim.x) {
       const int d = done[i >> 4], t = d / ntiles;
       const int n = (d - t * ntiles) * 16 + (i & 15);
       float s = 0.0f;
@@ -538,48 +443,31 @@ __device__ void arrive_and_combine(const MoeArgs &a, const Route &R, const eng::
 }
 
 // LOCAL: one slice per tile (J == 1), each wave finishes its own tile
-// PRE (up to one pair per thread): the routing gate_up published is loaded
-// into registers first, then each wave issues its first weight blocks for
-// the slot's expert, and only then are the routing stored and the rows
-// staged.
-template <int FMT, int PP, bool LOCAL, bool PRE>
+template <int FMT, int PP, bool LOCAL>
 __global__ __launch_bounds__(eng::kMaxThreads) void moe_down(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ Route R;
+  load_route(a, R, blockIdx.y);
+  const int e = __builtin_amdgcn_readfirstlane(R.e);
+  if (e < 0) return;  // a slot past the unique experts (whole workgroup)
+  const int first = __builtin_amdgcn_readfirstlane(R.first);
+  const int rows = __builtin_amdgcn_readfirstlane(R.rows);
   const int P = eng::pairs_of(a.F);
+  const uint8_t *w = a.dn_packed + (int64_t)e * eng::packed_bytes(a.H, a.F);
   eng::Plan pl;
   pl.TW = a.dn.TW; pl.J = a.dn.J; pl.S = a.dn.S; pl.ppj = a.dn.ppj; pl.KG = 1; pl.kg = 0;
   pl.tg_first = blockIdx.x; pl.tg_step = gridDim.x;
   pl.tg_count = (a.dn.tg - pl.tg_first + gridDim.x - 1) / gridDim.x;
   const DownTiles tiles{pl.TW, eng::tiles_of(a.H)};
-  const size_t mat = eng::packed_bytes(a.H, a.F);
-  eng::Blk<FMT> pre[PP];
-  if constexpr (PRE) {   // (up to one pair per thread)
-    const RouteRegs rr = load_route_regs(a, blockIdx.y);
-    if (rr.e < 0) return;  // a slot past the unique experts (whole workgroup)
-    eng::issue_first<FMT, PP, 1>(a.dn_packed + (int64_t)rr.e * mat, P, pl, tiles, pre);
-    store_route(a, R, rr);
-  } else {
-    load_route(a, R, blockIdx.y);
-    if (R.e < 0) return;
-  }
-  const int e = __builtin_amdgcn_readfirstlane(R.e);
-  const int first = __builtin_amdgcn_readfirstlane(R.first);
-  const int rows = __builtin_amdgcn_readfirstlane(R.rows);
-  const uint8_t *w = a.dn_packed + (int64_t)e * mat;
   const float gsc = a.dn_global ? a.dn_global[e] : 1.0f;
-  auto pass = [&](int c0, auto pre_tag) {
-    constexpr bool kPre = decltype(pre_tag)::value;
+  for (int c0 = 0; c0 < rows; c0 += a.rc) {
     const int mc = min(a.rc, rows - c0);
     const int32_t *pairs = R.order + first + c0;
     const eng::XSource xs{a.h, a.F, pairs, 1};
-    eng::run<FMT, PP, 1, LOCAL, true, kPre>(w, P, a.F, mc, xs, pl, tiles,
-                                            eng::Fixup{nullptr, nullptr}, lds, c0 > 0,
-                                            DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, pairs, gsc},
-                                            pre);
-  };
-  pass(0, eng::BoolTag<PRE>{});
-  for (int c0 = a.rc; c0 < rows; c0 += a.rc) pass(c0, eng::BoolTag<false>{});
+    eng::run<FMT, PP, 1, LOCAL, true>(w, P, a.F, mc, xs, pl, tiles, eng::Fixup{nullptr, nullptr},
+                                      lds, c0 > 0,
+                                      DownEpi{&a, pl.TW, pl.TW * pl.J * kWave, mc, pairs, gsc});
+  }
   arrive_and_combine(a, R, pl, first, rows);
 }
 
@@ -710,23 +598,20 @@ hipError_t launch_moe(int format, int T, int H, int F, int E, int topk, const ui
     hipLaunchKernelGGL(gate_up, dim3(gu.G, slots), dim3(gu.threads), gu.lds, stream, a);
     hipLaunchKernelGGL(down, dim3(dn.G, slots), dim3(dn.threads), dn.lds, stream, a);
   };
-  // four blocks per wave in flight; gate_up finds its expert from topk_ids
-  // alone when there are few pairs and experts
+  // four blocks per wave in flight
   constexpr int kD = eng::kPPDeep, kN = MTP_FMT_NVFP4, kQ = MTP_FMT_Q4_0;
-  const bool pg = gu.J == 1, ld = dn.J == 1, quick = a.P <= kWave && E <= kQuickExperts;
-  auto by_format = [&](auto fmt_tag) {
-    constexpr int F = decltype(fmt_tag)::value;
-    auto with_down = [&](auto gate_up) {
-      if (a.P <= dn.threads)
-        ld ? go(gate_up, moe_down<F, kD, true, true>) : go(gate_up, moe_down<F, kD, false, true>);
-      else
-        ld ? go(gate_up, moe_down<F, kD, true, false>) : go(gate_up, moe_down<F, kD, false, false>);
-    };
-    if (pg) quick ? with_down(moe_gate_up<F, kD, true, true>) : with_down(moe_gate_up<F, kD, true, false>);
-    else    quick ? with_down(moe_gate_up<F, kD, false, true>) : with_down(moe_gate_up<F, kD, false, false>);
-  };
-  if (format == kN) by_format(std::integral_constant<int, kN>{});
-  else by_format(std::integral_constant<int, kQ>{});
+  const bool pg = gu.J == 1, ld = dn.J == 1;
+  if (format == kN) {
+    if (pg) ld ? go(moe_gate_up<kN, kD, true>, moe_down<kN, kD, true>)
+               : go(moe_gate_up<kN, kD, true>, moe_down<kN, kD, false>);
+    else    ld ? go(moe_gate_up<kN, kD, false>, moe_down<kN, kD, true>)
+               : go(moe_gate_up<kN, kD, false>, moe_down<kN, kD, false>);
+  } else {
+    if (pg) ld ? go(moe_gate_up<kQ, kD, true>, moe_down<kQ, kD, true>)
+               : go(moe_gate_up<kQ, kD, true>, moe_down<kQ, kD, false>);
+    else    ld ? go(moe_gate_up<kQ, kD, false>, moe_down<kQ, kD, true>)
+               : go(moe_gate_up<kQ, kD, false>, moe_down<kQ, kD, false>);
+  }
   return hipGetLastError();
 }
 

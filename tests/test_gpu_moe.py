@@ -108,6 +108,14 @@ def test_moe_128_experts_top8_full_size():
     check(cfg, "C4")
 
 
+def test_c4_one_token():
+    # the one-token baseline of the MoE workload at full size (its 8 experts,
+    # the quick routing path): every weight block of those experts must be read
+    cfg = W.config4()
+    one = dict(cfg, T=1, x=cfg["x"][:1], ids=cfg["ids"][:1], gw=cfg["gw"][:1])
+    check(one, "C4 one token")
+
+
 def test_many_pairs():
     # 1024 (token, slot) pairs, the most the call takes: every workgroup ranks
     # all of them, and an expert's 60-odd rows take several staging passes
